@@ -1,0 +1,287 @@
+"""ctypes binding of libmk.so (include/mk.h, include/mk_debug.h).
+
+Argument marshalling only: every function here forwards to the C entry point
+of the same name and raises MkError on a non-zero status.  Device buffers are
+torch tensors (their data_ptr()); PyTorch is used only for device memory and
+streams.  There is no CPU fallback: importing this module without a built
+libmk.so raises.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmk.so")
+
+MK_ABI_VERSION = 1
+MK_OK, MK_ERR_INVALID_ARG, MK_ERR_OUT_OF_MEMORY, MK_ERR_HIP = 0, -1, -2, -3
+MK_ERR_CAPACITY, MK_ERR_TIMEOUT, MK_ERR_STATE, MK_ERR_UNSUPPORTED = -4, -5, -6, -7
+MK_MODE_MEGAKERNEL, MK_MODE_PER_OP = 0, 1
+MK_FLAG_TRACE, MK_FLAG_POISON = 1, 2
+STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_OUT_OF_MEMORY", -3: "MK_ERR_HIP",
+                -4: "MK_ERR_CAPACITY", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE", -7: "MK_ERR_UNSUPPORTED"}
+
+
+class MkError(RuntimeError):
+    def __init__(self, status, fn, msg):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class mk_config(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("tie_embeddings", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_seq", ctypes.c_int32), ("mode", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("watchdog_ms", ctypes.c_uint32), ("num_cus", ctypes.c_int32), ("attn_split", ctypes.c_int32)]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class mk_weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("attn_norm", _PP), ("wq", _PP), ("wk", _PP), ("wv", _PP), ("wo", _PP), ("ffn_norm", _PP),
+                ("w_gate", _PP), ("w_up", _PP), ("w_down", _PP)]
+
+
+class mk_kv_layout(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_layer", ctypes.c_int64),
+                ("stride_batch", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("stride_pos", ctypes.c_int64),
+                ("length", ctypes.c_int32), ("batch", ctypes.c_int32)]
+
+
+class mk_graph_info(ctypes.Structure):
+    _fields_ = [("n_tasks", ctypes.c_int32), ("n_events", ctypes.c_int32), ("n_stages", ctypes.c_int32),
+                ("ncu", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("split", ctypes.c_int32),
+                ("max_queue", ctypes.c_int32), ("min_queue", ctypes.c_int32), ("max_cu_bytes", ctypes.c_int64),
+                ("min_cu_bytes", ctypes.c_int64), ("weight_bytes", ctypes.c_int64)]
+
+
+class mk_sim_result(ctypes.Structure):
+    _fields_ = [("completed", ctypes.c_int32), ("executed", ctypes.c_int32), ("blocked_event", ctypes.c_int32),
+                ("race", ctypes.c_int32)]
+
+
+class mk_debug_view(ctypes.Structure):
+    _fields_ = [("xs", ctypes.c_void_p), ("xmid", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("attn_out", ctypes.c_void_p), ("h", ctypes.c_void_p), ("events", ctypes.c_void_p),
+                ("n_events", ctypes.c_int32), ("n_tasks", ctypes.c_int32), ("ncu", ctypes.c_int32),
+                ("nsplit", ctypes.c_int32), ("split", ctypes.c_int32), ("lds_bytes", ctypes.c_int32)]
+
+
+# Every symbol the headers declare, with its ctypes signature.
+_P, _I32, _I64, _U64, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+SIGNATURES = {
+    "mk_create": ([ctypes.POINTER(mk_config), ctypes.POINTER(mk_weights), _P, ctypes.POINTER(_P)], _I32),
+    "mk_prefill": ([_P, _P, _I32, _I32, _P, _P], _I32),
+    "mk_decode_step": ([_P, _P, _P, _P], _I32),
+    "mk_synchronize": ([_P], _I32),
+    "mk_reset": ([_P], _I32),
+    "mk_kv_view": ([_P, ctypes.POINTER(mk_kv_layout)], _I32),
+    "mk_last_error": ([], ctypes.c_char_p),
+    "mk_destroy": ([_P], None),
+    "mk_graph_inspect": ([ctypes.POINTER(mk_config), _I32, ctypes.POINTER(mk_graph_info)], _I32),
+    "mk_graph_simulate": ([ctypes.POINTER(mk_config), _I32, _U64, _I32, _I32, ctypes.POINTER(mk_sim_result)], _I32),
+    "mk_graph_export": ([ctypes.POINTER(mk_config), _I32, _P, _P, _I32, ctypes.POINTER(_I32)], _I32),
+    "mk_get_debug_view": ([_P, ctypes.POINTER(mk_debug_view)], _I32),
+    "mk_read_status": ([_P, ctypes.POINTER(ctypes.c_uint32)], _I32),
+    "mk_read_trace": ([_P, ctypes.POINTER(ctypes.c_uint64), _I32, ctypes.POINTER(_I32),
+                       ctypes.POINTER(ctypes.c_double)], _I32),
+    "mk_t_gemv": ([_P, _P, _P, _I32, _I32, _P], _I32),
+    "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
+    "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "mk_t_argmax": ([_P, _I32, _P, _P], _I32),
+    "mk_device_info": ([ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
+}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_persistent_megakernel_02_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+for _name, (_args, _res) in SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+def _check(status, fn):
+    if status != MK_OK:
+        raise MkError(status, fn, lib.mk_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream) or 0)
+
+
+def make_config(shape, max_seq, max_batch=1, mode=MK_MODE_MEGAKERNEL, flags=0, watchdog_ms=0, num_cus=0,
+                attn_split=0) -> mk_config:
+    """mk_config from a synth.presets.ModelShape-like object."""
+    c = mk_config()
+    c.abi_version = MK_ABI_VERSION
+    c.n_layers, c.hidden, c.n_q_heads = shape.n_layers, shape.hidden, shape.n_q_heads
+    c.n_kv_heads, c.head_dim, c.ffn, c.vocab = shape.n_kv_heads, shape.head_dim, shape.ffn, shape.vocab
+    c.rms_eps, c.rope_theta = shape.rms_eps, shape.rope_theta
+    c.tie_embeddings = 1 if shape.tie_embeddings else 0
+    c.max_batch, c.max_seq, c.mode, c.flags = max_batch, max_seq, mode, flags
+    c.watchdog_ms, c.num_cus, c.attn_split = watchdog_ms, num_cus, attn_split
+    return c
+
+
+class Handle:
+    """An mk_handle plus the Python objects whose memory it borrows."""
+
+    def __init__(self, ptr, keep):
+        self.ptr = ptr
+        self._keep = keep
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            mk_destroy(self)
+
+
+LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+def mk_create(cfg: mk_config, weights: dict, stream=None) -> Handle:
+    """weights: name -> device tensor (bf16 or int16/uint16 bits), names as synth.presets.weight_shapes."""
+    L = cfg.n_layers
+    arrays = {}
+    for f in LAYER_FIELDS:
+        arr = (ctypes.c_void_p * L)(*[weights[f"layers.{l}.{f}"].data_ptr() for l in range(L)])
+        arrays[f] = arr
+    w = mk_weights()
+    w.embed = weights["embed"].data_ptr()
+    w.lm_head = weights["lm_head"].data_ptr() if "lm_head" in weights and not cfg.tie_embeddings else None
+    w.final_norm = weights["final_norm"].data_ptr()
+    for f in LAYER_FIELDS:
+        setattr(w, f, ctypes.cast(arrays[f], _PP))
+    out = ctypes.c_void_p()
+    _check(lib.mk_create(ctypes.byref(cfg), ctypes.byref(w), _stream(stream), ctypes.byref(out)), "mk_create")
+    return Handle(out, (weights, arrays, w, cfg))
+
+
+def mk_prefill(h: Handle, tokens, next_out, logits=None):
+    B, P = tokens.shape
+    _check(lib.mk_prefill(h.ptr, _ptr(tokens), B, P, _ptr(next_out), _ptr(logits)), "mk_prefill")
+
+
+def mk_decode_step(h: Handle, d_in, d_out, logits=None):
+    _check(lib.mk_decode_step(h.ptr, _ptr(d_in), _ptr(d_out), _ptr(logits)), "mk_decode_step")
+
+
+def mk_synchronize(h: Handle):
+    _check(lib.mk_synchronize(h.ptr), "mk_synchronize")
+
+
+def mk_reset(h: Handle):
+    _check(lib.mk_reset(h.ptr), "mk_reset")
+
+
+def mk_kv_view(h: Handle) -> mk_kv_layout:
+    out = mk_kv_layout()
+    _check(lib.mk_kv_view(h.ptr, ctypes.byref(out)), "mk_kv_view")
+    return out
+
+
+def mk_last_error() -> str:
+    return lib.mk_last_error().decode()
+
+
+def mk_destroy(h: Handle):
+    if h.ptr:
+        lib.mk_destroy(h.ptr)
+        h.ptr = None
+
+
+def mk_graph_inspect(cfg: mk_config, ncu: int) -> mk_graph_info:
+    out = mk_graph_info()
+    _check(lib.mk_graph_inspect(ctypes.byref(cfg), ncu, ctypes.byref(out)), "mk_graph_inspect")
+    return out
+
+
+def mk_graph_simulate(cfg: mk_config, ncu: int, seed: int, workers: int = 7, drop_event: int = -1) -> mk_sim_result:
+    out = mk_sim_result()
+    _check(lib.mk_graph_simulate(ctypes.byref(cfg), ncu, seed, workers, drop_event, ctypes.byref(out)),
+           "mk_graph_simulate")
+    return out
+
+
+TASK_DTYPE = None
+
+
+def task_dtype():
+    import numpy as np
+    return np.dtype([("type", "u1"), ("page", "u1"), ("layer", "<u2"), ("in_event", "<u2"), ("out_event", "<u2"),
+                     ("in_count", "<u4"), ("stage", "<u2"), ("batch", "<u2"), ("local_slot", "<u2"),
+                     ("local_count", "<u2"), ("id", "<u4"), ("a0", "<i4"), ("a1", "<i4"), ("a2", "<i4"),
+                     ("a3", "<i4"), ("_pad", "V8")])
+
+
+def mk_graph_export(cfg: mk_config, ncu: int):
+    """(tasks structured array in global order, cu of each task)."""
+    import numpy as np
+    n = ctypes.c_int32()
+    _check(lib.mk_graph_export(ctypes.byref(cfg), ncu, None, None, 0, ctypes.byref(n)), "mk_graph_export")
+    tasks = np.zeros(n.value, dtype=task_dtype())
+    cu = np.zeros(n.value, dtype=np.int32)
+    _check(lib.mk_graph_export(ctypes.byref(cfg), ncu, tasks.ctypes.data, cu.ctypes.data, n.value, ctypes.byref(n)),
+           "mk_graph_export")
+    return tasks, cu
+
+
+def mk_get_debug_view(h: Handle) -> mk_debug_view:
+    out = mk_debug_view()
+    _check(lib.mk_get_debug_view(h.ptr, ctypes.byref(out)), "mk_get_debug_view")
+    return out
+
+
+def mk_read_status(h: Handle):
+    out = (ctypes.c_uint32 * 8)()
+    _check(lib.mk_read_status(h.ptr, out), "mk_read_status")
+    return list(out)
+
+
+def mk_read_trace(h: Handle):
+    import numpy as np
+    n = ctypes.c_int32()
+    tpu = ctypes.c_double()
+    _check(lib.mk_read_trace(h.ptr, None, 0, ctypes.byref(n), ctypes.byref(tpu)), "mk_read_trace")
+    buf = np.zeros(2 * n.value, dtype=np.uint64)
+    _check(lib.mk_read_trace(h.ptr, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n.value, ctypes.byref(n),
+                             ctypes.byref(tpu)), "mk_read_trace")
+    return buf.reshape(-1, 2), tpu.value
+
+
+def mk_t_gemv(W, x, y, stream=None):
+    N, K = W.shape
+    _check(lib.mk_t_gemv(_ptr(W), _ptr(x), _ptr(y), N, K, _stream(stream)), "mk_t_gemv")
+
+
+def mk_t_rmsnorm(x, gamma, eps, y, stream=None):
+    _check(lib.mk_t_rmsnorm(_ptr(x), _ptr(gamma), eps, _ptr(y), x.numel(), _stream(stream)), "mk_t_rmsnorm")
+
+
+def mk_t_attention(q, k, v, T, split, o, stream=None):
+    """q [nq, hd] fp32; k, v [nkv, S, hd] bf16 (S >= T); o [nq, hd] fp32."""
+    nq, hd = q.shape
+    nkv, S, _ = k.shape
+    _check(lib.mk_t_attention(_ptr(q), _ptr(k), _ptr(v), S * hd, nq, nkv, hd, T, split, _ptr(o), _stream(stream)),
+           "mk_t_attention")
+
+
+def mk_t_argmax(x, out, stream=None):
+    _check(lib.mk_t_argmax(_ptr(x), x.numel(), _ptr(out), _stream(stream)), "mk_t_argmax")
+
+
+def mk_device_info():
+    n, l = ctypes.c_int32(), ctypes.c_int32()
+    t = ctypes.c_double()
+    _check(lib.mk_device_info(ctypes.byref(n), ctypes.byref(t), ctypes.byref(l)), "mk_device_info")
+    return n.value, t.value, l.value

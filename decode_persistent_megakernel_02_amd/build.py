@@ -1,0 +1,62 @@
+"""Build libmk.so (HIP, gfx950) and the seeded-input helper library in-tree.
+
+Run as `python -m decode_persistent_megakernel_02_amd.build`; __graft_entry__.build()
+calls `build_all()`.  Always recompiles.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libmk.so")
+ARCH = os.environ.get("MK_OFFLOAD_ARCH", "gfx950")
+
+# Packed-fp32 instructions are kept out of every device build.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build_lib(verbose=False, out=LIB):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    srcs = [os.path.join(CSRC, f) for f in ("kernels.hip", "api.hip")]
+    host = os.path.join(CSRC, "graph.cpp")
+    inc = ["-I", CSRC, "-I", os.path.join(ROOT, "include")]
+    bdir = os.path.join(PKG, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = []
+    for src in srcs:
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
+        _run([hipcc] + HIP_FLAGS + inc + ["-c", "-o", obj, src], verbose)
+        objs.append(obj)
+    obj = os.path.join(bdir, "graph.o")
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall"] + inc + ["-c", "-o", obj, host], verbose)
+    objs.append(obj)
+    tmp = out + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, out)
+    return out
+
+
+def build_synth(verbose=False):
+    src = os.path.join(ROOT, "synth", "gen.c")
+    out = os.path.join(ROOT, "synth", "libsynth.so")
+    _run(["gcc", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-pthread", "-o", out, src], verbose)
+    return out
+
+
+def build_all(verbose=False):
+    build_synth(verbose)
+    build_lib(verbose)
+
+
+if __name__ == "__main__":
+    build_all(verbose="-q" not in sys.argv)

@@ -1,0 +1,603 @@
+// Host implementation of the C ABI (include/mk.h, include/mk_debug.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "graph.h"
+#include "kernels.h"
+#include "mk.h"
+#include "mk_debug.h"
+
+using namespace mk;
+
+namespace {
+
+thread_local std::string g_err;
+
+mk_status fail(mk_status s, const std::string& m) {
+  g_err = m;
+  return s;
+}
+
+#define HIP_TRY(x)                                                                              \
+  do {                                                                                          \
+    hipError_t e_ = (x);                                                                        \
+    if (e_ != hipSuccess) return fail(MK_ERR_HIP, std::string(#x) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+std::string check_config(const mk_config* c) {
+  if (!c) return "config is NULL";
+  if (c->abi_version != MK_ABI_VERSION) return "abi_version mismatch";
+  if (c->n_layers < 1 || c->hidden < 8 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->ffn < 8 || c->vocab < 1)
+    return "non-positive model dimension";
+  if (c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 64 or 128";
+  if (c->n_q_heads % c->n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
+  if (c->n_q_heads / c->n_kv_heads > kMaxGqa) return "at most 8 query heads per KV head";
+  if (c->hidden % 8 || c->ffn % 8 || (c->n_q_heads * c->head_dim) % 8)
+    return "hidden, ffn and n_q_heads*head_dim must be multiples of 8";
+  if (c->max_batch < 1 || c->max_batch > kMaxBatch) return "max_batch must be in [1, 64]";
+  if (c->max_seq < 1) return "max_seq must be >= 1";
+  if (c->mode != MK_MODE_MEGAKERNEL && c->mode != MK_MODE_PER_OP) return "unknown mode";
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return "rms_eps must be >= 0 and rope_theta > 0";
+  if (c->attn_split < 0 || c->attn_split > kMaxSplit) return "attn_split must be in [0, 64]";
+  if (c->num_cus < 0) return "num_cus must be >= 0";
+  if ((int64_t)c->vocab * c->hidden >= (1ll << 40)) return "vocab * hidden too large";
+  return "";
+}
+
+GraphConfig graph_config(const mk_config* c, int ncu) {
+  GraphConfig g;
+  g.L = c->n_layers; g.H = c->hidden; g.nq = c->n_q_heads; g.nkv = c->n_kv_heads; g.hd = c->head_dim;
+  g.F = c->ffn; g.V = c->vocab; g.B = c->max_batch; g.max_seq = c->max_seq;
+  g.split = c->attn_split ? c->attn_split : auto_split(c->max_seq);
+  g.ncu = ncu;
+  return g;
+}
+
+int64_t task_weight_bytes(const GraphConfig& c, const Task& t) {
+  switch (t.type) {
+    case TT_QKV: return (int64_t)t.a2 * c.H * 2;
+    case TT_O: return (int64_t)t.a2 * c.nq * c.hd * 2;
+    case TT_GU: return (int64_t)2 * t.a2 * c.H * 2;
+    case TT_DOWN: return (int64_t)t.a2 * c.F * 2;
+    case TT_LM: return (int64_t)t.a2 * c.H * 2;
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+struct mk_handle {
+  mk_config cfg{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  Graph graph;
+  Params P{};
+  std::vector<void*> allocs;
+  Task* d_stage_tasks = nullptr;
+  int page_floats = 0, scratch_floats = 0, lds_mega = 0, lds_stage = 0;
+  int length = 0, batch = 0;
+  uint32_t epoch = 0;
+  bool poisoned = false;
+  int32_t* d_tok_scratch = nullptr;
+  float* act = nullptr;
+  int64_t act_floats = 0;
+  double ticks_per_us = 100.0;
+
+  template <class T>
+  mk_status alloc(T** p, int64_t count) {
+    void* q = nullptr;
+    const size_t bytes = std::max<int64_t>(count, 1) * sizeof(T);
+    if (hipMalloc(&q, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MK_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
+    }
+    allocs.push_back(q);
+    *p = static_cast<T*>(q);
+    return MK_OK;
+  }
+  ~mk_handle() {
+    for (void* p : allocs) (void)hipFree(p);
+  }
+};
+
+#define MK_TRY(x)                     \
+  do {                                \
+    mk_status s_ = (x);               \
+    if (s_ != MK_OK) return s_;       \
+  } while (0)
+
+namespace {
+
+mk_status device_facts(int* ncu, double* ticks_per_us, int* max_lds) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  int n = 0, khz = 0, lds = 0;
+  HIP_TRY(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
+  HIP_TRY(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+  HIP_TRY(hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+  int optin = 0;
+  if (hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess && optin > lds)
+    lds = optin;
+  (void)hipGetLastError();
+  if (ncu) *ncu = n;
+  if (ticks_per_us) *ticks_per_us = khz > 0 ? khz / 1000.0 : 100.0;
+  if (max_lds) *max_lds = lds;
+  return MK_OK;
+}
+
+mk_status launch_step(mk_handle* h, const Step& S) {
+  const Params& P = h->P;
+  if (h->cfg.flags & MK_FLAG_POISON) {
+    hipLaunchKernelGGL(mk_fill_u32, dim3(1024), dim3(256), 0, h->stream, reinterpret_cast<uint32_t*>(h->act),
+                       h->act_floats, 0xFFFFFFFFu);
+    HIP_TRY(hipGetLastError());
+  }
+  int pf = h->page_floats, sf = h->scratch_floats;
+  if (h->cfg.mode == MK_MODE_MEGAKERNEL) {
+    Params Pc = P;
+    Step Sc = S;
+    void* args[] = {&Pc, &Sc, &pf, &sf};
+    HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mk_persistent), dim3(P.ncu),
+                                       dim3(kWaves * kWave), args, (unsigned)h->lds_mega, h->stream));
+  } else {
+    const auto& g = h->graph;
+    for (size_t s = 0; s + 1 < g.stage_begin.size(); ++s) {
+      const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
+      if (count <= 0) continue;
+      int grid = std::min((count + kWaves - 1) / kWaves, P.ncu);
+      hipLaunchKernelGGL(mk_stage, dim3(grid), dim3(kWaves * kWave), (unsigned)h->lds_stage, h->stream, P, S,
+                         h->d_stage_tasks + b0, count, pf, sf);
+      HIP_TRY(hipGetLastError());
+    }
+  }
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_last_error(void) { return g_err.c_str(); }
+
+mk_status mk_device_info(int32_t* ncu, double* ticks_per_us, int32_t* max_lds) {
+  int n = 0, l = 0;
+  double t = 0;
+  MK_TRY(device_facts(&n, &t, &l));
+  if (ncu) *ncu = n;
+  if (ticks_per_us) *ticks_per_us = t;
+  if (max_lds) *max_lds = l;
+  return MK_OK;
+}
+
+mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream, mk_handle** out) {
+  g_err.clear();
+  if (!out) return fail(MK_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  const std::string cerr = check_config(cfg);
+  if (!cerr.empty()) return fail(MK_ERR_INVALID_ARG, cerr);
+  if (!w || !w->embed || !w->final_norm || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->ffn_norm ||
+      !w->w_gate || !w->w_up || !w->w_down)
+    return fail(MK_ERR_INVALID_ARG, "weights: NULL pointer");
+  if ((w->lm_head == nullptr) != (cfg->tie_embeddings != 0))
+    return fail(MK_ERR_INVALID_ARG, "weights: lm_head must be NULL exactly when tie_embeddings is set");
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
+        !w->w_up[l] || !w->w_down[l])
+      return fail(MK_ERR_INVALID_ARG, "weights: NULL pointer in layer " + std::to_string(l));
+  if (cfg->max_batch != 1) return fail(MK_ERR_UNSUPPORTED, "max_batch > 1 is not implemented yet");
+
+  int dev_cus = 0, max_lds = 0;
+  double tpu = 100.0;
+  MK_TRY(device_facts(&dev_cus, &tpu, &max_lds));
+  const int ncu = cfg->num_cus > 0 ? std::min(cfg->num_cus, dev_cus) : dev_cus;
+  if (ncu < 1) return fail(MK_ERR_HIP, "no compute units reported");
+
+  auto* h = new mk_handle();
+  std::unique_ptr<mk_handle> guard(h);
+  h->cfg = *cfg;
+  h->stream = static_cast<hipStream_t>(hip_stream);
+  HIP_TRY(hipGetDevice(&h->device));
+  h->ticks_per_us = tpu;
+
+  const GraphConfig gc = graph_config(cfg, ncu);
+  std::string e = build_graph(gc, h->graph);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
+  e = validate_graph(h->graph);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "graph validation: " + e);
+  const Graph& g = h->graph;
+
+  const int L = cfg->n_layers, H = cfg->hidden, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, hd = cfg->head_dim;
+  const int F = cfg->ffn, V = cfg->vocab, B = cfg->max_batch, S = cfg->max_seq, G = nq / nkv;
+  Params& P = h->P;
+  P.L = L; P.H = H; P.nq = nq; P.nkv = nkv; P.hd = hd; P.F = F; P.V = V; P.B = B; P.max_seq = S;
+  P.split = gc.split; P.nsplit = g.nsplit; P.tied = cfg->tie_embeddings ? 1 : 0; P.eps = cfg->rms_eps;
+  P.ncu = ncu;
+  const double wd_ms = cfg->watchdog_ms ? cfg->watchdog_ms : 2000.0;
+  P.timeout_ticks = (uint32_t)std::min(4.0e9, wd_ms * 1000.0 * tpu);
+  P.embed = static_cast<const uint16_t*>(w->embed);
+  P.lm_head = static_cast<const uint16_t*>(w->lm_head);
+  P.final_norm = static_cast<const uint16_t*>(w->final_norm);
+
+  // layer pointer tables
+  const void* const* lists[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down};
+  const uint16_t** d_ptrs = nullptr;
+  MK_TRY(h->alloc(&d_ptrs, 9 * (int64_t)L));
+  std::vector<const void*> hp(9 * (size_t)L);
+  for (int i = 0; i < 9; ++i)
+    for (int l = 0; l < L; ++l) hp[(size_t)i * L + l] = lists[i][l];
+  HIP_TRY(hipMemcpy(d_ptrs, hp.data(), hp.size() * sizeof(void*), hipMemcpyHostToDevice));
+  P.attn_norm = d_ptrs + 0 * L; P.wq = d_ptrs + 1 * L; P.wk = d_ptrs + 2 * L; P.wv = d_ptrs + 3 * L;
+  P.wo = d_ptrs + 4 * L; P.ffn_norm = d_ptrs + 5 * L; P.w_gate = d_ptrs + 6 * L; P.w_up = d_ptrs + 7 * L;
+  P.w_down = d_ptrs + 8 * L;
+
+  // KV cache
+  const int64_t kv_elems = (int64_t)L * B * nkv * S * hd;
+  MK_TRY(h->alloc(&P.kcache, kv_elems));
+  MK_TRY(h->alloc(&P.vcache, kv_elems));
+  HIP_TRY(hipMemset(P.kcache, 0, kv_elems * 2));
+  HIP_TRY(hipMemset(P.vcache, 0, kv_elems * 2));
+
+  // activations, one allocation
+  const int64_t n_xs = (int64_t)(L + 1) * B * H, n_xmid = (int64_t)L * B * H, n_q = (int64_t)L * B * nq * hd;
+  const int64_t n_part = (int64_t)L * B * nkv * g.nsplit * G * (hd + 2), n_aout = n_q, n_h = (int64_t)L * B * F;
+  h->act_floats = n_xs + n_xmid + n_q + n_part + n_aout + n_h;
+  MK_TRY(h->alloc(&h->act, h->act_floats));
+  HIP_TRY(hipMemset(h->act, 0, h->act_floats * 4));
+  P.xs = h->act;
+  P.xmid = P.xs + n_xs;
+  P.q = P.xmid + n_xmid;
+  P.attn_part = P.q + n_q;
+  P.attn_out = P.attn_part + n_part;
+  P.h = P.attn_out + n_aout;
+  MK_TRY(h->alloc(&P.lm_part, B));
+  HIP_TRY(hipMemset(P.lm_part, 0, B * sizeof(unsigned long long)));
+
+  // RoPE angle tables, computed in double precision
+  {
+    const int half = hd / 2;
+    std::vector<float> cs((size_t)S * half), sn((size_t)S * half);
+    for (int p = 0; p < S; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double a = (double)p * std::pow((double)cfg->rope_theta, -2.0 * i / hd);
+        cs[(size_t)p * half + i] = (float)std::cos(a);
+        sn[(size_t)p * half + i] = (float)std::sin(a);
+      }
+    float *dc = nullptr, *ds = nullptr;
+    MK_TRY(h->alloc(&dc, (int64_t)S * half));
+    MK_TRY(h->alloc(&ds, (int64_t)S * half));
+    HIP_TRY(hipMemcpy(dc, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(ds, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+    P.rope_cos = dc;
+    P.rope_sin = ds;
+  }
+
+  // task tables
+  Task* d_flat = nullptr;
+  int32_t* d_qoff = nullptr;
+  MK_TRY(h->alloc(&d_flat, (int64_t)g.flat.size()));
+  MK_TRY(h->alloc(&d_qoff, (int64_t)g.queue_off.size()));
+  MK_TRY(h->alloc(&h->d_stage_tasks, (int64_t)g.tasks.size()));
+  HIP_TRY(hipMemcpy(d_flat, g.flat.data(), g.flat.size() * sizeof(Task), hipMemcpyHostToDevice));
+  HIP_TRY(hipMemcpy(d_qoff, g.queue_off.data(), g.queue_off.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(hipMemcpy(h->d_stage_tasks, g.tasks.data(), g.tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
+  P.tasks = d_flat;
+  P.queue_off = d_qoff;
+  MK_TRY(h->alloc(&P.events, (int64_t)g.event_count.size()));
+  HIP_TRY(hipMemset(P.events, 0, g.event_count.size() * 4));
+  MK_TRY(h->alloc(&P.status, 8));
+  HIP_TRY(hipMemset(P.status, 0, 32));
+  if (cfg->flags & MK_FLAG_TRACE) {
+    MK_TRY(h->alloc(&P.trace, 2 * (int64_t)g.tasks.size()));
+    HIP_TRY(hipMemset(P.trace, 0, 16 * g.tasks.size()));
+    P.trace_cap = (int32_t)g.tasks.size();
+  }
+  MK_TRY(h->alloc(&h->d_tok_scratch, B));
+
+  // LDS budget
+  h->page_floats = round_up(std::max({H, nq * hd, F}), 8);
+  h->scratch_floats = round_up(G * hd + G * kWave, 4);
+  h->lds_mega = (int)sizeof(Lds) + 2 * h->page_floats * 4 + kWorkers * h->scratch_floats * 4;
+  h->lds_stage = (int)sizeof(Lds) + h->page_floats * 4 + kWaves * h->scratch_floats * 4;
+  if (h->lds_mega > max_lds || h->lds_stage > max_lds)
+    return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(h->lds_mega) + " B exceeds " + std::to_string(max_lds));
+  // keep one persistent workgroup per CU: ask for more than half the LDS
+  if (h->lds_mega <= max_lds / 2) h->lds_mega = max_lds / 2 + 1024;
+  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_persistent),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, h->lds_mega));
+  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_stage), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              h->lds_stage));
+  if (cfg->mode == MK_MODE_MEGAKERNEL) {
+    int nb = 0;
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&mk_persistent),
+                                                         kWaves * kWave, h->lds_mega));
+    if (nb < 1) return fail(MK_ERR_UNSUPPORTED, "persistent kernel does not fit on a CU");
+  }
+  HIP_TRY(hipDeviceSynchronize());
+  *out = guard.release();
+  return MK_OK;
+}
+
+mk_status mk_decode_step(mk_handle* h, const int32_t* d_in, int32_t* d_out, float* d_logits) {
+  g_err.clear();
+  if (!h || !d_in || !d_out) return fail(MK_ERR_INVALID_ARG, "NULL handle or token pointer");
+  if (h->poisoned) return fail(MK_ERR_STATE, "handle poisoned by an earlier in-kernel error");
+  if (h->length >= h->cfg.max_seq) return fail(MK_ERR_CAPACITY, "KV cache full");
+  if (h->batch == 0) h->batch = h->cfg.max_batch;
+  Step S{};
+  S.epoch = ++h->epoch;
+  S.pos = h->length;
+  S.tokens = d_in;
+  S.tok_stride = 1;
+  S.out = d_out;
+  S.logits = d_logits;
+  MK_TRY(launch_step(h, S));
+  h->length++;
+  return MK_OK;
+}
+
+mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P, int32_t* d_next, float* d_logits) {
+  g_err.clear();
+  if (!h || !d_tokens || !d_next) return fail(MK_ERR_INVALID_ARG, "NULL handle or token pointer");
+  if (h->poisoned) return fail(MK_ERR_STATE, "handle poisoned by an earlier in-kernel error");
+  if (h->length != 0) return fail(MK_ERR_STATE, "prefill requires an empty cache (call mk_reset)");
+  if (P < 1) return fail(MK_ERR_INVALID_ARG, "prefill length must be >= 1");
+  if (B < 1 || B > h->cfg.max_batch) return fail(MK_ERR_CAPACITY, "batch outside [1, max_batch]");
+  if (B != h->cfg.max_batch) return fail(MK_ERR_UNSUPPORTED, "batch must equal max_batch");
+  if (P > h->cfg.max_seq) return fail(MK_ERR_CAPACITY, "prompt longer than max_seq");
+  h->batch = B;
+  for (int p = 0; p < P; ++p) {
+    Step S{};
+    S.epoch = ++h->epoch;
+    S.pos = p;
+    S.tokens = d_tokens + p;
+    S.tok_stride = P;
+    const bool last = p == P - 1;
+    S.out = last ? d_next : h->d_tok_scratch;
+    S.logits = last ? d_logits : nullptr;
+    MK_TRY(launch_step(h, S));
+    h->length++;
+  }
+  return MK_OK;
+}
+
+mk_status mk_read_status(mk_handle* h, uint32_t out[8]) {
+  if (!h || !out) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  HIP_TRY(hipStreamSynchronize(h->stream));
+  HIP_TRY(hipMemcpy(out, h->P.status, 32, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+mk_status mk_synchronize(mk_handle* h) {
+  g_err.clear();
+  if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
+  uint32_t st[8];
+  MK_TRY(mk_read_status(h, st));
+  if (st[1] == ST_TIMEOUT) {
+    h->poisoned = true;
+    return fail(MK_ERR_TIMEOUT, "watchdog: CU " + std::to_string(st[2]) + " task " + std::to_string(st[3]) +
+                                    " waited on event " + std::to_string(st[4]) + " (counter " +
+                                    std::to_string(st[5]) + ", threshold " + std::to_string(st[6]) + ")");
+  }
+  if (st[1] == ST_NONFINITE) {
+    h->poisoned = true;
+    return fail(MK_ERR_STATE, "non-finite logits");
+  }
+  if (st[1] == ST_BADTOKEN) {
+    h->poisoned = true;
+    return fail(MK_ERR_INVALID_ARG, "a token id outside [0, vocab) was fed to the kernel (clamped)");
+  }
+  if (h->poisoned) return fail(MK_ERR_STATE, "handle poisoned");
+  return MK_OK;
+}
+
+mk_status mk_reset(mk_handle* h) {
+  g_err.clear();
+  if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
+  HIP_TRY(hipStreamSynchronize(h->stream));
+  if (h->poisoned) return fail(MK_ERR_STATE, "handle poisoned; destroy and recreate it");
+  HIP_TRY(hipMemset(h->P.events, 0, h->graph.event_count.size() * 4));
+  HIP_TRY(hipMemset(h->P.lm_part, 0, h->cfg.max_batch * sizeof(unsigned long long)));
+  HIP_TRY(hipDeviceSynchronize());
+  h->length = 0;
+  h->batch = 0;
+  h->epoch = 0;
+  return MK_OK;
+}
+
+mk_status mk_kv_view(mk_handle* h, mk_kv_layout* out) {
+  if (!h || !out) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  const auto& P = h->P;
+  out->k = P.kcache;
+  out->v = P.vcache;
+  out->stride_pos = P.hd;
+  out->stride_head = (int64_t)P.max_seq * P.hd;
+  out->stride_batch = (int64_t)P.nkv * out->stride_head;
+  out->stride_layer = (int64_t)P.B * out->stride_batch;
+  out->length = h->length;
+  out->batch = h->batch;
+  return MK_OK;
+}
+
+void mk_destroy(mk_handle* h) {
+  if (!h) return;
+  (void)hipStreamSynchronize(h->stream);
+  delete h;
+}
+
+// ---- debug / inspection ------------------------------------------------------
+
+mk_status mk_graph_inspect(const mk_config* cfg, int32_t ncu, mk_graph_info* out) {
+  g_err.clear();
+  const std::string cerr = check_config(cfg);
+  if (!cerr.empty()) return fail(MK_ERR_INVALID_ARG, cerr);
+  if (ncu < 1 || !out) return fail(MK_ERR_INVALID_ARG, "ncu < 1 or out NULL");
+  const GraphConfig gc = graph_config(cfg, ncu);
+  Graph g;
+  std::string e = build_graph(gc, g);
+  if (!e.empty()) return fail(cfg->max_batch > 1 ? MK_ERR_UNSUPPORTED : MK_ERR_INVALID_ARG, e);
+  e = validate_graph(g);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "graph validation: " + e);
+  out->n_tasks = (int32_t)g.tasks.size();
+  out->n_events = (int32_t)g.event_count.size();
+  out->n_stages = (int32_t)g.stage_begin.size() - 1;
+  out->ncu = ncu;
+  out->nsplit = g.nsplit;
+  out->split = gc.split;
+  out->max_queue = 0;
+  out->min_queue = 1 << 30;
+  out->max_cu_bytes = 0;
+  out->min_cu_bytes = INT64_MAX;
+  out->weight_bytes = 0;
+  for (int cu = 0; cu < ncu; ++cu) {
+    const int n = (int)g.queues[cu].size();
+    out->max_queue = std::max(out->max_queue, n);
+    out->min_queue = std::min(out->min_queue, n);
+    int64_t bytes = 0;
+    for (int id : g.queues[cu]) bytes += task_weight_bytes(gc, g.tasks[id]);
+    out->max_cu_bytes = std::max(out->max_cu_bytes, bytes);
+    out->min_cu_bytes = std::min(out->min_cu_bytes, bytes);
+    out->weight_bytes += bytes;
+  }
+  return MK_OK;
+}
+
+mk_status mk_graph_simulate(const mk_config* cfg, int32_t ncu, uint64_t seed, int32_t workers, int32_t drop_event,
+                            mk_sim_result* out) {
+  g_err.clear();
+  const std::string cerr = check_config(cfg);
+  if (!cerr.empty()) return fail(MK_ERR_INVALID_ARG, cerr);
+  if (ncu < 1 || !out || workers < 1 || workers > kWorkers) return fail(MK_ERR_INVALID_ARG, "bad ncu/workers/out");
+  Graph g;
+  std::string e = build_graph(graph_config(cfg, ncu), g);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
+  SimResult r = simulate_graph(g, seed, workers, drop_event);
+  out->completed = r.completed ? 1 : 0;
+  out->executed = r.executed;
+  out->blocked_event = r.blocked_event;
+  out->race = r.error.empty() ? 0 : 1;
+  if (!r.error.empty()) g_err = r.error;
+  return MK_OK;
+}
+
+mk_status mk_graph_export(const mk_config* cfg, int32_t ncu, void* out, int32_t* cu, int32_t cap, int32_t* n) {
+  g_err.clear();
+  const std::string cerr = check_config(cfg);
+  if (!cerr.empty()) return fail(MK_ERR_INVALID_ARG, cerr);
+  if (ncu < 1 || !n) return fail(MK_ERR_INVALID_ARG, "ncu < 1 or n NULL");
+  Graph g;
+  std::string e = build_graph(graph_config(cfg, ncu), g);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
+  *n = (int32_t)g.tasks.size();
+  if ((out || cu) && cap < *n) return fail(MK_ERR_CAPACITY, "capacity too small");
+  if (out) std::memcpy(out, g.tasks.data(), g.tasks.size() * sizeof(Task));
+  if (cu) std::memcpy(cu, g.cu_of.data(), g.cu_of.size() * 4);
+  return MK_OK;
+}
+
+mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out) {
+  if (!h || !out) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  out->xs = h->P.xs;
+  out->xmid = h->P.xmid;
+  out->q = h->P.q;
+  out->attn_out = h->P.attn_out;
+  out->h = h->P.h;
+  out->events = h->P.events;
+  out->n_events = (int32_t)h->graph.event_count.size();
+  out->n_tasks = (int32_t)h->graph.tasks.size();
+  out->ncu = h->P.ncu;
+  out->nsplit = h->P.nsplit;
+  out->split = h->P.split;
+  out->lds_bytes = h->lds_mega;
+  return MK_OK;
+}
+
+mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, double* ticks_per_us) {
+  if (!h || !n) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  if (!h->P.trace) return fail(MK_ERR_STATE, "handle created without MK_FLAG_TRACE");
+  *n = h->P.trace_cap;
+  if (ticks_per_us) *ticks_per_us = h->ticks_per_us;
+  if (!out) return MK_OK;
+  if (cap < h->P.trace_cap) return fail(MK_ERR_CAPACITY, "capacity too small");
+  HIP_TRY(hipStreamSynchronize(h->stream));
+  HIP_TRY(hipMemcpy(out, h->P.trace, 16 * (size_t)h->P.trace_cap, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+// ---- single bodies -----------------------------------------------------------
+
+mk_status mk_t_gemv(const void* W, const float* x, float* y, int32_t N, int32_t K, void* stream) {
+  g_err.clear();
+  if (!W || !x || !y || N < 1 || K < 8 || K % 8) return fail(MK_ERR_INVALID_ARG, "bad gemv arguments");
+  int max_lds = 0;
+  MK_TRY(device_facts(nullptr, nullptr, &max_lds));
+  const int lds = K * 4;
+  if (lds > max_lds) return fail(MK_ERR_UNSUPPORTED, "K too large for LDS staging");
+  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_t_gemv_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  const int grid = std::min((N + kWaves * kRows - 1) / (kWaves * kRows), 1024);
+  hipLaunchKernelGGL(mk_t_gemv_kernel, dim3(grid), dim3(kWaves * kWave), (unsigned)lds,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W), x, y, N, K);
+  HIP_TRY(hipGetLastError());
+  return MK_OK;
+}
+
+mk_status mk_t_rmsnorm(const float* x, const void* gamma, float eps, float* y, int32_t n, void* stream) {
+  g_err.clear();
+  if (!x || !gamma || !y || n < 8 || n % 8) return fail(MK_ERR_INVALID_ARG, "bad rmsnorm arguments");
+  int max_lds = 0;
+  MK_TRY(device_facts(nullptr, nullptr, &max_lds));
+  if (n * 4 > max_lds) return fail(MK_ERR_UNSUPPORTED, "n too large");
+  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_t_rmsnorm_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, n * 4));
+  hipLaunchKernelGGL(mk_t_rmsnorm_kernel, dim3(1), dim3(256), (unsigned)(n * 4), static_cast<hipStream_t>(stream), x,
+                     static_cast<const uint16_t*>(gamma), eps, y, n);
+  HIP_TRY(hipGetLastError());
+  return MK_OK;
+}
+
+mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t head_stride, int32_t nq, int32_t nkv,
+                         int32_t hd, int32_t T, int32_t split, float* o, void* stream) {
+  g_err.clear();
+  if (!q || !k || !v || !o || nq < 1 || nkv < 1 || nq % nkv || nq / nkv > kMaxGqa || (hd != 64 && hd != 128) ||
+      T < 1 || split < 1 || split > kMaxSplit || head_stride < (int64_t)T * hd)
+    return fail(MK_ERR_INVALID_ARG, "bad attention arguments");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int G = nq / nkv, nsplit = (T + split - 1) / split;
+  float* part = nullptr;
+  HIP_TRY(hipMalloc(&part, (size_t)nkv * nsplit * G * (hd + 2) * 4));
+  const unsigned lds = (unsigned)((G * hd + G * kWave) * 4);
+  hipLaunchKernelGGL(mk_t_attn_partial_kernel, dim3(nkv * nsplit), dim3(kWave), lds, st, q,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), head_stride, nq, nkv, hd, T,
+                     split, nsplit, part);
+  hipLaunchKernelGGL(mk_t_attn_merge_kernel, dim3(nkv), dim3(kWave), 0, st, part, nq, nkv, hd, T, split, nsplit, o);
+  hipError_t e = hipStreamSynchronize(st);
+  (void)hipFree(part);
+  if (e != hipSuccess) return fail(MK_ERR_HIP, std::string("attention: ") + hipGetErrorString(e));
+  return MK_OK;
+}
+
+mk_status mk_t_argmax(const float* x, int32_t n, int32_t* out, void* stream) {
+  g_err.clear();
+  if (!x || !out || n < 1) return fail(MK_ERR_INVALID_ARG, "bad argmax arguments");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned long long* slot = nullptr;
+  HIP_TRY(hipMalloc(&slot, 8));
+  HIP_TRY(hipMemsetAsync(slot, 0, 8, st));
+  const int grid = std::min((n + 255) / 256, 256);
+  hipLaunchKernelGGL(mk_t_argmax_kernel, dim3(grid), dim3(256), 0, st, x, n, slot);
+  hipLaunchKernelGGL(mk_t_argmax_final, dim3(1), dim3(64), 0, st, slot, out);
+  hipError_t e = hipStreamSynchronize(st);
+  (void)hipFree(slot);
+  if (e != hipSuccess) return fail(MK_ERR_HIP, std::string("argmax: ") + hipGetErrorString(e));
+  return MK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,310 @@
+// Device helpers and task bodies shared by the persistent runtime, the
+// kernel-per-operator baseline and the single-body test kernels.
+//
+// Bodies are written for one 64-lane wavefront each: a worker wave owns a task
+// from start to end, so no workgroup barrier is ever taken inside a task.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_internal.h"
+
+namespace mk {
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bf16 is the upper half of an fp32 bit pattern)
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float bf1(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even (finite inputs)
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions with DPP inside each 16-lane row, then the four row
+// results combined through readlane (uniform result in every lane).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float rd_lane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  return (rd_lane(v, 0) + rd_lane(v, 16)) + (rd_lane(v, 32) + rd_lane(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(rd_lane(v, 0), rd_lane(v, 16)), fmaxf(rd_lane(v, 32), rd_lane(v, 48)));
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    unsigned long long w = __shfl_xor(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Argmax key: larger key = larger value, ties -> smaller index.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ float argmax_key_value(unsigned long long k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------------------
+// Memory ordering (HIP scoped atomics; the compiler emits the gfx950 cache
+// maintenance for each scope).
+__device__ __forceinline__ uint32_t ld_relaxed_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void fence_acq_rel_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent"); }
+__device__ __forceinline__ void fence_release_wg() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup"); }
+__device__ __forceinline__ void fence_acquire_wg() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
+__device__ __forceinline__ uint32_t lds_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ uint32_t lds_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ uint64_t clock_now() { return __builtin_amdgcn_s_memrealtime(); }
+
+// ---------------------------------------------------------------------------
+// GEMV core: kRows weight rows (bf16, each K contiguous elements) dotted with
+// one fp32 vector held in LDS.  Each lane owns 8 consecutive columns of every
+// 512-column chunk, so one wave load instruction reads 1 KiB of a row.  kDepth
+// chunks per row stay in flight; `prefetch` issues them (weights do not depend
+// on any event, so this runs before the task's dependency is satisfied) and
+// `run` consumes them, refilling each slot with the chunk kDepth ahead.
+constexpr int kDepth = 8;
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+struct GemvRows {
+  const v4u* row[kRows];
+  uint32_t mask;  // bit r set: row r valid
+  int nvec;       // K / 8 (16-byte vectors per row)
+};
+
+__device__ __forceinline__ v4u ld_w(const v4u* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ void gemv_prefetch(v4u (&buf)[kDepth][kRows], const GemvRows& g, int lane) {
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s) {
+    const int v = s * kWave + lane;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+      buf[s][r] = ((g.mask >> r) & 1) && v < g.nvec ? ld_w(g.row[r] + v) : v4u{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ float dot8(v4u w, const float4& a, const float4& b, float acc) {
+  acc = fmaf(bf_lo(w.x), a.x, acc);
+  acc = fmaf(bf_hi(w.x), a.y, acc);
+  acc = fmaf(bf_lo(w.y), a.z, acc);
+  acc = fmaf(bf_hi(w.y), a.w, acc);
+  acc = fmaf(bf_lo(w.z), b.x, acc);
+  acc = fmaf(bf_hi(w.z), b.y, acc);
+  acc = fmaf(bf_lo(w.w), b.z, acc);
+  acc = fmaf(bf_hi(w.w), b.w, acc);
+  return acc;
+}
+
+// Returns the kRows dot products (uniform across the wave).
+__device__ __forceinline__ void gemv_run(v4u (&buf)[kDepth][kRows], const GemvRows& g, const float* xs, int lane,
+                                         float (&y)[kRows]) {
+  float acc[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
+  const int nchunks = (g.nvec + kWave - 1) / kWave;
+  for (int c0 = 0; c0 < nchunks; c0 += kDepth) {
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) {
+      const int c = c0 + s;
+      if (c < nchunks) {
+        const int v = c * kWave + lane;
+        float4 xa = make_float4(0.f, 0.f, 0.f, 0.f), xb = xa;
+        if (v < g.nvec) {
+          xa = *reinterpret_cast<const float4*>(xs + v * 8);
+          xb = *reinterpret_cast<const float4*>(xs + v * 8 + 4);
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) acc[r] = dot8(buf[s][r], xa, xb, acc[r]);
+        const int vn = (c + kDepth) * kWave + lane;
+        if (c + kDepth < nchunks) {
+#pragma unroll
+          for (int r = 0; r < kRows; ++r)
+            buf[s][r] = ((g.mask >> r) & 1) && vn < g.nvec ? ld_w(g.row[r] + vn) : v4u{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) y[r] = wave_sum(acc[r]);
+}
+
+// ---------------------------------------------------------------------------
+// Staging: one wave loads an activation vector into an LDS page, applying
+// RMSNorm (x * (mean(x^2) + eps)^-1/2 * gamma) when a gain is given.
+__device__ __forceinline__ void stage_vector(float* page, const float* src, const uint16_t* src_bf16, int n,
+                                             const uint16_t* gamma, float eps, int lane) {
+  float ss = 0.f;
+  for (int i = lane * 8; i < n; i += kWave * 8) {
+    float v[8];
+    if (src_bf16) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src_bf16 + i);
+      v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+      v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(src + i);
+      const float4 b = *reinterpret_cast<const float4*>(src + i + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
+    *reinterpret_cast<float4*>(page + i) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(page + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  if (gamma) {
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)n + eps);
+    for (int i = lane * 8; i < n; i += kWave * 8) {
+      const uint4 gu = *reinterpret_cast<const uint4*>(gamma + i);
+      float4 a = *reinterpret_cast<float4*>(page + i);
+      float4 b = *reinterpret_cast<float4*>(page + i + 4);
+      a.x = a.x * inv * bf_lo(gu.x); a.y = a.y * inv * bf_hi(gu.x);
+      a.z = a.z * inv * bf_lo(gu.y); a.w = a.w * inv * bf_hi(gu.y);
+      b.x = b.x * inv * bf_lo(gu.z); b.y = b.y * inv * bf_hi(gu.z);
+      b.z = b.z * inv * bf_lo(gu.w); b.w = b.w * inv * bf_hi(gu.w);
+      *reinterpret_cast<float4*>(page + i) = a;
+      *reinterpret_cast<float4*>(page + i + 4) = b;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV decode attention partial for one KV group: positions [p0, p1)
+// (at most 64, one per lane for the scores), G query heads of head_dim HD.
+// Writes o (unnormalised, HD floats), then m (max score) and l (sum of
+// exp(score - m)) per head into out[G][HD + 2].  scratch: LDS, G*HD + G*64 floats.
+template <int HD>
+__device__ void attn_partial(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t pos_stride, int p0,
+                             int p1, int G, float* out, float* scratch, int lane) {
+  constexpr int DPL = HD / kWave;  // dims per lane for the value accumulation (1 or 2)
+  float* qs = scratch;              // [G][HD]
+  float* pr = scratch + G * HD;     // [G][64]
+  for (int i = lane; i < G * HD; i += kWave) qs[i] = q[i];
+  __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
+  const int np = p1 - p0;
+  const float scale = 1.0f / sqrtf((float)HD);
+  float sc[kMaxGqa];
+#pragma unroll
+  for (int h = 0; h < kMaxGqa; ++h) sc[h] = 0.f;
+  if (lane < np) {
+    const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)(p0 + lane) * pos_stride);
+#pragma unroll 4
+    for (int d8 = 0; d8 < HD / 8; ++d8) {
+      const v4u k8 = krow[d8];
+#pragma unroll
+      for (int h = 0; h < kMaxGqa; ++h) {
+        if (h < G) {
+          const float4 a = *reinterpret_cast<const float4*>(qs + h * HD + d8 * 8);
+          const float4 b = *reinterpret_cast<const float4*>(qs + h * HD + d8 * 8 + 4);
+          sc[h] = dot8(k8, a, b, sc[h]);
+        }
+      }
+    }
+  }
+  float m[kMaxGqa], l[kMaxGqa];
+#pragma unroll
+  for (int h = 0; h < kMaxGqa; ++h) {
+    if (h < G) {
+      const float s = lane < np ? sc[h] * scale : -INFINITY;
+      m[h] = wave_max(s);
+      const float p = lane < np ? __expf(s - m[h]) : 0.f;
+      l[h] = wave_sum(p);
+      pr[h * kWave + lane] = p;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  float o[kMaxGqa][DPL];
+#pragma unroll
+  for (int h = 0; h < kMaxGqa; ++h)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
+  for (int j = 0; j < np; ++j) {
+    const uint16_t* vrow = vc + (int64_t)(p0 + j) * pos_stride + lane * DPL;
+    float vv[DPL];
+    if (DPL == 2) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(vrow);
+      vv[0] = bf_lo(u);
+      vv[DPL - 1] = bf_hi(u);
+    } else {
+      vv[0] = bf1(vrow[0]);
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxGqa; ++h) {
+      if (h < G) {
+        const float p = pr[h * kWave + j];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxGqa; ++h) {
+    if (h < G) {
+      float* oh = out + h * (HD + 2);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) oh[lane * DPL + e] = o[h][e];
+      if (lane == 0) { oh[HD] = m[h]; oh[HD + 1] = l[h]; }
+    }
+  }
+}
+
+// Log-sum-exp merge of nsplit partials laid out [nsplit][G][HD + 2]; writes
+// the normalised outputs of the G heads to out[G][HD].
+template <int HD>
+__device__ void attn_merge(const float* part, int nsplit, int G, float* out, int lane) {
+  constexpr int DPL = HD / kWave;
+  for (int h = 0; h < G; ++h) {
+    float M = -INFINITY, Lsum = 0.f, o[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float* ps = part + ((int64_t)s * G + h) * (HD + 2);
+      const float ms = ps[HD], ls = ps[HD + 1];
+      const float Mn = fmaxf(M, ms);
+      const float a = __expf(M - Mn), b = __expf(ms - Mn);
+      Lsum = Lsum * a + ls * b;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + ps[lane * DPL + e] * b;
+      M = Mn;
+    }
+    const float inv = 1.0f / Lsum;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) out[h * HD + lane * DPL + e] = o[e] * inv;
+  }
+}
+
+__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+
+}  // namespace mk

@@ -1,0 +1,65 @@
+// Host-side task-graph (tGraph) builder, validator and CPU simulator.
+//
+// The builder follows the compiler half of MPK ("Compilar LLM en un
+// MegaKernel ...", section "Parte 1. Compilador"; "MPK: A Compiler and Runtime
+// for Mega-Kernelizing Tensor Programs", section 2 "La Carte au Niveau SM"):
+// every operator of the decode step is cut into tasks small enough for one
+// wavefront, tasks are placed on per-CU queues, and producers are wired to
+// consumers through counting events.  Because a decode step's graph is fully
+// known before launch, all placement is ahead of time (the AOT case of the MPK
+// explainer's section 3).
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "mk_internal.h"
+
+namespace mk {
+
+struct GraphConfig {
+  int L, H, nq, nkv, hd, F, V, B, max_seq, split, ncu;
+};
+
+struct Graph {
+  GraphConfig cfg;
+  int nsplit = 0;
+  std::vector<Task> tasks;                 // by global id (topological order)
+  std::vector<int> stage_of;               // stage index of each task
+  std::vector<int> cu_of;                  // CU of each task
+  std::vector<std::vector<int>> queues;    // per CU: task ids in execution order
+  std::vector<uint32_t> event_count;       // signals per step of each event
+  std::vector<int> stage_begin;            // tasks [stage_begin[s], stage_begin[s+1]) form stage s
+  std::vector<uint8_t> stage_type;
+  // device tables
+  std::vector<Task> flat;                  // queue order, CU-major
+  std::vector<int32_t> queue_off;          // [ncu + 1]
+};
+
+// Positions per split-KV attention task for a given max context.
+int auto_split(int max_seq);
+
+// Build the decode-step graph.  Returns "" on success, else a message.
+std::string build_graph(const GraphConfig& cfg, Graph& g);
+
+// Static checks: every task once; queues in topological order; event counts
+// equal the number of signals; every output element written exactly once per
+// step; every element a task (or its staged input) reads is written by a task
+// the reader transitively waits for; RoPE pairs inside one task.
+std::string validate_graph(const Graph& g);
+
+struct SimResult {
+  bool completed = false;
+  int blocked_event = -1;   // an event some blocked task waits on
+  int executed = 0;
+  std::string error;        // race or protocol error, "" if none
+};
+
+// Run the per-CU queues under the runtime's protocol (scheduler frontier,
+// worker tickets, staged pages, aggregated signals, event thresholds) in a
+// random interleaving.  `drop_event` >= 0 suppresses one signal of that event
+// (fault injection: the run must then report a deadlock on it).
+SimResult simulate_graph(const Graph& g, uint64_t seed, int workers, int drop_event);
+
+}  // namespace mk

@@ -1,0 +1,138 @@
+// Internal structures shared by the host task-graph builder and the device
+// runtime.  Not part of the public ABI.
+//
+// The task graph follows the MPK description ("Compilar LLM en un MegaKernel
+// ...", section "Parte 1. Compilador"): each operator is cut into tasks that
+// each run on one compute unit, and tasks are wired through events; a task
+// signals its output event when done, and an event is "fired" once its counter
+// reaches a threshold (section "Parte 2. Runtime", event-driven execution).
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 8;             // waves per workgroup (1 scheduler + workers)
+constexpr int kWorkers = kWaves - 1;  // worker waves per CU in the persistent kernel
+constexpr int kRows = 4;              // weight rows streamed together by one GEMV task
+constexpr int kMaxGqa = 8;            // query heads per KV head supported
+constexpr int kMaxSplit = 64;         // positions per split-KV attention task (one per lane)
+constexpr int kLocalSlots = 64;       // per-CU LDS counters for aggregated event signals
+constexpr int kMaxBatch = 64;         // sequences per step
+constexpr uint16_t kNone16 = 0xFFFF;
+constexpr uint8_t kNone8 = 0xFF;
+
+// Task types.
+enum TaskType : uint8_t {
+  TT_QKV = 1,     // rows of Wq/Wk/Wv on norm(x); epilogue RoPE, q -> scratch, k/v -> cache
+  TT_ATTN = 2,    // split-KV partial (m, l, o) for one (batch row, KV group, split)
+  TT_MERGE = 3,   // log-sum-exp merge of the splits of one (batch row, KV group)
+  TT_O = 4,       // rows of Wo on attention output; epilogue residual add
+  TT_GU = 5,      // rows of W_gate and W_up on norm(xmid); epilogue SwiGLU
+  TT_DOWN = 6,    // rows of W_down on h; epilogue residual add
+  TT_LM = 7,      // rows of the LM head on norm(x_L); epilogue logits + argmax partial
+  TT_ARGMAX = 8   // reduce the argmax partials -> next token
+};
+
+// Staged-input kinds (what the LDS activation page holds).
+enum StageKind : uint16_t {
+  SK_NONE = 0,
+  SK_ATTN_NORM = 1,  // rmsnorm(x_l) * gamma_attn[l]   (x_0 = embedding row)
+  SK_O_IN = 2,       // attention output of layer l
+  SK_FFN_NORM = 3,   // rmsnorm(xmid_l) * gamma_ffn[l]
+  SK_H = 4,          // SwiGLU output of layer l
+  SK_FINAL_NORM = 5  // rmsnorm(x_L) * gamma_final
+};
+inline constexpr uint16_t stage_key(int kind, int layer) { return (uint16_t)((kind << 12) | (layer + 1)); }
+inline constexpr int stage_kind(uint16_t key) { return key >> 12; }
+inline constexpr int stage_layer(uint16_t key) { return (key & 0xFFF) - 1; }
+
+// One task.  Interpretation of a0..a3 by type:
+//   QKV   a0 = matrix (0 q, 1 k, 2 v), a1 = first row, a2 = rows, a3 = RoPE pair offset (0 = none)
+//          rows are {a1 + i} for i < a2 when a3 == 0, else {a1 + i, a1 + a3 + i} for i < a2/2
+//   ATTN  a0 = KV group, a1 = split index
+//   MERGE a0 = KV group
+//   O, DOWN, LM  a1 = first row, a2 = rows (<= kRows)
+//   GU    a1 = first row, a2 = rows per matrix (<= kRows/2)
+struct alignas(16) Task {
+  uint8_t type;
+  uint8_t page;          // LDS page of the staged input, kNone8 if none
+  uint16_t layer;
+  uint16_t in_event;     // event waited on, kNone16 if none
+  uint16_t out_event;    // event signalled, kNone16 if none
+  uint32_t in_count;     // signals on in_event per step (threshold = in_count * epoch)
+  uint16_t stage;        // stage_key of the staged input, 0 if none
+  uint16_t batch;        // batch row
+  uint16_t local_slot;   // per-CU LDS counter used to aggregate out_event
+  uint16_t local_count;  // tasks of this CU that signal out_event in one step
+  uint32_t id;           // global task id (topological order)
+  int32_t a0, a1, a2, a3;
+};
+static_assert(sizeof(Task) == 48, "Task layout");
+
+// Device-visible description of a handle: shapes, weights, buffers, tables.
+struct Params {
+  // shape
+  int32_t L, H, nq, nkv, hd, F, V, B, max_seq, split, nsplit, tied;
+  float eps;
+  int32_t ncu;          // persistent grid
+  uint32_t timeout_ticks;
+  // weights (bf16)
+  const uint16_t* embed;
+  const uint16_t* lm_head;
+  const uint16_t* final_norm;
+  const uint16_t* const* attn_norm;
+  const uint16_t* const* wq;
+  const uint16_t* const* wk;
+  const uint16_t* const* wv;
+  const uint16_t* const* wo;
+  const uint16_t* const* ffn_norm;
+  const uint16_t* const* w_gate;
+  const uint16_t* const* w_up;
+  const uint16_t* const* w_down;
+  // KV cache bf16 [L][B][nkv][max_seq][hd]
+  uint16_t* kcache;
+  uint16_t* vcache;
+  // fp32 activations (one buffer per layer, each written once per step)
+  float* xs;         // [L+1][B][H]   x_{l+1} = output of layer l (x_0 unused: embedding row)
+  float* xmid;       // [L][B][H]
+  float* q;          // [L][B][nq*hd] (rotated)
+  float* attn_part;  // [L][B][nkv][nsplit][G][hd + 2]  (o[hd], m, l)
+  float* attn_out;   // [L][B][nq*hd]
+  float* h;          // [L][B][F]
+  unsigned long long* lm_part;  // [B] running argmax key (ordered value, ~index), cleared by the argmax task
+  const float* rope_cos;  // [max_seq][hd/2]
+  const float* rope_sin;
+  // task tables
+  const Task* tasks;        // persistent: grouped by CU queue
+  const int32_t* queue_off; // [ncu + 1]
+  uint32_t* events;
+  uint32_t* status;         // [8]: 0 abort flag, 1 error code, 2 cu, 3 task id, 4 event, 5 value, 6 need
+  unsigned long long* trace;  // optional per-task timestamps
+  int32_t trace_cap;
+};
+
+// Per-launch arguments.
+struct Step {
+  uint32_t epoch;    // 1 for the first step after create/reset, +1 per launch
+  int32_t pos;       // position written by this step (attention covers 0..pos)
+  const int32_t* tokens;  // token of batch row b at tokens[b * tok_stride]
+  int32_t tok_stride;
+  int32_t* out;      // [B] greedy ids
+  float* logits;     // [B][V] or null
+};
+
+// LDS header of the persistent and per-operator kernels (followed by the
+// activation pages and the per-wave attention scratch).
+struct Lds {
+  uint32_t frontier, ticket, abort, pad0;
+  uint32_t page_done[2];
+  uint32_t pad1[2];
+  uint32_t slot[kLocalSlots];
+  unsigned long long lm_best[kMaxBatch];
+};
+
+// Status codes latched by the kernel.
+enum : uint32_t { ST_OK = 0, ST_TIMEOUT = 1, ST_NONFINITE = 2, ST_BADTOKEN = 3 };
+
+}  // namespace mk

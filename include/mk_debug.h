@@ -1,0 +1,93 @@
+/* mk_debug.h -- inspection and single-body entry points of libmk (tests,
+ * profiling).  Same conventions as mk.h: device pointers are HIP device
+ * memory, errors are reported through mk_status + mk_last_error().
+ */
+#ifndef MK_DEBUG_H
+#define MK_DEBUG_H
+
+#include "mk.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- task graph (host only; no GPU needed) ------------------------------
+ * The graph cuts every operator of one decode step into wavefront-sized tasks
+ * placed on per-CU queues and wired by counting events ("Compilar LLM en un
+ * MegaKernel ...", section "Parte 1. Compilador"). */
+typedef struct {
+  int32_t n_tasks, n_events, n_stages, ncu, nsplit, split;
+  int32_t max_queue, min_queue;        /* tasks per CU */
+  int64_t max_cu_bytes, min_cu_bytes;  /* weight bytes streamed per CU per step */
+  int64_t weight_bytes;                /* all weight bytes of one step */
+} mk_graph_info;
+
+/* Build the graph for `cfg` on `ncu` CUs and run the static validator
+ * (coverage, topological queues, thresholds, read-after-write covered by
+ * waits, RoPE pairs whole).  MK_ERR_INVALID_ARG with the validator's message
+ * on failure. */
+mk_status mk_graph_inspect(const mk_config* cfg, int32_t ncu, mk_graph_info* out);
+
+typedef struct {
+  int32_t completed;     /* 1 if every task ran */
+  int32_t executed;      /* tasks run before completion or deadlock */
+  int32_t blocked_event; /* on deadlock: an event a blocked task waits on, else -1 */
+  int32_t race;          /* 1 if a task or staging read incomplete data */
+} mk_sim_result;
+
+/* Execute the graph's queues on the CPU under the runtime protocol in a random
+ * interleaving (seeded).  drop_event >= 0 suppresses one signal of that event
+ * (fault injection). `workers` = worker waves per CU (1..kWaves-1). */
+mk_status mk_graph_simulate(const mk_config* cfg, int32_t ncu, uint64_t seed, int32_t workers, int32_t drop_event,
+                            mk_sim_result* out);
+
+/* Copy the graph's tasks in global order into `out` (48 bytes per task,
+ * layout of the internal Task struct) and the CU of each task into `cu`.
+ * Either may be NULL; `cap` is the capacity in tasks. Returns the count in *n. */
+mk_status mk_graph_export(const mk_config* cfg, int32_t ncu, void* out, int32_t* cu, int32_t cap, int32_t* n);
+
+/* ---- internal buffers of a handle (device pointers, fp32) ------------------ */
+typedef struct {
+  float* xs;        /* [L+1][B][H]: xs[l+1] = residual stream after layer l */
+  float* xmid;      /* [L][B][H]:   residual after attention of layer l */
+  float* q;         /* [L][B][nq*hd]: rotated queries */
+  float* attn_out;  /* [L][B][nq*hd]: attention output before O-proj */
+  float* h;         /* [L][B][F]: SwiGLU output */
+  uint32_t* events; /* event counters */
+  int32_t n_events, n_tasks, ncu, nsplit, split;
+  int32_t lds_bytes; /* dynamic LDS of the persistent kernel */
+} mk_debug_view;
+mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out);
+
+/* Kernel status words (synchronous): [0] abort flag, [1] error code (0 ok,
+ * 1 timeout, 2 non-finite logits, 3 token id out of range), [2] CU, [3] task id, [4] event, [5] counter
+ * value, [6] threshold. */
+mk_status mk_read_status(mk_handle* h, uint32_t out[8]);
+
+/* Per-task timestamps of the last megakernel step when created with
+ * MK_FLAG_TRACE: out[2*i] = (cu << 48) | start, out[2*i+1] = end, in ticks of
+ * the device wall clock (`ticks_per_us` returned). Synchronous. */
+mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, double* ticks_per_us);
+
+/* ---- single task bodies on explicit buffers (asynchronous on `stream`) ----- */
+/* y[N] = W[N,K] x[K]; W bf16 row-major, x/y fp32; K a multiple of 8. */
+mk_status mk_t_gemv(const void* W, const float* x, float* y, int32_t N, int32_t K, void* stream);
+/* y = x * (mean(x^2) + eps)^-1/2 * gamma; gamma bf16; n a multiple of 8. */
+mk_status mk_t_rmsnorm(const float* x, const void* gamma, float eps, float* y, int32_t n, void* stream);
+/* Decode attention of one sequence: q fp32 [nq, hd]; k, v bf16 with head g at
+ * k + g*head_stride, position p at + p*hd; T positions; split-KV partials of
+ * `split` positions merged by log-sum-exp; o fp32 [nq, hd].  Synchronous
+ * (allocates and frees its partial buffer). */
+mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t head_stride, int32_t nq, int32_t nkv,
+                         int32_t hd, int32_t T, int32_t split, float* o, void* stream);
+/* out[0] = lowest index of the maximum of x[n] (fp32).  Synchronous. */
+mk_status mk_t_argmax(const float* x, int32_t n, int32_t* out, void* stream);
+
+/* Device facts used by the runtime: compute units, wall-clock ticks per us,
+ * max dynamic LDS per workgroup. */
+mk_status mk_device_info(int32_t* ncu, double* ticks_per_us, int32_t* max_lds);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_DEBUG_H */

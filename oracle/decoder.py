@@ -84,9 +84,14 @@ def silu(u: np.ndarray) -> np.ndarray:
     return u / (1.0 + np.exp(-u))
 
 
+def swiglu(r, w_gate, w_up) -> np.ndarray:
+    """silu(r W_g^T) * (r W_u^T) (reading R-ffn); weights [out, in]."""
+    return silu(r @ w_gate.T) * (r @ w_up.T)
+
+
 def swiglu_ffn(r, w_gate, w_up, w_down) -> np.ndarray:
-    """down(silu(r W_g^T) * (r W_u^T)) (reading R-ffn); weights [out, in]."""
-    return (silu(r @ w_gate.T) * (r @ w_up.T)) @ w_down.T
+    """down(silu(r W_g^T) * (r W_u^T)) (reading R-ffn)."""
+    return swiglu(r, w_gate, w_up) @ w_down.T
 
 
 def greedy(logits: np.ndarray) -> np.ndarray:
@@ -135,8 +140,14 @@ class Decoder:
         r = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
         return (((u + r) >> np.uint32(16)) << np.uint32(16)).view(np.float32).astype(np.float64)
 
-    def step(self, tokens) -> np.ndarray:
-        """One decode step at position `length` for every sequence; returns logits [B, V]."""
+    def step(self, tokens, trace: dict = None) -> np.ndarray:
+        """One decode step at position `length` for every sequence; returns logits [B, V].
+
+        If `trace` is a dict, the per-layer intermediates are stored in it:
+        ("q", l) rotated queries [B, nq*hd], ("attn", l) attention output,
+        ("xmid", l) residual after attention, ("h", l) SwiGLU output, ("x", l+1)
+        residual after layer l.
+        """
         sh = self.shape
         tokens = np.asarray(tokens, dtype=np.int64).reshape(self.B)
         p = self.length
@@ -159,7 +170,15 @@ class Decoder:
                           for b in range(self.B)])
             x = x + o.reshape(self.B, nq * hd) @ self.W(pre + "wo").T
             r = rmsnorm(x, self.W(pre + "ffn_norm")[0], sh.rms_eps)
-            x = x + swiglu_ffn(r, self.W(pre + "w_gate"), self.W(pre + "w_up"), self.W(pre + "w_down"))
+            hh = swiglu(r, self.W(pre + "w_gate"), self.W(pre + "w_up"))
+            if trace is not None:
+                trace[("q", l)] = q.reshape(self.B, nq * hd)
+                trace[("attn", l)] = o.reshape(self.B, nq * hd)
+                trace[("xmid", l)] = x
+                trace[("h", l)] = hh
+            x = x + hh @ self.W(pre + "w_down").T
+            if trace is not None:
+                trace[("x", l + 1)] = x
         r = rmsnorm(x, self.W("final_norm")[0], sh.rms_eps)
         logits = r @ self.W(self._lm_head()).T
         self.length = p + 1

@@ -4,3 +4,9 @@ from synth.presets import ModelShape
 MICRO = ModelShape("micro", 2, 64, 4, 2, 16, 96, 128, 1e-5, 10000.0, False)
 MICRO_TIED = ModelShape("micro_tied", 2, 64, 4, 2, 16, 96, 128, 1e-5, 10000.0, True)
 MICRO_MHA = ModelShape("micro_mha", 1, 64, 4, 4, 16, 96, 128, 1e-5, 10000.0, False)
+
+# Shapes the GPU library accepts (head_dim 64/128), with ragged tails:
+# ffn and vocab are not multiples of the 512-column chunk / 4-row task.
+MINI = ModelShape("mini", 2, 128, 4, 2, 64, 264, 322, 1e-5, 10000.0, False)
+MINI_TIED = ModelShape("mini_tied", 2, 128, 4, 2, 64, 264, 322, 1e-5, 10000.0, True)
+MINI_G8 = ModelShape("mini_g8", 1, 256, 8, 1, 128, 520, 258, 1e-5, 500000.0, False)

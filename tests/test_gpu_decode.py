@@ -1,0 +1,168 @@
+"""End-to-end decode on the GPU (both execution modes) against the oracle.
+
+Bars ("Parity"):
+  * logits: max|gpu - oracle| / max|oracle| <= 2e-2 per step against the fp64
+    oracle, and <= 1e-3 against the oracle with a bf16-rounded KV cache (the
+    remaining error is fp32 accumulation order only);
+  * tokens: the GPU's greedy token equals the oracle's wherever the oracle's
+    top-2 margin exceeds 5e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decoder as D
+from synth import gen, presets
+from tests.gpu_util import Case, debug_arrays, rel_err
+from tests.shapes import MINI, MINI_TIED, MINI_G8
+
+pytestmark = pytest.mark.gpu
+
+CONTRACT = 2e-2
+TIGHT = 1e-3
+MARGIN = 5e-2
+
+
+@pytest.fixture(scope="module")
+def abi():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_persistent_megakernel_02_amd import abi as a
+    return a
+
+
+MODES = {"megakernel": 0, "per_op": 1}
+
+
+def check_step(g, r, nxt, errs, bar):
+    e = float(rel_err(g, r))
+    errs.append(e)
+    assert e <= bar, f"logit error {e:.3e} > {bar}"
+    if D.top2_margin(r) > MARGIN:
+        assert nxt == int(D.greedy(r)), "greedy token differs at a clear margin"
+
+
+def teacher_forced(case, prompt, steps, bar):
+    errs = []
+    g, r, nxt = case.prefill(prompt)
+    check_step(g, r, nxt, errs, bar)
+    tok = int(D.greedy(r))
+    for _ in range(steps):
+        g, r, nxt = case.step(tok)
+        check_step(g, r, nxt, errs, bar)
+        tok = int(D.greedy(r))
+    return errs
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_workload_teacher_forced(abi, mode):
+    wl = presets.WORKLOADS["tiny"]
+    prompt = gen.gen_prompt(wl)[0]
+    case = Case(wl.shape, wl.max_seq, MODES[mode])
+    errs = teacher_forced(case, prompt, wl.decode_steps, CONTRACT)
+    print(f"tiny {mode}: max rel err {max(errs):.2e}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_tight_against_bf16_kv_oracle(abi, mode):
+    wl = presets.WORKLOADS["tiny"]
+    case = Case(wl.shape, wl.max_seq, MODES[mode], kv_bf16_oracle=True)
+    teacher_forced(case, gen.gen_prompt(wl)[0], wl.decode_steps, TIGHT)
+
+
+@pytest.mark.parametrize("shape", [MINI, MINI_TIED, MINI_G8], ids=lambda s: s.name)
+@pytest.mark.parametrize("mode", MODES)
+def test_ragged_shapes_multi_split(abi, shape, mode):
+    # 16-position attention splits, prompt 21 + 14 steps: positions span 3 splits
+    case = Case(shape, 40, MODES[mode], seed=5, random_norms=True, attn_split=16, kv_bf16_oracle=True)
+    prompt = gen.tokens(9, 3, 0, 21, shape.vocab)
+    teacher_forced(case, prompt, 14, TIGHT)
+
+
+def test_free_running_matches_until_low_margin(abi):
+    wl = presets.WORKLOADS["tiny"]
+    shape = wl.shape
+    w = gen.gen_weights(shape, 0)
+    from decode_persistent_megakernel_02_amd import runtime
+    dw = runtime.upload_weights(w)
+    h = runtime.create(shape, dw, wl.max_seq)
+    prompt = gen.gen_prompt(wl)
+    toks = torch.zeros(wl.decode_steps + 1, dtype=torch.int32, device="cuda")
+    abi.mk_prefill(h, torch.from_numpy(prompt).cuda(), toks[0:1])
+    for s in range(wl.decode_steps):  # device-side feedback, no host sync
+        abi.mk_decode_step(h, toks[s:s + 1], toks[s + 1:s + 2])
+    abi.mk_synchronize(h)
+    gpu = toks.cpu().numpy()
+    ref_tokens, ref_logits = D.Decoder(shape, w, 1, wl.max_seq).generate(prompt, wl.decode_steps)
+    last = D.Decoder(shape, w, 1, wl.max_seq).prefill(prompt)[0]
+    margins = [D.top2_margin(last)] + [D.top2_margin(ref_logits[0, s]) for s in range(wl.decode_steps)]
+    ref_seq = [int(D.greedy(last))] + list(ref_tokens[0])
+    for s in range(wl.decode_steps + 1):
+        if margins[s] <= MARGIN:
+            break
+        assert gpu[s] == ref_seq[s], f"step {s}"
+
+
+def test_modes_and_poison_are_bit_identical(abi):
+    """Same task bodies and per-task reduction order: megakernel, per-op and
+    NaN-poisoned scratch must give the same bits."""
+    shape = MINI_G8
+    prompt = gen.tokens(4, 3, 0, 9, shape.vocab)
+    outs = []
+    w = gen.gen_weights(shape, 2, True)
+    for mode, flags in ((0, 0), (1, 0), (0, abi.MK_FLAG_POISON), (1, abi.MK_FLAG_POISON)):
+        case = Case(shape, 16, mode, flags=flags, attn_split=4, weights=w)
+        res = [case.prefill(prompt)[0]]
+        for t in (3, 77, 200):
+            res.append(case.step(t)[0])
+        outs.append(np.stack(res))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_intermediates_match_oracle_per_layer(abi):
+    shape = MINI
+    case = Case(shape, 24, 0, seed=8, random_norms=True, attn_split=4)
+    case.prefill(gen.tokens(1, 3, 0, 6, shape.vocab))
+    trace = {}
+    case.step(17, trace)
+    got = debug_arrays(abi, case.h, shape)
+    for l in range(shape.n_layers):
+        for name, key in (("q", "q"), ("attn", "attn"), ("xmid", "xmid"), ("h", "h")):
+            ref = trace[(key, l)][0]
+            err = np.abs(got[name][l] - ref).max() / np.abs(ref).max()
+            assert err < 1e-2, (name, l, err)
+        ref = trace[("x", l + 1)][0]
+        assert np.abs(got["xs"][l + 1] - ref).max() / np.abs(ref).max() < 1e-2
+
+
+def test_reset_reproduces_and_capacity_is_enforced(abi):
+    shape = MINI
+    case = Case(shape, 5, 0)
+    prompt = gen.tokens(1, 3, 0, 4, shape.vocab)
+    a = case.prefill(prompt)[0]
+    case.step(5)
+    with pytest.raises(abi.MkError) as e:
+        abi.mk_decode_step(case.h, case.tok, case.out, case.logits)
+    assert e.value.status == abi.MK_ERR_CAPACITY
+    abi.mk_reset(case.h)
+    p = torch.from_numpy(prompt.reshape(1, -1)).cuda()
+    abi.mk_prefill(case.h, p, case.out, case.logits)
+    abi.mk_synchronize(case.h)
+    assert np.array_equal(case.logits.cpu().numpy()[0], a)
+    with pytest.raises(abi.MkError) as e:
+        abi.mk_prefill(case.h, p, case.out, case.logits)  # cache not empty
+    assert e.value.status == abi.MK_ERR_STATE
+
+
+@pytest.mark.parametrize("ncu", [1, 7, 64])
+def test_few_compute_units(abi, ncu):
+    shape = MINI_TIED
+    case = Case(shape, 20, 0, seed=3, random_norms=True, attn_split=8, num_cus=ncu, kv_bf16_oracle=True)
+    teacher_forced(case, gen.tokens(2, 3, 0, 9, shape.vocab), 6, TIGHT)
+
+
+def test_llama1b_shape_two_layers(abi):
+    shape = presets.with_layers(presets.LLAMA1B, 2)
+    case = Case(shape, 48, 0, kv_bf16_oracle=True)
+    teacher_forced(case, gen.tokens(1001, 3, 0, 39, shape.vocab), 4, TIGHT)

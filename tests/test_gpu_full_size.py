@@ -1,0 +1,60 @@
+"""Full-size parity: the Llama-3.2-1B and Llama-3-8B shapes in the launch
+configuration the benchmark times (megakernel, every CU).
+
+The oracle cannot afford hundreds of fp64 decode steps at these sizes, so the
+GPU decodes seeded random tokens after the seeded 39-token prompt (teacher
+forcing with inputs that come from the generator, never from the GPU), and the
+oracle's cache-free causal forward over the same sequence gives the expected
+logits at every compared position.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decoder as D
+from synth import gen, presets
+from tests.gpu_util import rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("wl_name", ["llama1b", "llama8b"])
+def test_full_size_logits_and_tokens(wl_name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_persistent_megakernel_02_amd import abi, runtime
+    wl = presets.WORKLOADS[wl_name]
+    shape = wl.shape
+    n_dec = 3
+    prompt = gen.gen_prompt(wl)[0]
+    extra = gen.tokens(77, presets.TID_PROMPT, 0, n_dec, shape.vocab)
+    seq = np.concatenate([prompt, extra]).astype(np.int32)
+    print(f"[{wl_name}] generating weights", flush=True)
+    w = gen.gen_weights(shape, wl.weight_seed)
+    dw = runtime.upload_weights(w)
+    h = runtime.create(shape, dw, wl.max_seq)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
+    got_logits, got_tok = [], []
+    abi.mk_prefill(h, torch.from_numpy(prompt.reshape(1, -1)).cuda(), out, lg)
+    abi.mk_synchronize(h)
+    got_logits.append(lg.cpu().numpy()[0])
+    got_tok.append(int(out.item()))
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for t in extra:
+        tok.fill_(int(t))
+        abi.mk_decode_step(h, tok, out, lg)
+        abi.mk_synchronize(h)
+        got_logits.append(lg.cpu().numpy()[0])
+        got_tok.append(int(out.item()))
+    abi.mk_destroy(h)
+    del dw
+    print(f"[{wl_name}] oracle forward", flush=True)
+    ref = D.forward_full(shape, w, seq[None, :])[0]         # [T, V]
+    ref = ref[len(prompt) - 1:]                              # positions compared
+    errs = rel_err(np.stack(got_logits), ref)
+    print(f"[{wl_name}] max rel err {errs.max():.3e}", flush=True)
+    assert np.all(errs <= 2e-2)
+    for s in range(n_dec + 1):
+        if D.top2_margin(ref[s]) > 5e-2:
+            assert got_tok[s] == int(D.greedy(ref[s]))

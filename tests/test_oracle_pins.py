@@ -250,7 +250,7 @@ PLANTS = {
     "rope_sign": ("rope", _rope_sign),
     "gqa_modulo": ("gqa_attention", _gqa_modulo),
     "relu_not_silu": ("silu", lambda u: np.maximum(u, 0.0)),
-    "ffn_swapped_gate_up": ("swiglu_ffn", lambda r, g, u, d: (D.silu(r @ u.T) * (r @ g.T)) @ d.T),
+    "ffn_swapped_gate_up": ("swiglu", lambda r, g, u: D.silu(r @ u.T) * (r @ g.T)),
     "no_softmax_scale": ("gqa_attention",
                          lambda q, K, V: np.stack([D.softmax(K[(h * K.shape[0]) // q.shape[0]] @ q[h]) @
                                                    V[(h * K.shape[0]) // q.shape[0]] for h in range(q.shape[0])])),
