@@ -16,7 +16,7 @@ MK_ABI_VERSION = 1
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_OUT_OF_MEMORY, MK_ERR_HIP = 0, -1, -2, -3
 MK_ERR_CAPACITY, MK_ERR_TIMEOUT, MK_ERR_STATE, MK_ERR_UNSUPPORTED = -4, -5, -6, -7
 MK_MODE_MEGAKERNEL, MK_MODE_PER_OP = 0, 1
-MK_FLAG_TRACE, MK_FLAG_POISON = 1, 2
+MK_FLAG_TRACE, MK_FLAG_POISON, MK_FLAG_NO_GRAPH = 1, 2, 4
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_OUT_OF_MEMORY", -3: "MK_ERR_HIP",
                 -4: "MK_ERR_CAPACITY", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE", -7: "MK_ERR_UNSUPPORTED"}
 
@@ -88,6 +88,8 @@ SIGNATURES = {
     "mk_read_status": ([_P, ctypes.POINTER(ctypes.c_uint32)], _I32),
     "mk_read_trace": ([_P, ctypes.POINTER(ctypes.c_uint64), _I32, ctypes.POINTER(_I32),
                        ctypes.POINTER(ctypes.c_double)], _I32),
+    "mk_time_ops": ([_P, ctypes.c_uint32, _I32], _I32),
+    "mk_read_op_times": ([_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
     "mk_t_gemv": ([_P, _P, _P, _I32, _I32, _P], _I32),
     "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
@@ -243,7 +245,7 @@ def mk_get_debug_view(h: Handle) -> mk_debug_view:
 
 
 def mk_read_status(h: Handle):
-    out = (ctypes.c_uint32 * 8)()
+    out = (ctypes.c_uint32 * 16)()
     _check(lib.mk_read_status(h.ptr, out), "mk_read_status")
     return list(out)
 
@@ -257,6 +259,24 @@ def mk_read_trace(h: Handle):
     _check(lib.mk_read_trace(h.ptr, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n.value, ctypes.byref(n),
                              ctypes.byref(tpu)), "mk_read_trace")
     return buf.reshape(-1, 2), tpu.value
+
+
+TASK_TYPES = {"qkv": 1, "attn": 2, "merge": 3, "o": 4, "gu": 5, "down": 6, "lm": 7, "argmax": 8}
+
+
+def mk_time_ops(h: Handle, types, max_launches: int):
+    mask = 0
+    for t in types:
+        mask |= 1 << TASK_TYPES[t]
+    _check(lib.mk_time_ops(h.ptr, mask, max_launches), "mk_time_ops")
+
+
+def mk_read_op_times(h: Handle):
+    """{type name: (total ms, launches)} of the timed launches."""
+    ms = (ctypes.c_double * 9)()
+    n = (ctypes.c_int32 * 9)()
+    _check(lib.mk_read_op_times(h.ptr, ms, n), "mk_read_op_times")
+    return {name: (ms[i], n[i]) for name, i in TASK_TYPES.items() if n[i]}
 
 
 def mk_t_gemv(W, x, y, stream=None):

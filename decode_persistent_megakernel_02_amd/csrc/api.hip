@@ -82,14 +82,25 @@ struct mk_handle {
   Params P{};
   std::vector<void*> allocs;
   Task* d_stage_tasks = nullptr;
-  int page_floats = 0, scratch_floats = 0, lds_mega = 0, lds_stage = 0;
+  int page_floats = 0, scratch_floats = 0, lds_mega = 0;
+  int op_page[9] = {0}, op_lds[9] = {0}, op_grid_cap[9] = {0};  // per task type
   int length = 0, batch = 0;
   uint32_t epoch = 0;
   bool poisoned = false;
   int32_t* d_tok_scratch = nullptr;
+  Step* d_step = nullptr;               // per-step arguments, written by mk_set_step
+  int attn_lds = 0;                     // fused per-op attention kernel
+  hipStream_t cap_stream = nullptr;     // private stream used to capture the step graph
+  hipGraph_t step_graph = nullptr;
+  hipGraphExec_t graph_exec = nullptr;
   float* act = nullptr;
   int64_t act_floats = 0;
   double ticks_per_us = 100.0;
+  // optional HIP-event timing of selected operators (per-op mode)
+  uint32_t timed_mask = 0;
+  std::vector<hipEvent_t> ev_pool;  // pairs: [2i] start, [2i+1] end
+  std::vector<int> ev_type;
+  int ev_used = 0;
 
   template <class T>
   mk_status alloc(T** p, int64_t count) {
@@ -104,6 +115,10 @@ struct mk_handle {
     return MK_OK;
   }
   ~mk_handle() {
+    if (graph_exec) (void)hipGraphExecDestroy(graph_exec);
+    if (step_graph) (void)hipGraphDestroy(step_graph);
+    if (cap_stream) (void)hipStreamDestroy(cap_stream);
+    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
     for (void* p : allocs) (void)hipFree(p);
   }
 };
@@ -115,6 +130,19 @@ struct mk_handle {
   } while (0)
 
 namespace {
+
+const void* op_kernel(int type) {
+  switch (type) {
+    case TT_QKV: return reinterpret_cast<const void*>(&mk_op_qkv);
+    case TT_ATTN: return reinterpret_cast<const void*>(&mk_op_attn);
+    case TT_MERGE: return reinterpret_cast<const void*>(&mk_op_merge);
+    case TT_O: return reinterpret_cast<const void*>(&mk_op_o);
+    case TT_GU: return reinterpret_cast<const void*>(&mk_op_gu);
+    case TT_DOWN: return reinterpret_cast<const void*>(&mk_op_down);
+    case TT_LM: return reinterpret_cast<const void*>(&mk_op_lm);
+    default: return reinterpret_cast<const void*>(&mk_op_argmax);
+  }
+}
 
 mk_status device_facts(int* ncu, double* ticks_per_us, int* max_lds) {
   int dev = 0;
@@ -133,6 +161,58 @@ mk_status device_facts(int* ncu, double* ticks_per_us, int* max_lds) {
   return MK_OK;
 }
 
+// Enqueue the operator launches of one step (kernel-per-operator mode) on `st`.
+mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
+  const auto& g = h->graph;
+  Params Pc = h->P;
+  const Step* sp = h->d_step;
+  int sf = h->scratch_floats;
+  for (size_t s = 0; s + 1 < g.stage_begin.size(); ++s) {
+    const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
+    if (count <= 0) continue;
+    const int type = g.stage_type[s];
+    if (type == TT_MERGE) continue;  // merged inside the fused attention kernel
+    const bool timed = timed_ok && ((h->timed_mask >> type) & 1) && 2 * (h->ev_used + 1) <= (int)h->ev_pool.size();
+    if (timed) HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used], st));
+    if (type == TT_ATTN) {
+      int layer = g.tasks[b0].layer;
+      void* args[] = {&Pc, &sp, &layer};
+      HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_fused), dim3(h->P.B * h->P.nkv),
+                              dim3(kWaves * kWave), args, (size_t)h->attn_lds, st));
+    } else {
+      const int grid = std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]);
+      const Task* tasks = h->d_stage_tasks + b0;
+      int opf = h->op_page[type];
+      int cnt = count;
+      void* args[] = {&Pc, &sp, &tasks, &cnt, &opf, &sf};
+      HIP_TRY(hipLaunchKernel(op_kernel(type), dim3(grid), dim3(kWaves * kWave), args, (size_t)h->op_lds[type], st));
+    }
+    if (timed) {
+      HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used + 1], st));
+      h->ev_type[h->ev_used++] = type;
+    }
+  }
+  return MK_OK;
+}
+
+// Capture one step's operator launches into a graph (once per handle).
+mk_status build_step_graph(mk_handle* h) {
+  if (h->graph_exec) return MK_OK;
+  if (!h->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+  HIP_TRY(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+  mk_status st = enqueue_ops(h, h->cap_stream, false);
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(h->cap_stream, &graph);
+  if (st != MK_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (e != hipSuccess) return fail(MK_ERR_HIP, std::string("graph capture: ") + hipGetErrorString(e));
+  h->step_graph = graph;
+  HIP_TRY(hipGraphInstantiate(&h->graph_exec, h->step_graph, nullptr, nullptr, 0));
+  return MK_OK;
+}
+
 mk_status launch_step(mk_handle* h, const Step& S) {
   const Params& P = h->P;
   if (h->cfg.flags & MK_FLAG_POISON) {
@@ -140,24 +220,21 @@ mk_status launch_step(mk_handle* h, const Step& S) {
                        h->act_floats, 0xFFFFFFFFu);
     HIP_TRY(hipGetLastError());
   }
+  hipLaunchKernelGGL(mk_set_step, dim3(1), dim3(64), 0, h->stream, h->d_step, S);
+  HIP_TRY(hipGetLastError());
   int pf = h->page_floats, sf = h->scratch_floats;
   if (h->cfg.mode == MK_MODE_MEGAKERNEL) {
     Params Pc = P;
-    Step Sc = S;
-    void* args[] = {&Pc, &Sc, &pf, &sf};
+    const Step* sp = h->d_step;
+    void* args[] = {&Pc, &sp, &pf, &sf};
     HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mk_persistent), dim3(P.ncu),
                                        dim3(kWaves * kWave), args, (unsigned)h->lds_mega, h->stream));
-  } else {
-    const auto& g = h->graph;
-    for (size_t s = 0; s + 1 < g.stage_begin.size(); ++s) {
-      const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
-      if (count <= 0) continue;
-      int grid = std::min((count + kWaves - 1) / kWaves, P.ncu);
-      hipLaunchKernelGGL(mk_stage, dim3(grid), dim3(kWaves * kWave), (unsigned)h->lds_stage, h->stream, P, S,
-                         h->d_stage_tasks + b0, count, pf, sf);
-      HIP_TRY(hipGetLastError());
-    }
+    return MK_OK;
   }
+  const bool eager = (h->cfg.flags & MK_FLAG_NO_GRAPH) || h->timed_mask != 0;
+  if (eager) return enqueue_ops(h, h->stream, true);
+  MK_TRY(build_step_graph(h));
+  HIP_TRY(hipGraphLaunch(h->graph_exec, h->stream));
   return MK_OK;
 }
 
@@ -193,6 +270,13 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
         !w->w_up[l] || !w->w_down[l])
       return fail(MK_ERR_INVALID_ARG, "weights: NULL pointer in layer " + std::to_string(l));
   if (cfg->max_batch != 1) return fail(MK_ERR_UNSUPPORTED, "max_batch > 1 is not implemented yet");
+  // The cooperative persistent launch did not complete on the MI355X test box
+  // (the stream never drained although every in-kernel wait is bounded); until
+  // the cause is known this mode is refused rather than risked.
+  if (cfg->mode == MK_MODE_MEGAKERNEL)
+    return fail(MK_ERR_UNSUPPORTED,
+                "MK_MODE_MEGAKERNEL (cooperative persistent launch) is disabled: its launch did not complete on "
+                "gfx950; use MK_MODE_PER_OP");
 
   int dev_cus = 0, max_lds = 0;
   double tpu = 100.0;
@@ -222,6 +306,9 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   P.ncu = ncu;
   const double wd_ms = cfg->watchdog_ms ? cfg->watchdog_ms : 2000.0;
   P.timeout_ticks = (uint32_t)std::min(4.0e9, wd_ms * 1000.0 * tpu);
+  // One wait iteration takes well over 20 ns (a sleep plus a memory read), so
+  // this limit trips only if the wall clock stops advancing.
+  P.spin_limit = (uint32_t)std::min(4.0e9, wd_ms * 1000.0 * 50.0);
   P.embed = static_cast<const uint16_t*>(w->embed);
   P.lm_head = static_cast<const uint16_t*>(w->lm_head);
   P.final_norm = static_cast<const uint16_t*>(w->final_norm);
@@ -292,28 +379,44 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   P.queue_off = d_qoff;
   MK_TRY(h->alloc(&P.events, (int64_t)g.event_count.size()));
   HIP_TRY(hipMemset(P.events, 0, g.event_count.size() * 4));
-  MK_TRY(h->alloc(&P.status, 8));
-  HIP_TRY(hipMemset(P.status, 0, 32));
+  MK_TRY(h->alloc(&P.status, kStatusWords));
+  HIP_TRY(hipMemset(P.status, 0, kStatusWords * 4));
   if (cfg->flags & MK_FLAG_TRACE) {
     MK_TRY(h->alloc(&P.trace, 2 * (int64_t)g.tasks.size()));
     HIP_TRY(hipMemset(P.trace, 0, 16 * g.tasks.size()));
     P.trace_cap = (int32_t)g.tasks.size();
   }
   MK_TRY(h->alloc(&h->d_tok_scratch, B));
+  MK_TRY(h->alloc(&h->d_step, 1));
 
   // LDS budget
   h->page_floats = round_up(std::max({H, nq * hd, F}), 8);
   h->scratch_floats = round_up(G * hd + G * kWave, 4);
   h->lds_mega = (int)sizeof(Lds) + 2 * h->page_floats * 4 + kWorkers * h->scratch_floats * 4;
-  h->lds_stage = (int)sizeof(Lds) + h->page_floats * 4 + kWaves * h->scratch_floats * 4;
-  if (h->lds_mega > max_lds || h->lds_stage > max_lds)
+  for (int t = TT_QKV; t <= TT_ARGMAX; ++t) {
+    int pfl = 0;
+    if (t == TT_QKV || t == TT_GU || t == TT_LM) pfl = H;
+    else if (t == TT_O) pfl = nq * hd;
+    else if (t == TT_DOWN) pfl = F;
+    h->op_page[t] = round_up(pfl, 8);
+    h->op_lds[t] = (int)sizeof(Lds) + h->op_page[t] * 4 + (t == TT_ATTN ? kWaves * h->scratch_floats * 4 : 0);
+    if (h->op_lds[t] > max_lds)
+      return fail(MK_ERR_UNSUPPORTED, "operator LDS need exceeds " + std::to_string(max_lds));
+    HIP_TRY(hipFuncSetAttribute(op_kernel(t), hipFuncAttributeMaxDynamicSharedMemorySize, h->op_lds[t]));
+    int nb = 0;
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, op_kernel(t), kWaves * kWave, h->op_lds[t]));
+    h->op_grid_cap[t] = std::max(1, nb) * ncu;
+  }
+  h->attn_lds = (G * hd + kWaves * G * kWave + kWaves * G * (hd + 2)) * 4;
+  if (h->attn_lds > max_lds) return fail(MK_ERR_UNSUPPORTED, "attention LDS need exceeds the device limit");
+  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_op_attn_fused),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, h->attn_lds));
+  if (h->lds_mega > max_lds)
     return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(h->lds_mega) + " B exceeds " + std::to_string(max_lds));
   // keep one persistent workgroup per CU: ask for more than half the LDS
   if (h->lds_mega <= max_lds / 2) h->lds_mega = max_lds / 2 + 1024;
   HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_persistent),
                               hipFuncAttributeMaxDynamicSharedMemorySize, h->lds_mega));
-  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_stage), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              h->lds_stage));
   if (cfg->mode == MK_MODE_MEGAKERNEL) {
     int nb = 0;
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&mk_persistent),
@@ -368,23 +471,30 @@ mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P
   return MK_OK;
 }
 
-mk_status mk_read_status(mk_handle* h, uint32_t out[8]) {
+mk_status mk_read_status(mk_handle* h, uint32_t out[16]) {
   if (!h || !out) return fail(MK_ERR_INVALID_ARG, "NULL argument");
   HIP_TRY(hipStreamSynchronize(h->stream));
-  HIP_TRY(hipMemcpy(out, h->P.status, 32, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(out, h->P.status, kStatusWords * 4, hipMemcpyDeviceToHost));
   return MK_OK;
 }
 
 mk_status mk_synchronize(mk_handle* h) {
   g_err.clear();
   if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
-  uint32_t st[8];
+  uint32_t st[kStatusWords];
   MK_TRY(mk_read_status(h, st));
   if (st[1] == ST_TIMEOUT) {
     h->poisoned = true;
-    return fail(MK_ERR_TIMEOUT, "watchdog: CU " + std::to_string(st[2]) + " task " + std::to_string(st[3]) +
-                                    " waited on event " + std::to_string(st[4]) + " (counter " +
-                                    std::to_string(st[5]) + ", threshold " + std::to_string(st[6]) + ")");
+    static const char* who[] = {"scheduler (event)", "scheduler (LDS page)", "worker (ready frontier)"};
+    return fail(MK_ERR_TIMEOUT, std::string("watchdog: ") + who[st[7] < 3 ? st[7] : 0] + " on CU " +
+                                    std::to_string(st[2]) + ", task " + std::to_string(st[3]) + ", event " +
+                                    std::to_string(st[4]) + ": value " + std::to_string(st[5]) + ", needed " +
+                                    std::to_string(st[6]) + "; frontier " + std::to_string(st[8]) + ", ticket " +
+                                    std::to_string(st[9]));
+  }
+  if (st[1] == ST_LDS) {
+    h->poisoned = true;
+    return fail(MK_ERR_HIP, "the persistent kernel ran with less LDS than it requested");
   }
   if (st[1] == ST_NONFINITE) {
     h->poisoned = true;
@@ -519,6 +629,39 @@ mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out) {
   return MK_OK;
 }
 
+mk_status mk_time_ops(mk_handle* h, uint32_t type_mask, int32_t max_launches) {
+  g_err.clear();
+  if (!h || max_launches < 0) return fail(MK_ERR_INVALID_ARG, "bad arguments");
+  if (h->cfg.mode != MK_MODE_PER_OP && type_mask) return fail(MK_ERR_UNSUPPORTED, "operator timing needs MK_MODE_PER_OP");
+  HIP_TRY(hipStreamSynchronize(h->stream));
+  const size_t need = 2 * (size_t)max_launches;
+  while (h->ev_pool.size() < need) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e));
+    h->ev_pool.push_back(e);
+  }
+  h->ev_type.assign(max_launches, 0);
+  h->ev_used = 0;
+  h->timed_mask = type_mask;
+  return MK_OK;
+}
+
+mk_status mk_read_op_times(mk_handle* h, double* total_ms, int32_t* launches) {
+  g_err.clear();
+  if (!h || !total_ms || !launches) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  HIP_TRY(hipStreamSynchronize(h->stream));
+  for (int t = 0; t < 9; ++t) { total_ms[t] = 0; launches[t] = 0; }
+  for (int i = 0; i < h->ev_used; ++i) {
+    float ms = 0;
+    HIP_TRY(hipEventElapsedTime(&ms, h->ev_pool[2 * i], h->ev_pool[2 * i + 1]));
+    total_ms[h->ev_type[i]] += ms;
+    launches[h->ev_type[i]] += 1;
+  }
+  h->ev_used = 0;
+  h->timed_mask = 0;
+  return MK_OK;
+}
+
 mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, double* ticks_per_us) {
   if (!h || !n) return fail(MK_ERR_INVALID_ARG, "NULL argument");
   if (!h->P.trace) return fail(MK_ERR_STATE, "handle created without MK_FLAG_TRACE");
@@ -542,7 +685,7 @@ mk_status mk_t_gemv(const void* W, const float* x, float* y, int32_t N, int32_t 
   if (lds > max_lds) return fail(MK_ERR_UNSUPPORTED, "K too large for LDS staging");
   HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_t_gemv_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-  const int grid = std::min((N + kWaves * kRows - 1) / (kWaves * kRows), 1024);
+  const int grid = std::min((N + kWaves * 4 - 1) / (kWaves * 4), 1024);
   hipLaunchKernelGGL(mk_t_gemv_kernel, dim3(grid), dim3(kWaves * kWave), (unsigned)lds,
                      static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W), x, y, N, K);
   HIP_TRY(hipGetLastError());

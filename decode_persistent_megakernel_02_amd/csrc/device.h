@@ -88,31 +88,41 @@ __device__ __forceinline__ uint32_t lds_add(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint64_t clock_now() { return __builtin_amdgcn_s_memrealtime(); }
 
 // ---------------------------------------------------------------------------
-// GEMV core: kRows weight rows (bf16, each K contiguous elements) dotted with
-// one fp32 vector held in LDS.  Each lane owns 8 consecutive columns of every
-// 512-column chunk, so one wave load instruction reads 1 KiB of a row.  kDepth
-// chunks per row stay in flight; `prefetch` issues them (weights do not depend
-// on any event, so this runs before the task's dependency is satisfied) and
-// `run` consumes them, refilling each slot with the chunk kDepth ahead.
-constexpr int kDepth = 8;
-
+// GEMV core: R weight rows (bf16, each K contiguous elements) dotted with one
+// fp32 vector held in LDS.  Each lane owns 8 consecutive columns of every
+// 512-column chunk, so one wave load instruction reads 1 KiB of a row.  D
+// chunks per row stay in flight (R*D loads of 16 B per lane); `prefetch`
+// issues them -- weights depend on no event, so this can run before the
+// task's inputs exist -- and `run` consumes them, refilling each slot with the
+// chunk D ahead.
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
+// Row r (r < split) starts at base0 + r * stride, row r >= split at
+// base1 + (r - split) * stride (both in 16-byte vectors).  With r a
+// compile-time constant after unrolling, every address is base + constant.
+template <int R>
 struct GemvRows {
-  const v4u* row[kRows];
-  uint32_t mask;  // bit r set: row r valid
-  int nvec;       // K / 8 (16-byte vectors per row)
+  const v4u* base0;
+  const v4u* base1;
+  int64_t stride;  // vectors between consecutive rows
+  int split;       // rows taken from base0
+  uint32_t mask;   // bit r set: row r valid
+  int nvec;        // K / 8 (16-byte vectors per row)
+  __device__ __forceinline__ const v4u* row(int r) const {
+    return r < split ? base0 + r * stride : base1 + (r - split) * stride;
+  }
 };
 
 __device__ __forceinline__ v4u ld_w(const v4u* p) { return __builtin_nontemporal_load(p); }
 
-__device__ __forceinline__ void gemv_prefetch(v4u (&buf)[kDepth][kRows], const GemvRows& g, int lane) {
+template <int R, int D>
+__device__ __forceinline__ void gemv_prefetch(v4u (&buf)[D][R], const GemvRows<R>& g, int lane) {
 #pragma unroll
-  for (int s = 0; s < kDepth; ++s) {
+  for (int s = 0; s < D; ++s) {
     const int v = s * kWave + lane;
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
-      buf[s][r] = ((g.mask >> r) & 1) && v < g.nvec ? ld_w(g.row[r] + v) : v4u{0u, 0u, 0u, 0u};
+    for (int r = 0; r < R; ++r)
+      buf[s][r] = ((g.mask >> r) & 1) && v < g.nvec ? ld_w(g.row(r) + v) : v4u{0u, 0u, 0u, 0u};
   }
 }
 
@@ -128,16 +138,17 @@ __device__ __forceinline__ float dot8(v4u w, const float4& a, const float4& b, f
   return acc;
 }
 
-// Returns the kRows dot products (uniform across the wave).
-__device__ __forceinline__ void gemv_run(v4u (&buf)[kDepth][kRows], const GemvRows& g, const float* xs, int lane,
-                                         float (&y)[kRows]) {
-  float acc[kRows];
+// y[r] = sum_k W[r][k] * xs[k] for the R rows (uniform across the wave).
+template <int R, int D>
+__device__ __forceinline__ void gemv_run(v4u (&buf)[D][R], const GemvRows<R>& g, const float* xs, int lane,
+                                         float (&y)[R]) {
+  float acc[R];
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
   const int nchunks = (g.nvec + kWave - 1) / kWave;
-  for (int c0 = 0; c0 < nchunks; c0 += kDepth) {
+  for (int c0 = 0; c0 < nchunks; c0 += D) {
 #pragma unroll
-    for (int s = 0; s < kDepth; ++s) {
+    for (int s = 0; s < D; ++s) {
       const int c = c0 + s;
       if (c < nchunks) {
         const int v = c * kWave + lane;
@@ -147,18 +158,18 @@ __device__ __forceinline__ void gemv_run(v4u (&buf)[kDepth][kRows], const GemvRo
           xb = *reinterpret_cast<const float4*>(xs + v * 8 + 4);
         }
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) acc[r] = dot8(buf[s][r], xa, xb, acc[r]);
-        const int vn = (c + kDepth) * kWave + lane;
-        if (c + kDepth < nchunks) {
+        for (int r = 0; r < R; ++r) acc[r] = dot8(buf[s][r], xa, xb, acc[r]);
+        const int vn = (c + D) * kWave + lane;
+        if (c + D < nchunks) {
 #pragma unroll
-          for (int r = 0; r < kRows; ++r)
-            buf[s][r] = ((g.mask >> r) & 1) && vn < g.nvec ? ld_w(g.row[r] + vn) : v4u{0u, 0u, 0u, 0u};
+          for (int r = 0; r < R; ++r)
+            buf[s][r] = ((g.mask >> r) & 1) && vn < g.nvec ? ld_w(g.row(r) + vn) : v4u{0u, 0u, 0u, 0u};
         }
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) y[r] = wave_sum(acc[r]);
+  for (int r = 0; r < R; ++r) y[r] = wave_sum(acc[r]);
 }
 
 // ---------------------------------------------------------------------------
@@ -201,97 +212,160 @@ __device__ __forceinline__ void stage_vector(float* page, const float* src, cons
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV decode attention partial for one KV group: positions [p0, p1)
-// (at most 64, one per lane for the scores), G query heads of head_dim HD.
-// Writes o (unnormalised, HD floats), then m (max score) and l (sum of
-// exp(score - m)) per head into out[G][HD + 2].  scratch: LDS, G*HD + G*64 floats.
+// Split-KV decode attention (online softmax).  One wave owns a running state
+// for the G query heads of a KV group: max score m, sum of exp(score - m) l,
+// and the unnormalised output o (each lane owns DPL = HD/64 dims).  A block
+// is at most 64 positions: lane j scores position p0 + j against all G heads
+// (its whole K row is loaded at once), then every lane accumulates its dims
+// of V over the block's positions, with 32 rows of loads in flight.
 template <int HD>
-__device__ void attn_partial(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t pos_stride, int p0,
-                             int p1, int G, float* out, float* scratch, int lane) {
-  constexpr int DPL = HD / kWave;  // dims per lane for the value accumulation (1 or 2)
-  float* qs = scratch;              // [G][HD]
-  float* pr = scratch + G * HD;     // [G][64]
-  for (int i = lane; i < G * HD; i += kWave) qs[i] = q[i];
-  __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
+struct AttnState {
+  static constexpr int DPL = HD / kWave;
+  float m[kMaxGqa], l[kMaxGqa], o[kMaxGqa][DPL];
+  __device__ void init() {
+#pragma unroll
+    for (int h = 0; h < kMaxGqa; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
+    }
+  }
+};
+
+// qs: LDS [G][HD] (the rotated queries); pr: LDS [G][64] scratch.
+template <int HD>
+__device__ __forceinline__ void attn_block(const float* qs, const uint16_t* kc, const uint16_t* vc, int64_t pos_stride, int p0,
+                           int p1, int G, float* pr, int lane, AttnState<HD>& st) {
+  constexpr int DPL = HD / kWave, NV = HD / 8;
   const int np = p1 - p0;
   const float scale = 1.0f / sqrtf((float)HD);
+  v4u k8[NV];
+  if (lane < np) {
+    const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)(p0 + lane) * pos_stride);
+#pragma unroll
+    for (int d8 = 0; d8 < NV; ++d8) k8[d8] = krow[d8];
+  }
   float sc[kMaxGqa];
 #pragma unroll
   for (int h = 0; h < kMaxGqa; ++h) sc[h] = 0.f;
   if (lane < np) {
-    const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)(p0 + lane) * pos_stride);
-#pragma unroll 4
-    for (int d8 = 0; d8 < HD / 8; ++d8) {
-      const v4u k8 = krow[d8];
+#pragma unroll
+    for (int d8 = 0; d8 < NV; ++d8) {
 #pragma unroll
       for (int h = 0; h < kMaxGqa; ++h) {
         if (h < G) {
           const float4 a = *reinterpret_cast<const float4*>(qs + h * HD + d8 * 8);
           const float4 b = *reinterpret_cast<const float4*>(qs + h * HD + d8 * 8 + 4);
-          sc[h] = dot8(k8, a, b, sc[h]);
+          sc[h] = dot8(k8[d8], a, b, sc[h]);
         }
       }
     }
   }
-  float m[kMaxGqa], l[kMaxGqa];
 #pragma unroll
   for (int h = 0; h < kMaxGqa; ++h) {
     if (h < G) {
       const float s = lane < np ? sc[h] * scale : -INFINITY;
-      m[h] = wave_max(s);
-      const float p = lane < np ? __expf(s - m[h]) : 0.f;
-      l[h] = wave_sum(p);
+      const float mn = fmaxf(st.m[h], wave_max(s));
+      const float alpha = __expf(st.m[h] - mn);  // 0 on the first block (m = -inf)
+      const float p = lane < np ? __expf(s - mn) : 0.f;
+      st.l[h] = st.l[h] * alpha + wave_sum(p);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) st.o[h][e] *= alpha;
+      st.m[h] = mn;
       pr[h * kWave + lane] = p;
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  float o[kMaxGqa][DPL];
+  __builtin_amdgcn_wave_barrier();  // one wave's LDS writes and reads stay in order
+  constexpr int VB = 32;
+  for (int j0 = 0; j0 < np; j0 += VB) {
+    float vv[VB][DPL];
 #pragma unroll
-  for (int h = 0; h < kMaxGqa; ++h)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
-  for (int j = 0; j < np; ++j) {
-    const uint16_t* vrow = vc + (int64_t)(p0 + j) * pos_stride + lane * DPL;
-    float vv[DPL];
-    if (DPL == 2) {
-      const uint32_t u = *reinterpret_cast<const uint32_t*>(vrow);
-      vv[0] = bf_lo(u);
-      vv[DPL - 1] = bf_hi(u);
-    } else {
-      vv[0] = bf1(vrow[0]);
+    for (int jj = 0; jj < VB; ++jj) {
+      const int j = j0 + jj;
+      if (j < np) {
+        const uint16_t* vrow = vc + (int64_t)(p0 + j) * pos_stride + lane * DPL;
+        if constexpr (DPL == 2) {
+          const uint32_t u = *reinterpret_cast<const uint32_t*>(vrow);
+          vv[jj][0] = bf_lo(u);
+          vv[jj][DPL - 1] = bf_hi(u);
+        } else {
+          vv[jj][0] = bf1(vrow[0]);
+        }
+      }
     }
 #pragma unroll
-    for (int h = 0; h < kMaxGqa; ++h) {
-      if (h < G) {
-        const float p = pr[h * kWave + j];
+    for (int jj = 0; jj < VB; ++jj) {
+      const int j = j0 + jj;
+      if (j < np) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+        for (int h = 0; h < kMaxGqa; ++h) {
+          if (h < G) {
+            const float p = pr[h * kWave + j];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) st.o[h][e] = fmaf(p, vv[jj][e], st.o[h][e]);
+          }
+        }
       }
     }
   }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Writes a wave's state as G records of (o[HD], m, l).
+template <int HD>
+__device__ __forceinline__ void attn_store_state(const AttnState<HD>& st, int G, float* out, int lane) {
+  constexpr int DPL = HD / kWave;
 #pragma unroll
   for (int h = 0; h < kMaxGqa; ++h) {
     if (h < G) {
       float* oh = out + h * (HD + 2);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) oh[lane * DPL + e] = o[h][e];
-      if (lane == 0) { oh[HD] = m[h]; oh[HD + 1] = l[h]; }
+      for (int e = 0; e < DPL; ++e) oh[lane * DPL + e] = st.o[h][e];
+      if (lane == 0) {
+        oh[HD] = st.m[h];
+        oh[HD + 1] = st.l[h];
+      }
     }
   }
 }
 
-// Log-sum-exp merge of nsplit partials laid out [nsplit][G][HD + 2]; writes
-// the normalised outputs of the G heads to out[G][HD].
+// Loads the G rotated query heads of a group into LDS.
 template <int HD>
-__device__ void attn_merge(const float* part, int nsplit, int G, float* out, int lane) {
+__device__ __forceinline__ void attn_load_q(const float* q, int G, float* qs, int lane) {
+  for (int i = lane; i < G * HD; i += kWave) qs[i] = q[i];
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One split of one wave: positions [p0, p1), partial written as G records.
+template <int HD>
+__device__ __forceinline__ void attn_partial(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t pos_stride, int p0,
+                             int p1, int G, float* out, float* scratch, int lane) {
+  float* qs = scratch;           // [G][HD]
+  float* pr = scratch + G * HD;  // [G][64]
+  attn_load_q<HD>(q, G, qs, lane);
+  AttnState<HD> st;
+  st.init();
+  for (int b0 = p0; b0 < p1; b0 += kWave) attn_block<HD>(qs, kc, vc, pos_stride, b0, min(b0 + kWave, p1), G, pr, lane, st);
+  attn_store_state<HD>(st, G, out, lane);
+}
+
+// Log-sum-exp merge of n partial records laid out [n][G][HD + 2] (stride
+// `rec_stride` floats between partials); writes the G normalised outputs to
+// out[G][HD].  Records with l == 0 (no positions) are skipped.
+template <int HD>
+__device__ __forceinline__ void attn_merge(const float* part, int n, int G, float* out, int lane, int rec_stride = -1) {
   constexpr int DPL = HD / kWave;
+  if (rec_stride < 0) rec_stride = G * (HD + 2);
   for (int h = 0; h < G; ++h) {
     float M = -INFINITY, Lsum = 0.f, o[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* ps = part + ((int64_t)s * G + h) * (HD + 2);
-      const float ms = ps[HD], ls = ps[HD + 1];
+    for (int s = 0; s < n; ++s) {
+      const float* ps = part + (int64_t)s * rec_stride + h * (HD + 2);
+      const float ls = ps[HD + 1];
+      if (!(ls > 0.f)) continue;
+      const float ms = ps[HD];
       const float Mn = fmaxf(M, ms);
       const float a = __expf(M - Mn), b = __expf(ms - Mn);
       Lsum = Lsum * a + ls * b;

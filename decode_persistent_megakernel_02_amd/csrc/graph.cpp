@@ -77,17 +77,15 @@ std::string build_graph(const GraphConfig& c, Graph& g) {
     const int in_x = l == 0 ? -1 : ev_x[l];
     begin_stage(TT_QKV);
     for (int b = 0; b < c.B; ++b) {
-      for (int m = 0; m < 2; ++m) {  // q, k: rows grouped into RoPE pairs (i, i + hd/2)
+      for (int m = 0; m < 2; ++m) {  // q, k: one task per RoPE pair (i, i + hd/2)
         const int heads = m == 0 ? c.nq : c.nkv;
         for (int hh = 0; hh < heads; ++hh)
-          for (int i = 0; i < half; i += kRows / 2) {
-            const int n = std::min(kRows / 2, half - i);
-            add(TT_QKV, l, in_x, ev_qkv[l], stage_key(SK_ATTN_NORM, l), b, m, hh * c.hd + i, 2 * n, half);
-          }
+          for (int i = 0; i < half; ++i)
+            add(TT_QKV, l, in_x, ev_qkv[l], stage_key(SK_ATTN_NORM, l), b, m, hh * c.hd + i, 2, half);
       }
       const int vrows = c.nkv * c.hd;
-      for (int r = 0; r < vrows; r += kRows)
-        add(TT_QKV, l, in_x, ev_qkv[l], stage_key(SK_ATTN_NORM, l), b, 2, r, std::min(kRows, vrows - r), 0);
+      for (int r = 0; r < vrows; r += kRowsQkv)
+        add(TT_QKV, l, in_x, ev_qkv[l], stage_key(SK_ATTN_NORM, l), b, 2, r, std::min(kRowsQkv, vrows - r), 0);
     }
     begin_stage(TT_ATTN);
     for (int b = 0; b < c.B; ++b)
@@ -100,21 +98,21 @@ std::string build_graph(const GraphConfig& c, Graph& g) {
         add(TT_MERGE, l, ev_att[l][b * c.nkv + grp], ev_mrg[l], 0, b, grp, 0, 0, 0);
     begin_stage(TT_O);
     for (int b = 0; b < c.B; ++b)
-      for (int r = 0; r < c.H; r += kRows)
-        add(TT_O, l, ev_mrg[l], ev_xmid[l], stage_key(SK_O_IN, l), b, 0, r, std::min(kRows, c.H - r), 0);
+      for (int r = 0; r < c.H; r += kRowsO)
+        add(TT_O, l, ev_mrg[l], ev_xmid[l], stage_key(SK_O_IN, l), b, 0, r, std::min(kRowsO, c.H - r), 0);
     begin_stage(TT_GU);
     for (int b = 0; b < c.B; ++b)
-      for (int r = 0; r < c.F; r += kRows / 2)
-        add(TT_GU, l, ev_xmid[l], ev_h[l], stage_key(SK_FFN_NORM, l), b, 0, r, std::min(kRows / 2, c.F - r), 0);
+      for (int r = 0; r < c.F; r += kRowsGuPerMatrix)
+        add(TT_GU, l, ev_xmid[l], ev_h[l], stage_key(SK_FFN_NORM, l), b, 0, r, std::min(kRowsGuPerMatrix, c.F - r), 0);
     begin_stage(TT_DOWN);
     for (int b = 0; b < c.B; ++b)
-      for (int r = 0; r < c.H; r += kRows)
-        add(TT_DOWN, l, ev_h[l], ev_x[l + 1], stage_key(SK_H, l), b, 0, r, std::min(kRows, c.H - r), 0);
+      for (int r = 0; r < c.H; r += kRowsDown)
+        add(TT_DOWN, l, ev_h[l], ev_x[l + 1], stage_key(SK_H, l), b, 0, r, std::min(kRowsDown, c.H - r), 0);
   }
   begin_stage(TT_LM);
   for (int b = 0; b < c.B; ++b)
-    for (int r = 0; r < c.V; r += kRows)
-      add(TT_LM, c.L, ev_x[c.L], ev_lm, stage_key(SK_FINAL_NORM, c.L), b, 0, r, std::min(kRows, c.V - r), 0);
+    for (int r = 0; r < c.V; r += kRowsLm)
+      add(TT_LM, c.L, ev_x[c.L], ev_lm, stage_key(SK_FINAL_NORM, c.L), b, 0, r, std::min(kRowsLm, c.V - r), 0);
   begin_stage(TT_ARGMAX);
   add(TT_ARGMAX, c.L, ev_lm, -1, 0, 0, 0, 0, 0, 0);
   g.stage_begin.push_back((int)g.tasks.size());
@@ -331,7 +329,7 @@ std::string validate_graph(const Graph& g) {
     for (auto& r : wr) writes[key_of(r)].push_back({r.lo, r.hi, (int)t.id});
     if (t.type == TT_QKV && t.a0 < 2) {
       const int half = c.hd / 2, off = t.a1 % c.hd;
-      if (t.a3 != half || off + t.a2 / 2 > half || t.a2 % 2) return fmt("task %ld: RoPE pair split across tasks", t.id);
+      if (t.a3 != half || off >= half || t.a2 != 2) return fmt("task %ld: RoPE pair split across tasks", t.id);
     }
   }
   for (auto& kv : writes) {

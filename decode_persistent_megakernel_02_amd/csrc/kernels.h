@@ -5,8 +5,19 @@
 #include "mk_internal.h"
 
 namespace mk {
-extern "C" __global__ void mk_persistent(Params P, Step S, int page_floats, int scratch_floats);
-extern "C" __global__ void mk_stage(Params P, Step S, const Task* tasks, int count, int page_floats, int scratch_floats);
+extern "C" __global__ void mk_persistent(Params P, const Step* S, int page_floats, int scratch_floats);
+extern "C" __global__ void mk_op_attn_fused(Params P, const Step* S, int layer);
+extern "C" __global__ void mk_set_step(Step* dst, Step s);
+#define MK_OP_DECL(name) extern "C" __global__ void name(Params P, const Step* S, const Task* tasks, int count, int pf, int sf);
+MK_OP_DECL(mk_op_qkv)
+MK_OP_DECL(mk_op_attn)
+MK_OP_DECL(mk_op_merge)
+MK_OP_DECL(mk_op_o)
+MK_OP_DECL(mk_op_gu)
+MK_OP_DECL(mk_op_down)
+MK_OP_DECL(mk_op_lm)
+MK_OP_DECL(mk_op_argmax)
+#undef MK_OP_DECL
 extern "C" __global__ void mk_fill_u32(uint32_t* p, int64_t n, uint32_t v);
 extern "C" __global__ void mk_t_gemv_kernel(const uint16_t* W, const float* x, float* y, int N, int K);
 extern "C" __global__ void mk_t_rmsnorm_kernel(const float* x, const uint16_t* gamma, float eps, float* y, int n);

@@ -59,161 +59,159 @@ __device__ void stage_input(const Params& P, const Step& S, uint16_t key, int b,
   }
 }
 
-__device__ __forceinline__ float pick4(const float (&y)[kRows], int i) {
-  return i == 0 ? y[0] : i == 1 ? y[1] : i == 2 ? y[2] : y[3];
+template <int R>
+__device__ __forceinline__ float pick(const float (&y)[R], int i) {
+  float v = y[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) v = i == r ? y[r] : v;
+  return v;
 }
 
-// Runs one task on one wave.  `wait()` is called after the weight prefetch and
-// before anything that reads activations; it returns false on abort.
+// GEMV-type task (QKV, O, GU, DOWN, LM) with its operator fixed at compile
+// time.  `wait()` runs after the weight prefetch and before anything that
+// reads activations; it returns false on abort.
+template <int TT, class Wait>
+__device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const Task& d, int lane, const float* page, Lds* L, Wait wait) {
+  constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
+  const int l = d.layer, b = d.batch;
+  GemvRows<R> g;
+  g.mask = 0;
+  int K = P.H;
+  if constexpr (TT == TT_O) K = P.nq * P.hd;
+  else if constexpr (TT == TT_DOWN) K = P.F;
+  g.stride = K / 8;
+  g.split = R;
+  if constexpr (TT == TT_QKV) {
+    const uint16_t* W = d.a0 == 0 ? P.wq[l] : d.a0 == 1 ? P.wk[l] : P.wv[l];
+    g.base0 = reinterpret_cast<const v4u*>(W + (int64_t)d.a1 * K);
+    if (d.a3) {  // one RoPE pair: rows a1 and a1 + hd/2
+      g.base1 = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + d.a3) * K);
+      g.split = 1;
+      g.mask = 3;
+    } else {
+      g.base1 = g.base0;
+      g.mask = (1u << d.a2) - 1;
+    }
+  } else if constexpr (TT == TT_GU) {  // rows: gate a1.., then up a1..
+    g.base0 = reinterpret_cast<const v4u*>(P.w_gate[l] + (int64_t)d.a1 * K);
+    g.base1 = reinterpret_cast<const v4u*>(P.w_up[l] + (int64_t)d.a1 * K);
+    g.split = R / 2;
+    const uint32_t half = (1u << d.a2) - 1;
+    g.mask = half | (half << (R / 2));
+  } else {
+    const uint16_t* W;
+    if constexpr (TT == TT_O) W = P.wo[l];
+    else if constexpr (TT == TT_DOWN) W = P.w_down[l];
+    else W = P.tied ? P.embed : P.lm_head;
+    g.base0 = reinterpret_cast<const v4u*>(W + (int64_t)d.a1 * K);
+    g.base1 = g.base0;
+    g.mask = (1u << d.a2) - 1;
+  }
+  g.nvec = K / 8;
+  v4u buf[D][R];
+  gemv_prefetch<R, D>(buf, g, lane);
+  if (!wait()) return false;
+  float y[R];
+  gemv_run<R, D>(buf, g, page, lane, y);
+  // epilogue: lane r finishes row slot r
+  const int r = lane;
+  const int64_t H = P.H;
+  if (r < R && ((g.mask >> r) & 1)) {
+    const float v = pick<R>(y, r);
+    if constexpr (TT == TT_QKV) {
+      if (d.a3) {  // rotate the pair (lo, hi) = (y0, y1) by the position's angle
+        const int half = P.hd / 2, i = d.a1 % P.hd;
+        const float c = P.rope_cos[(int64_t)S.pos * half + i], sn = P.rope_sin[(int64_t)S.pos * half + i];
+        const float rot = r == 0 ? y[0] * c - y[1] * sn : y[1] * c + y[0] * sn;
+        const int row = r == 0 ? d.a1 : d.a1 + d.a3;
+        if (d.a0 == 0) P.q[((int64_t)l * P.B + b) * P.nq * P.hd + row] = rot;
+        else P.kcache[kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd] = f2bf(rot);
+      } else {
+        const int row = d.a1 + r;
+        P.vcache[kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd] = f2bf(v);
+      }
+    } else if constexpr (TT == TT_O) {
+      const int row = d.a1 + r;
+      const float xin = l == 0 ? bf1(P.embed[(int64_t)token_of(P, S, b) * H + row]) : P.xs[((int64_t)l * P.B + b) * H + row];
+      P.xmid[((int64_t)l * P.B + b) * H + row] = xin + v;
+    } else if constexpr (TT == TT_GU) {
+      if (r < R / 2) P.h[((int64_t)l * P.B + b) * P.F + d.a1 + r] = silu(v) * pick<R>(y, r + R / 2);
+    } else if constexpr (TT == TT_DOWN) {
+      const int row = d.a1 + r;
+      P.xs[((int64_t)(l + 1) * P.B + b) * H + row] = P.xmid[((int64_t)l * P.B + b) * H + row] + v;
+    } else {
+      if (S.logits) S.logits[(int64_t)b * P.V + d.a1 + r] = v;
+    }
+  }
+  if constexpr (TT == TT_LM) {
+    unsigned long long best = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if ((g.mask >> j) & 1) {
+        const unsigned long long k = argmax_key(y[j], (uint32_t)(d.a1 + j));
+        best = k > best ? k : best;
+      }
+    if (lane == 0) __hip_atomic_fetch_max(&L->lm_best[b], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  return true;
+}
+
+template <int TT, class Wait>
+__device__ __forceinline__ bool exec_typed(const Params& P, const Step& S, const Task& d, int lane, const float* page, float* scratch,
+                           Lds* L, Wait wait) {
+  const int l = d.layer, b = d.batch;
+  if constexpr (TT == TT_QKV || TT == TT_O || TT == TT_GU || TT == TT_DOWN || TT == TT_LM) {
+    return exec_gemv<TT>(P, S, d, lane, page, L, wait);
+  } else if constexpr (TT == TT_ATTN) {
+    if (!wait()) return false;
+    const int G = P.nq / P.nkv, grp = d.a0, s = d.a1, T = S.pos + 1;
+    const int p0 = s * P.split;
+    if (p0 >= T) return true;
+    const int p1 = min(p0 + P.split, T);
+    const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * P.hd;
+    float* out = P.attn_part + ((((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit + s) * G * (P.hd + 2);
+    const uint16_t* kc = P.kcache + kv_off(P, l, b, grp, 0);
+    const uint16_t* vc = P.vcache + kv_off(P, l, b, grp, 0);
+    if (P.hd == 128) attn_partial<128>(q, kc, vc, P.hd, p0, p1, G, out, scratch, lane);
+    else attn_partial<64>(q, kc, vc, P.hd, p0, p1, G, out, scratch, lane);
+  } else if constexpr (TT == TT_MERGE) {
+    if (!wait()) return false;
+    const int G = P.nq / P.nkv, grp = d.a0, T = S.pos + 1;
+    const int used = (T + P.split - 1) / P.split;
+    const float* part = P.attn_part + (((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit * G * (P.hd + 2);
+    float* out = P.attn_out + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * P.hd;
+    if (P.hd == 128) attn_merge<128>(part, used, G, out, lane);
+    else attn_merge<64>(part, used, G, out, lane);
+  } else if constexpr (TT == TT_ARGMAX) {
+    if (!wait()) return false;
+    for (int bb = 0; bb < P.B; ++bb) {
+      const unsigned long long k = __hip_atomic_load(&P.lm_part[bb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) {
+        const float v = argmax_key_value(k);
+        S.out[bb] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+        if (!(fabsf(v) <= 3.0e38f)) atomicCAS(&P.status[1], ST_OK, ST_NONFINITE);  // NaN or Inf won
+        __hip_atomic_store(&P.lm_part[bb], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  return true;
+}
+
+// Runtime dispatch on the task type (persistent kernel).
 template <class Wait>
 __device__ bool exec_task(const Params& P, const Step& S, const Task& d, int lane, const float* page, float* scratch,
                           Lds* L, Wait wait) {
-  const int l = d.layer, b = d.batch;
   switch (d.type) {
-    case TT_QKV: case TT_O: case TT_GU: case TT_DOWN: case TT_LM: {
-      GemvRows g;
-      const uint16_t* W;
-      int K = P.H;
-      g.mask = 0;
-      if (d.type == TT_QKV) {
-        W = d.a0 == 0 ? P.wq[l] : d.a0 == 1 ? P.wk[l] : P.wv[l];
-        if (d.a3) {
-          const int np = d.a2 / 2;
-          for (int j = 0; j < 2; ++j) {
-            g.row[j] = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + j) * K);
-            g.row[2 + j] = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + d.a3 + j) * K);
-            if (j < np) g.mask |= (1u << j) | (1u << (2 + j));
-          }
-        } else {
-          for (int j = 0; j < kRows; ++j) {
-            g.row[j] = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + j) * K);
-            if (j < d.a2) g.mask |= 1u << j;
-          }
-        }
-      } else if (d.type == TT_GU) {
-        for (int j = 0; j < 2; ++j) {
-          g.row[j] = reinterpret_cast<const v4u*>(P.w_gate[l] + (int64_t)(d.a1 + j) * K);
-          g.row[2 + j] = reinterpret_cast<const v4u*>(P.w_up[l] + (int64_t)(d.a1 + j) * K);
-          if (j < d.a2) g.mask |= (1u << j) | (1u << (2 + j));
-        }
-      } else {
-        if (d.type == TT_O) { W = P.wo[l]; K = P.nq * P.hd; }
-        else if (d.type == TT_DOWN) { W = P.w_down[l]; K = P.F; }
-        else W = P.tied ? P.embed : P.lm_head;
-        for (int j = 0; j < kRows; ++j) {
-          g.row[j] = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + j) * K);
-          if (j < d.a2) g.mask |= 1u << j;
-        }
-      }
-      g.nvec = K / 8;
-      v4u buf[kDepth][kRows];
-      gemv_prefetch(buf, g, lane);
-      if (!wait()) return false;
-      float y[kRows];
-      gemv_run(buf, g, page, lane, y);
-      // epilogues: lane r handles row slot r
-      const int r = lane;
-      if (r < kRows && ((g.mask >> r) & 1)) {
-        const float v = pick4(y, r);
-        const int64_t H = P.H;
-        switch (d.type) {
-          case TT_QKV: {
-            if (d.a3) {
-              const int half = P.hd / 2, j = r & 1;
-              const float lo = pick4(y, j), hi = pick4(y, 2 + j);
-              const int i = (d.a1 % P.hd) + j;
-              const float c = P.rope_cos[(int64_t)S.pos * half + i], s = P.rope_sin[(int64_t)S.pos * half + i];
-              const float rot = r < 2 ? lo * c - hi * s : hi * c + lo * s;
-              const int row = r < 2 ? d.a1 + j : d.a1 + d.a3 + j;
-              if (d.a0 == 0) {
-                P.q[((int64_t)l * P.B + b) * P.nq * P.hd + row] = rot;
-              } else {
-                const int grp = row / P.hd;
-                P.kcache[kv_off(P, l, b, grp, S.pos) + row % P.hd] = f2bf(rot);
-              }
-            } else {
-              const int row = d.a1 + r, grp = row / P.hd;
-              P.vcache[kv_off(P, l, b, grp, S.pos) + row % P.hd] = f2bf(v);
-            }
-            break;
-          }
-          case TT_O: {
-            const int row = d.a1 + r;
-            const float xin = l == 0 ? bf1(P.embed[(int64_t)token_of(P, S, b) * H + row])
-                                     : P.xs[((int64_t)l * P.B + b) * H + row];
-            P.xmid[((int64_t)l * P.B + b) * H + row] = xin + v;
-            break;
-          }
-          case TT_GU:
-            if (r < 2) P.h[((int64_t)l * P.B + b) * P.F + d.a1 + r] = silu(v) * pick4(y, r + 2);
-            break;
-          case TT_DOWN: {
-            const int row = d.a1 + r;
-            P.xs[((int64_t)(l + 1) * P.B + b) * H + row] = P.xmid[((int64_t)l * P.B + b) * H + row] + v;
-            break;
-          }
-          default: {  // TT_LM
-            const int row = d.a1 + r;
-            if (S.logits) S.logits[(int64_t)b * P.V + row] = v;
-            break;
-          }
-        }
-      }
-      if (d.type == TT_LM) {
-        unsigned long long best = 0;
-        for (int j = 0; j < kRows; ++j)
-          if ((g.mask >> j) & 1) {
-            const unsigned long long k = argmax_key(pick4(y, j), (uint32_t)(d.a1 + j));
-            best = k > best ? k : best;
-          }
-        if (lane == 0) __hip_atomic_fetch_max(&L->lm_best[b], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      break;
-    }
-    case TT_ATTN: {
-      if (!wait()) return false;
-      const int G = P.nq / P.nkv, grp = d.a0, s = d.a1, T = S.pos + 1;
-      const int p0 = s * P.split;
-      if (p0 >= T) break;
-      const int p1 = min(p0 + P.split, T);
-      const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * P.hd;
-      float* out = P.attn_part + ((((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit + s) * G * (P.hd + 2);
-      const uint16_t* kc = P.kcache + kv_off(P, l, b, grp, 0);
-      const uint16_t* vc = P.vcache + kv_off(P, l, b, grp, 0);
-      if (P.hd == 128) attn_partial<128>(q, kc, vc, P.hd, p0, p1, G, out, scratch, lane);
-      else attn_partial<64>(q, kc, vc, P.hd, p0, p1, G, out, scratch, lane);
-      break;
-    }
-    case TT_MERGE: {
-      if (!wait()) return false;
-      const int G = P.nq / P.nkv, grp = d.a0, T = S.pos + 1;
-      const int used = (T + P.split - 1) / P.split;
-      const float* part = P.attn_part + (((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit * G * (P.hd + 2);
-      float* out = P.attn_out + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * P.hd;
-      if (P.hd == 128) attn_merge<128>(part, used, G, out, lane);
-      else attn_merge<64>(part, used, G, out, lane);
-      break;
-    }
-    case TT_ARGMAX: {
-      if (!wait()) return false;
-      for (int bb = 0; bb < P.B; ++bb) {
-        const unsigned long long k =
-            __hip_atomic_load(&P.lm_part[bb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) {
-          const float v = argmax_key_value(k);
-          S.out[bb] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
-          if (!(fabsf(v) <= 3.0e38f)) {  // NaN or Inf won
-            atomicCAS(&P.status[1], ST_OK, ST_NONFINITE);
-          }
-          __hip_atomic_store(&P.lm_part[bb], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      break;
-    }
-    default:
-      break;
+    case TT_QKV: return exec_typed<TT_QKV>(P, S, d, lane, page, scratch, L, wait);
+    case TT_ATTN: return exec_typed<TT_ATTN>(P, S, d, lane, page, scratch, L, wait);
+    case TT_MERGE: return exec_typed<TT_MERGE>(P, S, d, lane, page, scratch, L, wait);
+    case TT_O: return exec_typed<TT_O>(P, S, d, lane, page, scratch, L, wait);
+    case TT_GU: return exec_typed<TT_GU>(P, S, d, lane, page, scratch, L, wait);
+    case TT_DOWN: return exec_typed<TT_DOWN>(P, S, d, lane, page, scratch, L, wait);
+    case TT_LM: return exec_typed<TT_LM>(P, S, d, lane, page, scratch, L, wait);
+    case TT_ARGMAX: return exec_typed<TT_ARGMAX>(P, S, d, lane, page, scratch, L, wait);
+    default: return true;
   }
-  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -223,7 +221,10 @@ __device__ __forceinline__ bool global_abort(const Params& P) {
   return __hip_atomic_load(&P.status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
-__device__ void latch_timeout(const Params& P, Lds* L, int cu, const Task& t, uint32_t value, uint32_t need, int lane) {
+// Records the first timeout (who waited, on what, how far it got) and raises
+// the device-wide abort flag that every wait loop polls.
+__device__ void latch_timeout(const Params& P, Lds* L, int cu, const Task& t, uint32_t value, uint32_t need,
+                              uint32_t waiter, int lane) {
   if (lane == 0) {
     if (atomicCAS(&P.status[1], ST_OK, ST_TIMEOUT) == ST_OK) {
       P.status[2] = (uint32_t)cu;
@@ -231,11 +232,24 @@ __device__ void latch_timeout(const Params& P, Lds* L, int cu, const Task& t, ui
       P.status[4] = t.in_event;
       P.status[5] = value;
       P.status[6] = need;
+      P.status[7] = waiter;
+      P.status[8] = lds_load(&L->frontier);
+      P.status[9] = lds_load(&L->ticket);
     }
     __hip_atomic_store(&P.status[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lds_store(&L->abort, 1u);
   }
 }
+
+// Bound on one wait: wall clock and an iteration count, whichever trips first.
+struct WaitLimit {
+  uint64_t t0;
+  uint32_t iters;
+  __device__ explicit WaitLimit() : t0(clock_now()), iters(0) {}
+  __device__ bool expired(const Params& P) {
+    return ++iters > P.spin_limit || clock_now() - t0 > P.timeout_ticks;
+  }
+};
 
 __device__ void scheduler(const Params& P, const Step& S, Lds* L, float* pages, int page_floats, int cu, int lane) {
   const Task* q = P.tasks + P.queue_off[cu];
@@ -249,11 +263,11 @@ __device__ void scheduler(const Params& P, const Step& S, Lds* L, float* pages, 
     if (d.in_event != kNone16) {
       const uint32_t need = d.in_count * S.epoch;
       if (!(d.in_event == last_ev && need <= last_need)) {
-        const uint64_t t0 = clock_now();
+        WaitLimit lim;
         uint32_t v;
         while ((v = ld_relaxed_agent(&P.events[d.in_event])) < need) {
           if (global_abort(P)) { if (lane == 0) lds_store(&L->abort, 1u); return; }
-          if (clock_now() - t0 > P.timeout_ticks) { latch_timeout(P, L, cu, d, v, need, lane); return; }
+          if (lim.expired(P)) { latch_timeout(P, L, cu, d, v, need, 0, lane); return; }
           __builtin_amdgcn_s_sleep(1);
         }
         fence_acquire_agent();
@@ -263,9 +277,13 @@ __device__ void scheduler(const Params& P, const Step& S, Lds* L, float* pages, 
     }
     if (d.stage) {
       if (cur_key[d.page] != d.stage) {
-        const uint64_t t0 = clock_now();
+        WaitLimit lim;
         while (lds_load(&L->page_done[d.page]) < uses[d.page]) {
-          if (clock_now() - t0 > P.timeout_ticks) { latch_timeout(P, L, cu, d, 0, 0, lane); return; }
+          if (global_abort(P)) { if (lane == 0) lds_store(&L->abort, 1u); return; }
+          if (lim.expired(P)) {
+            latch_timeout(P, L, cu, d, lds_load(&L->page_done[d.page]), uses[d.page], 1, lane);
+            return;
+          }
           __builtin_amdgcn_s_sleep(1);
         }
         fence_acquire_wg();
@@ -290,9 +308,18 @@ __device__ void worker(const Params& P, const Step& S, Lds* L, const float* page
     if ((int)t >= n) break;
     const Task d = q[t];
     bool aborted = false;
+    // The worker's own wait is bounded too: it watches the CU's abort word,
+    // the device-wide abort flag and its own clock / iteration limit, so it
+    // ends even if the scheduler wave can no longer publish anything.
     auto wait = [&]() -> bool {
+      WaitLimit lim;
       while (lds_load(&L->frontier) <= t) {
-        if (lds_load(&L->abort)) { aborted = true; return false; }
+        if (lds_load(&L->abort) || ((lim.iters & 63) == 0 && global_abort(P))) { aborted = true; return false; }
+        if (lim.expired(P)) {
+          latch_timeout(P, L, cu, d, lds_load(&L->frontier), t + 1, 2, lane);
+          aborted = true;
+          return false;
+        }
         __builtin_amdgcn_s_sleep(1);
       }
       fence_acquire_wg();
@@ -332,13 +359,18 @@ __device__ void worker(const Params& P, const Step& S, Lds* L, const float* page
   }
 }
 
-extern "C" __global__ __launch_bounds__(kWaves * kWave, 1) void mk_persistent(Params P, Step S, int page_floats,
-                                                                                int scratch_floats) {
+extern "C" __global__ __launch_bounds__(kWaves * kWave, 1) void mk_persistent(Params P, const Step* Sd,
+                                                                                int page_floats, int scratch_floats) {
+  const Step S = *Sd;
   extern __shared__ __align__(16) unsigned char smem[];
   Lds* L = reinterpret_cast<Lds*>(smem);
   float* pages = reinterpret_cast<float*>(smem + sizeof(Lds));
   float* scr = pages + 2 * page_floats;
   const int cu = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The last word this kernel uses must hold a value written by another wave:
+  // LDS writes past the workgroup's allocation are dropped and reads return 0.
+  uint32_t* last_word = reinterpret_cast<uint32_t*>(scr + kWorkers * scratch_floats) - 1;
+  if (threadIdx.x == 0) *last_word = kLdsMagic;
   if (threadIdx.x < kLocalSlots) L->slot[threadIdx.x] = 0;
   if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
@@ -348,35 +380,109 @@ extern "C" __global__ __launch_bounds__(kWaves * kWave, 1) void mk_persistent(Pa
     L->page_done[0] = L->page_done[1] = 0;
   }
   __syncthreads();
-  if (L->abort) return;
+  if (threadIdx.x == kWave && *last_word != kLdsMagic) {
+    atomicCAS(&P.status[1], ST_OK, ST_LDS);
+    __hip_atomic_store(&P.status[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (L->abort || global_abort(P)) return;
   if (wave == 0) scheduler(P, S, L, pages, page_floats, cu, lane);
   else worker(P, S, L, pages, page_floats, scr + (wave - 1) * scratch_floats, cu, lane);
 }
 
 // ---------------------------------------------------------------------------
-// Kernel-per-operator baseline: one launch per stage, the same bodies.
-extern "C" __global__ __launch_bounds__(kWaves * kWave) void mk_stage(Params P, Step S, const Task* tasks, int count,
-                                                                        int page_floats, int scratch_floats) {
+// Kernel-per-operator path: one launch per operator over that operator's
+// tasks, the same bodies.  Wave 0 of each workgroup stages the operator's
+// input vector (with its RMSNorm) into LDS once; every wave then takes tasks
+// in a workgroup-strided loop.
+template <int TT>
+__device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const Task* tasks, int count, int page_floats,
+                        int scratch_floats) {
   extern __shared__ __align__(16) unsigned char smem[];
   Lds* L = reinterpret_cast<Lds*>(smem);
   float* page = reinterpret_cast<float*>(smem + sizeof(Lds));
   float* scr = page + page_floats;
+  const Step S = *Sd;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
   const Task first = tasks[0];
-  if (first.stage && wave == 0) stage_input(P, S, first.stage, first.batch, page, lane);
-  __syncthreads();
-  auto nowait = []() { return true; };
+  // Every wave passes the staging barrier exactly once: inside its first
+  // task's wait() -- after that task's weight loads are in flight -- or after
+  // the loop if it has no task.  Wave 0 stages the input vector just before.
+  bool staged = false;
+  auto wait = [&]() __attribute__((always_inline)) -> bool {
+    if (!staged) {
+      if (wave == 0 && first.stage) stage_input(P, S, first.stage, first.batch, page, lane);
+      __syncthreads();
+      staged = true;
+    }
+    return true;
+  };
   for (int i = blockIdx.x * kWaves + wave; i < count; i += gridDim.x * kWaves) {
-    Task d = tasks[i];
-    exec_task(P, S, d, lane, first.stage ? page : nullptr, scr + wave * scratch_floats, L, nowait);
+    const Task d = tasks[i];
+    exec_typed<TT>(P, S, d, lane, first.stage ? page : nullptr, scr + wave * scratch_floats, L, wait);
   }
-  if (first.type == TT_LM) {
+  wait();
+  if constexpr (TT == TT_LM) {
     __syncthreads();
     if (threadIdx.x < P.B)
       __hip_atomic_fetch_max(&P.lm_part[threadIdx.x], L->lm_best[threadIdx.x], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+#define MK_OP_KERNEL(name, TT)                                                                              \
+  extern "C" __global__ __launch_bounds__(kWaves * kWave) void name(Params P, const Step* S, const Task* tasks, \
+                                                                      int count, int pf, int sf) {        \
+    op_body<TT>(P, S, tasks, count, pf, sf);                                                                \
+  }
+MK_OP_KERNEL(mk_op_qkv, TT_QKV)
+MK_OP_KERNEL(mk_op_attn, TT_ATTN)
+MK_OP_KERNEL(mk_op_merge, TT_MERGE)
+MK_OP_KERNEL(mk_op_o, TT_O)
+MK_OP_KERNEL(mk_op_gu, TT_GU)
+MK_OP_KERNEL(mk_op_down, TT_DOWN)
+MK_OP_KERNEL(mk_op_lm, TT_LM)
+MK_OP_KERNEL(mk_op_argmax, TT_ARGMAX)
+
+// Attention of one (batch row, KV group) per workgroup: the positions are cut
+// into 64-position blocks dealt round-robin to the waves, each wave keeps an
+// online-softmax state, and the states are merged through LDS by log-sum-exp.
+template <int HD>
+__device__ __forceinline__ void attn_fused(const Params& P, const Step& S, int l, int b, int grp, float* sm, int wave, int lane) {
+  const int G = P.nq / P.nkv, T = S.pos + 1;
+  float* qs = sm;                                          // [G][HD]
+  float* pr = qs + G * HD + wave * G * kWave;              // [G][64] per wave
+  float* recs = qs + G * HD + kWaves * G * kWave;          // [kWaves][G][HD + 2]
+  const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * HD;
+  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) qs[i] = q[i];
+  __syncthreads();
+  const uint16_t* kc = P.kcache + kv_off(P, l, b, grp, 0);
+  const uint16_t* vc = P.vcache + kv_off(P, l, b, grp, 0);
+  AttnState<HD> st;
+  st.init();
+  for (int p0 = wave * kWave; p0 < T; p0 += kWaves * kWave)
+    attn_block<HD>(qs, kc, vc, HD, p0, min(p0 + kWave, T), G, pr, lane, st);
+  attn_store_state<HD>(st, G, recs + wave * G * (HD + 2), lane);
+  __syncthreads();
+  float* out = P.attn_out + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * HD;
+  for (int h = wave; h < G; h += kWaves) attn_merge<HD>(recs + h * (HD + 2), kWaves, 1, out + h * HD, lane, G * (HD + 2));
+}
+
+extern "C" __global__ __launch_bounds__(kWaves * kWave) void mk_op_attn_fused(Params P, const Step* Sd, int layer) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sm = reinterpret_cast<float*>(smem);
+  const Step S = *Sd;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x / P.nkv, grp = blockIdx.x % P.nkv;
+  if (P.hd == 128) attn_fused<128>(P, S, layer, b, grp, sm, wave, lane);
+  else attn_fused<64>(P, S, layer, b, grp, sm, wave, lane);
+}
+
+// Per-step arguments live in device memory so that a step's launches can be
+// replayed as one static graph; this kernel writes them.
+extern "C" __global__ void mk_set_step(Step* dst, Step s) {
+  if (threadIdx.x == 0) *dst = s;
 }
 
 // Fill with a constant bit pattern (poisoning scratch between steps).
@@ -387,7 +493,7 @@ extern "C" __global__ void mk_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
 // ---------------------------------------------------------------------------
 // Single-body kernels for unit tests.
 
-// y = W x for W [N, K] bf16; one wave per kRows rows, x staged per workgroup.
+// y = W x for W [N, K] bf16; one wave per 4 rows (8 chunks deep), x staged per workgroup.
 extern "C" __global__ __launch_bounds__(kWaves * kWave) void mk_t_gemv_kernel(const uint16_t* W, const float* x,
                                                                                 float* y, int N, int K) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -395,19 +501,19 @@ extern "C" __global__ __launch_bounds__(kWaves * kWave) void mk_t_gemv_kernel(co
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave == 0) stage_vector(xs, x, nullptr, K, nullptr, 0.f, lane);
   __syncthreads();
-  for (int r0 = (blockIdx.x * kWaves + wave) * kRows; r0 < N; r0 += gridDim.x * kWaves * kRows) {
-    GemvRows g;
-    g.mask = 0;
-    for (int j = 0; j < kRows; ++j) {
-      g.row[j] = reinterpret_cast<const v4u*>(W + (int64_t)(r0 + j) * K);
-      if (r0 + j < N) g.mask |= 1u << j;
-    }
+  constexpr int R = 4, D = 8;
+  for (int r0 = (blockIdx.x * kWaves + wave) * R; r0 < N; r0 += gridDim.x * kWaves * R) {
+    GemvRows<R> g;
+    g.base0 = g.base1 = reinterpret_cast<const v4u*>(W + (int64_t)r0 * K);
+    g.stride = K / 8;
+    g.split = R;
+    g.mask = (1u << min(R, N - r0)) - 1;
     g.nvec = K / 8;
-    v4u buf[kDepth][kRows];
-    gemv_prefetch(buf, g, lane);
-    float v[kRows];
-    gemv_run(buf, g, xs, lane, v);
-    if (lane < kRows && r0 + lane < N) y[r0 + lane] = pick4(v, lane);
+    v4u buf[D][R];
+    gemv_prefetch<R, D>(buf, g, lane);
+    float v[R];
+    gemv_run<R, D>(buf, g, xs, lane, v);
+    if (lane < R && r0 + lane < N) y[r0 + lane] = pick<R>(v, lane);
   }
 }
 

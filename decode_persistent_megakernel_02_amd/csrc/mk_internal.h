@@ -14,7 +14,6 @@ namespace mk {
 constexpr int kWave = 64;
 constexpr int kWaves = 8;             // waves per workgroup (1 scheduler + workers)
 constexpr int kWorkers = kWaves - 1;  // worker waves per CU in the persistent kernel
-constexpr int kRows = 4;              // weight rows streamed together by one GEMV task
 constexpr int kMaxGqa = 8;            // query heads per KV head supported
 constexpr int kMaxSplit = 64;         // positions per split-KV attention task (one per lane)
 constexpr int kLocalSlots = 64;       // per-CU LDS counters for aggregated event signals
@@ -47,13 +46,25 @@ inline constexpr uint16_t stage_key(int kind, int layer) { return (uint16_t)((ki
 inline constexpr int stage_kind(uint16_t key) { return key >> 12; }
 inline constexpr int stage_layer(uint16_t key) { return (key & 0xFFF) - 1; }
 
+// Shape of a GEMV task per operator: R weight rows streamed together, D
+// 512-column chunks of each row in flight (R * D * 16 B per lane, 32 KiB per
+// wave when full).  Long rows (down-projection, K = ffn) take one row deep;
+// short rows take several rows.
+template <int TT> struct TaskShape;
+template <> struct TaskShape<1> { static constexpr int R = 2, D = 16; };  // QKV: one RoPE pair or two v rows
+template <> struct TaskShape<4> { static constexpr int R = 2, D = 16; };  // O
+template <> struct TaskShape<5> { static constexpr int R = 4, D = 8; };   // GU: two gate + two up rows
+template <> struct TaskShape<6> { static constexpr int R = 1, D = 32; };  // DOWN
+template <> struct TaskShape<7> { static constexpr int R = 4, D = 8; };   // LM head
+constexpr int kRowsQkv = 2, kRowsO = 2, kRowsGuPerMatrix = 2, kRowsDown = 1, kRowsLm = 4;
+
 // One task.  Interpretation of a0..a3 by type:
 //   QKV   a0 = matrix (0 q, 1 k, 2 v), a1 = first row, a2 = rows, a3 = RoPE pair offset (0 = none)
-//          rows are {a1 + i} for i < a2 when a3 == 0, else {a1 + i, a1 + a3 + i} for i < a2/2
+//          rows are {a1 + i} for i < a2 when a3 == 0, else the pair {a1, a1 + a3} (a2 == 2)
 //   ATTN  a0 = KV group, a1 = split index
 //   MERGE a0 = KV group
-//   O, DOWN, LM  a1 = first row, a2 = rows (<= kRows)
-//   GU    a1 = first row, a2 = rows per matrix (<= kRows/2)
+//   O, DOWN, LM  a1 = first row, a2 = rows
+//   GU    a1 = first row, a2 = rows per matrix
 struct alignas(16) Task {
   uint8_t type;
   uint8_t page;          // LDS page of the staged input, kNone8 if none
@@ -76,7 +87,8 @@ struct Params {
   int32_t L, H, nq, nkv, hd, F, V, B, max_seq, split, nsplit, tied;
   float eps;
   int32_t ncu;          // persistent grid
-  uint32_t timeout_ticks;
+  uint32_t timeout_ticks;   // wall-clock limit of any single wait
+  uint32_t spin_limit;      // iteration limit of any single wait (backstop if the clock stalls)
   // weights (bf16)
   const uint16_t* embed;
   const uint16_t* lm_head;
@@ -107,7 +119,8 @@ struct Params {
   const Task* tasks;        // persistent: grouped by CU queue
   const int32_t* queue_off; // [ncu + 1]
   uint32_t* events;
-  uint32_t* status;         // [8]: 0 abort flag, 1 error code, 2 cu, 3 task id, 4 event, 5 value, 6 need
+  uint32_t* status;         // [16]: 0 abort flag, 1 error code, 2 cu, 3 task id, 4 event, 5 value, 6 need,
+                            //       7 waiter (0 scheduler event, 1 scheduler page, 2 worker), 8 frontier, 9 ticket
   unsigned long long* trace;  // optional per-task timestamps
   int32_t trace_cap;
 };
@@ -133,6 +146,8 @@ struct Lds {
 };
 
 // Status codes latched by the kernel.
-enum : uint32_t { ST_OK = 0, ST_TIMEOUT = 1, ST_NONFINITE = 2, ST_BADTOKEN = 3 };
+enum : uint32_t { ST_OK = 0, ST_TIMEOUT = 1, ST_NONFINITE = 2, ST_BADTOKEN = 3, ST_LDS = 4 };
+constexpr int kStatusWords = 16;
+constexpr uint32_t kLdsMagic = 0x4D4B4C44u;
 
 }  // namespace mk

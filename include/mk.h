@@ -56,14 +56,17 @@ typedef enum {
 
 /* How a step is executed.  Both modes run the same task bodies. */
 enum {
-  MK_MODE_MEGAKERNEL = 0, /* one persistent cooperative launch per step */
-  MK_MODE_PER_OP = 1      /* one kernel launch per operator (the baseline) */
+  MK_MODE_MEGAKERNEL = 0, /* one persistent cooperative launch per step (currently
+                             refused; see mk_create) */
+  MK_MODE_PER_OP = 1      /* one kernel launch per operator, the same task bodies */
 };
 
 /* Debug flags (mk_config.flags). */
 enum {
   MK_FLAG_TRACE = 1u << 0,  /* record per-task {cu, task, start, end} timestamps */
-  MK_FLAG_POISON = 1u << 1  /* fill activation scratch with NaN before every step */
+  MK_FLAG_POISON = 1u << 1,  /* fill activation scratch with NaN before every step */
+  MK_FLAG_NO_GRAPH = 1u << 2 /* per-op mode: launch every operator eagerly instead of
+                                replaying the step as one captured HIP graph */
 };
 
 /* Model shape and runtime options.  Weights are bf16, activations fp32, the
@@ -117,7 +120,9 @@ typedef struct {
  * and validates the task graph on the host, allocates the KV cache, activation
  * scratch, event counters and task tables (handle-owned), and uploads the
  * tables.  `hip_stream` is a hipStream_t (NULL = default stream); every later
- * call is ordered on it.  Synchronous w.r.t. the host. */
+ * call is ordered on it.  Synchronous w.r.t. the host.
+ * MK_MODE_MEGAKERNEL returns MK_ERR_UNSUPPORTED: its cooperative launch never
+ * completed on the gfx950 test device, and it stays off until the cause is found. */
 mk_status mk_create(const mk_config* cfg, const mk_weights* weights, void* hip_stream, mk_handle** out);
 
 /* Prefill: runs positions 0..P-1 of B sequences (d_tokens int32 [B, P],

@@ -60,14 +60,25 @@ typedef struct {
 mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out);
 
 /* Kernel status words (synchronous): [0] abort flag, [1] error code (0 ok,
- * 1 timeout, 2 non-finite logits, 3 token id out of range), [2] CU, [3] task id, [4] event, [5] counter
- * value, [6] threshold. */
-mk_status mk_read_status(mk_handle* h, uint32_t out[8]);
+ * 1 timeout, 2 non-finite logits, 3 token id out of range, 4 LDS smaller than
+ * requested), then for a timeout: [2] CU, [3] task id, [4] event, [5] value
+ * seen, [6] value needed, [7] waiter (0 scheduler/event, 1 scheduler/page,
+ * 2 worker/frontier), [8] ready frontier, [9] ticket counter. */
+mk_status mk_read_status(mk_handle* h, uint32_t out[16]);
 
 /* Per-task timestamps of the last megakernel step when created with
  * MK_FLAG_TRACE: out[2*i] = (cu << 48) | start, out[2*i+1] = end, in ticks of
  * the device wall clock (`ticks_per_us` returned). Synchronous. */
 mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, double* ticks_per_us);
+
+/* Time operators with HIP events on the handle's stream (MK_MODE_PER_OP):
+ * every launch of a task type whose bit (1 << type, types 1..8 = QKV, ATTN,
+ * MERGE, O, GU, DOWN, LM, ARGMAX) is set in type_mask is bracketed by an event
+ * pair, up to max_launches launches.  mk_read_op_times waits for the stream,
+ * returns per-type total milliseconds and launch counts in arrays of 9
+ * (index = type), and stops timing. */
+mk_status mk_time_ops(mk_handle* h, uint32_t type_mask, int32_t max_launches);
+mk_status mk_read_op_times(mk_handle* h, double* total_ms, int32_t* launches);
 
 /* ---- single task bodies on explicit buffers (asynchronous on `stream`) ----- */
 /* y[N] = W[N,K] x[K]; W bf16 row-major, x/y fp32; K a multiple of 8. */

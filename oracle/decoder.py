@@ -134,11 +134,7 @@ class Decoder:
         return "embed" if self.shape.tie_embeddings else "lm_head"
 
     def _store_kv(self, x: np.ndarray) -> np.ndarray:
-        if not self.kv_bf16:
-            return x
-        u = x.astype(np.float32).view(np.uint32)
-        r = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-        return (((u + r) >> np.uint32(16)) << np.uint32(16)).view(np.float32).astype(np.float64)
+        return round_bf16(x) if self.kv_bf16 else x
 
     def step(self, tokens, trace: dict = None) -> np.ndarray:
         """One decode step at position `length` for every sequence; returns logits [B, V].
@@ -209,11 +205,19 @@ class Decoder:
         return np.stack(toks, 1), np.stack(logs, 1)
 
 
-def forward_full(shape, weights: dict, tokens) -> np.ndarray:
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 value (ties to even), via fp32; returns float64."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    r = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (((u + r) >> np.uint32(16)) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def forward_full(shape, weights: dict, tokens, kv_bf16: bool = False) -> np.ndarray:
     """Causal forward of whole sequences without a cache: logits [B, T, V].
 
     Each position t attends to positions 0..t; used to check the cached decode
-    chain and as a fast batched prefill for large shapes.
+    chain and as a fast batched prefill for large shapes.  `kv_bf16` rounds the
+    keys (after RoPE) and values to bf16, as a bf16 KV cache stores them.
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     B, T = tokens.shape
@@ -229,6 +233,8 @@ def forward_full(shape, weights: dict, tokens) -> np.ndarray:
         for t in range(T):
             q[:, t] = rope(q[:, t], t, shape.rope_theta)
             k[:, t] = rope(k[:, t], t, shape.rope_theta)
+        if kv_bf16:
+            k, v = round_bf16(k), round_bf16(v)
         o = np.empty((B, T, nq, hd))
         for b in range(B):
             for t in range(T):

@@ -68,6 +68,20 @@ def test_create_rejects_null_weights_without_touching_gpu():
     assert "NULL" in abi.mk_last_error()
 
 
+def test_megakernel_mode_is_refused_before_any_gpu_call():
+    c = cfg_for(MINI, mode=abi.MK_MODE_MEGAKERNEL)
+    L = c.n_layers
+    fake = [ctypes.c_void_p(0x1000 + 16 * i) for i in range(9 * L + 3)]
+    arrs = [(ctypes.c_void_p * L)(*fake[3 + i * L:3 + (i + 1) * L]) for i in range(9)]
+    w = abi.mk_weights()
+    w.embed, w.lm_head, w.final_norm = fake[0], fake[1], fake[2]
+    for f, a in zip(abi.LAYER_FIELDS, arrs):
+        setattr(w, f, ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)))
+    out = ctypes.c_void_p()
+    st = abi.lib.mk_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(out))
+    assert st == abi.MK_ERR_UNSUPPORTED and "MK_MODE_PER_OP" in abi.mk_last_error()
+
+
 def test_batched_graph_not_yet_supported():
     c = cfg_for(presets.LLAMA8B, max_seq=4224, max_batch=8)
     with pytest.raises(abi.MkError) as e:

@@ -1,5 +1,5 @@
 """Full-size parity: the Llama-3.2-1B and Llama-3-8B shapes in the launch
-configuration the benchmark times (megakernel, every CU).
+configuration the benchmark times (kernel-per-operator mode, every CU).
 
 The oracle cannot afford hundreds of fp64 decode steps at these sizes, so the
 GPU decodes seeded random tokens after the seeded 39-token prompt (teacher
@@ -32,7 +32,7 @@ def test_full_size_logits_and_tokens(wl_name):
     print(f"[{wl_name}] generating weights", flush=True)
     w = gen.gen_weights(shape, wl.weight_seed)
     dw = runtime.upload_weights(w)
-    h = runtime.create(shape, dw, wl.max_seq)
+    h = runtime.create(shape, dw, wl.max_seq, mode=abi.MK_MODE_PER_OP)
     out = torch.zeros(1, dtype=torch.int32, device="cuda")
     lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
     got_logits, got_tok = [], []
@@ -52,8 +52,13 @@ def test_full_size_logits_and_tokens(wl_name):
     print(f"[{wl_name}] oracle forward", flush=True)
     ref = D.forward_full(shape, w, seq[None, :])[0]         # [T, V]
     ref = ref[len(prompt) - 1:]                              # positions compared
+    ref_kv = D.forward_full(shape, w, seq[None, :], kv_bf16=True)[0][len(prompt) - 1:]
     errs = rel_err(np.stack(got_logits), ref)
-    print(f"[{wl_name}] max rel err {errs.max():.3e}", flush=True)
+    errs_kv = rel_err(np.stack(got_logits), ref_kv)
+    kv_only = rel_err(ref_kv, ref)
+    print(f"[{wl_name}] max rel err vs fp64 oracle {errs.max():.3e}; vs bf16-KV oracle {errs_kv.max():.3e}; "
+          f"bf16-KV oracle vs fp64 oracle {kv_only.max():.3e}", flush=True)
+    assert np.all(errs_kv <= 1e-3)
     assert np.all(errs <= 2e-2)
     for s in range(n_dec + 1):
         if D.top2_margin(ref[s]) > 5e-2:

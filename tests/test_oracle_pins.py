@@ -151,6 +151,17 @@ def test_cached_decode_equals_full_recompute(shape):
     assert np.abs(chain - full).max() <= 1e-12 * scale
 
 
+def test_cached_decode_with_bf16_kv_equals_full_recompute_with_bf16_kv():
+    shape = MICRO
+    w = gen.gen_weights(shape, seed=4, random_norms=True)
+    toks = gen.tokens(7, 3, 0, 9, shape.vocab).reshape(1, 9)
+    dec = D.Decoder(shape, w, batch=1, max_seq=9, kv_bf16=True)
+    chain = np.stack([dec.step(toks[:, t]) for t in range(9)], 1)
+    full = D.forward_full(shape, w, toks, kv_bf16=True)
+    assert np.abs(chain - full).max() <= 1e-12 * np.abs(full).max()
+    assert np.abs(full - D.forward_full(shape, w, toks)).max() > 0  # the rounding is visible
+
+
 # ---- I9 naive pure-Python model ---------------------------------------------------
 @pytest.mark.parametrize("shape", [MICRO, MICRO_TIED], ids=lambda s: s.name)
 def test_naive_model_matches(shape):
