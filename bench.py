@@ -30,19 +30,20 @@ METRIC = "ms/token decode (8B shape, batch 1) + achieved HBM GB/s vs peak, 1 MI3
 PEAK_GBPS = 8000.0
 
 
-def step_bytes(shape, T, batch=1):
+def step_bytes(shape, T, batch=1, kv_bytes=4):
     """Algorithmic HBM bytes of one decode step with T cached positions (incl. the new one).
 
     Every weight matrix once, one embedding row per sequence, the norm gains,
-    K and V of T positions read per layer and sequence, the new K/V written.
+    K and V of T positions read per layer and sequence, the new K/V written
+    (kv_bytes per cached element: 4 for the fp32 cache of batch-1 decode).
     """
     s = shape
     qd, kd = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
     per_layer = s.hidden * (qd + 2 * kd) + s.hidden * qd + 3 * s.hidden * s.ffn + 2 * s.hidden
     weights = 2 * (s.n_layers * per_layer + s.vocab * s.hidden + s.hidden)
     emb = 2 * s.hidden * batch
-    kv_read = 2 * 2 * s.n_layers * kd * T * batch
-    kv_write = 2 * 2 * s.n_layers * kd * batch
+    kv_read = 2 * kv_bytes * s.n_layers * kd * T * batch
+    kv_write = 2 * kv_bytes * s.n_layers * kd * batch
     return weights + emb + kv_read + kv_write
 
 

@@ -33,7 +33,8 @@ class mk_config(ctypes.Structure):
                 ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("tie_embeddings", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_seq", ctypes.c_int32), ("mode", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("watchdog_ms", ctypes.c_uint32), ("num_cus", ctypes.c_int32), ("attn_split", ctypes.c_int32)]
+                ("watchdog_ms", ctypes.c_uint32), ("num_cus", ctypes.c_int32), ("attn_split", ctypes.c_int32),
+                ("kv_fp32", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -48,7 +49,7 @@ class mk_weights(ctypes.Structure):
 class mk_kv_layout(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_layer", ctypes.c_int64),
                 ("stride_batch", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("stride_pos", ctypes.c_int64),
-                ("length", ctypes.c_int32), ("batch", ctypes.c_int32)]
+                ("length", ctypes.c_int32), ("batch", ctypes.c_int32), ("elem_bytes", ctypes.c_int32)]
 
 
 class mk_graph_info(ctypes.Structure):
@@ -92,7 +93,7 @@ SIGNATURES = {
     "mk_read_op_times": ([_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
     "mk_t_gemv": ([_P, _P, _P, _I32, _I32, _P], _I32),
     "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
-    "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_argmax": ([_P, _I32, _P, _P], _I32),
     "mk_device_info": ([ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
 }
@@ -122,8 +123,8 @@ def _stream(stream):
     return ctypes.c_void_p(getattr(stream, "cuda_stream", stream) or 0)
 
 
-def make_config(shape, max_seq, max_batch=1, mode=MK_MODE_MEGAKERNEL, flags=0, watchdog_ms=0, num_cus=0,
-                attn_split=0) -> mk_config:
+def make_config(shape, max_seq, max_batch=1, mode=MK_MODE_PER_OP, flags=0, watchdog_ms=0, num_cus=0,
+                attn_split=0, kv_fp32=True) -> mk_config:
     """mk_config from a synth.presets.ModelShape-like object."""
     c = mk_config()
     c.abi_version = MK_ABI_VERSION
@@ -133,6 +134,7 @@ def make_config(shape, max_seq, max_batch=1, mode=MK_MODE_MEGAKERNEL, flags=0, w
     c.tie_embeddings = 1 if shape.tie_embeddings else 0
     c.max_batch, c.max_seq, c.mode, c.flags = max_batch, max_seq, mode, flags
     c.watchdog_ms, c.num_cus, c.attn_split = watchdog_ms, num_cus, attn_split
+    c.kv_fp32 = 1 if kv_fp32 else 0
     return c
 
 
@@ -289,11 +291,12 @@ def mk_t_rmsnorm(x, gamma, eps, y, stream=None):
 
 
 def mk_t_attention(q, k, v, T, split, o, stream=None):
-    """q [nq, hd] fp32; k, v [nkv, S, hd] bf16 (S >= T); o [nq, hd] fp32."""
+    """q [nq, hd] fp32; k, v [nkv, S, hd] bf16 or fp32 (S >= T); o [nq, hd] fp32."""
     nq, hd = q.shape
     nkv, S, _ = k.shape
-    _check(lib.mk_t_attention(_ptr(q), _ptr(k), _ptr(v), S * hd, nq, nkv, hd, T, split, _ptr(o), _stream(stream)),
-           "mk_t_attention")
+    f32 = 1 if k.element_size() == 4 else 0
+    _check(lib.mk_t_attention(_ptr(q), _ptr(k), _ptr(v), S * hd, nq, nkv, hd, T, split, f32, _ptr(o),
+                              _stream(stream)), "mk_t_attention")
 
 
 def mk_t_argmax(x, out, stream=None):

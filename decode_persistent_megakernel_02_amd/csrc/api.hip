@@ -46,7 +46,7 @@ std::string check_config(const mk_config* c) {
   if (c->max_seq < 1) return "max_seq must be >= 1";
   if (c->mode != MK_MODE_MEGAKERNEL && c->mode != MK_MODE_PER_OP) return "unknown mode";
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return "rms_eps must be >= 0 and rope_theta > 0";
-  if (c->attn_split < 0 || c->attn_split > kMaxSplit) return "attn_split must be in [0, 64]";
+  if (c->attn_split < 0 || c->attn_split > kMaxSplit) return "attn_split must be in [0, 4096]";
   if (c->num_cus < 0) return "num_cus must be >= 0";
   if ((int64_t)c->vocab * c->hidden >= (1ll << 40)) return "vocab * hidden too large";
   return "";
@@ -89,7 +89,7 @@ struct mk_handle {
   bool poisoned = false;
   int32_t* d_tok_scratch = nullptr;
   Step* d_step = nullptr;               // per-step arguments, written by mk_set_step
-  int attn_lds = 0;                     // fused per-op attention kernel
+  int attn_lds = 0;                     // per-op split attention kernel
   hipStream_t cap_stream = nullptr;     // private stream used to capture the step graph
   hipGraph_t step_graph = nullptr;
   hipGraphExec_t graph_exec = nullptr;
@@ -171,14 +171,18 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
     const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
     if (count <= 0) continue;
     const int type = g.stage_type[s];
-    if (type == TT_MERGE) continue;  // merged inside the fused attention kernel
     const bool timed = timed_ok && ((h->timed_mask >> type) & 1) && 2 * (h->ev_used + 1) <= (int)h->ev_pool.size();
     if (timed) HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used], st));
-    if (type == TT_ATTN) {
+    if (type == TT_ATTN || type == TT_MERGE) {
       int layer = g.tasks[b0].layer;
       void* args[] = {&Pc, &sp, &layer};
-      HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_fused), dim3(h->P.B * h->P.nkv),
-                              dim3(kWaves * kWave), args, (size_t)h->attn_lds, st));
+      if (type == TT_ATTN)
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_split),
+                                dim3(h->P.B * h->P.nkv * h->P.nsplit), dim3(kAttnWaves * kWave), args,
+                                (size_t)h->attn_lds, st));
+      else
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(h->P.B * h->P.nkv),
+                                dim3((h->P.nq / h->P.nkv) * kWave), args, 0, st));
     } else {
       const int grid = std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]);
       const Task* tasks = h->d_stage_tasks + b0;
@@ -303,6 +307,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   Params& P = h->P;
   P.L = L; P.H = H; P.nq = nq; P.nkv = nkv; P.hd = hd; P.F = F; P.V = V; P.B = B; P.max_seq = S;
   P.split = gc.split; P.nsplit = g.nsplit; P.tied = cfg->tie_embeddings ? 1 : 0; P.eps = cfg->rms_eps;
+  P.kv_f32 = cfg->kv_fp32 ? 1 : 0;
   P.ncu = ncu;
   const double wd_ms = cfg->watchdog_ms ? cfg->watchdog_ms : 2000.0;
   P.timeout_ticks = (uint32_t)std::min(4.0e9, wd_ms * 1000.0 * tpu);
@@ -326,11 +331,16 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   P.w_down = d_ptrs + 8 * L;
 
   // KV cache
-  const int64_t kv_elems = (int64_t)L * B * nkv * S * hd;
-  MK_TRY(h->alloc(&P.kcache, kv_elems));
-  MK_TRY(h->alloc(&P.vcache, kv_elems));
-  HIP_TRY(hipMemset(P.kcache, 0, kv_elems * 2));
-  HIP_TRY(hipMemset(P.vcache, 0, kv_elems * 2));
+  const int64_t kv_elems = (int64_t)L * B * nkv * S * hd, kv_bytes = kv_elems * (P.kv_f32 ? 4 : 2);
+  {
+    uint8_t *kc = nullptr, *vc = nullptr;
+    MK_TRY(h->alloc(&kc, kv_bytes));
+    MK_TRY(h->alloc(&vc, kv_bytes));
+    HIP_TRY(hipMemset(kc, 0, kv_bytes));
+    HIP_TRY(hipMemset(vc, 0, kv_bytes));
+    P.kcache = kc;
+    P.vcache = vc;
+  }
 
   // activations, one allocation
   const int64_t n_xs = (int64_t)(L + 1) * B * H, n_xmid = (int64_t)L * B * H, n_q = (int64_t)L * B * nq * hd;
@@ -407,9 +417,9 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, op_kernel(t), kWaves * kWave, h->op_lds[t]));
     h->op_grid_cap[t] = std::max(1, nb) * ncu;
   }
-  h->attn_lds = (G * hd + kWaves * G * kWave + kWaves * G * (hd + 2)) * 4;
+  h->attn_lds = (G * hd + kAttnWaves * G * kWave + kAttnWaves * G * (hd + 2)) * 4;
   if (h->attn_lds > max_lds) return fail(MK_ERR_UNSUPPORTED, "attention LDS need exceeds the device limit");
-  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_op_attn_fused),
+  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_op_attn_split),
                               hipFuncAttributeMaxDynamicSharedMemorySize, h->attn_lds));
   if (h->lds_mega > max_lds)
     return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(h->lds_mega) + " B exceeds " + std::to_string(max_lds));
@@ -533,6 +543,7 @@ mk_status mk_kv_view(mk_handle* h, mk_kv_layout* out) {
   out->stride_layer = (int64_t)P.B * out->stride_batch;
   out->length = h->length;
   out->batch = h->batch;
+  out->elem_bytes = P.kv_f32 ? 4 : 2;
   return MK_OK;
 }
 
@@ -707,7 +718,7 @@ mk_status mk_t_rmsnorm(const float* x, const void* gamma, float eps, float* y, i
 }
 
 mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t head_stride, int32_t nq, int32_t nkv,
-                         int32_t hd, int32_t T, int32_t split, float* o, void* stream) {
+                         int32_t hd, int32_t T, int32_t split, int32_t kv_f32, float* o, void* stream) {
   g_err.clear();
   if (!q || !k || !v || !o || nq < 1 || nkv < 1 || nq % nkv || nq / nkv > kMaxGqa || (hd != 64 && hd != 128) ||
       T < 1 || split < 1 || split > kMaxSplit || head_stride < (int64_t)T * hd)
@@ -717,9 +728,9 @@ mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t h
   float* part = nullptr;
   HIP_TRY(hipMalloc(&part, (size_t)nkv * nsplit * G * (hd + 2) * 4));
   const unsigned lds = (unsigned)((G * hd + G * kWave) * 4);
-  hipLaunchKernelGGL(mk_t_attn_partial_kernel, dim3(nkv * nsplit), dim3(kWave), lds, st, q,
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), head_stride, nq, nkv, hd, T,
-                     split, nsplit, part);
+  const int f32 = kv_f32 ? 1 : 0;
+  hipLaunchKernelGGL(mk_t_attn_partial_kernel, dim3(nkv * nsplit), dim3(kWave), lds, st, q, k, v, head_stride, nq,
+                     nkv, hd, T, split, nsplit, f32, part);
   hipLaunchKernelGGL(mk_t_attn_merge_kernel, dim3(nkv), dim3(kWave), 0, st, part, nq, nkv, hd, T, split, nsplit, o);
   hipError_t e = hipStreamSynchronize(st);
   (void)hipFree(part);

@@ -214,10 +214,25 @@ __device__ __forceinline__ void stage_vector(float* page, const float* src, cons
 // ---------------------------------------------------------------------------
 // Split-KV decode attention (online softmax).  One wave owns a running state
 // for the G query heads of a KV group: max score m, sum of exp(score - m) l,
-// and the unnormalised output o (each lane owns DPL = HD/64 dims).  A block
-// is at most 64 positions: lane j scores position p0 + j against all G heads
-// (its whole K row is loaded at once), then every lane accumulates its dims
-// of V over the block's positions, with 32 rows of loads in flight.
+// and the unnormalised output o (each lane owns DPL = HD/64 dims).  The cache
+// element type KT is bf16 (uint16_t) or fp32 (float).
+//
+// A block covers NP positions.  For the scores, LPP lanes share one position
+// (each lane holds HD/LPP elements = at most 256 bytes of the K row, loaded
+// with 16-byte loads); their partial dot products are combined with a DPP
+// swap.  For the values, every lane owns DPL dims of every position.  K and V
+// of the whole block are loaded up front, so a block costs one memory round
+// trip.
+template <int HD, typename KT>
+struct AttnGeom {
+  static constexpr int ROW_BYTES = HD * (int)sizeof(KT);
+  static constexpr int LPP = ROW_BYTES > 256 ? ROW_BYTES / 256 : 1;  // lanes per position (1 or 2)
+  static constexpr int NP = kWave / LPP;                               // positions per block
+  static constexpr int EPL = HD / LPP;                                 // K elements per lane
+  static constexpr int KV16 = EPL * (int)sizeof(KT) / 16;             // 16-byte K loads per lane
+  static constexpr int DPL = HD / kWave;                               // V dims per lane
+};
+
 template <int HD>
 struct AttnState {
   static constexpr int DPL = HD / kWave;
@@ -233,78 +248,105 @@ struct AttnState {
   }
 };
 
-// qs: LDS [G][HD] (the rotated queries); pr: LDS [G][64] scratch.
-template <int HD>
-__device__ __forceinline__ void attn_block(const float* qs, const uint16_t* kc, const uint16_t* vc, int64_t pos_stride, int p0,
-                           int p1, int G, float* pr, int lane, AttnState<HD>& st) {
-  constexpr int DPL = HD / kWave, NV = HD / 8;
-  const int np = p1 - p0;
-  const float scale = 1.0f / sqrtf((float)HD);
-  v4u k8[NV];
-  if (lane < np) {
-    const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)(p0 + lane) * pos_stride);
-#pragma unroll
-    for (int d8 = 0; d8 < NV; ++d8) k8[d8] = krow[d8];
+// 8 K elements at a 16-byte vector (bf16: one vector; fp32: two vectors).
+template <typename KT>
+__device__ __forceinline__ float dot_k(const v4u* kv, int i, const float* q, float acc) {
+  const float4 a = *reinterpret_cast<const float4*>(q);
+  const float4 b = *reinterpret_cast<const float4*>(q + 4);
+  if constexpr (sizeof(KT) == 2) {
+    return dot8(kv[i], a, b, acc);
+  } else {
+    const v4u u = kv[2 * i], w = kv[2 * i + 1];
+    acc = fmaf(__uint_as_float(u.x), a.x, acc);
+    acc = fmaf(__uint_as_float(u.y), a.y, acc);
+    acc = fmaf(__uint_as_float(u.z), a.z, acc);
+    acc = fmaf(__uint_as_float(u.w), a.w, acc);
+    acc = fmaf(__uint_as_float(w.x), b.x, acc);
+    acc = fmaf(__uint_as_float(w.y), b.y, acc);
+    acc = fmaf(__uint_as_float(w.z), b.z, acc);
+    return fmaf(__uint_as_float(w.w), b.w, acc);
   }
+}
+
+// qs: LDS [G][HD] (rotated queries); pr: LDS [G][64] scratch of this wave.
+// kc, vc: this group's cache rows (position p at + p * HD elements).
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_block(const float* qs, const KT* kc, const KT* vc, int p0, int p1, int G,
+                                           float* pr, int lane, AttnState<HD>& st) {
+  using Gm = AttnGeom<HD, KT>;
+  constexpr int DPL = Gm::DPL, NP = Gm::NP, LPP = Gm::LPP, EPL = Gm::EPL, KV16 = Gm::KV16;
+  const int np = p1 - p0;
+  const int my = lane / LPP, part = lane % LPP;  // position and row part this lane scores
+  // K: this lane's part of its position's row; V: this lane's dims of every position
+  v4u kr[KV16];
+  if (my < np) {
+    const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)(p0 + my) * HD + part * EPL);
+#pragma unroll
+    for (int i = 0; i < KV16; ++i) kr[i] = krow[i];
+  }
+  constexpr int VW = (DPL * (int)sizeof(KT) + 3) / 4;  // 32-bit words of V per lane and position
+  uint32_t vr[NP][VW];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    if (j < np) {
+      const KT* vrow = vc + (int64_t)(p0 + j) * HD + lane * DPL;
+      if constexpr (sizeof(KT) == 2 && DPL == 1) {
+        vr[j][0] = reinterpret_cast<const uint16_t*>(vrow)[0];
+      } else {
+#pragma unroll
+        for (int w = 0; w < VW; ++w) vr[j][w] = reinterpret_cast<const uint32_t*>(vrow)[w];
+      }
+    }
+  }
+  const float scale = 1.0f / sqrtf((float)HD);
   float sc[kMaxGqa];
 #pragma unroll
   for (int h = 0; h < kMaxGqa; ++h) sc[h] = 0.f;
-  if (lane < np) {
+  if (my < np) {
 #pragma unroll
-    for (int d8 = 0; d8 < NV; ++d8) {
+    for (int i = 0; i < EPL / 8; ++i) {
 #pragma unroll
-      for (int h = 0; h < kMaxGqa; ++h) {
-        if (h < G) {
-          const float4 a = *reinterpret_cast<const float4*>(qs + h * HD + d8 * 8);
-          const float4 b = *reinterpret_cast<const float4*>(qs + h * HD + d8 * 8 + 4);
-          sc[h] = dot8(k8[d8], a, b, sc[h]);
-        }
-      }
+      for (int h = 0; h < kMaxGqa; ++h)
+        if (h < G) sc[h] = dot_k<KT>(kr, i, qs + h * HD + part * EPL + i * 8, sc[h]);
     }
   }
 #pragma unroll
   for (int h = 0; h < kMaxGqa; ++h) {
     if (h < G) {
-      const float s = lane < np ? sc[h] * scale : -INFINITY;
+      if constexpr (LPP == 2) sc[h] += dpp_f<0xB1>(sc[h]);  // add the neighbour lane's half
+      const float s = my < np ? sc[h] * scale : -INFINITY;
       const float mn = fmaxf(st.m[h], wave_max(s));
       const float alpha = __expf(st.m[h] - mn);  // 0 on the first block (m = -inf)
-      const float p = lane < np ? __expf(s - mn) : 0.f;
-      st.l[h] = st.l[h] * alpha + wave_sum(p);
+      const float p = my < np ? __expf(s - mn) : 0.f;
+      st.l[h] = st.l[h] * alpha + wave_sum(p) * (1.0f / LPP);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) st.o[h][e] *= alpha;
       st.m[h] = mn;
-      pr[h * kWave + lane] = p;
+      if (part == 0) pr[h * kWave + my] = p;
     }
   }
   __builtin_amdgcn_wave_barrier();  // one wave's LDS writes and reads stay in order
-  constexpr int VB = 32;
-  for (int j0 = 0; j0 < np; j0 += VB) {
-    float vv[VB][DPL];
 #pragma unroll
-    for (int jj = 0; jj < VB; ++jj) {
-      const int j = j0 + jj;
-      if (j < np) {
-        const uint16_t* vrow = vc + (int64_t)(p0 + j) * pos_stride + lane * DPL;
-        if constexpr (DPL == 2) {
-          const uint32_t u = *reinterpret_cast<const uint32_t*>(vrow);
-          vv[jj][0] = bf_lo(u);
-          vv[jj][DPL - 1] = bf_hi(u);
-        } else {
-          vv[jj][0] = bf1(vrow[0]);
-        }
-      }
-    }
+  for (int j = 0; j < NP; ++j) {
+    if (j < np) {
 #pragma unroll
-    for (int jj = 0; jj < VB; ++jj) {
-      const int j = j0 + jj;
-      if (j < np) {
+      for (int h = 0; h < kMaxGqa; ++h) {
+        if (h < G) {
+          const float p = pr[h * kWave + j];
+          float v[DPL];
+          if constexpr (sizeof(KT) == 2) {
+            if constexpr (DPL == 2) {
+              v[0] = bf_lo(vr[j][0]);
+              v[DPL - 1] = bf_hi(vr[j][0]);
+            } else {
+              v[0] = bf_lo(vr[j][0]);
+            }
+          } else {
 #pragma unroll
-        for (int h = 0; h < kMaxGqa; ++h) {
-          if (h < G) {
-            const float p = pr[h * kWave + j];
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) st.o[h][e] = fmaf(p, vv[jj][e], st.o[h][e]);
+            for (int e = 0; e < DPL; ++e) v[e] = __uint_as_float(vr[j][e]);
           }
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) st.o[h][e] = fmaf(p, v[e], st.o[h][e]);
         }
       }
     }
@@ -330,23 +372,24 @@ __device__ __forceinline__ void attn_store_state(const AttnState<HD>& st, int G,
   }
 }
 
-// Loads the G rotated query heads of a group into LDS.
+// Loads the G rotated query heads of a group into LDS (one wave).
 template <int HD>
 __device__ __forceinline__ void attn_load_q(const float* q, int G, float* qs, int lane) {
   for (int i = lane; i < G * HD; i += kWave) qs[i] = q[i];
   __builtin_amdgcn_wave_barrier();
 }
 
-// One split of one wave: positions [p0, p1), partial written as G records.
-template <int HD>
-__device__ __forceinline__ void attn_partial(const float* q, const uint16_t* kc, const uint16_t* vc, int64_t pos_stride, int p0,
-                             int p1, int G, float* out, float* scratch, int lane) {
+// One wave, positions [p0, p1) in blocks: partial written as G records.
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_partial(const float* q, const KT* kc, const KT* vc, int p0, int p1, int G,
+                                             float* out, float* scratch, int lane) {
+  constexpr int NP = AttnGeom<HD, KT>::NP;
   float* qs = scratch;           // [G][HD]
   float* pr = scratch + G * HD;  // [G][64]
   attn_load_q<HD>(q, G, qs, lane);
   AttnState<HD> st;
   st.init();
-  for (int b0 = p0; b0 < p1; b0 += kWave) attn_block<HD>(qs, kc, vc, pos_stride, b0, min(b0 + kWave, p1), G, pr, lane, st);
+  for (int b0 = p0; b0 < p1; b0 += NP) attn_block<HD, KT>(qs, kc, vc, b0, min(b0 + NP, p1), G, pr, lane, st);
   attn_store_state<HD>(st, G, out, lane);
 }
 

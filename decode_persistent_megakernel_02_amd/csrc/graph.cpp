@@ -22,7 +22,7 @@ std::string fmt(const char* f, long a = 0, long b = 0, long c = 0, long d = 0) {
 
 int auto_split(int max_seq) {
   (void)max_seq;
-  return kMaxSplit;  // one position per lane
+  return 256;  // four 64-position blocks: one per wave of a per-operator attention workgroup
 }
 
 std::string build_graph(const GraphConfig& c, Graph& g) {
@@ -33,7 +33,7 @@ std::string build_graph(const GraphConfig& c, Graph& g) {
   if (c.nq % c.nkv) return "graph: n_q_heads must be a multiple of n_kv_heads";
   if (c.nq / c.nkv > kMaxGqa) return "graph: more than 8 query heads per KV head";
   if (c.H % 8 || c.F % 8 || (c.nq * c.hd) % 8) return "graph: hidden, ffn and n_q_heads*head_dim must be multiples of 8";
-  if (c.split < 1 || c.split > kMaxSplit) return "graph: attention split must be in [1, 64]";
+  if (c.split < 1 || c.split > kMaxSplit) return "graph: attention split must be in [1, 4096]";
   g = Graph();
   g.cfg = c;
   g.nsplit = (c.max_seq + c.split - 1) / c.split;

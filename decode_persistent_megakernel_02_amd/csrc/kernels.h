@@ -6,7 +6,8 @@
 
 namespace mk {
 extern "C" __global__ void mk_persistent(Params P, const Step* S, int page_floats, int scratch_floats);
-extern "C" __global__ void mk_op_attn_fused(Params P, const Step* S, int layer);
+extern "C" __global__ void mk_op_attn_split(Params P, const Step* S, int layer);
+extern "C" __global__ void mk_op_attn_merge(Params P, const Step* S, int layer);
 extern "C" __global__ void mk_set_step(Step* dst, Step s);
 #define MK_OP_DECL(name) extern "C" __global__ void name(Params P, const Step* S, const Task* tasks, int count, int pf, int sf);
 MK_OP_DECL(mk_op_qkv)
@@ -21,9 +22,9 @@ MK_OP_DECL(mk_op_argmax)
 extern "C" __global__ void mk_fill_u32(uint32_t* p, int64_t n, uint32_t v);
 extern "C" __global__ void mk_t_gemv_kernel(const uint16_t* W, const float* x, float* y, int N, int K);
 extern "C" __global__ void mk_t_rmsnorm_kernel(const float* x, const uint16_t* gamma, float eps, float* y, int n);
-extern "C" __global__ void mk_t_attn_partial_kernel(const float* q, const uint16_t* k, const uint16_t* v,
-                                                    int64_t head_stride, int nq, int nkv, int hd, int T, int split,
-                                                    int nsplit, float* part);
+extern "C" __global__ void mk_t_attn_partial_kernel(const float* q, const void* k, const void* v, int64_t head_stride,
+                                                    int nq, int nkv, int hd, int T, int split, int nsplit, int kv_f32,
+                                                    float* part);
 extern "C" __global__ void mk_t_attn_merge_kernel(const float* part, int nq, int nkv, int hd, int T, int split,
                                                   int nsplit, float* o);
 extern "C" __global__ void mk_t_argmax_kernel(const float* x, int n, unsigned long long* slot);

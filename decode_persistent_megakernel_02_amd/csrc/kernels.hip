@@ -24,6 +24,12 @@ __device__ __forceinline__ int64_t kv_off(const Params& P, int l, int b, int g, 
   return ((((int64_t)l * P.B + b) * P.nkv + g) * P.max_seq + p) * P.hd;
 }
 
+// Stores one K or V element in the cache's element type.
+__device__ __forceinline__ void kv_store(const Params& P, void* cache, int64_t off, float v) {
+  if (P.kv_f32) static_cast<float*>(cache)[off] = v;
+  else static_cast<uint16_t*>(cache)[off] = f2bf(v);
+}
+
 // Token id of batch row b, clamped into [0, V) so that a bad id can never
 // address outside the embedding table; a clamp latches ST_BADTOKEN.
 __device__ __forceinline__ int token_of(const Params& P, const Step& S, int b) {
@@ -33,30 +39,110 @@ __device__ __forceinline__ int token_of(const Params& P, const Step& S, int b) {
   return 0;
 }
 
-// Source of a staged input vector.
-__device__ void stage_input(const Params& P, const Step& S, uint16_t key, int b, float* page, int lane) {
+// Where a staged input vector comes from.
+struct StageSrc {
+  const float* f32;   // fp32 source, or
+  const uint16_t* bf; // bf16 source (the embedding row of layer 0)
+  const uint16_t* gamma;  // RMSNorm gain, null = copy only
+  int n;
+};
+
+__device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, uint16_t key, int b) {
   const int kind = stage_kind(key), l = stage_layer(key);
   const int64_t H = P.H;
+  StageSrc r{nullptr, nullptr, nullptr, P.H};
   switch (kind) {
     case SK_ATTN_NORM:
-      if (l == 0) stage_vector(page, nullptr, P.embed + (int64_t)token_of(P, S, b) * H, P.H, P.attn_norm[0], P.eps, lane);
-      else stage_vector(page, P.xs + ((int64_t)l * P.B + b) * H, nullptr, P.H, P.attn_norm[l], P.eps, lane);
+      r.gamma = P.attn_norm[l];
+      if (l == 0) r.bf = P.embed + (int64_t)token_of(P, S, b) * H;
+      else r.f32 = P.xs + ((int64_t)l * P.B + b) * H;
       break;
-    case SK_O_IN: {
-      const int n = P.nq * P.hd;
-      stage_vector(page, P.attn_out + ((int64_t)l * P.B + b) * n, nullptr, n, nullptr, 0.f, lane);
+    case SK_O_IN:
+      r.n = P.nq * P.hd;
+      r.f32 = P.attn_out + ((int64_t)l * P.B + b) * r.n;
       break;
-    }
     case SK_FFN_NORM:
-      stage_vector(page, P.xmid + ((int64_t)l * P.B + b) * H, nullptr, P.H, P.ffn_norm[l], P.eps, lane);
+      r.gamma = P.ffn_norm[l];
+      r.f32 = P.xmid + ((int64_t)l * P.B + b) * H;
       break;
     case SK_H:
-      stage_vector(page, P.h + ((int64_t)l * P.B + b) * P.F, nullptr, P.F, nullptr, 0.f, lane);
+      r.n = P.F;
+      r.f32 = P.h + ((int64_t)l * P.B + b) * P.F;
       break;
     default:
-      stage_vector(page, P.xs + ((int64_t)P.L * P.B + b) * H, nullptr, P.H, P.final_norm, P.eps, lane);
+      r.gamma = P.final_norm;
+      r.f32 = P.xs + ((int64_t)P.L * P.B + b) * H;
       break;
   }
+  return r;
+}
+
+// One wave stages the vector (persistent kernel's scheduler wave).
+__device__ void stage_input(const Params& P, const Step& S, uint16_t key, int b, float* page, int lane) {
+  const StageSrc r = stage_src(P, S, key, b);
+  stage_vector(page, r.f32, r.bf, r.n, r.gamma, P.eps, lane);
+}
+
+// All kWaves waves of a workgroup stage the vector: each lane owns 8-element
+// groups g = wave*64 + lane + k*512 and loads up to four of them at once;
+// the RMSNorm sum of squares is reduced per wave, then across the waves in a
+// fixed order.  Ends with a workgroup barrier; every wave must call it once.
+__device__ void stage_input_wg(const Params& P, const Step& S, uint16_t key, int b, float* page, float* red,
+                               int wave, int lane) {
+  const StageSrc r = stage_src(P, S, key, b);
+  constexpr int NG = kWaves * kWave, U = 4;
+  const int g0 = wave * kWave + lane;
+  float ss = 0.f;
+  for (int base = 0; base < r.n; base += U * NG * 8) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + (g0 + u * NG) * 8;
+      if (i < r.n) {
+        if (r.bf) {
+          const v4u w = *reinterpret_cast<const v4u*>(r.bf + i);
+          v[u][0] = bf_lo(w.x); v[u][1] = bf_hi(w.x); v[u][2] = bf_lo(w.y); v[u][3] = bf_hi(w.y);
+          v[u][4] = bf_lo(w.z); v[u][5] = bf_hi(w.z); v[u][6] = bf_lo(w.w); v[u][7] = bf_hi(w.w);
+        } else {
+          const float4 a = *reinterpret_cast<const float4*>(r.f32 + i);
+          const float4 c = *reinterpret_cast<const float4*>(r.f32 + i + 4);
+          v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+          v[u][4] = c.x; v[u][5] = c.y; v[u][6] = c.z; v[u][7] = c.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + (g0 + u * NG) * 8;
+      if (i < r.n) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(v[u][j], v[u][j], ss);
+        *reinterpret_cast<float4*>(page + i) = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+        *reinterpret_cast<float4*>(page + i + 4) = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+      }
+    }
+  }
+  if (r.gamma) {
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += red[w];
+    const float inv = 1.0f / sqrtf(tot / (float)r.n + P.eps);
+    for (int i = g0 * 8; i < r.n; i += NG * 8) {  // the groups this lane wrote
+      const v4u gu = *reinterpret_cast<const v4u*>(r.gamma + i);
+      float4 a = *reinterpret_cast<float4*>(page + i);
+      float4 c = *reinterpret_cast<float4*>(page + i + 4);
+      a.x = a.x * inv * bf_lo(gu.x); a.y = a.y * inv * bf_hi(gu.x);
+      a.z = a.z * inv * bf_lo(gu.y); a.w = a.w * inv * bf_hi(gu.y);
+      c.x = c.x * inv * bf_lo(gu.z); c.y = c.y * inv * bf_hi(gu.z);
+      c.z = c.z * inv * bf_lo(gu.w); c.w = c.w * inv * bf_hi(gu.w);
+      *reinterpret_cast<float4*>(page + i) = a;
+      *reinterpret_cast<float4*>(page + i + 4) = c;
+    }
+  }
+  __syncthreads();
 }
 
 template <int R>
@@ -125,10 +211,10 @@ __device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const 
         const float rot = r == 0 ? y[0] * c - y[1] * sn : y[1] * c + y[0] * sn;
         const int row = r == 0 ? d.a1 : d.a1 + d.a3;
         if (d.a0 == 0) P.q[((int64_t)l * P.B + b) * P.nq * P.hd + row] = rot;
-        else P.kcache[kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd] = f2bf(rot);
+        else kv_store(P, P.kcache, kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd, rot);
       } else {
         const int row = d.a1 + r;
-        P.vcache[kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd] = f2bf(v);
+        kv_store(P, P.vcache, kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd, v);
       }
     } else if constexpr (TT == TT_O) {
       const int row = d.a1 + r;
@@ -170,10 +256,18 @@ __device__ __forceinline__ bool exec_typed(const Params& P, const Step& S, const
     const int p1 = min(p0 + P.split, T);
     const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * P.hd;
     float* out = P.attn_part + ((((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit + s) * G * (P.hd + 2);
-    const uint16_t* kc = P.kcache + kv_off(P, l, b, grp, 0);
-    const uint16_t* vc = P.vcache + kv_off(P, l, b, grp, 0);
-    if (P.hd == 128) attn_partial<128>(q, kc, vc, P.hd, p0, p1, G, out, scratch, lane);
-    else attn_partial<64>(q, kc, vc, P.hd, p0, p1, G, out, scratch, lane);
+    const int64_t o0 = kv_off(P, l, b, grp, 0);
+    if (P.kv_f32) {
+      const float* kc = static_cast<const float*>(P.kcache) + o0;
+      const float* vc = static_cast<const float*>(P.vcache) + o0;
+      if (P.hd == 128) attn_partial<128, float>(q, kc, vc, p0, p1, G, out, scratch, lane);
+      else attn_partial<64, float>(q, kc, vc, p0, p1, G, out, scratch, lane);
+    } else {
+      const uint16_t* kc = static_cast<const uint16_t*>(P.kcache) + o0;
+      const uint16_t* vc = static_cast<const uint16_t*>(P.vcache) + o0;
+      if (P.hd == 128) attn_partial<128, uint16_t>(q, kc, vc, p0, p1, G, out, scratch, lane);
+      else attn_partial<64, uint16_t>(q, kc, vc, p0, p1, G, out, scratch, lane);
+    }
   } else if constexpr (TT == TT_MERGE) {
     if (!wait()) return false;
     const int G = P.nq / P.nkv, grp = d.a0, T = S.pos + 1;
@@ -406,14 +500,15 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
   const Task first = tasks[0];
-  // Every wave passes the staging barrier exactly once: inside its first
-  // task's wait() -- after that task's weight loads are in flight -- or after
-  // the loop if it has no task.  Wave 0 stages the input vector just before.
+  // Every wave stages its slice of the input vector and passes the staging
+  // barriers exactly once: inside its first task's wait() -- after that task's
+  // weight loads are in flight -- or after the loop if it has no task.
   bool staged = false;
+  float* red = reinterpret_cast<float*>(L->slot);  // per-wave partial sums of squares
   auto wait = [&]() __attribute__((always_inline)) -> bool {
     if (!staged) {
-      if (wave == 0 && first.stage) stage_input(P, S, first.stage, first.batch, page, lane);
-      __syncthreads();
+      if (first.stage) stage_input_wg(P, S, first.stage, first.batch, page, red, wave, lane);
+      else __syncthreads();
       staged = true;
     }
     return true;
@@ -445,38 +540,87 @@ MK_OP_KERNEL(mk_op_down, TT_DOWN)
 MK_OP_KERNEL(mk_op_lm, TT_LM)
 MK_OP_KERNEL(mk_op_argmax, TT_ARGMAX)
 
-// Attention of one (batch row, KV group) per workgroup: the positions are cut
-// into 64-position blocks dealt round-robin to the waves, each wave keeps an
-// online-softmax state, and the states are merged through LDS by log-sum-exp.
-template <int HD>
-__device__ __forceinline__ void attn_fused(const Params& P, const Step& S, int l, int b, int grp, float* sm, int wave, int lane) {
+// Attention, per-operator path: one workgroup of kAttnWaves waves per
+// (batch row, KV group, split).  The split's positions are dealt to the waves
+// in blocks; each wave keeps an online-softmax state; the workgroup merges its
+// waves' states through LDS and writes one (o, m, l) record per head.
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, int l, int b, int grp, int s, float* sm,
+                                              int wave, int lane) {
+  using Gm = AttnGeom<HD, KT>;
   const int G = P.nq / P.nkv, T = S.pos + 1;
-  float* qs = sm;                                          // [G][HD]
-  float* pr = qs + G * HD + wave * G * kWave;              // [G][64] per wave
-  float* recs = qs + G * HD + kWaves * G * kWave;          // [kWaves][G][HD + 2]
+  const int p0 = s * P.split, p1 = min(p0 + P.split, T);
+  if (p0 >= T) return;
+  float* qs = sm;                                            // [G][HD]
+  float* pr = qs + G * HD + wave * G * kWave;                // [G][64] per wave
+  float* recs = qs + G * HD + kAttnWaves * G * kWave;        // [kAttnWaves][G][HD + 2]
   const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * HD;
   for (int i = threadIdx.x; i < G * HD; i += blockDim.x) qs[i] = q[i];
   __syncthreads();
-  const uint16_t* kc = P.kcache + kv_off(P, l, b, grp, 0);
-  const uint16_t* vc = P.vcache + kv_off(P, l, b, grp, 0);
+  const int64_t o0 = kv_off(P, l, b, grp, 0);
+  const KT* kc = static_cast<const KT*>(P.kcache) + o0;
+  const KT* vc = static_cast<const KT*>(P.vcache) + o0;
   AttnState<HD> st;
   st.init();
-  for (int p0 = wave * kWave; p0 < T; p0 += kWaves * kWave)
-    attn_block<HD>(qs, kc, vc, HD, p0, min(p0 + kWave, T), G, pr, lane, st);
+  for (int b0 = p0 + wave * Gm::NP; b0 < p1; b0 += kAttnWaves * Gm::NP)
+    attn_block<HD, KT>(qs, kc, vc, b0, min(b0 + Gm::NP, p1), G, pr, lane, st);
   attn_store_state<HD>(st, G, recs + wave * G * (HD + 2), lane);
   __syncthreads();
-  float* out = P.attn_out + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * HD;
-  for (int h = wave; h < G; h += kWaves) attn_merge<HD>(recs + h * (HD + 2), kWaves, 1, out + h * HD, lane, G * (HD + 2));
+  float* out = P.attn_part + ((((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit + s) * G * (HD + 2);
+  for (int h = wave; h < G; h += kAttnWaves) {
+    // merge the waves' records of head h into one (unnormalised) record
+    constexpr int DPL = HD / kWave;
+    float M = -INFINITY, Ls = 0.f, o[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float* r = recs + (w * G + h) * (HD + 2);
+      const float lw = r[HD + 1];
+      if (!(lw > 0.f)) continue;
+      const float mw = r[HD], Mn = fmaxf(M, mw);
+      const float a = __expf(M - Mn), c = __expf(mw - Mn);
+      Ls = Ls * a + lw * c;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + r[lane * DPL + e] * c;
+      M = Mn;
+    }
+    float* oh = out + h * (HD + 2);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) oh[lane * DPL + e] = o[e];
+    if (lane == 0) {
+      oh[HD] = M;
+      oh[HD + 1] = Ls;
+    }
+  }
 }
 
-extern "C" __global__ __launch_bounds__(kWaves * kWave) void mk_op_attn_fused(Params P, const Step* Sd, int layer) {
+extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_split(Params P, const Step* Sd, int layer) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sm = reinterpret_cast<float*>(smem);
   const Step S = *Sd;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int b = blockIdx.x / P.nkv, grp = blockIdx.x % P.nkv;
-  if (P.hd == 128) attn_fused<128>(P, S, layer, b, grp, sm, wave, lane);
-  else attn_fused<64>(P, S, layer, b, grp, sm, wave, lane);
+  const int s = blockIdx.x % P.nsplit, bg = blockIdx.x / P.nsplit;
+  const int b = bg / P.nkv, grp = bg % P.nkv;
+  if (P.kv_f32) {
+    if (P.hd == 128) attn_split_wg<128, float>(P, S, layer, b, grp, s, sm, wave, lane);
+    else attn_split_wg<64, float>(P, S, layer, b, grp, s, sm, wave, lane);
+  } else {
+    if (P.hd == 128) attn_split_wg<128, uint16_t>(P, S, layer, b, grp, s, sm, wave, lane);
+    else attn_split_wg<64, uint16_t>(P, S, layer, b, grp, s, sm, wave, lane);
+  }
+}
+
+// Log-sum-exp merge of the used splits: one wave per (batch row, query head).
+extern "C" __global__ __launch_bounds__(kMaxGqa * kWave) void mk_op_attn_merge(Params P, const Step* Sd, int layer) {
+  const Step S = *Sd;
+  const int G = P.nq / P.nkv, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave >= G) return;
+  const int b = blockIdx.x / P.nkv, grp = blockIdx.x % P.nkv, T = S.pos + 1;
+  const int used = (T + P.split - 1) / P.split;
+  const float* part = P.attn_part + (((int64_t)layer * P.B + b) * P.nkv + grp) * P.nsplit * G * (P.hd + 2);
+  float* out = P.attn_out + ((int64_t)layer * P.B + b) * P.nq * P.hd + (int64_t)(grp * G + wave) * P.hd;
+  if (P.hd == 128) attn_merge<128>(part + wave * (128 + 2), used, 1, out, lane, G * (128 + 2));
+  else attn_merge<64>(part + wave * (64 + 2), used, 1, out, lane, G * (64 + 2));
 }
 
 // Per-step arguments live in device memory so that a step's launches can be
@@ -527,9 +671,9 @@ extern "C" __global__ void mk_t_rmsnorm_kernel(const float* x, const uint16_t* g
 }
 
 // Split-KV attention partials: block = one wave per (group, split).
-extern "C" __global__ void mk_t_attn_partial_kernel(const float* q, const uint16_t* k, const uint16_t* v,
-                                                    int64_t head_stride, int nq, int nkv, int hd, int T, int split,
-                                                    int nsplit, float* part) {
+template <typename KT>
+__device__ void t_attn_partial(const float* q, const void* k, const void* v, int64_t head_stride, int nq, int nkv,
+                               int hd, int T, int split, int nsplit, float* part) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* scr = reinterpret_cast<float*>(smem);
   const int grp = blockIdx.x / nsplit, s = blockIdx.x % nsplit, lane = threadIdx.x;
@@ -537,13 +681,20 @@ extern "C" __global__ void mk_t_attn_partial_kernel(const float* q, const uint16
   if (p0 >= T) return;
   const int p1 = min(p0 + split, T);
   float* out = part + ((int64_t)grp * nsplit + s) * G * (hd + 2);
-  if (hd == 128)
-    attn_partial<128>(q + (int64_t)grp * G * hd, k + grp * head_stride, v + grp * head_stride, hd, p0, p1, G, out, scr, lane);
-  else
-    attn_partial<64>(q + (int64_t)grp * G * hd, k + grp * head_stride, v + grp * head_stride, hd, p0, p1, G, out, scr, lane);
+  const KT* kc = static_cast<const KT*>(k) + grp * head_stride;
+  const KT* vc = static_cast<const KT*>(v) + grp * head_stride;
+  if (hd == 128) attn_partial<128, KT>(q + (int64_t)grp * G * hd, kc, vc, p0, p1, G, out, scr, lane);
+  else attn_partial<64, KT>(q + (int64_t)grp * G * hd, kc, vc, p0, p1, G, out, scr, lane);
 }
 
-extern "C" __global__ void mk_t_attn_merge_kernel(const float* part, int nq, int nkv, int hd, int T, int split,
+extern "C" __global__ __launch_bounds__(kWave) void mk_t_attn_partial_kernel(const float* q, const void* k, const void* v, int64_t head_stride,
+                                                    int nq, int nkv, int hd, int T, int split, int nsplit, int kv_f32,
+                                                    float* part) {
+  if (kv_f32) t_attn_partial<float>(q, k, v, head_stride, nq, nkv, hd, T, split, nsplit, part);
+  else t_attn_partial<uint16_t>(q, k, v, head_stride, nq, nkv, hd, T, split, nsplit, part);
+}
+
+extern "C" __global__ __launch_bounds__(kWave) void mk_t_attn_merge_kernel(const float* part, int nq, int nkv, int hd, int T, int split,
                                                   int nsplit, float* o) {
   const int grp = blockIdx.x, lane = threadIdx.x, G = nq / nkv;
   const int used = (T + split - 1) / split;

@@ -15,7 +15,8 @@ constexpr int kWave = 64;
 constexpr int kWaves = 8;             // waves per workgroup (1 scheduler + workers)
 constexpr int kWorkers = kWaves - 1;  // worker waves per CU in the persistent kernel
 constexpr int kMaxGqa = 8;            // query heads per KV head supported
-constexpr int kMaxSplit = 64;         // positions per split-KV attention task (one per lane)
+constexpr int kMaxSplit = 4096;       // positions per split-KV attention task
+constexpr int kAttnWaves = 4;         // waves per split in the per-operator attention kernel
 constexpr int kLocalSlots = 64;       // per-CU LDS counters for aggregated event signals
 constexpr int kMaxBatch = 64;         // sequences per step
 constexpr uint16_t kNone16 = 0xFFFF;
@@ -53,10 +54,10 @@ inline constexpr int stage_layer(uint16_t key) { return (key & 0xFFF) - 1; }
 template <int TT> struct TaskShape;
 template <> struct TaskShape<1> { static constexpr int R = 2, D = 16; };  // QKV: one RoPE pair or two v rows
 template <> struct TaskShape<4> { static constexpr int R = 2, D = 16; };  // O
-template <> struct TaskShape<5> { static constexpr int R = 4, D = 8; };   // GU: two gate + two up rows
+template <> struct TaskShape<5> { static constexpr int R = 2, D = 16; };  // GU: one gate + one up row
 template <> struct TaskShape<6> { static constexpr int R = 1, D = 32; };  // DOWN
 template <> struct TaskShape<7> { static constexpr int R = 4, D = 8; };   // LM head
-constexpr int kRowsQkv = 2, kRowsO = 2, kRowsGuPerMatrix = 2, kRowsDown = 1, kRowsLm = 4;
+constexpr int kRowsQkv = 2, kRowsO = 2, kRowsGuPerMatrix = 1, kRowsDown = 1, kRowsLm = 4;
 
 // One task.  Interpretation of a0..a3 by type:
 //   QKV   a0 = matrix (0 q, 1 k, 2 v), a1 = first row, a2 = rows, a3 = RoPE pair offset (0 = none)
@@ -85,6 +86,7 @@ static_assert(sizeof(Task) == 48, "Task layout");
 struct Params {
   // shape
   int32_t L, H, nq, nkv, hd, F, V, B, max_seq, split, nsplit, tied;
+  int32_t kv_f32;       // KV cache element type: 0 bf16, 1 fp32
   float eps;
   int32_t ncu;          // persistent grid
   uint32_t timeout_ticks;   // wall-clock limit of any single wait
@@ -102,9 +104,9 @@ struct Params {
   const uint16_t* const* w_gate;
   const uint16_t* const* w_up;
   const uint16_t* const* w_down;
-  // KV cache bf16 [L][B][nkv][max_seq][hd]
-  uint16_t* kcache;
-  uint16_t* vcache;
+  // KV cache [L][B][nkv][max_seq][hd], bf16 or fp32 (kv_f32)
+  void* kcache;
+  void* vcache;
   // fp32 activations (one buffer per layer, each written once per step)
   float* xs;         // [L+1][B][H]   x_{l+1} = output of layer l (x_0 unused: embedding row)
   float* xmid;       // [L][B][H]

@@ -85,7 +85,8 @@ typedef struct {
   uint32_t flags;      /* MK_FLAG_* */
   uint32_t watchdog_ms;/* in-kernel dependency wait limit; 0 = 2000 ms */
   int32_t num_cus;     /* persistent grid size; 0 = every CU of the device */
-  int32_t attn_split;  /* positions per split-KV attention task; 0 = automatic */
+  int32_t attn_split;  /* positions per split-KV attention task; 0 = automatic (256) */
+  int32_t kv_fp32;     /* KV cache element type: 0 = bf16, nonzero = fp32 */
 } mk_config;
 
 /* Weights: bf16 bit patterns, row-major [out, in], contiguous, device memory.
@@ -106,14 +107,16 @@ typedef struct {
   const void* const* w_down;    /* [hidden, ffn] */
 } mk_weights;
 
-/* Layout of the handle-owned KV cache (element strides, bf16 elements):
+/* Layout of the handle-owned KV cache (element strides; elements are bf16 or
+ * fp32, see elem_bytes):
  * K[l][b][g][p][d] at k + l*stride_layer + b*stride_batch + g*stride_head + p*stride_pos + d. */
 typedef struct {
   void* k;
   void* v;
   int64_t stride_layer, stride_batch, stride_head, stride_pos;
-  int32_t length; /* positions currently valid */
-  int32_t batch;  /* sequences in use (0 before the first prefill) */
+  int32_t length;     /* positions currently valid */
+  int32_t batch;      /* sequences in use (0 before the first prefill) */
+  int32_t elem_bytes; /* 2 (bf16) or 4 (fp32) */
 } mk_kv_layout;
 
 /* Create a decoder on the current HIP device.  Validates the config, builds

@@ -85,12 +85,12 @@ mk_status mk_read_op_times(mk_handle* h, double* total_ms, int32_t* launches);
 mk_status mk_t_gemv(const void* W, const float* x, float* y, int32_t N, int32_t K, void* stream);
 /* y = x * (mean(x^2) + eps)^-1/2 * gamma; gamma bf16; n a multiple of 8. */
 mk_status mk_t_rmsnorm(const float* x, const void* gamma, float eps, float* y, int32_t n, void* stream);
-/* Decode attention of one sequence: q fp32 [nq, hd]; k, v bf16 with head g at
- * k + g*head_stride, position p at + p*hd; T positions; split-KV partials of
- * `split` positions merged by log-sum-exp; o fp32 [nq, hd].  Synchronous
- * (allocates and frees its partial buffer). */
+/* Decode attention of one sequence: q fp32 [nq, hd]; k, v (bf16, or fp32 if
+ * kv_f32) with head g at k + g*head_stride elements, position p at + p*hd; T
+ * positions; split-KV partials of `split` positions merged by log-sum-exp;
+ * o fp32 [nq, hd].  Synchronous (allocates and frees its partial buffer). */
 mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t head_stride, int32_t nq, int32_t nkv,
-                         int32_t hd, int32_t T, int32_t split, float* o, void* stream);
+                         int32_t hd, int32_t T, int32_t split, int32_t kv_f32, float* o, void* stream);
 /* out[0] = lowest index of the maximum of x[n] (fp32).  Synchronous. */
 mk_status mk_t_argmax(const float* x, int32_t n, int32_t* out, void* stream);
 

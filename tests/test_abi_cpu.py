@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 def test_config_struct_layout_matches_header():
     # 18 four-byte fields, no padding
-    assert ctypes.sizeof(abi.mk_config) == 18 * 4
+    assert ctypes.sizeof(abi.mk_config) == 19 * 4  # 19 four-byte fields, no padding
     assert ctypes.sizeof(abi.mk_weights) == 12 * 8
     assert abi.task_dtype().itemsize == 48
 
@@ -49,7 +49,7 @@ def cfg_for(shape, max_seq=64, **kw):
 
 def test_invalid_configs_are_rejected():
     bad = [dict(head_dim=96), dict(n_kv_heads=3), dict(hidden=100), dict(max_batch=0), dict(max_seq=0),
-           dict(mode=7), dict(attn_split=65), dict(abi_version=99)]
+           dict(mode=7), dict(attn_split=5000), dict(abi_version=99)]
     for b in bad:
         c = cfg_for(MINI)
         for k, v in b.items():

@@ -69,18 +69,27 @@ def test_rmsnorm(abi, n):
     np.testing.assert_allclose(y.cpu().numpy(), ref, rtol=2e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp32"])
 @pytest.mark.parametrize("nq,nkv,hd", [(4, 2, 64), (32, 8, 128), (8, 1, 128), (2, 2, 64)])
-@pytest.mark.parametrize("T,split", [(1, 64), (7, 64), (64, 64), (65, 64), (200, 16), (37, 1), (130, 13)])
-def test_attention_split_kv(abi, nq, nkv, hd, T, split):
+@pytest.mark.parametrize("T,split", [(1, 64), (7, 64), (64, 64), (65, 64), (200, 16), (37, 1), (130, 13),
+                                     (600, 256), (300, 1000)])
+def test_attention_split_kv(abi, nq, nkv, hd, T, split, kv):
     rng = np.random.default_rng(T * 131 + split + nq)
     S = T + 3
     q = rng.normal(size=(nq, hd)).astype(np.float32)
     kb = gen.bf16_normal(2, 7, 0, nkv * S * hd, 1.0).reshape(nkv, S, hd)
     vb = gen.bf16_normal(2, 8, 0, nkv * S * hd, 1.0).reshape(nkv, S, hd)
+    if kv == "bf16":
+        kd, vd = dev_bits(kb).view(nkv, S, hd), dev_bits(vb).view(nkv, S, hd)
+        K, V = D.widen_bf16(kb), D.widen_bf16(vb)
+    else:  # fp32 values that are not bf16-representable
+        K = rng.normal(size=(nkv, S, hd)).astype(np.float32)
+        V = rng.normal(size=(nkv, S, hd)).astype(np.float32)
+        kd, vd = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda()
+        K, V = K.astype(np.float64), V.astype(np.float64)
     o = torch.empty(nq, hd, dtype=torch.float32, device="cuda")
-    abi.mk_t_attention(torch.from_numpy(q).cuda(), dev_bits(kb).view(nkv, S, hd), dev_bits(vb).view(nkv, S, hd),
-                       T, split, o)
-    ref = D.gqa_attention(q.astype(np.float64), D.widen_bf16(kb)[:, :T], D.widen_bf16(vb)[:, :T])
+    abi.mk_t_attention(torch.from_numpy(q).cuda(), kd, vd, T, split, o)
+    ref = D.gqa_attention(q.astype(np.float64), K[:, :T], V[:, :T])
     np.testing.assert_allclose(o.cpu().numpy(), ref, rtol=1e-5, atol=2e-6)
 
 
