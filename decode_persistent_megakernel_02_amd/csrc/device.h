@@ -218,19 +218,17 @@ __device__ __forceinline__ void stage_vector(float* page, const float* src, cons
 // element type KT is bf16 (uint16_t) or fp32 (float).
 //
 // A block covers NP positions.  For the scores, LPP lanes share one position
-// (each lane holds HD/LPP elements = at most 256 bytes of the K row, loaded
-// with 16-byte loads); their partial dot products are combined with a DPP
-// swap.  For the values, every lane owns DPL dims of every position.  K and V
-// of the whole block are loaded up front, so a block costs one memory round
-// trip.
+// (each lane holds 32 elements of the K row, loaded with 16-byte loads) and
+// their partial dot products are combined with DPP swaps inside the quad.
+// For the values, every lane owns DPL dims of every position.  K and V of the
+// whole block are loaded up front, so a block costs one memory round trip.
 template <int HD, typename KT>
 struct AttnGeom {
-  static constexpr int ROW_BYTES = HD * (int)sizeof(KT);
-  static constexpr int LPP = ROW_BYTES > 256 ? ROW_BYTES / 256 : 1;  // lanes per position (1 or 2)
-  static constexpr int NP = kWave / LPP;                               // positions per block
-  static constexpr int EPL = HD / LPP;                                 // K elements per lane
-  static constexpr int KV16 = EPL * (int)sizeof(KT) / 16;             // 16-byte K loads per lane
-  static constexpr int DPL = HD / kWave;                               // V dims per lane
+  static constexpr int EPL = 32;                              // K elements per lane
+  static constexpr int LPP = HD / EPL;                        // lanes per position (2 or 4)
+  static constexpr int NP = kWave / LPP;                      // positions per block (32 or 16)
+  static constexpr int KV16 = EPL * (int)sizeof(KT) / 16;    // 16-byte K loads per lane
+  static constexpr int DPL = HD / kWave;                      // V dims per lane
 };
 
 template <int HD>
@@ -313,7 +311,8 @@ __device__ __forceinline__ void attn_block(const float* qs, const KT* kc, const 
 #pragma unroll
   for (int h = 0; h < kMaxGqa; ++h) {
     if (h < G) {
-      if constexpr (LPP == 2) sc[h] += dpp_f<0xB1>(sc[h]);  // add the neighbour lane's half
+      sc[h] += dpp_f<0xB1>(sc[h]);                        // lanes 2j, 2j+1
+      if constexpr (LPP == 4) sc[h] += dpp_f<0x4E>(sc[h]);  // and the other pair of the quad
       const float s = my < np ? sc[h] * scale : -INFINITY;
       const float mn = fmaxf(st.m[h], wave_max(s));
       const float alpha = __expf(st.m[h] - mn);  // 0 on the first block (m = -inf)

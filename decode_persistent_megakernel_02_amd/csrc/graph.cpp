@@ -22,7 +22,7 @@ std::string fmt(const char* f, long a = 0, long b = 0, long c = 0, long d = 0) {
 
 int auto_split(int max_seq) {
   (void)max_seq;
-  return 256;  // four 64-position blocks: one per wave of a per-operator attention workgroup
+  return 64;  // one 16-position block per wave of a 4-wave attention workgroup (head_dim 128)
 }
 
 std::string build_graph(const GraphConfig& c, Graph& g) {

@@ -154,17 +154,15 @@ __device__ __forceinline__ float pick(const float (&y)[R], int i) {
 }
 
 // GEMV-type task (QKV, O, GU, DOWN, LM) with its operator fixed at compile
-// time.  `wait()` runs after the weight prefetch and before anything that
-// reads activations; it returns false on abort.
-template <int TT, class Wait>
-__device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const Task& d, int lane, const float* page, Lds* L, Wait wait) {
-  constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
-  const int l = d.layer, b = d.batch;
-  GemvRows<R> g;
-  g.mask = 0;
+// time: where its rows are ...
+template <int TT>
+__device__ __forceinline__ void gemv_setup(const Params& P, const Task& d, GemvRows<TaskShape<TT>::R>& g) {
+  constexpr int R = TaskShape<TT>::R;
+  const int l = d.layer;
   int K = P.H;
   if constexpr (TT == TT_O) K = P.nq * P.hd;
   else if constexpr (TT == TT_DOWN) K = P.F;
+  g.nvec = K / 8;
   g.stride = K / 8;
   g.split = R;
   if constexpr (TT == TT_QKV) {
@@ -193,16 +191,17 @@ __device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const 
     g.base1 = g.base0;
     g.mask = (1u << d.a2) - 1;
   }
-  g.nvec = K / 8;
-  v4u buf[D][R];
-  gemv_prefetch<R, D>(buf, g, lane);
-  if (!wait()) return false;
-  float y[R];
-  gemv_run<R, D>(buf, g, page, lane, y);
-  // epilogue: lane r finishes row slot r
-  const int r = lane;
+}
+
+// ... and what it does with the R dot products y (uniform across the wave).
+template <int TT>
+__device__ __forceinline__ void gemv_epilogue(const Params& P, const Step& S, const Task& d, uint32_t mask,
+                                              const float (&y)[TaskShape<TT>::R], int lane, Lds* L) {
+  constexpr int R = TaskShape<TT>::R;
+  const int l = d.layer, b = d.batch;
+  const int r = lane;  // lane r finishes row slot r
   const int64_t H = P.H;
-  if (r < R && ((g.mask >> r) & 1)) {
+  if (r < R && ((mask >> r) & 1)) {
     const float v = pick<R>(y, r);
     if constexpr (TT == TT_QKV) {
       if (d.a3) {  // rotate the pair (lo, hi) = (y0, y1) by the position's angle
@@ -233,13 +232,68 @@ __device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const 
     unsigned long long best = 0;
 #pragma unroll
     for (int j = 0; j < R; ++j)
-      if ((g.mask >> j) & 1) {
+      if ((mask >> j) & 1) {
         const unsigned long long k = argmax_key(y[j], (uint32_t)(d.a1 + j));
         best = k > best ? k : best;
       }
     if (lane == 0) __hip_atomic_fetch_max(&L->lm_best[b], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
+}
+
+// One GEMV task: prefetch its weights, wait() for its inputs, dot, epilogue.
+// `wait()` returns false on abort.
+template <int TT, class Wait>
+__device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const Task& d, int lane, const float* page,
+                                          Lds* L, Wait wait) {
+  constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
+  GemvRows<R> g;
+  gemv_setup<TT>(P, d, g);
+  v4u buf[D][R];
+  gemv_prefetch<R, D>(buf, g, lane);
+  if (!wait()) return false;
+  float y[R];
+  gemv_run<R, D>(buf, g, page, lane, y);
+  gemv_epilogue<TT>(P, S, d, g.mask, y, lane, L);
   return true;
+}
+
+// A wave's whole sequence of GEMV tasks i0, i0 + stride, ... with two
+// buffers: the next task's first D chunks are in flight while the current
+// task is consumed, so the wave's weight stream does not drain between tasks.
+template <int TT, class Wait>
+__device__ __forceinline__ void gemv_stream(const Params& P, const Step& S, const Task* tasks, int count, int i0,
+                                            int stride, int lane, const float* page, Lds* L, Wait wait) {
+  constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
+  if (i0 >= count) return;
+  v4u bufA[D][R], bufB[D][R];
+  Task dA = tasks[i0], dB;
+  GemvRows<R> gA, gB;
+  gemv_setup<TT>(P, dA, gA);
+  gemv_prefetch<R, D>(bufA, gA, lane);
+  wait();
+  float y[R];
+  for (int i = i0;;) {
+    int n = i + stride;
+    if (n < count) {
+      dB = tasks[n];
+      gemv_setup<TT>(P, dB, gB);
+      gemv_prefetch<R, D>(bufB, gB, lane);
+    }
+    gemv_run<R, D>(bufA, gA, page, lane, y);
+    gemv_epilogue<TT>(P, S, dA, gA.mask, y, lane, L);
+    if (n >= count) break;
+    i = n;
+    n = i + stride;
+    if (n < count) {
+      dA = tasks[n];
+      gemv_setup<TT>(P, dA, gA);
+      gemv_prefetch<R, D>(bufA, gA, lane);
+    }
+    gemv_run<R, D>(bufB, gB, page, lane, y);
+    gemv_epilogue<TT>(P, S, dB, gB.mask, y, lane, L);
+    if (n >= count) break;
+    i = n;
+  }
 }
 
 template <int TT, class Wait>
@@ -513,9 +567,13 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
     }
     return true;
   };
-  for (int i = blockIdx.x * kWaves + wave; i < count; i += gridDim.x * kWaves) {
-    const Task d = tasks[i];
-    exec_typed<TT>(P, S, d, lane, first.stage ? page : nullptr, scr + wave * scratch_floats, L, wait);
+  if constexpr (TT == TT_QKV || TT == TT_O || TT == TT_GU || TT == TT_DOWN || TT == TT_LM) {
+    gemv_stream<TT>(P, S, tasks, count, blockIdx.x * kWaves + wave, gridDim.x * kWaves, lane, page, L, wait);
+  } else {
+    for (int i = blockIdx.x * kWaves + wave; i < count; i += gridDim.x * kWaves) {
+      const Task d = tasks[i];
+      exec_typed<TT>(P, S, d, lane, first.stage ? page : nullptr, scr + wave * scratch_floats, L, wait);
+    }
   }
   wait();
   if constexpr (TT == TT_LM) {

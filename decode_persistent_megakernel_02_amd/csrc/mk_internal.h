@@ -48,16 +48,16 @@ inline constexpr int stage_kind(uint16_t key) { return key >> 12; }
 inline constexpr int stage_layer(uint16_t key) { return (key & 0xFFF) - 1; }
 
 // Shape of a GEMV task per operator: R weight rows streamed together, D
-// 512-column chunks of each row in flight (R * D * 16 B per lane, 32 KiB per
-// wave when full).  Long rows (down-projection, K = ffn) take one row deep;
-// short rows take several rows.
+// 512-column chunks of each row in flight (R * D * 16 B per lane, 16 KiB per
+// wave).  The per-operator kernels double-buffer tasks, so a wave holds up to
+// two such buffers.  Long rows (down-projection, K = ffn) take one row.
 template <int TT> struct TaskShape;
-template <> struct TaskShape<1> { static constexpr int R = 2, D = 16; };  // QKV: one RoPE pair or two v rows
-template <> struct TaskShape<4> { static constexpr int R = 2, D = 16; };  // O
-template <> struct TaskShape<5> { static constexpr int R = 2, D = 16; };  // GU: one gate + one up row
-template <> struct TaskShape<6> { static constexpr int R = 1, D = 32; };  // DOWN
-template <> struct TaskShape<7> { static constexpr int R = 4, D = 8; };   // LM head
-constexpr int kRowsQkv = 2, kRowsO = 2, kRowsGuPerMatrix = 1, kRowsDown = 1, kRowsLm = 4;
+template <> struct TaskShape<1> { static constexpr int R = 2, D = 8; };   // QKV: one RoPE pair or two v rows
+template <> struct TaskShape<4> { static constexpr int R = 2, D = 8; };   // O
+template <> struct TaskShape<5> { static constexpr int R = 2, D = 8; };   // GU: one gate + one up row
+template <> struct TaskShape<6> { static constexpr int R = 1, D = 16; };  // DOWN
+template <> struct TaskShape<7> { static constexpr int R = 2, D = 8; };   // LM head
+constexpr int kRowsQkv = 2, kRowsO = 2, kRowsGuPerMatrix = 1, kRowsDown = 1, kRowsLm = 2;
 
 // One task.  Interpretation of a0..a3 by type:
 //   QKV   a0 = matrix (0 q, 1 k, 2 v), a1 = first row, a2 = rows, a3 = RoPE pair offset (0 = none)

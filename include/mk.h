@@ -85,7 +85,7 @@ typedef struct {
   uint32_t flags;      /* MK_FLAG_* */
   uint32_t watchdog_ms;/* in-kernel dependency wait limit; 0 = 2000 ms */
   int32_t num_cus;     /* persistent grid size; 0 = every CU of the device */
-  int32_t attn_split;  /* positions per split-KV attention task; 0 = automatic (256) */
+  int32_t attn_split;  /* positions per split-KV attention task; 0 = automatic (64) */
   int32_t kv_fp32;     /* KV cache element type: 0 = bf16, nonzero = fp32 */
 } mk_config;
 
