@@ -9,12 +9,17 @@ write-up, on synthetic inputs.  Prints ONE JSON line.
 Protocol: W untimed warm-up decode steps, reset + prefill, then exactly K
 decode steps with device-side token feedback, bracketed by synchronize.  The
 step runs in kernel-per-operator mode (the persistent single-launch mode is
-refused by the library on this device; see DESIGN.md).  Inside the timed
+refused by the library on this device).  Inside the timed
 region the library brackets every launch of the dominant operator (the
 gate/up projection + SwiGLU) with HIP events on the stream it runs on; their
 average gives the kernel duration of the roofline figure.  A second, untimed
 pass reports the per-operator breakdown.  The oracle's time on a bounded sample
 is reported as cpu_baseline.
+
+`--workload llama8b_b8_kv4096` (8 sequences, 4096-token prompts, 128 steps)
+and `--workload llama70b_b64` (the 70B shape, 64 sequences, 512-token prompts,
+64 steps) time the batched path the same way; their unit is ms per step (one
+token for every sequence) and they carry no cpu_baseline.
 """
 import argparse
 import hashlib
@@ -68,21 +73,29 @@ def load_traffic(workload):
     return d.get("bytes_per_launch")
 
 
-def gu_bytes(shape):
-    """Algorithmic bytes of one gate/up + SwiGLU launch: both weight matrices,
-    the norm gain, the input vector read once, the output written once."""
-    return 2 * shape.ffn * shape.hidden * 2 + 2 * shape.hidden + 4 * shape.hidden + 4 * shape.ffn
+def gu_bytes(shape, batch=1):
+    """Algorithmic bytes of one gate/up + SwiGLU launch.  Batch 1: both weight
+    matrices, the norm gain, the fp32 input vector read once, the output
+    written once.  Batched: both weight matrices, the bf16 normalised inputs
+    [B, H] read once, the outputs written once (fp32 and the bf16 operand of
+    the down-projection)."""
+    w = 2 * shape.ffn * shape.hidden * 2
+    if batch == 1:
+        return w + 2 * shape.hidden + 4 * shape.hidden + 4 * shape.ffn
+    return w + 2 * batch * shape.hidden + 6 * batch * shape.ffn
 
 
 def run_steps(abi, h, toks, first, steps):
+    """Decode steps with device-side feedback: row s of toks feeds step s, whose
+    greedy tokens land in row s + 1."""
     for s in range(first, first + steps):
-        abi.mk_decode_step(h, toks[s:s + 1], toks[s + 1:s + 2])
+        abi.mk_decode_step(h, toks[s], toks[s + 1])
 
 
 def timed_pass(abi, h, prompt_t, toks, steps, torch, time_types=()):
     """reset + prefill, then exactly `steps` decode steps between two events."""
     abi.mk_reset(h)
-    abi.mk_prefill(h, prompt_t, toks[0:1])
+    abi.mk_prefill(h, prompt_t, toks[0])
     abi.mk_synchronize(h)
     if time_types:
         abi.mk_time_ops(h, time_types, steps * 64 + 64)
@@ -101,8 +114,9 @@ def timed_pass(abi, h, prompt_t, toks, steps, torch, time_types=()):
 def time_decode(abi, h, prompt_t, steps, warmup, shape, torch):
     """Headline pass (graph-replayed steps), then an eager pass whose gate/up
     launches are bracketed by HIP events, then an untimed per-operator breakdown."""
-    toks = torch.zeros(max(steps, warmup) + 64 + 1, dtype=torch.int32, device=torch.device("cuda"))
-    abi.mk_prefill(h, prompt_t, toks[0:1])                       # warm-up generation
+    B = prompt_t.shape[0]
+    toks = torch.zeros(max(steps, warmup) + 64 + 1, B, dtype=torch.int32, device=torch.device("cuda"))
+    abi.mk_prefill(h, prompt_t, toks[0])                         # warm-up generation
     run_steps(abi, h, toks, 0, warmup)
     abi.mk_synchronize(h)
     total, _ = timed_pass(abi, h, prompt_t, toks, steps, torch)
@@ -110,7 +124,7 @@ def time_decode(abi, h, prompt_t, steps, warmup, shape, torch):
     eager_total, times = timed_pass(abi, h, prompt_t, toks, steps, torch, ["gu"])
     gu = times.get("gu", (0.0, 0))
     same = bool((toks[:steps + 1].cpu().numpy() == tokens).all())
-    abi.mk_time_ops(h, list(abi.TASK_TYPES), 32 * (6 * shape.n_layers + 2))
+    abi.mk_time_ops(h, list(abi.OP_TYPES), 32 * (8 * shape.n_layers + 3))
     run_steps(abi, h, toks, steps, 32)
     breakdown = abi.mk_read_op_times(h)
     return total, eager_total, gu, same, breakdown
@@ -127,7 +141,7 @@ def cpu_baseline(shape, weights, prompt):
             threads = max(i.get("num_threads", 0) for i in info) or threads
     except Exception:
         pass
-    dec = D.Decoder(shape, weights, 1, 4, cache_weights=False)
+    dec = D.Decoder(shape, weights, prompt.shape[0], 4, cache_weights=False)
     t = time.perf_counter()
     dec.step(prompt[:, 0])
     ms = (time.perf_counter() - t) * 1000.0
@@ -146,7 +160,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md).", file=sys.stderr)
+              "(it measures one GPU's share of the work).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -156,42 +170,44 @@ def main():
 
     log = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
     wl = presets.WORKLOADS[args.workload]
-    shape = wl.shape
-    if wl.batch != 1:
-        print(f"bench.py: workload {wl.name} (batch {wl.batch}) is not supported yet", file=sys.stderr)
-        sys.exit(2)
+    shape, B = wl.shape, wl.batch
     steps, warmup = args.steps, args.warmup
     max_seq = wl.prompt_len + max(steps, warmup)
     t = time.time()
-    weights = gen.gen_weights(shape, wl.weight_seed)
-    log(f"weights generated in {time.time() - t:.1f}s")
-    t = time.time()
-    dw = runtime.upload_weights(weights)
+    if B == 1:
+        weights = gen.gen_weights(shape, wl.weight_seed)
+        dw = runtime.upload_weights(weights)
+    else:  # one tensor at a time through host memory (the 70B shape is 141 GB)
+        weights = None
+        dw = runtime.generate_device_weights(shape, wl.weight_seed)
     torch.cuda.synchronize()
-    log(f"weights uploaded in {time.time() - t:.1f}s")
+    log(f"weights generated and uploaded in {time.time() - t:.1f}s")
     prompt = gen.gen_prompt(wl)
     prompt_t = torch.from_numpy(prompt).cuda()
 
-    h = runtime.create(shape, dw, max_seq + 64, 1, abi.MK_MODE_PER_OP)
+    # batch 1 keeps an fp32 KV cache; the batched workloads state a bf16 cache
+    kv_fp32 = B == 1
+    h = runtime.create(shape, dw, max_seq + 64, B, abi.MK_MODE_PER_OP, kv_fp32=kv_fp32)
     total, eager_total, (gu_ms, gu_n), same_tokens, breakdown = time_decode(abi, h, prompt_t, steps, warmup, shape,
                                                                              torch)
     abi.mk_destroy(h)
     ms = total / steps
     kern_ms = gu_ms / max(gu_n, 1)
-    bytes_steps = [step_bytes(shape, wl.prompt_len + s + 1) for s in range(steps)]
+    bytes_steps = [step_bytes(shape, wl.prompt_len + s + 1, B, 4 if kv_fp32 else 2) for s in range(steps)]
     alg_bytes = float(np.mean(bytes_steps))
     bound_ms = alg_bytes / (PEAK_GBPS * 1e9) * 1e3
-    kb = gu_bytes(shape)
+    kb = gu_bytes(shape, B)
     achieved = kb / (kern_ms * 1e-3) / 1e9
-    log(f"per-op: {ms:.4f} ms/token, bound {bound_ms:.4f} ms, step {alg_bytes / (ms * 1e-3) / 1e9:.0f} GB/s; "
+    unit = "ms/token" if B == 1 else "ms/step"
+    log(f"per-op: {ms:.4f} {unit}, bound {bound_ms:.4f} ms, step {alg_bytes / (ms * 1e-3) / 1e9:.0f} GB/s; "
         f"gate/up kernel {kern_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
     op_breakdown = {k: {"ms_per_step": v[0] / 32.0, "launches_per_step": v[1] / 32.0} for k, v in breakdown.items()}
     log("breakdown (ms/step): " + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in op_breakdown.items()))
     traffic = load_traffic(wl.name)
     res = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == "llama8b" else f"ms/step decode ({wl.name}, batch {B}), 1 MI355X",
         "value": ms,
-        "unit": "ms/token",
+        "unit": unit,
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
@@ -201,14 +217,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: batch 1, prompt {wl.prompt_len}, {steps} greedy decode steps",
-                   "batch": 1, "prompt_len": wl.prompt_len, "decode_steps": steps, "mode": "per_op (HIP graph per step)",
+        "config": {"workload": f"{wl.name}: batch {B}, prompt {wl.prompt_len}, {steps} greedy decode steps",
+                   "batch": B, "prompt_len": wl.prompt_len, "decode_steps": steps,
+                   "mode": "per_op (HIP graph per step)", "kv_cache": "fp32" if kv_fp32 else "bf16",
                    "parallelism": "none (1 GPU)"},
-        "tokens_per_s": 1000.0 / ms,
+        "tokens_per_s": 1000.0 * B / ms,
         "achieved_gbps": alg_bytes / (ms * 1e-3) / 1e9,
         "bound_ms_per_token": bound_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBPS, "traffic": traffic, "kernel": "mk_op_gu",
+                     "frac": achieved / PEAK_GBPS, "traffic": traffic,
+                     "kernel": "mk_op_gu" if B == 1 else f"mk_b_gu_b{1 if B <= 16 else 2 if B <= 32 else 4}",
                      "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": kb},
         "step_frac_of_hbm_bound": bound_ms / ms,
         "eager_ms_per_step": eager_total / steps,
@@ -217,7 +235,11 @@ def main():
         "megakernel": {"status": "disabled", "reason": "cooperative persistent launch did not complete on MI355X"},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if B > 1:
+        gu_flop = 2.0 * B * 2 * shape.ffn * shape.hidden
+        res["gu_matrix_core_tflops"] = gu_flop / (kern_ms * 1e-3) / 1e12
+        res["gu_matrix_core_frac_of_bf16_peak"] = res["gu_matrix_core_tflops"] / 2500.0
+    if not args.no_cpu_baseline and weights is not None:
         log("timing the oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(shape, weights, prompt)
     print(json.dumps(res), flush=True)

@@ -10,7 +10,7 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmk.so")
+LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(PKG, "libmk.so")  # MK_LIBRARY: another build of the library
 
 MK_ABI_VERSION = 1
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_OUT_OF_MEMORY, MK_ERR_HIP = 0, -1, -2, -3
@@ -94,6 +94,7 @@ SIGNATURES = {
     "mk_t_gemv": ([_P, _P, _P, _I32, _I32, _P], _I32),
     "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _P], _I32),
     "mk_t_argmax": ([_P, _I32, _P, _P], _I32),
     "mk_device_info": ([ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
 }
@@ -264,12 +265,14 @@ def mk_read_trace(h: Handle):
 
 
 TASK_TYPES = {"qkv": 1, "attn": 2, "merge": 3, "o": 4, "gu": 5, "down": 6, "lm": 7, "argmax": 8}
+# operator timing also knows the RMSNorm launches of the batched path
+OP_TYPES = {"norm": 0, **TASK_TYPES}
 
 
 def mk_time_ops(h: Handle, types, max_launches: int):
     mask = 0
     for t in types:
-        mask |= 1 << TASK_TYPES[t]
+        mask |= 1 << OP_TYPES[t]
     _check(lib.mk_time_ops(h.ptr, mask, max_launches), "mk_time_ops")
 
 
@@ -278,7 +281,7 @@ def mk_read_op_times(h: Handle):
     ms = (ctypes.c_double * 9)()
     n = (ctypes.c_int32 * 9)()
     _check(lib.mk_read_op_times(h.ptr, ms, n), "mk_read_op_times")
-    return {name: (ms[i], n[i]) for name, i in TASK_TYPES.items() if n[i]}
+    return {name: (ms[i], n[i]) for name, i in OP_TYPES.items() if n[i]}
 
 
 def mk_t_gemv(W, x, y, stream=None):
@@ -297,6 +300,15 @@ def mk_t_attention(q, k, v, T, split, o, stream=None):
     f32 = 1 if k.element_size() == 4 else 0
     _check(lib.mk_t_attention(_ptr(q), _ptr(k), _ptr(v), S * hd, nq, nkv, hd, T, split, f32, _ptr(o),
                               _stream(stream)), "mk_t_attention")
+
+
+def mk_t_bgemm(W, A, Y, B, stream=None):
+    """Y = (A[0, :B] + A[1, :B]) @ W.T on the matrix cores; A [2, Bp, K] bf16 hi/lo
+    planes with Bp = 16, 32 or 64 rows, rows >= B zero."""
+    N, K = W.shape
+    Bp = 16 * (1 if B <= 16 else 2 if B <= 32 else 4)
+    assert A.shape == (2, Bp, K) and Y.shape == (B, N)
+    _check(lib.mk_t_bgemm(_ptr(W), _ptr(A), _ptr(Y), N, K, B, _stream(stream)), "mk_t_bgemm")
 
 
 def mk_t_argmax(x, out, stream=None):

@@ -3,6 +3,7 @@
 Run as `python -m decode_persistent_megakernel_02_amd.build`; __graft_entry__.build()
 calls `build_all()`.  Always recompiles.
 """
+import hashlib
 import os
 import subprocess
 import sys
@@ -25,12 +26,15 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build_lib(verbose=False, out=LIB):
+def build_lib(verbose=False, out=LIB, defines=()):
+    """Compile the kernels and the host library into `out`; `defines` are extra
+    -D options (the MK_SHAPE_* tuning knobs) given to every compile."""
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    srcs = [os.path.join(CSRC, f) for f in ("kernels.hip", "api.hip")]
+    srcs = [os.path.join(CSRC, f) for f in ("kernels.hip", "batched.hip", "api.hip")]
     host = os.path.join(CSRC, "graph.cpp")
-    inc = ["-I", CSRC, "-I", os.path.join(ROOT, "include")]
-    bdir = os.path.join(PKG, "_build")
+    inc = ["-I", CSRC, "-I", os.path.join(ROOT, "include")] + [f"-D{d}" for d in defines]
+    bdir = os.path.join(PKG, "_build", hashlib.sha1(" ".join(defines).encode()).hexdigest()[:8]) if defines \
+        else os.path.join(PKG, "_build")
     os.makedirs(bdir, exist_ok=True)
     objs = []
     for src in srcs:

@@ -32,6 +32,14 @@ mk_status fail(mk_status s, const std::string& m) {
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+// Positions per attention split when several sequences share a step: the
+// (sequence, KV head) pairs already give the grid its width, so each
+// workgroup takes a longer stretch of the cache.
+constexpr int kBatchedSplit = 128;
+
+// Batch tiles (16 rows each) of the batched projections: 1, 2 or 4.
+int batch_tiles(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : 4; }
+
 std::string check_config(const mk_config* c) {
   if (!c) return "config is NULL";
   if (c->abi_version != MK_ABI_VERSION) return "abi_version mismatch";
@@ -56,7 +64,7 @@ GraphConfig graph_config(const mk_config* c, int ncu) {
   GraphConfig g;
   g.L = c->n_layers; g.H = c->hidden; g.nq = c->n_q_heads; g.nkv = c->n_kv_heads; g.hd = c->head_dim;
   g.F = c->ffn; g.V = c->vocab; g.B = c->max_batch; g.max_seq = c->max_seq;
-  g.split = c->attn_split ? c->attn_split : auto_split(c->max_seq);
+  g.split = c->attn_split ? c->attn_split : c->max_batch > 1 ? kBatchedSplit : auto_split(c->max_seq);
   g.ncu = ncu;
   return g;
 }
@@ -83,7 +91,9 @@ struct mk_handle {
   std::vector<void*> allocs;
   Task* d_stage_tasks = nullptr;
   int page_floats = 0, scratch_floats = 0, lds_mega = 0;
-  int op_page[9] = {0}, op_lds[9] = {0}, op_grid_cap[9] = {0};  // per task type
+  int op_page[9] = {0}, op_lds[9] = {0}, op_grid_cap[9] = {0}, op_sf[9] = {0};  // per task type
+  bool op_exact[9] = {false};
+  bool batched = false;                 // B > 1: matrix-core projections (batched.hip)
   int length = 0, batch = 0;
   uint32_t epoch = 0;
   bool poisoned = false;
@@ -131,7 +141,19 @@ struct mk_handle {
 
 namespace {
 
-const void* op_kernel(int type) {
+// The per-operator kernel of a task type; `exact` selects the variant for K a
+// multiple of 512 whose 512-column chunk count is a multiple of D.
+const void* op_kernel(int type, bool exact = false) {
+  if (exact) {
+    switch (type) {
+      case TT_QKV: return reinterpret_cast<const void*>(&mk_op_qkv_x);
+      case TT_O: return reinterpret_cast<const void*>(&mk_op_o_x);
+      case TT_GU: return reinterpret_cast<const void*>(&mk_op_gu_x);
+      case TT_DOWN: return reinterpret_cast<const void*>(&mk_op_down_x);
+      case TT_LM: return reinterpret_cast<const void*>(&mk_op_lm_x);
+      default: break;
+    }
+  }
   switch (type) {
     case TT_QKV: return reinterpret_cast<const void*>(&mk_op_qkv);
     case TT_ATTN: return reinterpret_cast<const void*>(&mk_op_attn);
@@ -161,12 +183,90 @@ mk_status device_facts(int* ncu, double* ticks_per_us, int* max_lds) {
   return MK_OK;
 }
 
+// Batched projection kernels by operator (QKV, O, GU, DOWN, LM) and batch tiles (1, 2, 4).
+const void* bgemm_kernel(int type, int bt) {
+  const int i = bt == 1 ? 0 : bt == 2 ? 1 : 2;
+  static const void* const k[5][3] = {
+      {reinterpret_cast<const void*>(&mk_b_qkv_b1), reinterpret_cast<const void*>(&mk_b_qkv_b2),
+       reinterpret_cast<const void*>(&mk_b_qkv_b4)},
+      {reinterpret_cast<const void*>(&mk_b_o_b1), reinterpret_cast<const void*>(&mk_b_o_b2),
+       reinterpret_cast<const void*>(&mk_b_o_b4)},
+      {reinterpret_cast<const void*>(&mk_b_gu_b1), reinterpret_cast<const void*>(&mk_b_gu_b2),
+       reinterpret_cast<const void*>(&mk_b_gu_b4)},
+      {reinterpret_cast<const void*>(&mk_b_down_b1), reinterpret_cast<const void*>(&mk_b_down_b2),
+       reinterpret_cast<const void*>(&mk_b_down_b4)},
+      {reinterpret_cast<const void*>(&mk_b_lm_b1), reinterpret_cast<const void*>(&mk_b_lm_b2),
+       reinterpret_cast<const void*>(&mk_b_lm_b4)}};
+  const int row = type == TT_QKV ? 0 : type == TT_O ? 1 : type == TT_GU ? 2 : type == TT_DOWN ? 3 : 4;
+  return k[row][i];
+}
+int bgemm_tiles(int type) { return type == TT_O || type == TT_DOWN ? 1 : 2; }  // 16-row tiles per workgroup
+int bgemm_lds(int type, int bt) { return kBgemmWaves * bgemm_tiles(type) * bt * 256 * 4 + kMaxBatch * 8; }
+
+// Workgroups of a batched projection: one per group of 16-row tiles.
+int bgemm_groups(const Params& P, int type) {
+  switch (type) {
+    case TT_QKV: return (P.nq + 2 * P.nkv) * P.hd / 32;
+    case TT_O: case TT_DOWN: return (P.H + 15) / 16;
+    case TT_GU: return (P.F + 15) / 16;
+    default: return (P.V + 31) / 32;
+  }
+}
+
+// One step of the batched path: per layer norm, QKV, attention, merge, O,
+// norm, gate/up, down; then the final norm, the LM head and the argmax.
+// Timed launches are bracketed by events (type 0 = the norms).
+mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
+  Params Pc = h->P;
+  const Step* sp = h->d_step;
+  const int bt = batch_tiles(Pc.B);
+  auto launch = [&](int type, const void* fn, dim3 grid, dim3 block, void** args, size_t lds) -> mk_status {
+    const bool timed = timed_ok && ((h->timed_mask >> type) & 1) && 2 * (h->ev_used + 1) <= (int)h->ev_pool.size();
+    if (timed) HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used], st));
+    HIP_TRY(hipLaunchKernel(fn, grid, block, args, lds, st));
+    if (timed) {
+      HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used + 1], st));
+      h->ev_type[h->ev_used++] = type;
+    }
+    return MK_OK;
+  };
+  auto norm = [&](int layer, int kind) -> mk_status {
+    void* args[] = {&Pc, &sp, &layer, &kind};
+    return launch(0, reinterpret_cast<const void*>(&mk_b_norm), dim3(Pc.B), dim3(kNormThreads), args, 0);
+  };
+  auto gemm = [&](int type, int layer) -> mk_status {
+    void* args[] = {&Pc, &sp, &layer};
+    return launch(type, bgemm_kernel(type, bt), dim3(bgemm_groups(Pc, type)), dim3(kBgemmWaves * kWave), args,
+                  (size_t)bgemm_lds(type, bt));
+  };
+  for (int l = 0; l < Pc.L; ++l) {
+    MK_TRY(norm(l, 0));
+    MK_TRY(gemm(TT_QKV, l));
+    {
+      int layer = l;
+      void* args[] = {&Pc, &sp, &layer};
+      MK_TRY(launch(TT_ATTN, reinterpret_cast<const void*>(&mk_op_attn_split), dim3(Pc.B * Pc.nkv * Pc.nsplit),
+                    dim3(kAttnWaves * kWave), args, (size_t)h->attn_lds));
+      MK_TRY(launch(TT_MERGE, reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(Pc.B * Pc.nkv),
+                    dim3((Pc.nq / Pc.nkv) * kWave), args, 0));
+    }
+    MK_TRY(gemm(TT_O, l));
+    MK_TRY(norm(l, 1));
+    MK_TRY(gemm(TT_GU, l));
+    MK_TRY(gemm(TT_DOWN, l));
+  }
+  MK_TRY(norm(Pc.L, 2));
+  MK_TRY(gemm(TT_LM, Pc.L));
+  void* args[] = {&Pc, &sp};
+  return launch(TT_ARGMAX, reinterpret_cast<const void*>(&mk_b_argmax), dim3(1), dim3(kMaxBatch), args, 0);
+}
+
 // Enqueue the operator launches of one step (kernel-per-operator mode) on `st`.
 mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
+  if (h->batched) return enqueue_batched(h, st, timed_ok);
   const auto& g = h->graph;
   Params Pc = h->P;
   const Step* sp = h->d_step;
-  int sf = h->scratch_floats;
   for (size_t s = 0; s + 1 < g.stage_begin.size(); ++s) {
     const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
     if (count <= 0) continue;
@@ -184,12 +284,16 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
         HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(h->P.B * h->P.nkv),
                                 dim3((h->P.nq / h->P.nkv) * kWave), args, 0, st));
     } else {
-      const int grid = std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]);
+      // a GEMV wave holds at most kMaxTasksPerWave results
+      const int min_grid = (count + kWaves * kMaxTasksPerWave - 1) / (kWaves * kMaxTasksPerWave);
+      const int grid = std::max(min_grid, std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]));
       const Task* tasks = h->d_stage_tasks + b0;
       int opf = h->op_page[type];
       int cnt = count;
-      void* args[] = {&Pc, &sp, &tasks, &cnt, &opf, &sf};
-      HIP_TRY(hipLaunchKernel(op_kernel(type), dim3(grid), dim3(kWaves * kWave), args, (size_t)h->op_lds[type], st));
+      int osf = h->op_sf[type];
+      void* args[] = {&Pc, &sp, &tasks, &cnt, &opf, &osf};
+      HIP_TRY(hipLaunchKernel(op_kernel(type, h->op_exact[type]), dim3(grid), dim3(kWaves * kWave), args,
+                              (size_t)h->op_lds[type], st));
     }
     if (timed) {
       HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used + 1], st));
@@ -273,7 +377,6 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
         !w->w_up[l] || !w->w_down[l])
       return fail(MK_ERR_INVALID_ARG, "weights: NULL pointer in layer " + std::to_string(l));
-  if (cfg->max_batch != 1) return fail(MK_ERR_UNSUPPORTED, "max_batch > 1 is not implemented yet");
   // The cooperative persistent launch did not complete on the MI355X test box
   // (the stream never drained although every in-kernel wait is bounded); until
   // the cause is known this mode is refused rather than risked.
@@ -296,10 +399,16 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   h->ticks_per_us = tpu;
 
   const GraphConfig gc = graph_config(cfg, ncu);
-  std::string e = build_graph(gc, h->graph);
-  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
-  e = validate_graph(h->graph);
-  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "graph validation: " + e);
+  h->batched = cfg->max_batch > 1;
+  if (h->batched) {  // launches are issued per operator; no task table
+    h->graph.cfg = gc;
+    h->graph.nsplit = (cfg->max_seq + gc.split - 1) / gc.split;
+  } else {
+    std::string e = build_graph(gc, h->graph);
+    if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
+    e = validate_graph(h->graph);
+    if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "graph validation: " + e);
+  }
   const Graph& g = h->graph;
 
   const int L = cfg->n_layers, H = cfg->hidden, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, hd = cfg->head_dim;
@@ -356,6 +465,21 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   P.h = P.attn_out + n_aout;
   MK_TRY(h->alloc(&P.lm_part, B));
   HIP_TRY(hipMemset(P.lm_part, 0, B * sizeof(unsigned long long)));
+  if (h->batched) {  // bf16 MFMA operands; rows B..Bp-1 are zero and never written
+    const int bt = batch_tiles(B);
+    P.Bp = 16 * bt;
+    const int64_t n_ax = 2ll * P.Bp * H, n_ao = 2ll * P.Bp * nq * hd, n_ah = 2ll * P.Bp * F;  // hi + lo planes
+    uint16_t* ops = nullptr;
+    MK_TRY(h->alloc(&ops, n_ax + n_ao + n_ah));
+    HIP_TRY(hipMemset(ops, 0, (n_ax + n_ao + n_ah) * 2));
+    P.ax = ops;
+    P.ao = ops + n_ax;
+    P.ah = ops + n_ax + n_ao;
+    for (int t : {TT_QKV, TT_O, TT_GU, TT_DOWN, TT_LM}) {
+      if (bgemm_lds(t, bt) > max_lds) return fail(MK_ERR_UNSUPPORTED, "batched projection LDS need exceeds the device");
+      HIP_TRY(hipFuncSetAttribute(bgemm_kernel(t, bt), hipFuncAttributeMaxDynamicSharedMemorySize, bgemm_lds(t, bt)));
+    }
+  }
 
   // RoPE angle tables, computed in double precision
   {
@@ -403,31 +527,42 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   h->page_floats = round_up(std::max({H, nq * hd, F}), 8);
   h->scratch_floats = round_up(G * hd + G * kWave, 4);
   h->lds_mega = (int)sizeof(Lds) + 2 * h->page_floats * 4 + kWorkers * h->scratch_floats * 4;
-  for (int t = TT_QKV; t <= TT_ARGMAX; ++t) {
+  for (int t = TT_QKV; t <= TT_ARGMAX && !h->batched; ++t) {  // single-sequence operator kernels
     int pfl = 0;
     if (t == TT_QKV || t == TT_GU || t == TT_LM) pfl = H;
     else if (t == TT_O) pfl = nq * hd;
     else if (t == TT_DOWN) pfl = F;
     h->op_page[t] = round_up(pfl, 8);
-    h->op_lds[t] = (int)sizeof(Lds) + h->op_page[t] * 4 + (t == TT_ATTN ? kWaves * h->scratch_floats * 4 : 0);
+    const int rows = t == TT_QKV ? TaskShape<TT_QKV>::R : t == TT_O ? TaskShape<TT_O>::R
+                   : t == TT_GU ? TaskShape<TT_GU>::R : t == TT_DOWN ? TaskShape<TT_DOWN>::R
+                   : t == TT_LM ? TaskShape<TT_LM>::R : 0;
+    const int depth = t == TT_QKV ? TaskShape<TT_QKV>::D : t == TT_O ? TaskShape<TT_O>::D
+                    : t == TT_GU ? TaskShape<TT_GU>::D : t == TT_DOWN ? TaskShape<TT_DOWN>::D
+                    : t == TT_LM ? TaskShape<TT_LM>::D : 0;
+    h->op_exact[t] = rows > 0 && pfl % 512 == 0 && (pfl / 512) % depth == 0;
+    // per-wave scratch: attention state, or the results of the wave's GEMV tasks
+    h->op_sf[t] = t == TT_ATTN ? h->scratch_floats : kMaxTasksPerWave * rows;
+    h->op_lds[t] = (int)sizeof(Lds) + h->op_page[t] * 4 + kWaves * h->op_sf[t] * 4;
     if (h->op_lds[t] > max_lds)
       return fail(MK_ERR_UNSUPPORTED, "operator LDS need exceeds " + std::to_string(max_lds));
-    HIP_TRY(hipFuncSetAttribute(op_kernel(t), hipFuncAttributeMaxDynamicSharedMemorySize, h->op_lds[t]));
+    const void* fn = op_kernel(t, h->op_exact[t]);
+    HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, h->op_lds[t]));
     int nb = 0;
-    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, op_kernel(t), kWaves * kWave, h->op_lds[t]));
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kWaves * kWave, h->op_lds[t]));
     h->op_grid_cap[t] = std::max(1, nb) * ncu;
   }
   h->attn_lds = (G * hd + kAttnWaves * G * kWave + kAttnWaves * G * (hd + 2)) * 4;
   if (h->attn_lds > max_lds) return fail(MK_ERR_UNSUPPORTED, "attention LDS need exceeds the device limit");
   HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_op_attn_split),
                               hipFuncAttributeMaxDynamicSharedMemorySize, h->attn_lds));
-  if (h->lds_mega > max_lds)
-    return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(h->lds_mega) + " B exceeds " + std::to_string(max_lds));
-  // keep one persistent workgroup per CU: ask for more than half the LDS
-  if (h->lds_mega <= max_lds / 2) h->lds_mega = max_lds / 2 + 1024;
-  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_persistent),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, h->lds_mega));
   if (cfg->mode == MK_MODE_MEGAKERNEL) {
+    if (h->lds_mega > max_lds)
+      return fail(MK_ERR_UNSUPPORTED,
+                  "LDS need " + std::to_string(h->lds_mega) + " B exceeds " + std::to_string(max_lds));
+    // keep one persistent workgroup per CU: ask for more than half the LDS
+    if (h->lds_mega <= max_lds / 2) h->lds_mega = max_lds / 2 + 1024;
+    HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_persistent),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, h->lds_mega));
     int nb = 0;
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&mk_persistent),
                                                          kWaves * kWave, h->lds_mega));
@@ -735,6 +870,20 @@ mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t h
   hipError_t e = hipStreamSynchronize(st);
   (void)hipFree(part);
   if (e != hipSuccess) return fail(MK_ERR_HIP, std::string("attention: ") + hipGetErrorString(e));
+  return MK_OK;
+}
+
+mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t K, int32_t B, void* stream) {
+  g_err.clear();
+  if (!W || !A || !Y || N < 1 || K < 8 || K % 8 || B < 1 || B > kMaxBatch)
+    return fail(MK_ERR_INVALID_ARG, "bad bgemm arguments");
+  const int lds = kBgemmWaves * batch_tiles(B) * 256 * 4;
+  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_t_bgemm_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+  hipLaunchKernelGGL(mk_t_bgemm_kernel, dim3((N + 15) / 16), dim3(kBgemmWaves * kWave), (unsigned)lds,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W),
+                     static_cast<const uint16_t*>(A), Y, N, K, B);
+  HIP_TRY(hipGetLastError());
   return MK_OK;
 }
 

@@ -100,29 +100,44 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // Row r (r < split) starts at base0 + r * stride, row r >= split at
 // base1 + (r - split) * stride (both in 16-byte vectors).  With r a
 // compile-time constant after unrolling, every address is base + constant.
+// A row outside `mask` reads row 0 instead (always in bounds; its result is
+// discarded), so no load is ever predicated.
 template <int R>
 struct GemvRows {
   const v4u* base0;
   const v4u* base1;
   int64_t stride;  // vectors between consecutive rows
   int split;       // rows taken from base0
-  uint32_t mask;   // bit r set: row r valid
+  uint32_t mask;   // bit r set: row r valid (bit 0 always set)
   int nvec;        // K / 8 (16-byte vectors per row)
   __device__ __forceinline__ const v4u* row(int r) const {
+    if (!((mask >> r) & 1)) return base0;
     return r < split ? base0 + r * stride : base1 + (r - split) * stride;
   }
 };
 
-__device__ __forceinline__ v4u ld_w(const v4u* p) { return __builtin_nontemporal_load(p); }
+// Weight loads go through the global address space explicitly: the layer
+// pointer tables hold generic pointers, and a generic (flat) load also counts
+// against the LDS counter, so every wait for one weight vector would drain
+// all loads in flight.
+typedef const __attribute__((address_space(1))) v4u* gv4u_ptr;
+__device__ __forceinline__ v4u ld_w(const v4u* p) { return __builtin_nontemporal_load((gv4u_ptr)p); }
+__device__ __forceinline__ v4u ld_g(const v4u* p) { return *(gv4u_ptr)p; }
 
-template <int R, int D>
+// Every streaming load below is unconditional.  A load under a divergent
+// branch leaves the compiler unable to count loads in flight, and it then
+// waits for all of them at the next use, draining the pipeline.  With EXACT
+// (K a multiple of 512 and the chunk count a multiple of D, true of every
+// production shape) no lane is ever out of range and every address is the
+// row base plus a constant; otherwise out-of-range vectors read a clamped,
+// in-bounds address and are zeroed on the activation side.
+template <int R, int D, bool EXACT>
 __device__ __forceinline__ void gemv_prefetch(v4u (&buf)[D][R], const GemvRows<R>& g, int lane) {
 #pragma unroll
   for (int s = 0; s < D; ++s) {
-    const int v = s * kWave + lane;
+    const int v = EXACT ? s * kWave + lane : min(s * kWave + lane, g.nvec - 1);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      buf[s][r] = ((g.mask >> r) & 1) && v < g.nvec ? ld_w(g.row(r) + v) : v4u{0u, 0u, 0u, 0u};
+    for (int r = 0; r < R; ++r) buf[s][r] = ld_w(g.row(r) + v);
   }
 }
 
@@ -138,36 +153,40 @@ __device__ __forceinline__ float dot8(v4u w, const float4& a, const float4& b, f
   return acc;
 }
 
-// y[r] = sum_k W[r][k] * xs[k] for the R rows (uniform across the wave).
-template <int R, int D>
+// Chunk c (vectors c*64 + lane) of the R rows, held in `slot`, dotted with xs.
+template <int R, bool EXACT>
+__device__ __forceinline__ void gemv_consume(const v4u (&slot)[R], int c, int nvec, const float* xs, int lane,
+                                             float (&acc)[R]) {
+  const int v = c * kWave + lane, vc = EXACT ? v : min(v, nvec - 1);
+  float4 xa = *reinterpret_cast<const float4*>(xs + vc * 8);
+  float4 xb = *reinterpret_cast<const float4*>(xs + vc * 8 + 4);
+  if (!EXACT && v >= nvec) xa = xb = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = dot8(slot[r], xa, xb, acc[r]);
+}
+
+// y[r] = sum_k W[r][k] * xs[k] for the R rows (uniform across the wave).  The
+// chunks run in rounds of D: every round but the last refills each slot with
+// the chunk D ahead right after consuming it, the last round only consumes.
+template <int R, int D, bool EXACT>
 __device__ __forceinline__ void gemv_run(v4u (&buf)[D][R], const GemvRows<R>& g, const float* xs, int lane,
                                          float (&y)[R]) {
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  const int nchunks = (g.nvec + kWave - 1) / kWave;
-  for (int c0 = 0; c0 < nchunks; c0 += D) {
+  const int nchunks = (g.nvec + kWave - 1) / kWave, nrounds = (nchunks + D - 1) / D;
+  for (int rd = 0; rd + 1 < nrounds; ++rd) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      const int c = c0 + s;
-      if (c < nchunks) {
-        const int v = c * kWave + lane;
-        float4 xa = make_float4(0.f, 0.f, 0.f, 0.f), xb = xa;
-        if (v < g.nvec) {
-          xa = *reinterpret_cast<const float4*>(xs + v * 8);
-          xb = *reinterpret_cast<const float4*>(xs + v * 8 + 4);
-        }
+      const int c = rd * D + s;
+      gemv_consume<R, EXACT>(buf[s], c, g.nvec, xs, lane, acc);
+      const int vn = EXACT ? (c + D) * kWave + lane : min((c + D) * kWave + lane, g.nvec - 1);
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = dot8(buf[s][r], xa, xb, acc[r]);
-        const int vn = (c + D) * kWave + lane;
-        if (c + D < nchunks) {
-#pragma unroll
-          for (int r = 0; r < R; ++r)
-            buf[s][r] = ((g.mask >> r) & 1) && vn < g.nvec ? ld_w(g.row(r) + vn) : v4u{0u, 0u, 0u, 0u};
-        }
-      }
+      for (int r = 0; r < R; ++r) buf[s][r] = ld_w(g.row(r) + vn);
     }
   }
+#pragma unroll
+  for (int s = 0; s < D; ++s) gemv_consume<R, EXACT>(buf[s], (nrounds - 1) * D + s, g.nvec, xs, lane, acc);
 #pragma unroll
   for (int r = 0; r < R; ++r) y[r] = wave_sum(acc[r]);
 }
@@ -395,8 +414,17 @@ __device__ __forceinline__ void attn_partial(const float* q, const KT* kc, const
 // Log-sum-exp merge of n partial records laid out [n][G][HD + 2] (stride
 // `rec_stride` floats between partials); writes the G normalised outputs to
 // out[G][HD].  Records with l == 0 (no positions) are skipped.
+// Splits v into bf16 hi = bf16(v) and lo = bf16(v - hi): hi + lo carries 16
+// significant bits, the operand pair of the batched matrix-core products.
+__device__ __forceinline__ void split_bf16(float v, uint16_t* hi, uint16_t* lo) {
+  const uint16_t h = f2bf(v);
+  *hi = h;
+  *lo = f2bf(v - bf1(h));
+}
+
 template <int HD>
-__device__ __forceinline__ void attn_merge(const float* part, int n, int G, float* out, int lane, int rec_stride = -1) {
+__device__ __forceinline__ void attn_merge(const float* part, int n, int G, float* out, int lane, int rec_stride = -1,
+                                           uint16_t* out_hi = nullptr, uint16_t* out_lo = nullptr) {
   constexpr int DPL = HD / kWave;
   if (rec_stride < 0) rec_stride = G * (HD + 2);
   for (int h = 0; h < G; ++h) {
@@ -417,10 +445,35 @@ __device__ __forceinline__ void attn_merge(const float* part, int n, int G, floa
     }
     const float inv = 1.0f / Lsum;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) out[h * HD + lane * DPL + e] = o[e] * inv;
+    for (int e = 0; e < DPL; ++e) {
+      out[h * HD + lane * DPL + e] = o[e] * inv;
+      if (out_hi) split_bf16(o[e] * inv, out_hi + h * HD + lane * DPL + e, out_lo + h * HD + lane * DPL + e);
+    }
   }
 }
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+
+// ---------------------------------------------------------------------------
+// Cache addressing and token lookup shared by the single-sequence and batched paths.
+__device__ __forceinline__ int64_t kv_off(const Params& P, int l, int b, int g, int p) {
+  return ((((int64_t)l * P.B + b) * P.nkv + g) * P.max_seq + p) * P.hd;
+}
+
+// Stores one K or V element in the cache's element type.
+__device__ __forceinline__ void kv_store(const Params& P, void* cache, int64_t off, float v) {
+  if (P.kv_f32) static_cast<float*>(cache)[off] = v;
+  else static_cast<uint16_t*>(cache)[off] = f2bf(v);
+}
+
+// Token id of batch row b, clamped into [0, V) so that a bad id can never
+// address outside the embedding table; a clamp latches ST_BADTOKEN.
+__device__ __forceinline__ int token_of(const Params& P, const Step& S, int b) {
+  const int t = S.tokens[(int64_t)b * S.tok_stride];
+  if (t >= 0 && t < P.V) return t;
+  atomicCAS(&P.status[1], ST_OK, ST_BADTOKEN);
+  return 0;
+}
+
 
 }  // namespace mk

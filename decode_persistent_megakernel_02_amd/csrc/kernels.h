@@ -18,7 +18,23 @@ MK_OP_DECL(mk_op_gu)
 MK_OP_DECL(mk_op_down)
 MK_OP_DECL(mk_op_lm)
 MK_OP_DECL(mk_op_argmax)
+MK_OP_DECL(mk_op_qkv_x)
+MK_OP_DECL(mk_op_o_x)
+MK_OP_DECL(mk_op_gu_x)
+MK_OP_DECL(mk_op_down_x)
+MK_OP_DECL(mk_op_lm_x)
 #undef MK_OP_DECL
+// batched path (batched.hip)
+#define MK_BGEMM_DECL(name) extern "C" __global__ void name(Params P, const Step* S, int layer);
+MK_BGEMM_DECL(mk_b_qkv_b1) MK_BGEMM_DECL(mk_b_qkv_b2) MK_BGEMM_DECL(mk_b_qkv_b4)
+MK_BGEMM_DECL(mk_b_o_b1) MK_BGEMM_DECL(mk_b_o_b2) MK_BGEMM_DECL(mk_b_o_b4)
+MK_BGEMM_DECL(mk_b_gu_b1) MK_BGEMM_DECL(mk_b_gu_b2) MK_BGEMM_DECL(mk_b_gu_b4)
+MK_BGEMM_DECL(mk_b_down_b1) MK_BGEMM_DECL(mk_b_down_b2) MK_BGEMM_DECL(mk_b_down_b4)
+MK_BGEMM_DECL(mk_b_lm_b1) MK_BGEMM_DECL(mk_b_lm_b2) MK_BGEMM_DECL(mk_b_lm_b4)
+#undef MK_BGEMM_DECL
+extern "C" __global__ void mk_b_norm(Params P, const Step* S, int layer, int kind);
+extern "C" __global__ void mk_b_argmax(Params P, const Step* S);
+extern "C" __global__ void mk_t_bgemm_kernel(const uint16_t* W, const uint16_t* A, float* Y, int N, int K, int B);
 extern "C" __global__ void mk_fill_u32(uint32_t* p, int64_t n, uint32_t v);
 extern "C" __global__ void mk_t_gemv_kernel(const uint16_t* W, const float* x, float* y, int N, int K);
 extern "C" __global__ void mk_t_rmsnorm_kernel(const float* x, const uint16_t* gamma, float eps, float* y, int n);

@@ -20,25 +20,6 @@
 
 namespace mk {
 
-__device__ __forceinline__ int64_t kv_off(const Params& P, int l, int b, int g, int p) {
-  return ((((int64_t)l * P.B + b) * P.nkv + g) * P.max_seq + p) * P.hd;
-}
-
-// Stores one K or V element in the cache's element type.
-__device__ __forceinline__ void kv_store(const Params& P, void* cache, int64_t off, float v) {
-  if (P.kv_f32) static_cast<float*>(cache)[off] = v;
-  else static_cast<uint16_t*>(cache)[off] = f2bf(v);
-}
-
-// Token id of batch row b, clamped into [0, V) so that a bad id can never
-// address outside the embedding table; a clamp latches ST_BADTOKEN.
-__device__ __forceinline__ int token_of(const Params& P, const Step& S, int b) {
-  const int t = S.tokens[(int64_t)b * S.tok_stride];
-  if (t >= 0 && t < P.V) return t;
-  atomicCAS(&P.status[1], ST_OK, ST_BADTOKEN);
-  return 0;
-}
-
 // Where a staged input vector comes from.
 struct StageSrc {
   const float* f32;   // fp32 source, or
@@ -249,10 +230,10 @@ __device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const 
   GemvRows<R> g;
   gemv_setup<TT>(P, d, g);
   v4u buf[D][R];
-  gemv_prefetch<R, D>(buf, g, lane);
+  gemv_prefetch<R, D, false>(buf, g, lane);
   if (!wait()) return false;
   float y[R];
-  gemv_run<R, D>(buf, g, page, lane, y);
+  gemv_run<R, D, false>(buf, g, page, lane, y);
   gemv_epilogue<TT>(P, S, d, g.mask, y, lane, L);
   return true;
 }
@@ -260,39 +241,69 @@ __device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const 
 // A wave's whole sequence of GEMV tasks i0, i0 + stride, ... with two
 // buffers: the next task's first D chunks are in flight while the current
 // task is consumed, so the wave's weight stream does not drain between tasks.
-template <int TT, class Wait>
-__device__ __forceinline__ void gemv_stream(const Params& P, const Step& S, const Task* tasks, int count, int i0,
-                                            int stride, int lane, const float* page, Lds* L, Wait wait) {
+// The R dot products of the wave's j-th task go to res[j * R ...] (LDS); the
+// epilogues run afterwards (gemv_finish), so that no global store is pending
+// while weight loads are in flight (stores and loads share one counter, and
+// a mix of both forces a wait for everything).  Returns the number of tasks.
+template <int TT>
+__device__ __forceinline__ void gemv_put(float* res, int j, const float (&y)[TaskShape<TT>::R], int lane) {
+  constexpr int R = TaskShape<TT>::R;
+  if (lane < R) res[j * R + lane] = pick<R>(y, lane);
+}
+
+template <int TT, bool EXACT, class Wait>
+__device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, int count, int i0, int stride,
+                                           int lane, const float* page, float* res, Wait wait) {
   constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
-  if (i0 >= count) return;
+  if (i0 >= count) return 0;
   v4u bufA[D][R], bufB[D][R];
-  Task dA = tasks[i0], dB;
   GemvRows<R> gA, gB;
-  gemv_setup<TT>(P, dA, gA);
-  gemv_prefetch<R, D>(bufA, gA, lane);
+  gemv_setup<TT>(P, tasks[i0], gA);
+  gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
   wait();
   float y[R];
-  for (int i = i0;;) {
+  int i = i0, j = 0;
+  for (;;) {
     int n = i + stride;
-    if (n < count) {
-      dB = tasks[n];
-      gemv_setup<TT>(P, dB, gB);
-      gemv_prefetch<R, D>(bufB, gB, lane);
+    if (n >= count) {
+      gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
+      gemv_put<TT>(res, j++, y, lane);
+      break;
     }
-    gemv_run<R, D>(bufA, gA, page, lane, y);
-    gemv_epilogue<TT>(P, S, dA, gA.mask, y, lane, L);
-    if (n >= count) break;
+    gemv_setup<TT>(P, tasks[n], gB);
+    gemv_prefetch<R, D, EXACT>(bufB, gB, lane);
+    gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
+    gemv_put<TT>(res, j++, y, lane);
     i = n;
     n = i + stride;
-    if (n < count) {
-      dA = tasks[n];
-      gemv_setup<TT>(P, dA, gA);
-      gemv_prefetch<R, D>(bufA, gA, lane);
+    if (n >= count) {
+      gemv_run<R, D, EXACT>(bufB, gB, page, lane, y);
+      gemv_put<TT>(res, j++, y, lane);
+      break;
     }
-    gemv_run<R, D>(bufB, gB, page, lane, y);
-    gemv_epilogue<TT>(P, S, dB, gB.mask, y, lane, L);
-    if (n >= count) break;
+    gemv_setup<TT>(P, tasks[n], gA);
+    gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
+    gemv_run<R, D, EXACT>(bufB, gB, page, lane, y);
+    gemv_put<TT>(res, j++, y, lane);
     i = n;
+  }
+  return j;
+}
+
+// The epilogues of a wave's n streamed tasks, from their results in res.
+template <int TT>
+__device__ __forceinline__ void gemv_finish(const Params& P, const Step& S, const Task* tasks, int n, int i0,
+                                            int stride, int lane, const float* res, Lds* L) {
+  constexpr int R = TaskShape<TT>::R;
+  __builtin_amdgcn_wave_barrier();
+  for (int j = 0; j < n; ++j) {
+    const Task d = tasks[i0 + j * stride];
+    GemvRows<R> g;
+    gemv_setup<TT>(P, d, g);
+    float y[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) y[r] = res[j * R + r];
+    gemv_epilogue<TT>(P, S, d, g.mask, y, lane, L);
   }
 }
 
@@ -543,7 +554,7 @@ extern "C" __global__ __launch_bounds__(kWaves * kWave, 1) void mk_persistent(Pa
 // tasks, the same bodies.  Wave 0 of each workgroup stages the operator's
 // input vector (with its RMSNorm) into LDS once; every wave then takes tasks
 // in a workgroup-strided loop.
-template <int TT>
+template <int TT, bool EXACT>
 __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const Task* tasks, int count, int page_floats,
                         int scratch_floats) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -551,7 +562,9 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
   float* page = reinterpret_cast<float*>(smem + sizeof(Lds));
   float* scr = page + page_floats;
   const Step S = *Sd;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index made explicitly uniform: task descriptors then load through the
+  // scalar cache and never queue behind the weight stream
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
   const Task first = tasks[0];
   // Every wave stages its slice of the input vector and passes the staging
@@ -568,7 +581,12 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
     return true;
   };
   if constexpr (TT == TT_QKV || TT == TT_O || TT == TT_GU || TT == TT_DOWN || TT == TT_LM) {
-    gemv_stream<TT>(P, S, tasks, count, blockIdx.x * kWaves + wave, gridDim.x * kWaves, lane, page, L, wait);
+    // scratch_floats = result slots per wave (R per task of this wave)
+    const int i0 = blockIdx.x * kWaves + wave, stride = gridDim.x * kWaves;
+    float* res = scr + wave * scratch_floats;
+    const int n = gemv_stream<TT, EXACT>(P, tasks, count, i0, stride, lane, page, res, wait);
+    wait();
+    gemv_finish<TT>(P, S, tasks, n, i0, stride, lane, res, L);
   } else {
     for (int i = blockIdx.x * kWaves + wave; i < count; i += gridDim.x * kWaves) {
       const Task d = tasks[i];
@@ -584,19 +602,26 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
   }
 }
 
-#define MK_OP_KERNEL(name, TT)                                                                              \
+// Each GEMV operator has a generic kernel and an _x kernel for K a multiple of
+// 512 whose chunk count is a multiple of D (no clamped loads).
+#define MK_OP_KERNEL(name, TT, EXACT)                                                                       \
   extern "C" __global__ __launch_bounds__(kWaves * kWave) void name(Params P, const Step* S, const Task* tasks, \
                                                                       int count, int pf, int sf) {        \
-    op_body<TT>(P, S, tasks, count, pf, sf);                                                                \
+    op_body<TT, EXACT>(P, S, tasks, count, pf, sf);                                                         \
   }
-MK_OP_KERNEL(mk_op_qkv, TT_QKV)
-MK_OP_KERNEL(mk_op_attn, TT_ATTN)
-MK_OP_KERNEL(mk_op_merge, TT_MERGE)
-MK_OP_KERNEL(mk_op_o, TT_O)
-MK_OP_KERNEL(mk_op_gu, TT_GU)
-MK_OP_KERNEL(mk_op_down, TT_DOWN)
-MK_OP_KERNEL(mk_op_lm, TT_LM)
-MK_OP_KERNEL(mk_op_argmax, TT_ARGMAX)
+MK_OP_KERNEL(mk_op_qkv, TT_QKV, false)
+MK_OP_KERNEL(mk_op_attn, TT_ATTN, false)
+MK_OP_KERNEL(mk_op_merge, TT_MERGE, false)
+MK_OP_KERNEL(mk_op_o, TT_O, false)
+MK_OP_KERNEL(mk_op_gu, TT_GU, false)
+MK_OP_KERNEL(mk_op_down, TT_DOWN, false)
+MK_OP_KERNEL(mk_op_lm, TT_LM, false)
+MK_OP_KERNEL(mk_op_argmax, TT_ARGMAX, false)
+MK_OP_KERNEL(mk_op_qkv_x, TT_QKV, true)
+MK_OP_KERNEL(mk_op_o_x, TT_O, true)
+MK_OP_KERNEL(mk_op_gu_x, TT_GU, true)
+MK_OP_KERNEL(mk_op_down_x, TT_DOWN, true)
+MK_OP_KERNEL(mk_op_lm_x, TT_LM, true)
 
 // Attention, per-operator path: one workgroup of kAttnWaves waves per
 // (batch row, KV group, split).  The split's positions are dealt to the waves
@@ -676,9 +701,13 @@ extern "C" __global__ __launch_bounds__(kMaxGqa * kWave) void mk_op_attn_merge(P
   const int b = blockIdx.x / P.nkv, grp = blockIdx.x % P.nkv, T = S.pos + 1;
   const int used = (T + P.split - 1) / P.split;
   const float* part = P.attn_part + (((int64_t)layer * P.B + b) * P.nkv + grp) * P.nsplit * G * (P.hd + 2);
-  float* out = P.attn_out + ((int64_t)layer * P.B + b) * P.nq * P.hd + (int64_t)(grp * G + wave) * P.hd;
-  if (P.hd == 128) attn_merge<128>(part + wave * (128 + 2), used, 1, out, lane, G * (128 + 2));
-  else attn_merge<64>(part + wave * (64 + 2), used, 1, out, lane, G * (64 + 2));
+  const int64_t col = (int64_t)(grp * G + wave) * P.hd;
+  float* out = P.attn_out + ((int64_t)layer * P.B + b) * P.nq * P.hd + col;
+  // batched path: also the operand planes of the O-projection
+  uint16_t* ohi = P.ao ? P.ao + (int64_t)b * P.nq * P.hd + col : nullptr;
+  uint16_t* olo = P.ao ? ohi + (int64_t)P.Bp * P.nq * P.hd : nullptr;
+  if (P.hd == 128) attn_merge<128>(part + wave * (128 + 2), used, 1, out, lane, G * (128 + 2), ohi, olo);
+  else attn_merge<64>(part + wave * (64 + 2), used, 1, out, lane, G * (64 + 2), ohi, olo);
 }
 
 // Per-step arguments live in device memory so that a step's launches can be
@@ -712,9 +741,9 @@ extern "C" __global__ __launch_bounds__(kWaves * kWave) void mk_t_gemv_kernel(co
     g.mask = (1u << min(R, N - r0)) - 1;
     g.nvec = K / 8;
     v4u buf[D][R];
-    gemv_prefetch<R, D>(buf, g, lane);
+    gemv_prefetch<R, D, false>(buf, g, lane);
     float v[R];
-    gemv_run<R, D>(buf, g, xs, lane, v);
+    gemv_run<R, D, false>(buf, g, xs, lane, v);
     if (lane < R && r0 + lane < N) y[r0 + lane] = pick<R>(v, lane);
   }
 }

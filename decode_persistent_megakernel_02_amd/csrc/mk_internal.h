@@ -19,6 +19,9 @@ constexpr int kMaxSplit = 4096;       // positions per split-KV attention task
 constexpr int kAttnWaves = 4;         // waves per split in the per-operator attention kernel
 constexpr int kLocalSlots = 64;       // per-CU LDS counters for aggregated event signals
 constexpr int kMaxBatch = 64;         // sequences per step
+constexpr int kMaxTasksPerWave = 64; // GEMV results a wave of a per-operator kernel holds in LDS
+constexpr int kBgemmWaves = 8;        // waves per workgroup of the batched (MFMA) projections
+constexpr int kNormThreads = 256;     // threads per row of the batched RMSNorm kernel
 constexpr uint16_t kNone16 = 0xFFFF;
 constexpr uint8_t kNone8 = 0xFF;
 
@@ -51,13 +54,48 @@ inline constexpr int stage_layer(uint16_t key) { return (key & 0xFFF) - 1; }
 // 512-column chunks of each row in flight (R * D * 16 B per lane, 16 KiB per
 // wave).  The per-operator kernels double-buffer tasks, so a wave holds up to
 // two such buffers.  Long rows (down-projection, K = ffn) take one row.
+// The defaults can be overridden at build time (MK_SHAPE_<OP>_R / _D) to tune
+// for another device; the host graph builder and the kernels read the same
+// values.
+#ifndef MK_SHAPE_QKV_R
+#define MK_SHAPE_QKV_R 2
+#endif
+#ifndef MK_SHAPE_QKV_D
+#define MK_SHAPE_QKV_D 8
+#endif
+#ifndef MK_SHAPE_O_R
+#define MK_SHAPE_O_R 2
+#endif
+#ifndef MK_SHAPE_O_D
+#define MK_SHAPE_O_D 8
+#endif
+#ifndef MK_SHAPE_GU_R
+#define MK_SHAPE_GU_R 2
+#endif
+#ifndef MK_SHAPE_GU_D
+#define MK_SHAPE_GU_D 8
+#endif
+#ifndef MK_SHAPE_DOWN_R
+#define MK_SHAPE_DOWN_R 2
+#endif
+#ifndef MK_SHAPE_DOWN_D
+#define MK_SHAPE_DOWN_D 7
+#endif
+#ifndef MK_SHAPE_LM_R
+#define MK_SHAPE_LM_R 2
+#endif
+#ifndef MK_SHAPE_LM_D
+#define MK_SHAPE_LM_D 8
+#endif
 template <int TT> struct TaskShape;
-template <> struct TaskShape<1> { static constexpr int R = 2, D = 8; };   // QKV: one RoPE pair or two v rows
-template <> struct TaskShape<4> { static constexpr int R = 2, D = 8; };   // O
-template <> struct TaskShape<5> { static constexpr int R = 2, D = 8; };   // GU: one gate + one up row
-template <> struct TaskShape<6> { static constexpr int R = 1, D = 16; };  // DOWN
-template <> struct TaskShape<7> { static constexpr int R = 2, D = 8; };   // LM head
-constexpr int kRowsQkv = 2, kRowsO = 2, kRowsGuPerMatrix = 1, kRowsDown = 1, kRowsLm = 2;
+template <> struct TaskShape<1> { static constexpr int R = MK_SHAPE_QKV_R, D = MK_SHAPE_QKV_D; };    // QKV: one RoPE pair or R v rows
+template <> struct TaskShape<4> { static constexpr int R = MK_SHAPE_O_R, D = MK_SHAPE_O_D; };        // O
+template <> struct TaskShape<5> { static constexpr int R = MK_SHAPE_GU_R, D = MK_SHAPE_GU_D; };      // GU: R/2 gate + R/2 up rows
+template <> struct TaskShape<6> { static constexpr int R = MK_SHAPE_DOWN_R, D = MK_SHAPE_DOWN_D; };  // DOWN
+template <> struct TaskShape<7> { static constexpr int R = MK_SHAPE_LM_R, D = MK_SHAPE_LM_D; };      // LM head
+static_assert(TaskShape<1>::R >= 2 && TaskShape<5>::R % 2 == 0, "QKV needs a RoPE pair; GU pairs gate and up rows");
+constexpr int kRowsQkv = TaskShape<1>::R, kRowsO = TaskShape<4>::R, kRowsGuPerMatrix = TaskShape<5>::R / 2,
+              kRowsDown = TaskShape<6>::R, kRowsLm = TaskShape<7>::R;
 
 // One task.  Interpretation of a0..a3 by type:
 //   QKV   a0 = matrix (0 q, 1 k, 2 v), a1 = first row, a2 = rows, a3 = RoPE pair offset (0 = none)
@@ -114,6 +152,12 @@ struct Params {
   float* attn_part;  // [L][B][nkv][nsplit][G][hd + 2]  (o[hd], m, l)
   float* attn_out;   // [L][B][nq*hd]
   float* h;          // [L][B][F]
+  // bf16 MFMA operands of the batched path, each value v as a pair of planes
+  // hi = bf16(v), lo = bf16(v - hi) ([2][Bp][K]; rows B..Bp-1 stay zero); null when B == 1
+  uint16_t* ax;      // K = H:      normalised input of QKV, gate/up and the LM head
+  uint16_t* ao;      // K = nq*hd:  attention output
+  uint16_t* ah;      // K = F:      SwiGLU output
+  int32_t Bp;        // operand rows: B rounded up to 16, 32 or 64
   unsigned long long* lm_part;  // [B] running argmax key (ordered value, ~index), cleared by the argmax task
   const float* rope_cos;  // [max_seq][hd/2]
   const float* rope_sin;

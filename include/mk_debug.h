@@ -73,7 +73,8 @@ mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, do
 
 /* Time operators with HIP events on the handle's stream (MK_MODE_PER_OP):
  * every launch of a task type whose bit (1 << type, types 1..8 = QKV, ATTN,
- * MERGE, O, GU, DOWN, LM, ARGMAX) is set in type_mask is bracketed by an event
+ * MERGE, O, GU, DOWN, LM, ARGMAX; type 0 = the RMSNorm launches of the batched
+ * path) is set in type_mask is bracketed by an event
  * pair, up to max_launches launches.  mk_read_op_times waits for the stream,
  * returns per-type total milliseconds and launch counts in arrays of 9
  * (index = type), and stops timing. */
@@ -91,6 +92,12 @@ mk_status mk_t_rmsnorm(const float* x, const void* gamma, float eps, float* y, i
  * o fp32 [nq, hd].  Synchronous (allocates and frees its partial buffer). */
 mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t head_stride, int32_t nq, int32_t nkv,
                          int32_t hd, int32_t T, int32_t split, int32_t kv_f32, float* o, void* stream);
+/* Batched projection body (matrix cores): Y[b][n] = sum_k W[n][k] *
+ * (A[0][b][k] + A[1][b][k]) for b < B, n < N; W bf16 [N, K]; A bf16
+ * [2][Bp][K], the hi and lo planes of the activations, with Bp = 16, 32 or 64
+ * rows (the smallest that holds B; rows B..Bp-1 of both planes must be zero);
+ * Y fp32 [B, N]; K a multiple of 8, 1 <= B <= 64. */
+mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t K, int32_t B, void* stream);
 /* out[0] = lowest index of the maximum of x[n] (fp32).  Synchronous. */
 mk_status mk_t_argmax(const float* x, int32_t n, int32_t* out, void* stream);
 

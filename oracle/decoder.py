@@ -89,11 +89,6 @@ def swiglu(r, w_gate, w_up) -> np.ndarray:
     return silu(r @ w_gate.T) * (r @ w_up.T)
 
 
-def swiglu_ffn(r, w_gate, w_up, w_down) -> np.ndarray:
-    """down(silu(r W_g^T) * (r W_u^T)) (reading R-ffn)."""
-    return swiglu(r, w_gate, w_up) @ w_down.T
-
-
 def greedy(logits: np.ndarray) -> np.ndarray:
     """Lowest index of the maximum along the last axis (reading R-argmax)."""
     if not np.all(np.isfinite(logits)):
@@ -212,8 +207,9 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return (((u + r) >> np.uint32(16)) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def forward_full(shape, weights: dict, tokens, kv_bf16: bool = False) -> np.ndarray:
-    """Causal forward of whole sequences without a cache: logits [B, T, V].
+def forward_full(shape, weights: dict, tokens, kv_bf16: bool = False, positions=None) -> np.ndarray:
+    """Causal forward of whole sequences without a cache: logits [B, T, V]
+    (or [B, len(positions), V] for the listed positions only).
 
     Each position t attends to positions 0..t; used to check the cached decode
     chain and as a fast batched prefill for large shapes.  `kv_bf16` rounds the
@@ -241,7 +237,9 @@ def forward_full(shape, weights: dict, tokens, kv_bf16: bool = False) -> np.ndar
                 o[b, t] = gqa_attention(q[b, t], k[b, :t + 1].transpose(1, 0, 2), v[b, :t + 1].transpose(1, 0, 2))
         x = x + o.reshape(B, T, nq * hd) @ W(pre + "wo").T
         r = rmsnorm(x, W(pre + "ffn_norm")[0], shape.rms_eps)
-        x = x + swiglu_ffn(r, W(pre + "w_gate"), W(pre + "w_up"), W(pre + "w_down"))
+        x = x + swiglu(r, W(pre + "w_gate"), W(pre + "w_up")) @ W(pre + "w_down").T
+    if positions is not None:
+        x = x[:, list(positions)]
     r = rmsnorm(x, W("final_norm")[0], shape.rms_eps)
     return r @ W("embed" if shape.tie_embeddings else "lm_head").T
 

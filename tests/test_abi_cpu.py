@@ -82,7 +82,9 @@ def test_megakernel_mode_is_refused_before_any_gpu_call():
     assert st == abi.MK_ERR_UNSUPPORTED and "MK_MODE_PER_OP" in abi.mk_last_error()
 
 
-def test_batched_graph_not_yet_supported():
+def test_task_graph_is_single_sequence():
+    """The tGraph builder covers batch 1; batched steps run as per-operator
+    launches with no task table, so asking for a batched graph is refused."""
     c = cfg_for(presets.LLAMA8B, max_seq=4224, max_batch=8)
     with pytest.raises(abi.MkError) as e:
         abi.mk_graph_inspect(c, 256)

@@ -1,6 +1,6 @@
 """End-to-end decode on the GPU (both execution modes) against the oracle.
 
-Bars ("Parity"):
+Bars:
   * logits: max|gpu - oracle| / max|oracle| <= 2e-2 per step against the fp64
     oracle, and <= 1e-3 against the oracle with a bf16-rounded KV cache (the
     remaining error is fp32 accumulation order only);
@@ -32,7 +32,7 @@ def abi():
 
 
 MEGAKERNEL_OFF = ("the persistent megakernel's cooperative launch never completed on the MI355X test box; "
-                  "the mode is refused by mk_create until the cause is found (see DESIGN.md)")
+                  "the mode is refused by mk_create until the cause is found")
 MODES = {"megakernel": 0, "per_op": 1}
 MODE_PARAMS = [pytest.param("megakernel", marks=pytest.mark.skip(reason=MEGAKERNEL_OFF)), "per_op"]
 PER_OP = 1

@@ -162,6 +162,16 @@ def test_cached_decode_with_bf16_kv_equals_full_recompute_with_bf16_kv():
     assert np.abs(full - D.forward_full(shape, w, toks)).max() > 0  # the rounding is visible
 
 
+def test_forward_full_positions_select_rows():
+    shape = MICRO
+    w = gen.gen_weights(shape, seed=6, random_norms=True)
+    toks = gen.tokens(8, 3, 0, 2 * 7, shape.vocab).reshape(2, 7)
+    full = D.forward_full(shape, w, toks)
+    some = D.forward_full(shape, w, toks, positions=[2, 6])
+    assert some.shape == (2, 2, shape.vocab)
+    assert np.abs(some - full[:, [2, 6]]).max() <= 1e-12 * np.abs(full).max()
+
+
 # ---- I9 naive pure-Python model ---------------------------------------------------
 @pytest.mark.parametrize("shape", [MICRO, MICRO_TIED], ids=lambda s: s.name)
 def test_naive_model_matches(shape):
