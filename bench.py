@@ -111,7 +111,7 @@ def timed_pass(abi, h, prompt_t, toks, steps, torch, time_types=()):
     return t0.elapsed_time(t1), times
 
 
-def time_decode(abi, h, prompt_t, steps, warmup, shape, torch):
+def time_decode(abi, h, prompt_t, steps, warmup, shape, torch, log=lambda *a: None):
     """Headline pass (graph-replayed steps), then an eager pass whose gate/up
     launches are bracketed by HIP events, then an untimed per-operator breakdown."""
     B = prompt_t.shape[0]
@@ -119,12 +119,14 @@ def time_decode(abi, h, prompt_t, steps, warmup, shape, torch):
     abi.mk_prefill(h, prompt_t, toks[0])                         # warm-up generation
     run_steps(abi, h, toks, 0, warmup)
     abi.mk_synchronize(h)
+    log("warm-up done; timed pass")
     total, _ = timed_pass(abi, h, prompt_t, toks, steps, torch)
     tokens = toks[:steps + 1].cpu().numpy()
+    log(f"timed pass: {total / steps:.4f} ms/step; eager pass with gate/up events")
     eager_total, times = timed_pass(abi, h, prompt_t, toks, steps, torch, ["gu"])
     gu = times.get("gu", (0.0, 0))
     same = bool((toks[:steps + 1].cpu().numpy() == tokens).all())
-    abi.mk_time_ops(h, list(abi.OP_TYPES), 32 * (8 * shape.n_layers + 3))
+    abi.mk_time_ops(h, list(abi.OP_TYPES), 32 * (12 * shape.n_layers + 4))  # every launch of 32 steps
     run_steps(abi, h, toks, steps, 32)
     breakdown = abi.mk_read_op_times(h)
     return total, eager_total, gu, same, breakdown
@@ -157,6 +159,8 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--fused-merge", action="store_true",
+                    help="merge attention splits in the last split workgroup instead of a separate launch")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -179,7 +183,13 @@ def main():
         dw = runtime.upload_weights(weights)
     else:  # one tensor at a time through host memory (the 70B shape is 141 GB)
         weights = None
-        dw = runtime.generate_device_weights(shape, wl.weight_seed)
+        last = [time.time()]
+
+        def progress(i, n):
+            if time.time() - last[0] > 20 or i == n:
+                last[0] = time.time()
+                log(f"weights: {i}/{n} tensors on the device")
+        dw = runtime.generate_device_weights(shape, wl.weight_seed, progress=progress)
     torch.cuda.synchronize()
     log(f"weights generated and uploaded in {time.time() - t:.1f}s")
     prompt = gen.gen_prompt(wl)
@@ -187,9 +197,10 @@ def main():
 
     # batch 1 keeps an fp32 KV cache; the batched workloads state a bf16 cache
     kv_fp32 = B == 1
-    h = runtime.create(shape, dw, max_seq + 64, B, abi.MK_MODE_PER_OP, kv_fp32=kv_fp32)
+    flags = abi.MK_FLAG_FUSED_MERGE if args.fused_merge else 0
+    h = runtime.create(shape, dw, max_seq + 64, B, abi.MK_MODE_PER_OP, flags, kv_fp32=kv_fp32)
     total, eager_total, (gu_ms, gu_n), same_tokens, breakdown = time_decode(abi, h, prompt_t, steps, warmup, shape,
-                                                                             torch)
+                                                                             torch, log)
     abi.mk_destroy(h)
     ms = total / steps
     kern_ms = gu_ms / max(gu_n, 1)
@@ -219,7 +230,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: batch {B}, prompt {wl.prompt_len}, {steps} greedy decode steps",
                    "batch": B, "prompt_len": wl.prompt_len, "decode_steps": steps,
-                   "mode": "per_op (HIP graph per step)", "kv_cache": "fp32" if kv_fp32 else "bf16",
+                   "mode": "per_op (HIP graph per step)" + (", fused merge" if args.fused_merge else ""),
+                   "kv_cache": "fp32" if kv_fp32 else "bf16",
                    "parallelism": "none (1 GPU)"},
         "tokens_per_s": 1000.0 * B / ms,
         "achieved_gbps": alg_bytes / (ms * 1e-3) / 1e9,

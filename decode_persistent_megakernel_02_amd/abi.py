@@ -16,7 +16,7 @@ MK_ABI_VERSION = 1
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_OUT_OF_MEMORY, MK_ERR_HIP = 0, -1, -2, -3
 MK_ERR_CAPACITY, MK_ERR_TIMEOUT, MK_ERR_STATE, MK_ERR_UNSUPPORTED = -4, -5, -6, -7
 MK_MODE_MEGAKERNEL, MK_MODE_PER_OP = 0, 1
-MK_FLAG_TRACE, MK_FLAG_POISON, MK_FLAG_NO_GRAPH = 1, 2, 4
+MK_FLAG_TRACE, MK_FLAG_POISON, MK_FLAG_NO_GRAPH, MK_FLAG_FUSED_MERGE = 1, 2, 4, 8
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_OUT_OF_MEMORY", -3: "MK_ERR_HIP",
                 -4: "MK_ERR_CAPACITY", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE", -7: "MK_ERR_UNSUPPORTED"}
 
@@ -95,6 +95,7 @@ SIGNATURES = {
     "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _P], _I32),
+    "mk_trace_op": ([_P, _I32, _I32], _I32),
     "mk_t_argmax": ([_P, _I32, _P, _P], _I32),
     "mk_device_info": ([ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
 }
@@ -282,6 +283,12 @@ def mk_read_op_times(h: Handle):
     n = (ctypes.c_int32 * 9)()
     _check(lib.mk_read_op_times(h.ptr, ms, n), "mk_read_op_times")
     return {name: (ms[i], n[i]) for name, i in OP_TYPES.items() if n[i]}
+
+
+def mk_trace_op(h: Handle, type_name, layer: int):
+    """Log the wave timeline of one GEMV operator launch (None stops logging)."""
+    t = -1 if type_name is None else TASK_TYPES[type_name]
+    _check(lib.mk_trace_op(h.ptr, t, layer), "mk_trace_op")
 
 
 def mk_t_gemv(W, x, y, stream=None):

@@ -183,6 +183,8 @@ mk_status device_facts(int* ncu, double* ticks_per_us, int* max_lds) {
   return MK_OK;
 }
 
+bool fused_merge(const mk_handle* h) { return (h->cfg.flags & MK_FLAG_FUSED_MERGE) != 0; }
+
 // Batched projection kernels by operator (QKV, O, GU, DOWN, LM) and batch tiles (1, 2, 4).
 const void* bgemm_kernel(int type, int bt) {
   const int i = bt == 1 ? 0 : bt == 2 ? 1 : 2;
@@ -200,16 +202,38 @@ const void* bgemm_kernel(int type, int bt) {
   const int row = type == TT_QKV ? 0 : type == TT_O ? 1 : type == TT_GU ? 2 : type == TT_DOWN ? 3 : 4;
   return k[row][i];
 }
-int bgemm_tiles(int type) { return type == TT_O || type == TT_DOWN ? 1 : 2; }  // 16-row tiles per workgroup
-int bgemm_lds(int type, int bt) { return kBgemmWaves * bgemm_tiles(type) * bt * 256 * 4 + kMaxBatch * 8; }
+int bgemm_lds(int bt) { return b_lds_bytes(bt) + kMaxBatch * 8; }
 
-// Workgroups of a batched projection: one per group of 16-row tiles.
+// Row groups of a batched projection (one per wave: two 16-row tiles), and K.
 int bgemm_groups(const Params& P, int type) {
   switch (type) {
     case TT_QKV: return (P.nq + 2 * P.nkv) * P.hd / 32;
-    case TT_O: case TT_DOWN: return (P.H + 15) / 16;
+    case TT_O: case TT_DOWN: return (P.H + 31) / 32;
     case TT_GU: return (P.F + 15) / 16;
     default: return (P.V + 31) / 32;
+  }
+}
+int bgemm_k(const Params& P, int type) { return type == TT_O ? P.nq * P.hd : type == TT_DOWN ? P.F : P.H; }
+
+// Splits of K for a batched projection: enough workgroups for two per CU,
+// whole activation chunks per split, none empty; the LM head is not split
+// (its argmax runs in the epilogue).
+int bgemm_splits(const Params& P, int type, int ncu) {
+  if (type == TT_LM) return 1;
+  const int bt = batch_tiles(P.B), kc = kBChunkCols[bt];
+  const int ngx = (bgemm_groups(P, type) + kBgemmWaves - 1) / kBgemmWaves;
+  const int nch = (bgemm_k(P, type) + kc - 1) / kc;
+  int ks = std::max(1, std::min(nch, (2 * ncu + ngx - 1) / ngx));
+  const int per = (nch + ks - 1) / ks;
+  return (nch + per - 1) / per;
+}
+
+const void* bfin_kernel(int type) {
+  switch (type) {
+    case TT_QKV: return reinterpret_cast<const void*>(&mk_b_fin_qkv);
+    case TT_O: return reinterpret_cast<const void*>(&mk_b_fin_o);
+    case TT_GU: return reinterpret_cast<const void*>(&mk_b_fin_gu);
+    default: return reinterpret_cast<const void*>(&mk_b_fin_down);
   }
 }
 
@@ -235,20 +259,27 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
     return launch(0, reinterpret_cast<const void*>(&mk_b_norm), dim3(Pc.B), dim3(kNormThreads), args, 0);
   };
   auto gemm = [&](int type, int layer) -> mk_status {
+    const int ks = bgemm_splits(Pc, type, Pc.ncu);
+    const int ngx = (bgemm_groups(Pc, type) + kBgemmWaves - 1) / kBgemmWaves;
     void* args[] = {&Pc, &sp, &layer};
-    return launch(type, bgemm_kernel(type, bt), dim3(bgemm_groups(Pc, type)), dim3(kBgemmWaves * kWave), args,
-                  (size_t)bgemm_lds(type, bt));
+    MK_TRY(launch(type, bgemm_kernel(type, bt), dim3(ngx, ks), dim3(kBgemmWaves * kWave), args,
+                  (size_t)bgemm_lds(bt)));
+    if (ks == 1) return MK_OK;
+    int k = ks;
+    void* fargs[] = {&Pc, &sp, &layer, &k};
+    return launch(type, bfin_kernel(type), dim3(bgemm_groups(Pc, type)), dim3(256), fargs, 0);
   };
   for (int l = 0; l < Pc.L; ++l) {
     MK_TRY(norm(l, 0));
     MK_TRY(gemm(TT_QKV, l));
     {
-      int layer = l;
-      void* args[] = {&Pc, &sp, &layer};
+      int layer = l, fuse = fused_merge(h) ? 1 : 0;
+      void* args[] = {&Pc, &sp, &layer, &fuse};
       MK_TRY(launch(TT_ATTN, reinterpret_cast<const void*>(&mk_op_attn_split), dim3(Pc.B * Pc.nkv * Pc.nsplit),
                     dim3(kAttnWaves * kWave), args, (size_t)h->attn_lds));
-      MK_TRY(launch(TT_MERGE, reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(Pc.B * Pc.nkv),
-                    dim3((Pc.nq / Pc.nkv) * kWave), args, 0));
+      if (!fuse)
+        MK_TRY(launch(TT_MERGE, reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(Pc.B * Pc.nkv),
+                      dim3((Pc.nq / Pc.nkv) * kWave), args, 0));
     }
     MK_TRY(gemm(TT_O, l));
     MK_TRY(norm(l, 1));
@@ -271,11 +302,12 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
     const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
     if (count <= 0) continue;
     const int type = g.stage_type[s];
+    if (type == TT_MERGE && fused_merge(h)) continue;  // done by the last split workgroup
     const bool timed = timed_ok && ((h->timed_mask >> type) & 1) && 2 * (h->ev_used + 1) <= (int)h->ev_pool.size();
     if (timed) HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used], st));
     if (type == TT_ATTN || type == TT_MERGE) {
-      int layer = g.tasks[b0].layer;
-      void* args[] = {&Pc, &sp, &layer};
+      int layer = g.tasks[b0].layer, fuse = fused_merge(h) ? 1 : 0;
+      void* args[] = {&Pc, &sp, &layer, &fuse};
       if (type == TT_ATTN)
         HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_split),
                                 dim3(h->P.B * h->P.nkv * h->P.nsplit), dim3(kAttnWaves * kWave), args,
@@ -465,6 +497,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   P.h = P.attn_out + n_aout;
   MK_TRY(h->alloc(&P.lm_part, B));
   HIP_TRY(hipMemset(P.lm_part, 0, B * sizeof(unsigned long long)));
+  MK_TRY(h->alloc(&P.attn_count, (int64_t)B * nkv));
+  HIP_TRY(hipMemset(P.attn_count, 0, (size_t)B * nkv * 4));
   if (h->batched) {  // bf16 MFMA operands; rows B..Bp-1 are zero and never written
     const int bt = batch_tiles(B);
     P.Bp = 16 * bt;
@@ -475,10 +509,14 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     P.ax = ops;
     P.ao = ops + n_ax;
     P.ah = ops + n_ax + n_ao;
+    int64_t n_part = 1;
     for (int t : {TT_QKV, TT_O, TT_GU, TT_DOWN, TT_LM}) {
-      if (bgemm_lds(t, bt) > max_lds) return fail(MK_ERR_UNSUPPORTED, "batched projection LDS need exceeds the device");
-      HIP_TRY(hipFuncSetAttribute(bgemm_kernel(t, bt), hipFuncAttributeMaxDynamicSharedMemorySize, bgemm_lds(t, bt)));
+      if (bgemm_lds(bt) > max_lds) return fail(MK_ERR_UNSUPPORTED, "batched projection LDS need exceeds the device");
+      HIP_TRY(hipFuncSetAttribute(bgemm_kernel(t, bt), hipFuncAttributeMaxDynamicSharedMemorySize, bgemm_lds(bt)));
+      const int ks = bgemm_splits(P, t, ncu);
+      if (ks > 1) n_part = std::max<int64_t>(n_part, (int64_t)ks * bgemm_groups(P, t) * 2 * 16 * P.Bp);
     }
+    MK_TRY(h->alloc(&P.bpart, n_part));
   }
 
   // RoPE angle tables, computed in double precision
@@ -515,6 +553,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   HIP_TRY(hipMemset(P.events, 0, g.event_count.size() * 4));
   MK_TRY(h->alloc(&P.status, kStatusWords));
   HIP_TRY(hipMemset(P.status, 0, kStatusWords * 4));
+  P.trace_op = -1;
   if (cfg->flags & MK_FLAG_TRACE) {
     MK_TRY(h->alloc(&P.trace, 2 * (int64_t)g.tasks.size()));
     HIP_TRY(hipMemset(P.trace, 0, 16 * g.tasks.size()));
@@ -660,6 +699,7 @@ mk_status mk_reset(mk_handle* h) {
   if (h->poisoned) return fail(MK_ERR_STATE, "handle poisoned; destroy and recreate it");
   HIP_TRY(hipMemset(h->P.events, 0, h->graph.event_count.size() * 4));
   HIP_TRY(hipMemset(h->P.lm_part, 0, h->cfg.max_batch * sizeof(unsigned long long)));
+  HIP_TRY(hipMemset(h->P.attn_count, 0, (size_t)h->cfg.max_batch * h->P.nkv * 4));
   HIP_TRY(hipDeviceSynchronize());
   h->length = 0;
   h->batch = 0;
@@ -808,6 +848,15 @@ mk_status mk_read_op_times(mk_handle* h, double* total_ms, int32_t* launches) {
   return MK_OK;
 }
 
+mk_status mk_trace_op(mk_handle* h, int32_t type, int32_t layer) {
+  g_err.clear();
+  if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
+  if (!h->P.trace) return fail(MK_ERR_STATE, "handle created without MK_FLAG_TRACE");
+  if (!(h->cfg.flags & MK_FLAG_NO_GRAPH)) return fail(MK_ERR_STATE, "operator tracing needs MK_FLAG_NO_GRAPH");
+  h->P.trace_op = type < 0 ? -1 : (type << 16) | layer;
+  return MK_OK;
+}
+
 mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, double* ticks_per_us) {
   if (!h || !n) return fail(MK_ERR_INVALID_ARG, "NULL argument");
   if (!h->P.trace) return fail(MK_ERR_STATE, "handle created without MK_FLAG_TRACE");
@@ -877,10 +926,11 @@ mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t 
   g_err.clear();
   if (!W || !A || !Y || N < 1 || K < 8 || K % 8 || B < 1 || B > kMaxBatch)
     return fail(MK_ERR_INVALID_ARG, "bad bgemm arguments");
-  const int lds = kBgemmWaves * batch_tiles(B) * 256 * 4;
+  const int lds = b_lds_bytes(batch_tiles(B));
   HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_t_bgemm_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-  hipLaunchKernelGGL(mk_t_bgemm_kernel, dim3((N + 15) / 16), dim3(kBgemmWaves * kWave), (unsigned)lds,
+  hipLaunchKernelGGL(mk_t_bgemm_kernel, dim3((N + 32 * kBgemmWaves - 1) / (32 * kBgemmWaves)),
+                     dim3(kBgemmWaves * kWave), (unsigned)lds,
                      static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W),
                      static_cast<const uint16_t*>(A), Y, N, K, B);
   HIP_TRY(hipGetLastError());

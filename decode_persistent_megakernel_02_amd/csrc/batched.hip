@@ -16,8 +16,19 @@
 // bf16's 2^-9; the matrix cores have the throughput to spare at these batch
 // sizes.  Everything else (residual stream, RoPE, softmax, norms) is fp32.
 //
-// Operator order per layer (one launch each): norm -> QKV(+RoPE, KV append) ->
-// split-KV attention -> merge -> O(+residual) -> norm -> gate/up(+SwiGLU) ->
+// Work split: a workgroup of four waves owns four groups of two 16-row weight
+// tiles (one group per wave) and one range of K.  The activation operand is
+// shared by every row, so the workgroup stages it through LDS in 128- or
+// 256-column chunks (double-buffered, one barrier per chunk) and each wave
+// reads its fragments there; re-reading them from L2 per wave made the
+// activation traffic several times the weight traffic and bounded these
+// kernels by L2 bandwidth.  Each wave streams its own weight rows with a
+// chunk of k-steps in flight.  Operators with few row groups also split K
+// across workgroups: partial sums go to a buffer and a finishing launch adds
+// them in a fixed order and runs the epilogue.
+//
+// Operator order per layer: norm -> QKV(+RoPE, KV append) -> split-KV
+// attention -> merge -> O(+residual) -> norm -> gate/up(+SwiGLU) ->
 // down(+residual); then the final norm, the LM head with per-tile argmax
 // partials, and the argmax.
 #include "device.h"
@@ -38,89 +49,15 @@ __device__ __forceinline__ f32x4 mma16(v4u w, v4u a, f32x4 c) {
                                                  0, 0);
 }
 
-// One wave: acc[r][t] += W_r . (A_t.hi + A_t.lo)^T over the k-steps [s0, s1)
-// (32 columns each).  wr[r] / ar[t]: this lane's weight row / operand row (hi
-// plane; the lo plane is lo_off vectors further) as 16-byte vectors; nvec =
-// K / 8.  D k-steps of every operand stay in flight: rounds of D steps, each
-// slot refilled right after it is consumed, the last round only consuming.
-// No load is predicated (see gemv_run): with EXACT every step is in range;
-// otherwise addresses are clamped and the operand of an out-of-range step
-// is zeroed.
-template <int RT, int BT, int D, bool EXACT>
-__device__ __forceinline__ void mma_load(v4u (&wb)[RT], v4u (&ah)[BT], v4u (&al)[BT], const v4u* const (&wr)[RT],
-                                         const v4u* const (&ar)[BT], int64_t lo_off, int nvec, int s, int piece) {
-  const int v = EXACT ? 4 * s + piece : min(4 * s + piece, nvec - 1);
-#pragma unroll
-  for (int r = 0; r < RT; ++r) wb[r] = ld_w(wr[r] + v);
-#pragma unroll
-  for (int t = 0; t < BT; ++t) {
-    ah[t] = ld_g(ar[t] + v);
-    al[t] = ld_g(ar[t] + lo_off + v);
-  }
-}
-
-template <int RT, int BT, bool EXACT>
-__device__ __forceinline__ void mma_consume(const v4u (&wb)[RT], const v4u (&ah)[BT], const v4u (&al)[BT], bool ok,
-                                            f32x4 (&acc)[RT][BT]) {
-  const v4u z = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int t = 0; t < BT; ++t) {
-    const v4u h = EXACT || ok ? ah[t] : z, l = EXACT || ok ? al[t] : z;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      acc[r][t] = mma16(wb[r], h, acc[r][t]);
-      acc[r][t] = mma16(wb[r], l, acc[r][t]);
-    }
-  }
-}
-
-template <int RT, int BT, int D, bool EXACT>
-__device__ __forceinline__ void mma_run(const v4u* const (&wr)[RT], const v4u* const (&ar)[BT], int64_t lo_off,
-                                        int nvec, int s0, int s1, int lane, f32x4 (&acc)[RT][BT]) {
-  const int piece = lane >> 4;
-  const int nrounds = (s1 - s0 + D - 1) / D;
-  if (nrounds <= 0) return;
-  v4u wb[D][RT], ah[D][BT], al[D][BT];
-#pragma unroll
-  for (int d = 0; d < D; ++d) mma_load<RT, BT, D, EXACT>(wb[d], ah[d], al[d], wr, ar, lo_off, nvec, s0 + d, piece);
-  for (int rd = 0; rd + 1 < nrounds; ++rd) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int s = s0 + rd * D + d;
-      mma_consume<RT, BT, EXACT>(wb[d], ah[d], al[d], s < s1 && 4 * s + piece < nvec, acc);
-      mma_load<RT, BT, D, EXACT>(wb[d], ah[d], al[d], wr, ar, lo_off, nvec, s + D, piece);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    const int s = s0 + (nrounds - 1) * D + d;
-    mma_consume<RT, BT, EXACT>(wb[d], ah[d], al[d], s < s1 && 4 * s + piece < nvec, acc);
-  }
-}
-
-// Splits the K steps of a tile over the NW waves and runs the wave's share;
-// the exact variant when every wave gets the same multiple of D steps.
-template <int RT, int BT, int NW, int D>
-__device__ __forceinline__ void mma_wave(const v4u* const (&wr)[RT], const v4u* const (&ar)[BT], int64_t lo_off,
-                                         int nvec, int wave, int lane, f32x4 (&acc)[RT][BT]) {
-  const int nsteps = (nvec + 3) / 4, per = (nsteps + NW - 1) / NW;
-  const int s0 = min(wave * per, nsteps), s1 = min(s0 + per, nsteps);
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int t = 0; t < BT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (nvec % 4 == 0 && nsteps % NW == 0 && per % D == 0) mma_run<RT, BT, D, true>(wr, ar, lo_off, nvec, s0, s1, lane, acc);
-  else mma_run<RT, BT, D, false>(wr, ar, lo_off, nvec, s0, s1, lane, acc);
-}
-
-// Row layout of one workgroup's group of RT 16-row tiles, per operator.
+// Rows of one wave's group of two 16-row weight tiles, per operator.
 //   QKV (RT 2): groups [0, nq*hd/32) are query, then key, then value groups.
 //     A query/key group pairs tile rows i0.. and i0 + hd/2.. of one head
 //     (i0 < hd/2, a multiple of 16), so the RoPE pair (i, i + hd/2) of every
 //     row lands in the same thread; a value group is 32 consecutive rows.
-//   O, DOWN (RT 1): 16 consecutive rows.
+//   O, DOWN, LM (RT 2): 32 consecutive rows.
 //   GU (RT 2): the same 16 rows of W_gate and of W_up.
-//   LM (RT 2): 32 consecutive rows.
+constexpr int kRT = 2;  // 16-row tiles per wave
+
 struct GroupRows {
   const uint16_t* W[2];  // matrix of each tile
   int row0[2];           // first row of each tile
@@ -139,13 +76,13 @@ __device__ __forceinline__ GroupRows group_rows(const Params& P, int l, int g) {
       const bool isq = g < nqg;
       const int gg = isq ? g : g - nqg, head = gg / per_head, i0 = (gg % per_head) * 16;
       G.mat = isq ? 0 : 1;
-      G.W[0] = G.W[1] = isq ? P.wq[l] : P.wk[l];
+      G.W[0] = G.W[1] = isq ? ld_const(P.wq + l) : ld_const(P.wk + l);
       G.N = (isq ? P.nq : P.nkv) * hd;
       G.row0[0] = head * hd + i0;
       G.row0[1] = head * hd + hd / 2 + i0;
     } else {
       G.mat = 2;
-      G.W[0] = G.W[1] = P.wv[l];
+      G.W[0] = G.W[1] = ld_const(P.wv + l);
       G.N = P.nkv * hd;
       G.row0[0] = (g - nqg - nkg) * 32;
       G.row0[1] = G.row0[0] + 16;
@@ -153,19 +90,21 @@ __device__ __forceinline__ GroupRows group_rows(const Params& P, int l, int g) {
   } else if constexpr (TT == TT_O) {
     G.K = P.nq * hd;
     G.N = P.H;
-    G.W[0] = G.W[1] = P.wo[l];
-    G.row0[0] = G.row0[1] = g * 16;
+    G.W[0] = G.W[1] = ld_const(P.wo + l);
+    G.row0[0] = g * 32;
+    G.row0[1] = g * 32 + 16;
   } else if constexpr (TT == TT_GU) {
     G.K = P.H;
     G.N = P.F;
-    G.W[0] = P.w_gate[l];
-    G.W[1] = P.w_up[l];
+    G.W[0] = ld_const(P.w_gate + l);
+    G.W[1] = ld_const(P.w_up + l);
     G.row0[0] = G.row0[1] = g * 16;
   } else if constexpr (TT == TT_DOWN) {
     G.K = P.F;
     G.N = P.H;
-    G.W[0] = G.W[1] = P.w_down[l];
-    G.row0[0] = G.row0[1] = g * 16;
+    G.W[0] = G.W[1] = ld_const(P.w_down + l);
+    G.row0[0] = g * 32;
+    G.row0[1] = g * 32 + 16;
   } else {
     G.K = P.H;
     G.N = P.V;
@@ -209,11 +148,14 @@ __device__ __forceinline__ void bgemm_epilogue(const Params& P, const Step& S, i
       }
     }
   } else if constexpr (TT == TT_O) {
-    const int row = G.row0[0] + m;
-    if (row < G.N) {
-      const float xin = l == 0 ? bf1(P.embed[(int64_t)token_of(P, S, b) * H + row])
-                               : P.xs[((int64_t)l * P.B + b) * H + row];
-      P.xmid[((int64_t)l * P.B + b) * H + row] = xin + y[0];
+    const int64_t tok = l == 0 ? (int64_t)token_of(P, S, b) * H : 0;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row = G.row0[r] + m;
+      if (row < G.N) {
+        const float xin = l == 0 ? bf1(P.embed[tok + row]) : P.xs[((int64_t)l * P.B + b) * H + row];
+        P.xmid[((int64_t)l * P.B + b) * H + row] = xin + y[r];
+      }
     }
   } else if constexpr (TT == TT_GU) {
     const int row = G.row0[0] + m;
@@ -224,8 +166,11 @@ __device__ __forceinline__ void bgemm_epilogue(const Params& P, const Step& S, i
       split_bf16(hv, hi, hi + (int64_t)P.Bp * P.F);
     }
   } else if constexpr (TT == TT_DOWN) {
-    const int row = G.row0[0] + m;
-    if (row < G.N) P.xs[((int64_t)(l + 1) * P.B + b) * H + row] = P.xmid[((int64_t)l * P.B + b) * H + row] + y[0];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int row = G.row0[r] + m;
+      if (row < G.N) P.xs[((int64_t)(l + 1) * P.B + b) * H + row] = P.xmid[((int64_t)l * P.B + b) * H + row] + y[r];
+    }
   } else {
     unsigned long long k = 0;
 #pragma unroll
@@ -241,103 +186,289 @@ __device__ __forceinline__ void bgemm_epilogue(const Params& P, const Step& S, i
   }
 }
 
-// One workgroup = one group of RT row tiles x all batch tiles.  Its NW waves
-// split the K columns; each wave's partial accumulators go to LDS and are
-// summed in wave order (a fixed order: the result does not depend on timing).
-template <int TT, int RT, int BT, int NW, int D>
-__device__ __forceinline__ void bgemm(const Params& P, const Step& S, int l) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* red = reinterpret_cast<float*>(smem);                                    // [NW][RT][BT][4][64]
-  unsigned long long* best = reinterpret_cast<unsigned long long*>(red + NW * RT * BT * 256);  // [64]
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const GroupRows G = group_rows<TT>(P, l, blockIdx.x);
-  if constexpr (TT == TT_LM) {
-    if (threadIdx.x < kMaxBatch) best[threadIdx.x] = 0;
-  }
-  const int nvec = G.K / 8;
-  const v4u* wr[RT];
+// ---- the staged-activation GEMM core ------------------------------------------
+// An activation chunk in LDS: [2 planes][Bp rows][KC + 8] bf16; the 16-byte
+// row pad keeps the 16 rows of one fragment read on distinct banks.
+template <int BT, int KC>
+struct Chunk {
+  static constexpr int Bp = 16 * BT;
+  static constexpr int STEPS = KC / 32;              // k-steps per chunk (= weight steps in flight)
+  static constexpr int ROW = KC + 8;                 // padded row, elements
+  static constexpr int ELEMS = 2 * Bp * ROW;         // one buffer
+  static constexpr int PIECES = 2 * Bp * (KC / 8);   // 16-byte pieces per chunk
+  static constexpr int PER_THREAD = PIECES / (kBgemmWaves * kWave);
+};
+template <int BT, int KC>
+constexpr int chunk_lds_bytes() { return 2 * Chunk<BT, KC>::ELEMS * 2; }
+
+// This thread's pieces of chunk c (columns [c*KC, c*KC + KC)) of the operand
+// planes A [2][Bp][K]; columns at or past K read a clamped address and are
+// zeroed, so every load is issued unconditionally.
+template <int BT, int KC>
+__device__ __forceinline__ void chunk_load(const uint16_t* A, int K, int c, v4u (&cr)[Chunk<BT, KC>::PER_THREAD]) {
+  using C = Chunk<BT, KC>;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int row = min(G.row0[r] + (lane & 15), G.N - 1);  // rows past the end repeat the last (discarded)
-    wr[r] = reinterpret_cast<const v4u*>(G.W[r] + (int64_t)row * G.K);
-  }
-  const uint16_t* A = operand_of<TT>(P);
-  const v4u* ar[BT];
-#pragma unroll
-  for (int t = 0; t < BT; ++t) ar[t] = reinterpret_cast<const v4u*>(A + (int64_t)(t * 16 + (lane & 15)) * G.K);
-  f32x4 acc[RT][BT];
-  mma_wave<RT, BT, NW, D>(wr, ar, (int64_t)P.Bp * nvec, nvec, wave, lane, acc);
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int t = 0; t < BT; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[(((wave * RT + r) * BT + t) * 4 + j) * 64 + lane] = acc[r][t][j];
-  __syncthreads();
-  for (int e = threadIdx.x; e < BT * 256; e += NW * kWave) {
-    const int t = e >> 8, j = (e >> 6) & 3, ln = e & 63;
-    const int b = t * 16 + (ln & 15), m = 4 * (ln >> 4) + j;
-    if (b >= P.B) continue;
-    float y[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      float s = 0.f;
-      for (int w = 0; w < NW; ++w) s += red[(((w * RT + r) * BT + t) * 4 + j) * 64 + ln];
-      y[r] = s;
-    }
-    bgemm_epilogue<TT, RT>(P, S, l, G, m, b, y, best);
-  }
-  if constexpr (TT == TT_LM) {
-    __syncthreads();
-    if (threadIdx.x < P.B && best[threadIdx.x])
-      __hip_atomic_fetch_max(&P.lm_part[threadIdx.x], best[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < C::PER_THREAD; ++i) {
+    const int idx = threadIdx.x + i * kBgemmWaves * kWave;
+    const int piece = idx % (KC / 8), row = (idx / (KC / 8)) % C::Bp, plane = idx / (C::Bp * (KC / 8));
+    const int k = c * KC + piece * 8;
+    const v4u v = ld_g(reinterpret_cast<const v4u*>(A + ((int64_t)plane * C::Bp + row) * K + min(k, K - 8)));
+    cr[i] = k < K ? v : v4u{0u, 0u, 0u, 0u};
   }
 }
 
-// Prefetch depth by batch tiles: the operand fragments share the in-flight
-// register budget with the weight fragments.
-template <int BT> struct BDepth { static constexpr int D = BT == 1 ? 8 : 4; };
+template <int BT, int KC>
+__device__ __forceinline__ void chunk_store(uint16_t* buf, const v4u (&cr)[Chunk<BT, KC>::PER_THREAD]) {
+  using C = Chunk<BT, KC>;
+#pragma unroll
+  for (int i = 0; i < C::PER_THREAD; ++i) {
+    const int idx = threadIdx.x + i * kBgemmWaves * kWave;
+    const int piece = idx % (KC / 8), row = (idx / (KC / 8)) % C::Bp, plane = idx / (C::Bp * (KC / 8));
+    *reinterpret_cast<v4u*>(buf + (plane * C::Bp + row) * C::ROW + piece * 8) = cr[i];
+  }
+}
 
-#define MK_BGEMM(name, TT, RT, BT)                                                                            \
+// The weight fragments of k-step s (global step index) of the wave's two tiles.
+template <int RT>
+__device__ __forceinline__ void weights_load(v4u (&wb)[RT], const v4u* const (&wr)[RT], int s, int nvec, int piece) {
+  const int v = min(4 * s + piece, nvec - 1);  // past K: any in-bounds vector (the activations are zero there)
+#pragma unroll
+  for (int r = 0; r < RT; ++r) wb[r] = ld_w(wr[r] + v);
+}
+
+// acc[r][t] += W_r . (A_t.hi + A_t.lo)^T for k-step `ks` of the chunk in buf.
+template <int RT, int BT, int KC>
+__device__ __forceinline__ void chunk_mma(const v4u (&wb)[RT], const uint16_t* buf, int ks, int lane,
+                                          f32x4 (&acc)[RT][BT]) {
+  using C = Chunk<BT, KC>;
+  const int col = ks * 32 + (lane >> 4) * 8;
+#pragma unroll
+  for (int t = 0; t < BT; ++t) {
+    const int row = t * 16 + (lane & 15);
+    const v4u h = *reinterpret_cast<const v4u*>(buf + row * C::ROW + col);
+    const v4u lo = *reinterpret_cast<const v4u*>(buf + (C::Bp + row) * C::ROW + col);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r][t] = mma16(wb[r], h, acc[r][t]);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r][t] = mma16(wb[r], lo, acc[r][t]);
+  }
+}
+
+// One workgroup: the K chunks [c0, c1) of the four tile groups of its waves.
+// Chunk ci+1 (activations and weights) is in flight while chunk ci is
+// multiplied; the last chunk is peeled so that every loop iteration issues
+// the same loads.  Returns the accumulators of this wave's two tiles.
+template <int RT, int BT, int KC>
+__device__ __forceinline__ void staged_gemm(const uint16_t* A, int K, const v4u* const (&wr)[RT], int c0, int c1,
+                                            uint16_t* lds, int lane, f32x4 (&acc)[RT][BT]) {
+  using C = Chunk<BT, KC>;
+  constexpr int ST = C::STEPS;
+  const int piece = lane >> 4, nvec = K / 8;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < BT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  v4u cr[C::PER_THREAD];
+  v4u wb[ST][RT];
+  chunk_load<BT, KC>(A, K, c0, cr);
+#pragma unroll
+  for (int d = 0; d < ST; ++d) weights_load<RT>(wb[d], wr, c0 * ST + d, nvec, piece);
+  chunk_store<BT, KC>(lds, cr);
+  __syncthreads();
+  int ci = c0;
+  for (; ci + 1 < c1; ++ci) {
+    const uint16_t* buf = lds + ((ci - c0) & 1) * C::ELEMS;
+    chunk_load<BT, KC>(A, K, ci + 1, cr);
+#pragma unroll
+    for (int d = 0; d < ST; ++d) {
+      chunk_mma<RT, BT, KC>(wb[d], buf, d, lane, acc);
+      weights_load<RT>(wb[d], wr, (ci + 1) * ST + d, nvec, piece);
+    }
+    chunk_store<BT, KC>(lds + ((ci + 1 - c0) & 1) * C::ELEMS, cr);
+    __syncthreads();
+  }
+  const uint16_t* buf = lds + ((ci - c0) & 1) * C::ELEMS;
+#pragma unroll
+  for (int d = 0; d < ST; ++d) chunk_mma<RT, BT, KC>(wb[d], buf, d, lane, acc);
+}
+
+// Row groups per operator (each is one wave's two tiles).
+template <int TT>
+__device__ __forceinline__ int group_count(const Params& P) {
+  if constexpr (TT == TT_QKV) return (P.nq + 2 * P.nkv) * P.hd / 32;
+  else if constexpr (TT == TT_GU) return (P.F + 15) / 16;
+  else if constexpr (TT == TT_LM) return (P.V + 31) / 32;
+  else return (P.H + 31) / 32;  // O, DOWN
+}
+
+template <int TT>
+__device__ __forceinline__ void group_pointers(const Params& P, int l, int g, int lane, GroupRows& G,
+                                               const v4u* (&wr)[kRT]) {
+  G = group_rows<TT>(P, l, g);
+#pragma unroll
+  for (int r = 0; r < kRT; ++r) {
+    const int row = min(G.row0[r] + (lane & 15), G.N - 1);  // rows past the end repeat the last (discarded)
+    wr[r] = reinterpret_cast<const v4u*>(G.W[r] + (int64_t)row * G.K);
+  }
+}
+
+// Split-K partial layout: part[((kz * ngroups + g) * RT + r) * 16 + m][b].
+__device__ __forceinline__ int64_t part_index(int kz, int ngroups, int g, int r, int m, int b, int Bp) {
+  return ((((int64_t)kz * ngroups + g) * kRT + r) * 16 + m) * Bp + b;
+}
+
+// The projection kernel: grid (ceil(groups / 4), splits of K).  With one
+// split the epilogue runs here, straight from each wave's accumulators;
+// otherwise the partial sums go to P.bpart for the finishing launch.
+template <int TT, int BT, int KC>
+__device__ __forceinline__ void bgemm(const Params& P, const Step& S, int l) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+  unsigned long long* best = reinterpret_cast<unsigned long long*>(smem + chunk_lds_bytes<BT, KC>());  // [64]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int ngroups = group_count<TT>(P);
+  const int g = blockIdx.x * kBgemmWaves + wave, gc = min(g, ngroups - 1);  // a spare wave repeats the last group
+  if constexpr (TT == TT_LM) {
+    if (threadIdx.x < kMaxBatch) best[threadIdx.x] = 0;
+  }
+  GroupRows G;
+  const v4u* wr[kRT];
+  group_pointers<TT>(P, l, gc, lane, G, wr);
+  const int nch = (G.K + KC - 1) / KC, ks = gridDim.y, per = (nch + ks - 1) / ks;
+  const int c0 = blockIdx.y * per, c1 = min(c0 + per, nch);
+  f32x4 acc[kRT][BT];
+  staged_gemm<kRT, BT, KC>(operand_of<TT>(P), G.K, wr, c0, c1, lds, lane, acc);
+  if (ks == 1) {
+    if (g < ngroups) {
+#pragma unroll
+      for (int t = 0; t < BT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = 4 * (lane >> 4) + j, b = t * 16 + (lane & 15);
+          float y[kRT];
+#pragma unroll
+          for (int r = 0; r < kRT; ++r) y[r] = acc[r][t][j];
+          if (b < P.B) bgemm_epilogue<TT, kRT>(P, S, l, G, m, b, y, best);
+        }
+    }
+    if constexpr (TT == TT_LM) {
+      __syncthreads();
+      if (threadIdx.x < P.B && best[threadIdx.x])
+        __hip_atomic_fetch_max(&P.lm_part[threadIdx.x], best[threadIdx.x], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (g < ngroups) {
+#pragma unroll
+    for (int r = 0; r < kRT; ++r)
+#pragma unroll
+      for (int t = 0; t < BT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          P.bpart[part_index(blockIdx.y, ngroups, g, r, 4 * (lane >> 4) + j, t * 16 + (lane & 15), 16 * BT)] =
+              acc[r][t][j];
+  }
+}
+
+// Finishing launch of a split projection: one workgroup per row group adds
+// the splits' partial sums in split order and runs the epilogue.
+template <int TT>
+__device__ __forceinline__ void bgemm_finish(const Params& P, const Step& S, int l, int ks) {
+  __shared__ unsigned long long best[kMaxBatch];
+  const int g = blockIdx.x, ngroups = group_count<TT>(P);
+  const GroupRows G = group_rows<TT>(P, l, g);
+  for (int e = threadIdx.x; e < 16 * P.Bp; e += blockDim.x) {
+    const int m = e / P.Bp, b = e % P.Bp;
+    if (b >= P.B) continue;
+    float y[kRT];
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) {
+      float s = 0.f;
+      for (int kz = 0; kz < ks; ++kz) s += P.bpart[part_index(kz, ngroups, g, r, m, b, P.Bp)];
+      y[r] = s;
+    }
+    bgemm_epilogue<TT, kRT>(P, S, l, G, m, b, y, best);
+  }
+}
+
+// Chunk width by batch tiles: 256 columns at 16 rows, 128 at 32 and 64 (LDS).
+template <int BT> struct BChunk { static constexpr int KC = BT == 1 ? 256 : 128; };
+
+#define MK_BGEMM(name, TT, BT)                                                                                \
   extern "C" __global__ __launch_bounds__(kBgemmWaves * kWave) void name##_b##BT(Params P, const Step* Sd,     \
                                                                                   int layer) {                \
-    const Step S = *Sd;                                                                                       \
-    bgemm<TT, RT, BT, kBgemmWaves, BDepth<BT>::D>(P, S, layer);                                                \
+    const Step S = ld_const(Sd);                                                                              \
+    bgemm<TT, BT, BChunk<BT>::KC>(P, S, layer);                                                               \
   }
-#define MK_BGEMM_ALL(name, TT, RT) MK_BGEMM(name, TT, RT, 1) MK_BGEMM(name, TT, RT, 2) MK_BGEMM(name, TT, RT, 4)
-MK_BGEMM_ALL(mk_b_qkv, TT_QKV, 2)
-MK_BGEMM_ALL(mk_b_o, TT_O, 1)
-MK_BGEMM_ALL(mk_b_gu, TT_GU, 2)
-MK_BGEMM_ALL(mk_b_down, TT_DOWN, 1)
-MK_BGEMM_ALL(mk_b_lm, TT_LM, 2)
+#define MK_BGEMM_ALL(name, TT) MK_BGEMM(name, TT, 1) MK_BGEMM(name, TT, 2) MK_BGEMM(name, TT, 4)
+MK_BGEMM_ALL(mk_b_qkv, TT_QKV)
+MK_BGEMM_ALL(mk_b_o, TT_O)
+MK_BGEMM_ALL(mk_b_gu, TT_GU)
+MK_BGEMM_ALL(mk_b_down, TT_DOWN)
+MK_BGEMM_ALL(mk_b_lm, TT_LM)
 
-// RMSNorm of one batch row into the bf16 operand buffer ax:
-// ax[b] = bf16(x * (mean(x^2) + eps)^-1/2 * gamma).  kind 0: attention norm of
-// `layer` (x = embedding row at layer 0), 1: FFN norm, 2: final norm.  One
-// workgroup per row; the sum of squares is reduced in a fixed order.
+#define MK_BFIN(name, TT)                                                                                     \
+  extern "C" __global__ __launch_bounds__(256) void name(Params P, const Step* Sd, int layer, int ks) {        \
+    const Step S = ld_const(Sd);                                                                              \
+    bgemm_finish<TT>(P, S, layer, ks);                                                                        \
+  }
+MK_BFIN(mk_b_fin_qkv, TT_QKV)
+MK_BFIN(mk_b_fin_o, TT_O)
+MK_BFIN(mk_b_fin_gu, TT_GU)
+MK_BFIN(mk_b_fin_down, TT_DOWN)
+
+// RMSNorm of one batch row into the bf16 operand planes of ax:
+// ax[b] = x * (mean(x^2) + eps)^-1/2 * gamma as hi/lo.  kind 0: attention norm
+// of `layer` (x = embedding row at layer 0), 1: FFN norm, 2: final norm.  One
+// workgroup per row; each thread keeps up to kNormGroups groups of 8 values
+// in registers between the two passes; the sum of squares is reduced in a
+// fixed order.
+constexpr int kNormGroups = 4;  // rows up to 8192 in registers (longer rows are re-read)
 extern "C" __global__ __launch_bounds__(kNormThreads) void mk_b_norm(Params P, const Step* Sd, int layer, int kind) {
   __shared__ float part[kNormThreads / kWave];
-  const Step S = *Sd;
+  const Step S = ld_const(Sd);
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t H = P.H;
   const float* xf = nullptr;
   const uint16_t* xb = nullptr;
   const uint16_t* gamma;
   if (kind == 0) {
-    gamma = P.attn_norm[layer];
+    gamma = ld_const(P.attn_norm + layer);
     if (layer == 0) xb = P.embed + (int64_t)token_of(P, S, b) * H;
     else xf = P.xs + ((int64_t)layer * P.B + b) * H;
   } else if (kind == 1) {
-    gamma = P.ffn_norm[layer];
+    gamma = ld_const(P.ffn_norm + layer);
     xf = P.xmid + ((int64_t)layer * P.B + b) * H;
   } else {
     gamma = P.final_norm;
     xf = P.xs + ((int64_t)P.L * P.B + b) * H;
   }
+  auto load8 = [&](int i, float (&v)[8]) __attribute__((always_inline)) {
+    if (xf) {
+      const float4 a = *reinterpret_cast<const float4*>(xf + i), c = *reinterpret_cast<const float4*>(xf + i + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    } else {
+      const v4u u = ld_g(reinterpret_cast<const v4u*>(xb + i));
+      v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+      v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
+    }
+  };
+  constexpr int NT = kNormThreads * 8;  // elements per pass over the row
+  float v[kNormGroups][8];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < P.H; i += kNormThreads) {
-    const float v = xf ? xf[i] : bf1(xb[i]);
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int g = 0; g < kNormGroups; ++g) {
+    const int i = g * NT + threadIdx.x * 8;
+    if (i < P.H) {
+      load8(i, v[g]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf(v[g][j], v[g][j], ss);
+    }
+  }
+  for (int i = kNormGroups * NT + threadIdx.x * 8; i < P.H; i += NT) {
+    float w[8];
+    load8(i, w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(w[j], w[j], ss);
   }
   ss = wave_sum(ss);
   if (lane == 0) part[wave] = ss;
@@ -348,15 +479,35 @@ extern "C" __global__ __launch_bounds__(kNormThreads) void mk_b_norm(Params P, c
   const float inv = 1.0f / sqrtf(tot / (float)P.H + P.eps);
   uint16_t* hi = P.ax + (int64_t)b * H;
   uint16_t* lo = hi + (int64_t)P.Bp * H;
-  for (int i = threadIdx.x; i < P.H; i += kNormThreads) {
-    const float v = xf ? xf[i] : bf1(xb[i]);
-    split_bf16(v * inv * bf1(gamma[i]), hi + i, lo + i);
+  auto emit = [&](int i, const float (&w)[8]) __attribute__((always_inline)) {
+    const v4u g = ld_g(reinterpret_cast<const v4u*>(gamma + i));
+    const float gm[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y), bf_lo(g.z), bf_hi(g.z), bf_lo(g.w), bf_hi(g.w)};
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split_bf16(w[j] * inv * gm[j], &h[j], &l[j]);
+    v4u ph, pl;
+    ph.x = h[0] | (uint32_t)h[1] << 16; ph.y = h[2] | (uint32_t)h[3] << 16;
+    ph.z = h[4] | (uint32_t)h[5] << 16; ph.w = h[6] | (uint32_t)h[7] << 16;
+    pl.x = l[0] | (uint32_t)l[1] << 16; pl.y = l[2] | (uint32_t)l[3] << 16;
+    pl.z = l[4] | (uint32_t)l[5] << 16; pl.w = l[6] | (uint32_t)l[7] << 16;
+    *reinterpret_cast<v4u*>(hi + i) = ph;
+    *reinterpret_cast<v4u*>(lo + i) = pl;
+  };
+#pragma unroll
+  for (int g = 0; g < kNormGroups; ++g) {
+    const int i = g * NT + threadIdx.x * 8;
+    if (i < P.H) emit(i, v[g]);
+  }
+  for (int i = kNormGroups * NT + threadIdx.x * 8; i < P.H; i += NT) {
+    float w[8];
+    load8(i, w);
+    emit(i, w);
   }
 }
 
 // Next tokens from the LM head's argmax keys; clears the keys for the next step.
 extern "C" __global__ void mk_b_argmax(Params P, const Step* Sd) {
-  const Step S = *Sd;
+  const Step S = ld_const(Sd);
   const int b = threadIdx.x;
   if (b >= P.B) return;
   const unsigned long long k = P.lm_part[b];
@@ -366,35 +517,30 @@ extern "C" __global__ void mk_b_argmax(Params P, const Step* Sd) {
 }
 
 // Test entry: Y[b][n] = sum_k W[n][k] (A.hi[b][k] + A.lo[b][k]) for bf16 W
-// [N, K] and A [2][Bp][K] (rows B..Bp-1 zero), one 16-row tile per
-// workgroup, through the same wave loop and workgroup reduction as the
-// operators.
+// [N, K] and A [2][Bp][K] (rows B..Bp-1 zero): the same staged core, each
+// wave owning 32 consecutive rows, one split.
 template <int BT>
 __device__ __forceinline__ void t_bgemm(const uint16_t* W, const uint16_t* A, float* Y, int N, int K, int B) {
+  constexpr int KC = BChunk<BT>::KC;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* red = reinterpret_cast<float*>(smem);
-  constexpr int NW = kBgemmWaves, D = BDepth<BT>::D;
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int row0 = blockIdx.x * 16, nvec = K / 8;
-  const v4u* wr[1] = {reinterpret_cast<const v4u*>(W + (int64_t)min(row0 + (lane & 15), N - 1) * K)};
-  const v4u* ar[BT];
+  const int row0 = (blockIdx.x * kBgemmWaves + wave) * 32;
+  const v4u* wr[kRT];
 #pragma unroll
-  for (int t = 0; t < BT; ++t) ar[t] = reinterpret_cast<const v4u*>(A + (int64_t)(t * 16 + (lane & 15)) * K);
-  f32x4 acc[1][BT];
-  mma_wave<1, BT, NW, D>(wr, ar, (int64_t)16 * BT * nvec, nvec, wave, lane, acc);
+  for (int r = 0; r < kRT; ++r)
+    wr[r] = reinterpret_cast<const v4u*>(W + (int64_t)min(row0 + r * 16 + (lane & 15), N - 1) * K);
+  f32x4 acc[kRT][BT];
+  staged_gemm<kRT, BT, KC>(A, K, wr, 0, (K + KC - 1) / KC, lds, lane, acc);
 #pragma unroll
-  for (int t = 0; t < BT; ++t)
+  for (int r = 0; r < kRT; ++r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[((wave * BT + t) * 4 + j) * 64 + lane] = acc[0][t][j];
-  __syncthreads();
-  for (int e = threadIdx.x; e < BT * 256; e += NW * kWave) {
-    const int t = e >> 8, j = (e >> 6) & 3, ln = e & 63;
-    const int b = t * 16 + (ln & 15), row = row0 + 4 * (ln >> 4) + j;
-    if (b >= B || row >= N) continue;
-    float s = 0.f;
-    for (int w = 0; w < NW; ++w) s += red[((w * BT + t) * 4 + j) * 64 + ln];
-    Y[(int64_t)b * N + row] = s;
-  }
+    for (int t = 0; t < BT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = t * 16 + (lane & 15), row = row0 + r * 16 + 4 * (lane >> 4) + j;
+        if (b < B && row < N) Y[(int64_t)b * N + row] = acc[r][t][j];
+      }
 }
 extern "C" __global__ __launch_bounds__(kBgemmWaves * kWave) void mk_t_bgemm_kernel(const uint16_t* W,
                                                                                      const uint16_t* A, float* Y,
@@ -403,6 +549,13 @@ extern "C" __global__ __launch_bounds__(kBgemmWaves * kWave) void mk_t_bgemm_ker
   if (bt == 1) t_bgemm<1>(W, A, Y, N, K, B);
   else if (bt == 2) t_bgemm<2>(W, A, Y, N, K, B);
   else t_bgemm<4>(W, A, Y, N, K, B);
+}
+
+// LDS bytes of the batched projection kernels and the test entry, by batch
+// tiles (the argmax keys of the LM head come on top).
+int b_lds_bytes(int bt) {
+  return bt == 1 ? chunk_lds_bytes<1, BChunk<1>::KC>() : bt == 2 ? chunk_lds_bytes<2, BChunk<2>::KC>()
+                                                                 : chunk_lds_bytes<4, BChunk<4>::KC>();
 }
 
 }  // namespace mk

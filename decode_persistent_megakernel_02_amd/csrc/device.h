@@ -285,47 +285,60 @@ __device__ __forceinline__ float dot_k(const v4u* kv, int i, const float* q, flo
   }
 }
 
-// qs: LDS [G][HD] (rotated queries); pr: LDS [G][64] scratch of this wave.
-// kc, vc: this group's cache rows (position p at + p * HD elements).
+// A block's K and V in registers: K, this lane's part of its position's row;
+// V, this lane's dims of every position of the block.
 template <int HD, typename KT>
-__device__ __forceinline__ void attn_block(const float* qs, const KT* kc, const KT* vc, int p0, int p1, int G,
-                                           float* pr, int lane, AttnState<HD>& st) {
+struct AttnBuf {
   using Gm = AttnGeom<HD, KT>;
-  constexpr int DPL = Gm::DPL, NP = Gm::NP, LPP = Gm::LPP, EPL = Gm::EPL, KV16 = Gm::KV16;
-  const int np = p1 - p0;
-  const int my = lane / LPP, part = lane % LPP;  // position and row part this lane scores
-  // K: this lane's part of its position's row; V: this lane's dims of every position
-  v4u kr[KV16];
-  if (my < np) {
-    const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)(p0 + my) * HD + part * EPL);
+  static constexpr int VW = (Gm::DPL * (int)sizeof(KT) + 3) / 4;  // 32-bit words of V per lane and position
+  v4u kr[Gm::KV16];
+  uint32_t vr[Gm::NP][VW];
+};
+
+typedef const __attribute__((address_space(1))) uint32_t* gu32_ptr;
+typedef const __attribute__((address_space(1))) uint16_t* gu16_ptr;
+
+// Issues the K and V loads of the block [p0, p0 + NP).  Positions at or past
+// p1 read position p1 - 1 (in bounds; attn_compute masks them), so no load is
+// predicated.  kc, vc: this group's cache rows (position p at + p * HD).
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_load(const KT* kc, const KT* vc, int p0, int p1, int lane,
+                                          AttnBuf<HD, KT>& bf) {
+  using Gm = AttnGeom<HD, KT>;
+  const int my = lane / Gm::LPP, part = lane % Gm::LPP;
+  const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)min(p0 + my, p1 - 1) * HD + part * Gm::EPL);
 #pragma unroll
-    for (int i = 0; i < KV16; ++i) kr[i] = krow[i];
-  }
-  constexpr int VW = (DPL * (int)sizeof(KT) + 3) / 4;  // 32-bit words of V per lane and position
-  uint32_t vr[NP][VW];
+  for (int i = 0; i < Gm::KV16; ++i) bf.kr[i] = ld_g(krow + i);
 #pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    if (j < np) {
-      const KT* vrow = vc + (int64_t)(p0 + j) * HD + lane * DPL;
-      if constexpr (sizeof(KT) == 2 && DPL == 1) {
-        vr[j][0] = reinterpret_cast<const uint16_t*>(vrow)[0];
-      } else {
+  for (int j = 0; j < Gm::NP; ++j) {
+    const KT* vrow = vc + (int64_t)min(p0 + j, p1 - 1) * HD + lane * Gm::DPL;
+    if constexpr (sizeof(KT) == 2 && Gm::DPL == 1) {
+      bf.vr[j][0] = *(gu16_ptr)vrow;
+    } else {
 #pragma unroll
-        for (int w = 0; w < VW; ++w) vr[j][w] = reinterpret_cast<const uint32_t*>(vrow)[w];
-      }
+      for (int w = 0; w < AttnBuf<HD, KT>::VW; ++w) bf.vr[j][w] = ((gu32_ptr)vrow)[w];
     }
   }
+}
+
+// Online-softmax update with the block [p0, min(p0 + NP, p1)) held in bf.
+// qs: LDS [G][HD] (rotated queries); pr: LDS [G][64] scratch of this wave.
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_compute(const AttnBuf<HD, KT>& bf, const float* qs, int p0, int p1, int G,
+                                             float* pr, int lane, AttnState<HD>& st) {
+  using Gm = AttnGeom<HD, KT>;
+  constexpr int DPL = Gm::DPL, NP = Gm::NP, LPP = Gm::LPP, EPL = Gm::EPL;
+  const int np = min(NP, p1 - p0);
+  const int my = lane / LPP, part = lane % LPP;  // position and row part this lane scores
   const float scale = 1.0f / sqrtf((float)HD);
   float sc[kMaxGqa];
 #pragma unroll
   for (int h = 0; h < kMaxGqa; ++h) sc[h] = 0.f;
-  if (my < np) {
 #pragma unroll
-    for (int i = 0; i < EPL / 8; ++i) {
+  for (int i = 0; i < EPL / 8; ++i) {
 #pragma unroll
-      for (int h = 0; h < kMaxGqa; ++h)
-        if (h < G) sc[h] = dot_k<KT>(kr, i, qs + h * HD + part * EPL + i * 8, sc[h]);
-    }
+    for (int h = 0; h < kMaxGqa; ++h)
+      if (h < G) sc[h] = dot_k<KT>(bf.kr, i, qs + h * HD + part * EPL + i * 8, sc[h]);
   }
 #pragma unroll
   for (int h = 0; h < kMaxGqa; ++h) {
@@ -354,14 +367,14 @@ __device__ __forceinline__ void attn_block(const float* qs, const KT* kc, const 
           float v[DPL];
           if constexpr (sizeof(KT) == 2) {
             if constexpr (DPL == 2) {
-              v[0] = bf_lo(vr[j][0]);
-              v[DPL - 1] = bf_hi(vr[j][0]);
+              v[0] = bf_lo(bf.vr[j][0]);
+              v[DPL - 1] = bf_hi(bf.vr[j][0]);
             } else {
-              v[0] = bf_lo(vr[j][0]);
+              v[0] = bf_lo(bf.vr[j][0]);
             }
           } else {
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) v[e] = __uint_as_float(vr[j][e]);
+            for (int e = 0; e < DPL; ++e) v[e] = __uint_as_float(bf.vr[j][e]);
           }
 #pragma unroll
           for (int e = 0; e < DPL; ++e) st.o[h][e] = fmaf(p, v[e], st.o[h][e]);
@@ -370,6 +383,34 @@ __device__ __forceinline__ void attn_block(const float* qs, const KT* kc, const 
     }
   }
   __builtin_amdgcn_wave_barrier();
+}
+
+// A wave's blocks b, b + stride, ... (below p1), the first already loaded into
+// A: the next block's loads are in flight while the current one is computed.
+// Each exit path has its own code, so every path issues a fixed number of
+// loads (see gemv_stream).
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_pipeline(AttnBuf<HD, KT>& A, AttnBuf<HD, KT>& B, const float* qs, const KT* kc,
+                                              const KT* vc, int b, int p1, int stride, int G, float* pr, int lane,
+                                              AttnState<HD>& st) {
+  for (;;) {
+    int n = b + stride;
+    if (n >= p1) {
+      attn_compute<HD, KT>(A, qs, b, p1, G, pr, lane, st);
+      return;
+    }
+    attn_load<HD, KT>(kc, vc, n, p1, lane, B);
+    attn_compute<HD, KT>(A, qs, b, p1, G, pr, lane, st);
+    b = n;
+    n = b + stride;
+    if (n >= p1) {
+      attn_compute<HD, KT>(B, qs, b, p1, G, pr, lane, st);
+      return;
+    }
+    attn_load<HD, KT>(kc, vc, n, p1, lane, A);
+    attn_compute<HD, KT>(B, qs, b, p1, G, pr, lane, st);
+    b = n;
+  }
 }
 
 // Writes a wave's state as G records of (o[HD], m, l).
@@ -407,13 +448,12 @@ __device__ __forceinline__ void attn_partial(const float* q, const KT* kc, const
   attn_load_q<HD>(q, G, qs, lane);
   AttnState<HD> st;
   st.init();
-  for (int b0 = p0; b0 < p1; b0 += NP) attn_block<HD, KT>(qs, kc, vc, b0, min(b0 + NP, p1), G, pr, lane, st);
+  AttnBuf<HD, KT> A, B;
+  attn_load<HD, KT>(kc, vc, p0, p1, lane, A);
+  attn_pipeline<HD, KT>(A, B, qs, kc, vc, p0, p1, NP, G, pr, lane, st);
   attn_store_state<HD>(st, G, out, lane);
 }
 
-// Log-sum-exp merge of n partial records laid out [n][G][HD + 2] (stride
-// `rec_stride` floats between partials); writes the G normalised outputs to
-// out[G][HD].  Records with l == 0 (no positions) are skipped.
 // Splits v into bf16 hi = bf16(v) and lo = bf16(v - hi): hi + lo carries 16
 // significant bits, the operand pair of the batched matrix-core products.
 __device__ __forceinline__ void split_bf16(float v, uint16_t* hi, uint16_t* lo) {
@@ -422,28 +462,44 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t* hi, uint16_t* lo) 
   *lo = f2bf(v - bf1(h));
 }
 
+// Log-sum-exp merge of n partial records laid out [n][G][HD + 2] (stride
+// `rec_stride` floats between partials); writes the G normalised outputs to
+// out[G][HD] (and, if given, their bf16 hi/lo operand planes).  Records with
+// l == 0 (no positions) carry weight 0.  Lane s reads the (m, l) of record s
+// (64 records per pass), so the maximum and the weights come from two wave
+// reductions; the output loads of all records are then independent of each
+// other and stay in flight together.
 template <int HD>
 __device__ __forceinline__ void attn_merge(const float* part, int n, int G, float* out, int lane, int rec_stride = -1,
                                            uint16_t* out_hi = nullptr, uint16_t* out_lo = nullptr) {
   constexpr int DPL = HD / kWave;
   if (rec_stride < 0) rec_stride = G * (HD + 2);
   for (int h = 0; h < G; ++h) {
-    float M = -INFINITY, Lsum = 0.f, o[DPL];
+    const float* ph = part + h * (HD + 2);
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < n; s0 += kWave) {
+      const int s = min(s0 + lane, n - 1);
+      const float ls = ph[(int64_t)s * rec_stride + HD + 1], ms = ph[(int64_t)s * rec_stride + HD];
+      if (s0 + lane < n && ls > 0.f) M = fmaxf(M, ms);
+    }
+    M = wave_max(M);
+    float Lsum = 0.f, o[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const float* ps = part + (int64_t)s * rec_stride + h * (HD + 2);
-      const float ls = ps[HD + 1];
-      if (!(ls > 0.f)) continue;
-      const float ms = ps[HD];
-      const float Mn = fmaxf(M, ms);
-      const float a = __expf(M - Mn), b = __expf(ms - Mn);
-      Lsum = Lsum * a + ls * b;
+    for (int s0 = 0; s0 < n; s0 += kWave) {
+      const int s = min(s0 + lane, n - 1);
+      const float ls = ph[(int64_t)s * rec_stride + HD + 1], ms = ph[(int64_t)s * rec_stride + HD];
+      const float w = s0 + lane < n && ls > 0.f ? __expf(ms - M) : 0.f;  // this lane's record weight
+      Lsum += w * (ls > 0.f ? ls : 0.f);
+      const int cnt = min(kWave, n - s0);
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __shfl(w, j);
+        const float* pj = ph + (int64_t)(s0 + j) * rec_stride + lane * DPL;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + ps[lane * DPL + e] * b;
-      M = Mn;
+        for (int e = 0; e < DPL; ++e) o[e] = fmaf(wj, wj > 0.f ? pj[e] : 0.f, o[e]);
+      }
     }
-    const float inv = 1.0f / Lsum;
+    const float inv = 1.0f / wave_sum(Lsum);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
       out[h * HD + lane * DPL + e] = o[e] * inv;
@@ -453,6 +509,26 @@ __device__ __forceinline__ void attn_merge(const float* part, int n, int G, floa
 }
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+
+// Loads of data no kernel writes while it runs (the host-built task tables,
+// the per-layer weight pointer tables, the per-step argument record) go
+// through the constant address space as 32-bit words, so that a load at a
+// wave-uniform address uses the scalar cache.  As vector loads -- which the
+// 16-bit fields of a task descriptor would otherwise get -- they would queue
+// in order behind the weight stream.
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+template <class T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "loaded as 32-bit words");
+  struct Words {
+    uint32_t w[sizeof(T) / 4];
+  } t;
+  const_u32_ptr q = (const_u32_ptr)p;
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 4); ++k) t.w[k] = q[k];
+  return __builtin_bit_cast(T, t);
+}
+__device__ __forceinline__ Task load_task(const Task* tasks, int i) { return ld_const(tasks + i); }
 
 // ---------------------------------------------------------------------------
 // Cache addressing and token lookup shared by the single-sequence and batched paths.

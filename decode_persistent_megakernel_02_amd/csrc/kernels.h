@@ -6,7 +6,7 @@
 
 namespace mk {
 extern "C" __global__ void mk_persistent(Params P, const Step* S, int page_floats, int scratch_floats);
-extern "C" __global__ void mk_op_attn_split(Params P, const Step* S, int layer);
+extern "C" __global__ void mk_op_attn_split(Params P, const Step* S, int layer, int fuse_merge);
 extern "C" __global__ void mk_op_attn_merge(Params P, const Step* S, int layer);
 extern "C" __global__ void mk_set_step(Step* dst, Step s);
 #define MK_OP_DECL(name) extern "C" __global__ void name(Params P, const Step* S, const Task* tasks, int count, int pf, int sf);
@@ -32,6 +32,12 @@ MK_BGEMM_DECL(mk_b_gu_b1) MK_BGEMM_DECL(mk_b_gu_b2) MK_BGEMM_DECL(mk_b_gu_b4)
 MK_BGEMM_DECL(mk_b_down_b1) MK_BGEMM_DECL(mk_b_down_b2) MK_BGEMM_DECL(mk_b_down_b4)
 MK_BGEMM_DECL(mk_b_lm_b1) MK_BGEMM_DECL(mk_b_lm_b2) MK_BGEMM_DECL(mk_b_lm_b4)
 #undef MK_BGEMM_DECL
+extern "C" __global__ void mk_b_fin_qkv(Params P, const Step* S, int layer, int ks);
+extern "C" __global__ void mk_b_fin_o(Params P, const Step* S, int layer, int ks);
+extern "C" __global__ void mk_b_fin_gu(Params P, const Step* S, int layer, int ks);
+extern "C" __global__ void mk_b_fin_down(Params P, const Step* S, int layer, int ks);
+int b_lds_bytes(int bt);  // LDS of the batched projection kernels by batch tiles
+constexpr int kBChunkCols[5] = {0, 256, 128, 128, 128};  // activation chunk width by batch tiles
 extern "C" __global__ void mk_b_norm(Params P, const Step* S, int layer, int kind);
 extern "C" __global__ void mk_b_argmax(Params P, const Step* S);
 extern "C" __global__ void mk_t_bgemm_kernel(const uint16_t* W, const uint16_t* A, float* Y, int N, int K, int B);

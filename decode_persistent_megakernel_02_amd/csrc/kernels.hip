@@ -34,7 +34,7 @@ __device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, ui
   StageSrc r{nullptr, nullptr, nullptr, P.H};
   switch (kind) {
     case SK_ATTN_NORM:
-      r.gamma = P.attn_norm[l];
+      r.gamma = ld_const(P.attn_norm + l);
       if (l == 0) r.bf = P.embed + (int64_t)token_of(P, S, b) * H;
       else r.f32 = P.xs + ((int64_t)l * P.B + b) * H;
       break;
@@ -43,7 +43,7 @@ __device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, ui
       r.f32 = P.attn_out + ((int64_t)l * P.B + b) * r.n;
       break;
     case SK_FFN_NORM:
-      r.gamma = P.ffn_norm[l];
+      r.gamma = ld_const(P.ffn_norm + l);
       r.f32 = P.xmid + ((int64_t)l * P.B + b) * H;
       break;
     case SK_H:
@@ -64,44 +64,72 @@ __device__ void stage_input(const Params& P, const Step& S, uint16_t key, int b,
   stage_vector(page, r.f32, r.bf, r.n, r.gamma, P.eps, lane);
 }
 
-// All kWaves waves of a workgroup stage the vector: each lane owns 8-element
-// groups g = wave*64 + lane + k*512 and loads up to four of them at once;
-// the RMSNorm sum of squares is reduced per wave, then across the waves in a
-// fixed order.  Ends with a workgroup barrier; every wave must call it once.
-__device__ void stage_input_wg(const Params& P, const Step& S, uint16_t key, int b, float* page, float* red,
-                               int wave, int lane) {
-  const StageSrc r = stage_src(P, S, key, b);
-  constexpr int NG = kWaves * kWave, U = 4;
+// All kWaves waves of a workgroup stage the vector, in two halves so that
+// the loads can be issued before a task's weight prefetch (loads return in
+// issue order; staging loads issued after the prefetch would wait for it).
+// Each lane owns 8-element groups g = wave*64 + lane + u*512; the first SU
+// groups of every lane are loaded by stage_issue into registers, the rest (only
+// for vectors longer than SU * 4096) by stage_finish itself.  stage_finish sums
+// the squares per wave, then across the waves in a fixed order, normalises,
+// and ends with a workgroup barrier; every wave must call it once.
+template <int SU>
+struct StageRegs {
+  v4u raw[SU][2];  // fp32 source: the 8 values; bf16 source: raw[u][0] holds them
+  v4u gain[SU];    // the 8 RMSNorm gains (if any)
+};
+
+template <int SU>
+__device__ __forceinline__ void stage_issue(const StageSrc& r, int wave, int lane, StageRegs<SU>& st) {
+  constexpr int NG = kWaves * kWave;
+  const int g0 = wave * kWave + lane;
+#pragma unroll
+  for (int u = 0; u < SU; ++u) {
+    const int i = min((g0 + u * NG) * 8, r.n - 8);  // clamped: never predicated (see gemv_run)
+    const v4u* a = r.bf ? reinterpret_cast<const v4u*>(r.bf + i) : reinterpret_cast<const v4u*>(r.f32 + i);
+    const v4u* b = r.bf ? a : reinterpret_cast<const v4u*>(r.f32 + i + 4);
+    st.raw[u][0] = ld_g(a);
+    st.raw[u][1] = ld_g(b);
+    st.gain[u] = ld_g(r.gamma ? reinterpret_cast<const v4u*>(r.gamma + i) : a);  // no gain: a harmless reload
+  }
+}
+
+__device__ __forceinline__ void stage_unpack(const StageSrc& r, const v4u& a, const v4u& b, float (&v)[8]) {
+  if (r.bf) {
+    v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
+    v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
+  } else {
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+}
+
+template <int SU>
+__device__ void stage_finish(const Params& P, const StageSrc& r, const StageRegs<SU>& st, float* page, float* red,
+                             int wave, int lane) {
+  constexpr int NG = kWaves * kWave;
   const int g0 = wave * kWave + lane;
   float ss = 0.f;
-  for (int base = 0; base < r.n; base += U * NG * 8) {
-    float v[U][8];
+  auto put = [&](int i, const float (&v)[8]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + (g0 + u * NG) * 8;
-      if (i < r.n) {
-        if (r.bf) {
-          const v4u w = *reinterpret_cast<const v4u*>(r.bf + i);
-          v[u][0] = bf_lo(w.x); v[u][1] = bf_hi(w.x); v[u][2] = bf_lo(w.y); v[u][3] = bf_hi(w.y);
-          v[u][4] = bf_lo(w.z); v[u][5] = bf_hi(w.z); v[u][6] = bf_lo(w.w); v[u][7] = bf_hi(w.w);
-        } else {
-          const float4 a = *reinterpret_cast<const float4*>(r.f32 + i);
-          const float4 c = *reinterpret_cast<const float4*>(r.f32 + i + 4);
-          v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
-          v[u][4] = c.x; v[u][5] = c.y; v[u][6] = c.z; v[u][7] = c.w;
-        }
-      }
+    for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
+    *reinterpret_cast<float4*>(page + i) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(page + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  };
+#pragma unroll
+  for (int u = 0; u < SU; ++u) {
+    const int i = (g0 + u * NG) * 8;
+    if (i < r.n) {
+      float v[8];
+      stage_unpack(r, st.raw[u][0], st.raw[u][1], v);
+      put(i, v);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + (g0 + u * NG) * 8;
-      if (i < r.n) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(v[u][j], v[u][j], ss);
-        *reinterpret_cast<float4*>(page + i) = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
-        *reinterpret_cast<float4*>(page + i + 4) = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
-      }
-    }
+  }
+  for (int i = (g0 + SU * NG) * 8; i < r.n; i += NG * 8) {  // long vectors only
+    const v4u* a = r.bf ? reinterpret_cast<const v4u*>(r.bf + i) : reinterpret_cast<const v4u*>(r.f32 + i);
+    const v4u* b = r.bf ? a : reinterpret_cast<const v4u*>(r.f32 + i + 4);
+    float v[8];
+    stage_unpack(r, ld_g(a), ld_g(b), v);
+    put(i, v);
   }
   if (r.gamma) {
     ss = wave_sum(ss);
@@ -111,8 +139,11 @@ __device__ void stage_input_wg(const Params& P, const Step& S, uint16_t key, int
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) tot += red[w];
     const float inv = 1.0f / sqrtf(tot / (float)r.n + P.eps);
-    for (int i = g0 * 8; i < r.n; i += NG * 8) {  // the groups this lane wrote
-      const v4u gu = *reinterpret_cast<const v4u*>(r.gamma + i);
+    for (int i = g0 * 8, u = 0; i < r.n; i += NG * 8, ++u) {  // the groups this lane wrote
+      v4u gu = st.gain[0];
+#pragma unroll
+      for (int k = 1; k < SU; ++k) gu = u == k ? st.gain[k] : gu;
+      if (u >= SU) gu = ld_g(reinterpret_cast<const v4u*>(r.gamma + i));
       float4 a = *reinterpret_cast<float4*>(page + i);
       float4 c = *reinterpret_cast<float4*>(page + i + 4);
       a.x = a.x * inv * bf_lo(gu.x); a.y = a.y * inv * bf_hi(gu.x);
@@ -147,7 +178,7 @@ __device__ __forceinline__ void gemv_setup(const Params& P, const Task& d, GemvR
   g.stride = K / 8;
   g.split = R;
   if constexpr (TT == TT_QKV) {
-    const uint16_t* W = d.a0 == 0 ? P.wq[l] : d.a0 == 1 ? P.wk[l] : P.wv[l];
+    const uint16_t* W = d.a0 == 0 ? ld_const(P.wq + l) : d.a0 == 1 ? ld_const(P.wk + l) : ld_const(P.wv + l);
     g.base0 = reinterpret_cast<const v4u*>(W + (int64_t)d.a1 * K);
     if (d.a3) {  // one RoPE pair: rows a1 and a1 + hd/2
       g.base1 = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + d.a3) * K);
@@ -158,15 +189,15 @@ __device__ __forceinline__ void gemv_setup(const Params& P, const Task& d, GemvR
       g.mask = (1u << d.a2) - 1;
     }
   } else if constexpr (TT == TT_GU) {  // rows: gate a1.., then up a1..
-    g.base0 = reinterpret_cast<const v4u*>(P.w_gate[l] + (int64_t)d.a1 * K);
-    g.base1 = reinterpret_cast<const v4u*>(P.w_up[l] + (int64_t)d.a1 * K);
+    g.base0 = reinterpret_cast<const v4u*>(ld_const(P.w_gate + l) + (int64_t)d.a1 * K);
+    g.base1 = reinterpret_cast<const v4u*>(ld_const(P.w_up + l) + (int64_t)d.a1 * K);
     g.split = R / 2;
     const uint32_t half = (1u << d.a2) - 1;
     g.mask = half | (half << (R / 2));
   } else {
     const uint16_t* W;
-    if constexpr (TT == TT_O) W = P.wo[l];
-    else if constexpr (TT == TT_DOWN) W = P.w_down[l];
+    if constexpr (TT == TT_O) W = ld_const(P.wo + l);
+    else if constexpr (TT == TT_DOWN) W = ld_const(P.w_down + l);
     else W = P.tied ? P.embed : P.lm_head;
     g.base0 = reinterpret_cast<const v4u*>(W + (int64_t)d.a1 * K);
     g.base1 = g.base0;
@@ -258,7 +289,7 @@ __device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, i
   if (i0 >= count) return 0;
   v4u bufA[D][R], bufB[D][R];
   GemvRows<R> gA, gB;
-  gemv_setup<TT>(P, tasks[i0], gA);
+  gemv_setup<TT>(P, load_task(tasks, i0), gA);
   gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
   wait();
   float y[R];
@@ -270,7 +301,7 @@ __device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, i
       gemv_put<TT>(res, j++, y, lane);
       break;
     }
-    gemv_setup<TT>(P, tasks[n], gB);
+    gemv_setup<TT>(P, load_task(tasks, n), gB);
     gemv_prefetch<R, D, EXACT>(bufB, gB, lane);
     gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
     gemv_put<TT>(res, j++, y, lane);
@@ -281,7 +312,7 @@ __device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, i
       gemv_put<TT>(res, j++, y, lane);
       break;
     }
-    gemv_setup<TT>(P, tasks[n], gA);
+    gemv_setup<TT>(P, load_task(tasks, n), gA);
     gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
     gemv_run<R, D, EXACT>(bufB, gB, page, lane, y);
     gemv_put<TT>(res, j++, y, lane);
@@ -290,20 +321,88 @@ __device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, i
   return j;
 }
 
-// The epilogues of a wave's n streamed tasks, from their results in res.
+// One task's whole epilogue in one lane (the per-operator kernels run the
+// epilogues of a wave's tasks side by side, lane j finishing task j).
+// Rows as in gemv_setup; y[r] = dot product of row slot r.
+template <int TT>
+__device__ __forceinline__ void epilogue_lane(const Params& P, const Step& S, const Task& d,
+                                              const float (&y)[TaskShape<TT>::R], unsigned long long& best) {
+  constexpr int R = TaskShape<TT>::R;
+  const int l = d.layer, b = d.batch;
+  const int64_t H = P.H;
+  if constexpr (TT == TT_QKV) {
+    if (d.a3) {  // rotate the pair (lo, hi) = (y0, y1) by the position's angle
+      const int half = P.hd / 2, i = d.a1 % P.hd;
+      const float c = P.rope_cos[(int64_t)S.pos * half + i], sn = P.rope_sin[(int64_t)S.pos * half + i];
+      const float lo = y[0] * c - y[1] * sn, hi = y[1] * c + y[0] * sn;
+      if (d.a0 == 0) {
+        float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd;
+        q[d.a1] = lo;
+        q[d.a1 + d.a3] = hi;
+      } else {
+        const int64_t o = kv_off(P, l, b, d.a1 / P.hd, S.pos);
+        kv_store(P, P.kcache, o + i, lo);
+        kv_store(P, P.kcache, o + i + half, hi);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (r < d.a2) {
+          const int row = d.a1 + r;
+          kv_store(P, P.vcache, kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd, y[r]);
+        }
+    }
+  } else if constexpr (TT == TT_O) {
+    const int64_t tok = l == 0 ? (int64_t)token_of(P, S, b) * H : 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < d.a2) {
+        const int row = d.a1 + r;
+        const float xin = l == 0 ? bf1(P.embed[tok + row]) : P.xs[((int64_t)l * P.B + b) * H + row];
+        P.xmid[((int64_t)l * P.B + b) * H + row] = xin + y[r];
+      }
+  } else if constexpr (TT == TT_GU) {
+#pragma unroll
+    for (int r = 0; r < R / 2; ++r)
+      if (r < d.a2) P.h[((int64_t)l * P.B + b) * P.F + d.a1 + r] = silu(y[r]) * y[r + R / 2];
+  } else if constexpr (TT == TT_DOWN) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < d.a2) {
+        const int row = d.a1 + r;
+        P.xs[((int64_t)(l + 1) * P.B + b) * H + row] = P.xmid[((int64_t)l * P.B + b) * H + row] + y[r];
+      }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < d.a2) {
+        const int row = d.a1 + r;
+        if (S.logits) S.logits[(int64_t)b * P.V + row] = y[r];
+        const unsigned long long k = argmax_key(y[r], (uint32_t)row);
+        best = k > best ? k : best;
+      }
+  }
+}
+
+// The epilogues of a wave's n (<= 64) streamed tasks, from their results in
+// res: lane j finishes task j.
 template <int TT>
 __device__ __forceinline__ void gemv_finish(const Params& P, const Step& S, const Task* tasks, int n, int i0,
                                             int stride, int lane, const float* res, Lds* L) {
   constexpr int R = TaskShape<TT>::R;
   __builtin_amdgcn_wave_barrier();
-  for (int j = 0; j < n; ++j) {
-    const Task d = tasks[i0 + j * stride];
-    GemvRows<R> g;
-    gemv_setup<TT>(P, d, g);
+  unsigned long long best = 0;
+  if (lane < n) {
+    const Task d = tasks[i0 + lane * stride];
     float y[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) y[r] = res[j * R + r];
-    gemv_epilogue<TT>(P, S, d, g.mask, y, lane, L);
+    for (int r = 0; r < R; ++r) y[r] = res[lane * R + r];
+    epilogue_lane<TT>(P, S, d, y, best);
+  }
+  if constexpr (TT == TT_LM) {
+    best = wave_max_u64(best);
+    if (lane == 0 && n > 0) __hip_atomic_fetch_max(&L->lm_best[load_task(tasks, i0).batch], best, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
@@ -520,7 +619,7 @@ __device__ void worker(const Params& P, const Step& S, Lds* L, const float* page
 
 extern "C" __global__ __launch_bounds__(kWaves * kWave, 1) void mk_persistent(Params P, const Step* Sd,
                                                                                 int page_floats, int scratch_floats) {
-  const Step S = *Sd;
+  const Step S = ld_const(Sd);
   extern __shared__ __align__(16) unsigned char smem[];
   Lds* L = reinterpret_cast<Lds*>(smem);
   float* pages = reinterpret_cast<float*>(smem + sizeof(Lds));
@@ -561,20 +660,28 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
   Lds* L = reinterpret_cast<Lds*>(smem);
   float* page = reinterpret_cast<float*>(smem + sizeof(Lds));
   float* scr = page + page_floats;
-  const Step S = *Sd;
+  const Step S = ld_const(Sd);
   // wave index made explicitly uniform: task descriptors then load through the
   // scalar cache and never queue behind the weight stream
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
-  const Task first = tasks[0];
+  const Task first = load_task(tasks, 0);
   // Every wave stages its slice of the input vector and passes the staging
-  // barriers exactly once: inside its first task's wait() -- after that task's
-  // weight loads are in flight -- or after the loop if it has no task.
+  // barriers exactly once: the loads are issued first, then (in gemv_stream)
+  // the first task's weight prefetch, then wait() finishes the staging -- or
+  // after the loop if the wave has no task.
+  constexpr int SU = TT == TT_DOWN ? 4 : 2;  // register-staged groups per lane: vectors up to SU * 4096
+  StageSrc src{};
+  StageRegs<SU> st;
+  if (first.stage) {
+    src = stage_src(P, S, first.stage, first.batch);
+    stage_issue<SU>(src, wave, lane, st);
+  }
   bool staged = false;
   float* red = reinterpret_cast<float*>(L->slot);  // per-wave partial sums of squares
   auto wait = [&]() __attribute__((always_inline)) -> bool {
     if (!staged) {
-      if (first.stage) stage_input_wg(P, S, first.stage, first.batch, page, red, wave, lane);
+      if (first.stage) stage_finish<SU>(P, src, st, page, red, wave, lane);
       else __syncthreads();
       staged = true;
     }
@@ -584,9 +691,28 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
     // scratch_floats = result slots per wave (R per task of this wave)
     const int i0 = blockIdx.x * kWaves + wave, stride = gridDim.x * kWaves;
     float* res = scr + wave * scratch_floats;
-    const int n = gemv_stream<TT, EXACT>(P, tasks, count, i0, stride, lane, page, res, wait);
+    // optional wave timeline (debug): start, input staged, stream done, epilogues done
+    const bool tr = P.trace && P.trace_op == ((TT << 16) | first.layer) && 4 * (i0 + 1) <= 2 * P.trace_cap;
+    const uint64_t t0 = tr ? clock_now() : 0;
+    uint64_t t1 = 0;
+    auto wait_tr = [&]() __attribute__((always_inline)) -> bool {
+      const bool r = wait();
+      if (tr && !t1) t1 = clock_now();
+      return r;
+    };
+    const int n = gemv_stream<TT, EXACT>(P, tasks, count, i0, stride, lane, page, res, wait_tr);
+    const uint64_t t2 = tr ? clock_now() : 0;
     wait();
     gemv_finish<TT>(P, S, tasks, n, i0, stride, lane, res, L);
+    if (tr && lane == 0) {
+      const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID: wave, SIMD, CU, SE
+      const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // XCC_ID
+      unsigned long long* o = P.trace + 4 * (int64_t)i0;
+      o[0] = ((unsigned long long)((xcc & 0xF) << 28 | (hw & 0x0FFFFFFF)) << 32) | (uint32_t)t0;
+      o[1] = t1;
+      o[2] = t2;
+      o[3] = clock_now();
+    }
   } else {
     for (int i = blockIdx.x * kWaves + wave; i < count; i += gridDim.x * kWaves) {
       const Task d = tasks[i];
@@ -638,15 +764,27 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
   float* pr = qs + G * HD + wave * G * kWave;                // [G][64] per wave
   float* recs = qs + G * HD + kAttnWaves * G * kWave;        // [kAttnWaves][G][HD + 2]
   const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * HD;
-  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) qs[i] = q[i];
-  __syncthreads();
   const int64_t o0 = kv_off(P, l, b, grp, 0);
   const KT* kc = static_cast<const KT*>(P.kcache) + o0;
   const KT* vc = static_cast<const KT*>(P.vcache) + o0;
+  // The query loads first (every block needs them), then this wave's first
+  // K/V block; only then wait for the queries.
+  constexpr int QPT = (kMaxGqa * HD + kAttnWaves * kWave - 1) / (kAttnWaves * kWave);
+  float qv[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) qv[i] = q[min((int)threadIdx.x + i * kAttnWaves * kWave, G * HD - 1)];
+  const int b0 = p0 + wave * Gm::NP;
+  AttnBuf<HD, KT> A, B;
+  if (b0 < p1) attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = threadIdx.x + i * kAttnWaves * kWave;
+    if (idx < G * HD) qs[idx] = qv[i];
+  }
+  __syncthreads();
   AttnState<HD> st;
   st.init();
-  for (int b0 = p0 + wave * Gm::NP; b0 < p1; b0 += kAttnWaves * Gm::NP)
-    attn_block<HD, KT>(qs, kc, vc, b0, min(b0 + Gm::NP, p1), G, pr, lane, st);
+  if (b0 < p1) attn_pipeline<HD, KT>(A, B, qs, kc, vc, b0, p1, kAttnWaves * Gm::NP, G, pr, lane, st);
   attn_store_state<HD>(st, G, recs + wave * G * (HD + 2), lane);
   __syncthreads();
   float* out = P.attn_part + ((((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit + s) * G * (HD + 2);
@@ -677,13 +815,40 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
   }
 }
 
-extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_split(Params P, const Step* Sd, int layer) {
+// Log-sum-exp merge of the used splits of (batch row b, KV group grp): query
+// head h of the group by wave h % nw.  Writes the fp32 attention output and,
+// on the batched path, the O-projection's bf16 operand planes.
+__device__ __forceinline__ void merge_group(const Params& P, int layer, int b, int grp, int used, int wave, int nw,
+                                            int lane) {
+  const int G = P.nq / P.nkv;
+  const float* part = P.attn_part + (((int64_t)layer * P.B + b) * P.nkv + grp) * P.nsplit * G * (P.hd + 2);
+  for (int h = wave; h < G; h += nw) {
+    const int64_t col = (int64_t)(grp * G + h) * P.hd;
+    float* out = P.attn_out + ((int64_t)layer * P.B + b) * P.nq * P.hd + col;
+    uint16_t* ohi = P.ao ? P.ao + (int64_t)b * P.nq * P.hd + col : nullptr;
+    uint16_t* olo = P.ao ? ohi + (int64_t)P.Bp * P.nq * P.hd : nullptr;
+    if (P.hd == 128) attn_merge<128>(part + h * (128 + 2), used, 1, out, lane, G * (128 + 2), ohi, olo);
+    else attn_merge<64>(part + h * (64 + 2), used, 1, out, lane, G * (64 + 2), ohi, olo);
+  }
+}
+
+// Split-KV attention, one workgroup per (batch row, KV group, split).  With
+// `fuse_merge`, the last workgroup of a (batch row, KV group) to finish
+// merges all its splits: every workgroup publishes its records with an
+// agent-scope fence and counts itself in attn_count; the one that brings the
+// count to the number of used splits acquires, merges, and resets the count
+// for the next launch.  No workgroup ever waits for another.
+extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_split(Params P, const Step* Sd, int layer,
+                                                                                 int fuse_merge) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sm = reinterpret_cast<float*>(smem);
-  const Step S = *Sd;
+  __shared__ uint32_t is_last;
+  const Step S = ld_const(Sd);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s = blockIdx.x % P.nsplit, bg = blockIdx.x / P.nsplit;
   const int b = bg / P.nkv, grp = bg % P.nkv;
+  const int used = (S.pos + 1 + P.split - 1) / P.split;
+  if (s >= used) return;  // past the current length: no record, not counted
   if (P.kv_f32) {
     if (P.hd == 128) attn_split_wg<128, float>(P, S, layer, b, grp, s, sm, wave, lane);
     else attn_split_wg<64, float>(P, S, layer, b, grp, s, sm, wave, lane);
@@ -691,23 +856,28 @@ extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_spli
     if (P.hd == 128) attn_split_wg<128, uint16_t>(P, S, layer, b, grp, s, sm, wave, lane);
     else attn_split_wg<64, uint16_t>(P, S, layer, b, grp, s, sm, wave, lane);
   }
+  if (!fuse_merge) return;
+  __threadfence();  // release this wave's records at agent scope
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&P.attn_count[bg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = old + 1 == (uint32_t)used;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();  // acquire the other workgroups' records
+  merge_group(P, layer, b, grp, used, wave, kAttnWaves, lane);
+  if (threadIdx.x == 0) __hip_atomic_store(&P.attn_count[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Log-sum-exp merge of the used splits: one wave per (batch row, query head).
+// Log-sum-exp merge as its own launch: one wave per (batch row, query head).
 extern "C" __global__ __launch_bounds__(kMaxGqa * kWave) void mk_op_attn_merge(Params P, const Step* Sd, int layer) {
-  const Step S = *Sd;
+  const Step S = ld_const(Sd);
   const int G = P.nq / P.nkv, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave >= G) return;
-  const int b = blockIdx.x / P.nkv, grp = blockIdx.x % P.nkv, T = S.pos + 1;
-  const int used = (T + P.split - 1) / P.split;
-  const float* part = P.attn_part + (((int64_t)layer * P.B + b) * P.nkv + grp) * P.nsplit * G * (P.hd + 2);
-  const int64_t col = (int64_t)(grp * G + wave) * P.hd;
-  float* out = P.attn_out + ((int64_t)layer * P.B + b) * P.nq * P.hd + col;
-  // batched path: also the operand planes of the O-projection
-  uint16_t* ohi = P.ao ? P.ao + (int64_t)b * P.nq * P.hd + col : nullptr;
-  uint16_t* olo = P.ao ? ohi + (int64_t)P.Bp * P.nq * P.hd : nullptr;
-  if (P.hd == 128) attn_merge<128>(part + wave * (128 + 2), used, 1, out, lane, G * (128 + 2), ohi, olo);
-  else attn_merge<64>(part + wave * (64 + 2), used, 1, out, lane, G * (64 + 2), ohi, olo);
+  const int b = blockIdx.x / P.nkv, grp = blockIdx.x % P.nkv;
+  const int used = (S.pos + 1 + P.split - 1) / P.split;
+  merge_group(P, layer, b, grp, used, wave, G, lane);
 }
 
 // Per-step arguments live in device memory so that a step's launches can be

@@ -19,8 +19,9 @@ constexpr int kMaxSplit = 4096;       // positions per split-KV attention task
 constexpr int kAttnWaves = 4;         // waves per split in the per-operator attention kernel
 constexpr int kLocalSlots = 64;       // per-CU LDS counters for aggregated event signals
 constexpr int kMaxBatch = 64;         // sequences per step
-constexpr int kMaxTasksPerWave = 64; // GEMV results a wave of a per-operator kernel holds in LDS
-constexpr int kBgemmWaves = 8;        // waves per workgroup of the batched (MFMA) projections
+constexpr int kMaxTasksPerWave = 64; // GEMV results a wave of a per-operator kernel holds in LDS (<= wave size:
+                                      // lane j runs the epilogue of task j)
+constexpr int kBgemmWaves = 4;        // waves per workgroup of the batched (MFMA) projections
 constexpr int kNormThreads = 256;     // threads per row of the batched RMSNorm kernel
 constexpr uint16_t kNone16 = 0xFFFF;
 constexpr uint8_t kNone8 = 0xFF;
@@ -158,7 +159,9 @@ struct Params {
   uint16_t* ao;      // K = nq*hd:  attention output
   uint16_t* ah;      // K = F:      SwiGLU output
   int32_t Bp;        // operand rows: B rounded up to 16, 32 or 64
+  float* bpart;      // split-K partial sums of the batched projections
   unsigned long long* lm_part;  // [B] running argmax key (ordered value, ~index), cleared by the argmax task
+  uint32_t* attn_count;         // [B][nkv] split workgroups finished this launch (fused merge), reset by the last
   const float* rope_cos;  // [max_seq][hd/2]
   const float* rope_sin;
   // task tables
@@ -169,6 +172,7 @@ struct Params {
                             //       7 waiter (0 scheduler event, 1 scheduler page, 2 worker), 8 frontier, 9 ticket
   unsigned long long* trace;  // optional per-task timestamps
   int32_t trace_cap;
+  int32_t trace_op;           // per-operator kernels: (type << 16) | layer whose waves log timestamps, -1 none
 };
 
 // Per-launch arguments.

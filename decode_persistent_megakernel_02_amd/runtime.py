@@ -20,12 +20,16 @@ def upload_weights(weights: dict, device="cuda") -> dict:
     return {n: to_device_bits(a, device) for n, a in weights.items()}
 
 
-def generate_device_weights(shape, seed=0, random_norms=False, device="cuda") -> dict:
-    """Generate each weight with the seeded host generator and move it to the device."""
+def generate_device_weights(shape, seed=0, random_norms=False, device="cuda", progress=None) -> dict:
+    """Generate each weight with the seeded host generator and move it to the
+    device; `progress(done, total)` is called after every tensor if given."""
     from synth import gen, presets
     out = {}
-    for name in presets.weight_shapes(shape):
+    names = list(presets.weight_shapes(shape))
+    for i, name in enumerate(names):
         out[name] = to_device_bits(gen.gen_weight(shape, name, seed, random_norms), device)
+        if progress:
+            progress(i + 1, len(names))
     return out
 
 

@@ -65,8 +65,10 @@ enum {
 enum {
   MK_FLAG_TRACE = 1u << 0,  /* record per-task {cu, task, start, end} timestamps */
   MK_FLAG_POISON = 1u << 1,  /* fill activation scratch with NaN before every step */
-  MK_FLAG_NO_GRAPH = 1u << 2 /* per-op mode: launch every operator eagerly instead of
-                                replaying the step as one captured HIP graph */
+  MK_FLAG_NO_GRAPH = 1u << 2, /* per-op mode: launch every operator eagerly instead of
+                                 replaying the step as one captured HIP graph */
+  MK_FLAG_FUSED_MERGE = 1u << 3 /* per-op mode: run the attention log-sum-exp merge in the last
+                                   split workgroup of each KV group instead of as its own launch */
 };
 
 /* Model shape and runtime options.  Weights are bf16, activations fp32, the

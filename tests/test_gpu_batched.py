@@ -205,14 +205,15 @@ def test_batch_rows_are_independent(abi):
 
 
 def test_batched_graph_replay_equals_eager(abi):
-    """The captured step graph and eager launches give identical results."""
+    """The captured step graph, eager launches, and the attention merge run as
+    its own launch all give identical results."""
     from decode_persistent_megakernel_02_amd import runtime
     shape, B, P = MINI, 5, 6
     w = gen.gen_weights(shape, 4, True)
     dw = runtime.upload_weights(w)
     prompt = torch.from_numpy(gen.tokens(3, presets.TID_PROMPT, 0, B * P, shape.vocab).reshape(B, P)).cuda()
     res = []
-    for flags in (0, abi.MK_FLAG_NO_GRAPH):
+    for flags in (0, abi.MK_FLAG_NO_GRAPH, abi.MK_FLAG_FUSED_MERGE):
         h = runtime.create(shape, dw, P + 8, B, abi.MK_MODE_PER_OP, flags, kv_fp32=False)
         out = torch.zeros(B, dtype=torch.int32, device="cuda")
         lg = torch.zeros(B, shape.vocab, dtype=torch.float32, device="cuda")
@@ -222,7 +223,8 @@ def test_batched_graph_replay_equals_eager(abi):
         abi.mk_synchronize(h)
         res.append((out.cpu().numpy().copy(), lg.cpu().numpy().copy()))
         abi.mk_destroy(h)
-    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    for r in res[1:]:
+        assert np.array_equal(res[0][0], r[0]) and np.array_equal(res[0][1], r[1])
 
 
 def layer_subset(shape, n_layers):

@@ -201,3 +201,21 @@ def test_graph_replays_match_eager_bitwise(abi):
             torch.cuda.synchronize()
         runs.append(np.stack(res))
     assert np.array_equal(runs[0], runs[1])
+
+
+def test_fused_merge_equals_separate_merge_bitwise(abi):
+    """The log-sum-exp merge run by the last split workgroup of each KV group
+    gives the same bits as the merge launched on its own (same arithmetic,
+    same order), over contexts that span one to five 8-position splits."""
+    shape = MINI_G8
+    w = gen.gen_weights(shape, 9, True)
+    prompt = gen.tokens(9, 3, 0, 5, shape.vocab)
+    runs = []
+    for flags in (abi.MK_FLAG_FUSED_MERGE, 0):
+        case = Case(shape, 40, PER_OP, flags=flags, attn_split=8, weights=w)
+        res = [case.prefill(prompt)[0]]
+        for t in (3, 200, 17, 5, 99, 1, 250, 42, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23,
+                  24, 25, 26, 27, 28, 29, 30, 31, 32):
+            res.append(case.step(t)[0])
+        runs.append(np.stack(res))
+    assert np.array_equal(runs[0], runs[1])
