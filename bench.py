@@ -161,7 +161,23 @@ def main():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--fused-merge", action="store_true",
                     help="merge attention splits in the last split workgroup instead of a separate launch")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB five times (the known-size reference "
+                         "for scaling hardware byte counters) and exit")
+    ap.add_argument("--counters", type=int, default=0, metavar="STEPS",
+                    help="only run prefill and STEPS eager decode steps (no graph, no timing) so that a "
+                         "hardware-counter profiler sees each launch, and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(it measures one GPU's share of the work).", file=sys.stderr)
@@ -198,9 +214,22 @@ def main():
     # batch 1 keeps an fp32 KV cache; the batched workloads state a bf16 cache
     kv_fp32 = B == 1
     flags = abi.MK_FLAG_FUSED_MERGE if args.fused_merge else 0
+    if args.counters:
+        h = runtime.create(shape, dw, wl.prompt_len + args.counters + 1, B, abi.MK_MODE_PER_OP,
+                           flags | abi.MK_FLAG_NO_GRAPH, kv_fp32=kv_fp32)
+        toks = torch.zeros(args.counters + 1, B, dtype=torch.int32, device="cuda")
+        abi.mk_prefill(h, prompt_t, toks[0])
+        for s in range(args.counters):
+            abi.mk_decode_step(h, toks[s], toks[s + 1])
+            abi.mk_synchronize(h)
+            log(f"counter pass: decode step {s + 1}/{args.counters} done")
+        abi.mk_destroy(h)
+        print(json.dumps({"counter_pass_steps": args.counters, "workload": wl.name}))
+        return
     h = runtime.create(shape, dw, max_seq + 64, B, abi.MK_MODE_PER_OP, flags, kv_fp32=kv_fp32)
     total, eager_total, (gu_ms, gu_n), same_tokens, breakdown = time_decode(abi, h, prompt_t, steps, warmup, shape,
                                                                              torch, log)
+    gu_exact = bool(abi.mk_get_debug_view(h).exact_ops & (1 << abi.TASK_TYPES["gu"]))
     abi.mk_destroy(h)
     ms = total / steps
     kern_ms = gu_ms / max(gu_n, 1)
@@ -238,7 +267,7 @@ def main():
         "bound_ms_per_token": bound_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,
-                     "kernel": "mk_op_gu" if B == 1 else f"mk_b_gu_b{1 if B <= 16 else 2 if B <= 32 else 4}",
+                     "kernel": ("mk_op_gu_x" if gu_exact else "mk_op_gu") if B == 1 else f"mk_b_gu_b{1 if B <= 16 else 2 if B <= 32 else 4}",
                      "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": kb},
         "step_frac_of_hbm_bound": bound_ms / ms,
         "eager_ms_per_step": eager_total / steps,

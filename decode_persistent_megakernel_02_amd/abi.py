@@ -68,7 +68,8 @@ class mk_debug_view(ctypes.Structure):
     _fields_ = [("xs", ctypes.c_void_p), ("xmid", ctypes.c_void_p), ("q", ctypes.c_void_p),
                 ("attn_out", ctypes.c_void_p), ("h", ctypes.c_void_p), ("events", ctypes.c_void_p),
                 ("n_events", ctypes.c_int32), ("n_tasks", ctypes.c_int32), ("ncu", ctypes.c_int32),
-                ("nsplit", ctypes.c_int32), ("split", ctypes.c_int32), ("lds_bytes", ctypes.c_int32)]
+                ("nsplit", ctypes.c_int32), ("split", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("exact_ops", ctypes.c_uint32)]
 
 
 # Every symbol the headers declare, with its ctypes signature.

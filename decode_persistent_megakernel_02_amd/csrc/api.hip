@@ -33,9 +33,13 @@ mk_status fail(mk_status s, const std::string& m) {
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 // Positions per attention split when several sequences share a step: the
-// (sequence, KV head) pairs already give the grid its width, so each
-// workgroup takes a longer stretch of the cache.
-constexpr int kBatchedSplit = 128;
+// (sequence, KV head) pairs already widen the grid; 128 positions measured
+// better than 512 at 8 sequences of 4K tokens (more workgroups in flight).
+int batched_split(int max_seq) {
+  (void)max_seq;
+  return 128;
+}
+
 
 // Batch tiles (16 rows each) of the batched projections: 1, 2 or 4.
 int batch_tiles(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : 4; }
@@ -64,7 +68,7 @@ GraphConfig graph_config(const mk_config* c, int ncu) {
   GraphConfig g;
   g.L = c->n_layers; g.H = c->hidden; g.nq = c->n_q_heads; g.nkv = c->n_kv_heads; g.hd = c->head_dim;
   g.F = c->ffn; g.V = c->vocab; g.B = c->max_batch; g.max_seq = c->max_seq;
-  g.split = c->attn_split ? c->attn_split : c->max_batch > 1 ? kBatchedSplit : auto_split(c->max_seq);
+  g.split = c->attn_split ? c->attn_split : c->max_batch > 1 ? batched_split(c->max_seq) : auto_split(c->max_seq);
   g.ncu = ncu;
   return g;
 }
@@ -100,6 +104,7 @@ struct mk_handle {
   int32_t* d_tok_scratch = nullptr;
   Step* d_step = nullptr;               // per-step arguments, written by mk_set_step
   int attn_lds = 0;                     // per-op split attention kernel
+  int attn_full_lds = 0;                // whole-context attention kernel
   hipStream_t cap_stream = nullptr;     // private stream used to capture the step graph
   hipGraph_t step_graph = nullptr;
   hipGraphExec_t graph_exec = nullptr;
@@ -184,6 +189,11 @@ mk_status device_facts(int* ncu, double* ticks_per_us, int* max_lds) {
 }
 
 bool fused_merge(const mk_handle* h) { return (h->cfg.flags & MK_FLAG_FUSED_MERGE) != 0; }
+// A context that fits one split runs as one workgroup per (sequence, KV head)
+// that writes the final output (no merge launch).  Forcing that shape on
+// longer contexts measured slower: at the 8B shape, batch 1, 37 against 21 us
+// per layer (8 CUs busy), and at the 70B shape, 64 sequences, 100 against 73.
+bool single_split(const mk_handle* h) { return h->P.nsplit == 1; }
 
 // Batched projection kernels by operator (QKV, O, GU, DOWN, LM) and batch tiles (1, 2, 4).
 const void* bgemm_kernel(int type, int bt) {
@@ -272,7 +282,12 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
   for (int l = 0; l < Pc.L; ++l) {
     MK_TRY(norm(l, 0));
     MK_TRY(gemm(TT_QKV, l));
-    {
+    if (single_split(h)) {
+      int layer = l;
+      void* args[] = {&Pc, &sp, &layer};
+      MK_TRY(launch(TT_ATTN, reinterpret_cast<const void*>(&mk_op_attn_full), dim3(Pc.B * Pc.nkv),
+                    dim3(kAttnFullWaves * kWave), args, (size_t)h->attn_full_lds));
+    } else {
       int layer = l, fuse = fused_merge(h) ? 1 : 0;
       void* args[] = {&Pc, &sp, &layer, &fuse};
       MK_TRY(launch(TT_ATTN, reinterpret_cast<const void*>(&mk_op_attn_split), dim3(Pc.B * Pc.nkv * Pc.nsplit),
@@ -302,13 +317,16 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
     const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
     if (count <= 0) continue;
     const int type = g.stage_type[s];
-    if (type == TT_MERGE && fused_merge(h)) continue;  // done by the last split workgroup
+    if (type == TT_MERGE && (fused_merge(h) || single_split(h))) continue;  // done by the attention launch
     const bool timed = timed_ok && ((h->timed_mask >> type) & 1) && 2 * (h->ev_used + 1) <= (int)h->ev_pool.size();
     if (timed) HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used], st));
     if (type == TT_ATTN || type == TT_MERGE) {
       int layer = g.tasks[b0].layer, fuse = fused_merge(h) ? 1 : 0;
       void* args[] = {&Pc, &sp, &layer, &fuse};
-      if (type == TT_ATTN)
+      if (type == TT_ATTN && single_split(h))
+        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_full), dim3(h->P.B * h->P.nkv),
+                                dim3(kAttnFullWaves * kWave), args, (size_t)h->attn_full_lds, st));
+      else if (type == TT_ATTN)
         HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_split),
                                 dim3(h->P.B * h->P.nkv * h->P.nsplit), dim3(kAttnWaves * kWave), args,
                                 (size_t)h->attn_lds, st));
@@ -316,8 +334,8 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
         HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(h->P.B * h->P.nkv),
                                 dim3((h->P.nq / h->P.nkv) * kWave), args, 0, st));
     } else {
-      // a GEMV wave holds at most kMaxTasksPerWave results
-      const int min_grid = (count + kWaves * kMaxTasksPerWave - 1) / (kWaves * kMaxTasksPerWave);
+      // a GEMV wave holds at most kMaxTasksPerWave results: keep the average at half of that
+      const int min_grid = (count + kWaves * kMaxTasksPerWave / 2 - 1) / (kWaves * kMaxTasksPerWave / 2);
       const int grid = std::max(min_grid, std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]));
       const Task* tasks = h->d_stage_tasks + b0;
       int opf = h->op_page[type];
@@ -580,7 +598,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
                     : t == TT_LM ? TaskShape<TT_LM>::D : 0;
     h->op_exact[t] = rows > 0 && pfl % 512 == 0 && (pfl / 512) % depth == 0;
     // per-wave scratch: attention state, or the results of the wave's GEMV tasks
-    h->op_sf[t] = t == TT_ATTN ? h->scratch_floats : kMaxTasksPerWave * rows;
+    h->op_sf[t] = t == TT_ATTN ? h->scratch_floats : kMaxTasksPerWave * (rows + 1);  // results + task ids
     h->op_lds[t] = (int)sizeof(Lds) + h->op_page[t] * 4 + kWaves * h->op_sf[t] * 4;
     if (h->op_lds[t] > max_lds)
       return fail(MK_ERR_UNSUPPORTED, "operator LDS need exceeds " + std::to_string(max_lds));
@@ -591,9 +609,13 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     h->op_grid_cap[t] = std::max(1, nb) * ncu;
   }
   h->attn_lds = (G * hd + kAttnWaves * G * kWave + kAttnWaves * G * (hd + 2)) * 4;
-  if (h->attn_lds > max_lds) return fail(MK_ERR_UNSUPPORTED, "attention LDS need exceeds the device limit");
+  h->attn_full_lds = (G * hd + kAttnFullWaves * G * kWave + kAttnFullWaves * G * (hd + 2)) * 4;
+  if (std::max(h->attn_lds, h->attn_full_lds) > max_lds)
+    return fail(MK_ERR_UNSUPPORTED, "attention LDS need exceeds the device limit");
   HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_op_attn_split),
                               hipFuncAttributeMaxDynamicSharedMemorySize, h->attn_lds));
+  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_op_attn_full),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, h->attn_full_lds));
   if (cfg->mode == MK_MODE_MEGAKERNEL) {
     if (h->lds_mega > max_lds)
       return fail(MK_ERR_UNSUPPORTED,
@@ -812,6 +834,9 @@ mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out) {
   out->nsplit = h->P.nsplit;
   out->split = h->P.split;
   out->lds_bytes = h->lds_mega;
+  out->exact_ops = 0;
+  for (int t = 0; t < 9; ++t)
+    if (h->op_exact[t]) out->exact_ops |= 1u << t;
   return MK_OK;
 }
 

@@ -8,6 +8,7 @@ namespace mk {
 extern "C" __global__ void mk_persistent(Params P, const Step* S, int page_floats, int scratch_floats);
 extern "C" __global__ void mk_op_attn_split(Params P, const Step* S, int layer, int fuse_merge);
 extern "C" __global__ void mk_op_attn_merge(Params P, const Step* S, int layer);
+extern "C" __global__ void mk_op_attn_full(Params P, const Step* S, int layer);
 extern "C" __global__ void mk_set_step(Step* dst, Step s);
 #define MK_OP_DECL(name) extern "C" __global__ void name(Params P, const Step* S, const Task* tasks, int count, int pf, int sf);
 MK_OP_DECL(mk_op_qkv)

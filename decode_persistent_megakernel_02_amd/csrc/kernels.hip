@@ -269,22 +269,60 @@ __device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const 
   return true;
 }
 
-// A wave's whole sequence of GEMV tasks i0, i0 + stride, ... with two
-// buffers: the next task's first D chunks are in flight while the current
-// task is consumed, so the wave's weight stream does not drain between tasks.
-// The R dot products of the wave's j-th task go to res[j * R ...] (LDS); the
-// epilogues run afterwards (gemv_finish), so that no global store is pending
-// while weight loads are in flight (stores and loads share one counter, and
-// a mix of both forces a wait for everything).  Returns the number of tasks.
+// A wave's GEMV tasks with two buffers: the next task's first D chunks are in
+// flight while the current task is consumed, so the wave's weight stream
+// does not drain between tasks.  The tasks of a workgroup form a pool (slot p
+// is task slot_task(p)) whose first kWaves slots are the waves' first tasks;
+// after that a wave takes the next free slot from an LDS counter, so a wave
+// that streams faster takes more tasks and the workgroup's waves finish
+// together.  (A
+// device-wide counter would also balance across CUs, but thousands of waves
+// contending on one device-scope atomic serialise at the memory side; it made
+// every launch several times slower.)  The R dot products of the wave's j-th
+// task go to res[j * R ...] and its index to ids[j] (LDS); the epilogues run
+// afterwards (gemv_finish), so that no global store is pending while weight
+// loads are in flight (stores and loads share one counter, and a mix of both
+// forces a wait for everything).  Returns the number of tasks the wave ran.
 template <int TT>
-__device__ __forceinline__ void gemv_put(float* res, int j, const float (&y)[TaskShape<TT>::R], int lane) {
+__device__ __forceinline__ void gemv_put(float* res, int* ids, int j, int task, const float (&y)[TaskShape<TT>::R],
+                                         int lane) {
   constexpr int R = TaskShape<TT>::R;
   if (lane < R) res[j * R + lane] = pick<R>(y, lane);
+  if (lane == 0) ids[j] = task;
+}
+
+// The task of pool slot p of this workgroup, or `count` past its end.  The
+// dispatcher deals workgroups to the XCDs in turn (workgroup b runs on XCD
+// b % kXcds).  When the grid is a multiple of kXcds, the workgroups of one
+// XCD share one contiguous kXcds-th of the task list, dealt to them in runs of
+// kWaves tasks; otherwise the runs go to all workgroups in turn.  (Dealing
+// runs to all workgroups in turn makes XCD x read the same few consecutive
+// rows out of every kXcds runs -- for 8 KB rows a fixed 32 KB slice of every
+// 256 KB -- and the XCDs then finish up to a fifth apart.)
+__device__ __forceinline__ int slot_task(uint32_t p, int count) {
+  const int n = gridDim.x, run = (int)(p / kWaves), k = (int)(p % kWaves);
+  if (n % kXcds) {
+    const int t = (run * n + (int)blockIdx.x) * kWaves + k;
+    return t < count ? t : count;
+  }
+  const int per = (count + kXcds - 1) / kXcds, x = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+  const int t = (run * (n / kXcds) + j) * kWaves + k;
+  return t < per && x * per + t < count ? x * per + t : count;
+}
+
+// The next pool slot's task of this wave, or `count` when the pool is empty
+// or the wave's result slots are full (j results kept, one task in hand).
+__device__ __forceinline__ int gemv_next(uint32_t* pool, int j, int count, int lane) {
+  if (j + 2 > kMaxTasksPerWave) return count;
+  uint32_t p = 0;
+  if (lane == 0) p = lds_add(pool, 1u);
+  p = __builtin_amdgcn_readfirstlane(p);
+  return slot_task(p, count);
 }
 
 template <int TT, bool EXACT, class Wait>
-__device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, int count, int i0, int stride,
-                                           int lane, const float* page, float* res, Wait wait) {
+__device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, int count, int i0, int lane, const float* page, float* res, int* ids, uint32_t* pool,
+                                           Wait wait) {
   constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
   if (i0 >= count) return 0;
   v4u bufA[D][R], bufB[D][R];
@@ -293,30 +331,28 @@ __device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, i
   gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
   wait();
   float y[R];
-  int i = i0, j = 0;
+  int a = i0, b, j = 0;
   for (;;) {
-    int n = i + stride;
-    if (n >= count) {
+    b = gemv_next(pool, j, count, lane);
+    if (b >= count) {
       gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
-      gemv_put<TT>(res, j++, y, lane);
+      gemv_put<TT>(res, ids, j++, a, y, lane);
       break;
     }
-    gemv_setup<TT>(P, load_task(tasks, n), gB);
+    gemv_setup<TT>(P, load_task(tasks, b), gB);
     gemv_prefetch<R, D, EXACT>(bufB, gB, lane);
     gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
-    gemv_put<TT>(res, j++, y, lane);
-    i = n;
-    n = i + stride;
-    if (n >= count) {
+    gemv_put<TT>(res, ids, j++, a, y, lane);
+    a = gemv_next(pool, j, count, lane);
+    if (a >= count) {
       gemv_run<R, D, EXACT>(bufB, gB, page, lane, y);
-      gemv_put<TT>(res, j++, y, lane);
+      gemv_put<TT>(res, ids, j++, b, y, lane);
       break;
     }
-    gemv_setup<TT>(P, load_task(tasks, n), gA);
+    gemv_setup<TT>(P, load_task(tasks, a), gA);
     gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
     gemv_run<R, D, EXACT>(bufB, gB, page, lane, y);
-    gemv_put<TT>(res, j++, y, lane);
-    i = n;
+    gemv_put<TT>(res, ids, j++, b, y, lane);
   }
   return j;
 }
@@ -385,15 +421,15 @@ __device__ __forceinline__ void epilogue_lane(const Params& P, const Step& S, co
 }
 
 // The epilogues of a wave's n (<= 64) streamed tasks, from their results in
-// res: lane j finishes task j.
+// res and their task indices in ids: lane j finishes task j.
 template <int TT>
 __device__ __forceinline__ void gemv_finish(const Params& P, const Step& S, const Task* tasks, int n, int i0,
-                                            int stride, int lane, const float* res, Lds* L) {
+                                            int lane, const float* res, const int* ids, Lds* L) {
   constexpr int R = TaskShape<TT>::R;
   __builtin_amdgcn_wave_barrier();
   unsigned long long best = 0;
   if (lane < n) {
-    const Task d = tasks[i0 + lane * stride];
+    const Task d = tasks[ids[lane]];
     float y[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) y[r] = res[lane * R + r];
@@ -665,6 +701,7 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
   // scalar cache and never queue behind the weight stream
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
+  if (threadIdx.x == 0) L->ticket = kWaves;  // task pool: the first kWaves slots are the waves' own
   const Task first = load_task(tasks, 0);
   // Every wave stages its slice of the input vector and passes the staging
   // barriers exactly once: the loads are issued first, then (in gemv_stream)
@@ -689,10 +726,11 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
   };
   if constexpr (TT == TT_QKV || TT == TT_O || TT == TT_GU || TT == TT_DOWN || TT == TT_LM) {
     // scratch_floats = result slots per wave (R per task of this wave)
-    const int i0 = blockIdx.x * kWaves + wave, stride = gridDim.x * kWaves;
+    const int i0 = slot_task(wave, count), wid = blockIdx.x * kWaves + wave;
     float* res = scr + wave * scratch_floats;
+    int* ids = reinterpret_cast<int*>(res + kMaxTasksPerWave * TaskShape<TT>::R);
     // optional wave timeline (debug): start, input staged, stream done, epilogues done
-    const bool tr = P.trace && P.trace_op == ((TT << 16) | first.layer) && 4 * (i0 + 1) <= 2 * P.trace_cap;
+    const bool tr = P.trace && P.trace_op == ((TT << 16) | first.layer) && 4 * (wid + 1) <= 2 * P.trace_cap;
     const uint64_t t0 = tr ? clock_now() : 0;
     uint64_t t1 = 0;
     auto wait_tr = [&]() __attribute__((always_inline)) -> bool {
@@ -700,14 +738,14 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
       if (tr && !t1) t1 = clock_now();
       return r;
     };
-    const int n = gemv_stream<TT, EXACT>(P, tasks, count, i0, stride, lane, page, res, wait_tr);
+    const int n = gemv_stream<TT, EXACT>(P, tasks, count, i0, lane, page, res, ids, &L->ticket, wait_tr);
     const uint64_t t2 = tr ? clock_now() : 0;
     wait();
-    gemv_finish<TT>(P, S, tasks, n, i0, stride, lane, res, L);
+    gemv_finish<TT>(P, S, tasks, n, i0, lane, res, ids, L);
     if (tr && lane == 0) {
       const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID: wave, SIMD, CU, SE
       const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // XCC_ID
-      unsigned long long* o = P.trace + 4 * (int64_t)i0;
+      unsigned long long* o = P.trace + 4 * (int64_t)wid;
       o[0] = ((unsigned long long)((xcc & 0xF) << 28 | (hw & 0x0FFFFFFF)) << 32) | (uint32_t)t0;
       o[1] = t1;
       o[2] = t2;
@@ -749,52 +787,54 @@ MK_OP_KERNEL(mk_op_gu_x, TT_GU, true)
 MK_OP_KERNEL(mk_op_down_x, TT_DOWN, true)
 MK_OP_KERNEL(mk_op_lm_x, TT_LM, true)
 
-// Attention, per-operator path: one workgroup of kAttnWaves waves per
-// (batch row, KV group, split).  The split's positions are dealt to the waves
-// in blocks; each wave keeps an online-softmax state; the workgroup merges its
-// waves' states through LDS and writes one (o, m, l) record per head.
-template <int HD, typename KT>
+// Attention, per-operator path: one workgroup of NW waves per (batch row, KV
+// group, split).  The split's positions are dealt to the waves in blocks;
+// each wave keeps an online-softmax state; the workgroup merges its waves'
+// states through LDS.  With a single split (FINAL) the result is normalised
+// and written as the attention output itself (and, on the batched path, the
+// O-projection's operand planes), so no merge launch follows; otherwise it
+// is one (o, m, l) record per head for the merge.
+template <int HD, typename KT, int NW, bool FINAL>
 __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, int l, int b, int grp, int s, float* sm,
                                               int wave, int lane) {
   using Gm = AttnGeom<HD, KT>;
   const int G = P.nq / P.nkv, T = S.pos + 1;
   const int p0 = s * P.split, p1 = min(p0 + P.split, T);
   if (p0 >= T) return;
-  float* qs = sm;                                            // [G][HD]
-  float* pr = qs + G * HD + wave * G * kWave;                // [G][64] per wave
-  float* recs = qs + G * HD + kAttnWaves * G * kWave;        // [kAttnWaves][G][HD + 2]
+  float* qs = sm;                                     // [G][HD]
+  float* pr = qs + G * HD + wave * G * kWave;         // [G][64] per wave
+  float* recs = qs + G * HD + NW * G * kWave;         // [NW][G][HD + 2]
   const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * HD;
   const int64_t o0 = kv_off(P, l, b, grp, 0);
   const KT* kc = static_cast<const KT*>(P.kcache) + o0;
   const KT* vc = static_cast<const KT*>(P.vcache) + o0;
   // The query loads first (every block needs them), then this wave's first
   // K/V block; only then wait for the queries.
-  constexpr int QPT = (kMaxGqa * HD + kAttnWaves * kWave - 1) / (kAttnWaves * kWave);
+  constexpr int QPT = (kMaxGqa * HD + NW * kWave - 1) / (NW * kWave);
   float qv[QPT];
 #pragma unroll
-  for (int i = 0; i < QPT; ++i) qv[i] = q[min((int)threadIdx.x + i * kAttnWaves * kWave, G * HD - 1)];
+  for (int i = 0; i < QPT; ++i) qv[i] = q[min((int)threadIdx.x + i * NW * kWave, G * HD - 1)];
   const int b0 = p0 + wave * Gm::NP;
   AttnBuf<HD, KT> A, B;
   if (b0 < p1) attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
-    const int idx = threadIdx.x + i * kAttnWaves * kWave;
+    const int idx = threadIdx.x + i * NW * kWave;
     if (idx < G * HD) qs[idx] = qv[i];
   }
   __syncthreads();
   AttnState<HD> st;
   st.init();
-  if (b0 < p1) attn_pipeline<HD, KT>(A, B, qs, kc, vc, b0, p1, kAttnWaves * Gm::NP, G, pr, lane, st);
+  if (b0 < p1) attn_pipeline<HD, KT>(A, B, qs, kc, vc, b0, p1, NW * Gm::NP, G, pr, lane, st);
   attn_store_state<HD>(st, G, recs + wave * G * (HD + 2), lane);
   __syncthreads();
-  float* out = P.attn_part + ((((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit + s) * G * (HD + 2);
-  for (int h = wave; h < G; h += kAttnWaves) {
-    // merge the waves' records of head h into one (unnormalised) record
+  for (int h = wave; h < G; h += NW) {
+    // merge the waves' records of head h
     constexpr int DPL = HD / kWave;
     float M = -INFINITY, Ls = 0.f, o[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-    for (int w = 0; w < kAttnWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float* r = recs + (w * G + h) * (HD + 2);
       const float lw = r[HD + 1];
       if (!(lw > 0.f)) continue;
@@ -805,12 +845,26 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
       for (int e = 0; e < DPL; ++e) o[e] = o[e] * a + r[lane * DPL + e] * c;
       M = Mn;
     }
-    float* oh = out + h * (HD + 2);
+    if constexpr (FINAL) {
+      const int64_t col = (int64_t)(grp * G + h) * HD + lane * DPL;
+      float* out = P.attn_out + ((int64_t)l * P.B + b) * P.nq * P.hd + col;
+      const float inv = 1.0f / Ls;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) oh[lane * DPL + e] = o[e];
-    if (lane == 0) {
-      oh[HD] = M;
-      oh[HD + 1] = Ls;
+      for (int e = 0; e < DPL; ++e) {
+        out[e] = o[e] * inv;
+        if (P.ao) {
+          uint16_t* hi = P.ao + (int64_t)b * P.nq * P.hd + col + e;
+          split_bf16(o[e] * inv, hi, hi + (int64_t)P.Bp * P.nq * P.hd);
+        }
+      }
+    } else {
+      float* oh = P.attn_part + ((((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit + s) * G * (HD + 2) + h * (HD + 2);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) oh[lane * DPL + e] = o[e];
+      if (lane == 0) {
+        oh[HD] = M;
+        oh[HD + 1] = Ls;
+      }
     }
   }
 }
@@ -850,11 +904,11 @@ extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_spli
   const int used = (S.pos + 1 + P.split - 1) / P.split;
   if (s >= used) return;  // past the current length: no record, not counted
   if (P.kv_f32) {
-    if (P.hd == 128) attn_split_wg<128, float>(P, S, layer, b, grp, s, sm, wave, lane);
-    else attn_split_wg<64, float>(P, S, layer, b, grp, s, sm, wave, lane);
+    if (P.hd == 128) attn_split_wg<128, float, kAttnWaves, false>(P, S, layer, b, grp, s, sm, wave, lane);
+    else attn_split_wg<64, float, kAttnWaves, false>(P, S, layer, b, grp, s, sm, wave, lane);
   } else {
-    if (P.hd == 128) attn_split_wg<128, uint16_t>(P, S, layer, b, grp, s, sm, wave, lane);
-    else attn_split_wg<64, uint16_t>(P, S, layer, b, grp, s, sm, wave, lane);
+    if (P.hd == 128) attn_split_wg<128, uint16_t, kAttnWaves, false>(P, S, layer, b, grp, s, sm, wave, lane);
+    else attn_split_wg<64, uint16_t, kAttnWaves, false>(P, S, layer, b, grp, s, sm, wave, lane);
   }
   if (!fuse_merge) return;
   __threadfence();  // release this wave's records at agent scope
@@ -868,6 +922,25 @@ extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_spli
   __threadfence();  // acquire the other workgroups' records
   merge_group(P, layer, b, grp, used, wave, kAttnWaves, lane);
   if (threadIdx.x == 0) __hip_atomic_store(&P.attn_count[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whole-context attention: one workgroup of kAttnFullWaves waves per (batch
+// row, KV group) covers every position and writes the final output (used
+// when the context is short or the batch has many (row, group) pairs).
+extern "C" __global__ __launch_bounds__(kAttnFullWaves * kWave) void mk_op_attn_full(Params P, const Step* Sd,
+                                                                                    int layer) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sm = reinterpret_cast<float*>(smem);
+  const Step S = ld_const(Sd);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x / P.nkv, grp = blockIdx.x % P.nkv;
+  if (P.kv_f32) {
+    if (P.hd == 128) attn_split_wg<128, float, kAttnFullWaves, true>(P, S, layer, b, grp, 0, sm, wave, lane);
+    else attn_split_wg<64, float, kAttnFullWaves, true>(P, S, layer, b, grp, 0, sm, wave, lane);
+  } else {
+    if (P.hd == 128) attn_split_wg<128, uint16_t, kAttnFullWaves, true>(P, S, layer, b, grp, 0, sm, wave, lane);
+    else attn_split_wg<64, uint16_t, kAttnFullWaves, true>(P, S, layer, b, grp, 0, sm, wave, lane);
+  }
 }
 
 // Log-sum-exp merge as its own launch: one wave per (batch row, query head).

@@ -17,6 +17,11 @@ constexpr int kWorkers = kWaves - 1;  // worker waves per CU in the persistent k
 constexpr int kMaxGqa = 8;            // query heads per KV head supported
 constexpr int kMaxSplit = 4096;       // positions per split-KV attention task
 constexpr int kAttnWaves = 4;         // waves per split in the per-operator attention kernel
+#ifndef MK_XCDS
+#define MK_XCDS 8
+#endif
+constexpr int kXcds = MK_XCDS;        // accelerator complex dies (each with its own L2) of the device
+constexpr int kAttnFullWaves = 8;     // waves of the whole-context attention kernel
 constexpr int kLocalSlots = 64;       // per-CU LDS counters for aggregated event signals
 constexpr int kMaxBatch = 64;         // sequences per step
 constexpr int kMaxTasksPerWave = 64; // GEMV results a wave of a per-operator kernel holds in LDS (<= wave size:
@@ -62,31 +67,31 @@ inline constexpr int stage_layer(uint16_t key) { return (key & 0xFFF) - 1; }
 #define MK_SHAPE_QKV_R 2
 #endif
 #ifndef MK_SHAPE_QKV_D
-#define MK_SHAPE_QKV_D 8
+#define MK_SHAPE_QKV_D 4
 #endif
 #ifndef MK_SHAPE_O_R
 #define MK_SHAPE_O_R 2
 #endif
 #ifndef MK_SHAPE_O_D
-#define MK_SHAPE_O_D 8
+#define MK_SHAPE_O_D 4
 #endif
 #ifndef MK_SHAPE_GU_R
 #define MK_SHAPE_GU_R 2
 #endif
 #ifndef MK_SHAPE_GU_D
-#define MK_SHAPE_GU_D 8
+#define MK_SHAPE_GU_D 4
 #endif
 #ifndef MK_SHAPE_DOWN_R
 #define MK_SHAPE_DOWN_R 2
 #endif
 #ifndef MK_SHAPE_DOWN_D
-#define MK_SHAPE_DOWN_D 7
+#define MK_SHAPE_DOWN_D 4
 #endif
 #ifndef MK_SHAPE_LM_R
 #define MK_SHAPE_LM_R 2
 #endif
 #ifndef MK_SHAPE_LM_D
-#define MK_SHAPE_LM_D 8
+#define MK_SHAPE_LM_D 4
 #endif
 template <int TT> struct TaskShape;
 template <> struct TaskShape<1> { static constexpr int R = MK_SHAPE_QKV_R, D = MK_SHAPE_QKV_D; };    // QKV: one RoPE pair or R v rows

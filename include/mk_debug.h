@@ -56,6 +56,9 @@ typedef struct {
   uint32_t* events; /* event counters */
   int32_t n_events, n_tasks, ncu, nsplit, split;
   int32_t lds_bytes; /* dynamic LDS of the persistent kernel */
+  uint32_t exact_ops; /* per-operator mode: bit t set when operator type t runs
+                         the variant without row/column clamps (its rows fill
+                         whole tiles and its columns whole prefetch rounds) */
 } mk_debug_view;
 mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out);
 
