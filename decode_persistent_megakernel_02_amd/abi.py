@@ -92,6 +92,7 @@ SIGNATURES = {
                        ctypes.POINTER(ctypes.c_double)], _I32),
     "mk_time_ops": ([_P, ctypes.c_uint32, _I32], _I32),
     "mk_read_op_times": ([_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
+    "mk_time_op_replay": ([_P, _I32, _I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
     "mk_t_gemv": ([_P, _P, _P, _I32, _I32, _P], _I32),
     "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
@@ -103,6 +104,12 @@ SIGNATURES = {
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_persistent_megakernel_02_amd.build`")
+# PyTorch first: it loads its HIP runtime into the global symbol scope, so the
+# library's HIP calls bind to that same runtime (one set of devices, streams
+# and queues in the process).  Loaded the other way round, the library would
+# bring up a second HIP runtime next to PyTorch's, which then finds no device.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 for _name, (_args, _res) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -284,6 +291,16 @@ def mk_read_op_times(h: Handle):
     n = (ctypes.c_int32 * 9)()
     _check(lib.mk_read_op_times(h.ptr, ms, n), "mk_read_op_times")
     return {name: (ms[i], n[i]) for name, i in OP_TYPES.items() if n[i]}
+
+
+def mk_time_op_replay(h: Handle, type_name: str, reps: int):
+    """(total ms, launches) of `reps` back-to-back replays of one operator's
+    launches of a decode step (every layer)."""
+    ms = ctypes.c_double()
+    n = _I32()
+    _check(lib.mk_time_op_replay(h.ptr, OP_TYPES[type_name], reps, ctypes.byref(ms), ctypes.byref(n)),
+           "mk_time_op_replay")
+    return ms.value, n.value
 
 
 def mk_trace_op(h: Handle, type_name, layer: int):

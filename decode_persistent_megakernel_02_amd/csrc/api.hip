@@ -116,6 +116,9 @@ struct mk_handle {
   std::vector<hipEvent_t> ev_pool;  // pairs: [2i] start, [2i+1] end
   std::vector<int> ev_type;
   int ev_used = 0;
+  // back-to-back replay of one operator's launches (mk_time_op_replay)
+  int only_type = -1, replayed = 0;
+  hipEvent_t rep_ev[2] = {nullptr, nullptr};
 
   template <class T>
   mk_status alloc(T** p, int64_t count) {
@@ -134,6 +137,8 @@ struct mk_handle {
     if (step_graph) (void)hipGraphDestroy(step_graph);
     if (cap_stream) (void)hipStreamDestroy(cap_stream);
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : rep_ev)
+      if (e) (void)hipEventDestroy(e);
     for (void* p : allocs) (void)hipFree(p);
   }
 };
@@ -255,6 +260,10 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
   const Step* sp = h->d_step;
   const int bt = batch_tiles(Pc.B);
   auto launch = [&](int type, const void* fn, dim3 grid, dim3 block, void** args, size_t lds) -> mk_status {
+    if (h->only_type >= 0) {
+      if (type != h->only_type) return MK_OK;
+      ++h->replayed;
+    }
     const bool timed = timed_ok && ((h->timed_mask >> type) & 1) && 2 * (h->ev_used + 1) <= (int)h->ev_pool.size();
     if (timed) HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used], st));
     HIP_TRY(hipLaunchKernel(fn, grid, block, args, lds, st));
@@ -318,6 +327,10 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
     if (count <= 0) continue;
     const int type = g.stage_type[s];
     if (type == TT_MERGE && (fused_merge(h) || single_split(h))) continue;  // done by the attention launch
+    if (h->only_type >= 0) {
+      if (type != h->only_type) continue;
+      ++h->replayed;
+    }
     const bool timed = timed_ok && ((h->timed_mask >> type) & 1) && 2 * (h->ev_used + 1) <= (int)h->ev_pool.size();
     if (timed) HIP_TRY(hipEventRecord(h->ev_pool[2 * h->ev_used], st));
     if (type == TT_ATTN || type == TT_MERGE) {
@@ -873,6 +886,40 @@ mk_status mk_read_op_times(mk_handle* h, double* total_ms, int32_t* launches) {
   return MK_OK;
 }
 
+mk_status mk_time_op_replay(mk_handle* h, int32_t type, int32_t reps, double* total_ms, int32_t* launches) {
+  g_err.clear();
+  if (!h || !total_ms || !launches || reps < 1 || reps > 10000) return fail(MK_ERR_INVALID_ARG, "bad arguments");
+  if (h->cfg.mode != MK_MODE_PER_OP) return fail(MK_ERR_UNSUPPORTED, "operator replay needs MK_MODE_PER_OP");
+  // the LM head accumulates its argmax across launches and the argmax consumes
+  // it: replaying either would change the next step's token
+  if (type < 0 || type > TT_DOWN || (type == 0 && !h->batched))
+    return fail(MK_ERR_INVALID_ARG, "replay supports the norm (batched path), QKV, attention, merge, O, gate/up "
+                                    "and down launches");
+  // the batched path's operand planes are shared by the layers: a replayed
+  // QKV launch would append K/V computed from another layer's input
+  if (h->batched && type == TT_QKV)
+    return fail(MK_ERR_INVALID_ARG, "replay of the batched QKV launches would rewrite the KV cache");
+  if (h->length < 1) return fail(MK_ERR_STATE, "replay needs a prefilled sequence");
+  if (h->timed_mask) return fail(MK_ERR_STATE, "operator event timing is active");
+  for (hipEvent_t& e : h->rep_ev)
+    if (!e) HIP_TRY(hipEventCreate(&e));
+  HIP_TRY(hipStreamSynchronize(h->stream));
+  h->only_type = type;
+  h->replayed = 0;
+  mk_status st = MK_OK;
+  if (hipEventRecord(h->rep_ev[0], h->stream) != hipSuccess) st = fail(MK_ERR_HIP, "hipEventRecord failed");
+  for (int r = 0; r < reps && st == MK_OK; ++r) st = enqueue_ops(h, h->stream, false);
+  h->only_type = -1;
+  MK_TRY(st);
+  HIP_TRY(hipEventRecord(h->rep_ev[1], h->stream));
+  HIP_TRY(hipEventSynchronize(h->rep_ev[1]));
+  float ms = 0;
+  HIP_TRY(hipEventElapsedTime(&ms, h->rep_ev[0], h->rep_ev[1]));
+  *total_ms = ms;
+  *launches = h->replayed;
+  return MK_OK;
+}
+
 mk_status mk_trace_op(mk_handle* h, int32_t type, int32_t layer) {
   g_err.clear();
   if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
@@ -952,6 +999,10 @@ mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t 
   if (!W || !A || !Y || N < 1 || K < 8 || K % 8 || B < 1 || B > kMaxBatch)
     return fail(MK_ERR_INVALID_ARG, "bad bgemm arguments");
   const int lds = b_lds_bytes(batch_tiles(B));
+  // A device query first: as the first HIP call of a process,
+  // hipFuncSetAttribute reports that no device exists.
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
   HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_t_bgemm_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds));
   hipLaunchKernelGGL(mk_t_bgemm_kernel, dim3((N + 32 * kBgemmWaves - 1) / (32 * kBgemmWaves)),

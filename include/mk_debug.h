@@ -78,7 +78,7 @@ mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, do
  * MK_FLAG_TRACE | MK_FLAG_NO_GRAPH): from now on the waves of the GEMV
  * operator `type` (1 QKV, 4 O, 5 GU, 6 DOWN, 7 LM) of `layer` log four
  * wall-clock stamps each into the trace buffer read by mk_read_trace: entry
- * 4*w (w = block * 8 + wave) = (XCC_ID << 60 | HW_ID bits 0..27 << 32) |
+ * 4*w (w = block * 4 + wave) = (XCC_ID << 60 | HW_ID bits 0..27 << 32) |
  * start (low 32 bits), then input staged, weight stream done, epilogues done.
  * type < 0 stops logging. */
 mk_status mk_trace_op(mk_handle* h, int32_t type, int32_t layer);
@@ -92,6 +92,23 @@ mk_status mk_trace_op(mk_handle* h, int32_t type, int32_t layer);
  * (index = type), and stops timing. */
 mk_status mk_time_ops(mk_handle* h, uint32_t type_mask, int32_t max_launches);
 mk_status mk_read_op_times(mk_handle* h, double* total_ms, int32_t* launches);
+
+/* Back-to-back replay (MK_MODE_PER_OP, after at least one prefill): enqueues
+ * only the launches of operator `type` (0 = the RMSNorm launches of the
+ * batched path, 1 QKV, 2 ATTN, 3 MERGE, 4 O, 5 GU, 6 DOWN) of one decode step,
+ * for every layer, `reps` times in a row on the handle's stream between two
+ * HIP events, with the arguments of the last step.  Cycling through all
+ * layers keeps the weights from being served out of the last-level cache.
+ * The sequence state is unchanged: batch 1 stages each launch's input from
+ * per-layer buffers, so a replay rewrites the same outputs from the same
+ * inputs; the batched path shares its operand planes across layers, so its
+ * replays read the last-written planes (same shapes and bytes) and write only
+ * buffers that the next step rewrites before reading -- which is why its QKV
+ * launches (they append to the KV cache) are refused.  The LM head and argmax
+ * are refused on both paths (their argmax state carries into the next step).
+ * Waits for the stream; *total_ms = elapsed time, *launches = kernels
+ * launched. */
+mk_status mk_time_op_replay(mk_handle* h, int32_t type, int32_t reps, double* total_ms, int32_t* launches);
 
 /* ---- single task bodies on explicit buffers (asynchronous on `stream`) ----- */
 /* y[N] = W[N,K] x[K]; W bf16 row-major, x/y fp32; K a multiple of 8. */

@@ -227,6 +227,38 @@ def test_batched_graph_replay_equals_eager(abi):
         assert np.array_equal(res[0][0], r[0]) and np.array_equal(res[0][1], r[1])
 
 
+def test_batched_operator_replay_leaves_the_batch_unchanged(abi):
+    """Replaying the norm, attention and projection launches (with their
+    split-K finishing launches) between steps changes no later result bit; the
+    QKV launches (they append to the KV cache), LM head and argmax are refused."""
+    from decode_persistent_megakernel_02_amd import runtime
+    shape, B, P = MINI, 6, 5
+    w = gen.gen_weights(shape, 8, True)
+    dw = runtime.upload_weights(w)
+    prompt = torch.from_numpy(gen.tokens(8, presets.TID_PROMPT, 0, B * P, shape.vocab).reshape(B, P)).cuda()
+    res = []
+    for replay in (False, True):
+        h = runtime.create(shape, dw, P + 8, B, abi.MK_MODE_PER_OP, 0, attn_split=4, kv_fp32=False)
+        out = torch.zeros(B, dtype=torch.int32, device="cuda")
+        lg = torch.zeros(B, shape.vocab, dtype=torch.float32, device="cuda")
+        abi.mk_prefill(h, prompt, out, lg)
+        steps = []
+        for _ in range(6):
+            if replay:
+                for name in ("norm", "attn", "merge", "o", "gu", "down"):
+                    ms, n = abi.mk_time_op_replay(h, name, 2)
+                    assert n >= 2 * shape.n_layers and ms > 0.0, (name, n, ms)
+                for name in ("qkv", "lm", "argmax"):  # KV append / argmax state
+                    with pytest.raises(abi.MkError):
+                        abi.mk_time_op_replay(h, name, 1)
+            abi.mk_decode_step(h, out, out, lg)
+            abi.mk_synchronize(h)
+            steps.append(lg.cpu().numpy().copy())
+        res.append(np.stack(steps))
+        abi.mk_destroy(h)
+    assert np.array_equal(res[0], res[1])
+
+
 def layer_subset(shape, n_layers):
     from dataclasses import replace
     return replace(shape, name=f"{shape.name}_{n_layers}l", n_layers=n_layers)

@@ -219,3 +219,27 @@ def test_fused_merge_equals_separate_merge_bitwise(abi):
             res.append(case.step(t)[0])
         runs.append(np.stack(res))
     assert np.array_equal(runs[0], runs[1])
+
+
+def test_operator_replay_leaves_the_sequence_unchanged(abi):
+    """Back-to-back replays of one operator's launches (the bench's kernel
+    timing) rewrite the same outputs: the following steps are bit-identical to
+    a run without replays.  The LM head and argmax are refused."""
+    shape = MINI_G8
+    w = gen.gen_weights(shape, 12, True)
+    prompt = gen.tokens(12, 3, 0, 9, shape.vocab)
+    runs = []
+    for replay in (False, True):
+        case = Case(shape, 40, PER_OP, attn_split=8, weights=w)
+        res = [case.prefill(prompt)[0]]
+        for t in (4, 200, 8, 21, 250, 6, 13):
+            if replay:
+                for name in ("qkv", "attn", "merge", "o", "gu", "down"):
+                    ms, n = abi.mk_time_op_replay(case.h, name, 3)
+                    assert n == 3 * shape.n_layers and ms > 0.0, (name, n, ms)
+                for name in ("lm", "argmax", "norm"):
+                    with pytest.raises(abi.MkError):
+                        abi.mk_time_op_replay(case.h, name, 1)
+            res.append(case.step(t)[0])
+        runs.append(np.stack(res))
+    assert np.array_equal(runs[0], runs[1])
