@@ -84,6 +84,25 @@ int64_t task_weight_bytes(const GraphConfig& c, const Task& t) {
   }
 }
 
+// The per-operator kernels derive their tasks arithmetically
+// (op_task_fields); they must be the tasks the graph builder emitted.
+std::string check_op_tasks(const Graph& g) {
+  const GraphConfig& c = g.cfg;
+  for (size_t s = 0; s + 1 < g.stage_begin.size(); ++s) {
+    const int type = g.stage_type[s], b0 = g.stage_begin[s], n = g.stage_begin[s + 1] - b0;
+    if (type != TT_QKV && type != TT_O && type != TT_GU && type != TT_DOWN && type != TT_LM) continue;
+    for (int i = 0; i < n; ++i) {
+      const Task& t = g.tasks[b0 + i];
+      const Task d = op_task_fields(type, t.layer, i, c.H, c.nq, c.nkv, c.hd, c.F, c.V, c.L);
+      if (d.type != t.type || d.layer != t.layer || d.stage != t.stage || d.batch != t.batch || d.a0 != t.a0 ||
+          d.a1 != t.a1 || d.a2 != t.a2 || d.a3 != t.a3)
+        return "operator task formula differs from the graph at stage " + std::to_string(s) + ", task " +
+               std::to_string(i);
+    }
+  }
+  return "";
+}
+
 }  // namespace
 
 struct mk_handle {
@@ -93,7 +112,6 @@ struct mk_handle {
   Graph graph;
   Params P{};
   std::vector<void*> allocs;
-  Task* d_stage_tasks = nullptr;
   int page_floats = 0, scratch_floats = 0, lds_mega = 0;
   int op_page[9] = {0}, op_lds[9] = {0}, op_grid_cap[9] = {0}, op_sf[9] = {0};  // per task type
   bool op_exact[9] = {false};
@@ -116,6 +134,7 @@ struct mk_handle {
   std::vector<hipEvent_t> ev_pool;  // pairs: [2i] start, [2i+1] end
   std::vector<int> ev_type;
   int ev_used = 0;
+  std::vector<const void*> host_w;      // [9][L] layer pointer tables (as in P), host copy
   // back-to-back replay of one operator's launches (mk_time_op_replay)
   int only_type = -1, replayed = 0;
   hipEvent_t rep_ev[2] = {nullptr, nullptr};
@@ -166,8 +185,6 @@ const void* op_kernel(int type, bool exact = false) {
   }
   switch (type) {
     case TT_QKV: return reinterpret_cast<const void*>(&mk_op_qkv);
-    case TT_ATTN: return reinterpret_cast<const void*>(&mk_op_attn);
-    case TT_MERGE: return reinterpret_cast<const void*>(&mk_op_merge);
     case TT_O: return reinterpret_cast<const void*>(&mk_op_o);
     case TT_GU: return reinterpret_cast<const void*>(&mk_op_gu);
     case TT_DOWN: return reinterpret_cast<const void*>(&mk_op_down);
@@ -316,6 +333,24 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
   return launch(TT_ARGMAX, reinterpret_cast<const void*>(&mk_b_argmax), dim3(1), dim3(kMaxBatch), args, 0);
 }
 
+// Launch arguments of the single-sequence operator `type` of `layer`.
+OpArgs op_args(const mk_handle* h, int type, int layer, int count) {
+  const int L = h->P.L;
+  auto w = [&](int table) { return static_cast<const uint16_t*>(h->host_w[(size_t)table * L + layer]); };
+  OpArgs A{};
+  A.layer = layer;
+  A.count = count;
+  switch (type) {  // tables: attn_norm, wq, wk, wv, wo, ffn_norm, w_gate, w_up, w_down
+    case TT_QKV: A.w[0] = w(1); A.w[1] = w(2); A.w[2] = w(3); A.gain = w(0); break;
+    case TT_O: A.w[0] = w(4); break;
+    case TT_GU: A.w[0] = w(6); A.w[1] = w(7); A.gain = w(5); break;
+    case TT_DOWN: A.w[0] = w(8); break;
+    case TT_LM: A.w[0] = h->P.tied ? h->P.embed : h->P.lm_head; A.gain = h->P.final_norm; break;
+    default: break;
+  }
+  return A;
+}
+
 // Enqueue the operator launches of one step (kernel-per-operator mode) on `st`.
 mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
   if (h->batched) return enqueue_batched(h, st, timed_ok);
@@ -350,11 +385,10 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
       // a GEMV wave holds at most kMaxTasksPerWave results: keep the average at half of that
       const int min_grid = (count + kWaves * kMaxTasksPerWave / 2 - 1) / (kWaves * kMaxTasksPerWave / 2);
       const int grid = std::max(min_grid, std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]));
-      const Task* tasks = h->d_stage_tasks + b0;
+      OpArgs A = op_args(h, type, g.tasks[b0].layer, count);
       int opf = h->op_page[type];
-      int cnt = count;
       int osf = h->op_sf[type];
-      void* args[] = {&Pc, &sp, &tasks, &cnt, &opf, &osf};
+      void* args[] = {&Pc, &sp, &A, &opf, &osf};
       HIP_TRY(hipLaunchKernel(op_kernel(type, h->op_exact[type]), dim3(grid), dim3(kWaves * kWave), args,
                               (size_t)h->op_lds[type], st));
     }
@@ -498,6 +532,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   for (int i = 0; i < 9; ++i)
     for (int l = 0; l < L; ++l) hp[(size_t)i * L + l] = lists[i][l];
   HIP_TRY(hipMemcpy(d_ptrs, hp.data(), hp.size() * sizeof(void*), hipMemcpyHostToDevice));
+  h->host_w = hp;
   P.attn_norm = d_ptrs + 0 * L; P.wq = d_ptrs + 1 * L; P.wk = d_ptrs + 2 * L; P.wv = d_ptrs + 3 * L;
   P.wo = d_ptrs + 4 * L; P.ffn_norm = d_ptrs + 5 * L; P.w_gate = d_ptrs + 6 * L; P.w_up = d_ptrs + 7 * L;
   P.w_down = d_ptrs + 8 * L;
@@ -574,10 +609,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   int32_t* d_qoff = nullptr;
   MK_TRY(h->alloc(&d_flat, (int64_t)g.flat.size()));
   MK_TRY(h->alloc(&d_qoff, (int64_t)g.queue_off.size()));
-  MK_TRY(h->alloc(&h->d_stage_tasks, (int64_t)g.tasks.size()));
   HIP_TRY(hipMemcpy(d_flat, g.flat.data(), g.flat.size() * sizeof(Task), hipMemcpyHostToDevice));
   HIP_TRY(hipMemcpy(d_qoff, g.queue_off.data(), g.queue_off.size() * 4, hipMemcpyHostToDevice));
-  HIP_TRY(hipMemcpy(h->d_stage_tasks, g.tasks.data(), g.tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
   P.tasks = d_flat;
   P.queue_off = d_qoff;
   MK_TRY(h->alloc(&P.events, (int64_t)g.event_count.size()));
@@ -597,7 +630,12 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   h->page_floats = round_up(std::max({H, nq * hd, F}), 8);
   h->scratch_floats = round_up(G * hd + G * kWave, 4);
   h->lds_mega = (int)sizeof(Lds) + 2 * h->page_floats * 4 + kWorkers * h->scratch_floats * 4;
+  if (!h->batched) {
+    const std::string e = check_op_tasks(h->graph);
+    if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "internal: " + e);
+  }
   for (int t = TT_QKV; t <= TT_ARGMAX && !h->batched; ++t) {  // single-sequence operator kernels
+    if (t == TT_ATTN || t == TT_MERGE) continue;  // launched by their own kernels
     int pfl = 0;
     if (t == TT_QKV || t == TT_GU || t == TT_LM) pfl = H;
     else if (t == TT_O) pfl = nq * hd;
@@ -611,7 +649,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
                     : t == TT_LM ? TaskShape<TT_LM>::D : 0;
     h->op_exact[t] = rows > 0 && pfl % 512 == 0 && (pfl / 512) % depth == 0;
     // per-wave scratch: attention state, or the results of the wave's GEMV tasks
-    h->op_sf[t] = t == TT_ATTN ? h->scratch_floats : kMaxTasksPerWave * (rows + 1);  // results + task ids
+    h->op_sf[t] = kMaxTasksPerWave * (rows + 1);  // results + task ids
     h->op_lds[t] = (int)sizeof(Lds) + h->op_page[t] * 4 + kWaves * h->op_sf[t] * 4;
     if (h->op_lds[t] > max_lds)
       return fail(MK_ERR_UNSUPPORTED, "operator LDS need exceeds " + std::to_string(max_lds));
@@ -776,6 +814,8 @@ mk_status mk_graph_inspect(const mk_config* cfg, int32_t ncu, mk_graph_info* out
   if (!e.empty()) return fail(cfg->max_batch > 1 ? MK_ERR_UNSUPPORTED : MK_ERR_INVALID_ARG, e);
   e = validate_graph(g);
   if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "graph validation: " + e);
+  e = check_op_tasks(g);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "internal: " + e);
   out->n_tasks = (int32_t)g.tasks.size();
   out->n_events = (int32_t)g.event_count.size();
   out->n_stages = (int32_t)g.stage_begin.size() - 1;

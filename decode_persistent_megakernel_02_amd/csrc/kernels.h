@@ -10,10 +10,8 @@ extern "C" __global__ void mk_op_attn_split(Params P, const Step* S, int layer, 
 extern "C" __global__ void mk_op_attn_merge(Params P, const Step* S, int layer);
 extern "C" __global__ void mk_op_attn_full(Params P, const Step* S, int layer);
 extern "C" __global__ void mk_set_step(Step* dst, Step s);
-#define MK_OP_DECL(name) extern "C" __global__ void name(Params P, const Step* S, const Task* tasks, int count, int pf, int sf);
+#define MK_OP_DECL(name) extern "C" __global__ void name(Params P, const Step* S, OpArgs A, int pf, int sf);
 MK_OP_DECL(mk_op_qkv)
-MK_OP_DECL(mk_op_attn)
-MK_OP_DECL(mk_op_merge)
 MK_OP_DECL(mk_op_o)
 MK_OP_DECL(mk_op_gu)
 MK_OP_DECL(mk_op_down)

@@ -28,13 +28,24 @@ struct StageSrc {
   int n;
 };
 
-__device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, uint16_t key, int b) {
+// The RMSNorm gain of a staged input (null: copied without normalising),
+// from the per-layer tables.
+__device__ __forceinline__ const uint16_t* stage_gain(const Params& P, uint16_t key) {
+  switch (stage_kind(key)) {
+    case SK_ATTN_NORM: return ld_const(P.attn_norm + stage_layer(key));
+    case SK_FFN_NORM: return ld_const(P.ffn_norm + stage_layer(key));
+    case SK_FINAL_NORM: return P.final_norm;
+    default: return nullptr;
+  }
+}
+
+__device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, uint16_t key, int b,
+                                              const uint16_t* gain) {
   const int kind = stage_kind(key), l = stage_layer(key);
   const int64_t H = P.H;
-  StageSrc r{nullptr, nullptr, nullptr, P.H};
+  StageSrc r{nullptr, nullptr, gain, P.H};
   switch (kind) {
     case SK_ATTN_NORM:
-      r.gamma = ld_const(P.attn_norm + l);
       if (l == 0) r.bf = P.embed + (int64_t)token_of(P, S, b) * H;
       else r.f32 = P.xs + ((int64_t)l * P.B + b) * H;
       break;
@@ -43,7 +54,6 @@ __device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, ui
       r.f32 = P.attn_out + ((int64_t)l * P.B + b) * r.n;
       break;
     case SK_FFN_NORM:
-      r.gamma = ld_const(P.ffn_norm + l);
       r.f32 = P.xmid + ((int64_t)l * P.B + b) * H;
       break;
     case SK_H:
@@ -51,7 +61,6 @@ __device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, ui
       r.f32 = P.h + ((int64_t)l * P.B + b) * P.F;
       break;
     default:
-      r.gamma = P.final_norm;
       r.f32 = P.xs + ((int64_t)P.L * P.B + b) * H;
       break;
   }
@@ -60,7 +69,7 @@ __device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, ui
 
 // One wave stages the vector (persistent kernel's scheduler wave).
 __device__ void stage_input(const Params& P, const Step& S, uint16_t key, int b, float* page, int lane) {
-  const StageSrc r = stage_src(P, S, key, b);
+  const StageSrc r = stage_src(P, S, key, b, stage_gain(P, key));
   stage_vector(page, r.f32, r.bf, r.n, r.gamma, P.eps, lane);
 }
 
@@ -167,10 +176,12 @@ __device__ __forceinline__ float pick(const float (&y)[R], int i) {
 
 // GEMV-type task (QKV, O, GU, DOWN, LM) with its operator fixed at compile
 // time: where its rows are ...
+// Rows of task d in the matrices W0 (QKV: the task's own matrix; GU: gate)
+// and W1 (GU: up).
 template <int TT>
-__device__ __forceinline__ void gemv_setup(const Params& P, const Task& d, GemvRows<TaskShape<TT>::R>& g) {
+__device__ __forceinline__ void gemv_setup_w(const Params& P, const Task& d, const uint16_t* W0, const uint16_t* W1,
+                                             GemvRows<TaskShape<TT>::R>& g) {
   constexpr int R = TaskShape<TT>::R;
-  const int l = d.layer;
   int K = P.H;
   if constexpr (TT == TT_O) K = P.nq * P.hd;
   else if constexpr (TT == TT_DOWN) K = P.F;
@@ -178,7 +189,7 @@ __device__ __forceinline__ void gemv_setup(const Params& P, const Task& d, GemvR
   g.stride = K / 8;
   g.split = R;
   if constexpr (TT == TT_QKV) {
-    const uint16_t* W = d.a0 == 0 ? ld_const(P.wq + l) : d.a0 == 1 ? ld_const(P.wk + l) : ld_const(P.wv + l);
+    const uint16_t* W = W0;
     g.base0 = reinterpret_cast<const v4u*>(W + (int64_t)d.a1 * K);
     if (d.a3) {  // one RoPE pair: rows a1 and a1 + hd/2
       g.base1 = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + d.a3) * K);
@@ -189,20 +200,44 @@ __device__ __forceinline__ void gemv_setup(const Params& P, const Task& d, GemvR
       g.mask = (1u << d.a2) - 1;
     }
   } else if constexpr (TT == TT_GU) {  // rows: gate a1.., then up a1..
-    g.base0 = reinterpret_cast<const v4u*>(ld_const(P.w_gate + l) + (int64_t)d.a1 * K);
-    g.base1 = reinterpret_cast<const v4u*>(ld_const(P.w_up + l) + (int64_t)d.a1 * K);
+    g.base0 = reinterpret_cast<const v4u*>(W0 + (int64_t)d.a1 * K);
+    g.base1 = reinterpret_cast<const v4u*>(W1 + (int64_t)d.a1 * K);
     g.split = R / 2;
     const uint32_t half = (1u << d.a2) - 1;
     g.mask = half | (half << (R / 2));
   } else {
-    const uint16_t* W;
-    if constexpr (TT == TT_O) W = ld_const(P.wo + l);
-    else if constexpr (TT == TT_DOWN) W = ld_const(P.w_down + l);
-    else W = P.tied ? P.embed : P.lm_head;
-    g.base0 = reinterpret_cast<const v4u*>(W + (int64_t)d.a1 * K);
+    g.base0 = reinterpret_cast<const v4u*>(W0 + (int64_t)d.a1 * K);
     g.base1 = g.base0;
     g.mask = (1u << d.a2) - 1;
   }
+}
+
+// ... with the matrices taken from the per-layer tables (persistent kernel) ...
+template <int TT>
+__device__ __forceinline__ void gemv_setup(const Params& P, const Task& d, GemvRows<TaskShape<TT>::R>& g) {
+  const int l = d.layer;
+  const uint16_t *W0, *W1 = nullptr;
+  if constexpr (TT == TT_QKV) W0 = d.a0 == 0 ? ld_const(P.wq + l) : d.a0 == 1 ? ld_const(P.wk + l) : ld_const(P.wv + l);
+  else if constexpr (TT == TT_GU) { W0 = ld_const(P.w_gate + l); W1 = ld_const(P.w_up + l); }
+  else if constexpr (TT == TT_O) W0 = ld_const(P.wo + l);
+  else if constexpr (TT == TT_DOWN) W0 = ld_const(P.w_down + l);
+  else W0 = P.tied ? P.embed : P.lm_head;
+  gemv_setup_w<TT>(P, d, W0, W1, g);
+}
+
+// ... or from the launch arguments (per-operator kernels).
+template <int TT>
+__device__ __forceinline__ void gemv_setup(const Params& P, const OpArgs& A, const Task& d,
+                                           GemvRows<TaskShape<TT>::R>& g) {
+  const uint16_t* W0 = A.w[0];
+  if constexpr (TT == TT_QKV) W0 = d.a0 == 0 ? A.w[0] : d.a0 == 1 ? A.w[1] : A.w[2];
+  gemv_setup_w<TT>(P, d, W0, A.w[1], g);
+}
+
+// Task t of a per-operator launch.
+template <int TT>
+__device__ __forceinline__ Task op_task(const Params& P, const OpArgs& A, int t) {
+  return op_task_fields(TT, A.layer, t, P.H, P.nq, P.nkv, P.hd, P.F, P.V, P.L);
 }
 
 // ... and what it does with the R dot products y (uniform across the wave).
@@ -321,26 +356,28 @@ __device__ __forceinline__ int gemv_next(uint32_t* pool, int j, int count, int l
 }
 
 template <int TT, bool EXACT, class Wait>
-__device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, int count, int i0, int lane, const float* page, float* res, int* ids, uint32_t* pool,
-                                           Wait wait) {
+__device__ __forceinline__ int gemv_stream(const Params& P, const OpArgs& A, int count, int i0, int lane,
+                                           const float* page, float* res, int* ids, uint32_t* pool, Wait wait) {
   constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
   if (i0 >= count) return 0;
   v4u bufA[D][R], bufB[D][R];
   GemvRows<R> gA, gB;
-  gemv_setup<TT>(P, load_task(tasks, i0), gA);
+  // Both buffers are filled before the wait for the staged input, so two
+  // tasks' weights stream in while the input vector is loaded and normalised.
+  gemv_setup<TT>(P, A, op_task<TT>(P, A, i0), gA);
   gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
-  wait();
   float y[R];
-  int a = i0, b, j = 0;
-  for (;;) {
-    b = gemv_next(pool, j, count, lane);
-    if (b >= count) {
-      gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
-      gemv_put<TT>(res, ids, j++, a, y, lane);
-      break;
-    }
-    gemv_setup<TT>(P, load_task(tasks, b), gB);
-    gemv_prefetch<R, D, EXACT>(bufB, gB, lane);
+  int a = i0, b = gemv_next(pool, 0, count, lane), j = 0;
+  if (b >= count) {
+    wait();
+    gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
+    gemv_put<TT>(res, ids, j++, a, y, lane);
+    return j;
+  }
+  gemv_setup<TT>(P, A, op_task<TT>(P, A, b), gB);
+  gemv_prefetch<R, D, EXACT>(bufB, gB, lane);
+  wait();
+  for (;;) {  // tasks a (buffer A) and b (buffer B) in flight
     gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
     gemv_put<TT>(res, ids, j++, a, y, lane);
     a = gemv_next(pool, j, count, lane);
@@ -349,10 +386,18 @@ __device__ __forceinline__ int gemv_stream(const Params& P, const Task* tasks, i
       gemv_put<TT>(res, ids, j++, b, y, lane);
       break;
     }
-    gemv_setup<TT>(P, load_task(tasks, a), gA);
+    gemv_setup<TT>(P, A, op_task<TT>(P, A, a), gA);
     gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
     gemv_run<R, D, EXACT>(bufB, gB, page, lane, y);
     gemv_put<TT>(res, ids, j++, b, y, lane);
+    b = gemv_next(pool, j, count, lane);
+    if (b >= count) {
+      gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
+      gemv_put<TT>(res, ids, j++, a, y, lane);
+      break;
+    }
+    gemv_setup<TT>(P, A, op_task<TT>(P, A, b), gB);
+    gemv_prefetch<R, D, EXACT>(bufB, gB, lane);
   }
   return j;
 }
@@ -423,13 +468,13 @@ __device__ __forceinline__ void epilogue_lane(const Params& P, const Step& S, co
 // The epilogues of a wave's n (<= 64) streamed tasks, from their results in
 // res and their task indices in ids: lane j finishes task j.
 template <int TT>
-__device__ __forceinline__ void gemv_finish(const Params& P, const Step& S, const Task* tasks, int n, int i0,
-                                            int lane, const float* res, const int* ids, Lds* L) {
+__device__ __forceinline__ void gemv_finish(const Params& P, const Step& S, const OpArgs& A, int n, int lane,
+                                            const float* res, const int* ids, Lds* L) {
   constexpr int R = TaskShape<TT>::R;
   __builtin_amdgcn_wave_barrier();
   unsigned long long best = 0;
   if (lane < n) {
-    const Task d = tasks[ids[lane]];
+    const Task d = op_task<TT>(P, A, ids[lane]);
     float y[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) y[r] = res[lane * R + r];
@@ -437,8 +482,7 @@ __device__ __forceinline__ void gemv_finish(const Params& P, const Step& S, cons
   }
   if constexpr (TT == TT_LM) {
     best = wave_max_u64(best);
-    if (lane == 0 && n > 0) __hip_atomic_fetch_max(&L->lm_best[load_task(tasks, i0).batch], best, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0 && n > 0) __hip_atomic_fetch_max(&L->lm_best[0], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
@@ -690,19 +734,19 @@ extern "C" __global__ __launch_bounds__(kWaves * kWave, 1) void mk_persistent(Pa
 // input vector (with its RMSNorm) into LDS once; every wave then takes tasks
 // in a workgroup-strided loop.
 template <int TT, bool EXACT>
-__device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const Task* tasks, int count, int page_floats,
-                        int scratch_floats) {
+__device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const OpArgs& A, int page_floats,
+                                        int scratch_floats) {
+  const int count = A.count;
   extern __shared__ __align__(16) unsigned char smem[];
   Lds* L = reinterpret_cast<Lds*>(smem);
   float* page = reinterpret_cast<float*>(smem + sizeof(Lds));
   float* scr = page + page_floats;
   const Step S = ld_const(Sd);
-  // wave index made explicitly uniform: task descriptors then load through the
-  // scalar cache and never queue behind the weight stream
+  // wave index made explicitly uniform: task fields are then scalar values
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
   if (threadIdx.x == 0) L->ticket = kWaves;  // task pool: the first kWaves slots are the waves' own
-  const Task first = load_task(tasks, 0);
+  const Task first = op_task<TT>(P, A, 0);
   // Every wave stages its slice of the input vector and passes the staging
   // barriers exactly once: the loads are issued first, then (in gemv_stream)
   // the first task's weight prefetch, then wait() finishes the staging -- or
@@ -711,7 +755,7 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
   StageSrc src{};
   StageRegs<SU> st;
   if (first.stage) {
-    src = stage_src(P, S, first.stage, first.batch);
+    src = stage_src(P, S, first.stage, first.batch, A.gain);
     stage_issue<SU>(src, wave, lane, st);
   }
   bool staged = false;
@@ -738,10 +782,10 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
       if (tr && !t1) t1 = clock_now();
       return r;
     };
-    const int n = gemv_stream<TT, EXACT>(P, tasks, count, i0, lane, page, res, ids, &L->ticket, wait_tr);
+    const int n = gemv_stream<TT, EXACT>(P, A, count, i0, lane, page, res, ids, &L->ticket, wait_tr);
     const uint64_t t2 = tr ? clock_now() : 0;
     wait();
-    gemv_finish<TT>(P, S, tasks, n, i0, lane, res, ids, L);
+    gemv_finish<TT>(P, S, A, n, lane, res, ids, L);
     if (tr && lane == 0) {
       const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID: wave, SIMD, CU, SE
       const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // XCC_ID
@@ -752,10 +796,8 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
       o[3] = clock_now();
     }
   } else {
-    for (int i = blockIdx.x * kWaves + wave; i < count; i += gridDim.x * kWaves) {
-      const Task d = tasks[i];
-      exec_typed<TT>(P, S, d, lane, first.stage ? page : nullptr, scr + wave * scratch_floats, L, wait);
-    }
+    static_assert(TT == TT_ARGMAX, "per-operator kernels: GEMV operators and the argmax");
+    if (blockIdx.x == 0 && wave == 0) exec_typed<TT>(P, S, first, lane, nullptr, scr, L, wait);
   }
   wait();
   if constexpr (TT == TT_LM) {
@@ -768,14 +810,12 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const T
 
 // Each GEMV operator has a generic kernel and an _x kernel for K a multiple of
 // 512 whose chunk count is a multiple of D (no clamped loads).
-#define MK_OP_KERNEL(name, TT, EXACT)                                                                       \
-  extern "C" __global__ __launch_bounds__(kWaves * kWave) void name(Params P, const Step* S, const Task* tasks, \
-                                                                      int count, int pf, int sf) {        \
-    op_body<TT, EXACT>(P, S, tasks, count, pf, sf);                                                         \
+#define MK_OP_KERNEL(name, TT, EXACT)                                                                      \
+  extern "C" __global__ __launch_bounds__(kWaves * kWave) void name(Params P, const Step* S, OpArgs A, int pf, \
+                                                                      int sf) {                            \
+    op_body<TT, EXACT>(P, S, A, pf, sf);                                                                   \
   }
 MK_OP_KERNEL(mk_op_qkv, TT_QKV, false)
-MK_OP_KERNEL(mk_op_attn, TT_ATTN, false)
-MK_OP_KERNEL(mk_op_merge, TT_MERGE, false)
 MK_OP_KERNEL(mk_op_o, TT_O, false)
 MK_OP_KERNEL(mk_op_gu, TT_GU, false)
 MK_OP_KERNEL(mk_op_down, TT_DOWN, false)

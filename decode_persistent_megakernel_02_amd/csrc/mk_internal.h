@@ -126,6 +126,65 @@ struct alignas(16) Task {
 };
 static_assert(sizeof(Task) == 48, "Task layout");
 
+// Launch arguments of a single-sequence GEMV operator kernel: the layer's
+// weight matrices (QKV: q, k, v; GU: gate, up; O, DOWN, LM: w[0]) and the
+// operator's task count.  The kernel derives task t from t itself
+// (op_task_fields), so starting a weight stream takes no table lookups.
+struct OpArgs {
+  const uint16_t* w[3];
+  const uint16_t* gain;  // RMSNorm gain of the staged input, null if it is not normalised
+  int32_t layer;
+  int32_t count;
+};
+
+#if defined(__HIPCC__)
+#define MK_HD __host__ __device__
+#else
+#define MK_HD
+#endif
+
+// Task t of the single-sequence operator `type` (QKV, O, GU, DOWN, LM) of
+// `layer`, in the order the graph builder emits them: QKV = the q RoPE pairs
+// (head-major, pair i = rows i and i + hd/2), then the k pairs, then the v
+// rows in runs of kRowsQkv; the others = runs of their row count.  Fields
+// other than type, layer, stage, batch and a0..a3 are left zero.
+MK_HD inline Task op_task_fields(int type, int layer, int t, int H, int nq, int nkv, int hd, int F, int V, int L) {
+  Task d{};
+  d.type = (uint8_t)type;
+  d.page = kNone8;
+  d.layer = (uint16_t)layer;
+  d.in_event = kNone16;
+  d.out_event = kNone16;
+  d.batch = 0;
+  auto rows = [](int t, int per, int n, Task& d) {
+    d.a1 = t * per;
+    d.a2 = n - d.a1 < per ? n - d.a1 : per;
+  };
+  switch (type) {
+    case TT_QKV: {
+      d.stage = stage_key(SK_ATTN_NORM, layer);
+      const int half = hd / 2, pq = nq * half, pk = nkv * half;
+      if (t < pq + pk) {
+        const int u = t < pq ? t : t - pq;
+        d.a0 = t < pq ? 0 : 1;
+        d.a1 = (u / half) * hd + u % half;
+        d.a2 = 2;
+        d.a3 = half;
+      } else {
+        d.a0 = 2;
+        rows(t - pq - pk, kRowsQkv, nkv * hd, d);
+      }
+      break;
+    }
+    case TT_O: d.stage = stage_key(SK_O_IN, layer); rows(t, kRowsO, H, d); break;
+    case TT_GU: d.stage = stage_key(SK_FFN_NORM, layer); rows(t, kRowsGuPerMatrix, F, d); break;
+    case TT_DOWN: d.stage = stage_key(SK_H, layer); rows(t, kRowsDown, H, d); break;
+    case TT_LM: d.layer = (uint16_t)L; d.stage = stage_key(SK_FINAL_NORM, L); rows(t, kRowsLm, V, d); break;
+    default: d.layer = (uint16_t)L; break;
+  }
+  return d;
+}
+
 // Device-visible description of a handle: shapes, weights, buffers, tables.
 struct Params {
   // shape
