@@ -167,9 +167,14 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB five times (the known-size reference "
                          "for scaling hardware byte counters) and exit")
+    ap.add_argument("--attn-split", type=int, default=0, metavar="POSITIONS",
+                    help="positions per split-KV attention workgroup (0: the library's choice)")
     ap.add_argument("--counters", type=int, default=0, metavar="STEPS",
                     help="only run prefill and STEPS eager decode steps (no graph, no timing) so that a "
                          "hardware-counter profiler sees each launch, and exit")
+    ap.add_argument("--counters-prompt", type=int, default=0, metavar="TOKENS",
+                    help="with --counters: use only the first TOKENS prompt positions (a short prefill, so a "
+                         "kernel trace stays small; attention then sees a shorter context)")
     args = ap.parse_args()
     if args.copy_probe:
         import torch
@@ -218,8 +223,10 @@ def main():
     kv_fp32 = B == 1
     flags = abi.MK_FLAG_FUSED_MERGE if args.fused_merge else 0
     if args.counters:
-        h = runtime.create(shape, dw, wl.prompt_len + args.counters + 1, B, abi.MK_MODE_PER_OP,
-                           flags | abi.MK_FLAG_NO_GRAPH, kv_fp32=kv_fp32)
+        if args.counters_prompt:
+            prompt_t = prompt_t[:, :args.counters_prompt].contiguous()
+        h = runtime.create(shape, dw, prompt_t.shape[1] + args.counters + 1, B, abi.MK_MODE_PER_OP,
+                           flags | abi.MK_FLAG_NO_GRAPH, attn_split=args.attn_split, kv_fp32=kv_fp32)
         toks = torch.zeros(args.counters + 1, B, dtype=torch.int32, device="cuda")
         abi.mk_prefill(h, prompt_t, toks[0])
         for s in range(args.counters):
@@ -229,7 +236,8 @@ def main():
         abi.mk_destroy(h)
         print(json.dumps({"counter_pass_steps": args.counters, "workload": wl.name}))
         return
-    h = runtime.create(shape, dw, max_seq + 64, B, abi.MK_MODE_PER_OP, flags, kv_fp32=kv_fp32)
+    h = runtime.create(shape, dw, max_seq + 64, B, abi.MK_MODE_PER_OP, flags, attn_split=args.attn_split,
+                       kv_fp32=kv_fp32)
     total, eager_total, (gu_ms, gu_n), same_tokens, breakdown = time_decode(abi, h, prompt_t, steps, warmup, shape,
                                                                              torch, log)
     gu_exact = bool(abi.mk_get_debug_view(h).exact_ops & (1 << abi.TASK_TYPES["gu"]))
@@ -287,6 +295,7 @@ def main():
                    "batch": B, "prompt_len": wl.prompt_len, "decode_steps": steps,
                    "mode": "per_op (HIP graph per step)" + (", fused merge" if args.fused_merge else ""),
                    "kv_cache": "fp32" if kv_fp32 else "bf16",
+                   "attn_split": args.attn_split or "library default",
                    "parallelism": "none (1 GPU)"},
         "tokens_per_s": 1000.0 * B / ms,
         "achieved_gbps": alg_bytes / (ms * 1e-3) / 1e9,

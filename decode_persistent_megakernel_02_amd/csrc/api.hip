@@ -217,6 +217,33 @@ bool fused_merge(const mk_handle* h) { return (h->cfg.flags & MK_FLAG_FUSED_MERG
 // per layer (8 CUs busy), and at the 70B shape, 64 sequences, 100 against 73.
 bool single_split(const mk_handle* h) { return h->P.nsplit == 1; }
 
+// Attention kernels by cache element type and query heads per KV group
+// (compile-time group sizes 1, 2, 4, 8; other sizes use the run-time variant).
+const void* attn_split_kernel(bool f32, int G) {
+#define MK_PICK(KN)                                                                    \
+  switch (G) {                                                                         \
+    case 1: return reinterpret_cast<const void*>(&mk_op_attn_split_##KN##_g1);        \
+    case 2: return reinterpret_cast<const void*>(&mk_op_attn_split_##KN##_g2);        \
+    case 4: return reinterpret_cast<const void*>(&mk_op_attn_split_##KN##_g4);        \
+    case 8: return reinterpret_cast<const void*>(&mk_op_attn_split_##KN##_g8);        \
+    default: return reinterpret_cast<const void*>(&mk_op_attn_split_##KN##_g0);       \
+  }
+  if (f32) MK_PICK(f32) else MK_PICK(bf16)
+#undef MK_PICK
+}
+const void* attn_full_kernel(bool f32, int G) {
+#define MK_PICK(KN)                                                                    \
+  switch (G) {                                                                         \
+    case 1: return reinterpret_cast<const void*>(&mk_op_attn_full_##KN##_g1);         \
+    case 2: return reinterpret_cast<const void*>(&mk_op_attn_full_##KN##_g2);         \
+    case 4: return reinterpret_cast<const void*>(&mk_op_attn_full_##KN##_g4);         \
+    case 8: return reinterpret_cast<const void*>(&mk_op_attn_full_##KN##_g8);         \
+    default: return reinterpret_cast<const void*>(&mk_op_attn_full_##KN##_g0);        \
+  }
+  if (f32) MK_PICK(f32) else MK_PICK(bf16)
+#undef MK_PICK
+}
+
 // Batched projection kernels by operator (QKV, O, GU, DOWN, LM) and batch tiles (1, 2, 4).
 const void* bgemm_kernel(int type, int bt) {
   const int i = bt == 1 ? 0 : bt == 2 ? 1 : 2;
@@ -311,12 +338,12 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
     if (single_split(h)) {
       int layer = l;
       void* args[] = {&Pc, &sp, &layer};
-      MK_TRY(launch(TT_ATTN, reinterpret_cast<const void*>(&mk_op_attn_full), dim3(Pc.B * Pc.nkv),
+      MK_TRY(launch(TT_ATTN, attn_full_kernel(Pc.kv_f32, Pc.nq / Pc.nkv), dim3(Pc.B * Pc.nkv),
                     dim3(kAttnFullWaves * kWave), args, (size_t)h->attn_full_lds));
     } else {
       int layer = l, fuse = fused_merge(h) ? 1 : 0;
       void* args[] = {&Pc, &sp, &layer, &fuse};
-      MK_TRY(launch(TT_ATTN, reinterpret_cast<const void*>(&mk_op_attn_split), dim3(Pc.B * Pc.nkv * Pc.nsplit),
+      MK_TRY(launch(TT_ATTN, attn_split_kernel(Pc.kv_f32, Pc.nq / Pc.nkv), dim3(Pc.B * Pc.nkv * Pc.nsplit),
                     dim3(kAttnWaves * kWave), args, (size_t)h->attn_lds));
       if (!fuse)
         MK_TRY(launch(TT_MERGE, reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(Pc.B * Pc.nkv),
@@ -372,10 +399,10 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
       int layer = g.tasks[b0].layer, fuse = fused_merge(h) ? 1 : 0;
       void* args[] = {&Pc, &sp, &layer, &fuse};
       if (type == TT_ATTN && single_split(h))
-        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_full), dim3(h->P.B * h->P.nkv),
+        HIP_TRY(hipLaunchKernel(attn_full_kernel(h->P.kv_f32, h->P.nq / h->P.nkv), dim3(h->P.B * h->P.nkv),
                                 dim3(kAttnFullWaves * kWave), args, (size_t)h->attn_full_lds, st));
       else if (type == TT_ATTN)
-        HIP_TRY(hipLaunchKernel(reinterpret_cast<const void*>(&mk_op_attn_split),
+        HIP_TRY(hipLaunchKernel(attn_split_kernel(h->P.kv_f32, h->P.nq / h->P.nkv),
                                 dim3(h->P.B * h->P.nkv * h->P.nsplit), dim3(kAttnWaves * kWave), args,
                                 (size_t)h->attn_lds, st));
       else
@@ -657,15 +684,15 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, h->op_lds[t]));
     int nb = 0;
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kWaves * kWave, h->op_lds[t]));
-    h->op_grid_cap[t] = std::max(1, nb) * ncu;
+    h->op_grid_cap[t] = std::max(1, std::min(nb, kOpWgsPerCu)) * ncu;
   }
-  h->attn_lds = (G * hd + kAttnWaves * G * kWave + kAttnWaves * G * (hd + 2)) * 4;
-  h->attn_full_lds = (G * hd + kAttnFullWaves * G * kWave + kAttnFullWaves * G * (hd + 2)) * 4;
+  h->attn_lds = (G * hd + kAttnWaves * G * (hd + 2)) * 4;  // queries, then the waves' records
+  h->attn_full_lds = (G * hd + kAttnFullWaves * G * (hd + 2)) * 4;
   if (std::max(h->attn_lds, h->attn_full_lds) > max_lds)
     return fail(MK_ERR_UNSUPPORTED, "attention LDS need exceeds the device limit");
-  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_op_attn_split),
+  HIP_TRY(hipFuncSetAttribute(attn_split_kernel(P.kv_f32, G),
                               hipFuncAttributeMaxDynamicSharedMemorySize, h->attn_lds));
-  HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_op_attn_full),
+  HIP_TRY(hipFuncSetAttribute(attn_full_kernel(P.kv_f32, G),
                               hipFuncAttributeMaxDynamicSharedMemorySize, h->attn_full_lds));
   if (cfg->mode == MK_MODE_MEGAKERNEL) {
     if (h->lds_mega > max_lds)

@@ -237,26 +237,36 @@ __device__ __forceinline__ void stage_vector(float* page, const float* src, cons
 // element type KT is bf16 (uint16_t) or fp32 (float).
 //
 // A block covers NP positions.  For the scores, LPP lanes share one position
-// (each lane holds 32 elements of the K row, loaded with 16-byte loads) and
-// their partial dot products are combined with DPP swaps inside the quad.
+// (each lane holds 64 bytes of the K row -- 32 bf16 or 16 fp32 elements --
+// loaded with 16-byte loads) and their partial dot products are combined with
+// DPP swaps inside the group of LPP lanes.
 // For the values, every lane owns DPL dims of every position.  K and V of the
 // whole block are loaded up front, so a block costs one memory round trip.
 template <int HD, typename KT>
 struct AttnGeom {
-  static constexpr int EPL = 32;                              // K elements per lane
-  static constexpr int LPP = HD / EPL;                        // lanes per position (2 or 4)
-  static constexpr int NP = kWave / LPP;                      // positions per block (32 or 16)
+  static constexpr int EPL = sizeof(KT) == 4 ? 16 : 32;      // K elements per lane (64 bytes)
+  static constexpr int LPP = HD / EPL;                        // lanes per position (2, 4 or 8)
+  static constexpr int NP = kWave / LPP;                      // positions per block (32, 16 or 8)
   static constexpr int KV16 = EPL * (int)sizeof(KT) / 16;    // 16-byte K loads per lane
   static constexpr int DPL = HD / kWave;                      // V dims per lane
 };
 
-template <int HD>
+// GQ: the query heads per KV group when fixed at compile time (the state and
+// score arrays then hold exactly GQ heads), or 0: up to kMaxGqa heads, the
+// count given at run time.
+template <int GQ>
+struct GqaHeads {
+  static constexpr int MAX = GQ ? GQ : kMaxGqa;
+  __device__ static constexpr bool has(int h, int G) { return GQ ? h < GQ : h < G; }
+};
+
+template <int HD, int GQ = 0>
 struct AttnState {
-  static constexpr int DPL = HD / kWave;
-  float m[kMaxGqa], l[kMaxGqa], o[kMaxGqa][DPL];
+  static constexpr int DPL = HD / kWave, GM = GqaHeads<GQ>::MAX;
+  float m[GM], l[GM], o[GM][DPL];
   __device__ void init() {
 #pragma unroll
-    for (int h = 0; h < kMaxGqa; ++h) {
+    for (int h = 0; h < GM; ++h) {
       m[h] = -INFINITY;
       l[h] = 0.f;
 #pragma unroll
@@ -322,29 +332,32 @@ __device__ __forceinline__ void attn_load(const KT* kc, const KT* vc, int p0, in
 }
 
 // Online-softmax update with the block [p0, min(p0 + NP, p1)) held in bf.
-// qs: LDS [G][HD] (rotated queries); pr: LDS [G][64] scratch of this wave.
-template <int HD, typename KT>
+// qs: LDS [G][HD] (rotated queries).  The weight of position j reaches every
+// lane by a read of lane j * LPP into a scalar register.
+template <int HD, typename KT, int GQ = 0>
 __device__ __forceinline__ void attn_compute(const AttnBuf<HD, KT>& bf, const float* qs, int p0, int p1, int G,
-                                             float* pr, int lane, AttnState<HD>& st) {
+                                             int lane, AttnState<HD, GQ>& st) {
   using Gm = AttnGeom<HD, KT>;
-  constexpr int DPL = Gm::DPL, NP = Gm::NP, LPP = Gm::LPP, EPL = Gm::EPL;
+  using Hs = GqaHeads<GQ>;
+  constexpr int DPL = Gm::DPL, NP = Gm::NP, LPP = Gm::LPP, EPL = Gm::EPL, GM = Hs::MAX;
   const int np = min(NP, p1 - p0);
   const int my = lane / LPP, part = lane % LPP;  // position and row part this lane scores
   const float scale = 1.0f / sqrtf((float)HD);
-  float sc[kMaxGqa];
+  float sc[GM], pv[GM];
 #pragma unroll
-  for (int h = 0; h < kMaxGqa; ++h) sc[h] = 0.f;
+  for (int h = 0; h < GM; ++h) sc[h] = 0.f;
 #pragma unroll
   for (int i = 0; i < EPL / 8; ++i) {
 #pragma unroll
-    for (int h = 0; h < kMaxGqa; ++h)
-      if (h < G) sc[h] = dot_k<KT>(bf.kr, i, qs + h * HD + part * EPL + i * 8, sc[h]);
+    for (int h = 0; h < GM; ++h)
+      if (Hs::has(h, G)) sc[h] = dot_k<KT>(bf.kr, i, qs + h * HD + part * EPL + i * 8, sc[h]);
   }
 #pragma unroll
-  for (int h = 0; h < kMaxGqa; ++h) {
-    if (h < G) {
-      sc[h] += dpp_f<0xB1>(sc[h]);                        // lanes 2j, 2j+1
-      if constexpr (LPP == 4) sc[h] += dpp_f<0x4E>(sc[h]);  // and the other pair of the quad
+  for (int h = 0; h < GM; ++h) {
+    if (Hs::has(h, G)) {
+      sc[h] += dpp_f<0xB1>(sc[h]);                          // lanes 2j, 2j+1
+      if constexpr (LPP >= 4) sc[h] += dpp_f<0x4E>(sc[h]);  // and the other pair of the quad
+      if constexpr (LPP == 8) sc[h] += dpp_f<0x141>(sc[h]); // and the other quad of the eight
       const float s = my < np ? sc[h] * scale : -INFINITY;
       const float mn = fmaxf(st.m[h], wave_max(s));
       const float alpha = __expf(st.m[h] - mn);  // 0 on the first block (m = -inf)
@@ -353,17 +366,16 @@ __device__ __forceinline__ void attn_compute(const AttnBuf<HD, KT>& bf, const fl
 #pragma unroll
       for (int e = 0; e < DPL; ++e) st.o[h][e] *= alpha;
       st.m[h] = mn;
-      if (part == 0) pr[h * kWave + my] = p;
+      pv[h] = p;
     }
   }
-  __builtin_amdgcn_wave_barrier();  // one wave's LDS writes and reads stay in order
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     if (j < np) {
 #pragma unroll
-      for (int h = 0; h < kMaxGqa; ++h) {
-        if (h < G) {
-          const float p = pr[h * kWave + j];
+      for (int h = 0; h < GM; ++h) {
+        if (Hs::has(h, G)) {
+          const float p = rd_lane(pv[h], j * LPP);
           float v[DPL];
           if constexpr (sizeof(KT) == 2) {
             if constexpr (DPL == 2) {
@@ -382,6 +394,9 @@ __device__ __forceinline__ void attn_compute(const AttnBuf<HD, KT>& bf, const fl
       }
     }
   }
+  // Keeps the query reads from LDS inside each block: hoisted out of the
+  // block loop they would hold G * EPL values per lane in registers for the
+  // whole loop and push the kernel into spills.
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -389,37 +404,37 @@ __device__ __forceinline__ void attn_compute(const AttnBuf<HD, KT>& bf, const fl
 // A: the next block's loads are in flight while the current one is computed.
 // Each exit path has its own code, so every path issues a fixed number of
 // loads (see gemv_stream).
-template <int HD, typename KT>
+template <int HD, typename KT, int GQ = 0>
 __device__ __forceinline__ void attn_pipeline(AttnBuf<HD, KT>& A, AttnBuf<HD, KT>& B, const float* qs, const KT* kc,
-                                              const KT* vc, int b, int p1, int stride, int G, float* pr, int lane,
-                                              AttnState<HD>& st) {
+                                              const KT* vc, int b, int p1, int stride, int G, int lane,
+                                              AttnState<HD, GQ>& st) {
   for (;;) {
     int n = b + stride;
     if (n >= p1) {
-      attn_compute<HD, KT>(A, qs, b, p1, G, pr, lane, st);
+      attn_compute<HD, KT, GQ>(A, qs, b, p1, G, lane, st);
       return;
     }
     attn_load<HD, KT>(kc, vc, n, p1, lane, B);
-    attn_compute<HD, KT>(A, qs, b, p1, G, pr, lane, st);
+    attn_compute<HD, KT, GQ>(A, qs, b, p1, G, lane, st);
     b = n;
     n = b + stride;
     if (n >= p1) {
-      attn_compute<HD, KT>(B, qs, b, p1, G, pr, lane, st);
+      attn_compute<HD, KT, GQ>(B, qs, b, p1, G, lane, st);
       return;
     }
     attn_load<HD, KT>(kc, vc, n, p1, lane, A);
-    attn_compute<HD, KT>(B, qs, b, p1, G, pr, lane, st);
+    attn_compute<HD, KT, GQ>(B, qs, b, p1, G, lane, st);
     b = n;
   }
 }
 
 // Writes a wave's state as G records of (o[HD], m, l).
-template <int HD>
-__device__ __forceinline__ void attn_store_state(const AttnState<HD>& st, int G, float* out, int lane) {
+template <int HD, int GQ = 0>
+__device__ __forceinline__ void attn_store_state(const AttnState<HD, GQ>& st, int G, float* out, int lane) {
   constexpr int DPL = HD / kWave;
 #pragma unroll
-  for (int h = 0; h < kMaxGqa; ++h) {
-    if (h < G) {
+  for (int h = 0; h < GqaHeads<GQ>::MAX; ++h) {
+    if (GqaHeads<GQ>::has(h, G)) {
       float* oh = out + h * (HD + 2);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) oh[lane * DPL + e] = st.o[h][e];
@@ -444,13 +459,12 @@ __device__ __forceinline__ void attn_partial(const float* q, const KT* kc, const
                                              float* out, float* scratch, int lane) {
   constexpr int NP = AttnGeom<HD, KT>::NP;
   float* qs = scratch;           // [G][HD]
-  float* pr = scratch + G * HD;  // [G][64]
   attn_load_q<HD>(q, G, qs, lane);
   AttnState<HD> st;
   st.init();
   AttnBuf<HD, KT> A, B;
   attn_load<HD, KT>(kc, vc, p0, p1, lane, A);
-  attn_pipeline<HD, KT>(A, B, qs, kc, vc, p0, p1, NP, G, pr, lane, st);
+  attn_pipeline<HD, KT>(A, B, qs, kc, vc, p0, p1, NP, G, lane, st);
   attn_store_state<HD>(st, G, out, lane);
 }
 

@@ -6,9 +6,15 @@
 
 namespace mk {
 extern "C" __global__ void mk_persistent(Params P, const Step* S, int page_floats, int scratch_floats);
-extern "C" __global__ void mk_op_attn_split(Params P, const Step* S, int layer, int fuse_merge);
+#define MK_ATTN_DECL(KN, GQ)                                                                                 \
+  extern "C" __global__ void mk_op_attn_split_##KN##_g##GQ(Params P, const Step* S, int layer, int fuse_merge); \
+  extern "C" __global__ void mk_op_attn_full_##KN##_g##GQ(Params P, const Step* S, int layer);
+#define MK_ATTN_DECL_G(KN) MK_ATTN_DECL(KN, 0) MK_ATTN_DECL(KN, 1) MK_ATTN_DECL(KN, 2) MK_ATTN_DECL(KN, 4) MK_ATTN_DECL(KN, 8)
+MK_ATTN_DECL_G(f32)
+MK_ATTN_DECL_G(bf16)
+#undef MK_ATTN_DECL_G
+#undef MK_ATTN_DECL
 extern "C" __global__ void mk_op_attn_merge(Params P, const Step* S, int layer);
-extern "C" __global__ void mk_op_attn_full(Params P, const Step* S, int layer);
 extern "C" __global__ void mk_set_step(Step* dst, Step s);
 #define MK_OP_DECL(name) extern "C" __global__ void name(Params P, const Step* S, OpArgs A, int pf, int sf);
 MK_OP_DECL(mk_op_qkv)

@@ -834,23 +834,22 @@ MK_OP_KERNEL(mk_op_lm_x, TT_LM, true)
 // and written as the attention output itself (and, on the batched path, the
 // O-projection's operand planes), so no merge launch follows; otherwise it
 // is one (o, m, l) record per head for the merge.
-template <int HD, typename KT, int NW, bool FINAL>
+template <int HD, typename KT, int NW, bool FINAL, int GQ>
 __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, int l, int b, int grp, int s, float* sm,
-                                              int wave, int lane) {
+                                              int wave, int lane, uint64_t* stamps) {
   using Gm = AttnGeom<HD, KT>;
   const int G = P.nq / P.nkv, T = S.pos + 1;
   const int p0 = s * P.split, p1 = min(p0 + P.split, T);
   if (p0 >= T) return;
-  float* qs = sm;                                     // [G][HD]
-  float* pr = qs + G * HD + wave * G * kWave;         // [G][64] per wave
-  float* recs = qs + G * HD + NW * G * kWave;         // [NW][G][HD + 2]
+  float* qs = sm;                // [G][HD]
+  float* recs = qs + G * HD;     // [NW][G][HD + 2]
   const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * HD;
   const int64_t o0 = kv_off(P, l, b, grp, 0);
   const KT* kc = static_cast<const KT*>(P.kcache) + o0;
   const KT* vc = static_cast<const KT*>(P.vcache) + o0;
   // The query loads first (every block needs them), then this wave's first
   // K/V block; only then wait for the queries.
-  constexpr int QPT = (kMaxGqa * HD + NW * kWave - 1) / (NW * kWave);
+  constexpr int QPT = (GqaHeads<GQ>::MAX * HD + NW * kWave - 1) / (NW * kWave);
   float qv[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) qv[i] = q[min((int)threadIdx.x + i * NW * kWave, G * HD - 1)];
@@ -863,10 +862,12 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
     if (idx < G * HD) qs[idx] = qv[i];
   }
   __syncthreads();
-  AttnState<HD> st;
+  if (stamps) stamps[1] = clock_now();
+  AttnState<HD, GQ> st;
   st.init();
-  if (b0 < p1) attn_pipeline<HD, KT>(A, B, qs, kc, vc, b0, p1, NW * Gm::NP, G, pr, lane, st);
-  attn_store_state<HD>(st, G, recs + wave * G * (HD + 2), lane);
+  if (b0 < p1) attn_pipeline<HD, KT, GQ>(A, B, qs, kc, vc, b0, p1, NW * Gm::NP, G, lane, st);
+  if (stamps) stamps[2] = clock_now();
+  attn_store_state<HD, GQ>(st, G, recs + wave * G * (HD + 2), lane);
   __syncthreads();
   for (int h = wave; h < G; h += NW) {
     // merge the waves' records of head h
@@ -926,14 +927,40 @@ __device__ __forceinline__ void merge_group(const Params& P, int layer, int b, i
   }
 }
 
+// Optional wave timeline of an attention launch (debug): entry, queries
+// staged, positions done, exit -- the layout of the GEMV operator timelines.
+struct AttnTrace {
+  uint64_t t[4];
+  bool on;
+  __device__ AttnTrace(const Params& P, int layer, int nwaves) {
+    const int wid = blockIdx.x * nwaves + (int)(threadIdx.x >> 6);
+    on = P.trace && P.trace_op == ((TT_ATTN << 16) | layer) && 4 * (wid + 1) <= 2 * P.trace_cap;
+    t[0] = on ? clock_now() : 0;
+    t[1] = t[2] = t[3] = 0;
+  }
+  __device__ uint64_t* stamps() { return on ? t : nullptr; }
+  __device__ void write(const Params& P, int nwaves) {
+    if (!on || (threadIdx.x & 63)) return;
+    const int wid = blockIdx.x * nwaves + (int)(threadIdx.x >> 6);
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);
+    unsigned long long* o = P.trace + 4 * (int64_t)wid;
+    o[0] = ((unsigned long long)((xcc & 0xF) << 28 | (hw & 0x0FFFFFFF)) << 32) | (uint32_t)t[0];
+    o[1] = t[1];
+    o[2] = t[2];
+    o[3] = clock_now();
+  }
+};
+
 // Split-KV attention, one workgroup per (batch row, KV group, split).  With
 // `fuse_merge`, the last workgroup of a (batch row, KV group) to finish
 // merges all its splits: every workgroup publishes its records with an
 // agent-scope fence and counts itself in attn_count; the one that brings the
 // count to the number of used splits acquires, merges, and resets the count
-// for the next launch.  No workgroup ever waits for another.
-extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_split(Params P, const Step* Sd, int layer,
-                                                                                 int fuse_merge) {
+// for the next launch.  No workgroup ever waits for another.  GQ: the query
+// heads per KV group when fixed at compile time (0: given at run time).
+template <typename KT, int GQ>
+__device__ __forceinline__ void attn_split_body(const Params& P, const Step* Sd, int layer, int fuse_merge) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sm = reinterpret_cast<float*>(smem);
   __shared__ uint32_t is_last;
@@ -943,13 +970,10 @@ extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_spli
   const int b = bg / P.nkv, grp = bg % P.nkv;
   const int used = (S.pos + 1 + P.split - 1) / P.split;
   if (s >= used) return;  // past the current length: no record, not counted
-  if (P.kv_f32) {
-    if (P.hd == 128) attn_split_wg<128, float, kAttnWaves, false>(P, S, layer, b, grp, s, sm, wave, lane);
-    else attn_split_wg<64, float, kAttnWaves, false>(P, S, layer, b, grp, s, sm, wave, lane);
-  } else {
-    if (P.hd == 128) attn_split_wg<128, uint16_t, kAttnWaves, false>(P, S, layer, b, grp, s, sm, wave, lane);
-    else attn_split_wg<64, uint16_t, kAttnWaves, false>(P, S, layer, b, grp, s, sm, wave, lane);
-  }
+  AttnTrace tr(P, layer, kAttnWaves);
+  if (P.hd == 128) attn_split_wg<128, KT, kAttnWaves, false, GQ>(P, S, layer, b, grp, s, sm, wave, lane, tr.stamps());
+  else attn_split_wg<64, KT, kAttnWaves, false, GQ>(P, S, layer, b, grp, s, sm, wave, lane, tr.stamps());
+  tr.write(P, kAttnWaves);
   if (!fuse_merge) return;
   __threadfence();  // release this wave's records at agent scope
   __syncthreads();
@@ -966,22 +990,40 @@ extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_spli
 
 // Whole-context attention: one workgroup of kAttnFullWaves waves per (batch
 // row, KV group) covers every position and writes the final output (used
-// when the context is short or the batch has many (row, group) pairs).
-extern "C" __global__ __launch_bounds__(kAttnFullWaves * kWave) void mk_op_attn_full(Params P, const Step* Sd,
-                                                                                    int layer) {
+// when the context fits one split).
+template <typename KT, int GQ>
+__device__ __forceinline__ void attn_full_body(const Params& P, const Step* Sd, int layer) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* sm = reinterpret_cast<float*>(smem);
   const Step S = ld_const(Sd);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.x / P.nkv, grp = blockIdx.x % P.nkv;
-  if (P.kv_f32) {
-    if (P.hd == 128) attn_split_wg<128, float, kAttnFullWaves, true>(P, S, layer, b, grp, 0, sm, wave, lane);
-    else attn_split_wg<64, float, kAttnFullWaves, true>(P, S, layer, b, grp, 0, sm, wave, lane);
-  } else {
-    if (P.hd == 128) attn_split_wg<128, uint16_t, kAttnFullWaves, true>(P, S, layer, b, grp, 0, sm, wave, lane);
-    else attn_split_wg<64, uint16_t, kAttnFullWaves, true>(P, S, layer, b, grp, 0, sm, wave, lane);
-  }
+  AttnTrace tr(P, layer, kAttnFullWaves);
+  if (P.hd == 128) attn_split_wg<128, KT, kAttnFullWaves, true, GQ>(P, S, layer, b, grp, 0, sm, wave, lane, tr.stamps());
+  else attn_split_wg<64, KT, kAttnFullWaves, true, GQ>(P, S, layer, b, grp, 0, sm, wave, lane, tr.stamps());
+  tr.write(P, kAttnFullWaves);
 }
+
+// One kernel pair per cache element type and group size, so that each gets
+// its own register allocation: the state arrays hold exactly the group's
+// heads (with room for 8 heads and both element types in one kernel they no
+// longer fit in registers and spilled to scratch).
+#define MK_ATTN_KERNELS(KN, KT, GQ)                                                                           \
+  extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_split_##KN##_g##GQ(             \
+      Params P, const Step* Sd, int layer, int fuse_merge) {                                                  \
+    attn_split_body<KT, GQ>(P, Sd, layer, fuse_merge);                                                        \
+  }                                                                                                           \
+  extern "C" __global__ __launch_bounds__(kAttnFullWaves * kWave) void mk_op_attn_full_##KN##_g##GQ(          \
+      Params P, const Step* Sd, int layer) {                                                                  \
+    attn_full_body<KT, GQ>(P, Sd, layer);                                                                     \
+  }
+#define MK_ATTN_KERNELS_G(KN, KT) \
+  MK_ATTN_KERNELS(KN, KT, 0) MK_ATTN_KERNELS(KN, KT, 1) MK_ATTN_KERNELS(KN, KT, 2) MK_ATTN_KERNELS(KN, KT, 4) \
+  MK_ATTN_KERNELS(KN, KT, 8)
+MK_ATTN_KERNELS_G(f32, float)
+MK_ATTN_KERNELS_G(bf16, uint16_t)
+#undef MK_ATTN_KERNELS_G
+#undef MK_ATTN_KERNELS
 
 // Log-sum-exp merge as its own launch: one wave per (batch row, query head).
 extern "C" __global__ __launch_bounds__(kMaxGqa * kWave) void mk_op_attn_merge(Params P, const Step* Sd, int layer) {

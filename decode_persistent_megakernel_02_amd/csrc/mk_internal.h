@@ -17,6 +17,10 @@ constexpr int kWorkers = kWaves - 1;  // worker waves per CU in the persistent k
 constexpr int kMaxGqa = 8;            // query heads per KV head supported
 constexpr int kMaxSplit = 4096;       // positions per split-KV attention task
 constexpr int kAttnWaves = 4;         // waves per split in the per-operator attention kernel
+#ifndef MK_OP_WGS_PER_CU
+#define MK_OP_WGS_PER_CU 8
+#endif
+constexpr int kOpWgsPerCu = MK_OP_WGS_PER_CU;  // per-operator GEMV grid: at most this many workgroups per CU
 #ifndef MK_XCDS
 #define MK_XCDS 8
 #endif

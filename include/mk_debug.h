@@ -75,12 +75,14 @@ mk_status mk_read_status(mk_handle* h, uint32_t out[16]);
 mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, double* ticks_per_us);
 
 /* Per-operator wave timeline (MK_MODE_PER_OP, batch 1, handle created with
- * MK_FLAG_TRACE | MK_FLAG_NO_GRAPH): from now on the waves of the GEMV
- * operator `type` (1 QKV, 4 O, 5 GU, 6 DOWN, 7 LM) of `layer` log four
- * wall-clock stamps each into the trace buffer read by mk_read_trace: entry
- * 4*w (w = block * 4 + wave) = (XCC_ID << 60 | HW_ID bits 0..27 << 32) |
- * start (low 32 bits), then input staged, weight stream done, epilogues done.
- * type < 0 stops logging. */
+ * MK_FLAG_TRACE | MK_FLAG_NO_GRAPH): from now on the waves of operator
+ * `type` of `layer` log four wall-clock stamps each into the trace buffer
+ * read by mk_read_trace: entry 4*w (w = block * waves per block + wave) =
+ * (XCC_ID << 60 | HW_ID bits 0..27 << 32) | start (low 32 bits), then three
+ * stamps.  GEMV operators (1 QKV, 4 O, 5 GU, 6 DOWN, 7 LM; 4 waves per
+ * block): input staged, weight stream done, epilogues done.  Attention (2;
+ * 4 waves per block, 8 for the single-split kernel): queries staged,
+ * positions done, records written.  type < 0 stops logging. */
 mk_status mk_trace_op(mk_handle* h, int32_t type, int32_t layer);
 
 /* Time operators with HIP events on the handle's stream (MK_MODE_PER_OP):
