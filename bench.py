@@ -240,7 +240,9 @@ def main():
                        kv_fp32=kv_fp32)
     total, eager_total, (gu_ms, gu_n), same_tokens, breakdown = time_decode(abi, h, prompt_t, steps, warmup, shape,
                                                                              torch, log)
-    gu_exact = bool(abi.mk_get_debug_view(h).exact_ops & (1 << abi.TASK_TYPES["gu"]))
+    view = abi.mk_get_debug_view(h)
+    gu_exact = bool(view.exact_ops & (1 << abi.TASK_TYPES["gu"]))
+    op_grid = {k: view.op_grid[v] for k, v in abi.TASK_TYPES.items() if view.op_grid[v]}
     # The gate/up launches of every layer replayed back to back between two
     # events: per-launch time without the cost of an event pair around each
     # launch (cycling through the layers keeps the weights out of the caches).
@@ -311,6 +313,7 @@ def main():
         "graph_and_eager_tokens_equal": same_tokens,
         "op_breakdown": op_breakdown,
         "op_replay_us_per_layer": replay_us,
+        "op_grid": op_grid,
         "megakernel": {"status": "disabled", "reason": "cooperative persistent launch did not complete on MI355X"},
         "cpu_baseline": None,
     }

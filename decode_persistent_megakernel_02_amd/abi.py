@@ -69,7 +69,7 @@ class mk_debug_view(ctypes.Structure):
                 ("attn_out", ctypes.c_void_p), ("h", ctypes.c_void_p), ("events", ctypes.c_void_p),
                 ("n_events", ctypes.c_int32), ("n_tasks", ctypes.c_int32), ("ncu", ctypes.c_int32),
                 ("nsplit", ctypes.c_int32), ("split", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("exact_ops", ctypes.c_uint32)]
+                ("exact_ops", ctypes.c_uint32), ("op_grid", ctypes.c_int32 * 9)]
 
 
 # Every symbol the headers declare, with its ctypes signature.

@@ -114,6 +114,7 @@ struct mk_handle {
   std::vector<void*> allocs;
   int page_floats = 0, scratch_floats = 0, lds_mega = 0;
   int op_page[9] = {0}, op_lds[9] = {0}, op_grid_cap[9] = {0}, op_sf[9] = {0};  // per task type
+  int op_grid[9] = {0};  // grid of the last launch of each GEMV operator
   bool op_exact[9] = {false};
   bool batched = false;                 // B > 1: matrix-core projections (batched.hip)
   int length = 0, batch = 0;
@@ -412,6 +413,7 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
       // a GEMV wave holds at most kMaxTasksPerWave results: keep the average at half of that
       const int min_grid = (count + kWaves * kMaxTasksPerWave / 2 - 1) / (kWaves * kMaxTasksPerWave / 2);
       const int grid = std::max(min_grid, std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]));
+      h->op_grid[type] = grid;
       OpArgs A = op_args(h, type, g.tasks[b0].layer, count);
       int opf = h->op_page[type];
       int osf = h->op_sf[type];
@@ -915,8 +917,10 @@ mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out) {
   out->split = h->P.split;
   out->lds_bytes = h->lds_mega;
   out->exact_ops = 0;
-  for (int t = 0; t < 9; ++t)
+  for (int t = 0; t < 9; ++t) {
     if (h->op_exact[t]) out->exact_ops |= 1u << t;
+    out->op_grid[t] = h->op_grid[t];
+  }
   return MK_OK;
 }
 

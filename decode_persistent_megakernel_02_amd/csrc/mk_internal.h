@@ -16,7 +16,10 @@ constexpr int kWaves = 8;             // waves per workgroup (1 scheduler + work
 constexpr int kWorkers = kWaves - 1;  // worker waves per CU in the persistent kernel
 constexpr int kMaxGqa = 8;            // query heads per KV head supported
 constexpr int kMaxSplit = 4096;       // positions per split-KV attention task
-constexpr int kAttnWaves = 4;         // waves per split in the per-operator attention kernel
+#ifndef MK_ATTN_WAVES
+#define MK_ATTN_WAVES 4
+#endif
+constexpr int kAttnWaves = MK_ATTN_WAVES;         // waves per split in the per-operator attention kernel
 #ifndef MK_OP_WGS_PER_CU
 #define MK_OP_WGS_PER_CU 8
 #endif

@@ -59,6 +59,8 @@ typedef struct {
   uint32_t exact_ops; /* per-operator mode: bit t set when operator type t runs
                          the variant without row/column clamps (its rows fill
                          whole tiles and its columns whole prefetch rounds) */
+  int32_t op_grid[9];  /* per-operator mode: workgroups of each GEMV operator's
+                          last launch (index = task type) */
 } mk_debug_view;
 mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out);
 
