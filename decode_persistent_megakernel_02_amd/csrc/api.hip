@@ -684,9 +684,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
       return fail(MK_ERR_UNSUPPORTED, "operator LDS need exceeds " + std::to_string(max_lds));
     const void* fn = op_kernel(t, h->op_exact[t]);
     HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, h->op_lds[t]));
-    int nb = 0;
-    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kWaves * kWave, h->op_lds[t]));
-    h->op_grid_cap[t] = std::max(1, std::min(nb, kOpWgsPerCu)) * ncu;
+    h->op_grid_cap[t] = kOpWgsPerCu * ncu;
   }
   h->attn_lds = (G * hd + kAttnWaves * G * (hd + 2)) * 4;  // queries, then the waves' records
   h->attn_full_lds = (G * hd + kAttnFullWaves * G * (hd + 2)) * 4;

@@ -21,9 +21,9 @@ constexpr int kMaxSplit = 4096;       // positions per split-KV attention task
 #endif
 constexpr int kAttnWaves = MK_ATTN_WAVES;         // waves per split in the per-operator attention kernel
 #ifndef MK_OP_WGS_PER_CU
-#define MK_OP_WGS_PER_CU 8
+#define MK_OP_WGS_PER_CU 1
 #endif
-constexpr int kOpWgsPerCu = MK_OP_WGS_PER_CU;  // per-operator GEMV grid: at most this many workgroups per CU
+constexpr int kOpWgsPerCu = MK_OP_WGS_PER_CU;  // per-operator GEMV grid: workgroups per CU (1 measured best)
 #ifndef MK_XCDS
 #define MK_XCDS 8
 #endif
