@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB five times (the known-size reference "
                          "for scaling hardware byte counters) and exit")
+    ap.add_argument("--row-major", action="store_true",
+                    help="batched workloads: keep the projection weights row-major instead of tiled")
     ap.add_argument("--attn-split", type=int, default=0, metavar="POSITIONS",
                     help="positions per split-KV attention workgroup (0: the library's choice)")
     ap.add_argument("--counters", type=int, default=0, metavar="STEPS",
@@ -202,6 +204,8 @@ def main():
     steps, warmup = args.steps, args.warmup
     max_seq = wl.prompt_len + max(steps, warmup)
     t = time.time()
+    # the batched path reads its projection weights in the tiled layout
+    tiled = B > 1 and not args.row_major
     if B == 1:
         weights = gen.gen_weights(shape, wl.weight_seed)
         dw = runtime.upload_weights(weights)
@@ -213,7 +217,7 @@ def main():
             if time.time() - last[0] > 20 or i == n:
                 last[0] = time.time()
                 log(f"weights: {i}/{n} tensors on the device")
-        dw = runtime.generate_device_weights(shape, wl.weight_seed, progress=progress)
+        dw = runtime.generate_device_weights(shape, wl.weight_seed, progress=progress, tiled=tiled)
     torch.cuda.synchronize()
     log(f"weights generated and uploaded in {time.time() - t:.1f}s")
     prompt = gen.gen_prompt(wl)
@@ -221,7 +225,7 @@ def main():
 
     # batch 1 keeps an fp32 KV cache; the batched workloads state a bf16 cache
     kv_fp32 = B == 1
-    flags = abi.MK_FLAG_FUSED_MERGE if args.fused_merge else 0
+    flags = (abi.MK_FLAG_FUSED_MERGE if args.fused_merge else 0) | (abi.MK_FLAG_TILED_WEIGHTS if tiled else 0)
     if args.counters:
         if args.counters_prompt:
             prompt_t = prompt_t[:, :args.counters_prompt].contiguous()
@@ -298,6 +302,7 @@ def main():
                    "mode": "per_op (HIP graph per step)" + (", fused merge" if args.fused_merge else ""),
                    "kv_cache": "fp32" if kv_fp32 else "bf16",
                    "attn_split": args.attn_split or "library default",
+                   "weights": "tiled" if tiled else "row-major",
                    "parallelism": "none (1 GPU)"},
         "tokens_per_s": 1000.0 * B / ms,
         "achieved_gbps": alg_bytes / (ms * 1e-3) / 1e9,

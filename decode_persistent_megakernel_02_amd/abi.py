@@ -16,7 +16,7 @@ MK_ABI_VERSION = 1
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_OUT_OF_MEMORY, MK_ERR_HIP = 0, -1, -2, -3
 MK_ERR_CAPACITY, MK_ERR_TIMEOUT, MK_ERR_STATE, MK_ERR_UNSUPPORTED = -4, -5, -6, -7
 MK_MODE_MEGAKERNEL, MK_MODE_PER_OP = 0, 1
-MK_FLAG_TRACE, MK_FLAG_POISON, MK_FLAG_NO_GRAPH, MK_FLAG_FUSED_MERGE = 1, 2, 4, 8
+MK_FLAG_TRACE, MK_FLAG_POISON, MK_FLAG_NO_GRAPH, MK_FLAG_FUSED_MERGE, MK_FLAG_TILED_WEIGHTS = 1, 2, 4, 8, 16
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_OUT_OF_MEMORY", -3: "MK_ERR_HIP",
                 -4: "MK_ERR_CAPACITY", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE", -7: "MK_ERR_UNSUPPORTED"}
 
@@ -96,7 +96,8 @@ SIGNATURES = {
     "mk_t_gemv": ([_P, _P, _P, _I32, _I32, _P], _I32),
     "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
-    "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _P], _I32),
+    "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P], _I32),
+    "mk_tile_weights": ([_P, _P, _I64, _I64, _P], _I32),
     "mk_trace_op": ([_P, _I32, _I32], _I32),
     "mk_t_argmax": ([_P, _I32, _P, _P], _I32),
     "mk_device_info": ([ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
@@ -327,13 +328,21 @@ def mk_t_attention(q, k, v, T, split, o, stream=None):
                               _stream(stream)), "mk_t_attention")
 
 
-def mk_t_bgemm(W, A, Y, B, stream=None):
+def mk_t_bgemm(W, A, Y, B, tiled=False, stream=None):
     """Y = (A[0, :B] + A[1, :B]) @ W.T on the matrix cores; A [2, Bp, K] bf16 hi/lo
-    planes with Bp = 16, 32 or 64 rows, rows >= B zero."""
+    planes with Bp = 16, 32 or 64 rows, rows >= B zero.  tiled: W [N, K] holds
+    the mk_tile_weights layout."""
     N, K = W.shape
     Bp = 16 * (1 if B <= 16 else 2 if B <= 32 else 4)
     assert A.shape == (2, Bp, K) and Y.shape == (B, N)
-    _check(lib.mk_t_bgemm(_ptr(W), _ptr(A), _ptr(Y), N, K, B, _stream(stream)), "mk_t_bgemm")
+    _check(lib.mk_t_bgemm(_ptr(W), _ptr(A), _ptr(Y), N, K, B, 1 if tiled else 0, _stream(stream)), "mk_t_bgemm")
+
+
+def mk_tile_weights(src, dst, stream=None):
+    """dst = the tiled layout of the row-major bf16 matrix src [N, K] (device)."""
+    N, K = src.shape
+    assert dst.numel() == src.numel() and dst.data_ptr() != src.data_ptr()
+    _check(lib.mk_tile_weights(_ptr(src), _ptr(dst), N, K, _stream(stream)), "mk_tile_weights")
 
 
 def mk_t_argmax(x, out, stream=None):

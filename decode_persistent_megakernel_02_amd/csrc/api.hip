@@ -61,6 +61,12 @@ std::string check_config(const mk_config* c) {
   if (c->attn_split < 0 || c->attn_split > kMaxSplit) return "attn_split must be in [0, 4096]";
   if (c->num_cus < 0) return "num_cus must be >= 0";
   if ((int64_t)c->vocab * c->hidden >= (1ll << 40)) return "vocab * hidden too large";
+  if (c->flags & MK_FLAG_TILED_WEIGHTS) {
+    if (c->max_batch < 2) return "tiled weights are read by the batched path only (max_batch >= 2)";
+    const int qd = c->n_q_heads * c->head_dim, kd = c->n_kv_heads * c->head_dim;
+    if (c->hidden % 32 || c->ffn % 32 || qd % 32 || kd % 16 || (!c->tie_embeddings && c->vocab % 16))
+      return "tiled weights need row counts that are multiples of 16 and column counts that are multiples of 32";
+  }
   return "";
 }
 
@@ -245,22 +251,18 @@ const void* attn_full_kernel(bool f32, int G) {
 #undef MK_PICK
 }
 
-// Batched projection kernels by operator (QKV, O, GU, DOWN, LM) and batch tiles (1, 2, 4).
-const void* bgemm_kernel(int type, int bt) {
+// Batched projection kernels by operator (QKV, O, GU, DOWN, LM), batch tiles
+// (1, 2, 4) and weight layout (row-major, tiled).
+const void* bgemm_kernel(int type, int bt, bool tiled) {
   const int i = bt == 1 ? 0 : bt == 2 ? 1 : 2;
-  static const void* const k[5][3] = {
-      {reinterpret_cast<const void*>(&mk_b_qkv_b1), reinterpret_cast<const void*>(&mk_b_qkv_b2),
-       reinterpret_cast<const void*>(&mk_b_qkv_b4)},
-      {reinterpret_cast<const void*>(&mk_b_o_b1), reinterpret_cast<const void*>(&mk_b_o_b2),
-       reinterpret_cast<const void*>(&mk_b_o_b4)},
-      {reinterpret_cast<const void*>(&mk_b_gu_b1), reinterpret_cast<const void*>(&mk_b_gu_b2),
-       reinterpret_cast<const void*>(&mk_b_gu_b4)},
-      {reinterpret_cast<const void*>(&mk_b_down_b1), reinterpret_cast<const void*>(&mk_b_down_b2),
-       reinterpret_cast<const void*>(&mk_b_down_b4)},
-      {reinterpret_cast<const void*>(&mk_b_lm_b1), reinterpret_cast<const void*>(&mk_b_lm_b2),
-       reinterpret_cast<const void*>(&mk_b_lm_b4)}};
+#define MK_K(op) {reinterpret_cast<const void*>(&mk_b_##op##_b1), reinterpret_cast<const void*>(&mk_b_##op##_b2), \
+                   reinterpret_cast<const void*>(&mk_b_##op##_b4)},                                             \
+                  {reinterpret_cast<const void*>(&mk_b_##op##_b1_t), reinterpret_cast<const void*>(&mk_b_##op##_b2_t), \
+                   reinterpret_cast<const void*>(&mk_b_##op##_b4_t)}
+  static const void* const k[5][2][3] = {{MK_K(qkv)}, {MK_K(o)}, {MK_K(gu)}, {MK_K(down)}, {MK_K(lm)}};
+#undef MK_K
   const int row = type == TT_QKV ? 0 : type == TT_O ? 1 : type == TT_GU ? 2 : type == TT_DOWN ? 3 : 4;
-  return k[row][i];
+  return k[row][tiled ? 1 : 0][i];
 }
 int bgemm_lds(int bt) { return b_lds_bytes(bt) + kMaxBatch * 8; }
 
@@ -297,6 +299,12 @@ const void* bfin_kernel(int type) {
   }
 }
 
+// Whether the batched projection `type` reads tiled weights (the LM head of a
+// tied model reads the row-major embedding table).
+bool tiled_ops(const mk_handle* h, int type) {
+  return (h->cfg.flags & MK_FLAG_TILED_WEIGHTS) && !(type == TT_LM && h->P.tied);
+}
+
 // One step of the batched path: per layer norm, QKV, attention, merge, O,
 // norm, gate/up, down; then the final norm, the LM head and the argmax.
 // Timed launches are bracketed by events (type 0 = the norms).
@@ -326,7 +334,7 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
     const int ks = bgemm_splits(Pc, type, Pc.ncu);
     const int ngx = (bgemm_groups(Pc, type) + kBgemmWaves - 1) / kBgemmWaves;
     void* args[] = {&Pc, &sp, &layer};
-    MK_TRY(launch(type, bgemm_kernel(type, bt), dim3(ngx, ks), dim3(kBgemmWaves * kWave), args,
+    MK_TRY(launch(type, bgemm_kernel(type, bt, tiled_ops(h, type)), dim3(ngx, ks), dim3(kBgemmWaves * kWave), args,
                   (size_t)bgemm_lds(bt)));
     if (ks == 1) return MK_OK;
     int k = ks;
@@ -607,7 +615,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     int64_t n_part = 1;
     for (int t : {TT_QKV, TT_O, TT_GU, TT_DOWN, TT_LM}) {
       if (bgemm_lds(bt) > max_lds) return fail(MK_ERR_UNSUPPORTED, "batched projection LDS need exceeds the device");
-      HIP_TRY(hipFuncSetAttribute(bgemm_kernel(t, bt), hipFuncAttributeMaxDynamicSharedMemorySize, bgemm_lds(bt)));
+      HIP_TRY(hipFuncSetAttribute(bgemm_kernel(t, bt, tiled_ops(h, t)), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  bgemm_lds(bt)));
       const int ks = bgemm_splits(P, t, ncu);
       if (ks > 1) n_part = std::max<int64_t>(n_part, (int64_t)ks * bgemm_groups(P, t) * 2 * 16 * P.Bp);
     }
@@ -1063,10 +1072,12 @@ mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t h
   return MK_OK;
 }
 
-mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t K, int32_t B, void* stream) {
+mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t K, int32_t B, int32_t tiled,
+                     void* stream) {
   g_err.clear();
   if (!W || !A || !Y || N < 1 || K < 8 || K % 8 || B < 1 || B > kMaxBatch)
     return fail(MK_ERR_INVALID_ARG, "bad bgemm arguments");
+  if (tiled && (N % 16 || K % 32)) return fail(MK_ERR_INVALID_ARG, "tiled weights need N % 16 == 0 and K % 32 == 0");
   const int lds = b_lds_bytes(batch_tiles(B));
   // A device query first: as the first HIP call of a process,
   // hipFuncSetAttribute reports that no device exists.
@@ -1077,7 +1088,19 @@ mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t 
   hipLaunchKernelGGL(mk_t_bgemm_kernel, dim3((N + 32 * kBgemmWaves - 1) / (32 * kBgemmWaves)),
                      dim3(kBgemmWaves * kWave), (unsigned)lds,
                      static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W),
-                     static_cast<const uint16_t*>(A), Y, N, K, B);
+                     static_cast<const uint16_t*>(A), Y, N, K, B, tiled ? 1 : 0);
+  HIP_TRY(hipGetLastError());
+  return MK_OK;
+}
+
+mk_status mk_tile_weights(const void* src, void* dst, int64_t N, int64_t K, void* stream) {
+  g_err.clear();
+  if (!src || !dst || src == dst || N < 16 || K < 32 || N % 16 || K % 32)
+    return fail(MK_ERR_INVALID_ARG, "tiling needs distinct buffers, N % 16 == 0 and K % 32 == 0");
+  const int64_t nv = N * K / 8;
+  const int grid = (int)std::min<int64_t>((nv + 255) / 256, 4096);
+  hipLaunchKernelGGL(mk_tile_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), N, K);
   HIP_TRY(hipGetLastError());
   return MK_OK;
 }

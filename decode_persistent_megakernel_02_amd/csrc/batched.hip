@@ -228,12 +228,22 @@ __device__ __forceinline__ void chunk_store(uint16_t* buf, const v4u (&cr)[Chunk
   }
 }
 
-// The weight fragments of k-step s (global step index) of the wave's two tiles.
-template <int RT>
+// The weight fragments of k-step s (global step index) of the wave's two
+// tiles.  Row-major weights: this lane's 16 bytes of its row (16 rows x 64
+// bytes per wave load).  Tiled weights (16 x 32 blocks stored as the
+// fragments of one wave load): this lane's 16 bytes of the tile's block s,
+// so one wave load reads 1 KB in one piece.
+template <int RT, bool TILED>
 __device__ __forceinline__ void weights_load(v4u (&wb)[RT], const v4u* const (&wr)[RT], int s, int nvec, int piece) {
-  const int v = min(4 * s + piece, nvec - 1);  // past K: any in-bounds vector (the activations are zero there)
+  if constexpr (TILED) {
+    const int b = min(s, nvec / 4 - 1);  // past K: any in-bounds block (the activations are zero there)
 #pragma unroll
-  for (int r = 0; r < RT; ++r) wb[r] = ld_w(wr[r] + v);
+    for (int r = 0; r < RT; ++r) wb[r] = ld_w(wr[r] + 64 * b);
+  } else {
+    const int v = min(4 * s + piece, nvec - 1);  // past K: any in-bounds vector (the activations are zero there)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) wb[r] = ld_w(wr[r] + v);
+  }
 }
 
 // acc[r][t] += W_r . (A_t.hi + A_t.lo)^T for k-step `ks` of the chunk in buf.
@@ -258,7 +268,7 @@ __device__ __forceinline__ void chunk_mma(const v4u (&wb)[RT], const uint16_t* b
 // Chunk ci+1 (activations and weights) is in flight while chunk ci is
 // multiplied; the last chunk is peeled so that every loop iteration issues
 // the same loads.  Returns the accumulators of this wave's two tiles.
-template <int RT, int BT, int KC>
+template <int RT, int BT, int KC, bool TILED>
 __device__ __forceinline__ void staged_gemm(const uint16_t* A, int K, const v4u* const (&wr)[RT], int c0, int c1,
                                             uint16_t* lds, int lane, f32x4 (&acc)[RT][BT]) {
   using C = Chunk<BT, KC>;
@@ -272,7 +282,7 @@ __device__ __forceinline__ void staged_gemm(const uint16_t* A, int K, const v4u*
   v4u wb[ST][RT];
   chunk_load<BT, KC>(A, K, c0, cr);
 #pragma unroll
-  for (int d = 0; d < ST; ++d) weights_load<RT>(wb[d], wr, c0 * ST + d, nvec, piece);
+  for (int d = 0; d < ST; ++d) weights_load<RT, TILED>(wb[d], wr, c0 * ST + d, nvec, piece);
   chunk_store<BT, KC>(lds, cr);
   __syncthreads();
   int ci = c0;
@@ -282,7 +292,7 @@ __device__ __forceinline__ void staged_gemm(const uint16_t* A, int K, const v4u*
 #pragma unroll
     for (int d = 0; d < ST; ++d) {
       chunk_mma<RT, BT, KC>(wb[d], buf, d, lane, acc);
-      weights_load<RT>(wb[d], wr, (ci + 1) * ST + d, nvec, piece);
+      weights_load<RT, TILED>(wb[d], wr, (ci + 1) * ST + d, nvec, piece);
     }
     chunk_store<BT, KC>(lds + ((ci + 1 - c0) & 1) * C::ELEMS, cr);
     __syncthreads();
@@ -301,14 +311,21 @@ __device__ __forceinline__ int group_count(const Params& P) {
   else return (P.H + 31) / 32;  // O, DOWN
 }
 
-template <int TT>
+// This lane's weight stream of each tile: its row (row-major weights) or its
+// 16 bytes in the tile's first block (tiled weights: N % 16 == 0, K % 32 == 0).
+template <int TT, bool TILED>
 __device__ __forceinline__ void group_pointers(const Params& P, int l, int g, int lane, GroupRows& G,
                                                const v4u* (&wr)[kRT]) {
   G = group_rows<TT>(P, l, g);
 #pragma unroll
   for (int r = 0; r < kRT; ++r) {
-    const int row = min(G.row0[r] + (lane & 15), G.N - 1);  // rows past the end repeat the last (discarded)
-    wr[r] = reinterpret_cast<const v4u*>(G.W[r] + (int64_t)row * G.K);
+    if constexpr (TILED) {
+      const int row0 = min(G.row0[r], G.N - 16);  // a tile past the end re-reads the last one (discarded)
+      wr[r] = reinterpret_cast<const v4u*>(G.W[r] + (int64_t)row0 * G.K) + lane;
+    } else {
+      const int row = min(G.row0[r] + (lane & 15), G.N - 1);  // rows past the end repeat the last (discarded)
+      wr[r] = reinterpret_cast<const v4u*>(G.W[r] + (int64_t)row * G.K);
+    }
   }
 }
 
@@ -320,7 +337,7 @@ __device__ __forceinline__ int64_t part_index(int kz, int ngroups, int g, int r,
 // The projection kernel: grid (ceil(groups / 4), splits of K).  With one
 // split the epilogue runs here, straight from each wave's accumulators;
 // otherwise the partial sums go to P.bpart for the finishing launch.
-template <int TT, int BT, int KC>
+template <int TT, int BT, int KC, bool TILED>
 __device__ __forceinline__ void bgemm(const Params& P, const Step& S, int l) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
@@ -333,11 +350,11 @@ __device__ __forceinline__ void bgemm(const Params& P, const Step& S, int l) {
   }
   GroupRows G;
   const v4u* wr[kRT];
-  group_pointers<TT>(P, l, gc, lane, G, wr);
+  group_pointers<TT, TILED>(P, l, gc, lane, G, wr);
   const int nch = (G.K + KC - 1) / KC, ks = gridDim.y, per = (nch + ks - 1) / ks;
   const int c0 = blockIdx.y * per, c1 = min(c0 + per, nch);
   f32x4 acc[kRT][BT];
-  staged_gemm<kRT, BT, KC>(operand_of<TT>(P), G.K, wr, c0, c1, lds, lane, acc);
+  staged_gemm<kRT, BT, KC, TILED>(operand_of<TT>(P), G.K, wr, c0, c1, lds, lane, acc);
   if (ks == 1) {
     if (g < ngroups) {
 #pragma unroll
@@ -393,13 +410,16 @@ __device__ __forceinline__ void bgemm_finish(const Params& P, const Step& S, int
 // Chunk width by batch tiles: 256 columns at 16 rows, 128 at 32 and 64 (LDS).
 template <int BT> struct BChunk { static constexpr int KC = BT == 1 ? 256 : 128; };
 
-#define MK_BGEMM(name, TT, BT)                                                                                \
-  extern "C" __global__ __launch_bounds__(kBgemmWaves * kWave) void name##_b##BT(Params P, const Step* Sd,     \
-                                                                                  int layer) {                \
+#define MK_BGEMM(name, TT, BT, SUF, TILED)                                                                    \
+  extern "C" __global__ __launch_bounds__(kBgemmWaves * kWave) void name##_b##BT##SUF(Params P,               \
+                                                                                       const Step* Sd,         \
+                                                                                       int layer) {            \
     const Step S = ld_const(Sd);                                                                              \
-    bgemm<TT, BT, BChunk<BT>::KC>(P, S, layer);                                                               \
+    bgemm<TT, BT, BChunk<BT>::KC, TILED>(P, S, layer);                                                        \
   }
-#define MK_BGEMM_ALL(name, TT) MK_BGEMM(name, TT, 1) MK_BGEMM(name, TT, 2) MK_BGEMM(name, TT, 4)
+#define MK_BGEMM_ALL(name, TT)                                                                                \
+  MK_BGEMM(name, TT, 1, , false) MK_BGEMM(name, TT, 2, , false) MK_BGEMM(name, TT, 4, , false)                \
+  MK_BGEMM(name, TT, 1, _t, true) MK_BGEMM(name, TT, 2, _t, true) MK_BGEMM(name, TT, 4, _t, true)
 MK_BGEMM_ALL(mk_b_qkv, TT_QKV)
 MK_BGEMM_ALL(mk_b_o, TT_O)
 MK_BGEMM_ALL(mk_b_gu, TT_GU)
@@ -517,9 +537,9 @@ extern "C" __global__ void mk_b_argmax(Params P, const Step* Sd) {
 }
 
 // Test entry: Y[b][n] = sum_k W[n][k] (A.hi[b][k] + A.lo[b][k]) for bf16 W
-// [N, K] and A [2][Bp][K] (rows B..Bp-1 zero): the same staged core, each
-// wave owning 32 consecutive rows, one split.
-template <int BT>
+// [N, K] (row-major, or tiled) and A [2][Bp][K] (rows B..Bp-1 zero): the same
+// staged core, each wave owning 32 consecutive rows, one split.
+template <int BT, bool TILED>
 __device__ __forceinline__ void t_bgemm(const uint16_t* W, const uint16_t* A, float* Y, int N, int K, int B) {
   constexpr int KC = BChunk<BT>::KC;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -528,10 +548,14 @@ __device__ __forceinline__ void t_bgemm(const uint16_t* W, const uint16_t* A, fl
   const int row0 = (blockIdx.x * kBgemmWaves + wave) * 32;
   const v4u* wr[kRT];
 #pragma unroll
-  for (int r = 0; r < kRT; ++r)
-    wr[r] = reinterpret_cast<const v4u*>(W + (int64_t)min(row0 + r * 16 + (lane & 15), N - 1) * K);
+  for (int r = 0; r < kRT; ++r) {
+    if constexpr (TILED)
+      wr[r] = reinterpret_cast<const v4u*>(W + (int64_t)min(row0 + r * 16, N - 16) * K) + lane;
+    else
+      wr[r] = reinterpret_cast<const v4u*>(W + (int64_t)min(row0 + r * 16 + (lane & 15), N - 1) * K);
+  }
   f32x4 acc[kRT][BT];
-  staged_gemm<kRT, BT, KC>(A, K, wr, 0, (K + KC - 1) / KC, lds, lane, acc);
+  staged_gemm<kRT, BT, KC, TILED>(A, K, wr, 0, (K + KC - 1) / KC, lds, lane, acc);
 #pragma unroll
   for (int r = 0; r < kRT; ++r)
 #pragma unroll
@@ -544,11 +568,33 @@ __device__ __forceinline__ void t_bgemm(const uint16_t* W, const uint16_t* A, fl
 }
 extern "C" __global__ __launch_bounds__(kBgemmWaves * kWave) void mk_t_bgemm_kernel(const uint16_t* W,
                                                                                      const uint16_t* A, float* Y,
-                                                                                     int N, int K, int B) {
+                                                                                     int N, int K, int B, int tiled) {
   const int bt = (B + 15) / 16;
-  if (bt == 1) t_bgemm<1>(W, A, Y, N, K, B);
-  else if (bt == 2) t_bgemm<2>(W, A, Y, N, K, B);
-  else t_bgemm<4>(W, A, Y, N, K, B);
+  if (tiled) {
+    if (bt == 1) t_bgemm<1, true>(W, A, Y, N, K, B);
+    else if (bt == 2) t_bgemm<2, true>(W, A, Y, N, K, B);
+    else t_bgemm<4, true>(W, A, Y, N, K, B);
+  } else {
+    if (bt == 1) t_bgemm<1, false>(W, A, Y, N, K, B);
+    else if (bt == 2) t_bgemm<2, false>(W, A, Y, N, K, B);
+    else t_bgemm<4, false>(W, A, Y, N, K, B);
+  }
+}
+
+// Row-major W [N][K] bf16 -> the tiled layout read by the batched projections:
+// block (i, j) of 16 rows x 32 columns at element offset (i * K/32 + j) * 512,
+// holding lane l's 8 elements W[16i + l % 16][32j + 8 (l / 16) .. + 8] at
+// offset 8 l (the fragment lane l supplies to one matrix-core k-step).  One
+// thread per 16-byte vector of the destination.
+extern "C" __global__ __launch_bounds__(256) void mk_tile_kernel(const uint16_t* src, uint16_t* dst, int64_t N,
+                                                                 int64_t K) {
+  const int64_t nv = N * K / 8, bpr = K / 32;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nv; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t blk = v / 64, i = blk / bpr, j = blk % bpr;
+    const int l = (int)(v % 64);
+    const int64_t row = 16 * i + (l & 15), col = 32 * j + 8 * (l >> 4);
+    *reinterpret_cast<v4u*>(dst + 8 * v) = ld_g(reinterpret_cast<const v4u*>(src + row * K + col));
+  }
 }
 
 // LDS bytes of the batched projection kernels and the test entry, by batch

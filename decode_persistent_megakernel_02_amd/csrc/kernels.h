@@ -31,11 +31,11 @@ MK_OP_DECL(mk_op_lm_x)
 #undef MK_OP_DECL
 // batched path (batched.hip)
 #define MK_BGEMM_DECL(name) extern "C" __global__ void name(Params P, const Step* S, int layer);
-MK_BGEMM_DECL(mk_b_qkv_b1) MK_BGEMM_DECL(mk_b_qkv_b2) MK_BGEMM_DECL(mk_b_qkv_b4)
-MK_BGEMM_DECL(mk_b_o_b1) MK_BGEMM_DECL(mk_b_o_b2) MK_BGEMM_DECL(mk_b_o_b4)
-MK_BGEMM_DECL(mk_b_gu_b1) MK_BGEMM_DECL(mk_b_gu_b2) MK_BGEMM_DECL(mk_b_gu_b4)
-MK_BGEMM_DECL(mk_b_down_b1) MK_BGEMM_DECL(mk_b_down_b2) MK_BGEMM_DECL(mk_b_down_b4)
-MK_BGEMM_DECL(mk_b_lm_b1) MK_BGEMM_DECL(mk_b_lm_b2) MK_BGEMM_DECL(mk_b_lm_b4)
+#define MK_BGEMM_DECL_ALL(op)                                                                      \
+  MK_BGEMM_DECL(mk_b_##op##_b1) MK_BGEMM_DECL(mk_b_##op##_b2) MK_BGEMM_DECL(mk_b_##op##_b4)       \
+  MK_BGEMM_DECL(mk_b_##op##_b1_t) MK_BGEMM_DECL(mk_b_##op##_b2_t) MK_BGEMM_DECL(mk_b_##op##_b4_t)
+MK_BGEMM_DECL_ALL(qkv) MK_BGEMM_DECL_ALL(o) MK_BGEMM_DECL_ALL(gu) MK_BGEMM_DECL_ALL(down) MK_BGEMM_DECL_ALL(lm)
+#undef MK_BGEMM_DECL_ALL
 #undef MK_BGEMM_DECL
 extern "C" __global__ void mk_b_fin_qkv(Params P, const Step* S, int layer, int ks);
 extern "C" __global__ void mk_b_fin_o(Params P, const Step* S, int layer, int ks);
@@ -45,7 +45,9 @@ int b_lds_bytes(int bt);  // LDS of the batched projection kernels by batch tile
 constexpr int kBChunkCols[5] = {0, 256, 128, 128, 128};  // activation chunk width by batch tiles
 extern "C" __global__ void mk_b_norm(Params P, const Step* S, int layer, int kind);
 extern "C" __global__ void mk_b_argmax(Params P, const Step* S);
-extern "C" __global__ void mk_t_bgemm_kernel(const uint16_t* W, const uint16_t* A, float* Y, int N, int K, int B);
+extern "C" __global__ void mk_t_bgemm_kernel(const uint16_t* W, const uint16_t* A, float* Y, int N, int K, int B,
+                                             int tiled);
+extern "C" __global__ void mk_tile_kernel(const uint16_t* src, uint16_t* dst, int64_t N, int64_t K);
 extern "C" __global__ void mk_fill_u32(uint32_t* p, int64_t n, uint32_t v);
 extern "C" __global__ void mk_t_gemv_kernel(const uint16_t* W, const float* x, float* y, int N, int K);
 extern "C" __global__ void mk_t_rmsnorm_kernel(const float* x, const uint16_t* gamma, float eps, float* y, int n);

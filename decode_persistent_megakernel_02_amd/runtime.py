@@ -16,18 +16,42 @@ def to_device_bits(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(a.view(np.int16)).to(device, non_blocking=False).view(torch.bfloat16)
 
 
-def upload_weights(weights: dict, device="cuda") -> dict:
-    return {n: to_device_bits(a, device) for n, a in weights.items()}
+# Projection matrices that MK_FLAG_TILED_WEIGHTS stores tiled (the LM head only
+# when it is its own matrix; the embedding table stays row-major).
+TILED_FIELDS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
-def generate_device_weights(shape, seed=0, random_norms=False, device="cuda", progress=None) -> dict:
+def is_tiled_name(name: str) -> bool:
+    return name == "lm_head" or name.split(".")[-1] in TILED_FIELDS
+
+
+def tile(t: torch.Tensor) -> torch.Tensor:
+    """The tiled layout of a row-major bf16 device matrix (a new tensor)."""
+    out = torch.empty_like(t)
+    abi.mk_tile_weights(t, out)
+    return out
+
+
+def upload_weights(weights: dict, device="cuda", tiled=False) -> dict:
+    """tiled: store the projection matrices in the layout of MK_FLAG_TILED_WEIGHTS."""
+    out = {}
+    for n, a in weights.items():
+        t = to_device_bits(a, device)
+        out[n] = tile(t) if tiled and is_tiled_name(n) else t
+    return out
+
+
+def generate_device_weights(shape, seed=0, random_norms=False, device="cuda", progress=None, tiled=False) -> dict:
     """Generate each weight with the seeded host generator and move it to the
-    device; `progress(done, total)` is called after every tensor if given."""
+    device (tiled as in upload_weights); `progress(done, total)` is called
+    after every tensor if given."""
     from synth import gen, presets
     out = {}
     names = list(presets.weight_shapes(shape))
     for i, name in enumerate(names):
-        out[name] = to_device_bits(gen.gen_weight(shape, name, seed, random_norms), device)
+        t = to_device_bits(gen.gen_weight(shape, name, seed, random_norms), device)
+        out[name] = tile(t) if tiled and is_tiled_name(name) else t
+        del t
         if progress:
             progress(i + 1, len(names))
     return out

@@ -61,15 +61,31 @@ enum {
   MK_MODE_PER_OP = 1      /* one kernel launch per operator, the same task bodies */
 };
 
-/* Debug flags (mk_config.flags). */
+/* Flags (mk_config.flags). */
 enum {
   MK_FLAG_TRACE = 1u << 0,  /* record per-task {cu, task, start, end} timestamps */
   MK_FLAG_POISON = 1u << 1,  /* fill activation scratch with NaN before every step */
   MK_FLAG_NO_GRAPH = 1u << 2, /* per-op mode: launch every operator eagerly instead of
                                  replaying the step as one captured HIP graph */
-  MK_FLAG_FUSED_MERGE = 1u << 3 /* per-op mode: run the attention log-sum-exp merge in the last
-                                   split workgroup of each KV group instead of as its own launch */
+  MK_FLAG_FUSED_MERGE = 1u << 3, /* per-op mode: run the attention log-sum-exp merge in the last
+                                    split workgroup of each KV group instead of as its own launch */
+  MK_FLAG_TILED_WEIGHTS = 1u << 4 /* batched path (max_batch >= 2): wq, wk, wv, wo, w_gate, w_up,
+                                     w_down and (untied) lm_head are stored in the tiled layout that
+                                     mk_tile_weights writes; embed and the norm gains stay
+                                     row-major.  Needs every projection's row count a multiple of
+                                     16 and its column count a multiple of 32 (mk_create checks). */
 };
+
+/* Converts a row-major bf16 matrix W [N][K] (device memory) into the tiled
+ * layout of MK_FLAG_TILED_WEIGHTS, in dst (device, N*K elements, distinct
+ * from src), asynchronously on `hip_stream` (NULL: the default stream).
+ * Layout: 16 x 32 blocks; block (i, j) starts at element (i * K/32 + j) * 512
+ * and holds, at element 8*l + e (l < 64, e < 8), W[16i + l mod 16][32j +
+ * 8*floor(l/16) + e] -- the 16 bytes lane l supplies to one 16x16x32
+ * matrix-core step, so a wave reads each block as one contiguous kilobyte.
+ * Errors: MK_ERR_INVALID_ARG for NULL or equal pointers, N not a multiple of
+ * 16 or K not a multiple of 32. */
+mk_status mk_tile_weights(const void* src, void* dst, int64_t N, int64_t K, void* hip_stream);
 
 /* Model shape and runtime options.  Weights are bf16, activations fp32, the
  * KV cache bf16.  Shapes must satisfy: hidden, ffn and n_q_heads*head_dim are

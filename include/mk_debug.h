@@ -129,8 +129,10 @@ mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t h
  * (A[0][b][k] + A[1][b][k]) for b < B, n < N; W bf16 [N, K]; A bf16
  * [2][Bp][K], the hi and lo planes of the activations, with Bp = 16, 32 or 64
  * rows (the smallest that holds B; rows B..Bp-1 of both planes must be zero);
- * Y fp32 [B, N]; K a multiple of 8, 1 <= B <= 64. */
-mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t K, int32_t B, void* stream);
+ * Y fp32 [B, N]; K a multiple of 8, 1 <= B <= 64.  tiled != 0: W is in the
+ * layout of mk_tile_weights (N a multiple of 16, K of 32). */
+mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t K, int32_t B, int32_t tiled,
+                     void* stream);
 /* out[0] = lowest index of the maximum of x[n] (fp32).  Synchronous. */
 mk_status mk_t_argmax(const float* x, int32_t n, int32_t* out, void* stream);
 

@@ -10,3 +10,9 @@ MICRO_MHA = ModelShape("micro_mha", 1, 64, 4, 4, 16, 96, 128, 1e-5, 10000.0, Fal
 MINI = ModelShape("mini", 2, 128, 4, 2, 64, 264, 322, 1e-5, 10000.0, False)
 MINI_TIED = ModelShape("mini_tied", 2, 128, 4, 2, 64, 264, 322, 1e-5, 10000.0, True)
 MINI_G8 = ModelShape("mini_g8", 1, 256, 8, 1, 128, 520, 258, 1e-5, 500000.0, False)
+
+# Shapes whose projections fit the tiled weight layout (rows multiples of 16,
+# columns multiples of 32), untied, tied and with 8 query heads per KV head.
+MINI_TILE = ModelShape("mini_tile", 2, 128, 4, 2, 64, 256, 336, 1e-5, 10000.0, False)
+MINI_TILE_TIED = ModelShape("mini_tile_tied", 2, 128, 4, 2, 64, 256, 336, 1e-5, 10000.0, True)
+MINI_TILE_G8 = ModelShape("mini_tile_g8", 1, 256, 8, 1, 128, 512, 272, 1e-5, 500000.0, False)

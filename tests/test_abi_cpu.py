@@ -59,6 +59,32 @@ def test_invalid_configs_are_rejected():
         assert e.value.status == abi.MK_ERR_INVALID_ARG, b
 
 
+def test_tiled_weights_flag_is_checked_on_the_host():
+    from tests.shapes import MINI_TILE
+    # batch 1 never reads tiled weights; MINI's ffn (264) is not a multiple of 32
+    for shape, B in ((MINI_TILE, 1), (MINI, 4)):
+        c = cfg_for(shape, max_batch=B, flags=abi.MK_FLAG_TILED_WEIGHTS)
+        with pytest.raises(abi.MkError) as e:
+            abi.mk_graph_inspect(c, 8)
+        assert e.value.status == abi.MK_ERR_INVALID_ARG, (shape.name, B)
+    # a valid batched tiled config passes the checks (the task graph itself is batch-1 only)
+    c = cfg_for(MINI_TILE, max_batch=4, flags=abi.MK_FLAG_TILED_WEIGHTS)
+    with pytest.raises(abi.MkError) as e:
+        abi.mk_graph_inspect(c, 8)
+    assert e.value.status == abi.MK_ERR_UNSUPPORTED
+
+
+def test_tile_weights_rejects_bad_shapes_before_any_launch():
+    import torch
+    for n, k in ((15, 32), (16, 40), (0, 32)):
+        src = torch.zeros(max(n, 1), k, dtype=torch.int16)
+        dst = torch.zeros_like(src)
+        st = abi.lib.mk_tile_weights(src.data_ptr(), dst.data_ptr(), n, k, None)
+        assert st == abi.MK_ERR_INVALID_ARG, (n, k)
+    src = torch.zeros(16, 32, dtype=torch.int16)
+    assert abi.lib.mk_tile_weights(src.data_ptr(), src.data_ptr(), 16, 32, None) == abi.MK_ERR_INVALID_ARG
+
+
 def test_create_rejects_null_weights_without_touching_gpu():
     c = cfg_for(MINI)
     out = ctypes.c_void_p()

@@ -18,7 +18,7 @@ import torch
 from oracle import decoder as D
 from synth import gen, presets
 from tests.gpu_util import rel_err
-from tests.shapes import MINI, MINI_G8, MINI_TIED
+from tests.shapes import MINI, MINI_G8, MINI_TIED, MINI_TILE, MINI_TILE_G8, MINI_TILE_TIED
 
 pytestmark = pytest.mark.gpu
 
@@ -85,17 +85,62 @@ def test_bgemm_random(abi, N, K, B):
     assert err <= 2e-5, err
 
 
+def tile_ref(bits):
+    """The tiled layout of a row-major [N, K] array, written from its definition:
+    block (i, j) at (i * K/32 + j) * 512 holds at 8 l + e the element
+    W[16 i + l % 16][32 j + 8 (l // 16) + e]."""
+    N, K = bits.shape
+    out = np.empty(N * K, dtype=bits.dtype)
+    for i in range(N // 16):
+        for j in range(K // 32):
+            base = (i * (K // 32) + j) * 512
+            for l in range(64):
+                out[base + 8 * l: base + 8 * l + 8] = bits[16 * i + l % 16, 32 * j + 8 * (l // 16): 32 * j + 8 * (l // 16) + 8]
+    return out
+
+
+@pytest.mark.parametrize("N,K", [(16, 32), (48, 96), (336, 128)])
+def test_tile_layout_matches_its_definition(abi, N, K):
+    bits = np.random.default_rng(N + K).integers(0, 1 << 16, size=(N, K), dtype=np.uint64).astype(np.uint16)
+    src = torch.from_numpy(bits.view(np.int16)).cuda()
+    dst = torch.empty_like(src)
+    abi.mk_tile_weights(src, dst)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy().view(np.uint16).reshape(-1), tile_ref(bits))
+
+
+@pytest.mark.parametrize("N,K,B", [(16, 32, 1), (300 - 12, 4096, 8), (64, 512, 16), (48, 2048, 17), (128, 8192, 64),
+                                   (32, 28672, 5)])
+def test_bgemm_tiled_equals_row_major(abi, N, K, B):
+    """The same products from tiled weights: bit-identical to the row-major path
+    (the matrix cores see the same operands in the same order)."""
+    from decode_persistent_megakernel_02_amd import runtime
+    rng = np.random.default_rng(N + 3 * K + B)
+    W = torch.from_numpy(rng.normal(0, 0.02, size=(N, K)).astype(np.float32)).to(torch.bfloat16).cuda()
+    a = torch.from_numpy(rng.normal(0, 1, size=(B, K)).astype(np.float32))
+    A = torch.zeros(2, padded_rows(B), K, dtype=torch.bfloat16)
+    A[0, :B] = a.to(torch.bfloat16)
+    A[1, :B] = (a - A[0, :B].float()).to(torch.bfloat16)
+    A = A.cuda()
+    Y0 = torch.zeros(B, N, dtype=torch.float32, device="cuda")
+    Y1 = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    abi.mk_t_bgemm(W, A, Y0, B)
+    abi.mk_t_bgemm(runtime.tile(W), A, Y1, B, tiled=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y0.cpu().numpy(), Y1.cpu().numpy())
+
+
 # ---- end-to-end batched decode -------------------------------------------------------
 class BatchCase:
     """One batched model on the GPU; the oracles run on the same seeded inputs."""
 
-    def __init__(self, abi, shape, B, max_seq, seed=0, random_norms=True, attn_split=0, weights=None):
+    def __init__(self, abi, shape, B, max_seq, seed=0, random_norms=True, attn_split=0, weights=None, tiled=False):
         from decode_persistent_megakernel_02_amd import runtime
         self.abi, self.shape, self.B = abi, shape, B
         self.w = weights if weights is not None else gen.gen_weights(shape, seed, random_norms)
-        self.dw = runtime.upload_weights(self.w)
-        self.h = runtime.create(shape, self.dw, max_seq, B, abi.MK_MODE_PER_OP, attn_split=attn_split,
-                                kv_fp32=False)
+        self.dw = runtime.upload_weights(self.w, tiled=tiled)
+        self.h = runtime.create(shape, self.dw, max_seq, B, abi.MK_MODE_PER_OP,
+                                abi.MK_FLAG_TILED_WEIGHTS if tiled else 0, attn_split=attn_split, kv_fp32=False)
         self.out = torch.zeros(B, dtype=torch.int32, device="cuda")
         self.tok = torch.zeros(B, dtype=torch.int32, device="cuda")
         self.logits = torch.zeros(B, shape.vocab, dtype=torch.float32, device="cuda")
@@ -259,24 +304,54 @@ def test_batched_operator_replay_leaves_the_batch_unchanged(abi):
     assert np.array_equal(res[0], res[1])
 
 
+@pytest.mark.parametrize("shape,B", [(MINI_TILE, 5), (MINI_TILE_TIED, 20), (MINI_TILE_G8, 40)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_batched_tiled_weights_equal_row_major(abi, shape, B):
+    """Decoding from tiled weights gives the same bits as from row-major ones
+    (teacher-forced, prefill plus seeded steps), and both match the oracle."""
+    P, steps = 7, 4
+    prompt = gen.tokens(40 + B, presets.TID_PROMPT, 0, B * P, shape.vocab).reshape(B, P)
+    feed = gen.tokens(41 + B, presets.TID_PROMPT, 0, B * steps, shape.vocab).reshape(steps, B)
+    w = gen.gen_weights(shape, B, True)
+    runs = []
+    for tiled in (False, True):
+        print(f"{shape.name} B={B} tiled={tiled}", flush=True)
+        case = BatchCase(abi, shape, B, P + steps, weights=w, tiled=tiled)
+        res = [case.prefill(prompt)[0]]
+        for s in range(steps):
+            res.append(case.step(feed[s])[0])
+        case.close()
+        runs.append(np.stack(res))
+    assert np.array_equal(runs[0], runs[1])
+    ex = D.Decoder(shape, w, B, P + steps)
+    rd = D.Decoder(shape, w, B, P + steps, kv_bf16=True)
+    errs = []
+    refs = [(ex.prefill(prompt), rd.prefill(prompt))] + [(ex.step(feed[s]), rd.step(feed[s])) for s in range(steps)]
+    for g, (e, r) in zip(runs[1], refs):
+        e_c, e_t = rel_err(g, e), rel_err(g, r)
+        errs.append((float(e_c.max()), float(e_t.max())))
+    assert max(e[0] for e in errs) <= CONTRACT and max(e[1] for e in errs) <= TIGHT, errs
+
+
 def layer_subset(shape, n_layers):
     from dataclasses import replace
     return replace(shape, name=f"{shape.name}_{n_layers}l", n_layers=n_layers)
 
 
-@pytest.mark.parametrize("base,B,P", [(presets.LLAMA8B, 8, 40), (presets.LLAMA70B, 64, 12)],
-                         ids=["llama8b_b8", "llama70b_b64"])
-def test_real_layer_shapes_reduced_depth(abi, base, B, P):
+@pytest.mark.parametrize("base,B,P,tiled", [(presets.LLAMA8B, 8, 40, True), (presets.LLAMA70B, 64, 12, True),
+                                            (presets.LLAMA8B, 8, 40, False)],
+                         ids=["llama8b_b8_tiled", "llama70b_b64_tiled", "llama8b_b8_row_major"])
+def test_real_layer_shapes_reduced_depth(abi, base, B, P, tiled):
     """The batched workloads' layer shapes (8B at batch 8, 70B at batch 64), two
     layers deep, against the oracle's cache-free forward (teacher-forced with
-    seeded tokens)."""
+    seeded tokens); the workloads' tiled weights, and row-major ones."""
     shape = layer_subset(base, 2)
     steps = 2
     T = P + steps
     seq = gen.tokens(900 + B, presets.TID_PROMPT, 0, B * T, shape.vocab).reshape(B, T).astype(np.int32)
     print(f"[{shape.name} B={B}] generating weights", flush=True)
     w = gen.gen_weights(shape, 0)
-    case = BatchCase(abi, shape, B, T, weights=w)
+    case = BatchCase(abi, shape, B, T, weights=w, tiled=tiled)
     got = [case.prefill(seq[:, :P])]
     for s in range(steps):
         got.append(case.step(seq[:, P + s]))
