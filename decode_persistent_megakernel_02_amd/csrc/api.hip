@@ -223,6 +223,9 @@ bool fused_merge(const mk_handle* h) { return (h->cfg.flags & MK_FLAG_FUSED_MERG
 // longer contexts measured slower: at the 8B shape, batch 1, 37 against 21 us
 // per layer (8 CUs busy), and at the 70B shape, 64 sequences, 100 against 73.
 bool single_split(const mk_handle* h) { return h->P.nsplit == 1; }
+// Single sequence, split attention, no fused merge: the O-projection merges
+// the split records while it stages its input (one launch fewer per layer).
+bool merge_in_o(const mk_handle* h) { return !h->batched && !fused_merge(h) && !single_split(h); }
 
 // Attention kernels by cache element type and query heads per KV group
 // (compile-time group sizes 1, 2, 4, 8; other sizes use the run-time variant).
@@ -397,7 +400,7 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
     const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
     if (count <= 0) continue;
     const int type = g.stage_type[s];
-    if (type == TT_MERGE && (fused_merge(h) || single_split(h))) continue;  // done by the attention launch
+    if (type == TT_MERGE && (fused_merge(h) || single_split(h) || merge_in_o(h))) continue;  // done elsewhere
     if (h->only_type >= 0) {
       if (type != h->only_type) continue;
       ++h->replayed;
@@ -423,6 +426,7 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
       const int grid = std::max(min_grid, std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]));
       h->op_grid[type] = grid;
       OpArgs A = op_args(h, type, g.tasks[b0].layer, count);
+      A.merge = type == TT_O && merge_in_o(h) ? 1 : 0;
       int opf = h->op_page[type];
       int osf = h->op_sf[type];
       void* args[] = {&Pc, &sp, &A, &opf, &osf};

@@ -166,6 +166,71 @@ __device__ void stage_finish(const Params& P, const StageSrc& r, const StageRegs
   __syncthreads();
 }
 
+// The O-projection's input merged straight from the attention split records
+// of layer l (batch row 0), when no merge launch runs: for each 8-element
+// group of this lane, M = the largest split maximum, weights exp(m_s - M),
+// output = sum_s w_s o_s / sum_s w_s l_s (the log-sum-exp merge).  Eight
+// splits' maxima, then four splits' records, are loaded per round; every
+// load reads a clamped, in-bounds split (weight 0 past the used ones).
+// (A one-pass version with a running maximum and eight records per round
+// measured no faster and needs 60 more registers.)  Workgroup 0 also stores
+// the merged vector as the attention output.  Ends with a workgroup barrier;
+// every wave calls it once.
+__device__ void stage_merged(const Params& P, const Step& S, int l, float* page, int wave, int lane) {
+  const int hd = P.hd, G = P.nq / P.nkv, n = P.nq * hd;
+  const int used = (S.pos + 1 + P.split - 1) / P.split;
+  const int64_t rs = (int64_t)G * (hd + 2);  // floats between the records of consecutive splits
+  constexpr int NG = kWaves * kWave;
+  float* out = P.attn_out + (int64_t)l * P.B * n;
+  for (int i = (wave * kWave + lane) * 8; i < n; i += NG * 8) {
+    const int hq = i / hd, d = i % hd;
+    const float* rec = P.attn_part + ((int64_t)l * P.B * P.nkv + hq / G) * P.nsplit * rs + (hq % G) * (hd + 2);
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < used; s0 += 8) {
+      float2 ml[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        ml[k] = *reinterpret_cast<const float2*>(rec + (int64_t)min(s0 + k, used - 1) * rs + hd);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < used && ml[k].y > 0.f) M = fmaxf(M, ml[k].x);
+    }
+    float L = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    for (int s0 = 0; s0 < used; s0 += 4) {
+      float2 ml[4];
+      float4 a[4], c[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float* r = rec + (int64_t)min(s0 + k, used - 1) * rs;
+        ml[k] = *reinterpret_cast<const float2*>(r + hd);
+        a[k] = *reinterpret_cast<const float4*>(r + d);
+        c[k] = *reinterpret_cast<const float4*>(r + d + 4);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float w = s0 + k < used && ml[k].y > 0.f ? __expf(ml[k].x - M) : 0.f;
+        L = fmaf(w, ml[k].y, L);
+        o[0] = fmaf(w, a[k].x, o[0]); o[1] = fmaf(w, a[k].y, o[1]);
+        o[2] = fmaf(w, a[k].z, o[2]); o[3] = fmaf(w, a[k].w, o[3]);
+        o[4] = fmaf(w, c[k].x, o[4]); o[5] = fmaf(w, c[k].y, o[5]);
+        o[6] = fmaf(w, c[k].z, o[6]); o[7] = fmaf(w, c[k].w, o[7]);
+      }
+    }
+    const float inv = 1.0f / L;
+    const float4 v0 = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+    const float4 v1 = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+    *reinterpret_cast<float4*>(page + i) = v0;
+    *reinterpret_cast<float4*>(page + i + 4) = v1;
+    if (blockIdx.x == 0) {
+      *reinterpret_cast<float4*>(out + i) = v0;
+      *reinterpret_cast<float4*>(out + i + 4) = v1;
+    }
+  }
+  __syncthreads();
+}
+
 template <int R>
 __device__ __forceinline__ float pick(const float (&y)[R], int i) {
   float v = y[0];
@@ -754,7 +819,8 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const O
   constexpr int SU = TT == TT_DOWN ? 4 : 2;  // register-staged groups per lane: vectors up to SU * 4096
   StageSrc src{};
   StageRegs<SU> st;
-  if (first.stage) {
+  const bool merged = TT == TT_O && A.merge;  // input merged from the attention splits
+  if (first.stage && !merged) {
     src = stage_src(P, S, first.stage, first.batch, A.gain);
     stage_issue<SU>(src, wave, lane, st);
   }
@@ -762,7 +828,8 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const O
   float* red = reinterpret_cast<float*>(L->slot);  // per-wave partial sums of squares
   auto wait = [&]() __attribute__((always_inline)) -> bool {
     if (!staged) {
-      if (first.stage) stage_finish<SU>(P, src, st, page, red, wave, lane);
+      if (merged) stage_merged(P, S, A.layer, page, wave, lane);
+      else if (first.stage) stage_finish<SU>(P, src, st, page, red, wave, lane);
       else __syncthreads();
       staged = true;
     }

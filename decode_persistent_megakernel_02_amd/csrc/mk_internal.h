@@ -142,6 +142,7 @@ struct OpArgs {
   const uint16_t* gain;  // RMSNorm gain of the staged input, null if it is not normalised
   int32_t layer;
   int32_t count;
+  int32_t merge;         // O-projection: stage the input by merging the attention split records
 };
 
 #if defined(__HIPCC__)

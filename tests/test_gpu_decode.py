@@ -203,10 +203,11 @@ def test_graph_replays_match_eager_bitwise(abi):
     assert np.array_equal(runs[0], runs[1])
 
 
-def test_fused_merge_equals_separate_merge_bitwise(abi):
+def test_fused_merge_agrees_with_the_o_projection_merge(abi):
     """The log-sum-exp merge run by the last split workgroup of each KV group
-    gives the same bits as the merge launched on its own (same arithmetic,
-    same order), over contexts that span one to five 8-position splits."""
+    and the one the O-projection runs while staging its input agree to fp32
+    rounding (they add the weighted split sums in different orders), over
+    contexts that span one to five 8-position splits."""
     shape = MINI_G8
     w = gen.gen_weights(shape, 9, True)
     prompt = gen.tokens(9, 3, 0, 5, shape.vocab)
@@ -218,7 +219,8 @@ def test_fused_merge_equals_separate_merge_bitwise(abi):
                   24, 25, 26, 27, 28, 29, 30, 31, 32):
             res.append(case.step(t)[0])
         runs.append(np.stack(res))
-    assert np.array_equal(runs[0], runs[1])
+    err = np.abs(runs[0] - runs[1]).max() / np.abs(runs[1]).max()
+    assert err <= 1e-5, err
 
 
 def test_operator_replay_leaves_the_sequence_unchanged(abi):
@@ -234,9 +236,11 @@ def test_operator_replay_leaves_the_sequence_unchanged(abi):
         res = [case.prefill(prompt)[0]]
         for t in (4, 200, 8, 21, 250, 6, 13):
             if replay:
-                for name in ("qkv", "attn", "merge", "o", "gu", "down"):
+                for name in ("qkv", "attn", "o", "gu", "down"):
                     ms, n = abi.mk_time_op_replay(case.h, name, 3)
                     assert n == 3 * shape.n_layers and ms > 0.0, (name, n, ms)
+                # the O-projection merges the attention splits: no merge launches
+                assert abi.mk_time_op_replay(case.h, "merge", 3)[1] == 0
                 for name in ("lm", "argmax", "norm"):
                     with pytest.raises(abi.MkError):
                         abi.mk_time_op_replay(case.h, name, 1)
