@@ -255,14 +255,15 @@ const void* attn_full_kernel(bool f32, int G) {
 }
 
 // Batched projection kernels by operator (QKV, O, GU, DOWN, LM), batch tiles
-// (1, 2, 4) and weight layout (row-major, tiled).
-const void* bgemm_kernel(int type, int bt, bool tiled) {
-  const int i = bt == 1 ? 0 : bt == 2 ? 1 : 2;
+// (1, 2, 4), weight layout (row-major, tiled) and row groups per wave (1; 2
+// for 4 batch tiles).
+const void* bgemm_kernel(int type, int bt, bool tiled, int gpw) {
+  const int i = gpw == 2 ? 3 : bt == 1 ? 0 : bt == 2 ? 1 : 2;
 #define MK_K(op) {reinterpret_cast<const void*>(&mk_b_##op##_b1), reinterpret_cast<const void*>(&mk_b_##op##_b2), \
-                   reinterpret_cast<const void*>(&mk_b_##op##_b4)},                                             \
+                   reinterpret_cast<const void*>(&mk_b_##op##_b4), reinterpret_cast<const void*>(&mk_b_##op##_b4_g2)}, \
                   {reinterpret_cast<const void*>(&mk_b_##op##_b1_t), reinterpret_cast<const void*>(&mk_b_##op##_b2_t), \
-                   reinterpret_cast<const void*>(&mk_b_##op##_b4_t)}
-  static const void* const k[5][2][3] = {{MK_K(qkv)}, {MK_K(o)}, {MK_K(gu)}, {MK_K(down)}, {MK_K(lm)}};
+                   reinterpret_cast<const void*>(&mk_b_##op##_b4_t), reinterpret_cast<const void*>(&mk_b_##op##_b4_t_g2)}
+  static const void* const k[5][2][4] = {{MK_K(qkv)}, {MK_K(o)}, {MK_K(gu)}, {MK_K(down)}, {MK_K(lm)}};
 #undef MK_K
   const int row = type == TT_QKV ? 0 : type == TT_O ? 1 : type == TT_GU ? 2 : type == TT_DOWN ? 3 : 4;
   return k[row][tiled ? 1 : 0][i];
@@ -278,6 +279,18 @@ int bgemm_groups(const Params& P, int type) {
     default: return (P.V + 31) / 32;
   }
 }
+// Row groups per wave of a batched projection: two with 4 batch tiles when
+// that still leaves at least half a workgroup per CU without splitting K
+// (measured at the 70B shape, 64 sequences: gate/up 233 -> 211 us, but the
+// O-projection and down, with 8x fewer groups, got slower).
+int bgemm_gpw(const Params& P, int type) {
+  return batch_tiles(P.B) == 4 && bgemm_groups(P, type) / (2 * kBgemmWaves) >= P.ncu / 2 ? 2 : 1;
+}
+// Workgroups along the rows of a batched projection.
+int bgemm_blocks(const Params& P, int type) {
+  const int per = kBgemmWaves * bgemm_gpw(P, type);
+  return (bgemm_groups(P, type) + per - 1) / per;
+}
 int bgemm_k(const Params& P, int type) { return type == TT_O ? P.nq * P.hd : type == TT_DOWN ? P.F : P.H; }
 
 // Splits of K for a batched projection: enough workgroups for two per CU,
@@ -286,7 +299,7 @@ int bgemm_k(const Params& P, int type) { return type == TT_O ? P.nq * P.hd : typ
 int bgemm_splits(const Params& P, int type, int ncu) {
   if (type == TT_LM) return 1;
   const int bt = batch_tiles(P.B), kc = kBChunkCols[bt];
-  const int ngx = (bgemm_groups(P, type) + kBgemmWaves - 1) / kBgemmWaves;
+  const int ngx = bgemm_blocks(P, type);
   const int nch = (bgemm_k(P, type) + kc - 1) / kc;
   int ks = std::max(1, std::min(nch, (2 * ncu + ngx - 1) / ngx));
   const int per = (nch + ks - 1) / ks;
@@ -335,10 +348,10 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
   };
   auto gemm = [&](int type, int layer) -> mk_status {
     const int ks = bgemm_splits(Pc, type, Pc.ncu);
-    const int ngx = (bgemm_groups(Pc, type) + kBgemmWaves - 1) / kBgemmWaves;
+    const int ngx = bgemm_blocks(Pc, type);
     void* args[] = {&Pc, &sp, &layer};
-    MK_TRY(launch(type, bgemm_kernel(type, bt, tiled_ops(h, type)), dim3(ngx, ks), dim3(kBgemmWaves * kWave), args,
-                  (size_t)bgemm_lds(bt)));
+    const void* fn = bgemm_kernel(type, bt, tiled_ops(h, type), bgemm_gpw(Pc, type));
+    MK_TRY(launch(type, fn, dim3(ngx, ks), dim3(kBgemmWaves * kWave), args, (size_t)bgemm_lds(bt)));
     if (ks == 1) return MK_OK;
     int k = ks;
     void* fargs[] = {&Pc, &sp, &layer, &k};
@@ -619,8 +632,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     int64_t n_part = 1;
     for (int t : {TT_QKV, TT_O, TT_GU, TT_DOWN, TT_LM}) {
       if (bgemm_lds(bt) > max_lds) return fail(MK_ERR_UNSUPPORTED, "batched projection LDS need exceeds the device");
-      HIP_TRY(hipFuncSetAttribute(bgemm_kernel(t, bt, tiled_ops(h, t)), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  bgemm_lds(bt)));
+      HIP_TRY(hipFuncSetAttribute(bgemm_kernel(t, bt, tiled_ops(h, t), bgemm_gpw(P, t)),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, bgemm_lds(bt)));
       const int ks = bgemm_splits(P, t, ncu);
       if (ks > 1) n_part = std::max<int64_t>(n_part, (int64_t)ks * bgemm_groups(P, t) * 2 * 16 * P.Bp);
     }

@@ -334,39 +334,54 @@ __device__ __forceinline__ int64_t part_index(int kz, int ngroups, int g, int r,
   return ((((int64_t)kz * ngroups + g) * kRT + r) * 16 + m) * Bp + b;
 }
 
-// The projection kernel: grid (ceil(groups / 4), splits of K).  With one
-// split the epilogue runs here, straight from each wave's accumulators;
-// otherwise the partial sums go to P.bpart for the finishing launch.
-template <int TT, int BT, int KC, bool TILED>
+// The projection kernel: grid (ceil(groups / (4 * GPW)), splits of K); wave w
+// of workgroup x owns the GPW row groups (x * 4 + w) * GPW + i.  With 64
+// batch rows and many groups two groups per wave pay: every activation
+// fragment read from LDS then feeds four tiles instead of two (one group per
+// wave reads four bytes of LDS per weight byte, near the LDS bandwidth).
+// With one split the epilogue runs here, straight from each wave's
+// accumulators; otherwise the partial sums go to P.bpart for the finishing
+// launch.
+template <int TT, int BT, int KC, bool TILED, int GPW>
 __device__ __forceinline__ void bgemm(const Params& P, const Step& S, int l) {
+  constexpr int RT = kRT * GPW;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
   unsigned long long* best = reinterpret_cast<unsigned long long*>(smem + chunk_lds_bytes<BT, KC>());  // [64]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ngroups = group_count<TT>(P);
-  const int g = blockIdx.x * kBgemmWaves + wave, gc = min(g, ngroups - 1);  // a spare wave repeats the last group
+  const int g0 = (blockIdx.x * kBgemmWaves + wave) * GPW;
   if constexpr (TT == TT_LM) {
     if (threadIdx.x < kMaxBatch) best[threadIdx.x] = 0;
   }
-  GroupRows G;
-  const v4u* wr[kRT];
-  group_pointers<TT, TILED>(P, l, gc, lane, G, wr);
-  const int nch = (G.K + KC - 1) / KC, ks = gridDim.y, per = (nch + ks - 1) / ks;
+  GroupRows G[GPW];
+  const v4u* wr[RT];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const v4u* w2[kRT];
+    group_pointers<TT, TILED>(P, l, min(g0 + gi, ngroups - 1), lane, G[gi], w2);  // spares repeat the last group
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) wr[gi * kRT + r] = w2[r];
+  }
+  const int nch = (G[0].K + KC - 1) / KC, ks = gridDim.y, per = (nch + ks - 1) / ks;
   const int c0 = blockIdx.y * per, c1 = min(c0 + per, nch);
-  f32x4 acc[kRT][BT];
-  staged_gemm<kRT, BT, KC, TILED>(operand_of<TT>(P), G.K, wr, c0, c1, lds, lane, acc);
+  f32x4 acc[RT][BT];
+  staged_gemm<RT, BT, KC, TILED>(operand_of<TT>(P), G[0].K, wr, c0, c1, lds, lane, acc);
   if (ks == 1) {
-    if (g < ngroups) {
 #pragma unroll
-      for (int t = 0; t < BT; ++t)
+    for (int gi = 0; gi < GPW; ++gi) {
+      if (g0 + gi < ngroups) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = 4 * (lane >> 4) + j, b = t * 16 + (lane & 15);
-          float y[kRT];
+        for (int t = 0; t < BT; ++t)
 #pragma unroll
-          for (int r = 0; r < kRT; ++r) y[r] = acc[r][t][j];
-          if (b < P.B) bgemm_epilogue<TT, kRT>(P, S, l, G, m, b, y, best);
-        }
+          for (int j = 0; j < 4; ++j) {
+            const int m = 4 * (lane >> 4) + j, b = t * 16 + (lane & 15);
+            float y[kRT];
+#pragma unroll
+            for (int r = 0; r < kRT; ++r) y[r] = acc[gi * kRT + r][t][j];
+            if (b < P.B) bgemm_epilogue<TT, kRT>(P, S, l, G[gi], m, b, y, best);
+          }
+      }
     }
     if constexpr (TT == TT_LM) {
       __syncthreads();
@@ -374,15 +389,19 @@ __device__ __forceinline__ void bgemm(const Params& P, const Step& S, int l) {
         __hip_atomic_fetch_max(&P.lm_part[threadIdx.x], best[threadIdx.x], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-  } else if (g < ngroups) {
+  } else {
 #pragma unroll
-    for (int r = 0; r < kRT; ++r)
+    for (int gi = 0; gi < GPW; ++gi) {
+      if (g0 + gi >= ngroups) continue;
 #pragma unroll
-      for (int t = 0; t < BT; ++t)
+      for (int r = 0; r < kRT; ++r)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          P.bpart[part_index(blockIdx.y, ngroups, g, r, 4 * (lane >> 4) + j, t * 16 + (lane & 15), 16 * BT)] =
-              acc[r][t][j];
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            P.bpart[part_index(blockIdx.y, ngroups, g0 + gi, r, 4 * (lane >> 4) + j, t * 16 + (lane & 15), 16 * BT)] =
+                acc[gi * kRT + r][t][j];
+    }
   }
 }
 
@@ -410,16 +429,17 @@ __device__ __forceinline__ void bgemm_finish(const Params& P, const Step& S, int
 // Chunk width by batch tiles: 256 columns at 16 rows, 128 at 32 and 64 (LDS).
 template <int BT> struct BChunk { static constexpr int KC = BT == 1 ? 256 : 128; };
 
-#define MK_BGEMM(name, TT, BT, SUF, TILED)                                                                    \
+#define MK_BGEMM(name, TT, BT, SUF, TILED, GPW)                                                               \
   extern "C" __global__ __launch_bounds__(kBgemmWaves * kWave) void name##_b##BT##SUF(Params P,               \
                                                                                        const Step* Sd,         \
                                                                                        int layer) {            \
     const Step S = ld_const(Sd);                                                                              \
-    bgemm<TT, BT, BChunk<BT>::KC, TILED>(P, S, layer);                                                        \
+    bgemm<TT, BT, BChunk<BT>::KC, TILED, GPW>(P, S, layer);                                                   \
   }
 #define MK_BGEMM_ALL(name, TT)                                                                                \
-  MK_BGEMM(name, TT, 1, , false) MK_BGEMM(name, TT, 2, , false) MK_BGEMM(name, TT, 4, , false)                \
-  MK_BGEMM(name, TT, 1, _t, true) MK_BGEMM(name, TT, 2, _t, true) MK_BGEMM(name, TT, 4, _t, true)
+  MK_BGEMM(name, TT, 1, , false, 1) MK_BGEMM(name, TT, 2, , false, 1) MK_BGEMM(name, TT, 4, , false, 1)       \
+  MK_BGEMM(name, TT, 1, _t, true, 1) MK_BGEMM(name, TT, 2, _t, true, 1) MK_BGEMM(name, TT, 4, _t, true, 1)    \
+  MK_BGEMM(name, TT, 4, _g2, false, 2) MK_BGEMM(name, TT, 4, _t_g2, true, 2)
 MK_BGEMM_ALL(mk_b_qkv, TT_QKV)
 MK_BGEMM_ALL(mk_b_o, TT_O)
 MK_BGEMM_ALL(mk_b_gu, TT_GU)

@@ -33,7 +33,8 @@ MK_OP_DECL(mk_op_lm_x)
 #define MK_BGEMM_DECL(name) extern "C" __global__ void name(Params P, const Step* S, int layer);
 #define MK_BGEMM_DECL_ALL(op)                                                                      \
   MK_BGEMM_DECL(mk_b_##op##_b1) MK_BGEMM_DECL(mk_b_##op##_b2) MK_BGEMM_DECL(mk_b_##op##_b4)       \
-  MK_BGEMM_DECL(mk_b_##op##_b1_t) MK_BGEMM_DECL(mk_b_##op##_b2_t) MK_BGEMM_DECL(mk_b_##op##_b4_t)
+  MK_BGEMM_DECL(mk_b_##op##_b1_t) MK_BGEMM_DECL(mk_b_##op##_b2_t) MK_BGEMM_DECL(mk_b_##op##_b4_t) \
+  MK_BGEMM_DECL(mk_b_##op##_b4_g2) MK_BGEMM_DECL(mk_b_##op##_b4_t_g2)
 MK_BGEMM_DECL_ALL(qkv) MK_BGEMM_DECL_ALL(o) MK_BGEMM_DECL_ALL(gu) MK_BGEMM_DECL_ALL(down) MK_BGEMM_DECL_ALL(lm)
 #undef MK_BGEMM_DECL_ALL
 #undef MK_BGEMM_DECL

@@ -339,8 +339,9 @@ def layer_subset(shape, n_layers):
 
 
 @pytest.mark.parametrize("base,B,P,tiled", [(presets.LLAMA8B, 8, 40, True), (presets.LLAMA70B, 64, 12, True),
-                                            (presets.LLAMA8B, 8, 40, False)],
-                         ids=["llama8b_b8_tiled", "llama70b_b64_tiled", "llama8b_b8_row_major"])
+                                            (presets.LLAMA8B, 8, 40, False), (presets.LLAMA70B, 64, 12, False)],
+                         ids=["llama8b_b8_tiled", "llama70b_b64_tiled", "llama8b_b8_row_major",
+                              "llama70b_b64_row_major"])
 def test_real_layer_shapes_reduced_depth(abi, base, B, P, tiled):
     """The batched workloads' layer shapes (8B at batch 8, 70B at batch 64), two
     layers deep, against the oracle's cache-free forward (teacher-forced with
