@@ -54,14 +54,13 @@ def step_bytes(shape, T, batch=1, kv_bytes=4):
 
 
 def kernel_source_hash():
-    """Hash of the device-code sources and the task-graph builder (everything in
-    csrc/ except api.hip, the host-side launch and handle code): a counter
-    summary taken on other kernel sources is not reported."""
+    """Hash of the sources the batch-1 operator kernels are compiled from
+    (kernels.hip, device.h, mk_internal.h): a counter summary taken on other
+    kernel sources is not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_persistent_megakernel_02_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")) and f != "api.hip":
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in ("device.h", "kernels.hip", "mk_internal.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
