@@ -33,12 +33,11 @@ mk_status fail(mk_status s, const std::string& m) {
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 // Positions per attention split when several sequences share a step: the
-// (sequence, KV head) pairs already widen the grid; 128 positions measured
-// better than 512 at 8 sequences of 4K tokens (more workgroups in flight).
-int batched_split(int max_seq) {
-  (void)max_seq;
-  return 128;
-}
+// (sequence, KV head) pairs already widen the grid.  Up to 1024 positions the
+// whole context is one split (no merge launch; 70B shape, 64 sequences of
+// 640: 58 against 69 + 8 us per layer); longer contexts use 512-position
+// splits (8B shape, 8 sequences of 4K: 5.68 against 5.78 ms/step for 128).
+int batched_split(int max_seq) { return max_seq <= 1024 ? max_seq : 512; }
 
 
 // Batch tiles (16 rows each) of the batched projections: 1, 2 or 4.

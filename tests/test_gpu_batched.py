@@ -250,8 +250,9 @@ def test_batch_rows_are_independent(abi):
 
 
 def test_batched_graph_replay_equals_eager(abi):
-    """The captured step graph, eager launches, and the attention merge run as
-    its own launch all give identical results."""
+    """The captured step graph, eager launches, and the attention merge run by
+    the last split workgroup instead of its own launch all give identical
+    results (4-position splits)."""
     from decode_persistent_megakernel_02_amd import runtime
     shape, B, P = MINI, 5, 6
     w = gen.gen_weights(shape, 4, True)
@@ -259,7 +260,7 @@ def test_batched_graph_replay_equals_eager(abi):
     prompt = torch.from_numpy(gen.tokens(3, presets.TID_PROMPT, 0, B * P, shape.vocab).reshape(B, P)).cuda()
     res = []
     for flags in (0, abi.MK_FLAG_NO_GRAPH, abi.MK_FLAG_FUSED_MERGE):
-        h = runtime.create(shape, dw, P + 8, B, abi.MK_MODE_PER_OP, flags, kv_fp32=False)
+        h = runtime.create(shape, dw, P + 8, B, abi.MK_MODE_PER_OP, flags, attn_split=4, kv_fp32=False)
         out = torch.zeros(B, dtype=torch.int32, device="cuda")
         lg = torch.zeros(B, shape.vocab, dtype=torch.float32, device="cuda")
         abi.mk_prefill(h, prompt, out, lg)
