@@ -98,6 +98,7 @@ SIGNATURES = {
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P], _I32),
     "mk_tile_weights": ([_P, _P, _I64, _I64, _P], _I32),
+    "mk_kv_read": ([_P, _P, _P, _I64], _I32),
     "mk_trace_op": ([_P, _I32, _I32], _I32),
     "mk_t_argmax": ([_P, _I32, _P, _P], _I32),
     "mk_device_info": ([ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
@@ -203,6 +204,13 @@ def mk_kv_view(h: Handle) -> mk_kv_layout:
     out = mk_kv_layout()
     _check(lib.mk_kv_view(h.ptr, ctypes.byref(out)), "mk_kv_view")
     return out
+
+
+def mk_kv_read(h: Handle, k_host, v_host):
+    """Copy the K and V caches into two host numpy arrays of the cache's size
+    (uint16 for bf16 caches, float32 for fp32)."""
+    assert k_host.nbytes == v_host.nbytes and k_host.flags.c_contiguous and v_host.flags.c_contiguous
+    _check(lib.mk_kv_read(h.ptr, k_host.ctypes.data, v_host.ctypes.data, k_host.nbytes), "mk_kv_read")
 
 
 def mk_last_error() -> str:

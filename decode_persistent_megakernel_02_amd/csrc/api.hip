@@ -847,6 +847,18 @@ mk_status mk_kv_view(mk_handle* h, mk_kv_layout* out) {
   return MK_OK;
 }
 
+mk_status mk_kv_read(mk_handle* h, void* k_host, void* v_host, int64_t bytes) {
+  g_err.clear();
+  if (!h || !k_host || !v_host) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  const auto& P = h->P;
+  const int64_t need = (int64_t)P.L * P.B * P.nkv * P.max_seq * P.hd * (P.kv_f32 ? 4 : 2);
+  if (bytes != need) return fail(MK_ERR_INVALID_ARG, "bytes must equal the cache size " + std::to_string(need));
+  HIP_TRY(hipStreamSynchronize(h->stream));
+  HIP_TRY(hipMemcpy(k_host, P.kcache, (size_t)bytes, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(v_host, P.vcache, (size_t)bytes, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
 void mk_destroy(mk_handle* h) {
   if (!h) return;
   (void)hipStreamSynchronize(h->stream);

@@ -173,6 +173,13 @@ mk_status mk_reset(mk_handle* h);
 /* Describe the KV cache (device pointers owned by the handle). */
 mk_status mk_kv_view(mk_handle* h, mk_kv_layout* out);
 
+/* Copy the whole K and V caches (layout of mk_kv_view, every allocated
+ * position) into host memory: `bytes` must equal one cache's size,
+ * n_layers * max_batch * n_kv_heads * max_seq * head_dim * elem_bytes.
+ * Waits for the stream first; synchronous.  For checking a long cache
+ * against the oracle, which then continues from the imported state. */
+mk_status mk_kv_read(mk_handle* h, void* k_host, void* v_host, int64_t bytes);
+
 /* Message of the last failed mk_* call on this thread ("" if none). */
 const char* mk_last_error(void);
 

@@ -67,3 +67,55 @@ def test_full_size_logits_and_tokens(wl_name, kv_fp32):
         r = ref[s] if kv_fp32 else ref_kv[s]
         if D.top2_margin(r) > 5e-2:
             assert got_tok[s] == int(D.greedy(r))
+
+
+def test_batched_workload_long_cache_full_depth():
+    """The 8B-shape batched workload at full depth and context: 8 sequences
+    prefilled with their 4096-token seeded prompts on the GPU (tiled weights,
+    bf16 cache, the bench's launch configuration), then one seeded decode
+    step.  The oracle imports the GPU's bf16 cache through mk_kv_read and
+    runs the same step in fp64 from it, so the comparison covers every layer
+    of the decode step at a 4097-position context (the prefill itself is
+    covered by the other tests)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_persistent_megakernel_02_amd import abi, runtime
+    wl = presets.WORKLOADS["llama8b_b8_kv4096"]
+    shape, B, P = wl.shape, wl.batch, wl.prompt_len
+    max_seq = P + 1
+    prompt = gen.gen_prompt(wl)
+    step_tok = gen.tokens(78, presets.TID_PROMPT, 0, B, shape.vocab).astype(np.int32)
+    print(f"[c4 full depth] generating weights", flush=True)
+    w = gen.gen_weights(shape, wl.weight_seed)
+    dw = runtime.upload_weights(w, tiled=True)
+    h = runtime.create(shape, dw, max_seq, B, abi.MK_MODE_PER_OP, abi.MK_FLAG_TILED_WEIGHTS, kv_fp32=False)
+    out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(B, shape.vocab, dtype=torch.float32, device="cuda")
+    print(f"[c4 full depth] prefill {B} x {P} on the GPU", flush=True)
+    abi.mk_prefill(h, torch.from_numpy(prompt).cuda(), out, lg)
+    abi.mk_synchronize(h)
+    L, nkv, hd = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    kb = np.empty((L, B, nkv, max_seq, hd), dtype=np.uint16)
+    vb = np.empty_like(kb)
+    abi.mk_kv_read(h, kb, vb)
+    tok = torch.from_numpy(step_tok).cuda()
+    abi.mk_decode_step(h, tok, out, lg)
+    abi.mk_synchronize(h)
+    got = lg.cpu().numpy()
+    got_tok = out.cpu().numpy()
+    abi.mk_destroy(h)
+    del dw
+    print(f"[c4 full depth] oracle step from the imported cache", flush=True)
+    ora = D.Decoder(shape, w, B, max_seq, cache_weights=False, kv_bf16=True)
+    ora.K[:, :, :, :P] = D.widen_bf16(kb[:, :, :, :P])
+    ora.V[:, :, :, :P] = D.widen_bf16(vb[:, :, :, :P])
+    del kb, vb
+    ora.length = P
+    ref = ora.step(step_tok)
+    errs = rel_err(got, ref)
+    print(f"[c4 full depth] max rel err vs the bf16-KV oracle {errs.max():.3e}", flush=True)
+    assert np.all(errs <= 2e-2)   # the contract
+    assert np.all(errs <= 5e-3)   # fp32 accumulation order and the hi/lo operand split
+    for b in range(B):
+        if D.top2_margin(ref[b]) > 5e-2:
+            assert got_tok[b] == int(D.greedy(ref[b]))
