@@ -372,10 +372,12 @@ __device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const 
 // A wave's GEMV tasks with two buffers: the next task's first D chunks are in
 // flight while the current task is consumed, so the wave's weight stream
 // does not drain between tasks.  The tasks of a workgroup form a pool (slot p
-// is task slot_task(p)) whose first kWaves slots are the waves' first tasks;
-// after that a wave takes the next free slot from an LDS counter, so a wave
-// that streams faster takes more tasks and the workgroup's waves finish
-// together.  (A
+// is task slot_task(p)) whose first 2 * kWaves slots are the waves' first two
+// tasks (wave w: slots w and kWaves + w, passed in as i0 and i1); after that,
+// and only after the staging barrier that orders the counter's
+// initialisation before its first use, a wave takes the next free slot from
+// an LDS counter, so a wave that streams faster takes more tasks and the
+// workgroup's waves finish together.  (A
 // device-wide counter would also balance across CUs, but thousands of waves
 // contending on one device-scope atomic serialise at the memory side; it made
 // every launch several times slower.)  The R dot products of the wave's j-th
@@ -421,7 +423,7 @@ __device__ __forceinline__ int gemv_next(uint32_t* pool, int j, int count, int l
 }
 
 template <int TT, bool EXACT, class Wait>
-__device__ __forceinline__ int gemv_stream(const Params& P, const OpArgs& A, int count, int i0, int lane,
+__device__ __forceinline__ int gemv_stream(const Params& P, const OpArgs& A, int count, int i0, int i1, int lane,
                                            const float* page, float* res, int* ids, uint32_t* pool, Wait wait) {
   constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
   if (i0 >= count) return 0;
@@ -432,7 +434,7 @@ __device__ __forceinline__ int gemv_stream(const Params& P, const OpArgs& A, int
   gemv_setup<TT>(P, A, op_task<TT>(P, A, i0), gA);
   gemv_prefetch<R, D, EXACT>(bufA, gA, lane);
   float y[R];
-  int a = i0, b = gemv_next(pool, 0, count, lane), j = 0;
+  int a = i0, b = i1, j = 0;
   if (b >= count) {
     wait();
     gemv_run<R, D, EXACT>(bufA, gA, page, lane, y);
@@ -810,7 +812,7 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const O
   // wave index made explicitly uniform: task fields are then scalar values
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
-  if (threadIdx.x == 0) L->ticket = kWaves;  // task pool: the first kWaves slots are the waves' own
+  if (threadIdx.x == 0) L->ticket = 2 * kWaves;  // task pool: the first 2 * kWaves slots are the waves' own
   const Task first = op_task<TT>(P, A, 0);
   // Every wave stages its slice of the input vector and passes the staging
   // barriers exactly once: the loads are issued first, then (in gemv_stream)
@@ -837,7 +839,7 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const O
   };
   if constexpr (TT == TT_QKV || TT == TT_O || TT == TT_GU || TT == TT_DOWN || TT == TT_LM) {
     // scratch_floats = result slots per wave (R per task of this wave)
-    const int i0 = slot_task(wave, count), wid = blockIdx.x * kWaves + wave;
+    const int i0 = slot_task(wave, count), i1 = slot_task(kWaves + wave, count), wid = blockIdx.x * kWaves + wave;
     float* res = scr + wave * scratch_floats;
     int* ids = reinterpret_cast<int*>(res + kMaxTasksPerWave * TaskShape<TT>::R);
     // optional wave timeline (debug): start, input staged, stream done, epilogues done
@@ -849,7 +851,7 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const O
       if (tr && !t1) t1 = clock_now();
       return r;
     };
-    const int n = gemv_stream<TT, EXACT>(P, A, count, i0, lane, page, res, ids, &L->ticket, wait_tr);
+    const int n = gemv_stream<TT, EXACT>(P, A, count, i0, i1, lane, page, res, ids, &L->ticket, wait_tr);
     const uint64_t t2 = tr ? clock_now() : 0;
     wait();
     gemv_finish<TT>(P, S, A, n, lane, res, ids, L);

@@ -81,7 +81,7 @@ mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, do
  * `type` of `layer` log four wall-clock stamps each into the trace buffer
  * read by mk_read_trace: entry 4*w (w = block * waves per block + wave) =
  * (XCC_ID << 60 | HW_ID bits 0..27 << 32) | start (low 32 bits), then three
- * stamps.  GEMV operators (1 QKV, 4 O, 5 GU, 6 DOWN, 7 LM; 4 waves per
+ * stamps.  GEMV operators (1 QKV, 4 O, 5 GU, 6 DOWN, 7 LM; 8 waves per
  * block): input staged, weight stream done, epilogues done.  Attention (2;
  * 4 waves per block, 8 for the single-split kernel): queries staged,
  * positions done, records written.  type < 0 stops logging. */
