@@ -292,15 +292,21 @@ int bgemm_blocks(const Params& P, int type) {
 }
 int bgemm_k(const Params& P, int type) { return type == TT_O ? P.nq * P.hd : type == TT_DOWN ? P.F : P.H; }
 
-// Splits of K for a batched projection: enough workgroups for two per CU,
-// whole activation chunks per split, none empty; the LM head is not split
-// (its argmax runs in the epilogue).
+// Splits of K for a batched projection: enough workgroups for the target
+// below, whole activation chunks per split, none empty; the LM head is not
+// split (its argmax runs in the epilogue).
 int bgemm_splits(const Params& P, int type, int ncu) {
   if (type == TT_LM) return 1;
   const int bt = batch_tiles(P.B), kc = kBChunkCols[bt];
   const int ngx = bgemm_blocks(P, type);
   const int nch = (bgemm_k(P, type) + kc - 1) / kc;
-  int ks = std::max(1, std::min(nch, (2 * ncu + ngx - 1) / ngx));
+  // Workgroups to aim for: two per CU where each weight byte carries the most
+  // matrix-core and LDS work (64 sequences, one row group per wave), one
+  // elsewhere, which halves the partial sums the finishing launch adds.
+  // Measured per operator at the 8B shape with 8 sequences and the 70B shape
+  // with 64; three per CU was slower everywhere.
+  const int target = (bt == 4 && bgemm_gpw(P, type) == 1 ? 2 : 1) * ncu;
+  int ks = std::max(1, std::min(nch, (target + ngx - 1) / ngx));
   const int per = (nch + ks - 1) / ks;
   return (nch + per - 1) / per;
 }
