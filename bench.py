@@ -286,7 +286,13 @@ def main():
     if B == 1:
         gu_kernel = "mk_op_gu_x" if gu_exact else "mk_op_gu"
     else:
-        gu_kernel = f"mk_b_gu_b{1 if B <= 16 else 2 if B <= 32 else 4}" + (" + mk_b_fin_gu" if per_layer > 1 else "")
+        bt = 1 if B <= 16 else 2 if B <= 32 else 4
+        # the library gives a wave two row groups at four batch tiles when the
+        # operator has at least half a CU's worth of groups per CU
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        gpw2 = bt == 4 and -(-shape.ffn // 16) // 8 >= ncu // 2
+        gu_kernel = (f"mk_b_gu_b{bt}" + ("_t" if tiled else "") + ("_g2" if gpw2 else "")
+                     + (" + mk_b_fin_gu" if per_layer > 1 else ""))
     res = {
         "metric": METRIC if wl.name == "llama8b" else f"ms/step decode ({wl.name}, batch {B}), 1 MI355X",
         "value": ms,
