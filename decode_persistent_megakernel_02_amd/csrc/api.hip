@@ -360,7 +360,7 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
     if (ks == 1) return MK_OK;
     int k = ks;
     void* fargs[] = {&Pc, &sp, &layer, &k};
-    return launch(type, bfin_kernel(type), dim3(bgemm_groups(Pc, type)), dim3(256), fargs, 0);
+    return launch(type, bfin_kernel(type), dim3(bgemm_groups(Pc, type)), dim3(16 * Pc.Bp), fargs, 0);  // 16 * Bp <= 1024
   };
   for (int l = 0; l < Pc.L; ++l) {
     MK_TRY(norm(l, 0));

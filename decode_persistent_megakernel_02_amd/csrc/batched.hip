@@ -405,55 +405,40 @@ __device__ __forceinline__ void bgemm(const Params& P, const Step& S, int l) {
   }
 }
 
-// Finishing launch of a split projection: one workgroup of 256 threads per
-// row group.  The splits' partial sums are read in their stored order (batch
-// columns contiguous, so the loads coalesce), all of a split's loads in one
-// round, and added in split order (fixed, as before).  The sums then pass
-// through LDS so that the epilogue runs with consecutive threads on
+// Finishing launch of a split projection: one workgroup per row group, one
+// thread per (row, batch column) of its 16-row tiles (16 * Bp threads).  The
+// splits' partial sums are read in their stored order (batch columns
+// contiguous, so the loads coalesce), four splits' loads at a time, and added
+// in split order (fixed, so results do not depend on timing).  The sums then
+// pass through LDS so that the epilogue runs with consecutive threads on
 // consecutive rows of one batch row, which keeps its stores and residual loads
 // contiguous; with threads along the batch every store went to another row
 // (8 sequences of 4K tokens at the 8B shape: 31 us of finishing launches per
 // layer, 70B shape at 64 sequences: 101 us).
 template <int TT>
 __device__ __forceinline__ void bgemm_finish(const Params& P, const Step& S, int l, int ks) {
-  constexpr int kThreads = 256, kMaxE = 16 * kMaxBatch / kThreads;  // elements per thread
   __shared__ unsigned long long best[kMaxBatch];
   __shared__ float sy[kRT][16][kMaxBatch + 1];  // padded: the row-wise reads hit distinct banks
-  const int g = blockIdx.x, ngroups = group_count<TT>(P), Bp = P.Bp, n = 16 * Bp;
+  const int g = blockIdx.x, ngroups = group_count<TT>(P), Bp = P.Bp, n = 16 * Bp, e = threadIdx.x;
   const GroupRows G = group_rows<TT>(P, l, g);
   const int64_t kstride = (int64_t)ngroups * kRT * n;  // between splits (part_index layout)
-  const float* part = P.bpart + (int64_t)g * kRT * n + threadIdx.x;
-  float y[kMaxE][kRT];
+  const float* part = P.bpart + (int64_t)g * kRT * n + e;
+  float y[kRT];
 #pragma unroll
-  for (int i = 0; i < kMaxE; ++i)
-#pragma unroll
-    for (int r = 0; r < kRT; ++r) y[i][r] = 0.f;
+  for (int r = 0; r < kRT; ++r) y[r] = 0.f;
 #pragma unroll 4
-  for (int kz = 0; kz < ks; ++kz) {
-    const float* p = part + kz * kstride;
+  for (int kz = 0; kz < ks; ++kz)
 #pragma unroll
-    for (int i = 0; i < kMaxE; ++i)
-      if (i * kThreads < n)  // n is a multiple of kThreads: the same for every thread
+    for (int r = 0; r < kRT; ++r) y[r] += part[kz * kstride + r * n];
 #pragma unroll
-        for (int r = 0; r < kRT; ++r) y[i][r] += p[r * n + i * kThreads];
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxE; ++i) {
-    const int e = threadIdx.x + i * kThreads;  // element (m, b) = (e / Bp, e % Bp)
-    if (e < n)
-#pragma unroll
-      for (int r = 0; r < kRT; ++r) sy[r][e / Bp][e % Bp] = y[i][r];
-  }
+  for (int r = 0; r < kRT; ++r) sy[r][e / Bp][e % Bp] = y[r];  // element (m, b) = (e / Bp, e % Bp)
   __syncthreads();
+  const int m = e & 15, b = e >> 4;
+  if (b < P.B) {
+    float v[kRT];
 #pragma unroll
-  for (int i = 0; i < kMaxE; ++i) {
-    const int e = threadIdx.x + i * kThreads, m = e & 15, b = e >> 4;
-    if (e < n && b < P.B) {
-      float v[kRT];
-#pragma unroll
-      for (int r = 0; r < kRT; ++r) v[r] = sy[r][m][b];
-      bgemm_epilogue<TT, kRT>(P, S, l, G, m, b, v, best);
-    }
+    for (int r = 0; r < kRT; ++r) v[r] = sy[r][m][b];
+    bgemm_epilogue<TT, kRT>(P, S, l, G, m, b, v, best);
   }
 }
 
@@ -478,7 +463,7 @@ MK_BGEMM_ALL(mk_b_down, TT_DOWN)
 MK_BGEMM_ALL(mk_b_lm, TT_LM)
 
 #define MK_BFIN(name, TT)                                                                                     \
-  extern "C" __global__ __launch_bounds__(256) void name(Params P, const Step* Sd, int layer, int ks) {        \
+  extern "C" __global__ __launch_bounds__(16 * kMaxBatch) void name(Params P, const Step* Sd, int layer, int ks) { \
     const Step S = ld_const(Sd);                                                                              \
     bgemm_finish<TT>(P, S, layer, ks);                                                                        \
   }
