@@ -36,18 +36,9 @@
 
 namespace mk {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Operand fragments of v_mfma_f32_16x16x32_bf16.  Lane i supplies row (i & 15)
-// of its 16-row tile and the 8 consecutive k of piece (i >> 4) of the 32-wide
-// k-step; the weight tile (A) and the activation tile (B) use the same lane ->
-// k assignment, so products pair matching k.  Result: lane i holds
-// D[4 (i >> 4) + j][i & 15], j < 4 (weight row, batch row).
-__device__ __forceinline__ f32x4 mma16(v4u w, v4u a, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, a), c, 0,
-                                                 0, 0);
-}
+// The matrix-core fragments (mma16, in device.h): the weight tile is the A
+// operand (rows = weight rows), the activation tile the B operand (columns =
+// batch rows); the result holds D[weight row][batch row].
 
 // Rows of one wave's group of two 16-row weight tiles, per operator.
 //   QKV (RT 2): groups [0, nq*hd/32) are query, then key, then value groups.

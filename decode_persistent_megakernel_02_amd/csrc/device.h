@@ -331,6 +331,196 @@ __device__ __forceinline__ void attn_load(const KT* kc, const KT* vc, int p0, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core fragments of v_mfma_f32_16x16x32_bf16.  Lane i supplies row
+// (i & 15) of the 16-row A tile and column (i & 15) of the B tile, each with
+// the 8 consecutive k of piece (i >> 4) of the 32-wide k-step (both operands
+// use the same lane -> k assignment, so products pair matching k).  Result:
+// lane i holds D[4 (i >> 4) + j][i & 15], j < 4.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mma16(v4u a, v4u b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// Reductions over the 16 lanes of a DPP row (every lane gets the result).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+
+// ---- attention scores on the matrix cores (bf16 cache, head_dim 128) --------
+// The query heads of a KV group are the rows of the A operand (heads past G
+// are zero rows; G <= kMaxGqa = 8 keeps them in lanes 0-31 of the result) and
+// a block's 16 positions the columns of the B operand, so the block's scores
+// S = Q K^T take 8 matrix-core instructions: the fp32 queries enter as a bf16
+// pair hi = bf16(q), lo = bf16(q - hi) (16 significant bits), each multiplied
+// with the exact bf16 keys, fp32 accumulation.  The k index is permuted so that
+// a lane reads 64 contiguous bytes of its position's key row: in k-step ks
+// lane i holds dims 32 (i >> 4) + 8 ks .. + 7; the query fragments use the same
+// permutation.  Result: lane i holds S[head 4 (i >> 4) + j][position i & 15].
+// The softmax runs on that layout (row reductions over 16 lanes); the values
+// are accumulated as in attn_compute, each lane owning 2 dims of every head.
+struct AttnQFrag {
+  v4u hi[4], lo[4];
+};
+
+__device__ __forceinline__ uint32_t bf_pack(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+
+// This lane's query fragments from the rotated queries in LDS (qs[G][128]).
+__device__ __forceinline__ void attn_q_frags(const float* qs, int G, int lane, AttnQFrag& f) {
+  const int r = lane & 15, d0 = 32 * (lane >> 4);
+  const float* qr = qs + min(r, G - 1) * 128 + d0;  // rows past G read a valid row and are zeroed
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const float4 a = *reinterpret_cast<const float4*>(qr + 8 * ks);
+    const float4 c = *reinterpret_cast<const float4*>(qr + 8 * ks + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    uint16_t h[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = r < G ? v[e] : 0.f;
+      h[e] = f2bf(x);
+      lo[e] = f2bf(x - bf1(h[e]));
+    }
+    f.hi[ks] = v4u{bf_pack(h[0], h[1]), bf_pack(h[2], h[3]), bf_pack(h[4], h[5]), bf_pack(h[6], h[7])};
+    f.lo[ks] = v4u{bf_pack(lo[0], lo[1]), bf_pack(lo[2], lo[3]), bf_pack(lo[4], lo[5]), bf_pack(lo[6], lo[7])};
+  }
+}
+
+// K and V loads of the block [p0, p0 + 16) for the matrix-core scores: lane i
+// reads dims 32 (i >> 4) .. + 31 of position p0 + (i & 15)'s key row; values as
+// attn_load.  Positions at or past p1 read position p1 - 1 (masked later).
+__device__ __forceinline__ void attn_load_mf(const uint16_t* kc, const uint16_t* vc, int p0, int p1, int lane,
+                                             AttnBuf<128, uint16_t>& bf) {
+  using Gm = AttnGeom<128, uint16_t>;
+  const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)min(p0 + (lane & 15), p1 - 1) * 128 + 32 * (lane >> 4));
+#pragma unroll
+  for (int i = 0; i < Gm::KV16; ++i) bf.kr[i] = ld_g(krow + i);
+#pragma unroll
+  for (int j = 0; j < Gm::NP; ++j) bf.vr[j][0] = ((gu32_ptr)(vc + (int64_t)min(p0 + j, p1 - 1) * 128 + lane * 2))[0];
+}
+
+// Running state of the matrix-core path: m and l of this lane's row of heads
+// (4 (lane >> 4) + j), the outputs of every head for this lane's 2 dims.
+template <int GQ>
+struct AttnStateMf {
+  static constexpr int GM = GqaHeads<GQ>::MAX;
+  float m[4], l[4], o[GM][2];
+  __device__ void init() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) o[h][0] = o[h][1] = 0.f;
+  }
+};
+
+// Online-softmax update with the block [p0, min(p0 + 16, p1)) held in bf.
+template <int GQ>
+__device__ __forceinline__ void attn_compute_mf(const AttnBuf<128, uint16_t>& bf, const AttnQFrag& qf, int p0, int p1,
+                                                int G, int lane, AttnStateMf<GQ>& st) {
+  using Hs = GqaHeads<GQ>;
+  constexpr int NP = 16, GM = Hs::MAX;
+  const int np = min(NP, p1 - p0), pos = lane & 15, row0 = 4 * (lane >> 4);
+  const float scale = 1.0f / sqrtf(128.0f);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    acc = mma16(qf.hi[ks], bf.kr[ks], acc);
+    acc = mma16(qf.lo[ks], bf.kr[ks], acc);
+  }
+  float alpha[4], p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool valid = pos < np && row0 + j < G;
+    const float s = valid ? acc[j] * scale : -INFINITY;
+    const float mn = fmaxf(st.m[j], row16_max(s));
+    alpha[j] = mn == -INFINITY ? 1.f : __expf(st.m[j] - mn);  // 0 on a head's first block; rows past G stay empty
+    p[j] = valid ? __expf(s - mn) : 0.f;
+    st.l[j] = st.l[j] * alpha[j] + row16_sum(p[j]);
+    st.m[j] = mn;
+  }
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (Hs::has(h, G)) {
+      const float a = rd_lane(alpha[h & 3], 16 * (h >> 2));
+      st.o[h][0] *= a;
+      st.o[h][1] *= a;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    if (j < np) {
+      const float v0 = bf_lo(bf.vr[j][0]), v1 = bf_hi(bf.vr[j][0]);
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (Hs::has(h, G)) {
+          const float w = rd_lane(p[h & 3], 16 * (h >> 2) + j);
+          st.o[h][0] = fmaf(w, v0, st.o[h][0]);
+          st.o[h][1] = fmaf(w, v1, st.o[h][1]);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// attn_pipeline for the matrix-core path: the wave's blocks b, b + stride, ...
+// (below p1), the first already loaded into A.
+template <int GQ>
+__device__ __forceinline__ void attn_pipeline_mf(AttnBuf<128, uint16_t>& A, AttnBuf<128, uint16_t>& B,
+                                                 const AttnQFrag& qf, const uint16_t* kc, const uint16_t* vc, int b,
+                                                 int p1, int stride, int G, int lane, AttnStateMf<GQ>& st) {
+  for (;;) {
+    int n = b + stride;
+    if (n >= p1) {
+      attn_compute_mf<GQ>(A, qf, b, p1, G, lane, st);
+      return;
+    }
+    attn_load_mf(kc, vc, n, p1, lane, B);
+    attn_compute_mf<GQ>(A, qf, b, p1, G, lane, st);
+    b = n;
+    n = b + stride;
+    if (n >= p1) {
+      attn_compute_mf<GQ>(B, qf, b, p1, G, lane, st);
+      return;
+    }
+    attn_load_mf(kc, vc, n, p1, lane, A);
+    attn_compute_mf<GQ>(B, qf, b, p1, G, lane, st);
+    b = n;
+  }
+}
+
+// Writes a wave's matrix-core state as G records of (o[128], m, l).
+template <int GQ>
+__device__ __forceinline__ void attn_store_state_mf(const AttnStateMf<GQ>& st, int G, float* out, int lane) {
+#pragma unroll
+  for (int h = 0; h < GqaHeads<GQ>::MAX; ++h) {
+    if (GqaHeads<GQ>::has(h, G)) {
+      float* oh = out + h * (128 + 2);
+      oh[lane * 2] = st.o[h][0];
+      oh[lane * 2 + 1] = st.o[h][1];
+      const float m = rd_lane(st.m[h & 3], 16 * (h >> 2)), l = rd_lane(st.l[h & 3], 16 * (h >> 2));
+      if (lane == 0) {
+        oh[128] = m;
+        oh[129] = l;
+      }
+    }
+  }
+}
+
 // Online-softmax update with the block [p0, min(p0 + NP, p1)) held in bf.
 // qs: LDS [G][HD] (rotated queries).  The weight of position j reaches every
 // lane by a read of lane j * LPP into a scalar register.

@@ -922,9 +922,14 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
   float qv[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) qv[i] = q[min((int)threadIdx.x + i * NW * kWave, G * HD - 1)];
+  // bf16 cache at head_dim 128: scores on the matrix cores (attn_compute_mf)
+  constexpr bool MF = HD == 128 && sizeof(KT) == 2;
   const int b0 = p0 + wave * Gm::NP;
   AttnBuf<HD, KT> A, B;
-  if (b0 < p1) attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
+  if (b0 < p1) {
+    if constexpr (MF) attn_load_mf(kc, vc, b0, p1, lane, A);
+    else attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
+  }
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int idx = threadIdx.x + i * NW * kWave;
@@ -932,11 +937,21 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
   }
   __syncthreads();
   if (stamps) stamps[1] = clock_now();
-  AttnState<HD, GQ> st;
-  st.init();
-  if (b0 < p1) attn_pipeline<HD, KT, GQ>(A, B, qs, kc, vc, b0, p1, NW * Gm::NP, G, lane, st);
-  if (stamps) stamps[2] = clock_now();
-  attn_store_state<HD, GQ>(st, G, recs + wave * G * (HD + 2), lane);
+  if constexpr (MF) {
+    AttnQFrag qf;
+    attn_q_frags(qs, G, lane, qf);
+    AttnStateMf<GQ> st;
+    st.init();
+    if (b0 < p1) attn_pipeline_mf<GQ>(A, B, qf, kc, vc, b0, p1, NW * Gm::NP, G, lane, st);
+    if (stamps) stamps[2] = clock_now();
+    attn_store_state_mf<GQ>(st, G, recs + wave * G * (HD + 2), lane);
+  } else {
+    AttnState<HD, GQ> st;
+    st.init();
+    if (b0 < p1) attn_pipeline<HD, KT, GQ>(A, B, qs, kc, vc, b0, p1, NW * Gm::NP, G, lane, st);
+    if (stamps) stamps[2] = clock_now();
+    attn_store_state<HD, GQ>(st, G, recs + wave * G * (HD + 2), lane);
+  }
   __syncthreads();
   for (int h = wave; h < G; h += NW) {
     // merge the waves' records of head h
