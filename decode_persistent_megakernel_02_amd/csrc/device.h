@@ -428,9 +428,15 @@ struct AttnStateMf {
 };
 
 // Online-softmax update with the block [p0, min(p0 + 16, p1)) held in bf.
+// The weight of (head h, position j) reaches every lane for the values by a
+// read of lane 16 (h >> 2) + j; with 8 heads those 128 lane reads cost more
+// than passing the weights through pw, this wave's LDS scratch of 16 * 8
+// floats ([position][head], read back as broadcasts): 8 sequences at the 8B
+// shape (4 heads) 35.4 us per layer with lane reads, 39.5 through LDS; 64 at
+// the 70B shape (8 heads) 46.4 and 43.2.
 template <int GQ>
 __device__ __forceinline__ void attn_compute_mf(const AttnBuf<128, uint16_t>& bf, const AttnQFrag& qf, int p0, int p1,
-                                                int G, int lane, AttnStateMf<GQ>& st) {
+                                                int G, int lane, float* pw, AttnStateMf<GQ>& st) {
   using Hs = GqaHeads<GQ>;
   constexpr int NP = 16, GM = Hs::MAX;
   const int np = min(NP, p1 - p0), pos = lane & 15, row0 = 4 * (lane >> 4);
@@ -451,6 +457,8 @@ __device__ __forceinline__ void attn_compute_mf(const AttnBuf<128, uint16_t>& bf
     p[j] = valid ? __expf(s - mn) : 0.f;
     st.l[j] = st.l[j] * alpha[j] + row16_sum(p[j]);
     st.m[j] = mn;
+    if constexpr (GQ == 8)
+      if (row0 + j < GM) pw[pos * GM + row0 + j] = p[j];
   }
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
@@ -460,21 +468,31 @@ __device__ __forceinline__ void attn_compute_mf(const AttnBuf<128, uint16_t>& bf
       st.o[h][1] *= a;
     }
   }
+  __builtin_amdgcn_wave_barrier();  // the weights are in pw (one wave: its LDS operations stay in order)
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     if (j < np) {
       const float v0 = bf_lo(bf.vr[j][0]), v1 = bf_hi(bf.vr[j][0]);
+      float w[GM];
+      if constexpr (GQ == 8) {  // G = 8: the wave's records start 16-byte aligned
+        const float4 a = *reinterpret_cast<const float4*>(pw + j * 8);
+        const float4 c = *reinterpret_cast<const float4*>(pw + j * 8 + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
+      } else {
+#pragma unroll
+        for (int h = 0; h < GM; ++h) w[h] = rd_lane(p[h & 3], 16 * (h >> 2) + j);
+      }
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (Hs::has(h, G)) {
-          const float w = rd_lane(p[h & 3], 16 * (h >> 2) + j);
-          st.o[h][0] = fmaf(w, v0, st.o[h][0]);
-          st.o[h][1] = fmaf(w, v1, st.o[h][1]);
+          st.o[h][0] = fmaf(w[h], v0, st.o[h][0]);
+          st.o[h][1] = fmaf(w[h], v1, st.o[h][1]);
         }
       }
     }
   }
-  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_wave_barrier();  // the next block's writes to pw come after these reads
 }
 
 // attn_pipeline for the matrix-core path: the wave's blocks b, b + stride, ...
@@ -482,23 +500,24 @@ __device__ __forceinline__ void attn_compute_mf(const AttnBuf<128, uint16_t>& bf
 template <int GQ>
 __device__ __forceinline__ void attn_pipeline_mf(AttnBuf<128, uint16_t>& A, AttnBuf<128, uint16_t>& B,
                                                  const AttnQFrag& qf, const uint16_t* kc, const uint16_t* vc, int b,
-                                                 int p1, int stride, int G, int lane, AttnStateMf<GQ>& st) {
+                                                 int p1, int stride, int G, int lane, float* pw,
+                                                 AttnStateMf<GQ>& st) {
   for (;;) {
     int n = b + stride;
     if (n >= p1) {
-      attn_compute_mf<GQ>(A, qf, b, p1, G, lane, st);
+      attn_compute_mf<GQ>(A, qf, b, p1, G, lane, pw, st);
       return;
     }
     attn_load_mf(kc, vc, n, p1, lane, B);
-    attn_compute_mf<GQ>(A, qf, b, p1, G, lane, st);
+    attn_compute_mf<GQ>(A, qf, b, p1, G, lane, pw, st);
     b = n;
     n = b + stride;
     if (n >= p1) {
-      attn_compute_mf<GQ>(B, qf, b, p1, G, lane, st);
+      attn_compute_mf<GQ>(B, qf, b, p1, G, lane, pw, st);
       return;
     }
     attn_load_mf(kc, vc, n, p1, lane, A);
-    attn_compute_mf<GQ>(B, qf, b, p1, G, lane, st);
+    attn_compute_mf<GQ>(B, qf, b, p1, G, lane, pw, st);
     b = n;
   }
 }

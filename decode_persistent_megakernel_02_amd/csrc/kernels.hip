@@ -942,7 +942,10 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
     attn_q_frags(qs, G, lane, qf);
     AttnStateMf<GQ> st;
     st.init();
-    if (b0 < p1) attn_pipeline_mf<GQ>(A, B, qf, kc, vc, b0, p1, NW * Gm::NP, G, lane, st);
+    // the wave's record slot holds the position weights until the records are written
+    static_assert(16 * GqaHeads<GQ>::MAX <= HD + 2, "position weights fit the wave's first record");
+    float* pw = recs + wave * G * (HD + 2);
+    if (b0 < p1) attn_pipeline_mf<GQ>(A, B, qf, kc, vc, b0, p1, NW * Gm::NP, G, lane, pw, st);
     if (stamps) stamps[2] = clock_now();
     attn_store_state_mf<GQ>(st, G, recs + wave * G * (HD + 2), lane);
   } else {
