@@ -18,7 +18,8 @@ import torch
 from oracle import decoder as D
 from synth import gen, presets
 from tests.gpu_util import rel_err
-from tests.shapes import MINI, MINI_G8, MINI_TIED, MINI_TILE, MINI_TILE_G8, MINI_TILE_TIED
+from tests.shapes import (MINI, MINI_G8, MINI_HD128_G1, MINI_HD128_G2, MINI_TIED, MINI_TILE, MINI_TILE_G8,
+                          MINI_TILE_TIED)
 
 pytestmark = pytest.mark.gpu
 
@@ -189,7 +190,8 @@ def run_teacher_forced(case, prompt, steps, seed=99):
     return errs
 
 
-@pytest.mark.parametrize("shape,B", [(MINI, 2), (MINI, 8), (MINI_TIED, 17), (MINI_G8, 33), (presets.TINY, 64)],
+@pytest.mark.parametrize("shape,B", [(MINI, 2), (MINI, 8), (MINI_TIED, 17), (MINI_G8, 33), (presets.TINY, 64),
+                                     (MINI_HD128_G1, 5), (MINI_HD128_G2, 3)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_batched_teacher_forced(abi, shape, B):
     prompt = gen.tokens(500 + B, presets.TID_PROMPT, 0, B * 9, shape.vocab).reshape(B, 9)
@@ -209,6 +211,18 @@ def test_batched_many_splits(abi):
     errs = run_teacher_forced(case, prompt, steps)
     case.close()
     print(f"many splits: vs bf16-KV oracle {max(e[1] for e in errs):.2e}", flush=True)
+
+
+def test_batched_many_splits_matrix_core_scores(abi):
+    """The matrix-core score path (bf16 cache, head_dim 128) over many
+    16-position splits: one block per split, three idle waves in each
+    workgroup, a ragged last split."""
+    B, P, steps = 3, 53, 4
+    prompt = gen.tokens(73, presets.TID_PROMPT, 0, B * P, MINI_HD128_G2.vocab).reshape(B, P)
+    case = BatchCase(abi, MINI_HD128_G2, B, P + steps, seed=5, attn_split=16)
+    errs = run_teacher_forced(case, prompt, steps)
+    case.close()
+    print(f"many splits, matrix-core scores: vs bf16-KV oracle {max(e[1] for e in errs):.2e}", flush=True)
 
 
 def test_batched_free_running_matches_oracle(abi):
