@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mk_internal.h"
 
 namespace mk {
@@ -358,18 +360,33 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + dpp_f<0x140>(v);
 }
 
-// ---- attention scores on the matrix cores (bf16 cache, head_dim 128) --------
-// The query heads of a KV group are the rows of the A operand (heads past G
-// are zero rows; G <= kMaxGqa = 8 keeps them in lanes 0-31 of the result) and
-// a block's 16 positions the columns of the B operand, so the block's scores
-// S = Q K^T take 8 matrix-core instructions: the fp32 queries enter as a bf16
-// pair hi = bf16(q), lo = bf16(q - hi) (16 significant bits), each multiplied
-// with the exact bf16 keys, fp32 accumulation.  The k index is permuted so that
-// a lane reads 64 contiguous bytes of its position's key row: in k-step ks
-// lane i holds dims 32 (i >> 4) + 8 ks .. + 7; the query fragments use the same
-// permutation.  Result: lane i holds S[head 4 (i >> 4) + j][position i & 15].
-// The softmax runs on that layout (row reductions over 16 lanes); the values
-// are accumulated as in attn_compute, each lane owning 2 dims of every head.
+// ---- attention on the matrix cores (bf16 cache, head_dim 128) ----------------
+// Scores: the query heads of a KV group are the rows of the A operand of
+// v_mfma_f32_16x16x32_bf16 (heads past G are zero rows; G <= kMaxGqa = 8
+// keeps them in lanes 0-31 of the result) and a block's 16 positions the
+// columns of the B operand, so S = Q K^T for the block is 8 instructions: the
+// fp32 queries enter as a bf16 pair hi = bf16(q), lo = bf16(q - hi) (16
+// significant bits), each multiplied with the exact bf16 keys, fp32
+// accumulation.  The k index is permuted so that a lane reads 64 contiguous
+// bytes of its position's key row: in k-step ks lane i holds dims
+// 32 (i >> 4) + 8 ks .. + 7; the query fragments use the same permutation.
+// Result: lane i holds S[head 4 (i >> 4) + j][position i & 15], j < 4.
+// The online softmax runs on that layout (row reductions over 16 lanes), so
+// a lane keeps m and l of heads 4 (i >> 4) + j.
+// Values: O += P V is 8 instructions of v_mfma_f32_16x16x16_bf16 per operand
+// half, one per output tile t: A = P (rows = heads, k = the block's positions,
+// passed through LDS from the score layout, again as a bf16 hi/lo pair), B =
+// the values with the output dims permuted so that a lane's operands come
+// from one 16-byte load: column c of tile t is dim 8 c + t, and lane i loads
+// dims 8 (i & 15) .. + 7 of positions 4 (i >> 4) .. + 3, one vector each.
+// Result: lane i holds O[head 4 (i >> 4) + j][dim 8 (i & 15) + t] in tile t,
+// scaled by the same lane's softmax corrections.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma16k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 struct AttnQFrag {
   v4u hi[4], lo[4];
 };
@@ -397,25 +414,31 @@ __device__ __forceinline__ void attn_q_frags(const float* qs, int G, int lane, A
   }
 }
 
-// K and V loads of the block [p0, p0 + 16) for the matrix-core scores: lane i
-// reads dims 32 (i >> 4) .. + 31 of position p0 + (i & 15)'s key row; values as
-// attn_load.  Positions at or past p1 read position p1 - 1 (masked later).
+// One block of the matrix-core path in registers: kr, dims 32 (lane >> 4) ..
+// + 31 of position p0 + (lane & 15)'s key row; vk[i], dims 8 (lane & 15) .. + 7
+// of position p0 + 4 (lane >> 4) + i's value row.
+struct AttnBufMf {
+  v4u kr[4], vk[4];
+};
+
+// Issues the block's loads; positions at or past p1 read position p1 - 1
+// (their weights are zero).
 __device__ __forceinline__ void attn_load_mf(const uint16_t* kc, const uint16_t* vc, int p0, int p1, int lane,
-                                             AttnBuf<128, uint16_t>& bf) {
-  using Gm = AttnGeom<128, uint16_t>;
+                                             AttnBufMf& bf) {
   const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)min(p0 + (lane & 15), p1 - 1) * 128 + 32 * (lane >> 4));
 #pragma unroll
-  for (int i = 0; i < Gm::KV16; ++i) bf.kr[i] = ld_g(krow + i);
+  for (int i = 0; i < 4; ++i) bf.kr[i] = ld_g(krow + i);
 #pragma unroll
-  for (int j = 0; j < Gm::NP; ++j) bf.vr[j][0] = ((gu32_ptr)(vc + (int64_t)min(p0 + j, p1 - 1) * 128 + lane * 2))[0];
+  for (int i = 0; i < 4; ++i)
+    bf.vk[i] = ld_g(reinterpret_cast<const v4u*>(vc + (int64_t)min(p0 + 4 * (lane >> 4) + i, p1 - 1) * 128 +
+                                                 8 * (lane & 15)));
 }
 
-// Running state of the matrix-core path: m and l of this lane's row of heads
-// (4 (lane >> 4) + j), the outputs of every head for this lane's 2 dims.
-template <int GQ>
+// Running state: m and l of this lane's heads 4 (lane >> 4) + j, and the
+// output tiles (see above).
 struct AttnStateMf {
-  static constexpr int GM = GqaHeads<GQ>::MAX;
-  float m[4], l[4], o[GM][2];
+  float m[4], l[4];
+  f32x4 o[8];
   __device__ void init() {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -423,23 +446,24 @@ struct AttnStateMf {
       l[j] = 0.f;
     }
 #pragma unroll
-    for (int h = 0; h < GM; ++h) o[h][0] = o[h][1] = 0.f;
+    for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Elements E of two bf16 vectors as one 32-bit word (a's in the low half).
+template <int E>
+__device__ __forceinline__ uint32_t bf_pair(const v4u& a, const v4u& b) {
+  const uint32_t x = a[E >> 1], y = b[E >> 1];
+  return E & 1 ? (x >> 16) | (y & 0xFFFF0000u) : (x & 0xFFFFu) | (y << 16);
+}
+
 // Online-softmax update with the block [p0, min(p0 + 16, p1)) held in bf.
-// The weight of (head h, position j) reaches every lane for the values by a
-// read of lane 16 (h >> 2) + j; with 8 heads those 128 lane reads cost more
-// than passing the weights through pw, this wave's LDS scratch of 16 * 8
-// floats ([position][head], read back as broadcasts): 8 sequences at the 8B
-// shape (4 heads) 35.4 us per layer with lane reads, 39.5 through LDS; 64 at
-// the 70B shape (8 heads) 46.4 and 43.2.
-template <int GQ>
-__device__ __forceinline__ void attn_compute_mf(const AttnBuf<128, uint16_t>& bf, const AttnQFrag& qf, int p0, int p1,
-                                                int G, int lane, float* pw, AttnStateMf<GQ>& st) {
-  using Hs = GqaHeads<GQ>;
-  constexpr int NP = 16, GM = Hs::MAX;
-  const int np = min(NP, p1 - p0), pos = lane & 15, row0 = 4 * (lane >> 4);
+// pw: this wave's LDS scratch for the weights, [8 heads][16 positions].
+__device__ __forceinline__ void attn_compute_mf(const AttnBufMf& bf, const AttnQFrag& qf, int p0, int p1, int G,
+                                                int lane, float* pw, AttnStateMf& st) {
+  const int np = min(16, p1 - p0), pos = lane & 15, row0 = 4 * (lane >> 4);
   const float scale = 1.0f / sqrtf(128.0f);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -447,94 +471,92 @@ __device__ __forceinline__ void attn_compute_mf(const AttnBuf<128, uint16_t>& bf
     acc = mma16(qf.hi[ks], bf.kr[ks], acc);
     acc = mma16(qf.lo[ks], bf.kr[ks], acc);
   }
-  float alpha[4], p[4];
+  float alpha[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const bool valid = pos < np && row0 + j < G;
     const float s = valid ? acc[j] * scale : -INFINITY;
     const float mn = fmaxf(st.m[j], row16_max(s));
     alpha[j] = mn == -INFINITY ? 1.f : __expf(st.m[j] - mn);  // 0 on a head's first block; rows past G stay empty
-    p[j] = valid ? __expf(s - mn) : 0.f;
-    st.l[j] = st.l[j] * alpha[j] + row16_sum(p[j]);
+    const float p = valid ? __expf(s - mn) : 0.f;
+    st.l[j] = st.l[j] * alpha[j] + row16_sum(p);
     st.m[j] = mn;
-    if constexpr (GQ == 8)
-      if (row0 + j < GM) pw[pos * GM + row0 + j] = p[j];
+    if (row0 + j < G) pw[(row0 + j) * 16 + pos] = p;
   }
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    if (Hs::has(h, G)) {
-      const float a = rd_lane(alpha[h & 3], 16 * (h >> 2));
-      st.o[h][0] *= a;
-      st.o[h][1] *= a;
-    }
-  }
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.o[t][j] *= alpha[j];
   __builtin_amdgcn_wave_barrier();  // the weights are in pw (one wave: its LDS operations stay in order)
+  // A operand: weights of head (lane & 15) at positions 4 (lane >> 4) .. + 3
+  const int hr = lane & 15;
+  const float4 w = *reinterpret_cast<const float4*>(pw + min(hr, G - 1) * 16 + 4 * (lane >> 4));
+  const float wv[4] = {w.x, w.y, w.z, w.w};
+  uint16_t wh[4], wl[4];
 #pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    if (j < np) {
-      const float v0 = bf_lo(bf.vr[j][0]), v1 = bf_hi(bf.vr[j][0]);
-      float w[GM];
-      if constexpr (GQ == 8) {  // G = 8: the wave's records start 16-byte aligned
-        const float4 a = *reinterpret_cast<const float4*>(pw + j * 8);
-        const float4 c = *reinterpret_cast<const float4*>(pw + j * 8 + 4);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
-      } else {
-#pragma unroll
-        for (int h = 0; h < GM; ++h) w[h] = rd_lane(p[h & 3], 16 * (h >> 2) + j);
-      }
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (Hs::has(h, G)) {
-          st.o[h][0] = fmaf(w[h], v0, st.o[h][0]);
-          st.o[h][1] = fmaf(w[h], v1, st.o[h][1]);
-        }
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    const float x = hr < G ? wv[i] : 0.f;
+    wh[i] = f2bf(x);
+    wl[i] = f2bf(x - bf1(wh[i]));
   }
+  const s16x4 ah = __builtin_bit_cast(s16x4, u32x2{bf_pack(wh[0], wh[1]), bf_pack(wh[2], wh[3])});
+  const s16x4 al = __builtin_bit_cast(s16x4, u32x2{bf_pack(wl[0], wl[1]), bf_pack(wl[2], wl[3])});
+  auto tile = [&](auto tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(tc)::value;
+    const s16x4 b = __builtin_bit_cast(s16x4, u32x2{bf_pair<t>(bf.vk[0], bf.vk[1]), bf_pair<t>(bf.vk[2], bf.vk[3])});
+    st.o[t] = mma16k16(ah, b, st.o[t]);
+    st.o[t] = mma16k16(al, b, st.o[t]);
+  };
+  tile(std::integral_constant<int, 0>{});
+  tile(std::integral_constant<int, 1>{});
+  tile(std::integral_constant<int, 2>{});
+  tile(std::integral_constant<int, 3>{});
+  tile(std::integral_constant<int, 4>{});
+  tile(std::integral_constant<int, 5>{});
+  tile(std::integral_constant<int, 6>{});
+  tile(std::integral_constant<int, 7>{});
   __builtin_amdgcn_wave_barrier();  // the next block's writes to pw come after these reads
 }
 
 // attn_pipeline for the matrix-core path: the wave's blocks b, b + stride, ...
 // (below p1), the first already loaded into A.
-template <int GQ>
-__device__ __forceinline__ void attn_pipeline_mf(AttnBuf<128, uint16_t>& A, AttnBuf<128, uint16_t>& B,
-                                                 const AttnQFrag& qf, const uint16_t* kc, const uint16_t* vc, int b,
-                                                 int p1, int stride, int G, int lane, float* pw,
-                                                 AttnStateMf<GQ>& st) {
+__device__ __forceinline__ void attn_pipeline_mf(AttnBufMf& A, AttnBufMf& B, const AttnQFrag& qf, const uint16_t* kc,
+                                                 const uint16_t* vc, int b, int p1, int stride, int G, int lane,
+                                                 float* pw, AttnStateMf& st) {
   for (;;) {
     int n = b + stride;
     if (n >= p1) {
-      attn_compute_mf<GQ>(A, qf, b, p1, G, lane, pw, st);
+      attn_compute_mf(A, qf, b, p1, G, lane, pw, st);
       return;
     }
     attn_load_mf(kc, vc, n, p1, lane, B);
-    attn_compute_mf<GQ>(A, qf, b, p1, G, lane, pw, st);
+    attn_compute_mf(A, qf, b, p1, G, lane, pw, st);
     b = n;
     n = b + stride;
     if (n >= p1) {
-      attn_compute_mf<GQ>(B, qf, b, p1, G, lane, pw, st);
+      attn_compute_mf(B, qf, b, p1, G, lane, pw, st);
       return;
     }
     attn_load_mf(kc, vc, n, p1, lane, A);
-    attn_compute_mf<GQ>(B, qf, b, p1, G, lane, pw, st);
+    attn_compute_mf(B, qf, b, p1, G, lane, pw, st);
     b = n;
   }
 }
 
 // Writes a wave's matrix-core state as G records of (o[128], m, l).
-template <int GQ>
-__device__ __forceinline__ void attn_store_state_mf(const AttnStateMf<GQ>& st, int G, float* out, int lane) {
+__device__ __forceinline__ void attn_store_state_mf(const AttnStateMf& st, int G, float* out, int lane) {
+  const int c = lane & 15, row0 = 4 * (lane >> 4);
 #pragma unroll
-  for (int h = 0; h < GqaHeads<GQ>::MAX; ++h) {
-    if (GqaHeads<GQ>::has(h, G)) {
+  for (int j = 0; j < 4; ++j) {
+    const int h = row0 + j;
+    if (h < G) {
       float* oh = out + h * (128 + 2);
-      oh[lane * 2] = st.o[h][0];
-      oh[lane * 2 + 1] = st.o[h][1];
-      const float m = rd_lane(st.m[h & 3], 16 * (h >> 2)), l = rd_lane(st.l[h & 3], 16 * (h >> 2));
-      if (lane == 0) {
-        oh[128] = m;
-        oh[129] = l;
+#pragma unroll
+      for (int t = 0; t < 8; t += 2)  // records are 8-byte aligned (130 floats each)
+        *reinterpret_cast<float2*>(oh + 8 * c + t) = make_float2(st.o[t][j], st.o[t + 1][j]);
+      if (c == 0) {
+        oh[128] = st.m[j];
+        oh[129] = st.l[j];
       }
     }
   }

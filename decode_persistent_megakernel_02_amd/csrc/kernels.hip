@@ -15,6 +15,8 @@
 // way), and advances the frontier.  A finished task bumps a per-CU LDS counter;
 // the last task of a run of same-event tasks releases at agent scope and adds
 // one to the global event counter.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -925,7 +927,7 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
   // bf16 cache at head_dim 128: scores on the matrix cores (attn_compute_mf)
   constexpr bool MF = HD == 128 && sizeof(KT) == 2;
   const int b0 = p0 + wave * Gm::NP;
-  AttnBuf<HD, KT> A, B;
+  std::conditional_t<MF, AttnBufMf, AttnBuf<HD, KT>> A, B;
   if (b0 < p1) {
     if constexpr (MF) attn_load_mf(kc, vc, b0, p1, lane, A);
     else attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
@@ -940,14 +942,15 @@ __device__ __forceinline__ void attn_split_wg(const Params& P, const Step& S, in
   if constexpr (MF) {
     AttnQFrag qf;
     attn_q_frags(qs, G, lane, qf);
-    AttnStateMf<GQ> st;
+    AttnStateMf st;
     st.init();
-    // the wave's record slot holds the position weights until the records are written
-    static_assert(16 * GqaHeads<GQ>::MAX <= HD + 2, "position weights fit the wave's first record");
-    float* pw = recs + wave * G * (HD + 2);
-    if (b0 < p1) attn_pipeline_mf<GQ>(A, B, qf, kc, vc, b0, p1, NW * Gm::NP, G, lane, pw, st);
+    // The wave's record slot (G * 130 floats, an even offset) holds the
+    // weights ([G][16], 16-byte aligned) until the records are written.
+    static_assert(16 * kMaxGqa + 2 <= HD + 2, "the weights fit the wave's records");
+    float* pw = recs + ((wave * G * (HD + 2) + 3) & ~3);
+    if (b0 < p1) attn_pipeline_mf(A, B, qf, kc, vc, b0, p1, NW * Gm::NP, G, lane, pw, st);
     if (stamps) stamps[2] = clock_now();
-    attn_store_state_mf<GQ>(st, G, recs + wave * G * (HD + 2), lane);
+    attn_store_state_mf(st, G, recs + wave * G * (HD + 2), lane);
   } else {
     AttnState<HD, GQ> st;
     st.init();
@@ -1094,9 +1097,12 @@ __device__ __forceinline__ void attn_full_body(const Params& P, const Step* Sd, 
 // One kernel pair per cache element type and group size, so that each gets
 // its own register allocation: the state arrays hold exactly the group's
 // heads (with room for 8 heads and both element types in one kernel they no
-// longer fit in registers and spilled to scratch).
+// longer fit in registers and spilled to scratch).  The split kernel asks for
+// two waves per SIMD: left free, the compiler gave the matrix-core variant 272
+// registers, one wave per SIMD, and the 8-sequence 4K-context attention took
+// 39.3 us per layer against 32.3 us with 225 registers.
 #define MK_ATTN_KERNELS(KN, KT, GQ)                                                                           \
-  extern "C" __global__ __launch_bounds__(kAttnWaves * kWave) void mk_op_attn_split_##KN##_g##GQ(             \
+  extern "C" __global__ __launch_bounds__(kAttnWaves * kWave, 2) void mk_op_attn_split_##KN##_g##GQ(          \
       Params P, const Step* Sd, int layer, int fuse_merge) {                                                  \
     attn_split_body<KT, GQ>(P, Sd, layer, fuse_merge);                                                        \
   }                                                                                                           \
