@@ -35,9 +35,18 @@ int round_up(int x, int m) { return (x + m - 1) / m * m; }
 // Positions per attention split when several sequences share a step: the
 // (sequence, KV head) pairs already widen the grid.  Up to 1024 positions the
 // whole context is one split (no merge launch; 70B shape, 64 sequences of
-// 640: 58 against 69 + 8 us per layer); longer contexts use 512-position
-// splits (8B shape, 8 sequences of 4K: 5.68 against 5.78 ms/step for 128).
-int batched_split(int max_seq) { return max_seq <= 1024 ? max_seq : 512; }
+// 640: 58 against 69 + 8 us per layer).  Longer contexts use 512-position
+// splits (8B shape, 8 sequences of 4K: 5.68 against 5.78 ms/step for 128),
+// or the shortest multiple of 64 up to 1024 that keeps the workgroups within
+// two per CU, one round of them: with 9 splits of 512 positions the last 64 of
+// 576 workgroups ran in a second round (same workload: 31.3 + 6.0 us per
+// layer, 8 splits of 576: 28.0 + 5.5).
+int batched_split(int max_seq, int B, int nkv, int ncu) {
+  if (max_seq <= 1024) return max_seq;
+  for (int split = 512; split <= 1024; split += 64)
+    if ((int64_t)B * nkv * ((max_seq + split - 1) / split) <= 2 * ncu) return split;
+  return 512;
+}
 
 
 // Batch tiles (16 rows each) of the batched projections: 1, 2 or 4.
@@ -73,7 +82,9 @@ GraphConfig graph_config(const mk_config* c, int ncu) {
   GraphConfig g;
   g.L = c->n_layers; g.H = c->hidden; g.nq = c->n_q_heads; g.nkv = c->n_kv_heads; g.hd = c->head_dim;
   g.F = c->ffn; g.V = c->vocab; g.B = c->max_batch; g.max_seq = c->max_seq;
-  g.split = c->attn_split ? c->attn_split : c->max_batch > 1 ? batched_split(c->max_seq) : auto_split(c->max_seq);
+  g.split = c->attn_split                 ? c->attn_split
+            : c->max_batch > 1 ? batched_split(c->max_seq, c->max_batch, c->n_kv_heads, ncu)
+                               : auto_split(c->max_seq);
   g.ncu = ncu;
   return g;
 }
