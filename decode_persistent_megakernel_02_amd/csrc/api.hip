@@ -316,8 +316,12 @@ int bgemm_splits(const Params& P, int type, int ncu) {
   // elsewhere, which halves the partial sums the finishing launch adds.
   // Measured per operator at the 8B shape with 8 sequences and the 70B shape
   // with 64; three per CU was slower everywhere.
-  const int target = (bt == 4 && bgemm_gpw(P, type) == 1 ? 2 : 1) * ncu;
-  int ks = std::max(1, std::min(nch, (target + ngx - 1) / ngx));
+  // Two per CU is also as many of those workgroups as the CUs hold at once
+  // (LDS), so there the count rounds down: a few more would run in a second
+  // round (70B shape, 64 sequences: QKV in 7 splits was 560 workgroups).
+  const bool two = bt == 4 && bgemm_gpw(P, type) == 1;
+  const int target = (two ? 2 : 1) * ncu;
+  int ks = std::max(1, std::min(nch, two ? target / ngx : (target + ngx - 1) / ngx));
   const int per = (nch + ks - 1) / ks;
   return (nch + per - 1) / per;
 }
