@@ -306,3 +306,116 @@ def test_planted_transposed_wo_is_caught(monkeypatch):
     monkeypatch.undo()
     ref = hf_logits(shape, w, toks)
     assert np.abs(ours - ref).max() > 100 * HF_RTOL * np.abs(ref).max()
+
+
+# ---- bf16 rounding, top-2 margin and greedy generation ------------------------------
+def _torch_bf16(x):
+    """torch's own fp32 -> bfloat16 conversion (round to nearest, ties to even), widened."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_round_bf16_matches_torch_cast():
+    x = np.concatenate([RNG.normal(size=50_000) * 10.0 ** RNG.integers(-30, 30, size=50_000),
+                        -RNG.random(20_000), RNG.random(20_000) * 3e38, [0.0, -0.0, 1.0, -1.0]])
+    np.testing.assert_array_equal(D.round_bf16(x), _torch_bf16(x))
+
+
+def test_round_bf16_ties_to_even_exact_halfway():
+    # fp32 values exactly halfway between two neighbouring bf16 values: the
+    # result is the neighbour with an even last mantissa bit
+    cases = {0x3F808000: 0x3F80, 0x3F818000: 0x3F82, 0xBF808000: 0xBF80, 0xBF818000: 0xBF82,
+             0x7F7F8000: 0x7F80, 0x00018000: 0x0002, 0x3F80C000: 0x3F81, 0x3F804000: 0x3F80}
+    bits = np.array(list(cases), dtype=np.uint32)
+    want = (np.array(list(cases.values()), dtype=np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(D.round_bf16(bits.view(np.float32)), want)
+    np.testing.assert_array_equal(_torch_bf16(bits.view(np.float32)), want)
+
+
+def test_round_bf16_rejects_truncation():
+    # a value just above a halfway point must round up (truncation would not)
+    x = np.array([np.float32(1.0) + np.float32(2.0 ** -8) + np.float32(2.0 ** -20)], dtype=np.float32)
+    assert D.round_bf16(x)[0] == 1.0 + 2.0 ** -7
+
+
+def _brute_top2(row):
+    """top1 - top2 by two passes over the row (the second excludes the first index)."""
+    i1 = max(range(len(row)), key=lambda i: row[i])
+    v2 = max(row[i] for i in range(len(row)) if i != i1)
+    return row[i1] - v2
+
+
+def test_top2_margin_brute_force():
+    lg = RNG.normal(size=(6, 300))
+    lg[2, 10] = lg[2, 200] = lg[2].max() + 1.0       # tie at the top: margin 0
+    m = D.top2_margin(lg)
+    for r in range(lg.shape[0]):
+        assert m[r] == _brute_top2(lg[r])
+    assert m[2] == 0.0
+    assert D.top2_margin(np.array([3.0, 1.0, 2.0])) == 1.0   # not top1 - top3
+
+
+def test_generate_matches_greedy_recompute_without_cache():
+    """Brute force: each decode step is a cache-free forward of the whole
+    sequence so far, fed with the argmax of the previous step's logits."""
+    shape = MICRO
+    w = gen.gen_weights(shape, seed=21, random_norms=True)
+    prompt = gen.tokens(31, 3, 0, 5, shape.vocab).reshape(1, 5)
+    steps = 4
+    dec = D.Decoder(shape, w, batch=1, max_seq=5 + steps)
+    toks, logs = dec.generate(prompt, steps)
+    seq = [int(t) for t in prompt[0]]
+    nxt = max(range(shape.vocab), key=lambda i: (D.forward_full(shape, w, [seq])[0, -1][i], -i))
+    for s in range(steps):
+        seq.append(nxt)
+        lg = D.forward_full(shape, w, [seq])[0, -1]
+        assert np.abs(logs[0, s] - lg).max() <= 1e-12 * np.abs(lg).max()
+        nxt = max(range(shape.vocab), key=lambda i: (lg[i], -i))
+        assert toks[0, s] == nxt
+
+
+# planted slips in the three functions above; each pin must reject its slip
+def _trunc_bf16(x):
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return ((u >> np.uint32(16)) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _ties_away_bf16(x):
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return (((u + np.uint32(0x8000)) >> np.uint32(16)) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _top1_minus_top3(lg):
+    s = np.sort(lg, axis=-1)
+    return s[..., -1] - s[..., -3]
+
+
+def _generate_stale_feed(self, prompt, steps):
+    """Slip: each step is fed the token that was fed to the step before."""
+    last = self.prefill(prompt)
+    nxt = D.greedy(last)
+    prev = nxt
+    toks, logs = [], []
+    for _ in range(steps):
+        lg = self.step(prev)
+        logs.append(lg)
+        prev, nxt = nxt, D.greedy(lg)
+        toks.append(nxt)
+    return np.stack(toks, 1), np.stack(logs, 1)
+
+
+@pytest.mark.parametrize("plant,test", [
+    (("round_bf16", _trunc_bf16), test_round_bf16_matches_torch_cast),
+    (("round_bf16", _trunc_bf16), test_round_bf16_rejects_truncation),
+    (("round_bf16", _ties_away_bf16), test_round_bf16_ties_to_even_exact_halfway),
+    (("top2_margin", _top1_minus_top3), test_top2_margin_brute_force),
+], ids=["trunc_vs_torch", "trunc_halfway", "ties_away", "top1_minus_top3"])
+def test_planted_slip_in_helpers_is_caught(plant, test, monkeypatch):
+    monkeypatch.setattr(D, plant[0], plant[1])
+    with pytest.raises(AssertionError):
+        test()
+
+
+def test_planted_stale_feed_in_generate_is_caught(monkeypatch):
+    monkeypatch.setattr(D.Decoder, "generate", _generate_stale_feed)
+    with pytest.raises(AssertionError):
+        test_generate_matches_greedy_recompute_without_cache()
