@@ -17,6 +17,7 @@ MK_OK, MK_ERR_INVALID_ARG, MK_ERR_OUT_OF_MEMORY, MK_ERR_HIP = 0, -1, -2, -3
 MK_ERR_CAPACITY, MK_ERR_TIMEOUT, MK_ERR_STATE, MK_ERR_UNSUPPORTED = -4, -5, -6, -7
 MK_MODE_MEGAKERNEL, MK_MODE_PER_OP = 0, 1
 MK_FLAG_TRACE, MK_FLAG_POISON, MK_FLAG_NO_GRAPH, MK_FLAG_FUSED_MERGE, MK_FLAG_TILED_WEIGHTS = 1, 2, 4, 8, 16
+MK_FLAG_SPIN_LIMIT_1 = 32
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_OUT_OF_MEMORY", -3: "MK_ERR_HIP",
                 -4: "MK_ERR_CAPACITY", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE", -7: "MK_ERR_UNSUPPORTED"}
 

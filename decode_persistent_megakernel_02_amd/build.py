@@ -7,6 +7,7 @@ import hashlib
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -30,17 +31,25 @@ def build_lib(verbose=False, out=LIB, defines=()):
     """Compile the kernels and the host library into `out`; `defines` are extra
     -D options (the MK_SHAPE_* tuning knobs) given to every compile."""
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    srcs = [os.path.join(CSRC, f) for f in ("kernels.hip", "batched.hip", "api.hip")]
+    # (source, extra defines): the megakernel instances are split over three
+    # compiles so that they build in parallel
+    srcs = [("kernels.hip", ()), ("mega.hip", ("MK_MEGA_PART=0",)), ("mega.hip", ("MK_MEGA_PART=1",)),
+            ("mega.hip", ("MK_MEGA_PART=2",)), ("batched.hip", ()), ("api.hip", ())]
     host = os.path.join(CSRC, "graph.cpp")
     inc = ["-I", CSRC, "-I", os.path.join(ROOT, "include")] + [f"-D{d}" for d in defines]
     bdir = os.path.join(PKG, "_build", hashlib.sha1(" ".join(defines).encode()).hexdigest()[:8]) if defines \
         else os.path.join(PKG, "_build")
     os.makedirs(bdir, exist_ok=True)
-    objs = []
-    for src in srcs:
-        obj = os.path.join(bdir, os.path.basename(src) + ".o")
-        _run([hipcc] + HIP_FLAGS + inc + ["-c", "-o", obj, src], verbose)
-        objs.append(obj)
+    jobs = []
+    for name, extra in srcs:
+        tag = "_".join(d.replace("=", "") for d in extra)
+        obj = os.path.join(bdir, name + (("." + tag) if tag else "") + ".o")
+        jobs.append([hipcc] + HIP_FLAGS + inc + [f"-D{d}" for d in extra] + ["-c", "-o", obj, os.path.join(CSRC, name)])
+    objs = [j[-2] for j in jobs]
+    workers = int(os.environ.get("MAX_JOBS", "0")) or min(len(jobs), os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for f in [ex.submit(_run, j, verbose) for j in jobs]:
+            f.result()
     obj = os.path.join(bdir, "graph.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall"] + inc + ["-c", "-o", obj, host], verbose)
     objs.append(obj)

@@ -2,6 +2,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
+#include <thread>
 #include <cmath>
 #include <cstring>
 #include <memory>
@@ -49,6 +51,37 @@ int batched_split(int max_seq, int B, int nkv, int ncu) {
 }
 
 
+// Positions per attention split of the megakernel.  A (KV head, split) unit
+// runs on the kMegaStagers stager waves of one workgroup, each taking whole
+// position blocks of AttnGeom::NP positions; the split is the fewest such
+// rounds of blocks that keep the units within one per workgroup.
+int mega_block(int hd, bool f32) { return kWave / (hd / (f32 ? 16 : 32)); }
+int mega_split(int max_seq, int nkv, int ncu, int hd, bool f32) {
+  const int round = kMegaStagers * mega_block(hd, f32);
+  for (int split = round;; split += round)
+    if ((int64_t)nkv * ((max_seq + split - 1) / split) <= ncu || split >= kMaxSplit) return std::min(split, kMaxSplit);
+}
+
+// The megakernel instance for a shape: exact (no clamped loads) when every
+// GEMV operator's K is a multiple of 2048; by head_dim, cache type and query
+// heads per KV head (1, 2, 4, 8).
+const void* mega_kernel(int H, int qd, int F, int hd, bool f32, int G) {
+  const bool exact = H % 2048 == 0 && qd % 2048 == 0 && F % 2048 == 0 && G == 4;
+#define MK_K(X, HD, KN, G) reinterpret_cast<const void*>(&mk_mega_##X##_##HD##_##KN##_g##G)
+  if (exact) {
+    if (hd == 64) return f32 ? MK_K(x, 64, f32, 4) : MK_K(x, 64, bf16, 4);
+    return f32 ? MK_K(x, 128, f32, 4) : MK_K(x, 128, bf16, 4);
+  }
+  static const void* const k[2][2][4] = {
+      {{MK_K(n, 64, bf16, 1), MK_K(n, 64, bf16, 2), MK_K(n, 64, bf16, 4), MK_K(n, 64, bf16, 8)},
+       {MK_K(n, 64, f32, 1), MK_K(n, 64, f32, 2), MK_K(n, 64, f32, 4), MK_K(n, 64, f32, 8)}},
+      {{MK_K(n, 128, bf16, 1), MK_K(n, 128, bf16, 2), MK_K(n, 128, bf16, 4), MK_K(n, 128, bf16, 8)},
+       {MK_K(n, 128, f32, 1), MK_K(n, 128, f32, 2), MK_K(n, 128, f32, 4), MK_K(n, 128, f32, 8)}}};
+#undef MK_K
+  const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : -1;
+  return gi < 0 ? nullptr : k[hd == 128 ? 1 : 0][f32 ? 1 : 0][gi];
+}
+
 // Batch tiles (16 rows each) of the batched projections: 1, 2 or 4.
 int batch_tiles(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : 4; }
 
@@ -82,9 +115,10 @@ GraphConfig graph_config(const mk_config* c, int ncu) {
   GraphConfig g;
   g.L = c->n_layers; g.H = c->hidden; g.nq = c->n_q_heads; g.nkv = c->n_kv_heads; g.hd = c->head_dim;
   g.F = c->ffn; g.V = c->vocab; g.B = c->max_batch; g.max_seq = c->max_seq;
-  g.split = c->attn_split                 ? c->attn_split
+  g.split = c->attn_split ? c->attn_split
             : c->max_batch > 1 ? batched_split(c->max_seq, c->max_batch, c->n_kv_heads, ncu)
-                               : auto_split(c->max_seq);
+            : c->mode == MK_MODE_MEGAKERNEL ? mega_split(c->max_seq, c->n_kv_heads, ncu, c->head_dim, c->kv_fp32 != 0)
+                                            : auto_split(c->max_seq);
   g.ncu = ncu;
   return g;
 }
@@ -128,7 +162,12 @@ struct mk_handle {
   Graph graph;
   Params P{};
   std::vector<void*> allocs;
-  int page_floats = 0, scratch_floats = 0, lds_mega = 0;
+  int page_floats = 0, lds_mega = 0;  // megakernel: input page floats, LDS bytes
+  MegaBufs mega{};                    // megakernel: tagged hand-over buffers
+  const void* mega_fn = nullptr;      // megakernel: the instance for this shape
+  uint32_t* host_abort = nullptr;     // megakernel: host-mapped abort word (hipHostMalloc)
+  int64_t mega_trace_words = 0;       // megakernel: words of the timestamp buffer (0: off)
+  int pending = 0;                    // launches since the last synchronize (host watchdog)
   int op_page[9] = {0}, op_lds[9] = {0}, op_grid_cap[9] = {0}, op_sf[9] = {0};  // per task type
   int op_grid[9] = {0};  // grid of the last launch of each GEMV operator
   bool op_exact[9] = {false};
@@ -169,6 +208,7 @@ struct mk_handle {
     return MK_OK;
   }
   ~mk_handle() {
+    if (host_abort) (void)hipHostFree(host_abort);
     if (graph_exec) (void)hipGraphExecDestroy(graph_exec);
     if (step_graph) (void)hipGraphDestroy(step_graph);
     if (cap_stream) (void)hipStreamDestroy(cap_stream);
@@ -499,17 +539,23 @@ mk_status launch_step(mk_handle* h, const Step& S) {
                        h->act_floats, 0xFFFFFFFFu);
     HIP_TRY(hipGetLastError());
   }
-  hipLaunchKernelGGL(mk_set_step, dim3(1), dim3(64), 0, h->stream, h->d_step, S);
-  HIP_TRY(hipGetLastError());
-  int pf = h->page_floats, sf = h->scratch_floats;
   if (h->cfg.mode == MK_MODE_MEGAKERNEL) {
+    // One ordinary launch of one workgroup per CU (the LDS request keeps a
+    // second one off each CU).  The kernel uses no grid-wide barrier, so it
+    // needs no cooperative launch; every in-kernel wait is bounded, so a
+    // workgroup that were not resident would end the step with
+    // MK_ERR_TIMEOUT rather than hang it.
     Params Pc = P;
-    const Step* sp = h->d_step;
-    void* args[] = {&Pc, &sp, &pf, &sf};
-    HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mk_persistent), dim3(P.ncu),
-                                       dim3(kWaves * kWave), args, (unsigned)h->lds_mega, h->stream));
+    MegaBufs Mc = h->mega;
+    Step Sc = S;
+    int pf = h->page_floats;
+    void* args[] = {&Pc, &Mc, &Sc, &pf};
+    HIP_TRY(hipLaunchKernel(h->mega_fn, dim3(P.ncu), dim3(kMegaWaves * kWave), args, (size_t)h->lds_mega, h->stream));
+    ++h->pending;
     return MK_OK;
   }
+  hipLaunchKernelGGL(mk_set_step, dim3(1), dim3(64), 0, h->stream, h->d_step, S);
+  HIP_TRY(hipGetLastError());
   const bool eager = (h->cfg.flags & MK_FLAG_NO_GRAPH) || h->timed_mask != 0;
   if (eager) return enqueue_ops(h, h->stream, true);
   MK_TRY(build_step_graph(h));
@@ -548,13 +594,16 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
         !w->w_up[l] || !w->w_down[l])
       return fail(MK_ERR_INVALID_ARG, "weights: NULL pointer in layer " + std::to_string(l));
-  // The cooperative persistent launch did not complete on the MI355X test box
-  // (the stream never drained although every in-kernel wait is bounded); until
-  // the cause is known this mode is refused rather than risked.
-  if (cfg->mode == MK_MODE_MEGAKERNEL)
-    return fail(MK_ERR_UNSUPPORTED,
-                "MK_MODE_MEGAKERNEL (cooperative persistent launch) is disabled: its launch did not complete on "
-                "gfx950; use MK_MODE_PER_OP");
+  if (cfg->mode == MK_MODE_MEGAKERNEL) {
+    if (cfg->max_batch != 1)
+      return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL runs one sequence (max_batch 1); batched decode runs per operator");
+    const int G = cfg->n_q_heads / cfg->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+      return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports 1, 2, 4 or 8 query heads per KV head");
+    if (cfg->vocab > (1 << 17)) return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports vocab <= 131072");
+    if (cfg->flags & (MK_FLAG_FUSED_MERGE | MK_FLAG_NO_GRAPH | MK_FLAG_TILED_WEIGHTS | MK_FLAG_POISON))
+      return fail(MK_ERR_INVALID_ARG, "FUSED_MERGE, NO_GRAPH, TILED_WEIGHTS and POISON are per-operator flags");
+  }
 
   int dev_cus = 0, max_lds = 0;
   double tpu = 100.0;
@@ -594,6 +643,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   // One wait iteration takes well over 20 ns (a sleep plus a memory read), so
   // this limit trips only if the wall clock stops advancing.
   P.spin_limit = (uint32_t)std::min(4.0e9, wd_ms * 1000.0 * 50.0);
+  if (cfg->flags & MK_FLAG_SPIN_LIMIT_1) P.spin_limit = 1;
   P.embed = static_cast<const uint16_t*>(w->embed);
   P.lm_head = static_cast<const uint16_t*>(w->lm_head);
   P.final_norm = static_cast<const uint16_t*>(w->final_norm);
@@ -701,10 +751,41 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   MK_TRY(h->alloc(&h->d_tok_scratch, B));
   MK_TRY(h->alloc(&h->d_step, 1));
 
-  // LDS budget
-  h->page_floats = round_up(std::max({H, nq * hd, F}), 8);
-  h->scratch_floats = round_up(G * hd + G * kWave, 4);
-  h->lds_mega = (int)sizeof(Lds) + 2 * h->page_floats * 4 + kWorkers * h->scratch_floats * 4;
+  if (cfg->mode == MK_MODE_MEGAKERNEL) {  // tagged hand-over buffers, zero (tag 0: never a step's epoch)
+    const int64_t qkvw = (int64_t)(nq + 2 * nkv) * hd;
+    const int64_t n_x = (int64_t)(L + 1) * H, n_xmid = (int64_t)L * H, n_qkv = (int64_t)L * qkvw;
+    const int64_t n_rec = (int64_t)L * nkv * g.nsplit * G * (hd + 2), n_attn = (int64_t)L * nq * hd;
+    const int64_t n_h = (int64_t)L * F, total = n_x + n_xmid + n_qkv + n_rec + n_attn + n_h + ncu;
+    uint64_t* t = nullptr;
+    MK_TRY(h->alloc(&t, total));
+    HIP_TRY(hipMemset(t, 0, total * 8));
+    MegaBufs& M = h->mega;
+    M.x = t;
+    M.xmid = M.x + n_x;
+    M.qkv = M.xmid + n_xmid;
+    M.rec = M.qkv + n_qkv;
+    M.attn = M.rec + n_rec;
+    M.h = M.attn + n_attn;
+    M.key = M.h + n_h;
+    HIP_TRY(hipHostMalloc(&h->host_abort, 64, hipHostMallocMapped | hipHostMallocCoherent));
+    *h->host_abort = 0;
+    HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void**>(&M.host_abort), h->host_abort, 0));
+    if (cfg->flags & MK_FLAG_TRACE) {
+      h->mega_trace_words = (int64_t)(4 * L + 1) * ncu * (kMegaCompute + 1);
+      MK_TRY(h->alloc(&M.trace, h->mega_trace_words));
+      HIP_TRY(hipMemset(M.trace, 0, h->mega_trace_words * 8));
+    }
+    // every GEMV operator's tasks must fit the compute waves' result slots
+    const int counts[5] = {(nq + nkv) * (hd / 2) + (nkv * hd + kRowsQkv - 1) / kRowsQkv, (H + kRowsO - 1) / kRowsO,
+                           (F + kRowsGuPerMatrix - 1) / kRowsGuPerMatrix, (H + kRowsDown - 1) / kRowsDown,
+                           (V + kRowsLm - 1) / kRowsLm};
+    for (int c : counts)
+      if ((c + ncu * kMegaCompute - 1) / (ncu * kMegaCompute) > 64)
+        return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL: an operator has more than 64 tasks per compute wave "
+                                        "on this many CUs");
+    h->mega_fn = mega_kernel(H, nq * hd, F, hd, P.kv_f32 != 0, G);
+    if (!h->mega_fn) return fail(MK_ERR_UNSUPPORTED, "no megakernel instance for this shape");
+  }
   if (!h->batched) {
     const std::string e = check_op_tasks(h->graph);
     if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "internal: " + e);
@@ -741,17 +822,16 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   HIP_TRY(hipFuncSetAttribute(attn_full_kernel(P.kv_f32, G),
                               hipFuncAttributeMaxDynamicSharedMemorySize, h->attn_full_lds));
   if (cfg->mode == MK_MODE_MEGAKERNEL) {
+    h->lds_mega = mega_lds_bytes(H, nq, nkv, hd, F, &h->page_floats);
     if (h->lds_mega > max_lds)
       return fail(MK_ERR_UNSUPPORTED,
-                  "LDS need " + std::to_string(h->lds_mega) + " B exceeds " + std::to_string(max_lds));
+                  "megakernel LDS need " + std::to_string(h->lds_mega) + " B exceeds " + std::to_string(max_lds));
     // keep one persistent workgroup per CU: ask for more than half the LDS
     if (h->lds_mega <= max_lds / 2) h->lds_mega = max_lds / 2 + 1024;
-    HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&mk_persistent),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, h->lds_mega));
+    HIP_TRY(hipFuncSetAttribute(h->mega_fn, hipFuncAttributeMaxDynamicSharedMemorySize, h->lds_mega));
     int nb = 0;
-    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&mk_persistent),
-                                                         kWaves * kWave, h->lds_mega));
-    if (nb < 1) return fail(MK_ERR_UNSUPPORTED, "persistent kernel does not fit on a CU");
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, h->mega_fn, kMegaWaves * kWave, h->lds_mega));
+    if (nb < 1) return fail(MK_ERR_UNSUPPORTED, "the megakernel does not fit on a CU");
   }
   HIP_TRY(hipDeviceSynchronize());
   *out = guard.release();
@@ -801,9 +881,40 @@ mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P
   return MK_OK;
 }
 
+namespace {
+// Waits for the handle's stream.  In megakernel mode a host watchdog runs
+// beside the in-kernel limits: if the stream has not drained 10 s plus 100 ms
+// per launch since the last wait, it raises the host-mapped abort word, which
+// every in-kernel wait polls, and then waits for the kernels to end.
+mk_status drain(mk_handle* h) {
+  if (h->cfg.mode == MK_MODE_MEGAKERNEL && h->host_abort) {
+    const double limit_ms = 10000.0 + 100.0 * h->pending;
+    const auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+      const hipError_t e = hipStreamQuery(h->stream);
+      if (e == hipSuccess) break;
+      if (e != hipErrorNotReady) return fail(MK_ERR_HIP, std::string("hipStreamQuery: ") + hipGetErrorString(e));
+      const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+      if (ms > limit_ms) {
+        __atomic_store_n(h->host_abort, 1u, __ATOMIC_SEQ_CST);
+        h->poisoned = true;
+        HIP_TRY(hipStreamSynchronize(h->stream));
+        h->pending = 0;
+        return fail(MK_ERR_TIMEOUT, "host watchdog: the megakernel did not finish; aborted");
+      }
+      std::this_thread::sleep_for(std::chrono::microseconds(200));
+    }
+    h->pending = 0;
+    return MK_OK;
+  }
+  HIP_TRY(hipStreamSynchronize(h->stream));
+  return MK_OK;
+}
+}  // namespace
+
 mk_status mk_read_status(mk_handle* h, uint32_t out[16]) {
   if (!h || !out) return fail(MK_ERR_INVALID_ARG, "NULL argument");
-  HIP_TRY(hipStreamSynchronize(h->stream));
+  MK_TRY(drain(h));
   HIP_TRY(hipMemcpy(out, h->P.status, kStatusWords * 4, hipMemcpyDeviceToHost));
   return MK_OK;
 }
@@ -815,12 +926,13 @@ mk_status mk_synchronize(mk_handle* h) {
   MK_TRY(mk_read_status(h, st));
   if (st[1] == ST_TIMEOUT) {
     h->poisoned = true;
-    static const char* who[] = {"scheduler (event)", "scheduler (LDS page)", "worker (ready frontier)"};
-    return fail(MK_ERR_TIMEOUT, std::string("watchdog: ") + who[st[7] < 3 ? st[7] : 0] + " on CU " +
-                                    std::to_string(st[2]) + ", task " + std::to_string(st[3]) + ", event " +
-                                    std::to_string(st[4]) + ": value " + std::to_string(st[5]) + ", needed " +
-                                    std::to_string(st[6]) + "; frontier " + std::to_string(st[8]) + ", ticket " +
-                                    std::to_string(st[9]));
+    static const char* kinds[] = {"?", "input page", "compute completions", "stager rendezvous", "tagged input",
+                                  "queries/keys/values", "attention records", "LM-head keys"};
+    const uint32_t kind = st[4] & 0xFF;
+    return fail(MK_ERR_TIMEOUT, std::string("in-kernel watchdog: workgroup ") + std::to_string(st[2]) + ", wave " +
+                                    std::to_string(st[3]) + ", operator " + std::to_string(st[4] >> 8) +
+                                    ", waiting for " + kinds[kind < 8 ? kind : 0] + ": have " + std::to_string(st[5]) +
+                                    ", need " + std::to_string(st[6]));
   }
   if (st[1] == ST_LDS) {
     h->poisoned = true;
@@ -841,7 +953,7 @@ mk_status mk_synchronize(mk_handle* h) {
 mk_status mk_reset(mk_handle* h) {
   g_err.clear();
   if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
-  HIP_TRY(hipStreamSynchronize(h->stream));
+  MK_TRY(drain(h));
   if (h->poisoned) return fail(MK_ERR_STATE, "handle poisoned; destroy and recreate it");
   HIP_TRY(hipMemset(h->P.events, 0, h->graph.event_count.size() * 4));
   HIP_TRY(hipMemset(h->P.lm_part, 0, h->cfg.max_batch * sizeof(unsigned long long)));
@@ -849,7 +961,8 @@ mk_status mk_reset(mk_handle* h) {
   HIP_TRY(hipDeviceSynchronize());
   h->length = 0;
   h->batch = 0;
-  h->epoch = 0;
+  // the epoch keeps counting: megakernel words tagged before the reset can
+  // never carry a later step's epoch
   return MK_OK;
 }
 
@@ -874,7 +987,7 @@ mk_status mk_kv_read(mk_handle* h, void* k_host, void* v_host, int64_t bytes) {
   const auto& P = h->P;
   const int64_t need = (int64_t)P.L * P.B * P.nkv * P.max_seq * P.hd * (P.kv_f32 ? 4 : 2);
   if (bytes != need) return fail(MK_ERR_INVALID_ARG, "bytes must equal the cache size " + std::to_string(need));
-  HIP_TRY(hipStreamSynchronize(h->stream));
+  MK_TRY(drain(h));
   HIP_TRY(hipMemcpy(k_host, P.kcache, (size_t)bytes, hipMemcpyDeviceToHost));
   HIP_TRY(hipMemcpy(v_host, P.vcache, (size_t)bytes, hipMemcpyDeviceToHost));
   return MK_OK;
@@ -882,7 +995,7 @@ mk_status mk_kv_read(mk_handle* h, void* k_host, void* v_host, int64_t bytes) {
 
 void mk_destroy(mk_handle* h) {
   if (!h) return;
-  (void)hipStreamSynchronize(h->stream);
+  (void)drain(h);
   delete h;
 }
 

@@ -797,4 +797,90 @@ __device__ __forceinline__ int token_of(const Params& P, const Step& S, int b) {
 }
 
 
+// ---------------------------------------------------------------------------
+// GEMV task helpers shared by the per-operator kernels and the megakernel.
+
+template <int R>
+__device__ __forceinline__ float pick(const float (&y)[R], int i) {
+  float v = y[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) v = i == r ? y[r] : v;
+  return v;
+}
+
+// GEMV-type task (QKV, O, GU, DOWN, LM) with its operator fixed at compile
+// time: where its rows are ...
+// Rows of task d in the matrices W0 (QKV: the task's own matrix; GU: gate)
+// and W1 (GU: up).
+template <int TT>
+__device__ __forceinline__ void gemv_setup_w(const Params& P, const Task& d, const uint16_t* W0, const uint16_t* W1,
+                                             GemvRows<TaskShape<TT>::R>& g) {
+  constexpr int R = TaskShape<TT>::R;
+  int K = P.H;
+  if constexpr (TT == TT_O) K = P.nq * P.hd;
+  else if constexpr (TT == TT_DOWN) K = P.F;
+  g.nvec = K / 8;
+  g.stride = K / 8;
+  g.split = R;
+  if constexpr (TT == TT_QKV) {
+    const uint16_t* W = W0;
+    g.base0 = reinterpret_cast<const v4u*>(W + (int64_t)d.a1 * K);
+    if (d.a3) {  // one RoPE pair: rows a1 and a1 + hd/2
+      g.base1 = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + d.a3) * K);
+      g.split = 1;
+      g.mask = 3;
+    } else {
+      g.base1 = g.base0;
+      g.mask = (1u << d.a2) - 1;
+    }
+  } else if constexpr (TT == TT_GU) {  // rows: gate a1.., then up a1..
+    g.base0 = reinterpret_cast<const v4u*>(W0 + (int64_t)d.a1 * K);
+    g.base1 = reinterpret_cast<const v4u*>(W1 + (int64_t)d.a1 * K);
+    g.split = R / 2;
+    const uint32_t half = (1u << d.a2) - 1;
+    g.mask = half | (half << (R / 2));
+  } else {
+    g.base0 = reinterpret_cast<const v4u*>(W0 + (int64_t)d.a1 * K);
+    g.base1 = g.base0;
+    g.mask = (1u << d.a2) - 1;
+  }
+}
+
+template <int TT>
+__device__ __forceinline__ void gemv_put(float* res, int* ids, int j, int task, const float (&y)[TaskShape<TT>::R],
+                                         int lane) {
+  constexpr int R = TaskShape<TT>::R;
+  if (lane < R) res[j * R + lane] = pick<R>(y, lane);
+  if (lane == 0) ids[j] = task;
+}
+
+// The task of pool slot p of this workgroup, or `count` past its end.  The
+// dispatcher deals workgroups to the XCDs in turn (workgroup b runs on XCD
+// b % kXcds).  When the grid is a multiple of kXcds, the workgroups of one
+// XCD share one contiguous kXcds-th of the task list, dealt to them in runs of
+// kWaves tasks; otherwise the runs go to all workgroups in turn.  (Dealing
+// runs to all workgroups in turn makes XCD x read the same few consecutive
+// rows out of every kXcds runs -- for 8 KB rows a fixed 32 KB slice of every
+// 256 KB -- and the XCDs then finish up to a fifth apart.)
+__device__ __forceinline__ int slot_task(uint32_t p, int count) {
+  const int n = gridDim.x, run = (int)(p / kWaves), k = (int)(p % kWaves);
+  if (n % kXcds) {
+    const int t = (run * n + (int)blockIdx.x) * kWaves + k;
+    return t < count ? t : count;
+  }
+  const int per = (count + kXcds - 1) / kXcds, x = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+  const int t = (run * (n / kXcds) + j) * kWaves + k;
+  return t < per && x * per + t < count ? x * per + t : count;
+}
+
+// The next pool slot's task of this wave, or `count` when the pool is empty
+// or the wave's result slots are full (j results kept, one task in hand).
+__device__ __forceinline__ int gemv_next(uint32_t* pool, int j, int count, int lane) {
+  if (j + 2 > kMaxTasksPerWave) return count;
+  uint32_t p = 0;
+  if (lane == 0) p = lds_add(pool, 1u);
+  p = __builtin_amdgcn_readfirstlane(p);
+  return slot_task(p, count);
+}
+
 }  // namespace mk

@@ -5,7 +5,14 @@
 #include "mk_internal.h"
 
 namespace mk {
-extern "C" __global__ void mk_persistent(Params P, const Step* S, int page_floats, int scratch_floats);
+// megakernel instances (mega.hip): mk_mega_<x|n>_<head_dim>_<f32|bf16>_g<query heads per KV head>
+#define MK_MEGA_DECL(X, HD, KN, G) extern "C" __global__ void mk_mega_##X##_##HD##_##KN##_g##G(Params P, MegaBufs M, Step S, int pf);
+#define MK_MEGA_DECL_G(X, HD, KN) MK_MEGA_DECL(X, HD, KN, 1) MK_MEGA_DECL(X, HD, KN, 2) MK_MEGA_DECL(X, HD, KN, 4) MK_MEGA_DECL(X, HD, KN, 8)
+MK_MEGA_DECL_G(n, 64, f32) MK_MEGA_DECL_G(n, 64, bf16) MK_MEGA_DECL_G(n, 128, f32) MK_MEGA_DECL_G(n, 128, bf16)
+MK_MEGA_DECL(x, 64, f32, 4) MK_MEGA_DECL(x, 64, bf16, 4) MK_MEGA_DECL(x, 128, f32, 4) MK_MEGA_DECL(x, 128, bf16, 4)
+#undef MK_MEGA_DECL_G
+#undef MK_MEGA_DECL
+int mega_lds_bytes(int H, int nq, int nkv, int hd, int F, int* page_floats);  // megakernel LDS by shape
 #define MK_ATTN_DECL(KN, GQ)                                                                                 \
   extern "C" __global__ void mk_op_attn_split_##KN##_g##GQ(Params P, const Step* S, int layer, int fuse_merge); \
   extern "C" __global__ void mk_op_attn_full_##KN##_g##GQ(Params P, const Step* S, int layer);

@@ -1,20 +1,10 @@
-// Device entry points: the persistent megakernel (scheduler wave + worker
-// waves per CU), the kernel-per-operator baseline built from the same task
-// bodies, and single-body kernels used by the unit tests.
-//
-// Runtime design (after "Compilar LLM en un MegaKernel ...", section "Parte 2.
-// Runtime", and "MPK: A Compiler and Runtime ...", sections 3-4), re-cut for
-// CDNA4: one workgroup per CU; wave 0 is the CU's scheduler, waves 1..7 are
-// workers.  The host places every task on a per-CU queue ahead of time.  A
-// worker takes the next queue ticket as soon as it is free and starts
-// streaming that task's weights (they depend on no event), then waits until
-// the scheduler's ready frontier passes its ticket.  The scheduler walks the
-// queue in order: it waits for each task's input event in global memory
-// (counter >= threshold * epoch, agent-scope acquire), stages the task's input
-// activation vector into one of two LDS pages (computing the RMSNorm on the
-// way), and advances the frontier.  A finished task bumps a per-CU LDS counter;
-// the last task of a run of same-event tasks releases at agent scope and adds
-// one to the global event counter.
+// Device entry points of the kernel-per-operator baseline and the single-body
+// test kernels.  The baseline runs one launch per operator over that
+// operator's tasks, with the same GEMV task bodies (device.h) as the
+// persistent megakernel (mega.hip): every operator's weight rows are cut into
+// tasks of R rows, the tasks of one XCD's workgroups are one contiguous part
+// of the operator, and inside a workgroup the waves take tasks from an LDS
+// counter.  A step is one HIP graph of these launches.
 #include <type_traits>
 
 #include "device.h"
@@ -67,12 +57,6 @@ __device__ __forceinline__ StageSrc stage_src(const Params& P, const Step& S, ui
       break;
   }
   return r;
-}
-
-// One wave stages the vector (persistent kernel's scheduler wave).
-__device__ void stage_input(const Params& P, const Step& S, uint16_t key, int b, float* page, int lane) {
-  const StageSrc r = stage_src(P, S, key, b, stage_gain(P, key));
-  stage_vector(page, r.f32, r.bf, r.n, r.gamma, P.eps, lane);
 }
 
 // All kWaves waves of a workgroup stage the vector, in two halves so that
@@ -233,66 +217,7 @@ __device__ void stage_merged(const Params& P, const Step& S, int l, float* page,
   __syncthreads();
 }
 
-template <int R>
-__device__ __forceinline__ float pick(const float (&y)[R], int i) {
-  float v = y[0];
-#pragma unroll
-  for (int r = 1; r < R; ++r) v = i == r ? y[r] : v;
-  return v;
-}
-
-// GEMV-type task (QKV, O, GU, DOWN, LM) with its operator fixed at compile
-// time: where its rows are ...
-// Rows of task d in the matrices W0 (QKV: the task's own matrix; GU: gate)
-// and W1 (GU: up).
-template <int TT>
-__device__ __forceinline__ void gemv_setup_w(const Params& P, const Task& d, const uint16_t* W0, const uint16_t* W1,
-                                             GemvRows<TaskShape<TT>::R>& g) {
-  constexpr int R = TaskShape<TT>::R;
-  int K = P.H;
-  if constexpr (TT == TT_O) K = P.nq * P.hd;
-  else if constexpr (TT == TT_DOWN) K = P.F;
-  g.nvec = K / 8;
-  g.stride = K / 8;
-  g.split = R;
-  if constexpr (TT == TT_QKV) {
-    const uint16_t* W = W0;
-    g.base0 = reinterpret_cast<const v4u*>(W + (int64_t)d.a1 * K);
-    if (d.a3) {  // one RoPE pair: rows a1 and a1 + hd/2
-      g.base1 = reinterpret_cast<const v4u*>(W + (int64_t)(d.a1 + d.a3) * K);
-      g.split = 1;
-      g.mask = 3;
-    } else {
-      g.base1 = g.base0;
-      g.mask = (1u << d.a2) - 1;
-    }
-  } else if constexpr (TT == TT_GU) {  // rows: gate a1.., then up a1..
-    g.base0 = reinterpret_cast<const v4u*>(W0 + (int64_t)d.a1 * K);
-    g.base1 = reinterpret_cast<const v4u*>(W1 + (int64_t)d.a1 * K);
-    g.split = R / 2;
-    const uint32_t half = (1u << d.a2) - 1;
-    g.mask = half | (half << (R / 2));
-  } else {
-    g.base0 = reinterpret_cast<const v4u*>(W0 + (int64_t)d.a1 * K);
-    g.base1 = g.base0;
-    g.mask = (1u << d.a2) - 1;
-  }
-}
-
-// ... with the matrices taken from the per-layer tables (persistent kernel) ...
-template <int TT>
-__device__ __forceinline__ void gemv_setup(const Params& P, const Task& d, GemvRows<TaskShape<TT>::R>& g) {
-  const int l = d.layer;
-  const uint16_t *W0, *W1 = nullptr;
-  if constexpr (TT == TT_QKV) W0 = d.a0 == 0 ? ld_const(P.wq + l) : d.a0 == 1 ? ld_const(P.wk + l) : ld_const(P.wv + l);
-  else if constexpr (TT == TT_GU) { W0 = ld_const(P.w_gate + l); W1 = ld_const(P.w_up + l); }
-  else if constexpr (TT == TT_O) W0 = ld_const(P.wo + l);
-  else if constexpr (TT == TT_DOWN) W0 = ld_const(P.w_down + l);
-  else W0 = P.tied ? P.embed : P.lm_head;
-  gemv_setup_w<TT>(P, d, W0, W1, g);
-}
-
-// ... or from the launch arguments (per-operator kernels).
+// Rows of a task, with the matrices from the launch arguments.
 template <int TT>
 __device__ __forceinline__ void gemv_setup(const Params& P, const OpArgs& A, const Task& d,
                                            GemvRows<TaskShape<TT>::R>& g) {
@@ -305,70 +230,6 @@ __device__ __forceinline__ void gemv_setup(const Params& P, const OpArgs& A, con
 template <int TT>
 __device__ __forceinline__ Task op_task(const Params& P, const OpArgs& A, int t) {
   return op_task_fields(TT, A.layer, t, P.H, P.nq, P.nkv, P.hd, P.F, P.V, P.L);
-}
-
-// ... and what it does with the R dot products y (uniform across the wave).
-template <int TT>
-__device__ __forceinline__ void gemv_epilogue(const Params& P, const Step& S, const Task& d, uint32_t mask,
-                                              const float (&y)[TaskShape<TT>::R], int lane, Lds* L) {
-  constexpr int R = TaskShape<TT>::R;
-  const int l = d.layer, b = d.batch;
-  const int r = lane;  // lane r finishes row slot r
-  const int64_t H = P.H;
-  if (r < R && ((mask >> r) & 1)) {
-    const float v = pick<R>(y, r);
-    if constexpr (TT == TT_QKV) {
-      if (d.a3) {  // rotate the pair (lo, hi) = (y0, y1) by the position's angle
-        const int half = P.hd / 2, i = d.a1 % P.hd;
-        const float c = P.rope_cos[(int64_t)S.pos * half + i], sn = P.rope_sin[(int64_t)S.pos * half + i];
-        const float rot = r == 0 ? y[0] * c - y[1] * sn : y[1] * c + y[0] * sn;
-        const int row = r == 0 ? d.a1 : d.a1 + d.a3;
-        if (d.a0 == 0) P.q[((int64_t)l * P.B + b) * P.nq * P.hd + row] = rot;
-        else kv_store(P, P.kcache, kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd, rot);
-      } else {
-        const int row = d.a1 + r;
-        kv_store(P, P.vcache, kv_off(P, l, b, row / P.hd, S.pos) + row % P.hd, v);
-      }
-    } else if constexpr (TT == TT_O) {
-      const int row = d.a1 + r;
-      const float xin = l == 0 ? bf1(P.embed[(int64_t)token_of(P, S, b) * H + row]) : P.xs[((int64_t)l * P.B + b) * H + row];
-      P.xmid[((int64_t)l * P.B + b) * H + row] = xin + v;
-    } else if constexpr (TT == TT_GU) {
-      if (r < R / 2) P.h[((int64_t)l * P.B + b) * P.F + d.a1 + r] = silu(v) * pick<R>(y, r + R / 2);
-    } else if constexpr (TT == TT_DOWN) {
-      const int row = d.a1 + r;
-      P.xs[((int64_t)(l + 1) * P.B + b) * H + row] = P.xmid[((int64_t)l * P.B + b) * H + row] + v;
-    } else {
-      if (S.logits) S.logits[(int64_t)b * P.V + d.a1 + r] = v;
-    }
-  }
-  if constexpr (TT == TT_LM) {
-    unsigned long long best = 0;
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-      if ((mask >> j) & 1) {
-        const unsigned long long k = argmax_key(y[j], (uint32_t)(d.a1 + j));
-        best = k > best ? k : best;
-      }
-    if (lane == 0) __hip_atomic_fetch_max(&L->lm_best[b], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-}
-
-// One GEMV task: prefetch its weights, wait() for its inputs, dot, epilogue.
-// `wait()` returns false on abort.
-template <int TT, class Wait>
-__device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const Task& d, int lane, const float* page,
-                                          Lds* L, Wait wait) {
-  constexpr int R = TaskShape<TT>::R, D = TaskShape<TT>::D;
-  GemvRows<R> g;
-  gemv_setup<TT>(P, d, g);
-  v4u buf[D][R];
-  gemv_prefetch<R, D, false>(buf, g, lane);
-  if (!wait()) return false;
-  float y[R];
-  gemv_run<R, D, false>(buf, g, page, lane, y);
-  gemv_epilogue<TT>(P, S, d, g.mask, y, lane, L);
-  return true;
 }
 
 // A wave's GEMV tasks with two buffers: the next task's first D chunks are in
@@ -387,43 +248,6 @@ __device__ __forceinline__ bool exec_gemv(const Params& P, const Step& S, const 
 // afterwards (gemv_finish), so that no global store is pending while weight
 // loads are in flight (stores and loads share one counter, and a mix of both
 // forces a wait for everything).  Returns the number of tasks the wave ran.
-template <int TT>
-__device__ __forceinline__ void gemv_put(float* res, int* ids, int j, int task, const float (&y)[TaskShape<TT>::R],
-                                         int lane) {
-  constexpr int R = TaskShape<TT>::R;
-  if (lane < R) res[j * R + lane] = pick<R>(y, lane);
-  if (lane == 0) ids[j] = task;
-}
-
-// The task of pool slot p of this workgroup, or `count` past its end.  The
-// dispatcher deals workgroups to the XCDs in turn (workgroup b runs on XCD
-// b % kXcds).  When the grid is a multiple of kXcds, the workgroups of one
-// XCD share one contiguous kXcds-th of the task list, dealt to them in runs of
-// kWaves tasks; otherwise the runs go to all workgroups in turn.  (Dealing
-// runs to all workgroups in turn makes XCD x read the same few consecutive
-// rows out of every kXcds runs -- for 8 KB rows a fixed 32 KB slice of every
-// 256 KB -- and the XCDs then finish up to a fifth apart.)
-__device__ __forceinline__ int slot_task(uint32_t p, int count) {
-  const int n = gridDim.x, run = (int)(p / kWaves), k = (int)(p % kWaves);
-  if (n % kXcds) {
-    const int t = (run * n + (int)blockIdx.x) * kWaves + k;
-    return t < count ? t : count;
-  }
-  const int per = (count + kXcds - 1) / kXcds, x = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
-  const int t = (run * (n / kXcds) + j) * kWaves + k;
-  return t < per && x * per + t < count ? x * per + t : count;
-}
-
-// The next pool slot's task of this wave, or `count` when the pool is empty
-// or the wave's result slots are full (j results kept, one task in hand).
-__device__ __forceinline__ int gemv_next(uint32_t* pool, int j, int count, int lane) {
-  if (j + 2 > kMaxTasksPerWave) return count;
-  uint32_t p = 0;
-  if (lane == 0) p = lds_add(pool, 1u);
-  p = __builtin_amdgcn_readfirstlane(p);
-  return slot_task(p, count);
-}
-
 template <int TT, bool EXACT, class Wait>
 __device__ __forceinline__ int gemv_stream(const Params& P, const OpArgs& A, int count, int i0, int i1, int lane,
                                            const float* page, float* res, int* ids, uint32_t* pool, Wait wait) {
@@ -555,248 +379,6 @@ __device__ __forceinline__ void gemv_finish(const Params& P, const Step& S, cons
   }
 }
 
-template <int TT, class Wait>
-__device__ __forceinline__ bool exec_typed(const Params& P, const Step& S, const Task& d, int lane, const float* page, float* scratch,
-                           Lds* L, Wait wait) {
-  const int l = d.layer, b = d.batch;
-  if constexpr (TT == TT_QKV || TT == TT_O || TT == TT_GU || TT == TT_DOWN || TT == TT_LM) {
-    return exec_gemv<TT>(P, S, d, lane, page, L, wait);
-  } else if constexpr (TT == TT_ATTN) {
-    if (!wait()) return false;
-    const int G = P.nq / P.nkv, grp = d.a0, s = d.a1, T = S.pos + 1;
-    const int p0 = s * P.split;
-    if (p0 >= T) return true;
-    const int p1 = min(p0 + P.split, T);
-    const float* q = P.q + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * P.hd;
-    float* out = P.attn_part + ((((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit + s) * G * (P.hd + 2);
-    const int64_t o0 = kv_off(P, l, b, grp, 0);
-    if (P.kv_f32) {
-      const float* kc = static_cast<const float*>(P.kcache) + o0;
-      const float* vc = static_cast<const float*>(P.vcache) + o0;
-      if (P.hd == 128) attn_partial<128, float>(q, kc, vc, p0, p1, G, out, scratch, lane);
-      else attn_partial<64, float>(q, kc, vc, p0, p1, G, out, scratch, lane);
-    } else {
-      const uint16_t* kc = static_cast<const uint16_t*>(P.kcache) + o0;
-      const uint16_t* vc = static_cast<const uint16_t*>(P.vcache) + o0;
-      if (P.hd == 128) attn_partial<128, uint16_t>(q, kc, vc, p0, p1, G, out, scratch, lane);
-      else attn_partial<64, uint16_t>(q, kc, vc, p0, p1, G, out, scratch, lane);
-    }
-  } else if constexpr (TT == TT_MERGE) {
-    if (!wait()) return false;
-    const int G = P.nq / P.nkv, grp = d.a0, T = S.pos + 1;
-    const int used = (T + P.split - 1) / P.split;
-    const float* part = P.attn_part + (((int64_t)l * P.B + b) * P.nkv + grp) * P.nsplit * G * (P.hd + 2);
-    float* out = P.attn_out + ((int64_t)l * P.B + b) * P.nq * P.hd + (int64_t)grp * G * P.hd;
-    if (P.hd == 128) attn_merge<128>(part, used, G, out, lane);
-    else attn_merge<64>(part, used, G, out, lane);
-  } else if constexpr (TT == TT_ARGMAX) {
-    if (!wait()) return false;
-    for (int bb = 0; bb < P.B; ++bb) {
-      const unsigned long long k = __hip_atomic_load(&P.lm_part[bb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (lane == 0) {
-        const float v = argmax_key_value(k);
-        S.out[bb] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
-        if (!(fabsf(v) <= 3.0e38f)) atomicCAS(&P.status[1], ST_OK, ST_NONFINITE);  // NaN or Inf won
-        __hip_atomic_store(&P.lm_part[bb], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  return true;
-}
-
-// Runtime dispatch on the task type (persistent kernel).
-template <class Wait>
-__device__ bool exec_task(const Params& P, const Step& S, const Task& d, int lane, const float* page, float* scratch,
-                          Lds* L, Wait wait) {
-  switch (d.type) {
-    case TT_QKV: return exec_typed<TT_QKV>(P, S, d, lane, page, scratch, L, wait);
-    case TT_ATTN: return exec_typed<TT_ATTN>(P, S, d, lane, page, scratch, L, wait);
-    case TT_MERGE: return exec_typed<TT_MERGE>(P, S, d, lane, page, scratch, L, wait);
-    case TT_O: return exec_typed<TT_O>(P, S, d, lane, page, scratch, L, wait);
-    case TT_GU: return exec_typed<TT_GU>(P, S, d, lane, page, scratch, L, wait);
-    case TT_DOWN: return exec_typed<TT_DOWN>(P, S, d, lane, page, scratch, L, wait);
-    case TT_LM: return exec_typed<TT_LM>(P, S, d, lane, page, scratch, L, wait);
-    case TT_ARGMAX: return exec_typed<TT_ARGMAX>(P, S, d, lane, page, scratch, L, wait);
-    default: return true;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Persistent megakernel
-
-__device__ __forceinline__ bool global_abort(const Params& P) {
-  return __hip_atomic_load(&P.status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-}
-
-// Records the first timeout (who waited, on what, how far it got) and raises
-// the device-wide abort flag that every wait loop polls.
-__device__ void latch_timeout(const Params& P, Lds* L, int cu, const Task& t, uint32_t value, uint32_t need,
-                              uint32_t waiter, int lane) {
-  if (lane == 0) {
-    if (atomicCAS(&P.status[1], ST_OK, ST_TIMEOUT) == ST_OK) {
-      P.status[2] = (uint32_t)cu;
-      P.status[3] = t.id;
-      P.status[4] = t.in_event;
-      P.status[5] = value;
-      P.status[6] = need;
-      P.status[7] = waiter;
-      P.status[8] = lds_load(&L->frontier);
-      P.status[9] = lds_load(&L->ticket);
-    }
-    __hip_atomic_store(&P.status[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds_store(&L->abort, 1u);
-  }
-}
-
-// Bound on one wait: wall clock and an iteration count, whichever trips first.
-struct WaitLimit {
-  uint64_t t0;
-  uint32_t iters;
-  __device__ explicit WaitLimit() : t0(clock_now()), iters(0) {}
-  __device__ bool expired(const Params& P) {
-    return ++iters > P.spin_limit || clock_now() - t0 > P.timeout_ticks;
-  }
-};
-
-__device__ void scheduler(const Params& P, const Step& S, Lds* L, float* pages, int page_floats, int cu, int lane) {
-  const Task* q = P.tasks + P.queue_off[cu];
-  const int n = P.queue_off[cu + 1] - P.queue_off[cu];
-  uint16_t cur_key[2] = {0, 0};
-  uint32_t uses[2] = {0, 0};
-  int last_ev = -1;
-  uint32_t last_need = 0;
-  for (int f = 0; f < n; ++f) {
-    const Task d = q[f];
-    if (d.in_event != kNone16) {
-      const uint32_t need = d.in_count * S.epoch;
-      if (!(d.in_event == last_ev && need <= last_need)) {
-        WaitLimit lim;
-        uint32_t v;
-        while ((v = ld_relaxed_agent(&P.events[d.in_event])) < need) {
-          if (global_abort(P)) { if (lane == 0) lds_store(&L->abort, 1u); return; }
-          if (lim.expired(P)) { latch_timeout(P, L, cu, d, v, need, 0, lane); return; }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        fence_acquire_agent();
-        last_ev = d.in_event;
-        last_need = need;
-      }
-    }
-    if (d.stage) {
-      if (cur_key[d.page] != d.stage) {
-        WaitLimit lim;
-        while (lds_load(&L->page_done[d.page]) < uses[d.page]) {
-          if (global_abort(P)) { if (lane == 0) lds_store(&L->abort, 1u); return; }
-          if (lim.expired(P)) {
-            latch_timeout(P, L, cu, d, lds_load(&L->page_done[d.page]), uses[d.page], 1, lane);
-            return;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        fence_acquire_wg();
-        stage_input(P, S, d.stage, d.batch, pages + d.page * page_floats, lane);
-        cur_key[d.page] = d.stage;
-      }
-      uses[d.page]++;
-    }
-    fence_release_wg();
-    if (lane == 0) lds_store(&L->frontier, (uint32_t)(f + 1));
-  }
-}
-
-__device__ void worker(const Params& P, const Step& S, Lds* L, const float* pages, int page_floats, float* scratch,
-                       int cu, int lane) {
-  const Task* q = P.tasks + P.queue_off[cu];
-  const int n = P.queue_off[cu + 1] - P.queue_off[cu];
-  for (;;) {
-    uint32_t t = 0;
-    if (lane == 0) t = lds_add(&L->ticket, 1u);
-    t = __builtin_amdgcn_readfirstlane(t);
-    if ((int)t >= n) break;
-    const Task d = q[t];
-    bool aborted = false;
-    // The worker's own wait is bounded too: it watches the CU's abort word,
-    // the device-wide abort flag and its own clock / iteration limit, so it
-    // ends even if the scheduler wave can no longer publish anything.
-    auto wait = [&]() -> bool {
-      WaitLimit lim;
-      while (lds_load(&L->frontier) <= t) {
-        if (lds_load(&L->abort) || ((lim.iters & 63) == 0 && global_abort(P))) { aborted = true; return false; }
-        if (lim.expired(P)) {
-          latch_timeout(P, L, cu, d, lds_load(&L->frontier), t + 1, 2, lane);
-          aborted = true;
-          return false;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      fence_acquire_wg();
-      return true;
-    };
-    uint64_t t_start = 0;
-    if (P.trace) t_start = clock_now();
-    const float* page = d.page != kNone8 ? pages + d.page * page_floats : nullptr;
-    if (!exec_task(P, S, d, lane, page, scratch, L, wait) || aborted) break;
-    if (P.trace && lane == 0 && (int)d.id < P.trace_cap) {
-      P.trace[2 * (int64_t)d.id] = ((unsigned long long)cu << 48) | (t_start & 0xFFFFFFFFFFFFull);
-      P.trace[2 * (int64_t)d.id + 1] = clock_now();
-    }
-    if (d.page != kNone8) {
-      fence_release_wg();
-      if (lane == 0) lds_add(&L->page_done[d.page], 1u);
-    }
-    if (d.out_event != kNone16) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached L2
-      fence_release_wg();
-      uint32_t old = 0;
-      if (lane == 0) old = lds_add(&L->slot[d.local_slot], 1u);
-      old = __builtin_amdgcn_readfirstlane(old);
-      if (old + 1 == d.local_count) {
-        if (lane == 0) lds_store(&L->slot[d.local_slot], 0u);
-        fence_acq_rel_agent();
-        if (d.type == TT_LM && lane == 0) {
-          const unsigned long long best =
-              __hip_atomic_load(&L->lm_best[d.batch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          __hip_atomic_fetch_max(&P.lm_part[d.batch], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(&L->lm_best[d.batch], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-        fence_acq_rel_agent();
-        if (lane == 0) __hip_atomic_fetch_add(&P.events[d.out_event], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-}
-
-extern "C" __global__ __launch_bounds__(kWaves * kWave, 1) void mk_persistent(Params P, const Step* Sd,
-                                                                                int page_floats, int scratch_floats) {
-  const Step S = ld_const(Sd);
-  extern __shared__ __align__(16) unsigned char smem[];
-  Lds* L = reinterpret_cast<Lds*>(smem);
-  float* pages = reinterpret_cast<float*>(smem + sizeof(Lds));
-  float* scr = pages + 2 * page_floats;
-  const int cu = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // The last word this kernel uses must hold a value written by another wave:
-  // LDS writes past the workgroup's allocation are dropped and reads return 0.
-  uint32_t* last_word = reinterpret_cast<uint32_t*>(scr + kWorkers * scratch_floats) - 1;
-  if (threadIdx.x == 0) *last_word = kLdsMagic;
-  if (threadIdx.x < kLocalSlots) L->slot[threadIdx.x] = 0;
-  if (threadIdx.x < kMaxBatch) L->lm_best[threadIdx.x] = 0;
-  if (threadIdx.x == 0) {
-    L->frontier = 0;
-    L->ticket = 0;
-    L->abort = global_abort(P) ? 1u : 0u;
-    L->page_done[0] = L->page_done[1] = 0;
-  }
-  __syncthreads();
-  if (threadIdx.x == kWave && *last_word != kLdsMagic) {
-    atomicCAS(&P.status[1], ST_OK, ST_LDS);
-    __hip_atomic_store(&P.status[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (L->abort || global_abort(P)) return;
-  if (wave == 0) scheduler(P, S, L, pages, page_floats, cu, lane);
-  else worker(P, S, L, pages, page_floats, scr + (wave - 1) * scratch_floats, cu, lane);
-}
-
 // ---------------------------------------------------------------------------
 // Kernel-per-operator path: one launch per operator over that operator's
 // tasks, the same bodies.  Wave 0 of each workgroup stages the operator's
@@ -868,7 +450,15 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const O
     }
   } else {
     static_assert(TT == TT_ARGMAX, "per-operator kernels: GEMV operators and the argmax");
-    if (blockIdx.x == 0 && wave == 0) exec_typed<TT>(P, S, first, lane, nullptr, scr, L, wait);
+    // the LM head's running keys -> greedy ids; the keys are cleared for the next step
+    if (blockIdx.x == 0 && wave == 0 && lane == 0) {
+      for (int bb = 0; bb < P.B; ++bb) {
+        const unsigned long long k = __hip_atomic_load(&P.lm_part[bb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        S.out[bb] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+        if (!(fabsf(argmax_key_value(k)) <= 3.0e38f)) atomicCAS(&P.status[1], ST_OK, ST_NONFINITE);  // NaN or Inf won
+        __hip_atomic_store(&P.lm_part[bb], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
   wait();
   if constexpr (TT == TT_LM) {

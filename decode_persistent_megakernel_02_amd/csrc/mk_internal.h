@@ -267,6 +267,42 @@ struct Lds {
   unsigned long long lm_best[kMaxBatch];
 };
 
+// ---- persistent megakernel (one workgroup per CU, fixed wave roles) ----
+constexpr int kMegaStagers = 4;   // waves that stage operator inputs and run attention, merges, argmax
+constexpr int kMegaCompute = 4;   // waves that stream weights (the GEMV tasks), four tasks in flight each
+constexpr int kMegaWaves = kMegaStagers + kMegaCompute;
+
+// Buffers through which workgroups hand values to each other.  Each element
+// is a 64-bit word: fp32 value bits in the low half, the epoch of the step
+// that wrote it in the high half (the dependency signal).
+struct MegaBufs {
+  uint64_t* x;       // [L+1][H] residual stream after layer l-1 (row 0 unused: the embedding row)
+  uint64_t* xmid;    // [L][H] residual after attention
+  uint64_t* qkv;     // [L][(nq + 2 nkv) hd] rotated q, rotated k, v of the current position
+  uint64_t* rec;     // [L][nkv][nsplit][G][hd + 2] attention split records (o[hd], m, l)
+  uint64_t* attn;    // [L][nq hd] merged attention output
+  uint64_t* h;       // [L][F] SwiGLU output
+  uint64_t* key;     // [ncu] each workgroup's LM-head argmax key (epoch mod 2^15 in the low bits)
+  uint32_t* host_abort;          // host-mapped word: nonzero makes every wait give up
+  unsigned long long* trace;     // optional [ops][ncu][kMegaCompute + 1] timestamps, null if off
+};
+
+// LDS header of the megakernel (followed by the two input pages, the
+// residual copy, the RoPE angles, the compute waves' results and the stager
+// waves' query buffers).
+struct alignas(16) MegaLds {
+  uint32_t ready[2];   // page p holds the input of operator ready[p] - 1
+  uint32_t done[2];    // compute-wave completions of the operators on page p (cumulative)
+  uint32_t pool[2];    // task pool counter of the operator on page p
+  uint32_t ssync;      // stager rendezvous counter (cumulative)
+  uint32_t abort;      // nonzero: every wave of the workgroup stops
+  uint32_t lm_done;    // compute waves done with the LM head
+  uint32_t pad[3];
+  float red[kMegaStagers];     // stagers' partial sums of squares
+  unsigned long long lm_best;  // best LM-head key of the workgroup
+  unsigned long long pad2;
+};
+
 // Status codes latched by the kernel.
 enum : uint32_t { ST_OK = 0, ST_TIMEOUT = 1, ST_NONFINITE = 2, ST_BADTOKEN = 3, ST_LDS = 4 };
 constexpr int kStatusWords = 16;

@@ -69,6 +69,8 @@ enum {
                                  replaying the step as one captured HIP graph */
   MK_FLAG_FUSED_MERGE = 1u << 3, /* per-op mode: run the attention log-sum-exp merge in the last
                                     split workgroup of each KV group instead of as its own launch */
+  MK_FLAG_SPIN_LIMIT_1 = 1u << 5, /* test hook: every in-kernel wait gives up after one unsuccessful
+                                     check, so a step ends in MK_ERR_TIMEOUT without any wave hanging */
   MK_FLAG_TILED_WEIGHTS = 1u << 4 /* batched path (max_batch >= 2): wq, wk, wv, wo, w_gate, w_up,
                                      w_down and (untied) lm_head are stored in the tiled layout that
                                      mk_tile_weights writes; embed and the norm gains stay

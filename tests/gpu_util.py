@@ -21,7 +21,7 @@ class Case:
     """One model on the GPU plus its oracle, fed the same seeded inputs."""
 
     def __init__(self, shape, max_seq, mode, seed=0, random_norms=False, attn_split=0, flags=0, num_cus=0,
-                 kv_bf16_oracle=False, weights=None):
+                 kv_bf16_oracle=False, weights=None, watchdog_ms=0):
         """kv_bf16_oracle: the GPU keeps a bf16 KV cache and the oracle rounds its
         cached K/V to bf16 the same way; otherwise both keep full precision."""
         from decode_persistent_megakernel_02_amd import abi, runtime
@@ -29,7 +29,7 @@ class Case:
         self.shape = shape
         self.w = weights if weights is not None else gen.gen_weights(shape, seed, random_norms)
         self.dw = runtime.upload_weights(self.w)
-        self.h = runtime.create(shape, self.dw, max_seq, 1, mode, flags, 0, num_cus, attn_split,
+        self.h = runtime.create(shape, self.dw, max_seq, 1, mode, flags, watchdog_ms, num_cus, attn_split,
                                 kv_fp32=not kv_bf16_oracle)
         self.oracle = D.Decoder(shape, self.w, 1, max_seq, kv_bf16=kv_bf16_oracle)
         self.V = shape.vocab

@@ -94,18 +94,39 @@ def test_create_rejects_null_weights_without_touching_gpu():
     assert "NULL" in abi.mk_last_error()
 
 
-def test_megakernel_mode_is_refused_before_any_gpu_call():
-    c = cfg_for(MINI, mode=abi.MK_MODE_MEGAKERNEL)
-    L = c.n_layers
+def _fake_weights(L):
     fake = [ctypes.c_void_p(0x1000 + 16 * i) for i in range(9 * L + 3)]
     arrs = [(ctypes.c_void_p * L)(*fake[3 + i * L:3 + (i + 1) * L]) for i in range(9)]
     w = abi.mk_weights()
     w.embed, w.lm_head, w.final_norm = fake[0], fake[1], fake[2]
     for f, a in zip(abi.LAYER_FIELDS, arrs):
         setattr(w, f, ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)))
+    return w, arrs
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(max_batch=2, kv_fp32=False), "MK_ERR_UNSUPPORTED", "max_batch 1"),
+    (dict(flags=4), "MK_ERR_INVALID_ARG", "per-operator flags"),       # MK_FLAG_NO_GRAPH
+    (dict(flags=8), "MK_ERR_INVALID_ARG", "per-operator flags"),       # MK_FLAG_FUSED_MERGE
+])
+def test_megakernel_limits_are_checked_before_any_gpu_call(kw, status, msg):
+    c = cfg_for(MINI, mode=abi.MK_MODE_MEGAKERNEL, **kw)
+    w, keep = _fake_weights(c.n_layers)
     out = ctypes.c_void_p()
     st = abi.lib.mk_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(out))
-    assert st == abi.MK_ERR_UNSUPPORTED and "MK_MODE_PER_OP" in abi.mk_last_error()
+    assert st == getattr(abi, status) and msg in abi.mk_last_error(), abi.mk_last_error()
+
+
+def test_megakernel_split_keeps_one_attention_unit_per_workgroup():
+    """Megakernel attention splits are whole rounds of the stager waves'
+    position blocks, the fewest that keep (KV head, split) units within one per
+    workgroup: 8B shape, 39 + 512 (+ 64 spare) positions, fp32 cache -> 32."""
+    for shape, max_seq, f32, want in ((presets.LLAMA8B, 615, True, 32), (presets.LLAMA1B, 615, True, 64),
+                                     (presets.LLAMA8B, 615, False, 64), (presets.LLAMA8B, 4224, True, 160)):
+        c = cfg_for(shape, max_seq=max_seq, mode=abi.MK_MODE_MEGAKERNEL, kv_fp32=f32)
+        info = abi.mk_graph_inspect(c, 256)
+        assert info.split == want, (shape.name, max_seq, f32, info.split)
+        assert shape.n_kv_heads * info.nsplit <= 256
 
 
 def test_task_graph_is_single_sequence():

@@ -1,0 +1,170 @@
+"""The persistent megakernel (one launch per decode step) against the oracle
+and against the kernel-per-operator build of the same task bodies.
+
+Bars (as in test_gpu_decode):
+  * logits: max|gpu - oracle| / max|oracle| <= 2e-2 per step against the fp64
+    oracle; <= 1e-3 against the oracle with the GPU's KV-cache rounding;
+  * tokens: equal wherever the oracle's top-2 margin exceeds 5e-2;
+  * megakernel vs per-operator build: the same arithmetic up to the order of
+    fp32 sums in RMSNorm, attention and the split merge, so their logits agree
+    to 1e-5 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decoder as D
+from synth import gen, presets
+from tests.gpu_util import Case, rel_err
+from tests.shapes import MINI, MINI_TIED, MINI_G8, MINI_HD128_G1, MINI_HD128_G2
+
+pytestmark = pytest.mark.gpu
+
+CONTRACT = 2e-2
+TIGHT = 1e-3
+MARGIN = 5e-2
+MEGA, PER_OP = 0, 1
+WATCHDOG_MS = 500  # in-kernel wait limit for these small cases
+
+
+@pytest.fixture(scope="module")
+def abi():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_persistent_megakernel_02_amd import abi as a
+    return a
+
+
+def check_step(g, r, nxt, errs, bar):
+    e = float(rel_err(g, r))
+    errs.append(e)
+    assert e <= bar, f"logit error {e:.3e} > {bar}"
+    if D.top2_margin(r) > MARGIN:
+        assert nxt == int(D.greedy(r)), "greedy token differs at a clear margin"
+
+
+def teacher_forced(case, prompt, steps, bar):
+    errs = []
+    g, r, nxt = case.prefill(prompt)
+    check_step(g, r, nxt, errs, bar)
+    tok = int(D.greedy(r))
+    for _ in range(steps):
+        g, r, nxt = case.step(tok)
+        check_step(g, r, nxt, errs, bar)
+        tok = int(D.greedy(r))
+    return errs
+
+
+def test_tiny_workload_teacher_forced(abi):
+    wl = presets.WORKLOADS["tiny"]
+    case = Case(wl.shape, wl.max_seq, MEGA, watchdog_ms=WATCHDOG_MS)
+    errs = teacher_forced(case, gen.gen_prompt(wl)[0], wl.decode_steps, CONTRACT)
+    print(f"tiny megakernel: max rel err {max(errs):.2e}")
+    assert max(errs) <= TIGHT
+
+
+def test_tiny_tight_against_bf16_kv_oracle(abi):
+    wl = presets.WORKLOADS["tiny"]
+    case = Case(wl.shape, wl.max_seq, MEGA, kv_bf16_oracle=True, watchdog_ms=WATCHDOG_MS)
+    teacher_forced(case, gen.gen_prompt(wl)[0], wl.decode_steps, TIGHT)
+
+
+@pytest.mark.parametrize("shape", [MINI, MINI_TIED, MINI_G8, MINI_HD128_G1, MINI_HD128_G2], ids=lambda s: s.name)
+@pytest.mark.parametrize("kv_bf16", [False, True], ids=["kv_f32", "kv_bf16"])
+def test_ragged_shapes_multi_split(abi, shape, kv_bf16):
+    # 16-position attention splits, prompt 21 + 14 steps: positions span 3 splits
+    case = Case(shape, 40, MEGA, seed=5, random_norms=True, attn_split=16, kv_bf16_oracle=kv_bf16,
+                watchdog_ms=WATCHDOG_MS)
+    prompt = gen.tokens(9, 3, 0, 21, shape.vocab)
+    teacher_forced(case, prompt, 14, TIGHT)
+
+
+@pytest.mark.parametrize("shape", [MINI_G8, MINI], ids=lambda s: s.name)
+def test_megakernel_agrees_with_per_op(abi, shape):
+    """Same weights, same tokens: the two builds differ only in the order of
+    fp32 sums (norm, attention, merge)."""
+    prompt = gen.tokens(4, 3, 0, 9, shape.vocab)
+    w = gen.gen_weights(shape, 2, True)
+    outs = []
+    for mode in (MEGA, PER_OP):
+        case = Case(shape, 24, mode, attn_split=8, weights=w, watchdog_ms=WATCHDOG_MS)
+        outs.append(np.stack([case.prefill(prompt)[0]] + [case.step(t)[0] for t in (3, 77, 200, 5, 9, 11)]))
+    err = np.abs(outs[0] - outs[1]).max() / np.abs(outs[1]).max()
+    assert err <= 1e-5, err
+
+
+def test_free_running_matches_until_low_margin(abi):
+    from decode_persistent_megakernel_02_amd import runtime
+    wl = presets.WORKLOADS["tiny"]
+    shape = wl.shape
+    w = gen.gen_weights(shape, 0)
+    dw = runtime.upload_weights(w)
+    h = runtime.create(shape, dw, wl.max_seq, mode=MEGA, watchdog_ms=WATCHDOG_MS)
+    prompt = gen.gen_prompt(wl)
+    toks = torch.zeros(wl.decode_steps + 1, dtype=torch.int32, device="cuda")
+    abi.mk_prefill(h, torch.from_numpy(prompt).cuda(), toks[0:1])
+    for s in range(wl.decode_steps):  # device-side feedback, no host sync
+        abi.mk_decode_step(h, toks[s:s + 1], toks[s + 1:s + 2])
+    abi.mk_synchronize(h)
+    gpu = toks.cpu().numpy()
+    ref_tokens, ref_logits = D.Decoder(shape, w, 1, wl.max_seq).generate(prompt, wl.decode_steps)
+    last = D.Decoder(shape, w, 1, wl.max_seq).prefill(prompt)[0]
+    margins = [D.top2_margin(last)] + [D.top2_margin(ref_logits[0, s]) for s in range(wl.decode_steps)]
+    ref_seq = [int(D.greedy(last))] + list(ref_tokens[0])
+    for s in range(wl.decode_steps + 1):
+        if margins[s] <= MARGIN:
+            break
+        assert gpu[s] == ref_seq[s], f"step {s}"
+
+
+def test_llama1b_shape_two_layers(abi):
+    """The exact (no clamped loads) instance at head_dim 64."""
+    shape = presets.with_layers(presets.LLAMA1B, 2)
+    case = Case(shape, 48, MEGA, watchdog_ms=2000)
+    teacher_forced(case, gen.tokens(1001, 3, 0, 39, shape.vocab), 4, TIGHT)
+
+
+def test_reset_and_capacity(abi):
+    shape = MINI
+    case = Case(shape, 5, MEGA, watchdog_ms=WATCHDOG_MS)
+    prompt = gen.tokens(1, 3, 0, 4, shape.vocab)
+    a = case.prefill(prompt)[0]
+    case.step(5)
+    with pytest.raises(abi.MkError) as e:
+        abi.mk_decode_step(case.h, case.tok, case.out, case.logits)
+    assert e.value.status == abi.MK_ERR_CAPACITY
+    abi.mk_reset(case.h)
+    p = torch.from_numpy(prompt.reshape(1, -1)).cuda()
+    abi.mk_prefill(case.h, p, case.out, case.logits)
+    abi.mk_synchronize(case.h)
+    assert np.array_equal(case.logits.cpu().numpy()[0], a)
+
+
+def test_batched_config_is_refused(abi):
+    from decode_persistent_megakernel_02_amd import runtime
+    shape = MINI
+    dw = runtime.upload_weights(gen.gen_weights(shape, 0))
+    with pytest.raises(abi.MkError) as e:
+        runtime.create(shape, dw, 16, max_batch=2, mode=MEGA, kv_fp32=False)
+    assert e.value.status == abi.MK_ERR_UNSUPPORTED
+
+
+def test_watchdog_ends_a_step_with_timeout(abi):
+    """MK_FLAG_SPIN_LIMIT_1 makes every in-kernel wait give up after one
+    unsuccessful check (the host forces the condition; every wave still
+    exits): the step returns MK_ERR_TIMEOUT and poisons the handle, and a new
+    handle works."""
+    shape = MINI
+    w = gen.gen_weights(shape, 7)
+    case = Case(shape, 16, MEGA, weights=w, flags=abi.MK_FLAG_SPIN_LIMIT_1)
+    p = torch.from_numpy(gen.tokens(2, 3, 0, 3, shape.vocab).reshape(1, -1)).cuda()
+    abi.mk_prefill(case.h, p, case.out, case.logits)
+    with pytest.raises(abi.MkError) as e:
+        abi.mk_synchronize(case.h)
+    assert e.value.status == abi.MK_ERR_TIMEOUT
+    with pytest.raises(abi.MkError) as e:
+        abi.mk_decode_step(case.h, case.tok, case.out, case.logits)
+    assert e.value.status == abi.MK_ERR_STATE
+    ok = Case(shape, 16, MEGA, weights=w, watchdog_ms=WATCHDOG_MS)
+    g, r, _ = ok.prefill(gen.tokens(2, 3, 0, 3, shape.vocab))
+    assert rel_err(g, r) <= TIGHT
