@@ -6,21 +6,23 @@ heads of 128, FFN 14336, vocab 128256), random bf16 weights, batch 1, a 39-token
 seeded prompt and 512 greedy decode steps -- the 39/512 workload of the MPK
 write-up, on synthetic inputs.  Prints ONE JSON line.
 
-Protocol: W untimed warm-up decode steps, reset + prefill, then exactly K
-decode steps with device-side token feedback, bracketed by synchronize.  The
-step runs in kernel-per-operator mode, one HIP graph per step (the persistent
-single-launch mode is refused by the library on this device).  The dominant
-kernel's duration (gate/up projection + SwiGLU, the roofline figure) comes
-from back-to-back replays of its launches for every layer between two HIP
-events on the decode stream; an eager pass with an event pair around each
-launch, a per-operator breakdown and replays of the other operators are
-reported beside it.  The oracle's time on a bounded sample is reported as
-cpu_baseline.
+Headline: the persistent megakernel, one launch per decode step.  Protocol,
+for the megakernel and for the kernel-per-operator build of the same task
+bodies (one HIP graph per step) alike: one warm-up generation (prefill + W
+decode steps), then five runs of reset + prefill + exactly K decode steps with
+device-side token feedback between two HIP events on the decode stream; the
+value is the median run.  A sixth run brackets every step with events for the
+per-step p50/p99.  The roofline entry is the megakernel dispatch itself:
+whole-step algorithmic bytes over its duration.  A traced megakernel run gives
+the time the compute waves wait between operators; a streaming-read probe
+gives the measured HBM ceiling; the oracle's host time on a bounded sample is
+reported as cpu_baseline.
 
 `--workload llama8b_b8_kv4096` (8 sequences, 4096-token prompts, 128 steps)
 and `--workload llama70b_b64` (the 70B shape, 64 sequences, 512-token prompts,
-64 steps) time the batched path the same way; their unit is ms per step (one
-token for every sequence) and they carry no cpu_baseline.
+64 steps) time the batched path (per-operator launches, matrix cores); their
+unit is ms per step (one token for every sequence) and they carry no
+cpu_baseline.
 """
 import argparse
 import hashlib
@@ -95,6 +97,95 @@ def run_steps(abi, h, toks, first, steps):
         abi.mk_decode_step(h, toks[s], toks[s + 1])
 
 
+def protocol(abi, h, prompt_t, steps, warmup, torch, runs=5, log=lambda *a: None, name=""):
+    """Warm-up generation, then `runs` timed runs (reset + prefill + `steps`
+    decode steps between two events) and one run with an event pair around
+    every step.  Returns (median ms/step, run totals, per-step ms, tokens)."""
+    B = prompt_t.shape[0]
+    toks = torch.zeros(max(steps, warmup) + 1, B, dtype=torch.int32, device="cuda")
+    abi.mk_prefill(h, prompt_t, toks[0])
+    run_steps(abi, h, toks, 0, warmup)
+    abi.mk_synchronize(h)
+    totals = []
+    for r in range(runs):
+        total, _ = timed_pass(abi, h, prompt_t, toks, steps, torch)
+        totals.append(total)
+        log(f"{name} run {r + 1}/{runs}: {total / steps:.4f} ms/step")
+    tokens = toks[:steps + 1].cpu().numpy()
+    abi.mk_reset(h)
+    abi.mk_prefill(h, prompt_t, toks[0])
+    abi.mk_synchronize(h)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for s in range(steps):
+        abi.mk_decode_step(h, toks[s], toks[s + 1])
+        ev[s + 1].record()
+    torch.cuda.synchronize()
+    abi.mk_synchronize(h)
+    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(steps)]
+    totals.sort()
+    return totals[len(totals) // 2] / steps, totals, per, tokens
+
+
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def mega_overhead(abi, shape, dw, prompt_t, steps, torch, dump=None):
+    """Traced megakernel steps (the last one is analysed), per operator k and
+    workgroup w: publish time of k's input page and the end of k's tasks.
+      wait: compute waves idle between finishing k-1 and k's input being
+            staged (0 when it was staged first);
+      skew: how much later than the median workgroup the last one finished k-1;
+      latency: from the last workgroup finishing k-1 to the median workgroup
+            publishing k's input (signal propagation + staging).
+    In microseconds; per operator type (the input of QKV is the previous
+    layer's down output, of O the attention merge, ...)."""
+    import numpy as np
+    h = runtime_create(shape, dw, prompt_t.shape[1] + steps + 1, abi.MK_MODE_MEGAKERNEL, abi.MK_FLAG_TRACE, abi)
+    toks = torch.zeros(steps + 1, 1, dtype=torch.int32, device="cuda")
+    abi.mk_prefill(h, prompt_t, toks[0])
+    run_steps(abi, h, toks, 0, steps)
+    abi.mk_synchronize(h)
+    tr, tpu = abi.mk_mega_trace(h)
+    abi.mk_destroy(h)
+    if dump:
+        np.save(dump, tr)
+    ops, ncu, slots = tr.shape
+    nc = slots - 3  # compute waves; then the stager's publish, poll-start and input-complete times
+    end = (tr[:, :, :nc] & np.uint64(0xFFFFFFFF)).astype(np.int64)
+    dur = (tr[:, :, :nc] >> np.uint64(32)).astype(np.int64)
+    pub = (tr[:, :, nc] & np.uint64(0xFFFFFFFF)).astype(np.int64)
+    got = (tr[:, :, nc + 2] & np.uint64(0xFFFFFFFF)).astype(np.int64)
+    base = int(pub[0].min())
+    rel = lambda a: ((a - base) % (1 << 32)).astype(np.int64) / tpu   # us since the first publish
+    end_us, pub_us, got_us = rel(end).max(axis=2), rel(pub), rel(got)  # [ops, ncu]
+    wait = np.maximum(pub_us[1:] - end_us[:-1], 0.0)
+    skew = end_us[:-1].max(axis=1) - np.median(end_us[:-1], axis=1)
+    lat = np.median(pub_us[1:], axis=1) - end_us[:-1].max(axis=1)
+    stage = np.median(pub_us[1:] - got_us[1:], axis=1)   # input complete -> published (norm, rendezvous)
+    run = dur.max(axis=2) / tpu
+    names = ("qkv", "o", "gu", "down")
+    by = lambda a, i: float(np.median(a[(np.arange(1, ops) % 4) == i])) if ops > 1 else 0.0
+    return {"wait_us_median": float(np.median(wait)), "wait_us_p90": pct(wait.reshape(-1), 90),
+            "wait_us_per_step": float(wait.sum(axis=0).mean()),
+            "wait_us_median_by_op": {n: by(np.median(wait, axis=1), i) for i, n in enumerate(names)},
+            "skew_us_median_by_op_input": {n: by(skew, i) for i, n in enumerate(names)},
+            "latency_us_median_by_op_input": {n: by(lat, i) for i, n in enumerate(names)},
+            "stage_us_median_by_op": {n: by(stage, i) for i, n in enumerate(names)},
+            "op_run_us_median": {n: float(np.median(run[i::4][:shape.n_layers])) for i, n in enumerate(names)},
+            "lm_head_run_us_median": float(np.median(run[-1])),
+
+            "steps_traced": steps}
+
+
+def runtime_create(shape, dw, max_seq, mode, flags, abi):
+    from decode_persistent_megakernel_02_amd import runtime
+    return runtime.create(shape, dw, max_seq, 1, mode, flags, kv_fp32=True)
+
+
 def timed_pass(abi, h, prompt_t, toks, steps, torch, time_types=()):
     """reset + prefill, then exactly `steps` decode steps between two events."""
     abi.mk_reset(h)
@@ -114,27 +205,6 @@ def timed_pass(abi, h, prompt_t, toks, steps, torch, time_types=()):
     return t0.elapsed_time(t1), times
 
 
-def time_decode(abi, h, prompt_t, steps, warmup, shape, torch, log=lambda *a: None):
-    """Headline pass (graph-replayed steps), then an eager pass whose gate/up
-    launches are bracketed by HIP events, then an untimed per-operator breakdown."""
-    B = prompt_t.shape[0]
-    toks = torch.zeros(max(steps, warmup) + 64 + 1, B, dtype=torch.int32, device=torch.device("cuda"))
-    abi.mk_prefill(h, prompt_t, toks[0])                         # warm-up generation
-    run_steps(abi, h, toks, 0, warmup)
-    abi.mk_synchronize(h)
-    log("warm-up done; timed pass")
-    total, _ = timed_pass(abi, h, prompt_t, toks, steps, torch)
-    tokens = toks[:steps + 1].cpu().numpy()
-    log(f"timed pass: {total / steps:.4f} ms/step; eager pass with gate/up events")
-    eager_total, times = timed_pass(abi, h, prompt_t, toks, steps, torch, ["gu"])
-    gu = times.get("gu", (0.0, 0))
-    same = bool((toks[:steps + 1].cpu().numpy() == tokens).all())
-    abi.mk_time_ops(h, list(abi.OP_TYPES), 32 * (12 * shape.n_layers + 4))  # every launch of 32 steps
-    run_steps(abi, h, toks, steps, 32)
-    breakdown = abi.mk_read_op_times(h)
-    return total, eager_total, gu, same, breakdown
-
-
 def cpu_baseline(shape, weights, prompt):
     """The oracle as it stands on the host: one fp64 decode step (position 0)."""
     from oracle import decoder as D
@@ -152,9 +222,26 @@ def cpu_baseline(shape, weights, prompt):
     for i in range(n):
         dec.step(prompt[:, i])
     ms = (time.perf_counter() - t) * 1000.0 / n
+    # the oracle widens each bf16 matrix to fp64 when it uses it (a 15 GB model
+    # does not fit the host in fp64); that widening alone, timed the same way:
+    t = time.perf_counter()
+    for name in weights:
+        if name != "embed" or shape.tie_embeddings:
+            D.widen_bf16(weights[name])
+    widen = (time.perf_counter() - t) * 1000.0
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": ms, "unit": "ms/token", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} fp64 decode steps of the {shape.name} shape at positions 0 and 1 "
-                      "(weights widened per use), averaged"}
+            "sample": f"{n} fp64 decode steps of the {shape.name} shape at positions 0 and 1, averaged; each "
+                      "step widens the bf16 weights to fp64 as it uses them",
+            "widening_ms_per_step": widen, "arithmetic_ms_per_step": ms - widen,
+            "host_cpu": cpu, "os_cpu_count": os.cpu_count()}
 
 
 def main():
@@ -165,6 +252,13 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--no-megakernel", action="store_true", help="time only the per-operator build")
+    ap.add_argument("--no-trace", action="store_true", help="skip the traced megakernel steps")
+    ap.add_argument("--trace-dump", default=None, metavar="FILE.npy", help="save the raw megakernel trace")
+    ap.add_argument("--no-per-op", action="store_true", help="skip the per-operator baseline (quick runs)")
+    ap.add_argument("--no-stream-probe", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--counters-mode", choices=("mega", "per_op"), default="mega",
+                    help="with --counters: which build's launches the counter run sees")
     ap.add_argument("--fused-merge", action="store_true",
                     help="merge attention splits in the last split workgroup instead of a separate launch")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -232,8 +326,12 @@ def main():
     if args.counters:
         if args.counters_prompt:
             prompt_t = prompt_t[:, :args.counters_prompt].contiguous()
-        h = runtime.create(shape, dw, prompt_t.shape[1] + args.counters + 1, B, abi.MK_MODE_PER_OP,
-                           flags | abi.MK_FLAG_NO_GRAPH, attn_split=args.attn_split, kv_fp32=kv_fp32)
+        if B == 1 and args.counters_mode == "mega":
+            h = runtime.create(shape, dw, prompt_t.shape[1] + args.counters + 1, 1, abi.MK_MODE_MEGAKERNEL, 0,
+                               attn_split=args.attn_split, kv_fp32=True)
+        else:
+            h = runtime.create(shape, dw, prompt_t.shape[1] + args.counters + 1, B, abi.MK_MODE_PER_OP,
+                               flags | abi.MK_FLAG_NO_GRAPH, attn_split=args.attn_split, kv_fp32=kv_fp32)
         toks = torch.zeros(args.counters + 1, B, dtype=torch.int32, device="cuda")
         abi.mk_prefill(h, prompt_t, toks[0])
         for s in range(args.counters):
@@ -243,56 +341,60 @@ def main():
         abi.mk_destroy(h)
         print(json.dumps({"counter_pass_steps": args.counters, "workload": wl.name}))
         return
-    h = runtime.create(shape, dw, max_seq + 64, B, abi.MK_MODE_PER_OP, flags, attn_split=args.attn_split,
-                       kv_fp32=kv_fp32)
-    total, eager_total, (gu_ms, gu_n), same_tokens, breakdown = time_decode(abi, h, prompt_t, steps, warmup, shape,
-                                                                             torch, log)
-    view = abi.mk_get_debug_view(h)
-    gu_exact = bool(view.exact_ops & (1 << abi.TASK_TYPES["gu"]))
-    op_grid = {k: view.op_grid[v] for k, v in abi.TASK_TYPES.items() if view.op_grid[v]}
-    # The gate/up launches of every layer replayed back to back between two
-    # events: per-launch time without the cost of an event pair around each
-    # launch (cycling through the layers keeps the weights out of the caches).
-    reps = 64 if B == 1 else 8
-    rep_ms, rep_launches = abi.mk_time_op_replay(h, "gu", reps)
-    log(f"gate/up replay: {rep_launches} launches in {rep_ms:.2f} ms")
-    # every operator that can be replayed, the same way: us per layer
-    replay_us = {}
-    for name in (["norm"] if B > 1 else []) + ["qkv", "attn", "merge", "o", "gu", "down"]:
-        if B > 1 and name == "qkv":
-            continue  # appends to the KV cache; not replayable on the batched path
-        ms_r, n_r = abi.mk_time_op_replay(h, name, 8)
-        if n_r:
-            replay_us[name] = {"us_per_layer": 1e3 * ms_r / (8 * shape.n_layers),
-                               "launches_per_layer": n_r / (8 * shape.n_layers)}
-    log("replayed operators (us per layer): " +
-        ", ".join(f"{k} {v['us_per_layer']:.1f}" for k, v in replay_us.items()))
-    abi.mk_destroy(h)
-    ms = total / steps
-    kern_ms = rep_ms / (reps * shape.n_layers)  # one layer's gate/up operator
-    per_layer = rep_launches // (reps * shape.n_layers)  # 2 when a split-K finishing launch follows
-    eager_kern_ms = gu_ms * per_layer / max(gu_n, 1)
     bytes_steps = [step_bytes(shape, wl.prompt_len + s + 1, B, 4 if kv_fp32 else 2) for s in range(steps)]
     alg_bytes = float(np.mean(bytes_steps))
     bound_ms = alg_bytes / (PEAK_GBPS * 1e9) * 1e3
-    kb = gu_bytes(shape, B)
-    achieved = kb / (kern_ms * 1e-3) / 1e9
     unit = "ms/token" if B == 1 else "ms/step"
-    log(f"per-op: {ms:.4f} {unit}, bound {bound_ms:.4f} ms, step {alg_bytes / (ms * 1e-3) / 1e9:.0f} GB/s; "
-        f"gate/up kernel {kern_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
-    op_breakdown = {k: {"ms_per_step": v[0] / 32.0, "launches_per_step": v[1] / 32.0} for k, v in breakdown.items()}
-    log("breakdown (ms/step): " + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in op_breakdown.items()))
-    traffic = load_traffic(wl.name)
-    if B == 1:
-        gu_kernel = "mk_op_gu_x" if gu_exact else "mk_op_gu"
+
+    mega = None
+    if B == 1 and not args.no_megakernel:
+        h = runtime.create(shape, dw, max_seq + 64, 1, abi.MK_MODE_MEGAKERNEL, 0, attn_split=args.attn_split,
+                           kv_fp32=True)
+        mega_ms, mega_runs, mega_per, mega_tokens = protocol(abi, h, prompt_t, steps, warmup, torch, log=log,
+                                                             name="megakernel")
+        split = abi.mk_get_debug_view(h).split
+        abi.mk_destroy(h)
+        mega = {"ms_per_token": mega_ms, "runs_ms_per_token": [t / steps for t in mega_runs],
+                "step_p50_ms": pct(mega_per, 50), "step_p99_ms": pct(mega_per, 99),
+                "attn_split": split, "kernel": mega_kernel_name(shape)}
+        log(f"megakernel: {mega_ms:.4f} ms/token (median of 5), p50 {mega['step_p50_ms']:.4f}, "
+            f"p99 {mega['step_p99_ms']:.4f} ms; bound {bound_ms:.4f} ms")
+        if not args.no_trace:
+            mega["overhead"] = mega_overhead(abi, shape, dw, prompt_t, 8, torch, dump=args.trace_dump)
+            log(f"megakernel operator-boundary wait: median {mega['overhead']['wait_us_median']:.2f} us, "
+                f"{mega['overhead']['wait_us_per_step']:.1f} us per step")
+
+    per_op, op_ms, op_tokens = None, None, None
+    if not (args.no_per_op and mega is not None):
+        per_op, op_ms, op_tokens, gu_gbps, kern_ms, kb, gu_kernel = per_op_baseline(
+            abi, runtime, shape, dw, prompt_t, steps, warmup, max_seq, B, flags, args, kv_fp32, tiled, wl, torch, log)
+
+    ceiling = None
+    if B == 1 and not args.no_stream_probe:
+        buf = torch.empty(1 << 30, dtype=torch.int32, device="cuda").fill_(1)  # 4 GiB
+        ceiling = {}
+        for wgs, loads in ((256, 4), (256, 8), (512, 8), (1024, 8)):
+            ms = abi.mk_t_stream_read(buf, wgs, loads, reps=5)
+            ceiling[f"{wgs}x512_threads_{loads}_loads"] = buf.numel() * 4 / (ms * 1e-3) / 1e9
+        del buf
+        log("streaming-read ceiling (GB/s): " + ", ".join(f"{k} {v:.0f}" for k, v in ceiling.items()))
+
+    if mega is not None:
+        ms = mega["ms_per_token"]
+        achieved = alg_bytes / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / PEAK_GBPS, "traffic": load_traffic(wl.name + "_mega"),
+                    "kernel": mega["kernel"], "kernel_avg_ms": ms,
+                    "algorithmic_bytes_per_launch": alg_bytes,
+                    "timing": "one megakernel dispatch per step: median of 5 runs of the decode steps between two "
+                              "HIP events on the decode stream"}
+        mode = "megakernel (one persistent launch per step)"
     else:
-        bt = 1 if B <= 16 else 2 if B <= 32 else 4
-        # the library gives a wave two row groups at four batch tiles when the
-        # operator has at least half a CU's worth of groups per CU
-        ncu = torch.cuda.get_device_properties(0).multi_processor_count
-        gpw2 = bt == 4 and -(-shape.ffn // 16) // 8 >= ncu // 2
-        gu_kernel = (f"mk_b_gu_b{bt}" + ("_t" if tiled else "") + ("_g2" if gpw2 else "")
-                     + (" + mk_b_fin_gu" if per_layer > 1 else ""))
+        ms = op_ms
+        roofline = {"bound": "hbm", "achieved": gu_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
+                    "frac": gu_gbps / PEAK_GBPS, "traffic": load_traffic(wl.name), "kernel": gu_kernel,
+                    "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": kb}
+        mode = per_op["mode"]
     res = {
         "metric": METRIC if wl.name == "llama8b" else f"ms/step decode ({wl.name}, batch {B}), 1 MI355X",
         "value": ms,
@@ -307,8 +409,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: batch {B}, prompt {wl.prompt_len}, {steps} greedy decode steps",
-                   "batch": B, "prompt_len": wl.prompt_len, "decode_steps": steps,
-                   "mode": "per_op (HIP graph per step)" + (", fused merge" if args.fused_merge else ""),
+                   "batch": B, "prompt_len": wl.prompt_len, "decode_steps": steps, "mode": mode,
                    "kv_cache": "fp32" if kv_fp32 else "bf16",
                    "attn_split": args.attn_split or "library default",
                    "weights": "tiled" if tiled else "row-major",
@@ -316,22 +417,16 @@ def main():
         "tokens_per_s": 1000.0 * B / ms,
         "achieved_gbps": alg_bytes / (ms * 1e-3) / 1e9,
         "bound_ms_per_token": bound_ms,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBPS, "traffic": traffic,
-                     "kernel": gu_kernel, "kernel_avg_ms": kern_ms, "algorithmic_bytes_per_launch": kb,
-                     "timing": f"{reps} back-to-back replays of the {shape.n_layers} layers' gate/up launches "
-                               "between two HIP events on the decode stream",
-                     "kernel_avg_ms_event_pair_per_launch": eager_kern_ms},
         "step_frac_of_hbm_bound": bound_ms / ms,
-        "eager_ms_per_step": eager_total / steps,
-        "graph_and_eager_tokens_equal": same_tokens,
-        "op_breakdown": op_breakdown,
-        "op_replay_us_per_layer": replay_us,
-        "op_grid": op_grid,
-        "megakernel": {"status": "disabled", "reason": "cooperative persistent launch did not complete on MI355X"},
+        "roofline": roofline,
+        "megakernel": mega,
+        "per_op_baseline": per_op,
+        "megakernel_speedup_over_per_op": (op_ms / mega["ms_per_token"]) if mega and op_ms else None,
+        "streaming_read_ceiling_gbps": ceiling,
+        "tokens_equal_megakernel_per_op": bool((mega_tokens == op_tokens).all()) if mega and op_ms else None,
         "cpu_baseline": None,
     }
-    if B > 1:
+    if B > 1 and per_op:
         gu_flop = 2.0 * B * 2 * shape.ffn * shape.hidden
         res["gu_matrix_core_tflops"] = gu_flop / (kern_ms * 1e-3) / 1e12
         res["gu_matrix_core_frac_of_bf16_peak"] = res["gu_matrix_core_tflops"] / 2500.0
@@ -339,6 +434,74 @@ def main():
         log("timing the oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(shape, weights, prompt)
     print(json.dumps(res), flush=True)
+
+
+def per_op_baseline(abi, runtime, shape, dw, prompt_t, steps, warmup, max_seq, B, flags, args, kv_fp32, tiled, wl, torch, log):
+    """The kernel-per-operator build, same protocol; plus its gate/up kernel roofline, replays and breakdown."""
+    h = runtime.create(shape, dw, max_seq + 64, B, abi.MK_MODE_PER_OP, flags, attn_split=args.attn_split,
+                       kv_fp32=kv_fp32)
+    op_ms, op_runs, op_per, op_tokens = protocol(abi, h, prompt_t, steps, warmup, torch, log=log, name="per-op")
+    # per-operator breakdown (eager launches bracketed by events) of 32 more steps
+    toks = torch.zeros(33, B, dtype=torch.int32, device="cuda")
+    toks[0] = torch.from_numpy(op_tokens[-1]).cuda()
+    abi.mk_time_ops(h, list(abi.OP_TYPES), 32 * (12 * shape.n_layers + 4))
+    run_steps(abi, h, toks, 0, 32)
+    breakdown = abi.mk_read_op_times(h)
+    view = abi.mk_get_debug_view(h)
+    gu_exact = bool(view.exact_ops & (1 << abi.TASK_TYPES["gu"]))
+    op_grid = {k: view.op_grid[v] for k, v in abi.TASK_TYPES.items() if view.op_grid[v]}
+    # The gate/up launches of every layer replayed back to back between two
+    # events: per-launch time without the cost of an event pair around each
+    # launch (cycling through the layers keeps the weights out of the caches).
+    reps = 64 if B == 1 else 8
+    rep_ms, rep_launches = abi.mk_time_op_replay(h, "gu", reps)
+    log(f"gate/up replay: {rep_launches} launches in {rep_ms:.2f} ms")
+    replay_us = {}
+    for name in (["norm"] if B > 1 else []) + ["qkv", "attn", "merge", "o", "gu", "down"]:
+        if B > 1 and name == "qkv":
+            continue  # appends to the KV cache; not replayable on the batched path
+        ms_r, n_r = abi.mk_time_op_replay(h, name, 8)
+        if n_r:
+            replay_us[name] = {"us_per_layer": 1e3 * ms_r / (8 * shape.n_layers),
+                               "launches_per_layer": n_r / (8 * shape.n_layers)}
+    log("replayed operators (us per layer): " +
+        ", ".join(f"{k} {v['us_per_layer']:.1f}" for k, v in replay_us.items()))
+    abi.mk_destroy(h)
+    kern_ms = rep_ms / (reps * shape.n_layers)  # one layer's gate/up operator
+    kb = gu_bytes(shape, B)
+    gu_gbps = kb / (kern_ms * 1e-3) / 1e9
+    log(f"per-op: {op_ms:.4f} {unit} (median of 5), gate/up kernel {kern_ms * 1e3:.1f} us = {gu_gbps:.0f} GB/s")
+    op_breakdown = {k: {"ms_per_step": v[0] / 32.0, "launches_per_step": v[1] / 32.0} for k, v in breakdown.items()}
+    per_layer = rep_launches // (reps * shape.n_layers)  # 2 when a split-K finishing launch follows
+    if B == 1:
+        gu_kernel = "mk_op_gu_x" if gu_exact else "mk_op_gu"
+    else:
+        bt = 1 if B <= 16 else 2 if B <= 32 else 4
+        # the library gives a wave two row groups at four batch tiles when the
+        # operator has at least half a CU's worth of groups per CU
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        gpw2 = bt == 4 and -(-shape.ffn // 16) // 8 >= ncu // 2
+        gu_kernel = (f"mk_b_gu_b{bt}" + ("_t" if tiled else "") + ("_g2" if gpw2 else "")
+                     + (" + mk_b_fin_gu" if per_layer > 1 else ""))
+    per_op = {"ms_per_step": op_ms, "runs_ms_per_step": [t / steps for t in op_runs],
+              "step_p50_ms": pct(op_per, 50), "step_p99_ms": pct(op_per, 99),
+              "mode": "one HIP graph of per-operator launches per step" + (", fused merge" if args.fused_merge else ""),
+              "gu_kernel": {"kernel": gu_kernel, "avg_ms": kern_ms, "algorithmic_bytes_per_launch": kb,
+                            "achieved_gbps": gu_gbps, "frac_of_peak": gu_gbps / PEAK_GBPS,
+                            "traffic_bytes_per_launch": load_traffic(wl.name),
+                            "timing": f"{reps} back-to-back replays of the {shape.n_layers} layers' gate/up launches "
+                                      "between two HIP events on the decode stream"},
+              "op_breakdown_eager": op_breakdown, "op_replay_us_per_layer": replay_us, "op_grid": op_grid}
+
+    return per_op, op_ms, op_tokens, gu_gbps, kern_ms, kb, gu_kernel
+
+
+def mega_kernel_name(shape):
+    """The megakernel instance the library launches for a batch-1 shape with an fp32 cache."""
+    qd = shape.n_q_heads * shape.head_dim
+    G = shape.n_q_heads // shape.n_kv_heads
+    exact = shape.hidden % 2048 == 0 and qd % 2048 == 0 and shape.ffn % 2048 == 0 and G == 4
+    return f"mk_mega_{'x' if exact else 'n'}_{shape.head_dim}_f32_g{G}"
 
 
 if __name__ == "__main__":

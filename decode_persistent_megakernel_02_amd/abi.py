@@ -73,6 +73,11 @@ class mk_debug_view(ctypes.Structure):
                 ("exact_ops", ctypes.c_uint32), ("op_grid", ctypes.c_int32 * 9)]
 
 
+class mk_mega_view(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("xmid", ctypes.c_void_p), ("qkv", ctypes.c_void_p),
+                ("attn", ctypes.c_void_p), ("h", ctypes.c_void_p), ("epoch", ctypes.c_uint32)]
+
+
 # Every symbol the headers declare, with its ctypes signature.
 _P, _I32, _I64, _U64, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
 SIGNATURES = {
@@ -103,6 +108,10 @@ SIGNATURES = {
     "mk_trace_op": ([_P, _I32, _I32], _I32),
     "mk_t_argmax": ([_P, _I32, _P, _P], _I32),
     "mk_device_info": ([ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I32)], _I32),
+    "mk_mega_trace": ([_P, _P, _I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                       ctypes.POINTER(ctypes.c_double)], _I32),
+    "mk_get_mega_view": ([_P, ctypes.POINTER(mk_mega_view)], _I32),
+    "mk_t_stream_read": ([_P, _I64, _I32, _I32, _I32, _P, ctypes.POINTER(ctypes.c_float)], _I32),
 }
 
 if not os.path.exists(LIB_PATH):
@@ -363,3 +372,30 @@ def mk_device_info():
     t = ctypes.c_double()
     _check(lib.mk_device_info(ctypes.byref(n), ctypes.byref(t), ctypes.byref(l)), "mk_device_info")
     return n.value, t.value, l.value
+
+
+def mk_mega_trace(h: Handle):
+    """(timestamps uint64 [ops, ncu, slots], ticks per us) of the last megakernel step."""
+    import numpy as np
+    ops, ncu, slots = _I32(), _I32(), _I32()
+    tpu = ctypes.c_double()
+    _check(lib.mk_mega_trace(h.ptr, None, 0, ctypes.byref(ops), ctypes.byref(ncu), ctypes.byref(slots),
+                             ctypes.byref(tpu)), "mk_mega_trace")
+    buf = np.zeros(ops.value * ncu.value * slots.value, dtype=np.uint64)
+    _check(lib.mk_mega_trace(h.ptr, buf.ctypes.data, buf.size, ctypes.byref(ops), ctypes.byref(ncu),
+                             ctypes.byref(slots), ctypes.byref(tpu)), "mk_mega_trace")
+    return buf.reshape(ops.value, ncu.value, slots.value), tpu.value
+
+
+def mk_get_mega_view(h: Handle) -> mk_mega_view:
+    out = mk_mega_view()
+    _check(lib.mk_get_mega_view(h.ptr, ctypes.byref(out)), "mk_get_mega_view")
+    return out
+
+
+def mk_t_stream_read(src, wgs: int, loads: int, reps: int = 5, stream=None) -> float:
+    """Fastest of `reps` streaming reads of the device tensor src (ms)."""
+    ms = ctypes.c_float()
+    _check(lib.mk_t_stream_read(_ptr(src), src.numel() * src.element_size(), wgs, loads, reps, _stream(stream),
+                                ctypes.byref(ms)), "mk_t_stream_read")
+    return ms.value

@@ -601,6 +601,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     if (G != 1 && G != 2 && G != 4 && G != 8)
       return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports 1, 2, 4 or 8 query heads per KV head");
     if (cfg->vocab > (1 << 17)) return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports vocab <= 131072");
+    if (cfg->hidden > 16 * kMegaStagers * kWave)
+      return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports hidden <= 4096");
     if (cfg->flags & (MK_FLAG_FUSED_MERGE | MK_FLAG_NO_GRAPH | MK_FLAG_TILED_WEIGHTS | MK_FLAG_POISON))
       return fail(MK_ERR_INVALID_ARG, "FUSED_MERGE, NO_GRAPH, TILED_WEIGHTS and POISON are per-operator flags");
   }
@@ -771,7 +773,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     *h->host_abort = 0;
     HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void**>(&M.host_abort), h->host_abort, 0));
     if (cfg->flags & MK_FLAG_TRACE) {
-      h->mega_trace_words = (int64_t)(4 * L + 1) * ncu * (kMegaCompute + 1);
+      h->mega_trace_words = (int64_t)(4 * L + 1) * ncu * (kMegaCompute + 3);
       MK_TRY(h->alloc(&M.trace, h->mega_trace_words));
       HIP_TRY(hipMemset(M.trace, 0, h->mega_trace_words * 8));
     }
@@ -1166,6 +1168,64 @@ mk_status mk_trace_op(mk_handle* h, int32_t type, int32_t layer) {
   if (!h->P.trace) return fail(MK_ERR_STATE, "handle created without MK_FLAG_TRACE");
   if (!(h->cfg.flags & MK_FLAG_NO_GRAPH)) return fail(MK_ERR_STATE, "operator tracing needs MK_FLAG_NO_GRAPH");
   h->P.trace_op = type < 0 ? -1 : (type << 16) | layer;
+  return MK_OK;
+}
+
+mk_status mk_mega_trace(mk_handle* h, uint64_t* out, int64_t cap, int32_t* ops, int32_t* ncu, int32_t* slots,
+                        double* ticks_per_us) {
+  g_err.clear();
+  if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
+  if (!h->mega.trace) return fail(MK_ERR_STATE, "megakernel handle created without MK_FLAG_TRACE");
+  if (ops) *ops = 4 * h->P.L + 1;
+  if (ncu) *ncu = h->P.ncu;
+  if (slots) *slots = kMegaCompute + 3;
+  if (ticks_per_us) *ticks_per_us = h->ticks_per_us;
+  if (!out) return MK_OK;
+  if (cap < h->mega_trace_words) return fail(MK_ERR_CAPACITY, "capacity too small");
+  MK_TRY(drain(h));
+  HIP_TRY(hipMemcpy(out, h->mega.trace, 8 * (size_t)h->mega_trace_words, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+mk_status mk_get_mega_view(mk_handle* h, mk_mega_view* out) {
+  if (!h || !out) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  if (h->cfg.mode != MK_MODE_MEGAKERNEL) return fail(MK_ERR_STATE, "not a megakernel handle");
+  out->x = h->mega.x;
+  out->xmid = h->mega.xmid;
+  out->qkv = h->mega.qkv;
+  out->attn = h->mega.attn;
+  out->h = h->mega.h;
+  out->epoch = h->epoch;
+  return MK_OK;
+}
+
+mk_status mk_t_stream_read(const void* src, int64_t bytes, int32_t wgs, int32_t loads, int32_t reps, void* stream,
+                           float* best_ms) {
+  g_err.clear();
+  if (!src || !best_ms || bytes < 16 || bytes % 16 || wgs < 1 || reps < 1 || (loads != 4 && loads != 8 && loads != 16))
+    return fail(MK_ERR_INVALID_ARG, "bad stream-read arguments");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* sink = nullptr;
+  HIP_TRY(hipMalloc(&sink, 4));
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  float best = 1e30f;
+  hipError_t err = hipSuccess;
+  for (int r = 0; r < reps && err == hipSuccess; ++r) {
+    err = hipEventRecord(e0, st);
+    if (err == hipSuccess) err = launch_stream_read(src, bytes / 16, wgs, loads, sink, st);
+    if (err == hipSuccess) err = hipEventRecord(e1, st);
+    if (err == hipSuccess) err = hipEventSynchronize(e1);
+    float ms = 0;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+    if (err == hipSuccess) best = std::min(best, ms);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  (void)hipFree(sink);
+  if (err != hipSuccess) return fail(MK_ERR_HIP, std::string("stream read: ") + hipGetErrorString(err));
+  *best_ms = best;
   return MK_OK;
 }
 

@@ -66,4 +66,5 @@ extern "C" __global__ void mk_t_attn_merge_kernel(const float* part, int nq, int
                                                   int nsplit, float* o);
 extern "C" __global__ void mk_t_argmax_kernel(const float* x, int n, unsigned long long* slot);
 extern "C" __global__ void mk_t_argmax_final(const unsigned long long* slot, int32_t* out);
+hipError_t launch_stream_read(const void* src, int64_t nvec, int wgs, int loads, uint32_t* sink, hipStream_t st);
 }  // namespace mk

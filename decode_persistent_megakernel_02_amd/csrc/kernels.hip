@@ -815,6 +815,36 @@ extern "C" __global__ void mk_t_argmax_kernel(const float* x, int n, unsigned lo
   if (threadIdx.x == 0) __hip_atomic_fetch_max(slot, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Streaming read of nvec 16-byte vectors (HBM ceiling probe): every thread
+// keeps U non-temporal loads in flight; the xor of the data decides a store
+// that never happens for a constant-filled buffer, so no load is dead.
+template <int U>
+__global__ __launch_bounds__(512) void stream_read_kernel(const v4u* src, int64_t nvec, uint32_t* sink) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nth = (int64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  int64_t i = tid;
+  for (; i + (U - 1) * nth < nvec; i += U * nth) {
+    v4u v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld_w(src + i + u * nth);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < nvec; i += nth) {
+    const v4u v = ld_w(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, int64_t nvec, int wgs, int loads, uint32_t* sink, hipStream_t st) {
+  const v4u* p = static_cast<const v4u*>(src);
+  if (loads == 4) hipLaunchKernelGGL(stream_read_kernel<4>, dim3(wgs), dim3(512), 0, st, p, nvec, sink);
+  else if (loads == 8) hipLaunchKernelGGL(stream_read_kernel<8>, dim3(wgs), dim3(512), 0, st, p, nvec, sink);
+  else hipLaunchKernelGGL(stream_read_kernel<16>, dim3(wgs), dim3(512), 0, st, p, nvec, sink);
+  return hipGetLastError();
+}
+
 extern "C" __global__ void mk_t_argmax_final(const unsigned long long* slot, int32_t* out) {
   if (threadIdx.x == 0) out[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)slot[0]);
 }

@@ -59,6 +59,9 @@ constexpr int NB = 2;   // weight buffers (tasks in flight) per compute wave
 // A compute wave holds at most kMegaMaxTasks results of one operator (lane j
 // of pass p runs the epilogue of task 64 p + j).
 constexpr int kMegaMaxTasks = 128;
+// trace words per (operator, workgroup): compute waves' (duration, end), then
+// the stager's publish time, poll start and input-complete time
+constexpr int kTraceSlots = kMegaCompute + 3;
 
 // ---- tagged words ----------------------------------------------------------
 __device__ __forceinline__ void tput(uint64_t* p, float v, uint32_t epoch) {
@@ -88,25 +91,39 @@ __device__ __forceinline__ void lds_rel_add(uint32_t* p, uint32_t v) {
 }
 
 // ---- bounded waits ----------------------------------------------------------
+// s_sleep between re-reads of stale tagged words (64 clocks per unit): each
+// round reads the stale words again from the memory-side caches.
+#ifndef MK_POLL_SLEEP
+#define MK_POLL_SLEEP 2
+#endif
+constexpr int kPollSleep = MK_POLL_SLEEP;
 // One wait: tick() sleeps briefly and returns false when the wave must stop
 // (abort raised anywhere, or this wait ran out of time or iterations; then it
 // latches the timeout and raises the abort itself).
 struct Spin {
   uint64_t t0;
   uint32_t it;
-  __device__ __forceinline__ Spin() : t0(clock_now()), it(0) {}
-  __device__ __forceinline__ bool tick(const Params& P, const MegaBufs& M, MegaLds* L, uint32_t who, uint32_t what, uint32_t have,
-                       uint32_t need, int lane) {
-    ++it;
+  // The clock is first read on the first unsuccessful check: a wait that is
+  // already satisfied costs no clock read (s_memrealtime is a memory-path
+  // instruction with a round trip of its own).
+  __device__ __forceinline__ Spin() : t0(0), it(0) {}
+  // sleep: s_sleep argument between checks (64 clocks each).  The device
+  // status word and the host-mapped abort word are read only every 4096
+  // checks: 2048 waiting waves reading host memory every few microseconds
+  // would flood the fabric that the weight stream uses.
+  template <int SLEEP = 2>
+  __device__ __forceinline__ bool tick(const Params& P, const MegaBufs& M, MegaLds* L, uint32_t who, uint32_t what,
+                                       uint32_t have, uint32_t need, int lane) {
+    if (it++ == 0) t0 = clock_now();
     if (lds_load(&L->abort)) return false;
-    if ((it & 63) == 0) {
+    if ((it & 4095) == 0) {
       if (__hip_atomic_load(&P.status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
           __hip_atomic_load(M.host_abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) {
         if (lane == 0) lds_store(&L->abort, 1u);
         return false;
       }
     }
-    if (it > P.spin_limit || clock_now() - t0 > P.timeout_ticks) {
+    if (it > P.spin_limit || ((it & 63) == 0 && clock_now() - t0 > P.timeout_ticks)) {
       if (lane == 0) {
         if (atomicCAS(&P.status[1], ST_OK, ST_TIMEOUT) == ST_OK) {
           P.status[2] = blockIdx.x;
@@ -121,7 +138,7 @@ struct Spin {
       }
       return false;
     }
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(SLEEP);
     return true;
   }
 };
@@ -162,6 +179,24 @@ __device__ __forceinline__ uint32_t done_after(int k) { return (uint32_t)NC * (u
 __device__ __forceinline__ uint32_t free_for(int k) { return (uint32_t)NC * (uint32_t)(k / 2); }
 
 // ---- compute waves -------------------------------------------------------------
+// Pool slot p of this workgroup's share of an operator's `count` tasks, or
+// `count` past its end.  Workgroup b runs on die b % kXcds; the workgroups of
+// one die share one contiguous part of the tasks and take them in turn, one
+// task at a time, so every workgroup of a die gets the same number of tasks
+// to within one (in runs of several tasks, an operator with 1.5 runs per
+// workgroup -- QKV at the 8B shape -- gave half the workgroups twice the
+// tasks of the others).
+__device__ __forceinline__ int mslot(uint32_t p, int count) {
+  const int n = gridDim.x;
+  if (n % kXcds) {
+    const int t = (int)p * n + (int)blockIdx.x;
+    return t < count ? t : count;
+  }
+  const int per = (count + kXcds - 1) / kXcds, x = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+  const int t = (int)p * (n / kXcds) + j;
+  return t < per && x * per + t < count ? x * per + t : count;
+}
+
 struct WBuf {
   v4u w[kD][kR];
   GemvRows<kR> g;
@@ -193,7 +228,7 @@ __device__ __forceinline__ void fetch_first_t(const Params& P, int layer, int co
                                               int (&t)[NB], int lane) {
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    t[i] = slot_task(i * NC + c, count);
+    t[i] = mslot(i * NC + c, count);
     if (t[i] < count) fetch_task<TT, EXACT>(P, layer, t[i], B[i], lane);
   }
 }
@@ -216,7 +251,7 @@ __device__ __forceinline__ int mnext(uint32_t* pool, int j, int count, int lane)
   uint32_t p = 0;
   if (lane == 0) p = lds_add(pool, 1u);
   p = __builtin_amdgcn_readfirstlane(p);
-  return slot_task(p, count);
+  return mslot(p, count);
 }
 
 // Streams the wave's tasks of one operator.  On entry buffer i holds task t[i]
@@ -265,11 +300,20 @@ __device__ __forceinline__ void finish_op(const Params& P, const MegaBufs& M, co
   __builtin_amdgcn_wave_barrier();
   const uint32_t ep = S.epoch;
   unsigned long long best = 0;
+  // RMSNorm: the page holds gain * x, the stagers' sums of x^2 are in L->red;
+  // the 1/rms factor is common to every row, so it scales the outputs
+  float sc = 1.0f;
+  if constexpr (TT == TT_QKV || TT == TT_GU || TT == TT_LM) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NS; ++w) tot += L->red[w];
+    sc = 1.0f / sqrtf(tot / (float)P.H + P.eps);
+  }
   for (int jj = lane; jj < n; jj += kWave) {
     const Task d = op_task_fields(TT, layer, ids[jj], P.H, P.nq, P.nkv, P.hd, P.F, P.V, P.L);
     float y[kR];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) y[r] = res[jj * kR + r];
+    for (int r = 0; r < kR; ++r) y[r] = res[jj * kR + r] * sc;
     if constexpr (TT == TT_QKV) {
       const int qd = P.nq * P.hd, kd = P.nkv * P.hd;
       uint64_t* out = M.qkv + (size_t)layer * (qd + 2 * kd);
@@ -332,8 +376,10 @@ __device__ __forceinline__ void compute_wave(const Params& P, const MegaBufs& M,
   int t[NB];
   fetch_first<EXACT>(P, 0, c, B, t, lane);
   for (int k = 0; k < nops; ++k) {
-    if (!wait_lds(P, M, L, &L->ready[k & 1], (uint32_t)k + 1, NS + c, ((uint32_t)k << 8) | W_READY, lane)) return;
-    const float* page = pages + (k & 1) * pf;
+    if (!wait_lds(P, M, L, &L->ready[k & 1], (uint32_t)NS * (uint32_t)(k / 2 + 1), NS + c,
+                  ((uint32_t)k << 8) | W_READY, lane))
+      return;
+    const float* page = pages + ((k & 1) ? pf : 0);
     const uint64_t t0 = M.trace ? clock_now() : 0;
     switch (op_type(k, P.L)) {
       case TT_QKV: compute_op<TT_QKV, EXACT>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
@@ -345,7 +391,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const MegaBufs& M,
     if (k + 1 < nops) fetch_first<EXACT>(P, k + 1, c, B, t, lane);
     if (M.trace && lane == 0) {
       const uint64_t t1 = clock_now();
-      M.trace[((size_t)k * gridDim.x + blockIdx.x) * (NC + 1) + c] = ((t1 - t0) << 32) | (uint32_t)t1;
+      M.trace[((size_t)k * gridDim.x + blockIdx.x) * kTraceSlots + c] = ((t1 - t0) << 32) | (uint32_t)t1;
     }
     if (lane == 0) lds_rel_add(&L->done[k & 1], 1u);
   }
@@ -380,9 +426,17 @@ struct Stager {
 
   // Words [0, n) of the tagged vector src into dst: this stager takes the
   // 64-word groups s, s + NS, ...; a word is re-read until its tag is current.
-  __device__ __forceinline__ bool load_tagged(const uint64_t* src, int n, float* dst) {
+  // NORM (RMSNorm input): dst = gain * x, the raw x also into resid when
+  // given, and this wave's sum of x^2 into L->red[s] (the compute waves apply
+  // the 1/rms factor to the projection outputs).  gain and resid words are
+  // the ones this stager owns.
+  template <bool NORM = false>
+  __device__ __forceinline__ bool load_tagged(const uint64_t* src, int n, float* dst, const float* gain = nullptr,
+                                              float* resid = nullptr) {
     constexpr int BATCH = 28;
     const uint32_t ep = S.epoch;
+    float ss = 0.f;
+    mark(k, NC + 1);
     for (int g0 = s; g0 * kWave < n; g0 += NS * BATCH) {
       uint64_t w[BATCH];
 #pragma unroll
@@ -396,7 +450,7 @@ struct Stager {
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) pend |= tcur(w[j], ep) ? 0u : 1u << j;
         if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) break;
-        if (!sp.tick(P, M, L, s, ((uint32_t)k << 8) | W_DATA, (uint32_t)g0, (uint32_t)n, lane)) return false;
+        if (!sp.tick<kPollSleep>(P, M, L, s, ((uint32_t)k << 8) | W_DATA, (uint32_t)g0, (uint32_t)n, lane)) return false;
 #pragma unroll
         for (int j = 0; j < BATCH; ++j)
           if ((pend >> j) & 1) w[j] = tget(src + (g0 + j * NS) * kWave + lane);
@@ -404,56 +458,189 @@ struct Stager {
 #pragma unroll
       for (int j = 0; j < BATCH; ++j) {
         const int i = (g0 + j * NS) * kWave + lane;
-        if (i < n) dst[i] = tval(w[j]);
+        if (i < n) {
+          const float v = tval(w[j]);
+          if constexpr (NORM) {
+            if (resid) resid[i] = v;
+            dst[i] = v * gain[i];
+            ss = fmaf(v, v, ss);
+          } else {
+            dst[i] = v;
+          }
+        }
       }
     }
+    if constexpr (NORM) {
+      ss = wave_sum(ss);
+      if (lane == 0) L->red[s] = ss;
+    }
+    mark(k, NC + 2);
     return true;
   }
 
-  // The bf16 embedding row of the step's token (read-only data, plain loads).
-  __device__ __forceinline__ void load_embed(float* dst) {
+  // The bf16 embedding row of the step's token (read-only data, plain loads)
+  // as an RMSNorm input: page = gain * x, raw x into resid, sum of x^2 into
+  // L->red[s].
+  __device__ __forceinline__ void load_embed(float* dst, const float* gain, float* resid) {
     const uint16_t* row = P.embed + (int64_t)token_of(P, S, 0) * P.H;
-    for (int i = (s * kWave + lane); i < P.H; i += NS * kWave) dst[i] = bf1(row[i]);
-  }
-
-  // RMSNorm of page[0, n) in place (gain from global), copying the raw values
-  // to resid first when given; `resid_free` is the operator that last reads
-  // resid, which must be done before it is overwritten (-1: none).
-  __device__ __forceinline__ bool norm(float* page, int n, const uint16_t* gamma, float* resid, int resid_free) {
-    if (!sync()) return false;  // every stager's words are in the page
-    if (resid) {
-      if (resid_free >= 0 && !wait_done(resid_free, done_after(resid_free))) return false;
-      for (int i = s * kWave + lane; i < n; i += NS * kWave) resid[i] = page[i];
-    }
     float ss = 0.f;
-    for (int i = s * kWave + lane; i < n; i += NS * kWave) ss = fmaf(page[i], page[i], ss);
+    for (int i = (s * kWave + lane); i < P.H; i += NS * kWave) {
+      const float v = bf1(row[i]);
+      resid[i] = v;
+      dst[i] = v * gain[i];
+      ss = fmaf(v, v, ss);
+    }
     ss = wave_sum(ss);
     if (lane == 0) L->red[s] = ss;
-    if (!sync()) return false;
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < NS; ++w) tot += L->red[w];
-    const float inv = 1.0f / sqrtf(tot / (float)n + P.eps);
-    for (int i = s * kWave + lane; i < n; i += NS * kWave) page[i] = page[i] * inv * bf1(gamma[i]);
-    return sync();
   }
 
+  // This stager's RMSNorm gains (words s*64 + lane + 256 j) into the LDS gain
+  // buffer, loaded while nothing waits on them: staging a normalised input
+  // then needs no global load after the input has arrived.  Each stager reads
+  // back only the words it wrote.
+  __device__ __forceinline__ void load_gain(const uint16_t* gamma, int n, float* gain) {
+    for (int i = s * kWave + lane; i < n; i += NS * kWave) gain[i] = bf1(gamma[i]);
+  }
+
+  __device__ __forceinline__ void mark(int op, int slot) {
+    if (M.trace && s == 0 && lane == 0)
+      M.trace[((size_t)op * gridDim.x + blockIdx.x) * kTraceSlots + slot] = clock_now();
+  }
+
+  // This stager's part of op's input (and its L->red word) is in the page:
+  // ready[page] counts the stagers' releases, NS per operator on the page.
   __device__ __forceinline__ void publish(int op, int page) {
-    if (s == 0 && lane == 0) {
-      L->pool[page] = NB * NC;  // pool slots past the compute waves' first NB tasks
-      lds_rel_store(&L->ready[page], (uint32_t)op + 1);
-      if (M.trace) M.trace[((size_t)op * gridDim.x + blockIdx.x) * (NC + 1) + NC] = clock_now();
+    if (lane == 0) {
+      if (s == 0) {
+        L->pool[page] = NB * NC;  // pool slots past the compute waves' first NB tasks
+        if (M.trace) M.trace[((size_t)op * gridDim.x + blockIdx.x) * kTraceSlots + NC] = clock_now();
+      }
+      lds_rel_add(&L->ready[page], 1u);
     }
   }
 };
+
+// Log-sum-exp merge of query head hq's split records -> tagged attention
+// output.  Splits are taken SB at a time: every load of a round (this lane's
+// dims of each split's o, and split s0 + lane's m and l) is issued at once,
+// then only stale words are read again; the rounds merge online (running
+// maximum, rescaled sums), in split order.
+template <int HD>
+__device__ __forceinline__ bool merge_unit(Stager& st, int l, int hq) {
+  const Params& P = st.P;
+  const MegaBufs& M = st.M;
+  const int lane = st.lane, G = P.nq / P.nkv, g = hq / G, hh = hq % G;
+  const int used = (st.S.pos + 1 + P.split - 1) / P.split;
+  constexpr int DPL = HD / kWave, SB = 16;
+  const uint32_t ep = st.S.epoch;
+  const uint64_t cur = (uint64_t)ep << 32;
+  const size_t rs = (size_t)G * (HD + 2);
+  const uint64_t* base = M.rec + ((size_t)l * P.nkv + g) * P.nsplit * rs + (size_t)hh * (HD + 2);
+  float Mx = -INFINITY, Lsum = 0.f, o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  for (int s0 = 0; s0 < used; s0 += SB) {
+    const int n = min(SB, used - s0);
+    const bool mine = lane < n;  // this lane reads split s0 + lane's (m, l)
+    const uint64_t* ml = base + (size_t)(s0 + (mine ? lane : 0)) * rs + HD;
+    uint64_t wm = mine ? tget(ml) : cur, wl = mine ? tget(ml + 1) : cur, w[SB][DPL];
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) w[j][e] = j < n ? tget(base + (size_t)(s0 + j) * rs + lane * DPL + e) : cur;
+    Spin sp;
+    for (;;) {
+      bool ok = tcur(wm, ep) && tcur(wl, ep);
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ok = ok && tcur(w[j][e], ep);
+      if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+      if (!sp.tick<kPollSleep>(P, M, st.L, st.s, ((uint32_t)st.k << 8) | W_REC, (uint32_t)s0, (uint32_t)used, lane))
+        return false;
+      if (!tcur(wm, ep)) wm = tget(ml);
+      if (!tcur(wl, ep)) wl = tget(ml + 1);
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+          if (!tcur(w[j][e], ep)) w[j][e] = tget(base + (size_t)(s0 + j) * rs + lane * DPL + e);
+    }
+    // records with l == 0 hold no positions and carry weight 0
+    const float ms = tval(wm), ls = tval(wl);
+    const bool live = mine && ls > 0.f;
+    const float Mn = fmaxf(Mx, wave_max(live ? ms : -INFINITY));
+    const float alpha = Mx == -INFINITY ? 0.f : __expf(Mx - Mn);
+    const float wgt = live ? __expf(ms - Mn) : 0.f;
+    Lsum = Lsum * alpha + wave_sum(wgt * (live ? ls : 0.f));
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const float wj = __shfl(wgt, j);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wj, wj > 0.f ? tval(w[j][e]) : 0.f, o[e]);
+    }
+    Mx = Mn;
+  }
+  const float inv = 1.0f / Lsum;
+  uint64_t* out = M.attn + (size_t)l * P.nq * HD + (size_t)hq * HD + lane * DPL;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) tput(out + e, o[e] * inv, ep);
+  return true;
+}
+
+// Puts row jr of a block held in registers (the current position, whose
+// key and value arrive as tagged words this step) into the block: kv and vv
+// hold this lane's dims lane * DPL + e of the key and value.  The key part a
+// lane scores (dims part * EPL ..) is gathered from the lanes that hold those
+// dims; every lane takes part in the shuffles, the lanes of row jr keep them.
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_patch_row(AttnBuf<HD, KT>& A, int jr, const float (&kv)[HD / kWave],
+                                               const float (&vv)[HD / kWave], int lane) {
+  using Gm = AttnGeom<HD, KT>;
+  constexpr int DPL = Gm::DPL, EPL = Gm::EPL;
+  const int my = lane / Gm::LPP, part = lane % Gm::LPP;
+  float kp[EPL];
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) kp[m] = __shfl(kv[m % DPL], (part * EPL + m) / DPL);
+  if (my == jr) {
+#pragma unroll
+    for (int i = 0; i < Gm::KV16; ++i) {
+      if constexpr (sizeof(KT) == 4) {
+        A.kr[i] = v4u{__float_as_uint(kp[4 * i]), __float_as_uint(kp[4 * i + 1]), __float_as_uint(kp[4 * i + 2]),
+                      __float_as_uint(kp[4 * i + 3])};
+      } else {
+        A.kr[i] = v4u{bf_pack(f2bf(kp[8 * i]), f2bf(kp[8 * i + 1])), bf_pack(f2bf(kp[8 * i + 2]), f2bf(kp[8 * i + 3])),
+                      bf_pack(f2bf(kp[8 * i + 4]), f2bf(kp[8 * i + 5])), bf_pack(f2bf(kp[8 * i + 6]), f2bf(kp[8 * i + 7]))};
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < Gm::NP; ++j) {
+    if (j == jr) {
+      if constexpr (sizeof(KT) == 4) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) A.vr[j][e] = __float_as_uint(vv[e]);
+      } else if constexpr (DPL == 2) {
+        A.vr[j][0] = bf_pack(f2bf(vv[0]), f2bf(vv[1]));
+      } else {
+        A.vr[j][0] = f2bf(vv[0]);
+      }
+    }
+  }
+}
 
 // One decode-attention unit: the G query heads of KV head g over the split
 // [p0, p1) of the context, as one (o, m, l) record per head.  The workgroup's
 // NS stager waves share the unit: wave s takes the position blocks s, s + NS,
 // ... (one block each at the split sizes used), keeps an online-softmax state
-// per head, and the waves' states are merged through LDS.  The wave whose
-// block holds the current position first appends that position's key and
-// value to the cache.  A (KV head, split) unit always runs on the same
+// per head, and the waves' states are merged through LDS.  A wave's first
+// block is loaded from the cache before the queries are awaited: rows below
+// the current position depend on nothing this step writes, and the current
+// position's row (the block clamps at it) is put into the registers from its
+// tagged key and value once they arrive; that wave also appends the row to
+// the cache for later steps.  A (KV head, split) unit always runs on the same
 // workgroup, so every cache row this launch writes is read back only by the
 // workgroup that wrote it.
 template <int HD, typename KT, int GQ>
@@ -477,6 +664,14 @@ __device__ __forceinline__ bool attn_unit(Stager& st, int l, int g, int sp_i, fl
   const bool append = p1 == T && last_blk % NS == s;
   const uint64_t* ks = qkv + qd + (size_t)g * HD + lane * DPL;
   const uint64_t* vs = qkv + qd + kd + (size_t)g * HD + lane * DPL;
+  const int64_t o0 = kv_off(P, l, 0, g, 0);
+  KT* kc = static_cast<KT*>(P.kcache) + o0;
+  KT* vc = static_cast<KT*>(P.vcache) + o0;
+  // this wave's first block (rows from the cache, clamped at the current position)
+  int b0 = p0 + s * NP;
+  AttnBuf<HD, KT> A;
+  bool pre = b0 < p1;
+  if (pre) attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
   uint64_t qw[QW], kw[DPL], vw[DPL];
 #pragma unroll
   for (int j = 0; j < QW; ++j) qw[j] = (s + j * NS) * kWave < G * HD ? tget(qsrc + (s + j * NS) * kWave) : cur;
@@ -494,7 +689,7 @@ __device__ __forceinline__ bool attn_unit(Stager& st, int l, int g, int sp_i, fl
 #pragma unroll
       for (int e = 0; e < DPL; ++e) ok = ok && tcur(kw[e], ep) && tcur(vw[e], ep);
       if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
-      if (!sp.tick(P, M, st.L, s, ((uint32_t)st.k << 8) | W_QKV, (uint32_t)(g * P.nsplit + sp_i), 0u, lane))
+      if (!sp.tick<kPollSleep>(P, M, st.L, s, ((uint32_t)st.k << 8) | W_QKV, (uint32_t)(g * P.nsplit + sp_i), 0u, lane))
         return false;
 #pragma unroll
       for (int j = 0; j < QW; ++j)
@@ -509,26 +704,31 @@ __device__ __forceinline__ bool attn_unit(Stager& st, int l, int g, int sp_i, fl
 #pragma unroll
   for (int j = 0; j < QW; ++j)
     if ((s + j * NS) * kWave < G * HD) qs[(s + j * NS) * kWave + lane] = tval(qw[j]);
-  const int64_t o0 = kv_off(P, l, 0, g, 0);
-  KT* kc = static_cast<KT*>(P.kcache) + o0;
-  KT* vc = static_cast<KT*>(P.vcache) + o0;
-  if (append) {  // position T - 1 into the cache
+  if (append) {  // position T - 1: into the cache for later steps, into the preloaded block for this one
+    float kf[DPL], vf[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
+      kf[e] = tval(kw[e]);
+      vf[e] = tval(vw[e]);
       const int64_t at = (int64_t)(T - 1) * HD + lane * DPL + e;
-      if constexpr (sizeof(KT) == 4) { kc[at] = tval(kw[e]); vc[at] = tval(vw[e]); }
-      else { kc[at] = f2bf(tval(kw[e])); vc[at] = f2bf(tval(vw[e])); }
+      if constexpr (sizeof(KT) == 4) { kc[at] = kf[e]; vc[at] = vf[e]; }
+      else { kc[at] = f2bf(kf[e]); vc[at] = f2bf(vf[e]); }
     }
-    // the appended row is read back below by other lanes of this wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const int jr = T - 1 - b0;
+    if (jr < NP) {
+      attn_patch_row<HD, KT>(A, jr, kf, vf, lane);  // the row is in the preloaded first block
+    } else {
+      // the row is in a later block of this wave, loaded below by other lanes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
   }
   if (!st.sync()) return false;  // every wave's query words are in qs
   AttnState<HD, GQ> sta;
   sta.init();
-  for (int b0 = p0 + s * NP; b0 < p1; b0 += NS * NP) {
-    AttnBuf<HD, KT> A;
-    attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
+  for (; b0 < p1; b0 += NS * NP) {
+    if (!pre) attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
+    pre = false;
     attn_compute<HD, KT, GQ>(A, qs, b0, p1, G, lane, sta);
   }
   attn_store_state<HD, GQ>(sta, G, recs + s * G * (HD + 2), lane);
@@ -561,77 +761,6 @@ __device__ __forceinline__ bool attn_unit(Stager& st, int l, int g, int sp_i, fl
   return st.sync();  // qs and recs are reused by the next unit
 }
 
-// Log-sum-exp merge of query head hq's split records -> tagged attention output.
-template <int HD>
-__device__ __forceinline__ bool merge_unit(Stager& st, int l, int hq) {
-  const Params& P = st.P;
-  const MegaBufs& M = st.M;
-  const int lane = st.lane, G = P.nq / P.nkv, g = hq / G, hh = hq % G;
-  const int used = (st.S.pos + 1 + P.split - 1) / P.split;
-  constexpr int DPL = HD / kWave, SB = 16;
-  const uint32_t ep = st.S.epoch;
-  const size_t rs = (size_t)G * (HD + 2);
-  const uint64_t* base = M.rec + ((size_t)l * P.nkv + g) * P.nsplit * rs + (size_t)hh * (HD + 2);
-  // largest split maximum (records with l == 0 hold no positions)
-  float Mx = -INFINITY;
-  for (int s0 = 0; s0 < used; s0 += kWave) {
-    const int sidx = min(s0 + lane, used - 1);
-    uint64_t wm = tget(base + sidx * rs + HD), wl = tget(base + sidx * rs + HD + 1);
-    Spin sp;
-    while (__builtin_amdgcn_ballot_w64(!(tcur(wm, ep) && tcur(wl, ep))) != 0) {
-      if (!sp.tick(P, M, st.L, st.s, ((uint32_t)st.k << 8) | W_REC, (uint32_t)s0, (uint32_t)used, lane)) return false;
-      if (!tcur(wm, ep)) wm = tget(base + sidx * rs + HD);
-      if (!tcur(wl, ep)) wl = tget(base + sidx * rs + HD + 1);
-    }
-    if (s0 + lane < used && tval(wl) > 0.f) Mx = fmaxf(Mx, tval(wm));
-  }
-  Mx = wave_max(Mx);
-  float Lsum = 0.f, o[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int s0 = 0; s0 < used; s0 += SB) {
-    // weights of splits s0 .. s0 + SB - 1 (lane j holds split s0 + j's weight)
-    float wgt = 0.f;
-    {
-      const int sidx = min(s0 + (lane % SB), used - 1);
-      const float ms = tval(tget(base + sidx * rs + HD)), ls = tval(tget(base + sidx * rs + HD + 1));
-      wgt = s0 + (lane % SB) < used && ls > 0.f ? __expf(ms - Mx) : 0.f;
-      if (lane < SB) Lsum = fmaf(wgt, ls > 0.f ? ls : 0.f, Lsum);
-    }
-    uint64_t w[SB][DPL];
-#pragma unroll
-    for (int j = 0; j < SB; ++j)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) w[j][e] = tget(base + min(s0 + j, used - 1) * rs + lane * DPL + e);
-    Spin sp;
-    for (;;) {
-      bool ok = true;
-#pragma unroll
-      for (int j = 0; j < SB; ++j)
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) ok = ok && tcur(w[j][e], ep);
-      if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
-      if (!sp.tick(P, M, st.L, st.s, ((uint32_t)st.k << 8) | W_REC, (uint32_t)s0, 1u, lane)) return false;
-#pragma unroll
-      for (int j = 0; j < SB; ++j)
-#pragma unroll
-        for (int e = 0; e < DPL; ++e)
-          if (!tcur(w[j][e], ep)) w[j][e] = tget(base + min(s0 + j, used - 1) * rs + lane * DPL + e);
-    }
-#pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const float wj = __shfl(wgt, j);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wj, wj > 0.f ? tval(w[j][e]) : 0.f, o[e]);
-    }
-  }
-  const float inv = 1.0f / wave_sum(Lsum);
-  uint64_t* out = M.attn + (size_t)l * P.nq * HD + (size_t)hq * HD + lane * DPL;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) tput(out + e, o[e] * inv, ep);
-  return true;
-}
-
 // The step's greedy token from every workgroup's LM-head key.
 __device__ __forceinline__ bool argmax_unit(Stager& st) {
   const Params& P = st.P;
@@ -644,7 +773,7 @@ __device__ __forceinline__ bool argmax_unit(Stager& st) {
     uint64_t w = tget(M.key + i);
     Spin sp;
     while (__builtin_amdgcn_ballot_w64((w & 0x7FFFu) != tag) != 0) {
-      if (!sp.tick(P, M, st.L, st.s, ((uint32_t)st.k << 8) | W_KEY, (uint32_t)i0, (uint32_t)n, lane)) return false;
+      if (!sp.tick<kPollSleep>(P, M, st.L, st.s, ((uint32_t)st.k << 8) | W_KEY, (uint32_t)i0, (uint32_t)n, lane)) return false;
       if ((w & 0x7FFFu) != tag) w = tget(M.key + i);
     }
     best = (w >> 15) > best ? (w >> 15) : best;
@@ -661,8 +790,8 @@ __device__ __forceinline__ bool argmax_unit(Stager& st) {
 
 template <int HD, typename KT, int GQ>
 __device__ __forceinline__ void stager_wave(const Params& P, const MegaBufs& M, const Step& S, MegaLds* L,
-                                            float* pages, int pf, float* resid, float* rope, float* qs, float* recs,
-                                            int s, int lane) {
+                                            float* pages, int pf, float* resid, float* gain, float* rope, float* qs,
+                                            float* recs, int s, int lane) {
   Stager st{P, M, S, L, s, lane, 0u, 0};
   const int Lc = P.L, ncu = gridDim.x, wg = blockIdx.x;
   const int nunits = P.nkv * P.nsplit, used = (S.pos + 1 + P.split - 1) / P.split;
@@ -674,45 +803,49 @@ __device__ __forceinline__ void stager_wave(const Params& P, const MegaBufs& M, 
     rope[half + i] = P.rope_sin[(int64_t)S.pos * half + i];
   }
   float* page0 = pages;
-  float* page1 = pages + pf;
+  float* page1 = pages + pf;  // page 0 holds hidden-size inputs only
   for (int l = 0; l < Lc; ++l) {
     int k = 4 * l;
     // QKV: rmsnorm(x_l) (layer 0: the embedding row), raw x_l kept for the O residual
     st.k = k;
+    if (l == 0) st.load_gain(ld_const(P.attn_norm), P.H, gain);  // later layers: loaded during the previous DOWN
     if (!st.wait_done(k, free_for(k))) return;
-    if (l == 0) st.load_embed(page0);
-    else if (!st.wait_done(k - 1, done_after(k - 1)) || !st.load_tagged(M.x + (size_t)l * P.H, P.H, page0)) return;
-    if (!st.norm(page0, P.H, ld_const(P.attn_norm + l), resid, l == 0 ? -1 : k - 1)) return;
+    if (l == 0) st.load_embed(page0, gain, resid);
+    else if (!st.wait_done(k - 1, done_after(k - 1)) ||
+             !st.load_tagged<true>(M.x + (size_t)l * P.H, P.H, page0, gain, resid))
+      return;
     st.publish(k, 0);
-    // attention units of this workgroup (all stager waves), then the merges
-    // assigned to this wave
-    if (wg < nunits) {
-      if (!st.wait_done(k, done_after(k))) return;  // the local QKV tasks first: avoids polling while QKV runs
-      for (int u = wg; u < nunits; u += ncu) {
-        const int g = u / P.nsplit, sp_i = u % P.nsplit;
-        if (sp_i >= used) continue;
-        if (!attn_unit<HD, KT, GQ>(st, l, g, sp_i, qs, recs)) return;
-      }
+    // attention units of this workgroup (all stager waves), then the
+    // log-sum-exp merges of the query heads assigned to this wave; both wait
+    // for the local QKV tasks first, so that they do not poll while QKV runs
+    st.load_gain(ld_const(P.ffn_norm + l), P.H, gain);  // for GU, ahead of every wait below
+    const int hq0 = (ncu - 1 - wg) + ncu * s;
+    if (wg < nunits || hq0 < P.nq)
+      if (!st.wait_done(k, done_after(k))) return;
+    for (int u = wg; u < nunits; u += ncu) {
+      const int g = u / P.nsplit, sp_i = u % P.nsplit;
+      if (sp_i >= used) continue;
+      if (!attn_unit<HD, KT, GQ>(st, l, g, sp_i, qs, recs)) return;
     }
-    for (int hq = s * ncu + (ncu - 1 - wg); hq < P.nq; hq += NS * ncu)
+    for (int hq = hq0; hq < P.nq; hq += NS * ncu)
       if (!merge_unit<HD>(st, l, hq)) return;
     // O: the merged attention output
     st.k = ++k;
-    if (!st.wait_done(k, free_for(k)) || !st.load_tagged(M.attn + (size_t)l * P.nq * P.hd, P.nq * P.hd, page1) ||
-        !st.sync())
+    if (!st.wait_done(k, free_for(k)) || !st.load_tagged(M.attn + (size_t)l * P.nq * P.hd, P.nq * P.hd, page1))
       return;
     st.publish(k, 1);
     // GU: rmsnorm(xmid), raw xmid kept for the down residual
     st.k = ++k;
     if (!st.wait_done(k, free_for(k)) || !st.wait_done(k - 1, done_after(k - 1)) ||
-        !st.load_tagged(M.xmid + (size_t)l * P.H, P.H, page0) ||
-        !st.norm(page0, P.H, ld_const(P.ffn_norm + l), resid, k - 1))
+        !st.load_tagged<true>(M.xmid + (size_t)l * P.H, P.H, page0, gain, resid))
       return;
     st.publish(k, 0);
     // DOWN: the SwiGLU output
     st.k = ++k;
+    if (l + 1 < Lc) st.load_gain(ld_const(P.attn_norm + l + 1), P.H, gain);  // for the next QKV
+    else st.load_gain(P.final_norm, P.H, gain);                               // for the LM head
     if (!st.wait_done(k, free_for(k)) || !st.wait_done(k - 1, done_after(k - 1)) ||
-        !st.load_tagged(M.h + (size_t)l * P.F, P.F, page1) || !st.sync())
+        !st.load_tagged(M.h + (size_t)l * P.F, P.F, page1))
       return;
     st.publish(k, 1);
   }
@@ -720,7 +853,7 @@ __device__ __forceinline__ void stager_wave(const Params& P, const MegaBufs& M, 
   const int k = 4 * Lc;
   st.k = k;
   if (!st.wait_done(k, free_for(k)) || !st.wait_done(k - 1, done_after(k - 1)) ||
-      !st.load_tagged(M.x + (size_t)Lc * P.H, P.H, page0) || !st.norm(page0, P.H, P.final_norm, nullptr, -1))
+      !st.load_tagged<true>(M.x + (size_t)Lc * P.H, P.H, page0, gain, nullptr))
     return;
   st.publish(k, 0);
   if (wg == 0 && s == 1) {
@@ -731,12 +864,15 @@ __device__ __forceinline__ void stager_wave(const Params& P, const MegaBufs& M, 
 }
 
 template <bool EXACT, int HD, typename KT, int GQ>
-__device__ __forceinline__ void mega_body(const Params& P, const MegaBufs& M, const Step& S, int pf) {
+__device__ __forceinline__ void mega_body(const Params& P, const MegaBufs& M, const Step& S, int) {
   extern __shared__ __align__(16) unsigned char smem[];
   MegaLds* L = reinterpret_cast<MegaLds*>(smem);
   float* pages = reinterpret_cast<float*>(smem + sizeof(MegaLds));
-  float* resid = pages + 2 * pf;
-  float* rope = resid + ((P.H + 3) & ~3);
+  int pf, pf1;
+  mega_pages(P.H, P.nq * HD, P.F, &pf, &pf1);
+  float* resid = pages + pf + pf1;
+  float* gain = resid + ((P.H + 3) & ~3);
+  float* rope = gain + ((P.H + 3) & ~3);
   float* res = rope + ((HD + 3) & ~3);
   constexpr int rs = kMegaMaxTasks * (kR + 1);  // per compute wave: results + task ids
   float* qs = res + NC * rs;                     // attention unit: the group's queries [GQ][HD]
@@ -754,7 +890,7 @@ __device__ __forceinline__ void mega_body(const Params& P, const MegaBufs& M, co
   __syncthreads();  // the only workgroup barrier
   if (L->abort) return;
   if (wave < NS) {
-    stager_wave<HD, KT, GQ>(P, M, S, L, pages, pf, resid, rope, qs, recs, wave, lane);
+    stager_wave<HD, KT, GQ>(P, M, S, L, pages, pf, resid, gain, rope, qs, recs, wave, lane);
   } else {
     const int c = wave - NS;
     float* r = res + c * rs;
@@ -791,10 +927,11 @@ MK_MEGA(x, 128, f32, float, 4)
 MK_MEGA(x, 128, bf16, uint16_t, 4)
 // the LDS layout, once
 int mega_lds_bytes(int H, int nq, int nkv, int hd, int F, int* page_floats) {
-  const int pf = (std::max(std::max(H, nq * hd), F) + 7) & ~7;
-  if (page_floats) *page_floats = pf;
+  int pf0, pf1;
+  mega_pages(H, nq * hd, F, &pf0, &pf1);
+  if (page_floats) *page_floats = pf0 + pf1;
   const int G = nq / nkv;
-  const int floats = 2 * pf + ((H + 3) & ~3) + ((hd + 3) & ~3) + NC * kMegaMaxTasks * (kR + 1) + G * hd +
+  const int floats = pf0 + pf1 + 2 * ((H + 3) & ~3) + ((hd + 3) & ~3) + NC * kMegaMaxTasks * (kR + 1) + G * hd +
                      NS * G * (hd + 2);
   return (int)sizeof(MegaLds) + 4 * floats;
 }

@@ -284,7 +284,7 @@ struct MegaBufs {
   uint64_t* h;       // [L][F] SwiGLU output
   uint64_t* key;     // [ncu] each workgroup's LM-head argmax key (epoch mod 2^15 in the low bits)
   uint32_t* host_abort;          // host-mapped word: nonzero makes every wait give up
-  unsigned long long* trace;     // optional [ops][ncu][kMegaCompute + 1] timestamps, null if off
+  unsigned long long* trace;     // optional [ops][ncu][kMegaCompute + 3] timestamps, null if off
 };
 
 // LDS header of the megakernel (followed by the two input pages, the
@@ -302,6 +302,14 @@ struct alignas(16) MegaLds {
   unsigned long long lm_best;  // best LM-head key of the workgroup
   unsigned long long pad2;
 };
+
+// Input pages of the megakernel: page 0 holds the hidden-size inputs (QKV,
+// gate/up, LM head), page 1 the attention output and the SwiGLU output (O,
+// down); floats each, rounded to 8.
+MK_HD inline void mega_pages(int H, int qd, int F, int* pf0, int* pf1) {
+  *pf0 = (H + 7) & ~7;
+  *pf1 = ((qd > F ? qd : F) + 7) & ~7;
+}
 
 // Status codes latched by the kernel.
 enum : uint32_t { ST_OK = 0, ST_TIMEOUT = 1, ST_NONFINITE = 2, ST_BADTOKEN = 3, ST_LDS = 4 };

@@ -65,16 +65,48 @@ typedef struct {
 mk_status mk_get_debug_view(mk_handle* h, mk_debug_view* out);
 
 /* Kernel status words (synchronous): [0] abort flag, [1] error code (0 ok,
- * 1 timeout, 2 non-finite logits, 3 token id out of range, 4 LDS smaller than
- * requested), then for a timeout: [2] CU, [3] task id, [4] event, [5] value
- * seen, [6] value needed, [7] waiter (0 scheduler/event, 1 scheduler/page,
- * 2 worker/frontier), [8] ready frontier, [9] ticket counter. */
+ * 1 timeout, 2 non-finite logits, 3 token id out of range), then for a
+ * megakernel timeout: [2] workgroup, [3] wave (0..3 stagers, 4..7 compute
+ * waves), [4] (operator index << 8) | wait kind (1 input page, 2 compute
+ * completions, 3 stager rendezvous, 4 tagged operator input, 5 queries/keys/
+ * values, 6 attention records, 7 LM-head keys), [5] value seen or progress,
+ * [6] value needed, [7] 3. */
 mk_status mk_read_status(mk_handle* h, uint32_t out[16]);
 
-/* Per-task timestamps of the last megakernel step when created with
- * MK_FLAG_TRACE: out[2*i] = (cu << 48) | start, out[2*i+1] = end, in ticks of
- * the device wall clock (`ticks_per_us` returned). Synchronous. */
+/* Timestamps of the per-operator path's wave timelines (see mk_trace_op),
+ * when created with MK_FLAG_TRACE: *n = entry pairs, in ticks of the device
+ * wall clock (`ticks_per_us` returned).  Synchronous. */
 mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, double* ticks_per_us);
+
+/* Megakernel timestamps of the last step (MK_MODE_MEGAKERNEL created with
+ * MK_FLAG_TRACE), in ticks of the device wall clock (*ticks_per_us).  Layout
+ * out[(k * ncu + w) * (slots) + j] for GEMV operator k (k = 4 l + {0 QKV, 1 O,
+ * 2 gate/up, 3 down}; k = 4 L the LM head), workgroup w: j < slots - 1 is
+ * compute wave j's (duration << 32) | (end mod 2^32), from the moment its
+ * input page was published to the end of its epilogues; j = slots - 1 is the
+ * full 64-bit time at which the workgroup's stager published the page.
+ * *ops, *ncu and *slots give the dimensions; with out NULL only those are
+ * returned.  cap = capacity of out in words.  Synchronous. */
+mk_status mk_mega_trace(mk_handle* h, uint64_t* out, int64_t cap, int32_t* ops, int32_t* ncu, int32_t* slots,
+                        double* ticks_per_us);
+
+/* The megakernel's hand-over buffers (device pointers; 64-bit words, fp32
+ * value bits in the low half and the epoch of the step that wrote them in
+ * the high half): x [L+1][H] (row l+1 = residual after layer l), xmid [L][H],
+ * qkv [L][(nq + 2 nkv) hd] (rotated q, rotated k, v of the last position),
+ * attn [L][nq hd], h [L][F]; epoch = the epoch of the last enqueued step. */
+typedef struct {
+  const uint64_t *x, *xmid, *qkv, *attn, *h;
+  uint32_t epoch;
+} mk_mega_view;
+mk_status mk_get_mega_view(mk_handle* h, mk_mega_view* out);
+
+/* HBM streaming-read probe: reads `bytes` (a multiple of 16) of src with
+ * 16-byte non-temporal loads from `wgs` workgroups of 512 threads, `loads`
+ * loads in flight per thread (4, 8 or 16), `reps` times on `stream`;
+ * *best_ms = the fastest repetition (HIP events).  Synchronous. */
+mk_status mk_t_stream_read(const void* src, int64_t bytes, int32_t wgs, int32_t loads, int32_t reps, void* stream,
+                           float* best_ms);
 
 /* Per-operator wave timeline (MK_MODE_PER_OP, batch 1, handle created with
  * MK_FLAG_TRACE | MK_FLAG_NO_GRAPH): from now on the waves of operator
