@@ -154,7 +154,7 @@ def mega_overhead(abi, shape, dw, prompt_t, steps, torch, dump=None):
     if dump:
         np.save(dump, tr)
     ops, ncu, slots = tr.shape
-    nc = slots - 3  # compute waves; then the stager's publish, poll-start and input-complete times
+    nc = slots - 10  # compute waves; then the stager's publish, poll-start, input-complete and attention times
     end = (tr[:, :, :nc] & np.uint64(0xFFFFFFFF)).astype(np.int64)
     dur = (tr[:, :, :nc] >> np.uint64(32)).astype(np.int64)
     pub = (tr[:, :, nc] & np.uint64(0xFFFFFFFF)).astype(np.int64)
@@ -169,6 +169,21 @@ def mega_overhead(abi, shape, dw, prompt_t, steps, torch, dump=None):
     run = dur.max(axis=2) / tpu
     names = ("qkv", "o", "gu", "down")
     by = lambda a, i: float(np.median(a[(np.arange(1, ops) % 4) == i])) if ops > 1 else 0.0
+    # attention path of each layer, from the last workgroup finishing QKV:
+    # units' inputs complete, units' records written, merges' inputs complete,
+    # merges' outputs written (medians over the workgroups that ran them), and
+    # O's input complete (median workgroup)
+    path = {n: [] for n in ("unit_inputs", "unit_record", "merge_inputs", "merge_output", "o_input")}
+    for l in range(shape.n_layers):
+        k = 4 * l + 1
+        qe = end_us[k - 1].max()
+        for j, n in zip(range(3, 7), ("unit_inputs", "unit_record", "merge_inputs", "merge_output")):
+            raw = tr[k, :, nc + j]
+            m = raw != 0
+            if m.any():
+                path[n].append(float(np.median(rel((raw[m] & np.uint64(0xFFFFFFFF)).astype(np.int64)))) - qe)
+        path["o_input"].append(float(np.median(got_us[k])) - qe)
+    attn_path = {n: float(np.median(v)) for n, v in path.items() if v}
     return {"wait_us_median": float(np.median(wait)), "wait_us_p90": pct(wait.reshape(-1), 90),
             "wait_us_per_step": float(wait.sum(axis=0).mean()),
             "wait_us_median_by_op": {n: by(np.median(wait, axis=1), i) for i, n in enumerate(names)},
@@ -177,7 +192,7 @@ def mega_overhead(abi, shape, dw, prompt_t, steps, torch, dump=None):
             "stage_us_median_by_op": {n: by(stage, i) for i, n in enumerate(names)},
             "op_run_us_median": {n: float(np.median(run[i::4][:shape.n_layers])) for i, n in enumerate(names)},
             "lm_head_run_us_median": float(np.median(run[-1])),
-
+            "attention_path_us_after_qkv": attn_path,
             "steps_traced": steps}
 
 
@@ -360,7 +375,7 @@ def main():
         log(f"megakernel: {mega_ms:.4f} ms/token (median of 5), p50 {mega['step_p50_ms']:.4f}, "
             f"p99 {mega['step_p99_ms']:.4f} ms; bound {bound_ms:.4f} ms")
         if not args.no_trace:
-            mega["overhead"] = mega_overhead(abi, shape, dw, prompt_t, 8, torch, dump=args.trace_dump)
+            mega["overhead"] = mega_overhead(abi, shape, dw, prompt_t, args.steps, torch, dump=args.trace_dump)
             log(f"megakernel operator-boundary wait: median {mega['overhead']['wait_us_median']:.2f} us, "
                 f"{mega['overhead']['wait_us_per_step']:.1f} us per step")
 

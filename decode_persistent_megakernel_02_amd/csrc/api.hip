@@ -601,8 +601,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     if (G != 1 && G != 2 && G != 4 && G != 8)
       return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports 1, 2, 4 or 8 query heads per KV head");
     if (cfg->vocab > (1 << 17)) return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports vocab <= 131072");
-    if (cfg->hidden > 16 * kMegaStagers * kWave)
-      return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports hidden <= 4096");
+    if (cfg->n_q_heads > 256) return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL supports at most 256 query heads");
     if (cfg->flags & (MK_FLAG_FUSED_MERGE | MK_FLAG_NO_GRAPH | MK_FLAG_TILED_WEIGHTS | MK_FLAG_POISON))
       return fail(MK_ERR_INVALID_ARG, "FUSED_MERGE, NO_GRAPH, TILED_WEIGHTS and POISON are per-operator flags");
   }
@@ -612,6 +611,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   MK_TRY(device_facts(&dev_cus, &tpu, &max_lds));
   const int ncu = cfg->num_cus > 0 ? std::min(cfg->num_cus, dev_cus) : dev_cus;
   if (ncu < 1) return fail(MK_ERR_HIP, "no compute units reported");
+  if (cfg->mode == MK_MODE_MEGAKERNEL && ncu > 256)
+    return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL runs on at most 256 compute units (set num_cus)");
 
   auto* h = new mk_handle();
   std::unique_ptr<mk_handle> guard(h);
@@ -773,7 +774,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     *h->host_abort = 0;
     HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void**>(&M.host_abort), h->host_abort, 0));
     if (cfg->flags & MK_FLAG_TRACE) {
-      h->mega_trace_words = (int64_t)(4 * L + 1) * ncu * (kMegaCompute + 3);
+      h->mega_trace_words = (int64_t)(4 * L + 1) * ncu * kMegaTraceSlots;
       MK_TRY(h->alloc(&M.trace, h->mega_trace_words));
       HIP_TRY(hipMemset(M.trace, 0, h->mega_trace_words * 8));
     }
@@ -1178,7 +1179,7 @@ mk_status mk_mega_trace(mk_handle* h, uint64_t* out, int64_t cap, int32_t* ops, 
   if (!h->mega.trace) return fail(MK_ERR_STATE, "megakernel handle created without MK_FLAG_TRACE");
   if (ops) *ops = 4 * h->P.L + 1;
   if (ncu) *ncu = h->P.ncu;
-  if (slots) *slots = kMegaCompute + 3;
+  if (slots) *slots = kMegaTraceSlots;
   if (ticks_per_us) *ticks_per_us = h->ticks_per_us;
   if (!out) return MK_OK;
   if (cap < h->mega_trace_words) return fail(MK_ERR_CAPACITY, "capacity too small");

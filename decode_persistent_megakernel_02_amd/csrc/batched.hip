@@ -5,8 +5,10 @@
 // sequences that is 8 FMAs per weight element and at 64 it is 64, beyond what
 // the vector ALUs sustain at HBM speed.  The products therefore run on the
 // matrix cores (v_mfma_f32_16x16x32_bf16: bf16 operands, fp32 accumulation),
-// the skinny-GEMM form the Hazy Research megakernel write-up ("Look Ma, No
-// Bubbles!", its batched throughput section) gives for serving-size batches.
+// the matrix-matrix form that the summary of the Hazy Research throughput
+// megakernel (hakusoku, "全てのGPUを購入したので、徹底的にそのGPUを活用します。",
+// section 高スループットMegakernelの設計と工夫 / 命令セットの再設計) gives for
+// throughput-oriented batches, as against matrix-vector bodies for latency.
 // The activation operand is written, when it is produced, as two bf16 planes
 // hi = bf16(v) and lo = bf16(v - hi) -- by mk_b_norm for the normalised
 // inputs, the merge kernel for the attention output, the gate/up epilogue for

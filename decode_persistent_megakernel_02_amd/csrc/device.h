@@ -310,17 +310,21 @@ struct AttnBuf {
 typedef const __attribute__((address_space(1))) uint32_t* gu32_ptr;
 typedef const __attribute__((address_space(1))) uint16_t* gu16_ptr;
 
-// Issues the K and V loads of the block [p0, p0 + NP).  Positions at or past
-// p1 read position p1 - 1 (in bounds; attn_compute masks them), so no load is
-// predicated.  kc, vc: this group's cache rows (position p at + p * HD).
+// Issues the K loads of the block [p0, p0 + NP).  Positions at or past p1
+// read position p1 - 1 (in bounds; attn_compute masks them), so no load is
+// predicated.  kc: this group's cache rows (position p at + p * HD).
 template <int HD, typename KT>
-__device__ __forceinline__ void attn_load(const KT* kc, const KT* vc, int p0, int p1, int lane,
-                                          AttnBuf<HD, KT>& bf) {
+__device__ __forceinline__ void attn_load_k(const KT* kc, int p0, int p1, int lane, AttnBuf<HD, KT>& bf) {
   using Gm = AttnGeom<HD, KT>;
   const int my = lane / Gm::LPP, part = lane % Gm::LPP;
   const v4u* krow = reinterpret_cast<const v4u*>(kc + (int64_t)min(p0 + my, p1 - 1) * HD + part * Gm::EPL);
 #pragma unroll
   for (int i = 0; i < Gm::KV16; ++i) bf.kr[i] = ld_g(krow + i);
+}
+// The same for V (vc: position p at + p * HD).
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_load_v(const KT* vc, int p0, int p1, int lane, AttnBuf<HD, KT>& bf) {
+  using Gm = AttnGeom<HD, KT>;
 #pragma unroll
   for (int j = 0; j < Gm::NP; ++j) {
     const KT* vrow = vc + (int64_t)min(p0 + j, p1 - 1) * HD + lane * Gm::DPL;
@@ -331,6 +335,12 @@ __device__ __forceinline__ void attn_load(const KT* kc, const KT* vc, int p0, in
       for (int w = 0; w < AttnBuf<HD, KT>::VW; ++w) bf.vr[j][w] = ((gu32_ptr)vrow)[w];
     }
   }
+}
+template <int HD, typename KT>
+__device__ __forceinline__ void attn_load(const KT* kc, const KT* vc, int p0, int p1, int lane,
+                                          AttnBuf<HD, KT>& bf) {
+  attn_load_k<HD, KT>(kc, p0, p1, lane, bf);
+  attn_load_v<HD, KT>(vc, p0, p1, lane, bf);
 }
 
 // ---------------------------------------------------------------------------
@@ -565,9 +575,12 @@ __device__ __forceinline__ void attn_store_state_mf(const AttnStateMf& st, int G
 // Online-softmax update with the block [p0, min(p0 + NP, p1)) held in bf.
 // qs: LDS [G][HD] (rotated queries).  The weight of position j reaches every
 // lane by a read of lane j * LPP into a scalar register.
+// jr >= 0: row jr of the block takes its values from vcur (this lane's DPL
+// dims) instead of bf -- the current position, whose value arrived this step.
 template <int HD, typename KT, int GQ = 0>
 __device__ __forceinline__ void attn_compute(const AttnBuf<HD, KT>& bf, const float* qs, int p0, int p1, int G,
-                                             int lane, AttnState<HD, GQ>& st) {
+                                             int lane, AttnState<HD, GQ>& st, int jr = -1,
+                                             const float* vcur = nullptr) {
   using Gm = AttnGeom<HD, KT>;
   using Hs = GqaHeads<GQ>;
   constexpr int DPL = Gm::DPL, NP = Gm::NP, LPP = Gm::LPP, EPL = Gm::EPL, GM = Hs::MAX;
@@ -618,6 +631,10 @@ __device__ __forceinline__ void attn_compute(const AttnBuf<HD, KT>& bf, const fl
           } else {
 #pragma unroll
             for (int e = 0; e < DPL; ++e) v[e] = __uint_as_float(bf.vr[j][e]);
+          }
+          if (vcur) {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) v[e] = j == jr ? vcur[e] : v[e];
           }
 #pragma unroll
           for (int e = 0; e < DPL; ++e) st.o[h][e] = fmaf(p, v[e], st.o[h][e]);

@@ -61,7 +61,7 @@ constexpr int NB = 2;   // weight buffers (tasks in flight) per compute wave
 constexpr int kMegaMaxTasks = 128;
 // trace words per (operator, workgroup): compute waves' (duration, end), then
 // the stager's publish time, poll start and input-complete time
-constexpr int kTraceSlots = kMegaCompute + 3;
+constexpr int kTraceSlots = kMegaTraceSlots;
 
 // ---- tagged words ----------------------------------------------------------
 __device__ __forceinline__ void tput(uint64_t* p, float v, uint32_t epoch) {
@@ -388,6 +388,9 @@ __device__ __forceinline__ void compute_wave(const Params& P, const MegaBufs& M,
       case TT_DOWN: compute_op<TT_DOWN, EXACT>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
       default: compute_op<TT_LM, EXACT>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
     }
+    // the next operator's first tasks go in flight before this one is
+    // reported done: the stagers then poll the next input behind the burst
+    // of weight loads rather than competing with it
     if (k + 1 < nops) fetch_first<EXACT>(P, k + 1, c, B, t, lane);
     if (M.trace && lane == 0) {
       const uint64_t t1 = clock_now();
@@ -521,17 +524,20 @@ struct Stager {
 };
 
 // Log-sum-exp merge of query head hq's split records -> tagged attention
-// output.  Splits are taken SB at a time: every load of a round (this lane's
-// dims of each split's o, and split s0 + lane's m and l) is issued at once,
-// then only stale words are read again; the rounds merge online (running
-// maximum, rescaled sums), in split order.
+// output, by the workgroup's NS stager waves together.  Wave s takes the
+// splits s, s + NS, s + 2 NS, ..., SB of them per round: every load of a
+// round (this lane's dims of each split's o, and its (m, l) for lane < SB) is
+// issued at once, then only stale words are read again, so up to NS SB
+// splits cost one round trip.  Each wave merges its splits online (running
+// maximum, rescaled sums); the NS partial states then meet in LDS, where
+// wave 0 combines them in wave order and writes the output.
 template <int HD>
-__device__ __forceinline__ bool merge_unit(Stager& st, int l, int hq) {
+__device__ __forceinline__ bool merge_unit(Stager& st, int l, int hq, float* recs) {
   const Params& P = st.P;
   const MegaBufs& M = st.M;
-  const int lane = st.lane, G = P.nq / P.nkv, g = hq / G, hh = hq % G;
+  const int lane = st.lane, s = st.s, G = P.nq / P.nkv, g = hq / G, hh = hq % G;
   const int used = (st.S.pos + 1 + P.split - 1) / P.split;
-  constexpr int DPL = HD / kWave, SB = 16;
+  constexpr int DPL = HD / kWave, SB = 8;
   const uint32_t ep = st.S.epoch;
   const uint64_t cur = (uint64_t)ep << 32;
   const size_t rs = (size_t)G * (HD + 2);
@@ -539,15 +545,17 @@ __device__ __forceinline__ bool merge_unit(Stager& st, int l, int hq) {
   float Mx = -INFINITY, Lsum = 0.f, o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int s0 = 0; s0 < used; s0 += SB) {
-    const int n = min(SB, used - s0);
-    const bool mine = lane < n;  // this lane reads split s0 + lane's (m, l)
-    const uint64_t* ml = base + (size_t)(s0 + (mine ? lane : 0)) * rs + HD;
+  for (int s0 = 0; s0 < used; s0 += NS * SB) {
+    // this wave's splits of the round: s0 + s + NS j, j < n
+    const int first = s0 + s, n = first < used ? min(SB, (used - first + NS - 1) / NS) : 0;
+    const bool mine = lane < n;  // this lane reads split first + NS lane's (m, l)
+    const uint64_t* ml = base + (size_t)(first + NS * (mine ? lane : 0)) * rs + HD;
     uint64_t wm = mine ? tget(ml) : cur, wl = mine ? tget(ml + 1) : cur, w[SB][DPL];
 #pragma unroll
     for (int j = 0; j < SB; ++j)
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) w[j][e] = j < n ? tget(base + (size_t)(s0 + j) * rs + lane * DPL + e) : cur;
+      for (int e = 0; e < DPL; ++e)
+        w[j][e] = j < n ? tget(base + (size_t)(first + NS * j) * rs + lane * DPL + e) : cur;
     Spin sp;
     for (;;) {
       bool ok = tcur(wm, ep) && tcur(wl, ep);
@@ -556,7 +564,7 @@ __device__ __forceinline__ bool merge_unit(Stager& st, int l, int hq) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) ok = ok && tcur(w[j][e], ep);
       if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
-      if (!sp.tick<kPollSleep>(P, M, st.L, st.s, ((uint32_t)st.k << 8) | W_REC, (uint32_t)s0, (uint32_t)used, lane))
+      if (!sp.tick<kPollSleep>(P, M, st.L, s, ((uint32_t)st.k << 8) | W_REC, (uint32_t)s0, (uint32_t)used, lane))
         return false;
       if (!tcur(wm, ep)) wm = tget(ml);
       if (!tcur(wl, ep)) wl = tget(ml + 1);
@@ -564,12 +572,13 @@ __device__ __forceinline__ bool merge_unit(Stager& st, int l, int hq) {
       for (int j = 0; j < SB; ++j)
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
-          if (!tcur(w[j][e], ep)) w[j][e] = tget(base + (size_t)(s0 + j) * rs + lane * DPL + e);
+          if (!tcur(w[j][e], ep)) w[j][e] = tget(base + (size_t)(first + NS * j) * rs + lane * DPL + e);
     }
     // records with l == 0 hold no positions and carry weight 0
     const float ms = tval(wm), ls = tval(wl);
     const bool live = mine && ls > 0.f;
     const float Mn = fmaxf(Mx, wave_max(live ? ms : -INFINITY));
+    if (Mn == -INFINITY) continue;  // nothing live yet
     const float alpha = Mx == -INFINITY ? 0.f : __expf(Mx - Mn);
     const float wgt = live ? __expf(ms - Mn) : 0.f;
     Lsum = Lsum * alpha + wave_sum(wgt * (live ? ls : 0.f));
@@ -583,21 +592,48 @@ __device__ __forceinline__ bool merge_unit(Stager& st, int l, int hq) {
     }
     Mx = Mn;
   }
-  const float inv = 1.0f / Lsum;
-  uint64_t* out = M.attn + (size_t)l * P.nq * HD + (size_t)hq * HD + lane * DPL;
+  st.mark(st.k, NC + 5);
+  float* mine_rec = recs + s * (HD + 2);
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) tput(out + e, o[e] * inv, ep);
-  return true;
+  for (int e = 0; e < DPL; ++e) mine_rec[lane * DPL + e] = o[e];
+  if (lane == 0) {
+    mine_rec[HD] = Mx;
+    mine_rec[HD + 1] = Lsum;
+  }
+  if (!st.sync()) return false;  // every wave's state is in recs
+  if (s == 0) {
+    float Mt = -INFINITY, Lt = 0.f, ot[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) ot[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NS; ++w) {
+      const float* r = recs + w * (HD + 2);
+      const float lw = r[HD + 1];
+      if (!(lw > 0.f)) continue;
+      const float mw = r[HD], Mn = fmaxf(Mt, mw);
+      const float a = __expf(Mt - Mn), c = __expf(mw - Mn);
+      Lt = Lt * a + lw * c;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ot[e] = ot[e] * a + r[lane * DPL + e] * c;
+      Mt = Mn;
+    }
+    const float inv = 1.0f / Lt;
+    uint64_t* out = M.attn + (size_t)l * P.nq * HD + (size_t)hq * HD + lane * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) tput(out + e, ot[e] * inv, ep);
+    st.mark(st.k, NC + 6);
+  }
+  return st.sync();  // recs is reused by the next merge
 }
 
-// Puts row jr of a block held in registers (the current position, whose
-// key and value arrive as tagged words this step) into the block: kv and vv
-// hold this lane's dims lane * DPL + e of the key and value.  The key part a
-// lane scores (dims part * EPL ..) is gathered from the lanes that hold those
-// dims; every lane takes part in the shuffles, the lanes of row jr keep them.
+// Puts the key of row jr of a block held in registers (the current position,
+// whose key arrives as tagged words this step) into the block: kv holds this
+// lane's dims lane * DPL + e.  The key part a lane scores (dims part * EPL ..)
+// is gathered from the lanes that hold those dims; every lane takes part in
+// the shuffles, the lanes of row jr keep them.  (The row's value is taken
+// from registers when the block is computed.)
 template <int HD, typename KT>
-__device__ __forceinline__ void attn_patch_row(AttnBuf<HD, KT>& A, int jr, const float (&kv)[HD / kWave],
-                                               const float (&vv)[HD / kWave], int lane) {
+__device__ __forceinline__ void attn_patch_k(AttnBuf<HD, KT>& A, int jr, const float (&kv)[HD / kWave], int lane) {
   using Gm = AttnGeom<HD, KT>;
   constexpr int DPL = Gm::DPL, EPL = Gm::EPL;
   const int my = lane / Gm::LPP, part = lane % Gm::LPP;
@@ -613,19 +649,6 @@ __device__ __forceinline__ void attn_patch_row(AttnBuf<HD, KT>& A, int jr, const
       } else {
         A.kr[i] = v4u{bf_pack(f2bf(kp[8 * i]), f2bf(kp[8 * i + 1])), bf_pack(f2bf(kp[8 * i + 2]), f2bf(kp[8 * i + 3])),
                       bf_pack(f2bf(kp[8 * i + 4]), f2bf(kp[8 * i + 5])), bf_pack(f2bf(kp[8 * i + 6]), f2bf(kp[8 * i + 7]))};
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < Gm::NP; ++j) {
-    if (j == jr) {
-      if constexpr (sizeof(KT) == 4) {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) A.vr[j][e] = __float_as_uint(vv[e]);
-      } else if constexpr (DPL == 2) {
-        A.vr[j][0] = bf_pack(f2bf(vv[0]), f2bf(vv[1]));
-      } else {
-        A.vr[j][0] = f2bf(vv[0]);
       }
     }
   }
@@ -667,11 +690,13 @@ __device__ __forceinline__ bool attn_unit(Stager& st, int l, int g, int sp_i, fl
   const int64_t o0 = kv_off(P, l, 0, g, 0);
   KT* kc = static_cast<KT*>(P.kcache) + o0;
   KT* vc = static_cast<KT*>(P.vcache) + o0;
-  // this wave's first block (rows from the cache, clamped at the current position)
+  // this wave's first block: its keys from the cache (clamped at the current
+  // position) before the queries are awaited, its values once they are here
+  // (values are used after the scores, so their loads overlap the softmax)
   int b0 = p0 + s * NP;
   AttnBuf<HD, KT> A;
   bool pre = b0 < p1;
-  if (pre) attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
+  if (pre) attn_load_k<HD, KT>(kc, b0, p1, lane, A);
   uint64_t qw[QW], kw[DPL], vw[DPL];
 #pragma unroll
   for (int j = 0; j < QW; ++j) qw[j] = (s + j * NS) * kWave < G * HD ? tget(qsrc + (s + j * NS) * kWave) : cur;
@@ -704,8 +729,10 @@ __device__ __forceinline__ bool attn_unit(Stager& st, int l, int g, int sp_i, fl
 #pragma unroll
   for (int j = 0; j < QW; ++j)
     if ((s + j * NS) * kWave < G * HD) qs[(s + j * NS) * kWave + lane] = tval(qw[j]);
-  if (append) {  // position T - 1: into the cache for later steps, into the preloaded block for this one
-    float kf[DPL], vf[DPL];
+  float vf[DPL];  // the current position's value (this lane's dims), when this wave appends
+  int jr = -1;    // its row in the first block, if there
+  if (append) {  // position T - 1: into the cache for later steps, into the first block for this one
+    float kf[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
       kf[e] = tval(kw[e]);
@@ -714,25 +741,33 @@ __device__ __forceinline__ bool attn_unit(Stager& st, int l, int g, int sp_i, fl
       if constexpr (sizeof(KT) == 4) { kc[at] = kf[e]; vc[at] = vf[e]; }
       else { kc[at] = f2bf(kf[e]); vc[at] = f2bf(vf[e]); }
     }
-    const int jr = T - 1 - b0;
-    if (jr < NP) {
-      attn_patch_row<HD, KT>(A, jr, kf, vf, lane);  // the row is in the preloaded first block
+    if (T - 1 - b0 < NP) {
+      jr = T - 1 - b0;
+      attn_patch_k<HD, KT>(A, jr, kf, lane);  // the row is in the first block
     } else {
       // the row is in a later block of this wave, loaded below by other lanes
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
   }
+  if (pre) attn_load_v<HD, KT>(vc, b0, p1, lane, A);
+  st.mark(st.k, NC + 3);
   if (!st.sync()) return false;  // every wave's query words are in qs
+  st.mark(st.k, NC + 7);
   AttnState<HD, GQ> sta;
   sta.init();
+  if (pre) {
+    attn_compute<HD, KT, GQ>(A, qs, b0, p1, G, lane, sta, jr, vf);
+    b0 += NS * NP;
+  }
   for (; b0 < p1; b0 += NS * NP) {
-    if (!pre) attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
-    pre = false;
+    attn_load<HD, KT>(kc, vc, b0, p1, lane, A);
     attn_compute<HD, KT, GQ>(A, qs, b0, p1, G, lane, sta);
   }
   attn_store_state<HD, GQ>(sta, G, recs + s * G * (HD + 2), lane);
+  st.mark(st.k, NC + 8);
   if (!st.sync()) return false;  // every wave's state is in recs
+  st.mark(st.k, NC + 9);
   // merge the waves' states of head h (wave h % NS) into the unit's record
   uint64_t* rec = M.rec + (((size_t)l * P.nkv + g) * P.nsplit + sp_i) * G * (HD + 2);
   for (int h = s; h < G; h += NS) {
@@ -758,6 +793,7 @@ __device__ __forceinline__ bool attn_unit(Stager& st, int l, int g, int sp_i, fl
       tput(rec + h * (HD + 2) + HD + 1, Ls, ep);
     }
   }
+  st.mark(st.k, NC + 4);
   return st.sync();  // qs and recs are reused by the next unit
 }
 
@@ -819,7 +855,8 @@ __device__ __forceinline__ void stager_wave(const Params& P, const MegaBufs& M, 
     // log-sum-exp merges of the query heads assigned to this wave; both wait
     // for the local QKV tasks first, so that they do not poll while QKV runs
     st.load_gain(ld_const(P.ffn_norm + l), P.H, gain);  // for GU, ahead of every wait below
-    const int hq0 = (ncu - 1 - wg) + ncu * s;
+    const int hq0 = ncu - 1 - wg;  // query heads merged here: hq0, hq0 + ncu, ... (all stager waves)
+    st.k = k + 1;  // attention and merges are traced under the O operator
     if (wg < nunits || hq0 < P.nq)
       if (!st.wait_done(k, done_after(k))) return;
     for (int u = wg; u < nunits; u += ncu) {
@@ -827,8 +864,8 @@ __device__ __forceinline__ void stager_wave(const Params& P, const MegaBufs& M, 
       if (sp_i >= used) continue;
       if (!attn_unit<HD, KT, GQ>(st, l, g, sp_i, qs, recs)) return;
     }
-    for (int hq = hq0; hq < P.nq; hq += NS * ncu)
-      if (!merge_unit<HD>(st, l, hq)) return;
+    for (int hq = hq0; hq < P.nq; hq += ncu)
+      if (!merge_unit<HD>(st, l, hq, recs)) return;
     // O: the merged attention output
     st.k = ++k;
     if (!st.wait_done(k, free_for(k)) || !st.load_tagged(M.attn + (size_t)l * P.nq * P.hd, P.nq * P.hd, page1))

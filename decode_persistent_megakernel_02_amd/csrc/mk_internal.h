@@ -271,6 +271,7 @@ struct Lds {
 constexpr int kMegaStagers = 4;   // waves that stage operator inputs and run attention, merges, argmax
 constexpr int kMegaCompute = 4;   // waves that stream weights (the GEMV tasks), four tasks in flight each
 constexpr int kMegaWaves = kMegaStagers + kMegaCompute;
+constexpr int kMegaTraceSlots = kMegaCompute + 10;  // timestamps per (operator, workgroup) when tracing
 
 // Buffers through which workgroups hand values to each other.  Each element
 // is a 64-bit word: fp32 value bits in the low half, the epoch of the step
@@ -284,7 +285,7 @@ struct MegaBufs {
   uint64_t* h;       // [L][F] SwiGLU output
   uint64_t* key;     // [ncu] each workgroup's LM-head argmax key (epoch mod 2^15 in the low bits)
   uint32_t* host_abort;          // host-mapped word: nonzero makes every wait give up
-  unsigned long long* trace;     // optional [ops][ncu][kMegaCompute + 3] timestamps, null if off
+  unsigned long long* trace;     // optional [ops][ncu][kMegaTraceSlots] timestamps, null if off
 };
 
 // LDS header of the megakernel (followed by the two input pages, the

@@ -2,23 +2,38 @@
  *
  * One autoregressive decode step of a Llama-style decoder -- embedding
  * lookup, RMSNorm, QKV projection + RoPE + KV-cache append, GQA attention over
- * the bf16 KV cache, O-projection + residual, RMSNorm, SwiGLU MLP + residual,
- * final RMSNorm, LM head and greedy argmax -- runs as ONE launched kernel that
- * executes a fine-grained task graph.
+ * the KV cache, O-projection + residual, RMSNorm, SwiGLU MLP + residual,
+ * final RMSNorm, LM head and greedy argmax -- split into fine-grained tasks.
+ *
+ * How a step runs (mk_config.mode):
+ *  - MK_MODE_MEGAKERNEL (one sequence): ONE ordinary kernel launch per step.
+ *    Every compute unit holds one persistent workgroup of eight waves: four
+ *    stager waves stage each operator's input into LDS (with the RMSNorm
+ *    gain), run the split-KV attention units and the log-sum-exp merges;
+ *    four compute waves pull the operator's GEMV tasks from an LDS task pool
+ *    and run the fused epilogues (RoPE + KV append, residuals, SwiGLU, LM-head
+ *    argmax).  Dependencies between workgroups travel as epoch-tagged data
+ *    words: a consumer re-reads a word until it carries the step's epoch.
+ *  - MK_MODE_PER_OP: the same task bodies as one kernel launch per operator,
+ *    replayed as one captured HIP graph per step (the comparison build).
+ *  - max_batch >= 2 always runs per operator, with matrix-core (MFMA) bodies.
+ * The KV cache is bf16 or fp32 (mk_config.kv_fp32), in either mode.
  *
  * Sources of the method (web pages, cited by title and section):
  *  - "Compilar LLM en un MegaKernel para lograr inferencia de baja latencia"
  *    (GeekNews summary of the Mirage Persistent Kernel post), sections
  *    "Parte 1. Compilador" (operator graph -> fine-grained task graph of tasks
- *    and events) and "Parte 2. Runtime" (workers, schedulers, event counters
- *    with thresholds, 1-2 us inter-task overhead).
+ *    and events) and "Parte 2. Runtime" (workers, schedulers, event-driven
+ *    execution inside one kernel, 1-2 us inter-task overhead).
  *  - "MPK: A Compiler and Runtime for Mega-Kernelizing Tensor Programs"
- *    (gist.science explainer), sections 2-4 (tGraph, in-kernel runtime with
- *    ahead-of-time vs just-in-time task launch, paged shared memory).
- *  - "Llama-70B向け低レイテンシ・高スループットMegakernelの公開" (hakusoku.com
- *    summary of the Hazy Research post), section 命令セットの再設計 (fused
- *    RMS norm, QKV matmul + RoPE, attention, O-proj + residual instructions;
- *    matrix-vector bodies for latency, matrix-matrix for throughput).
+ *    (gist.science explainer), sections 1 and 3 (one kernel for the whole
+ *    program; an in-kernel runtime that starts tasks when their inputs are
+ *    ready).
+ *  - hakusoku summary of the Hazy Research megakernel posts,
+ *    "全てのGPUを購入したので、徹底的にそのGPUを活用します。", section
+ *    高スループットMegakernelの設計と工夫 / 命令セットの再設計 (fused RMS norm, QKV
+ *    matmul + RoPE, attention, O-proj + residual instructions; matrix-vector
+ *    bodies for latency, matrix-matrix for throughput).
  *  - "Cómo la fusión de kernels CUDA acelera la inferencia de LLM", section
  *    "Sigue los datos intermedios" (residual + norm fusion, SwiGLU FFN fusion).
  *
@@ -54,10 +69,9 @@ typedef enum {
   MK_ERR_UNSUPPORTED = -7    /* valid request this build does not implement */
 } mk_status;
 
-/* How a step is executed.  Both modes run the same task bodies. */
+/* How a step is executed (see the top of this file). */
 enum {
-  MK_MODE_MEGAKERNEL = 0, /* one persistent cooperative launch per step (currently
-                             refused; see mk_create) */
+  MK_MODE_MEGAKERNEL = 0, /* one persistent launch per step (max_batch 1) */
   MK_MODE_PER_OP = 1      /* one kernel launch per operator, the same task bodies */
 };
 
@@ -69,8 +83,9 @@ enum {
                                  replaying the step as one captured HIP graph */
   MK_FLAG_FUSED_MERGE = 1u << 3, /* per-op mode: run the attention log-sum-exp merge in the last
                                     split workgroup of each KV group instead of as its own launch */
-  MK_FLAG_SPIN_LIMIT_1 = 1u << 5, /* test hook: every in-kernel wait gives up after one unsuccessful
-                                     check, so a step ends in MK_ERR_TIMEOUT without any wave hanging */
+  MK_FLAG_SPIN_LIMIT_1 = 1u << 5, /* megakernel test hook: every in-kernel wait gives up after one
+                                     unsuccessful check, so a step ends in MK_ERR_TIMEOUT with every
+                                     wave exiting normally */
   MK_FLAG_TILED_WEIGHTS = 1u << 4 /* batched path (max_batch >= 2): wq, wk, wv, wo, w_gate, w_up,
                                      w_down and (untied) lm_head are stored in the tiled layout that
                                      mk_tile_weights writes; embed and the norm gains stay
@@ -90,21 +105,25 @@ enum {
 mk_status mk_tile_weights(const void* src, void* dst, int64_t N, int64_t K, void* hip_stream);
 
 /* Model shape and runtime options.  Weights are bf16, activations fp32, the
- * KV cache bf16.  Shapes must satisfy: hidden, ffn and n_q_heads*head_dim are
- * multiples of 8; head_dim is 64 or 128; n_q_heads is a multiple of
- * n_kv_heads. */
+ * KV cache bf16 or fp32 (kv_fp32).  Shapes must satisfy: hidden, ffn and
+ * n_q_heads*head_dim are multiples of 8; head_dim is 64 or 128; n_q_heads is
+ * a multiple of n_kv_heads.  MK_MODE_MEGAKERNEL further needs max_batch 1,
+ * 1, 2, 4 or 8 query heads per KV head, vocab <= 131072, n_q_heads <= 256 and
+ * at most 256 compute units (num_cus). */
 typedef struct {
   int32_t abi_version; /* must be MK_ABI_VERSION */
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
   float rms_eps;       /* RMSNorm epsilon (added to mean(x^2) inside the root) */
   float rope_theta;    /* RoPE base */
   int32_t tie_embeddings; /* nonzero: the LM head is the embedding table */
-  int32_t max_batch;   /* sequences decoded together (1..64) */
+  int32_t max_batch;   /* sequences decoded together (1..64); every prefill
+                          must use exactly this many (see mk_prefill) */
   int32_t max_seq;     /* KV-cache capacity in positions */
   int32_t mode;        /* MK_MODE_* */
   uint32_t flags;      /* MK_FLAG_* */
   uint32_t watchdog_ms;/* in-kernel dependency wait limit; 0 = 2000 ms */
-  int32_t num_cus;     /* persistent grid size; 0 = every CU of the device */
+  int32_t num_cus;     /* workgroups per operator (megakernel: persistent grid size);
+                          0 = every CU of the device */
   int32_t attn_split;  /* positions per split-KV attention task; 0 = automatic (64) */
   int32_t kv_fp32;     /* KV cache element type: 0 = bf16, nonzero = fp32 */
 } mk_config;
@@ -139,40 +158,59 @@ typedef struct {
   int32_t elem_bytes; /* 2 (bf16) or 4 (fp32) */
 } mk_kv_layout;
 
-/* Create a decoder on the current HIP device.  Validates the config, builds
- * and validates the task graph on the host, allocates the KV cache, activation
- * scratch, event counters and task tables (handle-owned), and uploads the
- * tables.  `hip_stream` is a hipStream_t (NULL = default stream); every later
- * call is ordered on it.  Synchronous w.r.t. the host.
- * MK_MODE_MEGAKERNEL returns MK_ERR_UNSUPPORTED: its cooperative launch never
- * completed on the gfx950 test device, and it stays off until the cause is found. */
+/* Create a decoder on the current HIP device ("Compilar LLM en un MegaKernel
+ * ...", section "Parte 1. Compilador": the operator graph is split into tasks
+ * and their dependencies before anything runs).  Validates the config, builds
+ * and validates the task graph on the host, allocates the KV cache, the
+ * activation and hand-over buffers and the task tables (handle-owned), and
+ * uploads the tables.  `hip_stream` is a hipStream_t (NULL = default stream);
+ * every later call is ordered on it.  Synchronous w.r.t. the host.
+ * Errors: MK_ERR_INVALID_ARG for a bad config or weight table,
+ * MK_ERR_UNSUPPORTED for a shape or mode combination this build does not run
+ * (the message names it), MK_ERR_OUT_OF_MEMORY, MK_ERR_HIP. */
 mk_status mk_create(const mk_config* cfg, const mk_weights* weights, void* hip_stream, mk_handle** out);
 
 /* Prefill: runs positions 0..P-1 of B sequences (d_tokens int32 [B, P],
  * row-major) through the decode graph one position at a time, and writes the
  * greedy token of the last position to d_next int32 [B].  If d_logits is not
- * NULL, the last position's logits are written to it (fp32 [B, vocab]).
- * Requires length == 0; sets the batch size B (1..max_batch) and length = P.
- * P + length must not exceed max_seq (MK_ERR_CAPACITY). */
+ * NULL, the last position's logits are written to it (fp32 [B, vocab]).  The
+ * pages' workload feeds a prompt before generating ("Compilar LLM en un
+ * MegaKernel ...", section "Valor central de MPK": a 39-token prompt, then
+ * 512 generated tokens); filling the cache with the decode step itself is
+ * this library's reading.  Requires length == 0; sets length = P.  B must
+ * equal max_batch: a handle is built for one batch size (task split, MFMA
+ * tiles, cache layout), so a smaller batch uses a handle created for it
+ * (B outside [1, max_batch]: MK_ERR_CAPACITY; 1 <= B < max_batch:
+ * MK_ERR_UNSUPPORTED).  P must not exceed max_seq (MK_ERR_CAPACITY). */
 mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P,
                      int32_t* d_next, float* d_logits);
 
-/* One decode step for every sequence: token ids d_in int32 [B] at position
- * `length`; writes greedy ids to d_out int32 [B] (lowest index among equal
- * maxima) and, if d_logits is not NULL, the logits fp32 [B, vocab].  d_out may
- * be the d_in of the next call (no host round trip).  length += 1.
- * MK_ERR_CAPACITY if length == max_seq (nothing enqueued). */
+/* One decode step for every sequence ("Compilar LLM en un MegaKernel ...",
+ * section "Parte 2. Runtime": the whole step's task graph executes inside one
+ * kernel in megakernel mode): token ids d_in int32 [B] at position `length`;
+ * writes greedy ids to d_out int32 [B] (lowest index among equal maxima) and,
+ * if d_logits is not NULL, the logits fp32 [B, vocab].  d_out may be the d_in
+ * of the next call (no host round trip).  length += 1.
+ * Without a prefill the first step runs at position 0 for max_batch
+ * sequences.  MK_ERR_CAPACITY if length == max_seq, MK_ERR_STATE on a
+ * poisoned handle (nothing enqueued in either case). */
 mk_status mk_decode_step(mk_handle* h, const int32_t* d_in, int32_t* d_out, float* d_logits);
 
 /* Wait for the stream; returns MK_ERR_TIMEOUT (and poisons the handle) if an
- * in-kernel watchdog fired during any earlier step. */
+ * in-kernel watchdog fired during any earlier step.  In megakernel mode a host
+ * watchdog also raises an abort word that every in-kernel wait polls, if the
+ * stream has not drained within 10 s plus 100 ms per step enqueued since the
+ * last wait, so that every wave exits.  (No passage defines this call: the
+ * pages' runtime has no host interface.) */
 mk_status mk_synchronize(mk_handle* h);
 
 /* length := 0 and batch unset; KV contents become undefined.  Clears a
- * poisoned state only for MK_ERR_STATE caused by misuse, not by a timeout. */
+ * poisoned state only for MK_ERR_STATE caused by misuse, not by a timeout.
+ * (Host plumbing; no passage.) */
 mk_status mk_reset(mk_handle* h);
 
-/* Describe the KV cache (device pointers owned by the handle). */
+/* Describe the KV cache (device pointers owned by the handle; the pages fix
+ * no cache layout, this is the library's). */
 mk_status mk_kv_view(mk_handle* h, mk_kv_layout* out);
 
 /* Copy the whole K and V caches (layout of mk_kv_view, every allocated
@@ -182,10 +220,12 @@ mk_status mk_kv_view(mk_handle* h, mk_kv_layout* out);
  * against the oracle, which then continues from the imported state. */
 mk_status mk_kv_read(mk_handle* h, void* k_host, void* v_host, int64_t bytes);
 
-/* Message of the last failed mk_* call on this thread ("" if none). */
+/* Message of the last failed mk_* call on this thread ("" if none).  (Host
+ * plumbing; no passage.) */
 const char* mk_last_error(void);
 
-/* Free everything the handle owns (waits for its stream first).  NULL-safe. */
+/* Free everything the handle owns (waits for its stream first).  NULL-safe.
+ * (Host plumbing; no passage.) */
 void mk_destroy(mk_handle* h);
 
 #ifdef __cplusplus

@@ -80,11 +80,24 @@ mk_status mk_read_trace(mk_handle* h, uint64_t* out, int32_t cap, int32_t* n, do
 
 /* Megakernel timestamps of the last step (MK_MODE_MEGAKERNEL created with
  * MK_FLAG_TRACE), in ticks of the device wall clock (*ticks_per_us).  Layout
- * out[(k * ncu + w) * (slots) + j] for GEMV operator k (k = 4 l + {0 QKV, 1 O,
- * 2 gate/up, 3 down}; k = 4 L the LM head), workgroup w: j < slots - 1 is
- * compute wave j's (duration << 32) | (end mod 2^32), from the moment its
- * input page was published to the end of its epilogues; j = slots - 1 is the
- * full 64-bit time at which the workgroup's stager published the page.
+ * out[(k * ncu + w) * slots + j] for GEMV operator k (k = 4 l + {0 QKV, 1 O,
+ * 2 gate/up, 3 down}; k = 4 L the LM head), workgroup w, with C = slots - 10
+ * compute waves:
+ *   j < C     compute wave j: (duration << 32) | (end mod 2^32), from the
+ *             moment it saw the input page published to the end of its
+ *             epilogues;
+ *   j = C     the moment the workgroup's first stager published its part of
+ *             the page (64-bit);
+ *   j = C + 1 the stager started polling operator k's input words;
+ *   j = C + 2 every word of the input had arrived;
+ *   j = C + 3 .. C + 9 (k = 4 l + 1 only, 0 elsewhere): an attention unit of
+ *             this workgroup had its query/key/value words (C + 3), had
+ *             written its record (C + 4); a merge of this workgroup had its
+ *             wave-0 share of the records (C + 5), had written its output
+ *             (C + 6); the unit's waves had met after staging the queries
+ *             (C + 7), its wave 0 had stored its softmax state (C + 8), the
+ *             waves had met after storing theirs (C + 9) (the last such unit
+ *             or merge of the workgroup).
  * *ops, *ncu and *slots give the dimensions; with out NULL only those are
  * returned.  cap = capacity of out in words.  Synchronous. */
 mk_status mk_mega_trace(mk_handle* h, uint64_t* out, int64_t cap, int32_t* ops, int32_t* ncu, int32_t* slots,

@@ -5,9 +5,9 @@ cpu_baseline leg of bench.py may import this module.  It shares no code with
 the GPU path and never receives values computed on the GPU.
 
 What is computed: the fused instruction list of the Hazy Research low-latency
-and high-throughput megakernels ("Llama-70B向け低レイテンシ・高スループット
-Megakernelの公開", section 高スループットMegakernelの設計と工夫 / 命令セットの
-再設計: RMS norm, QKV matmul + RoPE, attention, O-proj matmul + residual) and
+and high-throughput megakernels (hakusoku summary "全てのGPUを購入したので、徹底的にそのGPUを活用します。",
+section 高スループットMegakernelの設計と工夫 / 命令セットの再設計: RMS norm,
+QKV matmul + RoPE, attention, O-proj matmul + residual) and
 the SwiGLU feed-forward ("Cómo la fusión de kernels CUDA acelera la inferencia
 de LLM", section "Sigue los datos intermedios"), run for one token at a time
 against a key/value cache; then the final norm, the LM head and greedy argmax.
