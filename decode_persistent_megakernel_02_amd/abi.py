@@ -102,6 +102,7 @@ SIGNATURES = {
     "mk_t_gemv": ([_P, _P, _P, _I32, _I32, _P], _I32),
     "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "mk_t_attention_noalloc": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P], _I32),
     "mk_tile_weights": ([_P, _P, _I64, _I64, _P], _I32),
     "mk_kv_read": ([_P, _P, _P, _I64], _I32),
@@ -344,6 +345,16 @@ def mk_t_attention(q, k, v, T, split, o, stream=None):
     f32 = 1 if k.element_size() == 4 else 0
     _check(lib.mk_t_attention(_ptr(q), _ptr(k), _ptr(v), S * hd, nq, nkv, hd, T, split, f32, _ptr(o),
                               _stream(stream)), "mk_t_attention")
+
+
+def mk_t_attention_noalloc(q, k, v, T, split, o, stream=None):
+    """mk_t_attention without any device allocation (static per-device split
+    records); asynchronous on `stream`."""
+    nq, hd = q.shape
+    nkv, S, _ = k.shape
+    f32 = 1 if k.element_size() == 4 else 0
+    _check(lib.mk_t_attention_noalloc(_ptr(q), _ptr(k), _ptr(v), S * hd, nq, nkv, hd, T, split, f32, _ptr(o),
+                                      _stream(stream)), "mk_t_attention_noalloc")
 
 
 def mk_t_bgemm(W, A, Y, B, tiled=False, stream=None):

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstring>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1292,6 +1293,61 @@ mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t h
   hipError_t e = hipStreamSynchronize(st);
   (void)hipFree(part);
   if (e != hipSuccess) return fail(MK_ERR_HIP, std::string("attention: ") + hipGetErrorString(e));
+  return MK_OK;
+}
+
+// ---- allocation-free split-KV attention ------------------------------------
+// The partial records of mk_t_attention_noalloc live in one file-scope device
+// array.  On the host its name is only a stand-in for the symbol: its device
+// address, which differs per GPU, comes from hipGetSymbolAddress on the first
+// call on each device and is the only way host code refers to the array.
+namespace {
+constexpr int64_t kNoAllocFloats = int64_t(1) << 20;  // 4 MiB of split records per device
+__device__ __align__(256) float scratch[kNoAllocFloats];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+mk_status scratch_for_current_device(float** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MK_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MK_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MK_OK;
+}
+}  // namespace
+
+mk_status mk_t_attention_noalloc(const float* q, const void* k, const void* v, int64_t head_stride, int32_t nq,
+                                 int32_t nkv, int32_t hd, int32_t T, int32_t split, int32_t kv_f32, float* o,
+                                 void* stream) {
+  g_err.clear();
+  if (!q || !k || !v || !o || nq < 1 || nkv < 1 || nq % nkv || nq / nkv > kMaxGqa || (hd != 64 && hd != 128) ||
+      T < 1 || split < 1 || split > kMaxSplit || head_stride < (int64_t)T * hd)
+    return fail(MK_ERR_INVALID_ARG, "bad attention arguments");
+  const int G = nq / nkv, nsplit = (T + split - 1) / split;
+  const int64_t need = (int64_t)nkv * nsplit * G * (hd + 2);
+  if (need > kNoAllocFloats)
+    return fail(MK_ERR_CAPACITY, "split records need " + std::to_string(need) + " floats, more than the " +
+                                     std::to_string(kNoAllocFloats) + " of the static scratch (use a larger split)");
+  float* part = nullptr;
+  MK_TRY(scratch_for_current_device(&part));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned lds = (unsigned)((G * hd + G * kWave) * 4);
+  const int f32 = kv_f32 ? 1 : 0;
+  // every (group, split, head) record is written before the merge reads it,
+  // so nothing left by an earlier call needs clearing
+  hipLaunchKernelGGL(mk_t_attn_partial_kernel, dim3(nkv * nsplit), dim3(kWave), lds, st, q, k, v, head_stride, nq,
+                     nkv, hd, T, split, nsplit, f32, part);
+  hipLaunchKernelGGL(mk_t_attn_merge_kernel, dim3(nkv), dim3(kWave), 0, st, part, nq, nkv, hd, T, split, nsplit, o);
+  HIP_TRY(hipGetLastError());
   return MK_OK;
 }
 

@@ -170,6 +170,19 @@ mk_status mk_t_rmsnorm(const float* x, const void* gamma, float eps, float* y, i
  * o fp32 [nq, hd].  Synchronous (allocates and frees its partial buffer). */
 mk_status mk_t_attention(const float* q, const void* k, const void* v, int64_t head_stride, int32_t nq, int32_t nkv,
                          int32_t hd, int32_t T, int32_t split, int32_t kv_f32, float* o, void* stream);
+/* mk_t_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and result, but the split records live in a static
+ * per-device array of 2^20 floats (4 MiB), held by each GPU the library runs
+ * on until the process ends, and the call is asynchronous on `stream` (no
+ * allocation, no free, no synchronization).  Needs nkv * ceil(T / split) *
+ * (nq / nkv) * (hd + 2) <= 2^20 (MK_ERR_CAPACITY otherwise; use a larger
+ * split).  All calls on one GPU share its array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialised by the
+ * caller.  Arguments and other errors as mk_t_attention. */
+mk_status mk_t_attention_noalloc(const float* q, const void* k, const void* v, int64_t head_stride, int32_t nq,
+                                 int32_t nkv, int32_t hd, int32_t T, int32_t split, int32_t kv_f32, float* o,
+                                 void* stream);
 /* Batched projection body (matrix cores): Y[b][n] = sum_k W[n][k] *
  * (A[0][b][k] + A[1][b][k]) for b < B, n < N; W bf16 [N, K]; A bf16
  * [2][Bp][K], the hi and lo planes of the activations, with Bp = 16, 32 or 64
