@@ -103,6 +103,7 @@ SIGNATURES = {
     "mk_t_rmsnorm": ([_P, _P, _F, _P, _I32, _P], _I32),
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_attention_noalloc": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "mk_t_op_raw": ([_P, _I32, _I32, _P, _P], _I32),
     "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P], _I32),
     "mk_tile_weights": ([_P, _P, _I64, _I64, _P], _I32),
     "mk_kv_read": ([_P, _P, _P, _I64], _I32),
@@ -345,6 +346,12 @@ def mk_t_attention(q, k, v, T, split, o, stream=None):
     f32 = 1 if k.element_size() == 4 else 0
     _check(lib.mk_t_attention(_ptr(q), _ptr(k), _ptr(v), S * hd, nq, nkv, hd, T, split, f32, _ptr(o),
                               _stream(stream)), "mk_t_attention")
+
+
+def mk_t_op_raw(h: Handle, op_type: int, layer: int, x, y):
+    """The shipped GEMV operator kernel of op_type (1 QKV, 4 O, 5 gate/up, 6
+    down, 7 LM head) on the raw input x; y receives its raw dot products."""
+    _check(lib.mk_t_op_raw(h.ptr, op_type, layer, _ptr(x), _ptr(y)), "mk_t_op_raw")
 
 
 def mk_t_attention_noalloc(q, k, v, T, split, o, stream=None):

@@ -515,6 +515,29 @@ mk_status enqueue_ops(mk_handle* h, hipStream_t st, bool timed_ok) {
   return MK_OK;
 }
 
+// One single-sequence GEMV operator launch of `layer`, the shipped kernel and
+// launch configuration, with the given Params (enqueue_ops' GEMV branch).
+mk_status launch_op(mk_handle* h, const Params& Pin, int type, int layer, hipStream_t st) {
+  const auto& g = h->graph;
+  for (size_t s = 0; s + 1 < g.stage_begin.size(); ++s) {
+    const int b0 = g.stage_begin[s], count = g.stage_begin[s + 1] - b0;
+    if (count <= 0 || g.stage_type[s] != type || g.tasks[b0].layer != layer) continue;
+    Params Pc = Pin;
+    const Step* sp = h->d_step;
+    const int min_grid = (count + kWaves * kMaxTasksPerWave / 2 - 1) / (kWaves * kMaxTasksPerWave / 2);
+    const int grid = std::max(min_grid, std::min((count + kWaves - 1) / kWaves, h->op_grid_cap[type]));
+    OpArgs A = op_args(h, type, layer, count);
+    A.merge = 0;
+    int opf = h->op_page[type];
+    int osf = h->op_sf[type];
+    void* args[] = {&Pc, &sp, &A, &opf, &osf};
+    HIP_TRY(hipLaunchKernel(op_kernel(type, h->op_exact[type]), dim3(grid), dim3(kWaves * kWave), args,
+                            (size_t)h->op_lds[type], st));
+    return MK_OK;
+  }
+  return fail(MK_ERR_INVALID_ARG, "no such operator in the task graph");
+}
+
 // Capture one step's operator launches into a graph (once per handle).
 mk_status build_step_graph(mk_handle* h) {
   if (h->graph_exec) return MK_OK;
@@ -1349,6 +1372,21 @@ mk_status mk_t_attention_noalloc(const float* q, const void* k, const void* v, i
   hipLaunchKernelGGL(mk_t_attn_merge_kernel, dim3(nkv), dim3(kWave), 0, st, part, nq, nkv, hd, T, split, nsplit, o);
   HIP_TRY(hipGetLastError());
   return MK_OK;
+}
+
+mk_status mk_t_op_raw(mk_handle* h, int32_t type, int32_t layer, const float* x, float* y) {
+  g_err.clear();
+  if (!h || !x || !y) return fail(MK_ERR_INVALID_ARG, "NULL argument");
+  if (h->batched) return fail(MK_ERR_UNSUPPORTED, "single-sequence operator kernels only (max_batch 1)");
+  if (type != TT_QKV && type != TT_O && type != TT_GU && type != TT_DOWN && type != TT_LM)
+    return fail(MK_ERR_INVALID_ARG, "type must be 1 (QKV), 4 (O), 5 (gate/up), 6 (down) or 7 (LM head)");
+  if (layer < 0 || layer >= h->P.L || (type == TT_LM && layer != 0))
+    return fail(MK_ERR_INVALID_ARG, "layer out of range (the LM head takes layer 0)");
+  Params P = h->P;
+  P.raw_in = x;
+  P.raw_out = y;
+  P.trace_op = -1;
+  return launch_op(h, P, type, type == TT_LM ? h->P.L : layer, h->stream);
 }
 
 mk_status mk_t_bgemm(const void* W, const void* A, float* Y, int32_t N, int32_t K, int32_t B, int32_t tiled,

@@ -358,6 +358,36 @@ __device__ __forceinline__ void epilogue_lane(const Params& P, const Step& S, co
   }
 }
 
+// Debug path of the per-operator kernels: a task's raw dot products, at their
+// rows of the operator's matrix (QKV: [Wq; Wk; Wv], gate/up: [Wgate; Wup]).
+template <int TT>
+__device__ __forceinline__ void raw_lane(const Params& P, const Task& d, const float (&y)[TaskShape<TT>::R]) {
+  constexpr int R = TaskShape<TT>::R;
+  float* o = P.raw_out;
+  if constexpr (TT == TT_QKV) {
+    const int base = d.a0 == 0 ? 0 : d.a0 == 1 ? P.nq * P.hd : (P.nq + P.nkv) * P.hd;
+    if (d.a3) {
+      o[base + d.a1] = y[0];
+      o[base + d.a1 + d.a3] = y[1];
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (r < d.a2) o[base + d.a1 + r] = y[r];
+    }
+  } else if constexpr (TT == TT_GU) {
+#pragma unroll
+    for (int r = 0; r < R / 2; ++r)
+      if (r < d.a2) {
+        o[d.a1 + r] = y[r];
+        o[P.F + d.a1 + r] = y[r + R / 2];
+      }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < d.a2) o[d.a1 + r] = y[r];
+  }
+}
+
 // The epilogues of a wave's n (<= 64) streamed tasks, from their results in
 // res and their task indices in ids: lane j finishes task j.
 template <int TT>
@@ -371,7 +401,8 @@ __device__ __forceinline__ void gemv_finish(const Params& P, const Step& S, cons
     float y[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) y[r] = res[lane * R + r];
-    epilogue_lane<TT>(P, S, d, y, best);
+    if (P.raw_out) raw_lane<TT>(P, d, y);
+    else epilogue_lane<TT>(P, S, d, y, best);
   }
   if constexpr (TT == TT_LM) {
     best = wave_max_u64(best);
@@ -405,9 +436,17 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const O
   constexpr int SU = TT == TT_DOWN ? 4 : 2;  // register-staged groups per lane: vectors up to SU * 4096
   StageSrc src{};
   StageRegs<SU> st;
-  const bool merged = TT == TT_O && A.merge;  // input merged from the attention splits
+  const bool merged = TT == TT_O && A.merge && !P.raw_out;  // input merged from the attention splits
   if (first.stage && !merged) {
-    src = stage_src(P, S, first.stage, first.batch, A.gain);
+    if (P.raw_out) {
+      // debug: the raw input, copied without normalising.  stage_src is not
+      // called here: for layer 0 it reads the step's token, and a raw launch
+      // may come before any step has set one.
+      src = StageSrc{P.raw_in, nullptr, nullptr,
+                     TT == TT_O ? P.nq * P.hd : TT == TT_DOWN ? P.F : P.H};
+    } else {
+      src = stage_src(P, S, first.stage, first.batch, A.gain);
+    }
     stage_issue<SU>(src, wave, lane, st);
   }
   bool staged = false;
@@ -463,7 +502,7 @@ __device__ __forceinline__ void op_body(const Params& P, const Step* Sd, const O
   wait();
   if constexpr (TT == TT_LM) {
     __syncthreads();
-    if (threadIdx.x < P.B)
+    if (threadIdx.x < P.B && !P.raw_out)
       __hip_atomic_fetch_max(&P.lm_part[threadIdx.x], L->lm_best[threadIdx.x], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -245,6 +245,11 @@ struct Params {
   unsigned long long* trace;  // optional per-task timestamps
   int32_t trace_cap;
   int32_t trace_op;           // per-operator kernels: (type << 16) | layer whose waves log timestamps, -1 none
+  // debug (mk_t_op_raw): when raw_out is set, a per-operator GEMV kernel
+  // stages raw_in unnormalised and writes its raw dot products to raw_out
+  // instead of running its epilogues
+  const float* raw_in;
+  float* raw_out;
 };
 
 // Per-launch arguments.

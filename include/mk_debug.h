@@ -159,6 +159,20 @@ mk_status mk_read_op_times(mk_handle* h, double* total_ms, int32_t* launches);
  * launched. */
 mk_status mk_time_op_replay(mk_handle* h, int32_t type, int32_t reps, double* total_ms, int32_t* launches);
 
+/* The shipped single-sequence GEMV operator kernel of `type` (1 QKV, 4 O,
+ * 5 gate/up, 6 down, 7 LM head) for `layer` (0 for the LM head), in the
+ * launch configuration a decode step uses (grid, task split, EXACT or
+ * clamped instance), on explicit buffers: the input x (fp32 device, K = hidden
+ * for QKV, gate/up and the LM head, n_q_heads * head_dim for O, ffn for down)
+ * is staged as it is, without RMSNorm, and the operator's raw dot products go
+ * to y (fp32 device) at their rows of the operator's matrix -- QKV:
+ * [Wq; Wk; Wv] ((n_q + 2 n_kv) head_dim rows), gate/up: [Wgate; Wup]
+ * (2 ffn rows), the others their own row count -- instead of the epilogues
+ * (no RoPE, cache append, residual, SwiGLU or argmax; the handle's sequence
+ * state is untouched).  Asynchronous on the handle's stream.  max_batch 1
+ * handles only (MK_ERR_UNSUPPORTED otherwise). */
+mk_status mk_t_op_raw(mk_handle* h, int32_t type, int32_t layer, const float* x, float* y);
+
 /* ---- single task bodies on explicit buffers (asynchronous on `stream`) ----- */
 /* y[N] = W[N,K] x[K]; W bf16 row-major, x/y fp32; K a multiple of 8. */
 mk_status mk_t_gemv(const void* W, const float* x, float* y, int32_t N, int32_t K, void* stream);

@@ -31,10 +31,8 @@ def abi():
     return a
 
 
-MEGAKERNEL_OFF = ("the persistent megakernel's cooperative launch never completed on the MI355X test box; "
-                  "the mode is refused by mk_create until the cause is found")
 MODES = {"megakernel": 0, "per_op": 1}
-MODE_PARAMS = [pytest.param("megakernel", marks=pytest.mark.skip(reason=MEGAKERNEL_OFF)), "per_op"]
+MODE_PARAMS = ["megakernel", "per_op"]
 PER_OP = 1
 
 
@@ -124,9 +122,11 @@ def test_poison_and_cu_count_are_bit_identical(abi):
         assert np.array_equal(o, outs[0])
 
 
-@pytest.mark.skip(reason=MEGAKERNEL_OFF)
-def test_megakernel_matches_per_op_bitwise(abi):
-    """Both modes run the same bodies with the same per-task reduction order."""
+def test_megakernel_matches_per_op(abi):
+    """Both modes run the same GEMV bodies; they differ in the order of fp32
+    sums only where the megakernel restructures a step (RMSNorm's 1/rms
+    applied to the projection outputs, the attention split merge spread over
+    four waves), so the logits agree to rounding: 1e-5 relative."""
     shape = MINI_G8
     prompt = gen.tokens(4, 3, 0, 9, shape.vocab)
     w = gen.gen_weights(shape, 2, True)
@@ -134,7 +134,8 @@ def test_megakernel_matches_per_op_bitwise(abi):
     for mode in (0, 1):
         case = Case(shape, 16, mode, attn_split=4, weights=w)
         outs.append(np.stack([case.prefill(prompt)[0]] + [case.step(t)[0] for t in (3, 77, 200)]))
-    assert np.array_equal(outs[0], outs[1])
+    err = np.abs(outs[0] - outs[1]).max() / np.abs(outs[1]).max()
+    assert err <= 1e-5, err
 
 
 def test_intermediates_match_oracle_per_layer(abi):
@@ -148,9 +149,9 @@ def test_intermediates_match_oracle_per_layer(abi):
         for name, key in (("q", "q"), ("attn", "attn"), ("xmid", "xmid"), ("h", "h")):
             ref = trace[(key, l)][0]
             err = np.abs(got[name][l] - ref).max() / np.abs(ref).max()
-            assert err < 1e-2, (name, l, err)
+            assert err < 1e-4, (name, l, err)
         ref = trace[("x", l + 1)][0]
-        assert np.abs(got["xs"][l + 1] - ref).max() / np.abs(ref).max() < 1e-2
+        assert np.abs(got["xs"][l + 1] - ref).max() / np.abs(ref).max() < 1e-4
 
 
 def test_reset_reproduces_and_capacity_is_enforced(abi):

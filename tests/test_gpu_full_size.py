@@ -119,3 +119,56 @@ def test_batched_workload_long_cache_full_depth():
     for b in range(B):
         if D.top2_margin(ref[b]) > 5e-2:
             assert got_tok[b] == int(D.greedy(ref[b]))
+
+
+_W8X2 = {}
+
+
+def _weights_8b_two_layers(shape):
+    if "w" not in _W8X2:
+        _W8X2["w"] = gen.gen_weights(shape, 1002)
+    return _W8X2["w"]
+
+
+@pytest.mark.parametrize("mode", ["megakernel", "per_op"])
+def test_8b_shape_two_layers_multi_split_attention(mode):
+    """The 8B production attention instance (fp32 cache, 4 query heads per KV
+    head, head_dim 128) with several splits live: two layers of the 8B shape,
+    a 140-token seeded prompt and 3 seeded decode steps (context up to 143:
+    3 live splits at the per-operator default of 64 positions, 5 at the
+    megakernel's 32), each mode with the library's default split and every
+    CU.  Logits at the last prompt position and every decode step against the
+    oracle's cache-free forward at 5e-3."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_persistent_megakernel_02_amd import abi, runtime
+    shape = presets.with_layers(presets.LLAMA8B, 2)
+    P, n_dec = 140, 3
+    seq = gen.tokens(2024, presets.TID_PROMPT, 0, P + n_dec, shape.vocab).astype(np.int32)
+    print(f"[8b x2 {mode}] generating weights", flush=True)
+    w = _weights_8b_two_layers(shape)
+    dw = runtime.upload_weights(w)
+    m = abi.MK_MODE_MEGAKERNEL if mode == "megakernel" else abi.MK_MODE_PER_OP
+    h = runtime.create(shape, dw, P + n_dec + 1, mode=m, kv_fp32=True)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
+    got = []
+    abi.mk_prefill(h, torch.from_numpy(seq[:P].reshape(1, -1)).cuda(), out, lg)
+    abi.mk_synchronize(h)
+    got.append(lg.cpu().numpy()[0])
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for t in seq[P:]:
+        tok.fill_(int(t))
+        abi.mk_decode_step(h, tok, out, lg)
+        abi.mk_synchronize(h)
+        got.append(lg.cpu().numpy()[0])
+    split = abi.mk_get_debug_view(h).split
+    abi.mk_destroy(h)
+    del dw
+    live = (P + n_dec + split - 1) // split
+    print(f"[8b x2 {mode}] split {split}: {live} splits live at the last step; oracle forward", flush=True)
+    assert live >= 3
+    ref = D.forward_full(shape, w, seq[None, :P + n_dec], positions=range(P - 1, P + n_dec))[0]
+    errs = rel_err(np.stack(got), ref)
+    print(f"[8b x2 {mode}] max rel err {errs.max():.3e}", flush=True)
+    assert np.all(errs <= 5e-3)

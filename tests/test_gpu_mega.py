@@ -168,3 +168,46 @@ def test_watchdog_ends_a_step_with_timeout(abi):
     ok = Case(shape, 16, MEGA, weights=w, watchdog_ms=WATCHDOG_MS)
     g, r, _ = ok.prefill(gen.tokens(2, 3, 0, 3, shape.vocab))
     assert rel_err(g, r) <= TIGHT
+
+
+def test_intermediates_match_oracle_per_layer(abi):
+    """The megakernel's hand-over buffers after one step, layer by layer,
+    against the oracle's values: rotated q, k and v of the step's position,
+    the attention output, the residual after attention, the SwiGLU output and
+    the residual after each layer.  Every word read carries the step's epoch.
+    fp32 arithmetic with an fp32 cache against fp64: 1e-4 relative."""
+    from tests.gpu_util import d2h
+    shape = MINI
+    case = Case(shape, 24, MEGA, seed=8, random_norms=True, attn_split=4, watchdog_ms=WATCHDOG_MS)
+    case.prefill(gen.tokens(1, 3, 0, 6, shape.vocab))
+    p = case.oracle.length
+    trace = {}
+    case.step(17, trace)
+    v = abi.mk_get_mega_view(case.h)
+    L, H, F = shape.n_layers, shape.hidden, shape.ffn
+    nq, nkv, hd = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+
+    def grab(ptr, n, skip=0):
+        a = np.empty(n, dtype=np.uint64)
+        d2h(a.ctypes.data, ptr, n * 8)
+        assert np.all((a[skip:] >> np.uint64(32)) == v.epoch), "a word without the step's epoch"
+        return (a & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32).astype(np.float64)
+
+    x = grab(v.x, (L + 1) * H, skip=H).reshape(L + 1, H)  # row 0: the embedding row is never handed over
+    xmid = grab(v.xmid, L * H).reshape(L, H)
+    qkv = grab(v.qkv, L * (nq + 2 * nkv) * hd).reshape(L, -1)
+    attn = grab(v.attn, L * nq * hd).reshape(L, nq * hd)
+    hh = grab(v.h, L * F).reshape(L, F)
+
+    def close(got, ref, what):
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        assert err < 1e-4, (what, err)
+
+    for l in range(L):
+        close(qkv[l, :nq * hd], trace[("q", l)][0], f"q{l}")
+        close(qkv[l, nq * hd:(nq + nkv) * hd], case.oracle.K[l, 0, :, p].reshape(-1), f"k{l}")
+        close(qkv[l, (nq + nkv) * hd:], case.oracle.V[l, 0, :, p].reshape(-1), f"v{l}")
+        close(attn[l], trace[("attn", l)][0], f"attn{l}")
+        close(xmid[l], trace[("xmid", l)][0], f"xmid{l}")
+        close(hh[l], trace[("h", l)][0], f"h{l}")
+        close(x[l + 1], trace[("x", l + 1)][0], f"x{l + 1}")
