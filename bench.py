@@ -57,11 +57,11 @@ def step_bytes(shape, T, batch=1, kv_bytes=4):
 
 def kernel_source_hash():
     """Hash of the sources the batch-1 operator kernels are compiled from
-    (kernels.hip, device.h, mk_internal.h): a counter summary taken on other
+    (kernels.hip, mega.hip, device.h, mk_internal.h): a counter summary taken on other
     kernel sources is not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_persistent_megakernel_02_amd", "csrc")
-    for f in ("device.h", "kernels.hip", "mk_internal.h"):
+    for f in ("device.h", "kernels.hip", "mega.hip", "mk_internal.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -485,6 +485,7 @@ def per_op_baseline(abi, runtime, shape, dw, prompt_t, steps, warmup, max_seq, B
     kern_ms = rep_ms / (reps * shape.n_layers)  # one layer's gate/up operator
     kb = gu_bytes(shape, B)
     gu_gbps = kb / (kern_ms * 1e-3) / 1e9
+    unit = "ms/token" if B == 1 else "ms/step"
     log(f"per-op: {op_ms:.4f} {unit} (median of 5), gate/up kernel {kern_ms * 1e3:.1f} us = {gu_gbps:.0f} GB/s")
     op_breakdown = {k: {"ms_per_step": v[0] / 32.0, "launches_per_step": v[1] / 32.0} for k, v in breakdown.items()}
     per_layer = rep_launches // (reps * shape.n_layers)  # 2 when a split-K finishing launch follows
