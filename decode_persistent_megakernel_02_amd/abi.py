@@ -104,6 +104,7 @@ SIGNATURES = {
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_attention_noalloc": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_op_raw": ([_P, _I32, _I32, _P, _P], _I32),
+    "mk_generate": ([_P, _P, _I32, _P, _P], _I32),
     "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P], _I32),
     "mk_tile_weights": ([_P, _P, _I64, _I64, _P], _I32),
     "mk_kv_read": ([_P, _P, _P, _I64], _I32),
@@ -202,6 +203,13 @@ def mk_prefill(h: Handle, tokens, next_out, logits=None):
 
 def mk_decode_step(h: Handle, d_in, d_out, logits=None):
     _check(lib.mk_decode_step(h.ptr, _ptr(d_in), _ptr(d_out), _ptr(logits)), "mk_decode_step")
+
+
+def mk_generate(h: Handle, d_in, n_steps: int, d_out, logits=None):
+    """n_steps greedy steps from d_in[0]; ids into d_out[:n_steps] (one launch
+    in megakernel mode)."""
+    _check(lib.mk_generate(h.ptr, _ptr(d_in), n_steps, _ptr(d_out), _ptr(logits) if logits is not None else None),
+           "mk_generate")
 
 
 def mk_synchronize(h: Handle):

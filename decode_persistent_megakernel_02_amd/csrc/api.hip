@@ -575,7 +575,7 @@ mk_status launch_step(mk_handle* h, const Step& S) {
     int pf = h->page_floats;
     void* args[] = {&Pc, &Mc, &Sc, &pf};
     HIP_TRY(hipLaunchKernel(h->mega_fn, dim3(P.ncu), dim3(kMegaWaves * kWave), args, (size_t)h->lds_mega, h->stream));
-    ++h->pending;
+    h->pending += S.nsteps > 0 ? S.nsteps : 1;
     return MK_OK;
   }
   hipLaunchKernelGGL(mk_set_step, dim3(1), dim3(64), 0, h->stream, h->d_step, S);
@@ -782,7 +782,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     const int64_t qkvw = (int64_t)(nq + 2 * nkv) * hd;
     const int64_t n_x = (int64_t)(L + 1) * H, n_xmid = (int64_t)L * H, n_qkv = (int64_t)L * qkvw;
     const int64_t n_rec = (int64_t)L * nkv * g.nsplit * G * (hd + 2), n_attn = (int64_t)L * nq * hd;
-    const int64_t n_h = (int64_t)L * F, total = n_x + n_xmid + n_qkv + n_rec + n_attn + n_h + ncu;
+    const int64_t n_h = (int64_t)L * F, total = n_x + n_xmid + n_qkv + n_rec + n_attn + n_h + ncu + 1;
     uint64_t* t = nullptr;
     MK_TRY(h->alloc(&t, total));
     HIP_TRY(hipMemset(t, 0, total * 8));
@@ -794,6 +794,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     M.attn = M.rec + n_rec;
     M.h = M.attn + n_attn;
     M.key = M.h + n_h;
+    M.tok = M.key + ncu;
     HIP_TRY(hipHostMalloc(&h->host_abort, 64, hipHostMallocMapped | hipHostMallocCoherent));
     *h->host_abort = 0;
     HIP_TRY(hipHostGetDevicePointer(reinterpret_cast<void**>(&M.host_abort), h->host_abort, 0));
@@ -878,8 +879,48 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* d_in, int32_t* d_out, floa
   S.tok_stride = 1;
   S.out = d_out;
   S.logits = d_logits;
+  S.nsteps = 1;
   MK_TRY(launch_step(h, S));
   h->length++;
+  return MK_OK;
+}
+
+mk_status mk_generate(mk_handle* h, const int32_t* d_in, int32_t n, int32_t* d_out, float* d_logits) {
+  g_err.clear();
+  if (!h || !d_in || !d_out) return fail(MK_ERR_INVALID_ARG, "NULL handle or token pointer");
+  if (n < 1) return fail(MK_ERR_INVALID_ARG, "n_steps must be >= 1");
+  if (h->cfg.max_batch != 1) return fail(MK_ERR_UNSUPPORTED, "mk_generate runs one sequence (max_batch 1)");
+  if (h->poisoned) return fail(MK_ERR_STATE, "handle poisoned by an earlier in-kernel error");
+  if ((int64_t)h->length + n > h->cfg.max_seq) return fail(MK_ERR_CAPACITY, "n_steps past the KV-cache capacity");
+  if (h->batch == 0) h->batch = 1;
+  if (h->cfg.mode == MK_MODE_MEGAKERNEL) {  // one launch for all n steps
+    Step S{};
+    S.epoch = h->epoch + 1;
+    S.pos = h->length;
+    S.tokens = d_in;
+    S.tok_stride = 1;
+    S.out = d_out;
+    S.logits = d_logits;
+    S.nsteps = n;
+    S.tok_step = 0;  // step i > 0 takes step i - 1's greedy id
+    S.out_step = 1;
+    MK_TRY(launch_step(h, S));
+    h->epoch += (uint32_t)n;
+    h->length += n;
+    return MK_OK;
+  }
+  for (int i = 0; i < n; ++i) {  // per operator: one step graph per step, ids fed back on the device
+    Step S{};
+    S.epoch = ++h->epoch;
+    S.pos = h->length;
+    S.tokens = i == 0 ? d_in : d_out + i - 1;
+    S.tok_stride = 1;
+    S.out = d_out + i;
+    S.logits = i == n - 1 ? d_logits : nullptr;
+    S.nsteps = 1;
+    MK_TRY(launch_step(h, S));
+    h->length++;
+  }
   return MK_OK;
 }
 
@@ -893,6 +934,22 @@ mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P
   if (B != h->cfg.max_batch) return fail(MK_ERR_UNSUPPORTED, "batch must equal max_batch");
   if (P > h->cfg.max_seq) return fail(MK_ERR_CAPACITY, "prompt longer than max_seq");
   h->batch = B;
+  if (h->cfg.mode == MK_MODE_MEGAKERNEL) {  // B == 1: the whole prompt in one launch
+    Step S{};
+    S.epoch = h->epoch + 1;
+    S.pos = 0;
+    S.tokens = d_tokens;
+    S.tok_stride = P;
+    S.out = d_next;  // every step writes it; the last step's id stays
+    S.logits = d_logits;
+    S.nsteps = P;
+    S.tok_step = 1;
+    S.out_step = 0;
+    MK_TRY(launch_step(h, S));
+    h->epoch += (uint32_t)P;
+    h->length = P;
+    return MK_OK;
+  }
   for (int p = 0; p < P; ++p) {
     Step S{};
     S.epoch = ++h->epoch;
@@ -902,6 +959,7 @@ mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P
     const bool last = p == P - 1;
     S.out = last ? d_next : h->d_tok_scratch;
     S.logits = last ? d_logits : nullptr;
+    S.nsteps = 1;
     MK_TRY(launch_step(h, S));
     h->length++;
   }

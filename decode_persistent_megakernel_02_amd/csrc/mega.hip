@@ -370,11 +370,11 @@ __device__ __forceinline__ void compute_op(const Params& P, const MegaBufs& M, c
 template <bool EXACT>
 __device__ __forceinline__ void compute_wave(const Params& P, const MegaBufs& M, const Step& S, MegaLds* L,
                                              float* pages, int pf, const float* resid, const float* rope, float* res,
-                                             int* ids, int c, int lane) {
+                                             int* ids, int c, int lane, WBuf (&B)[NB], int (&t)[NB], bool more) {
+  // on entry the first tasks of operator 0 are in flight (B, t); with `more`
+  // (another step follows in this launch) the next step's are put in flight
+  // after the LM head
   const int nops = 4 * P.L + 1;
-  WBuf B[NB];
-  int t[NB];
-  fetch_first<EXACT>(P, 0, c, B, t, lane);
   for (int k = 0; k < nops; ++k) {
     if (!wait_lds(P, M, L, &L->ready[k & 1], (uint32_t)NS * (uint32_t)(k / 2 + 1), NS + c,
                   ((uint32_t)k << 8) | W_READY, lane))
@@ -392,6 +392,7 @@ __device__ __forceinline__ void compute_wave(const Params& P, const MegaBufs& M,
     // reported done: the stagers then poll the next input behind the burst
     // of weight loads rather than competing with it
     if (k + 1 < nops) fetch_first<EXACT>(P, k + 1, c, B, t, lane);
+    else if (more) fetch_first<EXACT>(P, 0, c, B, t, lane);
     if (M.trace && lane == 0) {
       const uint64_t t1 = clock_now();
       M.trace[((size_t)k * gridDim.x + blockIdx.x) * kTraceSlots + c] = ((t1 - t0) << 32) | (uint32_t)t1;
@@ -493,8 +494,28 @@ struct Stager {
   // The bf16 embedding row of the step's token (read-only data, plain loads)
   // as an RMSNorm input: page = gain * x, raw x into resid, sum of x^2 into
   // L->red[s].
-  __device__ __forceinline__ void load_embed(float* dst, const float* gain, float* resid) {
-    const uint16_t* row = P.embed + (int64_t)token_of(P, S, 0) * P.H;
+  // The step's token: from the caller's array, or (a later step of a
+  // multi-step launch, S.tokens null) the previous step's greedy id, a tagged
+  // word written by workgroup 0's argmax.
+  __device__ __forceinline__ bool step_token(int* tok) {
+    if (S.tokens) {
+      *tok = token_of(P, S, 0);
+      return true;
+    }
+    const uint64_t need = (uint64_t)(S.epoch - 1) << 32;
+    uint64_t w = tget(M.tok);
+    Spin sp;
+    while ((w >> 32) != (need >> 32)) {
+      if (!sp.tick<kPollSleep>(P, M, L, s, ((uint32_t)k << 8) | W_KEY, 0u, 1u, lane)) return false;
+      w = tget(M.tok);
+    }
+    const int t = (int)(uint32_t)w;
+    *tok = t >= 0 && t < P.V ? t : 0;
+    return true;
+  }
+
+  __device__ __forceinline__ void load_embed(float* dst, const float* gain, float* resid, int tok) {
+    const uint16_t* row = P.embed + (int64_t)tok * P.H;
     float ss = 0.f;
     for (int i = (s * kWave + lane); i < P.H; i += NS * kWave) {
       const float v = bf1(row[i]);
@@ -828,6 +849,8 @@ __device__ __forceinline__ bool argmax_unit(Stager& st) {
     const uint32_t idx = 0x1FFFFu - (uint32_t)(best & 0x1FFFFu);
     const unsigned long long k = ((best >> 17) << 32) | (0xFFFFFFFFu - idx);
     st.S.out[0] = (int32_t)idx;
+    // the next step of the same launch starts from this id
+    __hip_atomic_store(M.tok, ((uint64_t)st.S.epoch << 32) | idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!(fabsf(argmax_key_value(k)) <= 3.0e38f)) atomicCAS(&P.status[1], ST_OK, ST_NONFINITE);
   }
   return true;
@@ -855,7 +878,11 @@ __device__ __forceinline__ void stager_wave(const Params& P, const MegaBufs& M, 
     st.k = k;
     if (l == 0) st.load_gain(ld_const(P.attn_norm), P.H, gain);  // later layers: loaded during the previous DOWN
     if (!st.wait_done(k, free_for(k))) return;
-    if (l == 0) st.load_embed(page0, gain, resid);
+    if (l == 0) {
+      int tok = 0;
+      if (!st.step_token(&tok)) return;
+      st.load_embed(page0, gain, resid, tok);
+    }
     else if (!st.wait_done(k - 1, done_after(k - 1)) ||
              !st.load_tagged<true>(M.x + (size_t)l * P.H, P.H, page0, gain, resid))
       return;
@@ -924,31 +951,61 @@ __device__ __forceinline__ void mega_body(const Params& P, const MegaBufs& M, co
   float* qs = res + NC * rs;                     // attention unit: the group's queries [GQ][HD]
   float* recs = qs + GQ * HD;                    // attention unit: the waves' states [NS][GQ][HD + 2]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) {
-    L->ready[0] = L->ready[1] = 0;
-    L->done[0] = L->done[1] = 0;
-    L->pool[0] = L->pool[1] = 0;
-    L->ssync = 0;
-    L->lm_done = 0;
-    L->lm_best = 0;
-    L->abort = __hip_atomic_load(&P.status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 1u : 0u;
-  }
-  __syncthreads();  // the only workgroup barrier
-  if (L->abort) return;
+  const int nst = S.nsteps > 0 ? S.nsteps : 1;
+  // Step i of the launch; the LDS counters start again from zero at every
+  // step (wave 0 resets them after the barrier that ends the previous step).
+  auto begin_step = [&](int i, Step& Si) __attribute__((always_inline)) -> bool {
+    if (threadIdx.x == 0) {
+      L->ready[0] = L->ready[1] = 0;
+      L->done[0] = L->done[1] = 0;
+      L->pool[0] = L->pool[1] = 0;
+      L->ssync = 0;
+      L->lm_done = 0;
+      L->lm_best = 0;
+      if (i == 0) L->abort = __hip_atomic_load(&P.status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (L->abort) return false;  // the same decision in every wave of the workgroup
+    Si = S;
+    Si.epoch = S.epoch + (uint32_t)i;
+    Si.pos = S.pos + i;
+    Si.tokens = S.tok_step ? S.tokens + (int64_t)i * S.tok_step : (i == 0 ? S.tokens : nullptr);
+    Si.out = S.out + (int64_t)i * S.out_step;
+    Si.logits = i + 1 == nst ? S.logits : nullptr;
+    return true;
+  };
+  // The two roles run the same sequence of workgroup barriers (two per step)
+  // in separate loops, so that neither role's registers are live in the
+  // other's code.  A wave that stopped early (abort) still reaches the
+  // step's closing barrier: every wait sees the abort word, so the whole
+  // workgroup arrives.
   if (wave < NS) {
-    stager_wave<HD, KT, GQ>(P, M, S, L, pages, pf, resid, gain, rope, qs, recs, wave, lane);
+    for (int i = 0; i < nst; ++i) {
+      Step Si;
+      if (!begin_step(i, Si)) return;
+      stager_wave<HD, KT, GQ>(P, M, Si, L, pages, pf, resid, gain, rope, qs, recs, wave, lane);
+      __syncthreads();
+    }
   } else {
     const int c = wave - NS;
     float* r = res + c * rs;
-    compute_wave<EXACT>(P, M, S, L, pages, pf, resid, rope, r, reinterpret_cast<int*>(r + kMegaMaxTasks * kR), c,
-                        lane);
+    WBuf B[NB];  // the next operator's first tasks, in flight across operators and steps
+    int t[NB];
+    fetch_first<EXACT>(P, 0, c, B, t, lane);
+    for (int i = 0; i < nst; ++i) {
+      Step Si;
+      if (!begin_step(i, Si)) return;
+      compute_wave<EXACT>(P, M, Si, L, pages, pf, resid, rope, r, reinterpret_cast<int*>(r + kMegaMaxTasks * kR), c,
+                          lane, B, t, i + 1 < nst);
+      __syncthreads();
+    }
   }
 }
 
 }  // namespace
 
-// One decode step of one sequence, per (EXACT, head_dim, cache element type,
-// query heads per KV head).  EXACT: every GEMV operator's K is a multiple of
+// S.nsteps decode steps of one sequence, per (EXACT, head_dim, cache element
+// type, query heads per KV head).  EXACT: every GEMV operator's K is a multiple of
 // 512 with a chunk count that is a multiple of the in-flight depth (no
 // clamped loads).  The host picks the instance (mega_kernel).
 #define MK_MEGA(X, HD, KN, KT, G)                                                                          \

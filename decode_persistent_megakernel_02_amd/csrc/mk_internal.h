@@ -260,6 +260,11 @@ struct Step {
   int32_t tok_stride;
   int32_t* out;      // [B] greedy ids
   float* logits;     // [B][V] or null
+  // megakernel only: steps run by this launch (epochs epoch + i, positions
+  // pos + i); step i reads its token at tokens + i * tok_step, or, with
+  // tok_step 0 and i > 0, takes the previous step's greedy id; it writes its
+  // id to out + i * out_step; the logits are the last step's
+  int32_t nsteps, tok_step, out_step;
 };
 
 // LDS header of the persistent and per-operator kernels (followed by the
@@ -289,6 +294,7 @@ struct MegaBufs {
   uint64_t* attn;    // [L][nq hd] merged attention output
   uint64_t* h;       // [L][F] SwiGLU output
   uint64_t* key;     // [ncu] each workgroup's LM-head argmax key (epoch mod 2^15 in the low bits)
+  uint64_t* tok;     // [1] the greedy id of the last step, tagged (epoch << 32 | id): the next step's input
   uint32_t* host_abort;          // host-mapped word: nonzero makes every wait give up
   unsigned long long* trace;     // optional [ops][ncu][kMegaTraceSlots] timestamps, null if off
 };

@@ -181,7 +181,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* weights, void* hip_s
  * equal max_batch: a handle is built for one batch size (task split, MFMA
  * tiles, cache layout), so a smaller batch uses a handle created for it
  * (B outside [1, max_batch]: MK_ERR_CAPACITY; 1 <= B < max_batch:
- * MK_ERR_UNSUPPORTED).  P must not exceed max_seq (MK_ERR_CAPACITY). */
+ * MK_ERR_UNSUPPORTED).  P must not exceed max_seq (MK_ERR_CAPACITY).  In
+ * MK_MODE_MEGAKERNEL the P positions run in one launch. */
 mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P,
                      int32_t* d_next, float* d_logits);
 
@@ -195,6 +196,19 @@ mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P
  * sequences.  MK_ERR_CAPACITY if length == max_seq, MK_ERR_STATE on a
  * poisoned handle (nothing enqueued in either case). */
 mk_status mk_decode_step(mk_handle* h, const int32_t* d_in, int32_t* d_out, float* d_logits);
+
+/* n_steps greedy decode steps of one sequence (max_batch 1) from token id
+ * d_in[0] at position `length`: step i's greedy id goes to d_out[i] (int32
+ * [n_steps], device) and is the input of step i + 1; if d_logits is not NULL
+ * the last step's logits go there (fp32 [vocab]).  In MK_MODE_MEGAKERNEL the
+ * n_steps steps run in ONE launch ("Compilar LLM en un MegaKernel ...",
+ * section "Panorama general y ventajas": the whole inference in a single
+ * kernel, no launch per step): the argmax of step i reaches every workgroup
+ * as a tagged word that step i + 1's embedding lookup waits for.  Per
+ * operator, each step is one graph launch with the id fed back on the
+ * device.  length += n_steps.  MK_ERR_CAPACITY if length + n_steps >
+ * max_seq, MK_ERR_UNSUPPORTED for max_batch > 1 (nothing enqueued). */
+mk_status mk_generate(mk_handle* h, const int32_t* d_in, int32_t n_steps, int32_t* d_out, float* d_logits);
 
 /* Wait for the stream; returns MK_ERR_TIMEOUT (and poisons the handle) if an
  * in-kernel watchdog fired during any earlier step.  In megakernel mode a host

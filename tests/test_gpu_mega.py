@@ -211,3 +211,73 @@ def test_intermediates_match_oracle_per_layer(abi):
         close(xmid[l], trace[("xmid", l)][0], f"xmid{l}")
         close(hh[l], trace[("h", l)][0], f"h{l}")
         close(x[l + 1], trace[("x", l + 1)][0], f"x{l + 1}")
+
+
+def test_generate_in_one_launch(abi):
+    """mk_generate: 24 greedy steps in ONE megakernel launch, each step's
+    argmax feeding the next step's embedding inside the kernel.  The same
+    steps launched one at a time (ids fed back on the device) give the same
+    ids and the same last logits bit for bit (the same arithmetic per step);
+    the ids follow the oracle's greedy generation wherever its top-2 margin
+    exceeds 5e-2; a request past the cache capacity is refused."""
+    from decode_persistent_megakernel_02_amd import runtime
+    shape, n = MINI_G8, 24
+    w = gen.gen_weights(shape, 3, True)
+    prompt = gen.tokens(43, 3, 0, 7, shape.vocab)  # the oracle's first 19 margins exceed 5e-2
+    p_t = torch.from_numpy(prompt.reshape(1, -1)).cuda()
+    dw = runtime.upload_weights(w)
+    runs = []
+    for one_launch in (True, False):
+        h = runtime.create(shape, dw, 40, mode=MEGA, watchdog_ms=WATCHDOG_MS)
+        toks = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+        lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
+        abi.mk_prefill(h, p_t, toks[0:1])
+        if one_launch:
+            abi.mk_generate(h, toks[0:1], n, toks[1:], lg)
+        else:
+            for s in range(n):
+                abi.mk_decode_step(h, toks[s:s + 1], toks[s + 1:s + 2], lg if s == n - 1 else None)
+        abi.mk_synchronize(h)
+        runs.append((toks.cpu().numpy(), lg.cpu().numpy()[0]))
+        if one_launch:
+            with pytest.raises(abi.MkError) as e:  # 7 + 24 positions used of 40
+                abi.mk_generate(h, toks[0:1], 10, toks[1:11])
+            assert e.value.status == abi.MK_ERR_CAPACITY
+    assert np.array_equal(runs[0][0], runs[1][0])
+    assert np.array_equal(runs[0][1], runs[1][1])
+    gpu = runs[0][0]
+    ref_tokens, ref_logits = D.Decoder(shape, w, 1, 40).generate(prompt.reshape(1, -1), n)
+    last = D.Decoder(shape, w, 1, 40).prefill(prompt.reshape(1, -1))[0]
+    margins = [D.top2_margin(last)] + [D.top2_margin(ref_logits[0, s]) for s in range(n)]
+    ref_seq = [int(D.greedy(last))] + list(ref_tokens[0])
+    checked = 0
+    for s in range(n + 1):
+        if margins[s] <= MARGIN:
+            break
+        assert gpu[s] == ref_seq[s], f"step {s}"
+        checked += 1
+    print(f"one-launch generation: {checked} leading ids checked against the oracle")
+    assert checked >= 8
+
+
+def test_generate_per_operator_matches_oracle(abi):
+    from decode_persistent_megakernel_02_amd import runtime
+    wl = presets.WORKLOADS["tiny"]
+    shape = wl.shape
+    w = gen.gen_weights(shape, 0)
+    dw = runtime.upload_weights(w)
+    h = runtime.create(shape, dw, wl.max_seq, mode=PER_OP)
+    prompt = gen.gen_prompt(wl)
+    toks = torch.zeros(wl.decode_steps + 1, dtype=torch.int32, device="cuda")
+    abi.mk_prefill(h, torch.from_numpy(prompt).cuda(), toks[0:1])
+    abi.mk_generate(h, toks[0:1], wl.decode_steps, toks[1:])
+    abi.mk_synchronize(h)
+    gpu = toks.cpu().numpy()
+    ref_tokens, ref_logits = D.Decoder(shape, w, 1, wl.max_seq).generate(prompt, wl.decode_steps)
+    last = D.Decoder(shape, w, 1, wl.max_seq).prefill(prompt)[0]
+    margins = [D.top2_margin(last)] + [D.top2_margin(ref_logits[0, s]) for s in range(wl.decode_steps)]
+    ref_seq = [int(D.greedy(last))] + list(ref_tokens[0])
+    for s in range(wl.decode_steps + 1):
+        if margins[s] <= MARGIN:
+            break
+        assert gpu[s] == ref_seq[s], f"step {s}"
