@@ -128,6 +128,30 @@ def protocol(abi, h, prompt_t, steps, warmup, torch, runs=5, log=lambda *a: None
     return totals[len(totals) // 2] / steps, totals, per, tokens
 
 
+def one_launch(abi, h, prompt_t, steps, torch, log=lambda *a: None, runs=5):
+    """Megakernel: reset + prefill, then all `steps` decode steps in ONE launch
+    (mk_generate) between two events; median of `runs`.  Returns (median
+    ms/step, run totals, tokens [steps + 1, 1])."""
+    toks = torch.zeros(steps + 1, 1, dtype=torch.int32, device="cuda")
+    totals = []
+    for r in range(runs):
+        abi.mk_reset(h)
+        abi.mk_prefill(h, prompt_t, toks[0])
+        abi.mk_synchronize(h)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        abi.mk_generate(h, toks[0], steps, toks[1:].view(-1))
+        t1.record()
+        torch.cuda.synchronize()
+        abi.mk_synchronize(h)
+        totals.append(t0.elapsed_time(t1))
+        log(f"megakernel one-launch run {r + 1}/{runs}: {totals[-1] / steps:.4f} ms/step")
+    srt = sorted(totals)
+    return srt[len(srt) // 2] / steps, totals, toks.cpu().numpy()
+
+
 def pct(xs, q):
     import numpy as np
     return float(np.percentile(np.asarray(xs), q))
@@ -368,10 +392,15 @@ def main():
         mega_ms, mega_runs, mega_per, mega_tokens = protocol(abi, h, prompt_t, steps, warmup, torch, log=log,
                                                              name="megakernel")
         split = abi.mk_get_debug_view(h).split
+        one_ms, one_runs, one_tokens = one_launch(abi, h, prompt_t, steps, torch, log)
         abi.mk_destroy(h)
         mega = {"ms_per_token": mega_ms, "runs_ms_per_token": [t / steps for t in mega_runs],
                 "step_p50_ms": pct(mega_per, 50), "step_p99_ms": pct(mega_per, 99),
-                "attn_split": split, "kernel": mega_kernel_name(shape)}
+                "attn_split": split, "kernel": mega_kernel_name(shape),
+                "one_launch": {"ms_per_token": one_ms, "runs_ms_per_token": [t / steps for t in one_runs],
+                               "tokens_equal_per_step_launches": bool((one_tokens == mega_tokens).all()),
+                               "timing": f"mk_generate: all {steps} steps in one launch, median of 5 runs "
+                                         "between two HIP events"}}
         log(f"megakernel: {mega_ms:.4f} ms/token (median of 5), p50 {mega['step_p50_ms']:.4f}, "
             f"p99 {mega['step_p99_ms']:.4f} ms; bound {bound_ms:.4f} ms")
         if not args.no_trace:
