@@ -11,6 +11,9 @@ result is in bytes that moved, whatever the counter's own unit convention.
 
 Each DIR is a rocprofv3 output directory holding run_counter_collection.csv.
 Prints a per-kernel table (markdown) of every kernel in the --fetch run.
+--last N keeps only the kernel's last N dispatches for --out: a megakernel
+counter run starts with one launch that runs the whole prefill (one step
+per prompt position), then launches one decode step each.
 """
 import argparse
 import csv
@@ -21,13 +24,13 @@ from collections import defaultdict
 
 
 def per_kernel(run_dir, counter):
-    """{kernel name: [counter value (KiB) per dispatch]} of one rocprofv3 run."""
-    vals = defaultdict(list)
+    """{kernel name: [counter value (KiB) per dispatch, in dispatch order]} of one rocprofv3 run."""
+    rows = defaultdict(list)
     with open(os.path.join(run_dir, "run_counter_collection.csv")) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter:
-                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-    return vals
+                rows[r["Kernel_Name"]].append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return {k: [v for _, v in sorted(xs)] for k, xs in rows.items()}
 
 
 def copy_scale(run_dir, counter, nbytes):
@@ -51,6 +54,8 @@ def main():
     ap.add_argument("--workload", required=True)
     ap.add_argument("--source-hash", required=True)
     ap.add_argument("--out")
+    ap.add_argument("--last", type=int, default=0, metavar="N",
+                    help="--out: average only the kernel's last N dispatches")
     a = ap.parse_args()
     n = a.copy_mib << 20
     fs = copy_scale(a.copy_fetch, "FETCH_SIZE", n)
@@ -68,13 +73,16 @@ def main():
     if a.out:
         if a.kernel not in fetch or a.kernel not in write:
             raise SystemExit(f"kernel {a.kernel} missing from the counter runs")
-        f = statistics.mean(fetch[a.kernel])
-        w = statistics.mean(write[a.kernel])
+        fk, wk = fetch[a.kernel], write[a.kernel]
+        if a.last:
+            fk, wk = fk[-a.last:], wk[-a.last:]
+        f = statistics.mean(fk)
+        w = statistics.mean(wk)
         rec = {"workload": a.workload, "kernel": a.kernel, "kernel_source_hash": a.source_hash,
                "fetch_size_kib_per_dispatch": f, "write_size_kib_per_dispatch": w,
                "bytes_per_fetch_unit": fs, "bytes_per_write_unit": ws,
                "read_bytes_per_launch": f * fs, "written_bytes_per_launch": w * ws,
-               "bytes_per_launch": f * fs + w * ws, "dispatches": len(fetch[a.kernel])}
+               "bytes_per_launch": f * fs + w * ws, "dispatches": len(fk)}
         with open(a.out, "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")

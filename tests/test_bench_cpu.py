@@ -51,10 +51,10 @@ def _counter_dir(tmp_path, name, counter, rows):
     d = tmp_path / name
     d.mkdir()
     with open(d / "run_counter_collection.csv", "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
         w.writeheader()
-        for k, v in rows:
-            w.writerow({"Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v})
+        for i, (k, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v})
     return str(d)
 
 
@@ -84,6 +84,46 @@ def test_counter_scaling_needs_a_copy_kernel(tmp_path):
     cf = _counter_dir(tmp_path, "cf", "FETCH_SIZE", [("mk_op_gu_x", 512)])
     with pytest.raises(SystemExit):
         counters.copy_scale(cf, "FETCH_SIZE", 1 << 20)
+
+
+def test_counter_last_dispatches_skip_the_prefill_launch(tmp_path):
+    """A megakernel counter run: one launch of the whole prefill (40 steps'
+    bytes), then one launch per decode step; --last 3 keeps the decode steps."""
+    cf = _counter_dir(tmp_path, "cf", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 512)])
+    cw = _counter_dir(tmp_path, "cw", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1024)])
+    k = "mk_mega_x_128_f32_g4"
+    f = _counter_dir(tmp_path, "f", "FETCH_SIZE", [(k, 40000), (k, 1000), (k, 1001), (k, 1002)])
+    w = _counter_dir(tmp_path, "w", "WRITE_SIZE", [(k, 400), (k, 10), (k, 10), (k, 10)])
+    out = tmp_path / "t.json"
+    subprocess.run([sys.executable, "-m", "decode_persistent_megakernel_02_amd.counters", "--fetch", f, "--write", w,
+                    "--copy-fetch", cf, "--copy-write", cw, "--copy-mib", "1", "--kernel", k, "--last", "3",
+                    "--workload", "llama8b_mega", "--source-hash", "x", "--out", str(out)],
+                   check=True, cwd=ROOT, capture_output=True)
+    import json
+    rec = json.load(open(out))
+    assert rec["dispatches"] == 3
+    assert rec["read_bytes_per_launch"] == pytest.approx(1001 * 2048)
+    assert rec["written_bytes_per_launch"] == pytest.approx(10 * 1024)
+
+
+def test_kernel_stats_keep_one_step_dispatches_apart(tmp_path):
+    """kstats: dispatches longer than twice the kernel's median (multi-step
+    launches) are left out of the one-step row."""
+    from decode_persistent_megakernel_02_amd import kstats
+    d = tmp_path / "k"
+    d.mkdir()
+    with open(d / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 0
+        for dur in [3000, 3100, 3050, 120000, 3020, 200000]:
+            w.writerow({"Kernel_Name": "mk_mega_x", "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 10
+    r = subprocess.run([sys.executable, "-m", "decode_persistent_megakernel_02_amd.kstats", str(d),
+                        "--one-step", "mk_mega_x"], check=True, cwd=ROOT, capture_output=True, text=True)
+    one = [l for l in r.stdout.splitlines() if "(one-step)" in l][0].split("|")
+    assert int(one[2]) == 4 and float(one[3]) == pytest.approx(3042.5 / 1e3, abs=0.006)  # printed to 0.01 us
+    assert kstats.durations(str(d))["mk_mega_x"][3] == 120000
 
 
 def test_more_than_one_gpu_is_refused_with_a_message():
