@@ -18,6 +18,7 @@ MK_ERR_CAPACITY, MK_ERR_TIMEOUT, MK_ERR_STATE, MK_ERR_UNSUPPORTED = -4, -5, -6, 
 MK_MODE_MEGAKERNEL, MK_MODE_PER_OP = 0, 1
 MK_FLAG_TRACE, MK_FLAG_POISON, MK_FLAG_NO_GRAPH, MK_FLAG_FUSED_MERGE, MK_FLAG_TILED_WEIGHTS = 1, 2, 4, 8, 16
 MK_FLAG_SPIN_LIMIT_1 = 32
+MK_FLAG_BATCHED_PREFILL = 64
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_OUT_OF_MEMORY", -3: "MK_ERR_HIP",
                 -4: "MK_ERR_CAPACITY", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE", -7: "MK_ERR_UNSUPPORTED"}
 
@@ -104,6 +105,7 @@ SIGNATURES = {
     "mk_t_attention": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_attention_noalloc": ([_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "mk_t_op_raw": ([_P, _I32, _I32, _P, _P], _I32),
+    "mk_t_set_prefill_rows": ([_P, _I32], _I32),
     "mk_generate": ([_P, _P, _I32, _P, _P], _I32),
     "mk_t_bgemm": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P], _I32),
     "mk_tile_weights": ([_P, _P, _I64, _I64, _P], _I32),
@@ -354,6 +356,10 @@ def mk_t_attention(q, k, v, T, split, o, stream=None):
     f32 = 1 if k.element_size() == 4 else 0
     _check(lib.mk_t_attention(_ptr(q), _ptr(k), _ptr(v), S * hd, nq, nkv, hd, T, split, f32, _ptr(o),
                               _stream(stream)), "mk_t_attention")
+
+
+def mk_t_set_prefill_rows(h: Handle, rows: int):
+    _check(lib.mk_t_set_prefill_rows(h.ptr, rows), "mk_t_set_prefill_rows")
 
 
 def mk_t_op_raw(h: Handle, op_type: int, layer: int, x, y):

@@ -34,7 +34,7 @@ def build_lib(verbose=False, out=LIB, defines=()):
     # (source, extra defines): the megakernel instances are split over three
     # compiles so that they build in parallel
     srcs = [("kernels.hip", ()), ("mega.hip", ("MK_MEGA_PART=0",)), ("mega.hip", ("MK_MEGA_PART=1",)),
-            ("mega.hip", ("MK_MEGA_PART=2",)), ("batched.hip", ()), ("api.hip", ())]
+            ("mega.hip", ("MK_MEGA_PART=2",)), ("batched.hip", ()), ("prefill.hip", ()), ("api.hip", ())]
     host = os.path.join(CSRC, "graph.cpp")
     inc = ["-I", CSRC, "-I", os.path.join(ROOT, "include")] + [f"-D{d}" for d in defines]
     bdir = os.path.join(PKG, "_build", hashlib.sha1(" ".join(defines).encode()).hexdigest()[:8]) if defines \
@@ -54,7 +54,7 @@ def build_lib(verbose=False, out=LIB, defines=()):
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall"] + inc + ["-c", "-o", obj, host], verbose)
     objs.append(obj)
     tmp = out + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lrocblas"], verbose)
     os.replace(tmp, out)
     return out
 

@@ -11,10 +11,13 @@
 #include <string>
 #include <vector>
 
+#include <rocblas/rocblas.h>
+
 #include "graph.h"
 #include "kernels.h"
 #include "mk.h"
 #include "mk_debug.h"
+#include "prefill.h"
 
 using namespace mk;
 
@@ -195,6 +198,14 @@ struct mk_handle {
   // back-to-back replay of one operator's launches (mk_time_op_replay)
   int only_type = -1, replayed = 0;
   hipEvent_t rep_ev[2] = {nullptr, nullptr};
+  // batched prefill (MK_FLAG_BATCHED_PREFILL): matrix-core projections through rocBLAS
+  rocblas_handle blas = nullptr;
+  int pf_rows = 0, pf_cap = 0;          // rows (sequence x position) per chunk; its allocated maximum
+  float* pf_x = nullptr;                // [rows][H] residual stream of the chunk
+  float* pf_y = nullptr;                // [rows][max(qd + 2 kd, 2F, H)] projection outputs
+  uint16_t* pf_hi = nullptr;            // [rows][max(H, qd, F)] bf16 operand, high part
+  uint16_t* pf_lo = nullptr;            // ... low part
+  float* pf_logits = nullptr;           // [max_batch][V] when the caller passes no logits
 
   template <class T>
   mk_status alloc(T** p, int64_t count) {
@@ -209,6 +220,7 @@ struct mk_handle {
     return MK_OK;
   }
   ~mk_handle() {
+    if (blas) (void)rocblas_destroy_handle(blas);
     if (host_abort) (void)hipHostFree(host_abort);
     if (graph_exec) (void)hipGraphExecDestroy(graph_exec);
     if (step_graph) (void)hipGraphDestroy(step_graph);
@@ -861,6 +873,24 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, h->mega_fn, kMegaWaves * kWave, h->lds_mega));
     if (nb < 1) return fail(MK_ERR_UNSUPPORTED, "the megakernel does not fit on a CU");
   }
+  if (cfg->flags & MK_FLAG_BATCHED_PREFILL) {
+    if (cfg->flags & MK_FLAG_TILED_WEIGHTS)
+      return fail(MK_ERR_UNSUPPORTED, "MK_FLAG_BATCHED_PREFILL needs row-major weights (not MK_FLAG_TILED_WEIGHTS)");
+    const int qd = nq * hd, kd = nkv * hd;
+    h->pf_cap = h->pf_rows = std::max(kPrefillRows, B);
+    const int64_t wy = std::max<int64_t>({(int64_t)qd + 2 * kd, 2 * (int64_t)F, H});
+    const int64_t wk = std::max<int64_t>({(int64_t)H, qd, F});
+    MK_TRY(h->alloc(&h->pf_x, (int64_t)h->pf_cap * H));
+    MK_TRY(h->alloc(&h->pf_y, (int64_t)h->pf_cap * wy));
+    MK_TRY(h->alloc(&h->pf_hi, (int64_t)h->pf_cap * wk));
+    MK_TRY(h->alloc(&h->pf_lo, (int64_t)h->pf_cap * wk));
+    MK_TRY(h->alloc(&h->pf_logits, (int64_t)B * V));
+    HIP_TRY(pf_prepare(hd));
+    if (rocblas_create_handle(&h->blas) != rocblas_status_success)
+      return fail(MK_ERR_HIP, "rocblas_create_handle failed");
+    if (rocblas_set_stream(h->blas, h->stream) != rocblas_status_success)
+      return fail(MK_ERR_HIP, "rocblas_set_stream failed");
+  }
   HIP_TRY(hipDeviceSynchronize());
   *out = guard.release();
   return MK_OK;
@@ -924,6 +954,67 @@ mk_status mk_generate(mk_handle* h, const int32_t* d_in, int32_t n, int32_t* d_o
   return MK_OK;
 }
 
+namespace {
+// out[M][N] (row stride ldo, fp32) = X W^T for the bf16 weights W [N][K] and
+// X = hi + lo ([M][K] each): two matrix-core GEMMs, the second accumulating.
+// rocBLAS is column-major: out^T = W X^T with W^T stored [K][N] (lda K) and
+// X^T stored [K][M] (ldb K).
+mk_status pf_gemm(mk_handle* h, const uint16_t* W, int N, int K, int M, float* out, int ldo) {
+  const float one = 1.0f, zero = 0.0f;
+  for (int part = 0; part < 2; ++part) {
+    const rocblas_status st = rocblas_gemm_ex(
+        h->blas, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &one, W, rocblas_datatype_bf16_r, K,
+        part ? h->pf_lo : h->pf_hi, rocblas_datatype_bf16_r, K, part ? &one : &zero, out, rocblas_datatype_f32_r,
+        ldo, out, rocblas_datatype_f32_r, ldo, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    if (st != rocblas_status_success) return fail(MK_ERR_HIP, std::string("rocblas_gemm_ex: ") + rocblas_status_to_string(st));
+  }
+  return MK_OK;
+}
+
+// The whole prompt of every sequence, in chunks of rows (sequence b, position
+// p0 + i), row r = b c + i.  Per layer: RMSNorm (for layers after the first,
+// with the previous down projection's residual add) -> Q, K, V GEMMs -> RoPE
+// and KV append -> causal attention over the cache -> O GEMM -> residual add
+// and RMSNorm -> gate and up GEMMs -> SwiGLU -> down GEMM; after the last
+// layer of the last chunk the residual add, the final norm and the LM head run
+// on each sequence's last position only, then the argmax.
+mk_status prefill_batched(mk_handle* h, const int32_t* d_tokens, int B, int P, int32_t* d_next, float* d_logits) {
+  const Params& Pp = h->P;
+  const int L = Pp.L, H = Pp.H, qd = Pp.nq * Pp.hd, kd = Pp.nkv * Pp.hd, F = Pp.F, V = Pp.V, wq = qd + 2 * kd;
+  const int cmax = std::max(1, h->pf_rows / B);
+  hipStream_t s = h->stream;
+  float *X = h->pf_x, *Y = h->pf_y;
+  auto W = [&](int table, int l) { return static_cast<const uint16_t*>(h->host_w[(size_t)table * L + l]); };
+  for (int p0 = 0, c = 0; p0 < P; p0 += c) {
+    c = std::min(cmax, P - p0);
+    const int M = B * c;
+    HIP_TRY(pf_embed(s, Pp, d_tokens, P, B, c, p0, X));
+    for (int l = 0; l < L; ++l) {
+      HIP_TRY(pf_add_norm_split(s, Pp, X, l ? Y : nullptr, H, W(0, l), M, 1, 0, h->pf_hi, h->pf_lo));
+      MK_TRY(pf_gemm(h, W(1, l), qd, H, M, Y, wq));
+      MK_TRY(pf_gemm(h, W(2, l), kd, H, M, Y + qd, wq));
+      MK_TRY(pf_gemm(h, W(3, l), kd, H, M, Y + qd + kd, wq));
+      HIP_TRY(pf_rope_kv(s, Pp, l, Y, wq, B, c, p0));
+      HIP_TRY(pf_attention(s, Pp, l, Y, wq, B, c, p0, h->pf_hi, h->pf_lo));
+      MK_TRY(pf_gemm(h, W(4, l), H, qd, M, Y, H));
+      HIP_TRY(pf_add_norm_split(s, Pp, X, Y, H, W(5, l), M, 1, 0, h->pf_hi, h->pf_lo));
+      MK_TRY(pf_gemm(h, W(6, l), F, H, M, Y, 2 * F));
+      MK_TRY(pf_gemm(h, W(7, l), F, H, M, Y + F, 2 * F));
+      HIP_TRY(pf_swiglu_split(s, Pp, Y, M, h->pf_hi, h->pf_lo));
+      MK_TRY(pf_gemm(h, W(8, l), H, F, M, Y, H));
+    }
+    if (p0 + c == P) {
+      HIP_TRY(pf_add_norm_split(s, Pp, X, Y, H, Pp.final_norm, B, c, c - 1, h->pf_hi, h->pf_lo));
+      float* lg = d_logits ? d_logits : h->pf_logits;
+      MK_TRY(pf_gemm(h, Pp.tied ? Pp.embed : Pp.lm_head, V, H, B, lg, V));
+      HIP_TRY(pf_argmax(s, Pp, lg, B, d_next));
+    }
+  }
+  h->length = P;
+  return MK_OK;
+}
+}  // namespace
+
 mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P, int32_t* d_next, float* d_logits) {
   g_err.clear();
   if (!h || !d_tokens || !d_next) return fail(MK_ERR_INVALID_ARG, "NULL handle or token pointer");
@@ -934,6 +1025,7 @@ mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P
   if (B != h->cfg.max_batch) return fail(MK_ERR_UNSUPPORTED, "batch must equal max_batch");
   if (P > h->cfg.max_seq) return fail(MK_ERR_CAPACITY, "prompt longer than max_seq");
   h->batch = B;
+  if (h->cfg.flags & MK_FLAG_BATCHED_PREFILL) return prefill_batched(h, d_tokens, B, P, d_next, d_logits);
   if (h->cfg.mode == MK_MODE_MEGAKERNEL) {  // B == 1: the whole prompt in one launch
     Step S{};
     S.epoch = h->epoch + 1;
@@ -1429,6 +1521,15 @@ mk_status mk_t_attention_noalloc(const float* q, const void* k, const void* v, i
                      nkv, hd, T, split, nsplit, f32, part);
   hipLaunchKernelGGL(mk_t_attn_merge_kernel, dim3(nkv), dim3(kWave), 0, st, part, nq, nkv, hd, T, split, nsplit, o);
   HIP_TRY(hipGetLastError());
+  return MK_OK;
+}
+
+mk_status mk_t_set_prefill_rows(mk_handle* h, int32_t rows) {
+  g_err.clear();
+  if (!h) return fail(MK_ERR_INVALID_ARG, "NULL handle");
+  if (!(h->cfg.flags & MK_FLAG_BATCHED_PREFILL)) return fail(MK_ERR_STATE, "handle created without MK_FLAG_BATCHED_PREFILL");
+  if (rows < h->cfg.max_batch || rows > h->pf_cap) return fail(MK_ERR_INVALID_ARG, "rows outside [max_batch, 4096]");
+  h->pf_rows = rows;
   return MK_OK;
 }
 

@@ -1,0 +1,320 @@
+// Batched prefill: every prompt position of every sequence in one pass per
+// chunk of rows, instead of one decode step per position.  The projections run
+// as matrix-core GEMMs (the host calls rocBLAS on bf16 operands); this file
+// holds the work between them: the embedding gather, RMSNorm with the operand
+// split, RoPE with the KV append, causal attention, SwiGLU and the argmax.
+// What each step computes is the decode step's operator, for all positions at
+// once ("Compilar LLM en un MegaKernel para lograr inferencia de baja
+// latencia", "Parte 1. Compilador": the model's operators); prefill as the
+// throughput counterpart of decode ("Cómo la fusión de kernels CUDA acelera la
+// inferencia de LLM", section "Comprueba si la fusión ha ayudado"), on
+// matrix-by-matrix instructions (the hakusoku summary page, section
+// 命令セットの再設計).
+#include "device.h"
+#include "prefill.h"
+
+namespace mk {
+namespace {
+
+constexpr int kT = 256;  // threads per workgroup of every kernel here
+
+// Sum over the workgroup (all threads call it); red holds kT / 64 floats.
+__device__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();  // red may still be read from the previous call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kT / 64; ++i) t += red[i];
+  return t;
+}
+
+__device__ __forceinline__ void split_store(uint16_t* hi, uint16_t* lo, int64_t i, float v) {
+  const uint16_t h = f2bf(v);
+  hi[i] = h;
+  lo[i] = f2bf(v - bf1(h));
+}
+
+__global__ __launch_bounds__(kT) void k_embed(Params P, const int32_t* tokens, int tok_stride, int c, int p0,
+                                              float* X) {
+  const int r = blockIdx.x, b = r / c, i = r % c;
+  int t = tokens[(int64_t)b * tok_stride + p0 + i];
+  if (t < 0 || t >= P.V) {
+    if (threadIdx.x == 0) atomicCAS(&P.status[1], ST_OK, ST_BADTOKEN);
+    t = 0;
+  }
+  const uint16_t* e = P.embed + (int64_t)t * P.H;
+  float* x = X + (int64_t)r * P.H;
+  for (int k = threadIdx.x; k < P.H; k += kT) x[k] = bf1(e[k]);
+}
+
+__global__ __launch_bounds__(kT) void k_add_norm_split(Params P, float* X, const float* T, int ldt,
+                                                       const uint16_t* gamma, int rstride, int roff, uint16_t* hi,
+                                                       uint16_t* lo) {
+  __shared__ float red[kT / 64];
+  const int o = blockIdx.x, src = o * rstride + roff, H = P.H;
+  float* x = X + (int64_t)src * H;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += kT) {
+    float v = x[k];
+    if (T) {
+      v += T[(int64_t)src * ldt + k];
+      x[k] = v;
+    }
+    ss = fmaf(v, v, ss);
+  }
+  const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)H + P.eps);
+  for (int k = threadIdx.x; k < H; k += kT) split_store(hi, lo, (int64_t)o * H + k, x[k] * inv * bf1(gamma[k]));
+}
+
+__global__ __launch_bounds__(kT) void k_rope_kv(Params P, int l, float* QKV, int ldq, int c, int p0) {
+  const int r = blockIdx.x, b = r / c, p = p0 + r % c;
+  const int half = P.hd / 2, qd = P.nq * P.hd, kd = P.nkv * P.hd;
+  float* row = QKV + (int64_t)r * ldq;
+  for (int t = threadIdx.x; t < (P.nq + P.nkv) * half; t += kT) {
+    const int hh = t / half, i = t % half;
+    float* base = row + (hh < P.nq ? hh * P.hd : qd + (hh - P.nq) * P.hd);
+    const float cs = P.rope_cos[(int64_t)p * half + i], sn = P.rope_sin[(int64_t)p * half + i];
+    const float y0 = base[i], y1 = base[i + half];
+    const float a = y0 * cs - y1 * sn, z = y1 * cs + y0 * sn;
+    base[i] = a;
+    base[i + half] = z;
+    if (hh >= P.nq) {
+      const int64_t off = kv_off(P, l, b, hh - P.nq, p);
+      kv_store(P, P.kcache, off + i, a);
+      kv_store(P, P.kcache, off + i + half, z);
+    }
+  }
+  for (int t = threadIdx.x; t < kd; t += kT)
+    kv_store(P, P.vcache, kv_off(P, l, b, t / P.hd, p) + t % P.hd, row[qd + kd + t]);
+}
+
+// Causal attention.  Workgroup (query block, KV head g, sequence b) holds 64
+// query rows: Qb = 64 / G positions times the G query heads of g (row
+// q = position index * G + head index).  Keys and values stream through LDS
+// in blocks of 64 positions; each block's scores (4 x 4 per thread), an online
+// softmax (4 threads per row) and the output update (8 rows x HD/32 dims per
+// thread) follow one another between barriers.
+template <typename KT>
+__device__ __forceinline__ float kv_ld(const KT* p) {
+  if constexpr (std::is_same<KT, float>::value) return *p;
+  else return bf1(*p);
+}
+
+template <int HD, typename KT>
+__global__ __launch_bounds__(kT) void k_attention(Params P, int l, const float* QKV, int ldq, int c, int p0,
+                                                  uint16_t* hi, uint16_t* lo) {
+  extern __shared__ float sm[];
+  constexpr int KP = HD + 1, DPT = HD / 32;
+  float* Qs = sm;             // [64][HD], scaled by 1/sqrt(HD)
+  float* Ks = Qs + 64 * HD;   // [64][KP]
+  float* Vs = Ks + 64 * KP;   // [64][HD]
+  float* Ps = Vs + 64 * HD;   // [64][65] scores, then weights
+  float* mrow = Ps + 64 * 65; // running maximum per row
+  float* lrow = mrow + 64;    // running sum per row
+  float* arow = lrow + 64;    // this block's rescale factor per row
+  const int G = P.nq / P.nkv, Qb = 64 / G;
+  const int i0 = blockIdx.x * Qb, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int npos = min(Qb, c - i0);  // valid query positions of this block
+  const float scale = 1.0f / sqrtf((float)HD);
+  for (int e = t; e < 64 * HD; e += kT) {
+    const int q = e / HD, d = e % HD, qi = q / G, gi = q % G;
+    Qs[e] = qi < npos ? QKV[(int64_t)(b * c + i0 + qi) * ldq + (g * G + gi) * HD + d] * scale : 0.f;
+  }
+  if (t < 64) {
+    mrow[t] = -INFINITY;
+    lrow[t] = 0.f;
+  }
+  const int pmax = p0 + i0 + npos - 1;  // last key position any row of the block needs
+  const KT* kc = static_cast<const KT*>(P.kcache) + kv_off(P, l, b, g, 0);
+  const KT* vc = static_cast<const KT*>(P.vcache) + kv_off(P, l, b, g, 0);
+  float o[8][DPT];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) o[a][d] = 0.f;
+  const int rg = t / 16, kg = t % 16;  // scores: rows 4 rg .. 4 rg + 3, keys 4 kg .. 4 kg + 3
+  const int og = t / 32, dg = t % 32;  // output: rows 8 og .. 8 og + 7, dims DPT dg ..
+  for (int j0 = 0; j0 <= pmax; j0 += 64) {
+    __syncthreads();  // the previous block's keys, values and weights are consumed
+    for (int e = t; e < 64 * HD; e += kT) {
+      const int j = e / HD, d = e % HD;
+      const bool in = j0 + j <= pmax;
+      Ks[j * KP + d] = in ? kv_ld(kc + (int64_t)(j0 + j) * HD + d) : 0.f;
+      Vs[j * HD + d] = in ? kv_ld(vc + (int64_t)(j0 + j) * HD + d) : 0.f;
+    }
+    __syncthreads();
+    float s[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s[a][k] = 0.f;
+    for (int d = 0; d < HD; ++d) {
+      float qv[4], kv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) qv[a] = Qs[(4 * rg + a) * HD + d];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kv[k] = Ks[(4 * kg + k) * KP + d];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s[a][k] = fmaf(qv[a], kv[k], s[a][k]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int q = 4 * rg + a, pos = p0 + i0 + q / G;  // the row's query position
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = j0 + 4 * kg + k;
+        Ps[q * 65 + 4 * kg + k] = j <= pos ? s[a][k] : -INFINITY;
+      }
+    }
+    __syncthreads();
+    {  // online softmax: 4 threads per row, 16 keys each
+      const int q = t / 4, part = t % 4;
+      float mx = -INFINITY;
+      for (int k = 0; k < 16; ++k) mx = fmaxf(mx, Ps[q * 65 + part * 16 + k]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      const float mold = mrow[q], mnew = fmaxf(mold, mx);
+      float sum = 0.f;
+      for (int k = 0; k < 16; ++k) {
+        const float sv = Ps[q * 65 + part * 16 + k];
+        const float w = sv == -INFINITY ? 0.f : __expf(sv - mnew);
+        Ps[q * 65 + part * 16 + k] = w;
+        sum += w;
+      }
+      sum += __shfl_xor(sum, 1);
+      sum += __shfl_xor(sum, 2);
+      // every row has at least key 0 in the first block, so mnew is finite
+      const float alpha = mold == -INFINITY ? 0.f : __expf(mold - mnew);
+      __syncthreads();  // every thread of the row has read mrow before it changes
+      if (part == 0) {
+        mrow[q] = mnew;
+        lrow[q] = lrow[q] * alpha + sum;
+        arow[q] = alpha;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const float al = arow[8 * og + a];
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) o[a][d] *= al;
+    }
+    for (int k = 0; k < 64; ++k) {
+      float vv[DPT];
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) vv[d] = Vs[k * HD + dg * DPT + d];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const float w = Ps[(8 * og + a) * 65 + k];
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) o[a][d] = fmaf(w, vv[d], o[a][d]);
+      }
+    }
+  }
+  __syncthreads();
+  const int qd = P.nq * HD;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int q = 8 * og + a, qi = q / G, gi = q % G;
+    if (qi >= npos) continue;
+    const float inv = 1.0f / lrow[q];
+    const int64_t base = (int64_t)(b * c + i0 + qi) * qd + (g * G + gi) * HD + dg * DPT;
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) split_store(hi, lo, base + d, o[a][d] * inv);
+  }
+}
+
+constexpr int attn_lds_bytes(int hd) { return 4 * (64 * hd + 64 * (hd + 1) + 64 * hd + 64 * 65 + 3 * 64); }
+
+__global__ __launch_bounds__(kT) void k_swiglu_split(Params P, const float* GU, uint16_t* hi, uint16_t* lo) {
+  const int r = blockIdx.x, F = P.F;
+  const float* g = GU + (int64_t)r * 2 * F;
+  for (int k = threadIdx.x; k < F; k += kT) split_store(hi, lo, (int64_t)r * F + k, silu(g[k]) * g[F + k]);
+}
+
+__global__ __launch_bounds__(kT) void k_argmax(Params P, const float* logits, int32_t* next) {
+  __shared__ unsigned long long red[kT / 64];
+  const int b = blockIdx.x;
+  const float* x = logits + (int64_t)b * P.V;
+  unsigned long long best = 0;
+  for (int i = threadIdx.x; i < P.V; i += kT) {
+    const unsigned long long k = argmax_key(x[i], (uint32_t)i);
+    best = k > best ? k : best;
+  }
+  best = wave_max_u64(best);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kT / 64; ++w) best = red[w] > best ? red[w] : best;
+    best = red[0] > best ? red[0] : best;
+    next[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
+    if (!(fabsf(argmax_key_value(best)) <= 3.0e38f)) atomicCAS(&P.status[1], ST_OK, ST_NONFINITE);
+  }
+}
+
+}  // namespace
+
+hipError_t pf_embed(hipStream_t s, const Params& P, const int32_t* tokens, int tok_stride, int B, int c, int p0,
+                    float* X) {
+  k_embed<<<dim3(B * c), dim3(kT), 0, s>>>(P, tokens, tok_stride, c, p0, X);
+  return hipGetLastError();
+}
+
+hipError_t pf_add_norm_split(hipStream_t s, const Params& P, float* X, const float* T, int ldt, const uint16_t* gamma,
+                             int n, int rstride, int roff, uint16_t* hi, uint16_t* lo) {
+  k_add_norm_split<<<dim3(n), dim3(kT), 0, s>>>(P, X, T, ldt, gamma, rstride, roff, hi, lo);
+  return hipGetLastError();
+}
+
+hipError_t pf_rope_kv(hipStream_t s, const Params& P, int l, float* QKV, int ldq, int B, int c, int p0) {
+  k_rope_kv<<<dim3(B * c), dim3(kT), 0, s>>>(P, l, QKV, ldq, c, p0);
+  return hipGetLastError();
+}
+
+hipError_t pf_prepare(int hd) {
+  hipError_t e = hipSuccess;
+  if (hd == 64) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attention<64, float>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, attn_lds_bytes(64));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attention<64, uint16_t>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, attn_lds_bytes(64));
+  } else {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attention<128, float>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, attn_lds_bytes(128));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attention<128, uint16_t>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, attn_lds_bytes(128));
+  }
+  return e;
+}
+
+hipError_t pf_attention(hipStream_t s, const Params& P, int l, const float* QKV, int ldq, int B, int c, int p0,
+                        uint16_t* hi, uint16_t* lo) {
+  const int G = P.nq / P.nkv, Qb = 64 / G;
+  const dim3 grid((c + Qb - 1) / Qb, P.nkv, B);
+  if (P.hd == 64) {
+    if (P.kv_f32) k_attention<64, float><<<grid, dim3(kT), attn_lds_bytes(64), s>>>(P, l, QKV, ldq, c, p0, hi, lo);
+    else k_attention<64, uint16_t><<<grid, dim3(kT), attn_lds_bytes(64), s>>>(P, l, QKV, ldq, c, p0, hi, lo);
+  } else {
+    if (P.kv_f32) k_attention<128, float><<<grid, dim3(kT), attn_lds_bytes(128), s>>>(P, l, QKV, ldq, c, p0, hi, lo);
+    else k_attention<128, uint16_t><<<grid, dim3(kT), attn_lds_bytes(128), s>>>(P, l, QKV, ldq, c, p0, hi, lo);
+  }
+  return hipGetLastError();
+}
+
+hipError_t pf_swiglu_split(hipStream_t s, const Params& P, const float* GU, int rows, uint16_t* hi, uint16_t* lo) {
+  k_swiglu_split<<<dim3(rows), dim3(kT), 0, s>>>(P, GU, hi, lo);
+  return hipGetLastError();
+}
+
+hipError_t pf_argmax(hipStream_t s, const Params& P, const float* logits, int B, int32_t* next) {
+  k_argmax<<<dim3(B), dim3(kT), 0, s>>>(P, logits, next);
+  return hipGetLastError();
+}
+
+}  // namespace mk

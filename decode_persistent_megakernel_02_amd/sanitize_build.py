@@ -34,7 +34,7 @@ def build_sanitized(verbose=False):
     clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang++")
     bdir = os.path.join(PKG, "_build")
     dev = [os.path.join(bdir, n) for n in ("kernels.hip.o", "mega.hip.MK_MEGA_PART0.o", "mega.hip.MK_MEGA_PART1.o",
-                                            "mega.hip.MK_MEGA_PART2.o", "batched.hip.o")]
+                                            "mega.hip.MK_MEGA_PART2.o", "batched.hip.o", "prefill.hip.o")]
     if not all(os.path.exists(o) for o in dev):
         build_lib(verbose)
     sdir = os.path.dirname(SAN_LIB)
@@ -49,7 +49,7 @@ def build_sanitized(verbose=False):
          ["-c", "-o", graph_o, os.path.join(CSRC, "graph.cpp")], verbose)
     tmp = SAN_LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan", "-Xarch_host", "-fsanitize=address",
-          "-Xarch_host", "-fsanitize=undefined", "-o", tmp] + dev + [api_o, graph_o], verbose)
+          "-Xarch_host", "-fsanitize=undefined", "-o", tmp] + dev + [api_o, graph_o, "-lrocblas"], verbose)
     os.replace(tmp, SAN_LIB)
     return SAN_LIB
 

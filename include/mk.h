@@ -86,6 +86,11 @@ enum {
   MK_FLAG_SPIN_LIMIT_1 = 1u << 5, /* megakernel test hook: every in-kernel wait gives up after one
                                      unsuccessful check, so a step ends in MK_ERR_TIMEOUT with every
                                      wave exiting normally */
+  MK_FLAG_BATCHED_PREFILL = 1u << 6, /* mk_prefill runs every prompt position at once, in chunks of
+                                        4096 rows (sequence x position): the projections as bf16
+                                        matrix-core GEMMs on split fp32 activations, causal attention
+                                        over the cache; either mode.  Needs row-major weights.  Without
+                                        it, prefill runs one decode step per position */
   MK_FLAG_TILED_WEIGHTS = 1u << 4 /* batched path (max_batch >= 2): wq, wk, wv, wo, w_gate, w_up,
                                      w_down and (untied) lm_head are stored in the tiled layout that
                                      mk_tile_weights writes; embed and the norm gains stay

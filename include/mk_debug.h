@@ -173,6 +173,13 @@ mk_status mk_time_op_replay(mk_handle* h, int32_t type, int32_t reps, double* to
  * handles only (MK_ERR_UNSUPPORTED otherwise). */
 mk_status mk_t_op_raw(mk_handle* h, int32_t type, int32_t layer, const float* x, float* y);
 
+/* Rows (sequence x position) per chunk of the batched prefill of a handle
+ * created with MK_FLAG_BATCHED_PREFILL: rows in [max_batch, 4096]; a chunk
+ * then holds rows / max_batch positions of every sequence (the tests use
+ * small chunks to cross chunk boundaries).  MK_ERR_STATE without the flag,
+ * MK_ERR_INVALID_ARG outside the range. */
+mk_status mk_t_set_prefill_rows(mk_handle* h, int32_t rows);
+
 /* ---- single task bodies on explicit buffers (asynchronous on `stream`) ----- */
 /* y[N] = W[N,K] x[K]; W bf16 row-major, x/y fp32; K a multiple of 8. */
 mk_status mk_t_gemv(const void* W, const float* x, float* y, int32_t N, int32_t K, void* stream);
