@@ -152,6 +152,63 @@ def one_launch(abi, h, prompt_t, steps, torch, log=lambda *a: None, runs=5):
     return srt[len(srt) // 2] / steps, totals, toks.cpu().numpy()
 
 
+def prefill_flops(shape, B, P):
+    """Flops of a prefill of B prompts of P positions, each product counted once
+    (the second pass over the low parts of the split operands is not counted):
+    every projection for the B P rows, the LM head for the B last rows, and the
+    causal attention (q.k and p.v for every row over positions 0 .. p)."""
+    H, F, V, L = shape.hidden, shape.ffn, shape.vocab, shape.n_layers
+    qd, kd = shape.n_q_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim
+    per_row = L * (H * (qd + 2 * kd) + qd * H + 2 * H * F + F * H)
+    attn = L * qd * 2 * (P * (P + 1) // 2)
+    return 2.0 * (B * P * per_row + B * V * H + B * attn)
+
+
+def prefill_leg(abi, runtime, shape, dw, prompt_t, kv_fp32, torch, log, stepwise_mode=None, runs=5):
+    """The batched prefill (MK_FLAG_BATCHED_PREFILL) of the workload's prompts:
+    reset + prefill between two HIP events, median of `runs`; beside it, with
+    `stepwise_mode`, the step-by-step prefill of that mode timed the same way."""
+    B, P = prompt_t.shape
+
+    def time_it(h, name):
+        out = torch.zeros(B, dtype=torch.int32, device="cuda")
+        ts = []
+        for r in range(runs):
+            abi.mk_reset(h)
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record()
+            abi.mk_prefill(h, prompt_t, out)
+            t1.record()
+            torch.cuda.synchronize()
+            abi.mk_synchronize(h)
+            ts.append(t0.elapsed_time(t1))
+            log(f"{name} prefill run {r + 1}/{runs}: {ts[-1]:.2f} ms")
+        return sorted(ts)[len(ts) // 2], ts, out.cpu().numpy()
+
+    h = runtime.create(shape, dw, P + 1, B, abi.MK_MODE_PER_OP, abi.MK_FLAG_BATCHED_PREFILL, kv_fp32=kv_fp32)
+    ms, ts, ids = time_it(h, "batched")
+    abi.mk_destroy(h)
+    fl = prefill_flops(shape, B, P)
+    res = {"ms": ms, "runs_ms": ts, "sequences": B, "positions": P, "tokens_per_s": B * P / (ms * 1e-3),
+           "tflops_products_once": fl / (ms * 1e-3) / 1e12,
+           "frac_of_bf16_matrix_peak": fl / (ms * 1e-3) / 1e12 / 2500.0,
+           "timing": f"reset + mk_prefill of {B} x {P} positions between two HIP events, median of {runs}"}
+    if stepwise_mode is not None:
+        h = runtime.create(shape, dw, P + 1, B, stepwise_mode, 0, kv_fp32=kv_fp32)
+        sms, sts, sids = time_it(h, "step-by-step")
+        abi.mk_destroy(h)
+        res["step_by_step"] = {"ms": sms, "runs_ms": sts,
+                               "mode": "megakernel, one launch of P steps" if stepwise_mode == abi.MK_MODE_MEGAKERNEL
+                               else "per-operator, one step per position",
+                               "next_ids_equal": bool((sids == ids).all())}
+        res["speedup_over_step_by_step"] = sms / ms
+    log(f"batched prefill {B} x {P}: {ms:.2f} ms ({res['tokens_per_s']:.0f} tokens/s, "
+        f"{res['tflops_products_once']:.0f} TFLOP/s)")
+    return res
+
+
 def pct(xs, q):
     import numpy as np
     return float(np.percentile(np.asarray(xs), q))
@@ -296,6 +353,9 @@ def main():
     ap.add_argument("--trace-dump", default=None, metavar="FILE.npy", help="save the raw megakernel trace")
     ap.add_argument("--no-per-op", action="store_true", help="skip the per-operator baseline (quick runs)")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the batched-prefill timing")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the batched prefill of the workload's prompts (row-major weights) and exit")
     ap.add_argument("--counters-mode", choices=("mega", "per_op"), default="mega",
                     help="with --counters: which build's launches the counter run sees")
     ap.add_argument("--fused-merge", action="store_true",
@@ -341,7 +401,7 @@ def main():
     max_seq = wl.prompt_len + max(steps, warmup)
     t = time.time()
     # the batched path reads its projection weights in the tiled layout
-    tiled = B > 1 and not args.row_major
+    tiled = B > 1 and not args.row_major and not args.prefill_only
     if B == 1:
         weights = gen.gen_weights(shape, wl.weight_seed)
         dw = runtime.upload_weights(weights)
@@ -361,6 +421,11 @@ def main():
 
     # batch 1 keeps an fp32 KV cache; the batched workloads state a bf16 cache
     kv_fp32 = B == 1
+    if args.prefill_only:
+        pf = prefill_leg(abi, runtime, shape, dw, prompt_t, kv_fp32, torch, log)
+        print(json.dumps({"prefill": pf, "workload": wl.name, "kv_cache": "fp32" if kv_fp32 else "bf16",
+                          "weights": "row-major"}), flush=True)
+        return
     flags = (abi.MK_FLAG_FUSED_MERGE if args.fused_merge else 0) | (abi.MK_FLAG_TILED_WEIGHTS if tiled else 0)
     if args.counters:
         if args.counters_prompt:
@@ -412,6 +477,11 @@ def main():
     if not (args.no_per_op and mega is not None):
         per_op, op_ms, op_tokens, gu_gbps, kern_ms, kb, gu_kernel = per_op_baseline(
             abi, runtime, shape, dw, prompt_t, steps, warmup, max_seq, B, flags, args, kv_fp32, tiled, wl, torch, log)
+
+    prefill = None
+    if not tiled and not args.no_prefill:
+        prefill = prefill_leg(abi, runtime, shape, dw, prompt_t, kv_fp32, torch, log,
+                              stepwise_mode=abi.MK_MODE_MEGAKERNEL if B == 1 else None)
 
     ceiling = None
     if B == 1 and not args.no_stream_probe:
@@ -467,6 +537,7 @@ def main():
         "per_op_baseline": per_op,
         "megakernel_speedup_over_per_op": (op_ms / mega["ms_per_token"]) if mega and op_ms else None,
         "streaming_read_ceiling_gbps": ceiling,
+        "prefill": prefill,
         "tokens_equal_megakernel_per_op": bool((mega_tokens == op_tokens).all()) if mega and op_ms else None,
         "cpu_baseline": None,
     }
