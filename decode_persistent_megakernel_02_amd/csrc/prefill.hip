@@ -228,6 +228,155 @@ __global__ __launch_bounds__(kT) void k_attention(Params P, int l, const float* 
   }
 }
 
+// Causal attention on the matrix cores (bf16 cache, head_dim 128), the same
+// rows as k_attention: four waves, each 16 of the block's 64 query rows (wave
+// w: rows 16 w .. 16 w + 15), keys in blocks of 64 positions.
+// Scores: S = Q K^T as v_mfma_f32_16x16x32_bf16 per 16-key tile, the fp32
+// queries (scaled by 1/sqrt(128)) as a bf16 pair hi + lo, each times the exact
+// bf16 keys, fp32 accumulation.  Lane i supplies query row i & 15 and key
+// i & 15 of the tile, both with dims 32 ks + 8 (i >> 4) .. + 7 in k-step ks,
+// so a key fragment is 16 contiguous bytes of its cache row.  Result: lane i
+// holds S[row 4 (i >> 4) + j][key i & 15], j < 4; the online softmax works on
+// that layout (row reductions over 16 lanes), so a lane keeps the running
+// maximum and sum of rows 4 (i >> 4) + j.
+// Values: O += P V as v_mfma_f32_16x16x16_bf16 per 16-key step and 16-dim
+// output tile tt, P passed through LDS into the A layout (lane i: row i & 15,
+// keys 4 (i >> 4) .. + 3) as a bf16 pair, the values with dims permuted so
+// that column c of tile tt is dim 8 c + tt: lane i loads dims 8 (i & 15) .. + 7
+// of keys 4 (i >> 4) .. + 3, one 16-byte vector each, and takes element tt of
+// each for tile tt.  Result: lane i holds O[row 4 (i >> 4) + j][dim 8 (i & 15)
+// + tt], rescaled with the same lane's softmax corrections.
+__device__ __forceinline__ uint32_t pack_bf2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+// bf16 element e (0..7) of a 16-byte vector
+__device__ __forceinline__ short bf_elem(const v4u& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return (short)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+__global__ __launch_bounds__(kT) void k_attention_mma(Params P, int l, const float* QKV, int ldq, int c, int p0,
+                                                      uint16_t* hi, uint16_t* lo) {
+  constexpr int HD = 128, PB = 68;
+  __shared__ float pbuf[4 * 16 * PB];
+  const int G = P.nq / P.nkv, Qb = 64 / G;
+  const int i0 = blockIdx.x * Qb, g = blockIdx.y, b = blockIdx.z;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const int npos = min(Qb, c - i0), pmax = p0 + i0 + npos - 1;
+  const float scale = 1.0f / sqrtf((float)HD);
+  v4u qh[4], ql[4];
+  {
+    const int q = 16 * w + lr, qi = q / G, gi = q % G;
+    const bool valid = qi < npos;
+    const float* src = QKV + (int64_t)(b * c + i0 + (valid ? qi : 0)) * ldq + (g * G + gi) * HD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint16_t h8[8], l8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = valid ? src[32 * ks + 8 * lq + e] * scale : 0.f;
+        h8[e] = f2bf(x);
+        l8[e] = f2bf(x - bf1(h8[e]));
+      }
+      qh[ks] = v4u{pack_bf2(h8[0], h8[1]), pack_bf2(h8[2], h8[3]), pack_bf2(h8[4], h8[5]), pack_bf2(h8[6], h8[7])};
+      ql[ks] = v4u{pack_bf2(l8[0], l8[1]), pack_bf2(l8[2], l8[3]), pack_bf2(l8[4], l8[5]), pack_bf2(l8[6], l8[7])};
+    }
+  }
+  int qpos[4];  // query position of the lane's result rows
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qpos[j] = p0 + i0 + (16 * w + 4 * lq + j) / G;
+  const uint16_t* kc = static_cast<const uint16_t*>(P.kcache) + kv_off(P, l, b, g, 0);
+  const uint16_t* vc = static_cast<const uint16_t*>(P.vcache) + kv_off(P, l, b, g, 0);
+  float* pb = pbuf + w * 16 * PB;
+  float m[4], lsum[4];
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.f;
+  }
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) o[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const v4u zero{0u, 0u, 0u, 0u};
+  for (int j0 = 0; j0 <= pmax; j0 += 64) {
+    f32x4 s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = j0 + 16 * t + lr;
+      const bool kin = key <= pmax;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const v4u kf = kin ? *reinterpret_cast<const v4u*>(kc + (int64_t)key * HD + 32 * ks + 8 * lq) : zero;
+        s[t] = mma16(qh[ks], kf, s[t]);
+        s[t] = mma16(ql[ks], kf, s[t]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float v = j0 + 16 * t + lr <= qpos[j] ? s[t][j] : -INFINITY;
+        s[t][j] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = row16_max(mx);
+      const float mnew = fmaxf(m[j], mx);
+      const float alpha = m[j] == -INFINITY ? 0.f : __expf(m[j] - mnew);
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float pv = s[t][j] == -INFINITY ? 0.f : __expf(s[t][j] - mnew);
+        s[t][j] = pv;
+        sum += pv;
+      }
+      lsum[j] = lsum[j] * alpha + row16_sum(sum);
+      m[j] = mnew;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) o[tt][j] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pb[(4 * lq + j) * PB + 16 * t + lr] = s[t][j];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint16_t ph[4], pl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = pb[lr * PB + 16 * t + 4 * lq + e];
+        ph[e] = f2bf(x);
+        pl[e] = f2bf(x - bf1(ph[e]));
+      }
+      const s16x4 pa_h{(short)ph[0], (short)ph[1], (short)ph[2], (short)ph[3]};
+      const s16x4 pa_l{(short)pl[0], (short)pl[1], (short)pl[2], (short)pl[3]};
+      v4u vv[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int key = j0 + 16 * t + 4 * lq + kk;
+        vv[kk] = key <= pmax ? *reinterpret_cast<const v4u*>(vc + (int64_t)key * HD + 8 * lr) : zero;
+      }
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const s16x4 bv{bf_elem(vv[0], tt), bf_elem(vv[1], tt), bf_elem(vv[2], tt), bf_elem(vv[3], tt)};
+        o[tt] = mma16k16(pa_h, bv, o[tt]);
+        o[tt] = mma16k16(pa_l, bv, o[tt]);
+      }
+    }
+    __syncthreads();  // the weights are read before the next block writes them
+  }
+  const int qd = P.nq * HD;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = 16 * w + 4 * lq + j, qi = q / G, gi = q % G;
+    if (qi >= npos) continue;
+    const float inv = 1.0f / lsum[j];
+    const int64_t base = (int64_t)(b * c + i0 + qi) * qd + (g * G + gi) * HD + 8 * lr;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) split_store(hi, lo, base + tt, o[tt][j] * inv);
+  }
+}
+
 constexpr int attn_lds_bytes(int hd) { return 4 * (64 * hd + 64 * (hd + 1) + 64 * hd + 64 * 65 + 3 * 64); }
 
 __global__ __launch_bounds__(kT) void k_swiglu_split(Params P, const float* GU, uint16_t* hi, uint16_t* lo) {
@@ -297,7 +446,9 @@ hipError_t pf_attention(hipStream_t s, const Params& P, int l, const float* QKV,
                         uint16_t* hi, uint16_t* lo) {
   const int G = P.nq / P.nkv, Qb = 64 / G;
   const dim3 grid((c + Qb - 1) / Qb, P.nkv, B);
-  if (P.hd == 64) {
+  if (P.hd == 128 && !P.kv_f32) {  // bf16 cache: the matrix cores
+    k_attention_mma<<<grid, dim3(kT), 0, s>>>(P, l, QKV, ldq, c, p0, hi, lo);
+  } else if (P.hd == 64) {
     if (P.kv_f32) k_attention<64, float><<<grid, dim3(kT), attn_lds_bytes(64), s>>>(P, l, QKV, ldq, c, p0, hi, lo);
     else k_attention<64, uint16_t><<<grid, dim3(kT), attn_lds_bytes(64), s>>>(P, l, QKV, ldq, c, p0, hi, lo);
   } else {
