@@ -135,13 +135,15 @@ def test_bgemm_tiled_equals_row_major(abi, N, K, B):
 class BatchCase:
     """One batched model on the GPU; the oracles run on the same seeded inputs."""
 
-    def __init__(self, abi, shape, B, max_seq, seed=0, random_norms=True, attn_split=0, weights=None, tiled=False):
+    def __init__(self, abi, shape, B, max_seq, seed=0, random_norms=True, attn_split=0, weights=None, tiled=False,
+                 batched_prefill=False):
         from decode_persistent_megakernel_02_amd import runtime
         self.abi, self.shape, self.B = abi, shape, B
         self.w = weights if weights is not None else gen.gen_weights(shape, seed, random_norms)
         self.dw = runtime.upload_weights(self.w, tiled=tiled)
-        self.h = runtime.create(shape, self.dw, max_seq, B, abi.MK_MODE_PER_OP,
-                                abi.MK_FLAG_TILED_WEIGHTS if tiled else 0, attn_split=attn_split, kv_fp32=False)
+        flags = (abi.MK_FLAG_TILED_WEIGHTS if tiled else 0) | (abi.MK_FLAG_BATCHED_PREFILL if batched_prefill else 0)
+        self.h = runtime.create(shape, self.dw, max_seq, B, abi.MK_MODE_PER_OP, flags, attn_split=attn_split,
+                                kv_fp32=False)
         self.out = torch.zeros(B, dtype=torch.int32, device="cuda")
         self.tok = torch.zeros(B, dtype=torch.int32, device="cuda")
         self.logits = torch.zeros(B, shape.vocab, dtype=torch.float32, device="cuda")
@@ -353,21 +355,27 @@ def layer_subset(shape, n_layers):
     return replace(shape, name=f"{shape.name}_{n_layers}l", n_layers=n_layers)
 
 
-@pytest.mark.parametrize("base,B,P,tiled", [(presets.LLAMA8B, 8, 40, True), (presets.LLAMA70B, 64, 12, True),
-                                            (presets.LLAMA8B, 8, 40, False), (presets.LLAMA70B, 64, 12, False)],
+@pytest.mark.parametrize("base,B,P,tiled,bp", [(presets.LLAMA8B, 8, 40, True, False),
+                                               (presets.LLAMA70B, 64, 12, True, False),
+                                               (presets.LLAMA8B, 8, 40, False, False),
+                                               (presets.LLAMA70B, 64, 12, False, False),
+                                               (presets.LLAMA8B, 8, 40, False, True),
+                                               (presets.LLAMA70B, 64, 12, False, True)],
                          ids=["llama8b_b8_tiled", "llama70b_b64_tiled", "llama8b_b8_row_major",
-                              "llama70b_b64_row_major"])
-def test_real_layer_shapes_reduced_depth(abi, base, B, P, tiled):
+                              "llama70b_b64_row_major", "llama8b_b8_batched_prefill",
+                              "llama70b_b64_batched_prefill"])
+def test_real_layer_shapes_reduced_depth(abi, base, B, P, tiled, bp):
     """The batched workloads' layer shapes (8B at batch 8, 70B at batch 64), two
     layers deep, against the oracle's cache-free forward (teacher-forced with
-    seeded tokens); the workloads' tiled weights, and row-major ones."""
+    seeded tokens); the workloads' tiled weights, and row-major ones; and the
+    batched prefill (all prompt positions at once) followed by decode steps."""
     shape = layer_subset(base, 2)
     steps = 2
     T = P + steps
     seq = gen.tokens(900 + B, presets.TID_PROMPT, 0, B * T, shape.vocab).reshape(B, T).astype(np.int32)
     print(f"[{shape.name} B={B}] generating weights", flush=True)
     w = gen.gen_weights(shape, 0)
-    case = BatchCase(abi, shape, B, T, weights=w, tiled=tiled)
+    case = BatchCase(abi, shape, B, T, weights=w, tiled=tiled, batched_prefill=bp)
     got = [case.prefill(seq[:, :P])]
     for s in range(steps):
         got.append(case.step(seq[:, P + s]))

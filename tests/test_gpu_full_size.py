@@ -7,6 +7,8 @@ forcing with inputs that come from the generator, never from the GPU), and the
 oracle's cache-free causal forward over the same sequence gives the expected
 logits at every compared position.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -179,31 +181,40 @@ def test_8b_shape_two_layers_multi_split_attention(mode, batched_prefill):
     assert np.all(errs <= 5e-3)
 
 
-@pytest.mark.timeout(900)
-def test_batched_prefill_full_depth_agrees_with_step_by_step():
-    """The 8B shape at full depth: 8 sequences of 4096-token seeded prompts
-    prefilled both ways on the GPU (row-major weights, bf16 cache): batched
-    (chunks of 512 positions of every sequence, matrix-core GEMMs) and one
-    decode step per position.  The two caches agree layer by layer (the norm
-    of the difference within 1e-2 of the norm: the bf16 rounding of two fp32
-    summation orders), and the last-position logits within 5e-3 with the same
-    greedy ids at clear margins.  The oracle cannot recompute prompts this long
-    in fp64 on the host; the step-by-step path is held against it at every
-    other size."""
+@pytest.mark.timeout(1100)
+@pytest.mark.parametrize("name", [
+    "llama8b_b8_kv4096",
+    pytest.param("llama70b_b64", marks=pytest.mark.skipif(
+        os.environ.get("MK_LONG_TESTS") != "1",
+        reason="about 5 minutes (141 GB of weights generated on the host, 512 step-by-step decode steps); "
+               "run with MK_LONG_TESTS=1"))])
+def test_batched_prefill_full_depth_agrees_with_step_by_step(name):
+    """A batched workload at full depth: its seeded prompts (8 x 4096 at the
+    8B shape, 64 x 512 at the 70B shape) prefilled both ways on the GPU
+    (row-major weights, bf16 cache): batched (chunks of 4096 rows, matrix-core
+    GEMMs and attention) and one decode step per position.  The two differ by
+    the bf16 rounding of cache values that their fp32 summation orders leave
+    slightly apart, and that difference grows with depth: at the 8B shape (32
+    layers) the caches agree layer by layer within 1e-2 (norm of the
+    difference over the norm) and the last-position logits within 5e-3; at
+    the 70B shape (80 layers; 1.0e-2 measured) the logits are held to the
+    scope's 2e-2 contract, which each path meets against the oracle, and the
+    caches to 2e-2.  Greedy ids agree at clear margins.  The fp64
+    oracle cannot recompute these prompts on the host (one oracle step of the
+    70B shape widens 141 GB of weights); the step-by-step path is held against
+    it at every other size."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from decode_persistent_megakernel_02_amd import abi, runtime
-    wl = presets.WORKLOADS["llama8b_b8_kv4096"]
+    wl = presets.WORKLOADS[name]
     shape, B, P = wl.shape, wl.batch, wl.prompt_len
     prompt = torch.from_numpy(gen.gen_prompt(wl)).cuda()
-    print("[prefill full depth] generating weights", flush=True)
-    w = gen.gen_weights(shape, wl.weight_seed)
-    dw = runtime.upload_weights(w)
-    del w
+    print(f"[prefill full depth {name}] generating weights", flush=True)
+    dw = runtime.generate_device_weights(shape, wl.weight_seed)
     L, nkv, hd = shape.n_layers, shape.n_kv_heads, shape.head_dim
     got = []
     for flags in (abi.MK_FLAG_BATCHED_PREFILL, 0):
-        print(f"[prefill full depth] prefill {B} x {P}, flags {flags}", flush=True)
+        print(f"[prefill full depth {name}] prefill {B} x {P}, flags {flags}", flush=True)
         h = runtime.create(shape, dw, P, B, abi.MK_MODE_PER_OP, flags, kv_fp32=False)
         out = torch.zeros(B, dtype=torch.int32, device="cuda")
         lg = torch.zeros(B, shape.vocab, dtype=torch.float32, device="cuda")
@@ -216,14 +227,18 @@ def test_batched_prefill_full_depth_agrees_with_step_by_step():
         got.append((kb, vb, lg.cpu().numpy(), out.cpu().numpy()))
     del dw
     (ka, va, la, ia), (kb, vb, lb, ib) = got
+    cache_bar, logit_bar = (1e-2, 5e-3) if shape.n_layers <= 32 else (2e-2, 2e-2)
+    worst = 0.0
     for l in range(L):
-        for name, a, b in (("K", ka[l], kb[l]), ("V", va[l], vb[l])):
+        for nm, a, b in (("K", ka[l], kb[l]), ("V", va[l], vb[l])):
             a, b = D.widen_bf16(a), D.widen_bf16(b)
             err = np.linalg.norm(a - b) / np.linalg.norm(b)
-            assert err <= 1e-2, (name, l, err)
+            worst = max(worst, err)
+            assert err <= cache_bar, (nm, l, err)
     errs = rel_err(la, lb)
-    print(f"[prefill full depth] last-position logits: max rel diff {errs.max():.3e}", flush=True)
-    assert np.all(errs <= 5e-3)
+    print(f"[prefill full depth {name}] cache: worst layer {worst:.3e}; last-position logits: "
+          f"max rel diff {errs.max():.3e}", flush=True)
+    assert np.all(errs <= logit_bar)
     for b in range(B):
         if D.top2_margin(lb[b].astype(np.float64)) > 5e-2:
             assert ia[b] == ib[b]
