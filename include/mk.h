@@ -187,7 +187,15 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* weights, void* hip_s
  * tiles, cache layout), so a smaller batch uses a handle created for it
  * (B outside [1, max_batch]: MK_ERR_CAPACITY; 1 <= B < max_batch:
  * MK_ERR_UNSUPPORTED).  P must not exceed max_seq (MK_ERR_CAPACITY).  In
- * MK_MODE_MEGAKERNEL the P positions run in one launch. */
+ * MK_MODE_MEGAKERNEL the P positions run in one launch.  With
+ * MK_FLAG_BATCHED_PREFILL (either mode) every position of every sequence
+ * runs at once instead, in chunks of 4096 rows: the projections as bf16
+ * matrix-core GEMMs on fp32 activations split into a high and a low bf16
+ * part, causal attention over the cache, the same KV cache and outputs (to
+ * fp32 rounding; prefill as the throughput counterpart of decode: "Cómo la
+ * fusión de kernels CUDA acelera la inferencia de LLM", section "Comprueba si
+ * la fusión ha ayudado").  Asynchronous on the handle's stream in every case;
+ * a GEMM library error returns MK_ERR_HIP. */
 mk_status mk_prefill(mk_handle* h, const int32_t* d_tokens, int32_t B, int32_t P,
                      int32_t* d_next, float* d_logits);
 
