@@ -203,9 +203,8 @@ struct mk_handle {
   int pf_rows = 0, pf_cap = 0;          // rows (sequence x position) per chunk; its allocated maximum
   float* pf_x = nullptr;                // [rows][H] residual stream of the chunk
   float* pf_y = nullptr;                // [rows][max(qd + 2 kd, 2F, H)] projection outputs
-  uint16_t* pf_hi = nullptr;            // [rows][max(H, qd, F)] bf16 operand, high part
-  uint16_t* pf_lo = nullptr;            // ... low part
-  float* pf_logits = nullptr;           // [max_batch][V] when the caller passes no logits
+  uint16_t* pf_ops = nullptr;           // [2][rows][K] bf16 operand of one projection: high parts, then low
+  float* pf_logits = nullptr;           // [2][max_batch][V] LM-head outputs of the two operand parts
 
   template <class T>
   mk_status alloc(T** p, int64_t count) {
@@ -882,9 +881,8 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
     const int64_t wk = std::max<int64_t>({(int64_t)H, qd, F});
     MK_TRY(h->alloc(&h->pf_x, (int64_t)h->pf_cap * H));
     MK_TRY(h->alloc(&h->pf_y, (int64_t)h->pf_cap * wy));
-    MK_TRY(h->alloc(&h->pf_hi, (int64_t)h->pf_cap * wk));
-    MK_TRY(h->alloc(&h->pf_lo, (int64_t)h->pf_cap * wk));
-    MK_TRY(h->alloc(&h->pf_logits, (int64_t)B * V));
+    MK_TRY(h->alloc(&h->pf_ops, 2 * (int64_t)h->pf_cap * wk));
+    MK_TRY(h->alloc(&h->pf_logits, 2 * (int64_t)B * V));
     HIP_TRY(pf_prepare(hd));
     if (rocblas_create_handle(&h->blas) != rocblas_status_success)
       return fail(MK_ERR_HIP, "rocblas_create_handle failed");
@@ -956,18 +954,35 @@ mk_status mk_generate(mk_handle* h, const int32_t* d_in, int32_t n, int32_t* d_o
 
 namespace {
 // out[M][N] (row stride ldo, fp32) = X W^T for the bf16 weights W [N][K] and
-// X = hi + lo ([M][K] each): two matrix-core GEMMs, the second accumulating.
+// X = hi + lo, the operand planes pf_ops [2][M][K] (high parts, then low).
 // rocBLAS is column-major: out^T = W X^T with W^T stored [K][N] (lda K) and
-// X^T stored [K][M] (ldb K).
-mk_status pf_gemm(mk_handle* h, const uint16_t* W, int N, int K, int M, float* out, int ldo) {
+// X^T stored [K][rows] (ldb K).  Up to kPrefillStack rows (the weights'
+// bytes bound the time) one GEMM runs over the 2M stacked rows, so the
+// weights are read once, and the low part's rows are then added to the high
+// part's (out needs 2M rows; with fold_to the sums go there instead);
+// beyond that (the matrix cores bound it) a second GEMM accumulates the low
+// part into out.  Either way out = fl(hi W^T + lo W^T).
+mk_status pf_gemm(mk_handle* h, const uint16_t* W, int N, int K, int M, float* out, int ldo,
+                  float* fold_to = nullptr, int ld_fold = 0) {
   const float one = 1.0f, zero = 0.0f;
-  for (int part = 0; part < 2; ++part) {
+  const uint16_t* hi = h->pf_ops;
+  const uint16_t* lo = h->pf_ops + (int64_t)M * K;
+  auto gemm = [&](const uint16_t* x, int rows, const float* beta) -> mk_status {
     const rocblas_status st = rocblas_gemm_ex(
-        h->blas, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &one, W, rocblas_datatype_bf16_r, K,
-        part ? h->pf_lo : h->pf_hi, rocblas_datatype_bf16_r, K, part ? &one : &zero, out, rocblas_datatype_f32_r,
-        ldo, out, rocblas_datatype_f32_r, ldo, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+        h->blas, rocblas_operation_transpose, rocblas_operation_none, N, rows, K, &one, W, rocblas_datatype_bf16_r,
+        K, x, rocblas_datatype_bf16_r, K, beta, out, rocblas_datatype_f32_r, ldo, out, rocblas_datatype_f32_r, ldo,
+        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
     if (st != rocblas_status_success) return fail(MK_ERR_HIP, std::string("rocblas_gemm_ex: ") + rocblas_status_to_string(st));
+    return MK_OK;
+  };
+  if (M <= kPrefillStack) {
+    MK_TRY(gemm(hi, 2 * M, &zero));
+    HIP_TRY(pf_fold(h->stream, out, ldo, M, fold_to ? fold_to : out, fold_to ? ld_fold : ldo, M, N));
+    return MK_OK;
   }
+  MK_TRY(gemm(hi, M, &zero));
+  MK_TRY(gemm(lo, M, &one));
+  if (fold_to) HIP_TRY(pf_fold(h->stream, out, ldo, 0, fold_to, ld_fold, M, N));
   return MK_OK;
 }
 
@@ -984,29 +999,30 @@ mk_status prefill_batched(mk_handle* h, const int32_t* d_tokens, int B, int P, i
   const int cmax = std::max(1, h->pf_rows / B);
   hipStream_t s = h->stream;
   float *X = h->pf_x, *Y = h->pf_y;
+  uint16_t* ops = h->pf_ops;
   auto W = [&](int table, int l) { return static_cast<const uint16_t*>(h->host_w[(size_t)table * L + l]); };
   for (int p0 = 0, c = 0; p0 < P; p0 += c) {
     c = std::min(cmax, P - p0);
     const int M = B * c;
     HIP_TRY(pf_embed(s, Pp, d_tokens, P, B, c, p0, X));
     for (int l = 0; l < L; ++l) {
-      HIP_TRY(pf_add_norm_split(s, Pp, X, l ? Y : nullptr, H, W(0, l), M, 1, 0, h->pf_hi, h->pf_lo));
+      HIP_TRY(pf_add_norm_split(s, Pp, X, l ? Y : nullptr, H, W(0, l), M, 1, 0, ops, ops + (int64_t)M * H));
       MK_TRY(pf_gemm(h, W(1, l), qd, H, M, Y, wq));
       MK_TRY(pf_gemm(h, W(2, l), kd, H, M, Y + qd, wq));
       MK_TRY(pf_gemm(h, W(3, l), kd, H, M, Y + qd + kd, wq));
       HIP_TRY(pf_rope_kv(s, Pp, l, Y, wq, B, c, p0));
-      HIP_TRY(pf_attention(s, Pp, l, Y, wq, B, c, p0, h->pf_hi, h->pf_lo));
+      HIP_TRY(pf_attention(s, Pp, l, Y, wq, B, c, p0, ops, ops + (int64_t)M * qd));
       MK_TRY(pf_gemm(h, W(4, l), H, qd, M, Y, H));
-      HIP_TRY(pf_add_norm_split(s, Pp, X, Y, H, W(5, l), M, 1, 0, h->pf_hi, h->pf_lo));
+      HIP_TRY(pf_add_norm_split(s, Pp, X, Y, H, W(5, l), M, 1, 0, ops, ops + (int64_t)M * H));
       MK_TRY(pf_gemm(h, W(6, l), F, H, M, Y, 2 * F));
       MK_TRY(pf_gemm(h, W(7, l), F, H, M, Y + F, 2 * F));
-      HIP_TRY(pf_swiglu_split(s, Pp, Y, M, h->pf_hi, h->pf_lo));
+      HIP_TRY(pf_swiglu_split(s, Pp, Y, M, ops, ops + (int64_t)M * F));
       MK_TRY(pf_gemm(h, W(8, l), H, F, M, Y, H));
     }
     if (p0 + c == P) {
-      HIP_TRY(pf_add_norm_split(s, Pp, X, Y, H, Pp.final_norm, B, c, c - 1, h->pf_hi, h->pf_lo));
+      HIP_TRY(pf_add_norm_split(s, Pp, X, Y, H, Pp.final_norm, B, c, c - 1, ops, ops + (int64_t)B * H));
       float* lg = d_logits ? d_logits : h->pf_logits;
-      MK_TRY(pf_gemm(h, Pp.tied ? Pp.embed : Pp.lm_head, V, H, B, lg, V));
+      MK_TRY(pf_gemm(h, Pp.tied ? Pp.embed : Pp.lm_head, V, H, B, h->pf_logits, V, lg, V));
       HIP_TRY(pf_argmax(s, Pp, lg, B, d_next));
     }
   }

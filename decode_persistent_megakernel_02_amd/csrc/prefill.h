@@ -27,6 +27,9 @@ hipError_t pf_attention(hipStream_t s, const Params& P, int l, const float* QKV,
                         uint16_t* hi, uint16_t* lo);
 // h = silu(gate) * up for GU = [gate | up] (row stride 2F), as hi/lo planes [rows][F].
 hipError_t pf_swiglu_split(hipStream_t s, const Params& P, const float* GU, int rows, uint16_t* hi, uint16_t* lo);
+// dst[r][c] = src[r][c] + src[off + r][c] (off 0: a copy) for r < rows, c < n;
+// row strides lds, ldd; dst may be src.
+hipError_t pf_fold(hipStream_t s, const float* src, int lds, int off, float* dst, int ldd, int rows, int n);
 // next[b] = first index of the largest of logits[b][0, V).
 hipError_t pf_argmax(hipStream_t s, const Params& P, const float* logits, int B, int32_t* next);
 // LDS bytes of the attention kernel by head dim; registers its limit.

@@ -385,6 +385,18 @@ __global__ __launch_bounds__(kT) void k_swiglu_split(Params P, const float* GU, 
   for (int k = threadIdx.x; k < F; k += kT) split_store(hi, lo, (int64_t)r * F + k, silu(g[k]) * g[F + k]);
 }
 
+__global__ __launch_bounds__(kT) void k_fold(const float* src, int lds, int off, float* dst, int ldd, int n) {
+  const int r = blockIdx.x;
+  const float* a = src + (int64_t)r * lds;
+  float* d = dst + (int64_t)r * ldd;
+  if (off) {
+    const float* b = src + (int64_t)(r + off) * lds;
+    for (int c = threadIdx.x; c < n; c += kT) d[c] = a[c] + b[c];
+  } else {
+    for (int c = threadIdx.x; c < n; c += kT) d[c] = a[c];
+  }
+}
+
 __global__ __launch_bounds__(kT) void k_argmax(Params P, const float* logits, int32_t* next) {
   __shared__ unsigned long long red[kT / 64];
   const int b = blockIdx.x;
@@ -460,6 +472,11 @@ hipError_t pf_attention(hipStream_t s, const Params& P, int l, const float* QKV,
 
 hipError_t pf_swiglu_split(hipStream_t s, const Params& P, const float* GU, int rows, uint16_t* hi, uint16_t* lo) {
   k_swiglu_split<<<dim3(rows), dim3(kT), 0, s>>>(P, GU, hi, lo);
+  return hipGetLastError();
+}
+
+hipError_t pf_fold(hipStream_t s, const float* src, int lds, int off, float* dst, int ldd, int rows, int n) {
+  k_fold<<<dim3(rows), dim3(kT), 0, s>>>(src, lds, off, dst, ldd, n);
   return hipGetLastError();
 }
 

@@ -68,12 +68,14 @@ def test_single_sequence_then_decode(abi, shape, kv_bf16, mode):
     print(f"[prefill] max rel err {max(errs):.2e}", flush=True)
 
 
-@pytest.mark.parametrize("rows", [1, 5, 64, 4096])
-def test_cache_matches_oracle(abi, rows):
-    """The fp32 cache after a batched prefill of 67 positions against the
-    oracle's rotated keys and values, every layer and position; chunk sizes
-    from one position per chunk to the whole prompt in one."""
-    shape, P = MINI_HD128_G2, 67
+@pytest.mark.parametrize("P,rows", [(67, 1), (67, 5), (67, 64), (67, 4096), (1100, 600)])
+def test_cache_matches_oracle(abi, P, rows):
+    """The fp32 cache after a batched prefill against the oracle's rotated
+    keys and values, every layer and position; chunk sizes from one position
+    per chunk to the whole prompt in one.  Chunks of up to 512 rows run each
+    projection as one GEMM over the stacked operand parts, larger ones as two
+    (1100 positions in chunks of 600: one of each)."""
+    shape = MINI_HD128_G2
     case = Case(shape, P, PER_OP, seed=12, random_norms=True, flags=abi.MK_FLAG_BATCHED_PREFILL)
     abi.mk_t_set_prefill_rows(case.h, rows)
     prompt = gen.tokens(23, 3, 0, P, shape.vocab)
