@@ -32,7 +32,6 @@ constexpr int kAttnFullWaves = 8;     // waves of the whole-context attention ke
 constexpr int kLocalSlots = 64;       // per-CU LDS counters for aggregated event signals
 constexpr int kMaxBatch = 64;         // sequences per step
 constexpr int kPrefillRows = 4096;    // batched prefill: rows (sequence x position) per chunk
-constexpr int kPrefillStack = 512;    // batched prefill: up to this many rows, one GEMM over both operand parts
 constexpr int kMaxTasksPerWave = 64; // GEMV results a wave of a per-operator kernel holds in LDS (<= wave size:
                                       // lane j runs the epilogue of task j)
 constexpr int kBgemmWaves = 4;        // waves per workgroup of the batched (MFMA) projections

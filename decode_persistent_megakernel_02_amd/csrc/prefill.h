@@ -10,6 +10,8 @@
 
 namespace mk {
 
+constexpr int kPrefillStack = 512;  // up to this many rows a projection is one GEMM over both operand parts
+
 // X[r] = embedding row of the token of row r (tokens[b tok_stride + p0 + i]).
 hipError_t pf_embed(hipStream_t s, const Params& P, const int32_t* tokens, int tok_stride, int B, int c, int p0,
                     float* X);
