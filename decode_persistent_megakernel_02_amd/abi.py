@@ -12,13 +12,14 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(PKG, "libmk.so")  # MK_LIBRARY: another build of the library
 
-MK_ABI_VERSION = 1
+MK_ABI_VERSION = 2
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_OUT_OF_MEMORY, MK_ERR_HIP = 0, -1, -2, -3
 MK_ERR_CAPACITY, MK_ERR_TIMEOUT, MK_ERR_STATE, MK_ERR_UNSUPPORTED = -4, -5, -6, -7
 MK_MODE_MEGAKERNEL, MK_MODE_PER_OP = 0, 1
 MK_FLAG_TRACE, MK_FLAG_POISON, MK_FLAG_NO_GRAPH, MK_FLAG_FUSED_MERGE, MK_FLAG_TILED_WEIGHTS = 1, 2, 4, 8, 16
 MK_FLAG_SPIN_LIMIT_1 = 32
 MK_FLAG_BATCHED_PREFILL = 64
+MK_FLAG_SHUFFLE = 128
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_OUT_OF_MEMORY", -3: "MK_ERR_HIP",
                 -4: "MK_ERR_CAPACITY", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE", -7: "MK_ERR_UNSUPPORTED"}
 
@@ -36,7 +37,7 @@ class mk_config(ctypes.Structure):
                 ("rope_theta", ctypes.c_float), ("tie_embeddings", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_seq", ctypes.c_int32), ("mode", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("watchdog_ms", ctypes.c_uint32), ("num_cus", ctypes.c_int32), ("attn_split", ctypes.c_int32),
-                ("kv_fp32", ctypes.c_int32)]
+                ("kv_fp32", ctypes.c_int32), ("debug_seed", ctypes.c_uint32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -92,6 +93,7 @@ SIGNATURES = {
     "mk_destroy": ([_P], None),
     "mk_graph_inspect": ([ctypes.POINTER(mk_config), _I32, ctypes.POINTER(mk_graph_info)], _I32),
     "mk_graph_simulate": ([ctypes.POINTER(mk_config), _I32, _U64, _I32, _I32, ctypes.POINTER(mk_sim_result)], _I32),
+    "mk_batched_graph_fault": ([ctypes.POINTER(mk_config), _I32, _I32], _I32),
     "mk_graph_export": ([ctypes.POINTER(mk_config), _I32, _P, _P, _I32, ctypes.POINTER(_I32)], _I32),
     "mk_get_debug_view": ([_P, ctypes.POINTER(mk_debug_view)], _I32),
     "mk_read_status": ([_P, ctypes.POINTER(ctypes.c_uint32)], _I32),
@@ -151,7 +153,7 @@ def _stream(stream):
 
 
 def make_config(shape, max_seq, max_batch=1, mode=MK_MODE_PER_OP, flags=0, watchdog_ms=0, num_cus=0,
-                attn_split=0, kv_fp32=True) -> mk_config:
+                attn_split=0, kv_fp32=True, debug_seed=0) -> mk_config:
     """mk_config from a synth.presets.ModelShape-like object."""
     c = mk_config()
     c.abi_version = MK_ABI_VERSION
@@ -162,6 +164,7 @@ def make_config(shape, max_seq, max_batch=1, mode=MK_MODE_PER_OP, flags=0, watch
     c.max_batch, c.max_seq, c.mode, c.flags = max_batch, max_seq, mode, flags
     c.watchdog_ms, c.num_cus, c.attn_split = watchdog_ms, num_cus, attn_split
     c.kv_fp32 = 1 if kv_fp32 else 0
+    c.debug_seed = debug_seed
     return c
 
 
@@ -249,6 +252,11 @@ def mk_graph_inspect(cfg: mk_config, ncu: int) -> mk_graph_info:
     out = mk_graph_info()
     _check(lib.mk_graph_inspect(ctypes.byref(cfg), ncu, ctypes.byref(out)), "mk_graph_inspect")
     return out
+
+
+def mk_batched_graph_fault(cfg: mk_config, ncu: int, fault: int) -> None:
+    """Raises MkError(MK_ERR_INVALID_ARG) when the validator catches the planted mistake."""
+    _check(lib.mk_batched_graph_fault(ctypes.byref(cfg), ncu, fault), "mk_batched_graph_fault")
 
 
 def mk_graph_simulate(cfg: mk_config, ncu: int, seed: int, workers: int = 7, drop_event: int = -1) -> mk_sim_result:

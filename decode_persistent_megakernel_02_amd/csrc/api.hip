@@ -67,10 +67,11 @@ int mega_split(int max_seq, int nkv, int ncu, int hd, bool f32) {
 }
 
 // The megakernel instance for a shape: exact (no clamped loads) when every
-// GEMV operator's K is a multiple of 2048; by head_dim, cache type and query
+// GEMV operator's K is a multiple of 2048 and the task order is not shuffled
+// (only the generic instances rotate it); by head_dim, cache type and query
 // heads per KV head (1, 2, 4, 8).
-const void* mega_kernel(int H, int qd, int F, int hd, bool f32, int G) {
-  const bool exact = H % 2048 == 0 && qd % 2048 == 0 && F % 2048 == 0 && G == 4;
+const void* mega_kernel(int H, int qd, int F, int hd, bool f32, int G, bool shuffle) {
+  const bool exact = H % 2048 == 0 && qd % 2048 == 0 && F % 2048 == 0 && G == 4 && !shuffle;
 #define MK_K(X, HD, KN, G) reinterpret_cast<const void*>(&mk_mega_##X##_##HD##_##KN##_g##G)
   if (exact) {
     if (hd == 64) return f32 ? MK_K(x, 64, f32, 4) : MK_K(x, 64, bf16, 4);
@@ -106,6 +107,8 @@ std::string check_config(const mk_config* c) {
   if (c->attn_split < 0 || c->attn_split > kMaxSplit) return "attn_split must be in [0, 4096]";
   if (c->num_cus < 0) return "num_cus must be >= 0";
   if ((int64_t)c->vocab * c->hidden >= (1ll << 40)) return "vocab * hidden too large";
+  if ((c->flags & MK_FLAG_SHUFFLE) && (c->mode != MK_MODE_MEGAKERNEL || c->max_batch != 1))
+    return "MK_FLAG_SHUFFLE reorders the megakernel's task dealing (megakernel mode, max_batch 1)";
   if (c->flags & MK_FLAG_TILED_WEIGHTS) {
     if (c->max_batch < 2) return "tiled weights are read by the batched path only (max_batch >= 2)";
     const int qd = c->n_q_heads * c->head_dim, kd = c->n_kv_heads * c->head_dim;
@@ -163,7 +166,8 @@ struct mk_handle {
   mk_config cfg{};
   hipStream_t stream = nullptr;
   int device = 0;
-  Graph graph;
+  Graph graph;         // single sequence: the task graph (per-CU queues, events)
+  BatchedGraph bgraph; // B >= 2: the stages of the matrix-core launch plan
   Params P{};
   std::vector<void*> allocs;
   int page_floats = 0, lds_mega = 0;  // megakernel: input page floats, LDS bytes
@@ -378,6 +382,29 @@ int bgemm_splits(const Params& P, int type, int ncu) {
   return (nch + per - 1) / per;
 }
 
+// The tiling of every batched projection, from the helpers above (the same
+// values the launches use), for the batched task graph.
+BatchedConfig batched_config(const mk_config* c, int ncu, int nsplit) {
+  Params P{};
+  P.L = c->n_layers; P.H = c->hidden; P.nq = c->n_q_heads; P.nkv = c->n_kv_heads; P.hd = c->head_dim;
+  P.F = c->ffn; P.V = c->vocab; P.B = c->max_batch; P.ncu = ncu; P.nsplit = nsplit;
+  BatchedConfig bc{};
+  bc.L = P.L; bc.H = P.H; bc.nq = P.nq; bc.nkv = P.nkv; bc.hd = P.hd; bc.F = P.F; bc.V = P.V; bc.B = P.B;
+  bc.nsplit = nsplit;
+  bc.fused_merge = (c->flags & MK_FLAG_FUSED_MERGE) != 0;
+  for (int t : {TT_QKV, TT_O, TT_GU, TT_DOWN, TT_LM}) {
+    BGemm& m = bc.gemm[t];
+    m.groups = bgemm_groups(P, t);
+    m.per_block = kBgemmWaves * bgemm_gpw(P, t);
+    m.blocks = bgemm_blocks(P, t);
+    m.splits = bgemm_splits(P, t, ncu);
+    m.chunk_cols = kBChunkCols[batch_tiles(P.B)];
+    m.K = bgemm_k(P, t);
+    m.N = t == TT_QKV ? (P.nq + 2 * P.nkv) * P.hd : t == TT_GU ? P.F : t == TT_LM ? P.V : P.H;
+  }
+  return bc;
+}
+
 const void* bfin_kernel(int type) {
   switch (type) {
     case TT_QKV: return reinterpret_cast<const void*>(&mk_b_fin_qkv);
@@ -414,47 +441,59 @@ mk_status enqueue_batched(mk_handle* h, hipStream_t st, bool timed_ok) {
     }
     return MK_OK;
   };
-  auto norm = [&](int layer, int kind) -> mk_status {
-    void* args[] = {&Pc, &sp, &layer, &kind};
-    return launch(0, reinterpret_cast<const void*>(&mk_b_norm), dim3(Pc.B), dim3(kNormThreads), args, 0);
-  };
-  auto gemm = [&](int type, int layer) -> mk_status {
-    const int ks = bgemm_splits(Pc, type, Pc.ncu);
-    const int ngx = bgemm_blocks(Pc, type);
-    void* args[] = {&Pc, &sp, &layer};
-    const void* fn = bgemm_kernel(type, bt, tiled_ops(h, type), bgemm_gpw(Pc, type));
-    MK_TRY(launch(type, fn, dim3(ngx, ks), dim3(kBgemmWaves * kWave), args, (size_t)bgemm_lds(bt)));
-    if (ks == 1) return MK_OK;
-    int k = ks;
-    void* fargs[] = {&Pc, &sp, &layer, &k};
-    return launch(type, bfin_kernel(type), dim3(bgemm_groups(Pc, type)), dim3(16 * Pc.Bp), fargs, 0);  // 16 * Bp <= 1024
-  };
-  for (int l = 0; l < Pc.L; ++l) {
-    MK_TRY(norm(l, 0));
-    MK_TRY(gemm(TT_QKV, l));
-    if (single_split(h)) {
-      int layer = l;
-      void* args[] = {&Pc, &sp, &layer};
-      MK_TRY(launch(TT_ATTN, attn_full_kernel(Pc.kv_f32, Pc.nq / Pc.nkv), dim3(Pc.B * Pc.nkv),
-                    dim3(kAttnFullWaves * kWave), args, (size_t)h->attn_full_lds));
-    } else {
-      int layer = l, fuse = fused_merge(h) ? 1 : 0;
-      void* args[] = {&Pc, &sp, &layer, &fuse};
-      MK_TRY(launch(TT_ATTN, attn_split_kernel(Pc.kv_f32, Pc.nq / Pc.nkv), dim3(Pc.B * Pc.nkv * Pc.nsplit),
-                    dim3(kAttnWaves * kWave), args, (size_t)h->attn_lds));
-      if (!fuse)
-        MK_TRY(launch(TT_MERGE, reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(Pc.B * Pc.nkv),
+  // One launch per stage of the batched task graph, its grid the stage's task
+  // grid (validated at create against the buffers every stage reads and writes).
+  const BatchedGraph& g = h->bgraph;
+  for (const BStage& s : g.stages) {
+    int layer = s.layer;
+    switch (s.kind) {
+      case BK_NORM: {
+        int kind = s.sub;
+        void* args[] = {&Pc, &sp, &layer, &kind};
+        MK_TRY(launch(0, reinterpret_cast<const void*>(&mk_b_norm), dim3(s.gx), dim3(kNormThreads), args, 0));
+        break;
+      }
+      case BK_GEMM: {
+        void* args[] = {&Pc, &sp, &layer};
+        const void* fn = bgemm_kernel(s.type, bt, tiled_ops(h, s.type), bgemm_gpw(Pc, s.type));
+        MK_TRY(launch(s.type, fn, dim3(s.gx, s.gy), dim3(kBgemmWaves * kWave), args, (size_t)bgemm_lds(bt)));
+        break;
+      }
+      case BK_FIN: {
+        int k = g.cfg.gemm[s.type].splits;
+        void* args[] = {&Pc, &sp, &layer, &k};
+        MK_TRY(launch(s.type, bfin_kernel(s.type), dim3(s.gx), dim3(16 * Pc.Bp), args, 0));  // 16 * Bp <= 1024
+        break;
+      }
+      case BK_ATTN_FULL: {
+        void* args[] = {&Pc, &sp, &layer};
+        MK_TRY(launch(TT_ATTN, attn_full_kernel(Pc.kv_f32, Pc.nq / Pc.nkv), dim3(s.gx),
+                      dim3(kAttnFullWaves * kWave), args, (size_t)h->attn_full_lds));
+        break;
+      }
+      case BK_ATTN: {
+        int fuse = g.cfg.fused_merge ? 1 : 0;
+        void* args[] = {&Pc, &sp, &layer, &fuse};
+        MK_TRY(launch(TT_ATTN, attn_split_kernel(Pc.kv_f32, Pc.nq / Pc.nkv), dim3(s.gx), dim3(kAttnWaves * kWave),
+                      args, (size_t)h->attn_lds));
+        break;
+      }
+      case BK_MERGE: {
+        if (s.gx == 0) break;  // merged by the attention launch's last workgroups
+        int fuse = 0;
+        void* args[] = {&Pc, &sp, &layer, &fuse};
+        MK_TRY(launch(TT_MERGE, reinterpret_cast<const void*>(&mk_op_attn_merge), dim3(s.gx),
                       dim3((Pc.nq / Pc.nkv) * kWave), args, 0));
+        break;
+      }
+      default: {
+        void* args[] = {&Pc, &sp};
+        MK_TRY(launch(TT_ARGMAX, reinterpret_cast<const void*>(&mk_b_argmax), dim3(1), dim3(kMaxBatch), args, 0));
+        break;
+      }
     }
-    MK_TRY(gemm(TT_O, l));
-    MK_TRY(norm(l, 1));
-    MK_TRY(gemm(TT_GU, l));
-    MK_TRY(gemm(TT_DOWN, l));
   }
-  MK_TRY(norm(Pc.L, 2));
-  MK_TRY(gemm(TT_LM, Pc.L));
-  void* args[] = {&Pc, &sp};
-  return launch(TT_ARGMAX, reinterpret_cast<const void*>(&mk_b_argmax), dim3(1), dim3(kMaxBatch), args, 0);
+  return MK_OK;
 }
 
 // Launch arguments of the single-sequence operator `type` of `layer`.
@@ -658,9 +697,13 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
 
   const GraphConfig gc = graph_config(cfg, ncu);
   h->batched = cfg->max_batch > 1;
-  if (h->batched) {  // launches are issued per operator; no task table
+  if (h->batched) {  // launches are issued per operator, stage by stage of the batched graph
     h->graph.cfg = gc;
     h->graph.nsplit = (cfg->max_seq + gc.split - 1) / gc.split;
+    std::string e = build_batched_graph(batched_config(cfg, ncu, h->graph.nsplit), h->bgraph);
+    if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
+    e = validate_batched_graph(h->bgraph);
+    if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "batched graph validation: " + e);
   } else {
     std::string e = build_graph(gc, h->graph);
     if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
@@ -682,6 +725,13 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   // this limit trips only if the wall clock stops advancing.
   P.spin_limit = (uint32_t)std::min(4.0e9, wd_ms * 1000.0 * 50.0);
   if (cfg->flags & MK_FLAG_SPIN_LIMIT_1) P.spin_limit = 1;
+  P.shuffle_seed = 0;
+  if (cfg->flags & MK_FLAG_SHUFFLE) {  // splitmix64 of the caller's seed, made nonzero
+    uint64_t z = (uint64_t)cfg->debug_seed + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    P.shuffle_seed = (uint32_t)(z ^ (z >> 31)) | 1u;
+  }
   P.embed = static_cast<const uint16_t*>(w->embed);
   P.lm_head = static_cast<const uint16_t*>(w->lm_head);
   P.final_norm = static_cast<const uint16_t*>(w->final_norm);
@@ -822,7 +872,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
       if ((c + ncu * kMegaCompute - 1) / (ncu * kMegaCompute) > 64)
         return fail(MK_ERR_UNSUPPORTED, "MK_MODE_MEGAKERNEL: an operator has more than 64 tasks per compute wave "
                                         "on this many CUs");
-    h->mega_fn = mega_kernel(H, nq * hd, F, hd, P.kv_f32 != 0, G);
+    h->mega_fn = mega_kernel(H, nq * hd, F, hd, P.kv_f32 != 0, G, (cfg->flags & MK_FLAG_SHUFFLE) != 0);
     if (!h->mega_fn) return fail(MK_ERR_UNSUPPORTED, "no megakernel instance for this shape");
   }
   if (!h->batched) {
@@ -1200,9 +1250,29 @@ mk_status mk_graph_inspect(const mk_config* cfg, int32_t ncu, mk_graph_info* out
   if (!cerr.empty()) return fail(MK_ERR_INVALID_ARG, cerr);
   if (ncu < 1 || !out) return fail(MK_ERR_INVALID_ARG, "ncu < 1 or out NULL");
   const GraphConfig gc = graph_config(cfg, ncu);
+  if (cfg->max_batch > 1) {  // the batched launch plan: stages of tasks
+    BatchedGraph bg;
+    std::string e = build_batched_graph(batched_config(cfg, ncu, (cfg->max_seq + gc.split - 1) / gc.split), bg);
+    if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
+    e = validate_batched_graph(bg);
+    if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "batched graph validation: " + e);
+    *out = mk_graph_info{};
+    out->n_tasks = (int32_t)bg.tasks.size();
+    out->n_stages = (int32_t)bg.stages.size();
+    out->ncu = ncu;
+    out->nsplit = bg.cfg.nsplit;
+    out->split = gc.split;
+    out->min_queue = 1 << 30;
+    for (const BStage& s : bg.stages) {  // per launch: workgroups (tasks) of the stage
+      out->max_queue = std::max(out->max_queue, s.count);
+      out->min_queue = std::min(out->min_queue, s.count);
+    }
+    out->weight_bytes = batched_weight_bytes(bg);
+    return MK_OK;
+  }
   Graph g;
   std::string e = build_graph(gc, g);
-  if (!e.empty()) return fail(cfg->max_batch > 1 ? MK_ERR_UNSUPPORTED : MK_ERR_INVALID_ARG, e);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
   e = validate_graph(g);
   if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "graph validation: " + e);
   e = check_op_tasks(g);
@@ -1228,6 +1298,75 @@ mk_status mk_graph_inspect(const mk_config* cfg, int32_t ncu, mk_graph_info* out
     out->min_cu_bytes = std::min(out->min_cu_bytes, bytes);
     out->weight_bytes += bytes;
   }
+  return MK_OK;
+}
+
+mk_status mk_batched_graph_fault(const mk_config* cfg, int32_t ncu, int32_t fault) {
+  g_err.clear();
+  const std::string cerr = check_config(cfg);
+  if (!cerr.empty()) return fail(MK_ERR_INVALID_ARG, cerr);
+  if (ncu < 1 || cfg->max_batch < 2) return fail(MK_ERR_INVALID_ARG, "ncu < 1 or max_batch < 2");
+  const GraphConfig gc = graph_config(cfg, ncu);
+  BatchedGraph g;
+  std::string e = build_batched_graph(batched_config(cfg, ncu, (cfg->max_seq + gc.split - 1) / gc.split), g);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, e);
+  auto find = [&](uint8_t kind, int type, int from) {
+    for (int s = from; s < (int)g.stages.size(); ++s)
+      if (g.stages[s].kind == kind && (type < 0 || g.stages[s].type == type)) return s;
+    return -1;
+  };
+  switch (fault) {
+    case 1: {  // a projection workgroup computes its neighbour's row block
+      int s = -1;
+      for (int t : {TT_QKV, TT_O, TT_GU, TT_DOWN, TT_LM})
+        if (s < 0 && g.cfg.gemm[t].blocks > 1) s = find(BK_GEMM, t, 0);
+      if (s < 0) return fail(MK_ERR_UNSUPPORTED, "no projection with two row blocks");
+      BTask& t = g.tasks[g.stages[s].first + 1];
+      t.a0 = g.tasks[g.stages[s].first].a0;
+      break;
+    }
+    case 2: {  // a finishing task takes its neighbour's row group
+      const int s = find(BK_FIN, -1, 0);
+      if (s < 0 || g.stages[s].count < 2) return fail(MK_ERR_UNSUPPORTED, "no split projection");
+      g.tasks[g.stages[s].first + 1].a0 = g.tasks[g.stages[s].first].a0;
+      break;
+    }
+    case 3: {  // the O projection runs before the attention output is complete
+      const int so = find(BK_GEMM, TT_O, 0);
+      if (so < 1) return fail(MK_ERR_UNSUPPORTED, "no O projection");
+      const int sp = so - 1;  // the stage before it (the merge, or the attention itself)
+      std::vector<BTask> moved;
+      for (int i = g.stages[so].first; i < g.stages[so].first + g.stages[so].count; ++i) moved.push_back(g.tasks[i]);
+      std::vector<BTask> prev(g.tasks.begin() + g.stages[sp].first,
+                              g.tasks.begin() + g.stages[sp].first + g.stages[sp].count);
+      const int first = g.stages[sp].first;
+      for (auto& t : moved) t.stage = sp;
+      for (auto& t : prev) t.stage = so;
+      std::copy(moved.begin(), moved.end(), g.tasks.begin() + first);
+      std::copy(prev.begin(), prev.end(), g.tasks.begin() + first + (int)moved.size());
+      std::swap(g.stages[so], g.stages[sp]);
+      g.stages[sp].first = first;
+      g.stages[so].first = first + (int)moved.size();
+      break;
+    }
+    case 4: {  // the down projection's finishing launch expects one more K split
+      if (g.cfg.gemm[TT_DOWN].splits < 2) return fail(MK_ERR_UNSUPPORTED, "down projection not split");
+      g.cfg.gemm[TT_DOWN].splits += 1;
+      // the projection stages keep the workgroups that ran: re-derive only the finishing reads
+      for (auto& s : g.stages)
+        if (s.kind == BK_GEMM && s.type == TT_DOWN) s.gy = g.cfg.gemm[TT_DOWN].splits - 1;
+      break;
+    }
+    case 5: {  // the last attention split of a KV head repeats the first
+      const int s = find(BK_ATTN, -1, 0);
+      if (s < 0 || g.cfg.nsplit < 2) return fail(MK_ERR_UNSUPPORTED, "attention not split");
+      g.tasks[g.stages[s].first + g.cfg.nsplit - 1].a1 = 0;
+      break;
+    }
+    default: return fail(MK_ERR_INVALID_ARG, "unknown fault");
+  }
+  e = validate_batched_graph(g);
+  if (!e.empty()) return fail(MK_ERR_INVALID_ARG, "batched graph validation: " + e);
   return MK_OK;
 }
 

@@ -514,4 +514,313 @@ SimResult simulate_graph(const Graph& g, uint64_t seed, int workers, int drop_ev
   return res;
 }
 
+// ---------------------------------------------------------------------------
+// Batched decode step: stages of tasks
+namespace {
+
+const int kBTypes[5] = {TT_QKV, TT_O, TT_GU, TT_DOWN, TT_LM};
+
+bool bad_gemm(const BGemm& m) {
+  return m.groups < 1 || m.per_block < 1 || m.blocks < 1 || m.splits < 1 || m.chunk_cols < 1 || m.K < 1 || m.N < 1 ||
+         (int64_t)m.blocks * m.per_block < m.groups || (int64_t)(m.blocks - 1) * m.per_block >= m.groups;
+}
+int gemm_chunks(const BGemm& m) { return (m.K + m.chunk_cols - 1) / m.chunk_cols; }
+int gemm_chunks_per_split(const BGemm& m) { return (gemm_chunks(m) + m.splits - 1) / m.splits; }
+
+}  // namespace
+
+std::string build_batched_graph(const BatchedConfig& c, BatchedGraph& g) {
+  if (c.B < 2) return "batched graph: B must be >= 2";
+  if (c.L < 1 || c.H < 8 || c.nq < 1 || c.nkv < 1 || c.F < 8 || c.V < 1 || c.nsplit < 1)
+    return "batched graph: non-positive dimension";
+  if (c.nq % c.nkv) return "batched graph: n_q_heads must be a multiple of n_kv_heads";
+  for (int t : kBTypes)
+    if (bad_gemm(c.gemm[t])) return fmt("batched graph: inconsistent tiling of operator %ld", t);
+  if (c.gemm[TT_LM].splits != 1) return "batched graph: the LM head is not split (its argmax runs in the epilogue)";
+  g = BatchedGraph();
+  g.cfg = c;
+  auto stage = [&](uint8_t kind, int type, int layer, int sub, int gx, int gy) {
+    g.stages.push_back(BStage{kind, (uint8_t)type, layer, sub, (int)g.tasks.size(), 0, gx, gy});
+  };
+  auto task = [&](uint8_t kind, int type, int layer, int b, int a0, int a1) {
+    g.tasks.push_back(BTask{(int)g.stages.size() - 1, kind, (uint8_t)type, layer, b, a0, a1});
+    g.stages.back().count++;
+  };
+  auto norm = [&](int layer, int kind) {
+    stage(BK_NORM, 0, layer, kind, c.B, 1);
+    for (int b = 0; b < c.B; ++b) task(BK_NORM, 0, layer, b, kind, 0);
+  };
+  auto gemm = [&](int type, int layer) {
+    const BGemm& m = c.gemm[type];
+    stage(BK_GEMM, type, layer, 0, m.blocks, m.splits);
+    for (int kz = 0; kz < m.splits; ++kz)
+      for (int bx = 0; bx < m.blocks; ++bx) task(BK_GEMM, type, layer, -1, bx, kz);
+    if (m.splits > 1) {
+      stage(BK_FIN, type, layer, 0, m.groups, 1);
+      for (int gr = 0; gr < m.groups; ++gr) task(BK_FIN, type, layer, -1, gr, 0);
+    }
+  };
+  for (int l = 0; l < c.L; ++l) {
+    norm(l, 0);
+    gemm(TT_QKV, l);
+    if (c.nsplit == 1) {
+      stage(BK_ATTN_FULL, 0, l, 0, c.B * c.nkv, 1);
+      for (int b = 0; b < c.B; ++b)
+        for (int grp = 0; grp < c.nkv; ++grp) task(BK_ATTN_FULL, 0, l, b, grp, 0);
+    } else {
+      stage(BK_ATTN, 0, l, 0, c.B * c.nkv * c.nsplit, 1);
+      for (int b = 0; b < c.B; ++b)
+        for (int grp = 0; grp < c.nkv; ++grp)
+          for (int sp = 0; sp < c.nsplit; ++sp) task(BK_ATTN, 0, l, b, grp, sp);
+      // fused: the last split workgroup of each (sequence, KV head) merges inside the attention launch
+      stage(BK_MERGE, 0, l, 0, c.fused_merge ? 0 : c.B * c.nkv, c.fused_merge ? 0 : 1);
+      for (int b = 0; b < c.B; ++b)
+        for (int grp = 0; grp < c.nkv; ++grp) task(BK_MERGE, 0, l, b, grp, 0);
+    }
+    gemm(TT_O, l);
+    norm(l, 1);
+    gemm(TT_GU, l);
+    gemm(TT_DOWN, l);
+  }
+  norm(c.L, 2);
+  gemm(TT_LM, c.L);
+  stage(BK_ARGMAX, 0, c.L, 0, 1, 1);
+  task(BK_ARGMAX, 0, c.L, -1, 0, 0);
+  return "";
+}
+
+namespace {
+
+enum BBuf { BB_XN, BB_Q, BB_K, BB_V, BB_REC, BB_AO, BB_XMID, BB_H, BB_X, BB_PART, BB_COV, BB_KEY, BB_OUT };
+struct BRegion {
+  int buf, l, b, sub, lo, hi;
+};
+using BKey = std::tuple<int, int, int, int>;
+
+// Output rows of row group gr of a batched projection (one or two ranges of
+// the operator's output buffer), clipped to the matrix.
+void group_rows(const BatchedConfig& c, int type, int gr, int& buf, int (&lo)[2], int (&hi)[2], int& n) {
+  n = 1;
+  switch (type) {
+    case TT_QKV: {
+      const int per_head = c.hd / 32, nqg = c.nq * per_head, nkg = c.nkv * per_head;
+      if (gr < nqg + nkg) {
+        const bool isq = gr < nqg;
+        const int gg = isq ? gr : gr - nqg, head = gg / per_head, i0 = (gg % per_head) * 16;
+        buf = isq ? BB_Q : BB_K;
+        lo[0] = head * c.hd + i0;
+        lo[1] = head * c.hd + c.hd / 2 + i0;
+        hi[0] = lo[0] + 16;
+        hi[1] = lo[1] + 16;
+        n = 2;
+      } else {
+        buf = BB_V;
+        lo[0] = (gr - nqg - nkg) * 32;
+        hi[0] = std::min(lo[0] + 32, c.nkv * c.hd);
+      }
+      return;
+    }
+    case TT_O: buf = BB_XMID; lo[0] = gr * 32; hi[0] = std::min(lo[0] + 32, c.H); return;
+    case TT_GU: buf = BB_H; lo[0] = gr * 16; hi[0] = std::min(lo[0] + 16, c.F); return;
+    case TT_DOWN: buf = BB_X; lo[0] = gr * 32; hi[0] = std::min(lo[0] + 32, c.H); return;
+    default: buf = BB_KEY; lo[0] = 0; hi[0] = 1; return;
+  }
+}
+
+void btask_regions(const BatchedGraph& g, const BTask& t, std::vector<BRegion>& rd, std::vector<BRegion>& wr) {
+  const auto& c = g.cfg;
+  const int G = c.nq / c.nkv, l = t.layer;
+  rd.clear();
+  wr.clear();
+  // epilogue of row group gr for every sequence: outputs, and the residual
+  // rows O and down add (layer 0's O residual is the embedding row)
+  auto outputs = [&](int type, int gr) {
+    int buf, lo[2], hi[2], n;
+    group_rows(c, type, gr, buf, lo, hi, n);
+    const int lo_l = type == TT_DOWN ? l + 1 : type == TT_LM ? 0 : l;
+    for (int b = 0; b < c.B; ++b)
+      for (int i = 0; i < n; ++i) {
+        if (lo[i] >= hi[i]) continue;
+        wr.push_back({buf, lo_l, b, 0, lo[i], hi[i]});
+        if (type == TT_O && l > 0) rd.push_back({BB_X, l, b, 0, lo[i], hi[i]});
+        if (type == TT_DOWN) rd.push_back({BB_XMID, l, b, 0, lo[i], hi[i]});
+      }
+  };
+  switch (t.kind) {
+    case BK_NORM: {
+      const int kind = t.a0;
+      if (kind == 0 && l > 0) rd.push_back({BB_X, l, t.b, 0, 0, c.H});
+      if (kind == 1) rd.push_back({BB_XMID, l, t.b, 0, 0, c.H});
+      if (kind == 2) rd.push_back({BB_X, c.L, t.b, 0, 0, c.H});
+      wr.push_back({BB_XN, l, t.b, kind, 0, c.H});
+      break;
+    }
+    case BK_GEMM: {
+      const BGemm& m = c.gemm[t.type];
+      const int nch = gemm_chunks(m), cps = gemm_chunks_per_split(m);
+      const int g0 = t.a0 * m.per_block, g1 = std::min(g0 + m.per_block, m.groups);
+      const int c0 = std::min(t.a1 * cps, nch), c1 = std::min(c0 + cps, nch);
+      const int k0 = c0 * m.chunk_cols, k1 = std::min(c1 * m.chunk_cols, m.K);
+      for (int b = 0; b < c.B; ++b) {
+        if (k0 >= k1) break;
+        if (t.type == TT_O) rd.push_back({BB_AO, l, b, 0, k0, k1});
+        else if (t.type == TT_DOWN) rd.push_back({BB_H, l, b, 0, k0, k1});
+        else rd.push_back({BB_XN, l, b, t.type == TT_GU ? 1 : t.type == TT_LM ? 2 : 0, k0, k1});
+      }
+      const int key = l * 16 + t.type;
+      for (int gr = g0; gr < g1; ++gr)
+        if (c0 < c1) wr.push_back({BB_COV, key, 0, 0, gr * nch + c0, gr * nch + c1});
+      if (m.splits == 1) {
+        for (int gr = g0; gr < g1; ++gr) outputs(t.type, gr);
+      } else if (g0 < g1) {
+        wr.push_back({BB_PART, key, 0, t.a1, g0, g1});
+      }
+      break;
+    }
+    case BK_FIN: {
+      const BGemm& m = c.gemm[t.type];
+      for (int kz = 0; kz < m.splits; ++kz) rd.push_back({BB_PART, l * 16 + t.type, 0, kz, t.a0, t.a0 + 1});
+      outputs(t.type, t.a0);
+      break;
+    }
+    case BK_ATTN:
+    case BK_ATTN_FULL:
+      rd.push_back({BB_Q, l, t.b, 0, t.a0 * G * c.hd, (t.a0 + 1) * G * c.hd});
+      rd.push_back({BB_K, l, t.b, 0, t.a0 * c.hd, (t.a0 + 1) * c.hd});
+      rd.push_back({BB_V, l, t.b, 0, t.a0 * c.hd, (t.a0 + 1) * c.hd});
+      if (t.kind == BK_ATTN) wr.push_back({BB_REC, l, t.b, t.a0, t.a1, t.a1 + 1});
+      else wr.push_back({BB_AO, l, t.b, 0, t.a0 * G * c.hd, (t.a0 + 1) * G * c.hd});
+      break;
+    case BK_MERGE:
+      rd.push_back({BB_REC, l, t.b, t.a0, 0, c.nsplit});
+      wr.push_back({BB_AO, l, t.b, 0, t.a0 * G * c.hd, (t.a0 + 1) * G * c.hd});
+      break;
+    case BK_ARGMAX:
+      for (int b = 0; b < c.B; ++b) rd.push_back({BB_KEY, 0, b, 0, 0, 1});
+      wr.push_back({BB_OUT, 0, 0, 0, 0, c.B});
+      break;
+  }
+}
+
+}  // namespace
+
+std::string validate_batched_graph(const BatchedGraph& g) {
+  const auto& c = g.cfg;
+  const int ns = (int)g.stages.size(), nt = (int)g.tasks.size();
+  // stages partition the tasks in order, and each launch grid holds its tasks
+  int next = 0;
+  for (int s = 0; s < ns; ++s) {
+    const BStage& st = g.stages[s];
+    if (st.first != next || st.count < 1) return fmt("stage %ld does not follow its predecessor", s);
+    next += st.count;
+    for (int i = st.first; i < st.first + st.count; ++i)
+      if (g.tasks[i].stage != s || g.tasks[i].kind != st.kind) return fmt("task %ld is not in stage %ld", i, s);
+    if (st.gx == 0) {  // merged inside the attention launch before it
+      if (st.kind != BK_MERGE || !c.fused_merge || s == 0 || g.stages[s - 1].kind != BK_ATTN)
+        return fmt("stage %ld has no launch of its own", s);
+    } else if ((int64_t)st.gx * st.gy != st.count) {
+      return fmt("stage %ld: grid %ld does not hold its %ld tasks", s, (long)st.gx * st.gy, st.count);
+    }
+  }
+  if (next != nt) return "tasks outside every stage";
+  // writes, keyed by buffer; element ranges of one key must not overlap
+  struct W { int lo, hi, stage; };
+  std::map<BKey, std::vector<W>> writes;
+  std::vector<BRegion> rd, wr;
+  for (const BTask& t : g.tasks) {
+    btask_regions(g, t, rd, wr);
+    for (auto& r : wr) writes[BKey(r.buf, r.l, r.b, r.sub)].push_back({r.lo, r.hi, t.stage});
+  }
+  for (auto& kv : writes) {
+    auto& v = kv.second;
+    std::sort(v.begin(), v.end(), [](const W& a, const W& b) { return a.lo < b.lo || (a.lo == b.lo && a.hi < b.hi); });
+    if (std::get<0>(kv.first) == BB_KEY) continue;  // a maximum over many writers
+    for (size_t i = 1; i < v.size(); ++i)
+      if (v[i].lo < v[i - 1].hi)
+        return fmt("buffer %ld (layer key %ld): element %ld written twice", std::get<0>(kv.first), std::get<1>(kv.first),
+                   v[i].lo);
+  }
+  // every written buffer complete (per sequence, per layer)
+  auto extent = [&](const BKey& k) -> int64_t {
+    const int buf = std::get<0>(k);
+    switch (buf) {
+      case BB_XN: case BB_XMID: case BB_X: return c.H;
+      case BB_Q: case BB_AO: return (int64_t)c.nq * c.hd;
+      case BB_K: case BB_V: return (int64_t)c.nkv * c.hd;
+      case BB_REC: return c.nsplit;
+      case BB_H: return c.F;
+      case BB_OUT: return c.B;
+      case BB_PART: return c.gemm[std::get<1>(k) % 16].groups;
+      case BB_COV: {
+        const BGemm& m = c.gemm[std::get<1>(k) % 16];
+        return (int64_t)m.groups * gemm_chunks(m);
+      }
+      default: return -1;
+    }
+  };
+  for (auto& kv : writes) {
+    const int64_t ext = extent(kv.first);
+    if (ext < 0) continue;
+    int64_t covered = 0;
+    for (auto& w : kv.second) covered += w.hi - w.lo;
+    if (covered != ext)
+      return fmt("buffer %ld (layer key %ld): %ld of %ld elements written", std::get<0>(kv.first),
+                 std::get<1>(kv.first), covered, ext);
+  }
+  // each sequence's every buffer of every layer exists
+  for (int l = 0; l < c.L; ++l)
+    for (int b = 0; b < c.B; ++b)
+      for (int buf : {BB_Q, BB_K, BB_V, BB_AO, BB_XMID, BB_H, BB_X})
+        if (!writes.count(BKey(buf, buf == BB_X ? l + 1 : l, b, 0)))
+          return fmt("layer %ld sequence %ld: buffer %ld never written", l, b, buf);
+  // reads: covered by writes of earlier stages
+  for (const BTask& t : g.tasks) {
+    btask_regions(g, t, rd, wr);
+    for (auto& r : rd) {
+      auto it = writes.find(BKey(r.buf, r.l, r.b, r.sub));
+      if (it == writes.end()) return fmt("task %ld reads a buffer nobody writes (buf %ld)", (long)(&t - &g.tasks[0]), r.buf);
+      int cur = r.lo;
+      for (const W& w : it->second) {
+        if (w.hi <= cur) continue;
+        if (w.lo >= r.hi) break;
+        if (w.lo > cur) break;  // gap
+        if (w.stage >= t.stage)
+          return fmt("task %ld reads buffer %ld written by stage %ld, not before it", (long)(&t - &g.tasks[0]), r.buf,
+                     w.stage);
+        cur = std::max(cur, w.hi);
+        if (cur >= r.hi) break;
+      }
+      if (r.buf != BB_KEY && cur < r.hi)
+        return fmt("task %ld reads elements [%ld, %ld) of buffer %ld that no task writes", (long)(&t - &g.tasks[0]), cur,
+                   r.hi, r.buf);
+    }
+  }
+  return "";
+}
+
+int64_t batched_weight_bytes(const BatchedGraph& g) {
+  const auto& c = g.cfg;
+  int64_t bytes = 0;
+  for (const BTask& t : g.tasks) {
+    if (t.kind != BK_GEMM) continue;
+    const BGemm& m = c.gemm[t.type];
+    const int nch = gemm_chunks(m), cps = gemm_chunks_per_split(m);
+    const int c0 = std::min(t.a1 * cps, nch), c1 = std::min(c0 + cps, nch);
+    const int64_t cols = std::max(0, std::min(c1 * m.chunk_cols, m.K) - c0 * m.chunk_cols);
+    const int g0 = t.a0 * m.per_block, g1 = std::min(g0 + m.per_block, m.groups);
+    for (int gr = g0; gr < g1; ++gr) {
+      int buf, lo[2], hi[2], n;
+      if (t.type == TT_LM) {
+        lo[0] = gr * 32; hi[0] = std::min(lo[0] + 32, c.V); n = 1;
+      } else {
+        group_rows(c, t.type, gr, buf, lo, hi, n);
+      }
+      int64_t rows = 0;
+      for (int i = 0; i < n; ++i) rows += std::max(0, hi[i] - lo[i]);
+      bytes += rows * cols * 2 * (t.type == TT_GU ? 2 : 1);
+    }
+  }
+  return bytes;
+}
+
 }  // namespace mk

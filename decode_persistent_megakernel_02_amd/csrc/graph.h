@@ -62,4 +62,62 @@ struct SimResult {
 // (fault injection: the run must then report a deadlock on it).
 SimResult simulate_graph(const Graph& g, uint64_t seed, int workers, int drop_event);
 
+// ---------------------------------------------------------------------------
+// Batched decode step (B >= 2 sequences).  Every operator runs on the matrix
+// cores as launches of its own, so the task graph is a sequence of stages: a
+// stage's tasks read only what earlier stages wrote (stream order is the
+// dependency), and each stage is one launch whose grid is the stage's task
+// grid.  The tiling comes from the same helpers the launches use; the graph
+// is built and validated at create, and the step's launches are issued from
+// it.
+enum BKind : uint8_t { BK_NORM = 1, BK_GEMM, BK_FIN, BK_ATTN, BK_ATTN_FULL, BK_MERGE, BK_ARGMAX };
+
+struct BGemm {     // tiling of one batched projection
+  int groups;      // row groups: two 16-row tiles (gate/up: the same 16 rows of both matrices)
+  int per_block;   // row groups per workgroup
+  int blocks;      // workgroups along the rows
+  int splits;      // workgroups along K (1: the epilogue runs in the projection launch)
+  int chunk_cols;  // K columns per activation chunk
+  int K, N;        // contraction length, output rows
+};
+
+struct BatchedConfig {
+  int L, H, nq, nkv, hd, F, V, B, nsplit;
+  bool fused_merge;  // the last split workgroup of each (sequence, KV head) merges (no merge launch)
+  BGemm gemm[9];     // by operator type (TT_QKV, TT_O, TT_GU, TT_DOWN, TT_LM)
+};
+
+struct BTask {
+  int stage;
+  uint8_t kind, type;  // BK_*, operator type of GEMM / FIN tasks
+  int layer, b;        // b: sequence (-1: every sequence)
+  int a0, a1;          // GEMM: row block, K split; FIN: row group; ATTN: KV head, split; MERGE: KV head;
+                       // NORM: 0 attention, 1 FFN, 2 final
+};
+
+struct BStage {
+  uint8_t kind, type;
+  int layer, sub;   // sub: NORM kind
+  int first, count; // tasks [first, first + count)
+  int gx, gy;       // launch grid in workgroups (0 x 0: done inside the previous launch)
+};
+
+struct BatchedGraph {
+  BatchedConfig cfg;
+  std::vector<BTask> tasks;
+  std::vector<BStage> stages;
+};
+
+std::string build_batched_graph(const BatchedConfig& cfg, BatchedGraph& g);
+
+// Every projection's (row group, K chunk) pairs covered once; every output
+// element (per sequence) written exactly once per step; every split partial
+// written once and read by its finishing task; every element a task reads
+// written by an earlier stage.
+std::string validate_batched_graph(const BatchedGraph& g);
+
+// Weight bytes the GEMM tasks of the graph stream (bf16), for checking that
+// the tiling reads every weight once.
+int64_t batched_weight_bytes(const BatchedGraph& g);
+
 }  // namespace mk

@@ -186,7 +186,9 @@ __device__ __forceinline__ uint32_t free_for(int k) { return (uint32_t)NC * (uin
 // to within one (in runs of several tasks, an operator with 1.5 runs per
 // workgroup -- QKV at the 8B shape -- gave half the workgroups twice the
 // tasks of the others).
-__device__ __forceinline__ int mslot(uint32_t p, int count) {
+// rot (0 <= rot < count) rotates the task list: slot p then runs task
+// (t + rot) mod count instead of t (MK_FLAG_SHUFFLE; 0 otherwise).
+__device__ __forceinline__ int mslot_plain(uint32_t p, int count) {
   const int n = gridDim.x;
   if (n % kXcds) {
     const int t = (int)p * n + (int)blockIdx.x;
@@ -195,6 +197,29 @@ __device__ __forceinline__ int mslot(uint32_t p, int count) {
   const int per = (count + kXcds - 1) / kXcds, x = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
   const int t = (int)p * (n / kXcds) + j;
   return t < per && x * per + t < count ? x * per + t : count;
+}
+__device__ __forceinline__ int mslot(uint32_t p, int count, int rot) {
+  int t = mslot_plain(p, count);
+  if (rot == 0 || t >= count) return t;
+  t += rot;
+  return t < count ? t : t - count;
+}
+
+// The rotation of operator k's task list in the step with this epoch: 0, or
+// in the shuffling instances (SHUF, MK_FLAG_SHUFFLE) a hash of (seed, epoch,
+// k) reduced mod count (the 32-bit "lowbias32" integer mixer published by C.
+// Wellons).  The production instances are compiled without it.
+template <bool SHUF>
+__device__ __forceinline__ int op_rot(const Params& P, int k, uint32_t epoch, int count) {
+  if constexpr (!SHUF) return 0;
+  if (!P.shuffle_seed) return 0;
+  uint32_t h = P.shuffle_seed ^ (epoch * 0x9E3779B9u) ^ ((uint32_t)k * 0x85EBCA6Bu);
+  h ^= h >> 16;
+  h *= 0x7FEB352Du;
+  h ^= h >> 15;
+  h *= 0x846CA68Bu;
+  h ^= h >> 16;
+  return (int)(h % (uint32_t)count);
 }
 
 struct WBuf {
@@ -224,34 +249,37 @@ __device__ __forceinline__ void fetch_task(const Params& P, int layer, int t, WB
 // The first NB tasks of operator k for compute wave c: pool slots c, NC + c,
 // 2 NC + c, ... (increasing, so the valid ones are a prefix).
 template <int TT, bool EXACT>
-__device__ __forceinline__ void fetch_first_t(const Params& P, int layer, int count, int c, WBuf (&B)[NB],
+__device__ __forceinline__ void fetch_first_t(const Params& P, int layer, int count, int rot, int c, WBuf (&B)[NB],
                                               int (&t)[NB], int lane) {
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    t[i] = mslot(i * NC + c, count);
+    t[i] = mslot(i * NC + c, count, rot);
     if (t[i] < count) fetch_task<TT, EXACT>(P, layer, t[i], B[i], lane);
   }
 }
-template <bool EXACT>
-__device__ __forceinline__ void fetch_first(const Params& P, int k, int c, WBuf (&B)[NB], int (&t)[NB], int lane) {
+// (epoch: the step operator k belongs to)
+template <bool EXACT, bool SHUF>
+__device__ __forceinline__ void fetch_first(const Params& P, int k, uint32_t epoch, int c, WBuf (&B)[NB],
+                                            int (&t)[NB], int lane) {
   const int type = op_type(k, P.L), layer = type == TT_LM ? P.L : k / 4, count = op_count(P, type);
+  const int rot = op_rot<SHUF>(P, k, epoch, count);
   switch (type) {
-    case TT_QKV: fetch_first_t<TT_QKV, EXACT>(P, layer, count, c, B, t, lane); break;
-    case TT_O: fetch_first_t<TT_O, EXACT>(P, layer, count, c, B, t, lane); break;
-    case TT_GU: fetch_first_t<TT_GU, EXACT>(P, layer, count, c, B, t, lane); break;
-    case TT_DOWN: fetch_first_t<TT_DOWN, EXACT>(P, layer, count, c, B, t, lane); break;
-    default: fetch_first_t<TT_LM, EXACT>(P, layer, count, c, B, t, lane); break;
+    case TT_QKV: fetch_first_t<TT_QKV, EXACT>(P, layer, count, rot, c, B, t, lane); break;
+    case TT_O: fetch_first_t<TT_O, EXACT>(P, layer, count, rot, c, B, t, lane); break;
+    case TT_GU: fetch_first_t<TT_GU, EXACT>(P, layer, count, rot, c, B, t, lane); break;
+    case TT_DOWN: fetch_first_t<TT_DOWN, EXACT>(P, layer, count, rot, c, B, t, lane); break;
+    default: fetch_first_t<TT_LM, EXACT>(P, layer, count, rot, c, B, t, lane); break;
   }
 }
 
 // Next pool slot's task, or `count` when the pool is empty or the wave's
 // result slots would overflow (j results kept, NB - 1 tasks in flight).
-__device__ __forceinline__ int mnext(uint32_t* pool, int j, int count, int lane) {
+__device__ __forceinline__ int mnext(uint32_t* pool, int j, int count, int rot, int lane) {
   if (j + NB > kMegaMaxTasks) return count;
   uint32_t p = 0;
   if (lane == 0) p = lds_add(pool, 1u);
   p = __builtin_amdgcn_readfirstlane(p);
-  return mslot(p, count);
+  return mslot(p, count, rot);
 }
 
 // Streams the wave's tasks of one operator.  On entry buffer i holds task t[i]
@@ -259,8 +287,9 @@ __device__ __forceinline__ int mnext(uint32_t* pool, int j, int count, int lane)
 // Every exit has its own unrolled drain, so the loads in flight at each
 // consume are a fixed count.  Results go to res/ids; returns their number.
 template <int TT, bool EXACT>
-__device__ __forceinline__ int stream_op(const Params& P, int layer, int count, WBuf (&B)[NB], int (&t)[NB],
-                                         const float* page, float* res, int* ids, uint32_t* pool, int lane) {
+__device__ __forceinline__ int stream_op(const Params& P, int layer, int count, int rot, WBuf (&B)[NB],
+                                         int (&t)[NB], const float* page, float* res, int* ids, uint32_t* pool,
+                                         int lane) {
   float y[kR];
   int j = 0;
   if (t[NB - 1] >= count) {  // fewer than NB tasks: the valid prefix
@@ -277,7 +306,7 @@ __device__ __forceinline__ int stream_op(const Params& P, int layer, int count, 
     for (int i = 0; i < NB; ++i) {
       gemv_run<kR, kD, EXACT>(B[i].w, B[i].g, page, lane, y);
       gemv_put<TT>(res, ids, j++, t[i], y, lane);
-      const int n = mnext(pool, j, count, lane);
+      const int n = mnext(pool, j, count, rot, lane);
       if (n >= count) {
 #pragma unroll
         for (int m = 1; m < NB; ++m) {
@@ -358,16 +387,17 @@ __device__ __forceinline__ void finish_op(const Params& P, const MegaBufs& M, co
   }
 }
 
-template <int TT, bool EXACT>
+template <int TT, bool EXACT, bool SHUF>
 __device__ __forceinline__ void compute_op(const Params& P, const MegaBufs& M, const Step& S, int k, WBuf (&B)[NB],
                                            int (&t)[NB], const float* page, float* res, int* ids,
                                            const float* resid, const float* rope, MegaLds* L, int lane) {
   const int layer = TT == TT_LM ? P.L : k / 4, count = op_count(P, TT);
-  const int n = stream_op<TT, EXACT>(P, layer, count, B, t, page, res, ids, &L->pool[k & 1], lane);
+  const int n = stream_op<TT, EXACT>(P, layer, count, op_rot<SHUF>(P, k, S.epoch, count), B, t, page, res, ids,
+                                     &L->pool[k & 1], lane);
   finish_op<TT>(P, M, S, layer, n, res, ids, resid, rope, L, lane);
 }
 
-template <bool EXACT>
+template <bool EXACT, bool SHUF>
 __device__ __forceinline__ void compute_wave(const Params& P, const MegaBufs& M, const Step& S, MegaLds* L,
                                              float* pages, int pf, const float* resid, const float* rope, float* res,
                                              int* ids, int c, int lane, WBuf (&B)[NB], int (&t)[NB], bool more) {
@@ -382,17 +412,17 @@ __device__ __forceinline__ void compute_wave(const Params& P, const MegaBufs& M,
     const float* page = pages + ((k & 1) ? pf : 0);
     const uint64_t t0 = M.trace ? clock_now() : 0;
     switch (op_type(k, P.L)) {
-      case TT_QKV: compute_op<TT_QKV, EXACT>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
-      case TT_O: compute_op<TT_O, EXACT>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
-      case TT_GU: compute_op<TT_GU, EXACT>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
-      case TT_DOWN: compute_op<TT_DOWN, EXACT>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
-      default: compute_op<TT_LM, EXACT>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
+      case TT_QKV: compute_op<TT_QKV, EXACT, SHUF>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
+      case TT_O: compute_op<TT_O, EXACT, SHUF>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
+      case TT_GU: compute_op<TT_GU, EXACT, SHUF>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
+      case TT_DOWN: compute_op<TT_DOWN, EXACT, SHUF>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
+      default: compute_op<TT_LM, EXACT, SHUF>(P, M, S, k, B, t, page, res, ids, resid, rope, L, lane); break;
     }
     // the next operator's first tasks go in flight before this one is
     // reported done: the stagers then poll the next input behind the burst
     // of weight loads rather than competing with it
-    if (k + 1 < nops) fetch_first<EXACT>(P, k + 1, c, B, t, lane);
-    else if (more) fetch_first<EXACT>(P, 0, c, B, t, lane);
+    if (k + 1 < nops) fetch_first<EXACT, SHUF>(P, k + 1, S.epoch, c, B, t, lane);
+    else if (more) fetch_first<EXACT, SHUF>(P, 0, S.epoch + 1, c, B, t, lane);
     if (M.trace && lane == 0) {
       const uint64_t t1 = clock_now();
       M.trace[((size_t)k * gridDim.x + blockIdx.x) * kTraceSlots + c] = ((t1 - t0) << 32) | (uint32_t)t1;
@@ -937,7 +967,7 @@ __device__ __forceinline__ void stager_wave(const Params& P, const MegaBufs& M, 
   }
 }
 
-template <bool EXACT, int HD, typename KT, int GQ>
+template <bool EXACT, int HD, typename KT, int GQ, bool SHUF>
 __device__ __forceinline__ void mega_body(const Params& P, const MegaBufs& M, const Step& S, int) {
   extern __shared__ __align__(16) unsigned char smem[];
   MegaLds* L = reinterpret_cast<MegaLds*>(smem);
@@ -992,11 +1022,11 @@ __device__ __forceinline__ void mega_body(const Params& P, const MegaBufs& M, co
     float* r = res + c * rs;
     WBuf B[NB];  // the next operator's first tasks, in flight across operators and steps
     int t[NB];
-    fetch_first<EXACT>(P, 0, c, B, t, lane);
+    fetch_first<EXACT, SHUF>(P, 0, S.epoch, c, B, t, lane);
     for (int i = 0; i < nst; ++i) {
       Step Si;
       if (!begin_step(i, Si)) return;
-      compute_wave<EXACT>(P, M, Si, L, pages, pf, resid, rope, r, reinterpret_cast<int*>(r + kMegaMaxTasks * kR), c,
+      compute_wave<EXACT, SHUF>(P, M, Si, L, pages, pf, resid, rope, r, reinterpret_cast<int*>(r + kMegaMaxTasks * kR), c,
                           lane, B, t, i + 1 < nst);
       __syncthreads();
     }
@@ -1008,14 +1038,18 @@ __device__ __forceinline__ void mega_body(const Params& P, const MegaBufs& M, co
 // S.nsteps decode steps of one sequence, per (EXACT, head_dim, cache element
 // type, query heads per KV head).  EXACT: every GEMV operator's K is a multiple of
 // 512 with a chunk count that is a multiple of the in-flight depth (no
-// clamped loads).  The host picks the instance (mega_kernel).
+// clamped loads).  The generic (n) instances also deal tasks in the order
+// MK_FLAG_SHUFFLE asks for; the exact (x) ones, which the production shapes
+// run, carry no rotation at all.  The host picks the instance (mega_kernel).
 #define MK_MEGA(X, HD, KN, KT, G)                                                                          \
   extern "C" __global__ __launch_bounds__(kMegaWaves * kWave) void mk_mega_##X##_##HD##_##KN##_g##G(       \
       Params P, MegaBufs M, Step S, int pf) {                                                              \
-    mega_body<X##_EXACT, HD, KT, G>(P, M, S, pf);                                                          \
+    mega_body<X##_EXACT, HD, KT, G, X##_SHUF>(P, M, S, pf);                                                \
   }
 #define x_EXACT true
 #define n_EXACT false
+#define x_SHUF false
+#define n_SHUF true
 #define MK_MEGA_G(X, HD, KN, KT) MK_MEGA(X, HD, KN, KT, 1) MK_MEGA(X, HD, KN, KT, 2) MK_MEGA(X, HD, KN, KT, 4) \
   MK_MEGA(X, HD, KN, KT, 8)
 #if MK_MEGA_PART == 0
@@ -1043,6 +1077,8 @@ int mega_lds_bytes(int H, int nq, int nkv, int hd, int F, int* page_floats) {
 #undef MK_MEGA_G
 #undef n_EXACT
 #undef x_EXACT
+#undef n_SHUF
+#undef x_SHUF
 #undef MK_MEGA
 
 }  // namespace mk

@@ -203,6 +203,7 @@ struct Params {
   int32_t ncu;          // persistent grid
   uint32_t timeout_ticks;   // wall-clock limit of any single wait
   uint32_t spin_limit;      // iteration limit of any single wait (backstop if the clock stalls)
+  uint32_t shuffle_seed;    // nonzero: the megakernel rotates each operator's task dealing (MK_FLAG_SHUFFLE)
   // weights (bf16)
   const uint16_t* embed;
   const uint16_t* lm_head;

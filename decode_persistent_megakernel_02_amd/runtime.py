@@ -58,7 +58,8 @@ def generate_device_weights(shape, seed=0, random_norms=False, device="cuda", pr
 
 
 def create(shape, weights: dict, max_seq: int, max_batch: int = 1, mode=abi.MK_MODE_PER_OP, flags=0,
-           watchdog_ms=0, num_cus=0, attn_split=0, kv_fp32=True, stream=None) -> abi.Handle:
+           watchdog_ms=0, num_cus=0, attn_split=0, kv_fp32=True, stream=None, debug_seed=0) -> abi.Handle:
     """KV cache in fp32 by default (the batched workloads state a bf16 cache and pass kv_fp32=False)."""
-    cfg = abi.make_config(shape, max_seq, max_batch, mode, flags, watchdog_ms, num_cus, attn_split, kv_fp32)
+    cfg = abi.make_config(shape, max_seq, max_batch, mode, flags, watchdog_ms, num_cus, attn_split, kv_fp32,
+                          debug_seed)
     return abi.mk_create(cfg, weights, stream)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1
+#define MK_ABI_VERSION 2
 
 typedef struct mk_handle mk_handle; /* opaque */
 
@@ -91,6 +91,15 @@ enum {
                                         matrix-core GEMMs on split fp32 activations, causal attention
                                         over the cache; either mode.  Needs row-major weights.  Without
                                         it, prefill runs one decode step per position */
+  MK_FLAG_SHUFFLE = 1u << 7, /* megakernel mode: deal every GEMV operator's tasks to the
+                                workgroups in a rotated order, the rotation drawn per operator and
+                                step from mk_config.debug_seed.  Which workgroup runs a task, and
+                                when, must not change any result: the test suite compares the
+                                outputs bit for bit with and without it (a race or an
+                                order-dependent result would show as a difference).  A shuffled
+                                handle runs the generic megakernel instance (clamped loads), whose
+                                arithmetic is the same.  Per-operator and batched handles refuse
+                                it (MK_ERR_INVALID_ARG) */
   MK_FLAG_TILED_WEIGHTS = 1u << 4 /* batched path (max_batch >= 2): wq, wk, wv, wo, w_gate, w_up,
                                      w_down and (untied) lm_head are stored in the tiled layout that
                                      mk_tile_weights writes; embed and the norm gains stay
@@ -131,6 +140,7 @@ typedef struct {
                           0 = every CU of the device */
   int32_t attn_split;  /* positions per split-KV attention task; 0 = automatic (64) */
   int32_t kv_fp32;     /* KV cache element type: 0 = bf16, nonzero = fp32 */
+  uint32_t debug_seed; /* seed of MK_FLAG_SHUFFLE's task orders; ignored without it */
 } mk_config;
 
 /* Weights: bf16 bit patterns, row-major [out, in], contiguous, device memory.

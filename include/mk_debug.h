@@ -25,8 +25,24 @@ typedef struct {
 /* Build the graph for `cfg` on `ncu` CUs and run the static validator
  * (coverage, topological queues, thresholds, read-after-write covered by
  * waits, RoPE pairs whole).  MK_ERR_INVALID_ARG with the validator's message
- * on failure. */
+ * on failure.  For max_batch >= 2 the graph is the batched launch plan: one
+ * stage per launch (n_stages), each stage's tasks its workgroups (max_queue /
+ * min_queue: the largest and smallest stage), validated for coverage of
+ * every projection's (row group, K chunk) pairs, of every output element and
+ * split partial, and for reads of earlier stages only; n_events, the per-CU
+ * byte fields are 0 and weight_bytes is what the projections stream. */
 mk_status mk_graph_inspect(const mk_config* cfg, int32_t ncu, mk_graph_info* out);
+
+/* Test hook for the batched graph's validator (max_batch >= 2): build the
+ * graph, plant one mistake, validate.  fault: 1 a projection workgroup takes
+ * the row block of its neighbour, 2 a finishing task takes its neighbour's
+ * row group, 3 the O projection's launch moves before the attention merge, 4
+ * the down projection's finishing launch expects one K split more than ran,
+ * 5 the last attention split of a KV head repeats the first.  Returns
+ * MK_ERR_INVALID_ARG with the validator's message when it catches the mistake,
+ * MK_OK when it does not, MK_ERR_UNSUPPORTED if the config has no place for
+ * that mistake (e.g. no split projection). */
+mk_status mk_batched_graph_fault(const mk_config* cfg, int32_t ncu, int32_t fault);
 
 typedef struct {
   int32_t completed;     /* 1 if every task ran */

@@ -37,8 +37,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_config_struct_layout_matches_header():
-    # 18 four-byte fields, no padding
-    assert ctypes.sizeof(abi.mk_config) == 19 * 4  # 19 four-byte fields, no padding
+    assert ctypes.sizeof(abi.mk_config) == 20 * 4  # 20 four-byte fields, no padding
     assert ctypes.sizeof(abi.mk_weights) == 12 * 8
     assert abi.task_dtype().itemsize == 48
 
@@ -59,6 +58,19 @@ def test_invalid_configs_are_rejected():
         assert e.value.status == abi.MK_ERR_INVALID_ARG, b
 
 
+def test_shuffle_flag_is_megakernel_only():
+    """MK_FLAG_SHUFFLE reorders the megakernel's task dealing; per-operator and
+    batched handles refuse it on the host."""
+    for kw in (dict(mode=abi.MK_MODE_PER_OP), dict(mode=abi.MK_MODE_MEGAKERNEL, max_batch=2)):
+        c = cfg_for(MINI, flags=abi.MK_FLAG_SHUFFLE, debug_seed=7, **kw)
+        with pytest.raises(abi.MkError) as e:
+            abi.mk_graph_inspect(c, 8)
+        assert e.value.status == abi.MK_ERR_INVALID_ARG, kw
+    c = cfg_for(MINI, mode=abi.MK_MODE_MEGAKERNEL, flags=abi.MK_FLAG_SHUFFLE, debug_seed=7)
+    info = abi.mk_graph_inspect(c, 8)
+    assert info is not None
+
+
 def test_tiled_weights_flag_is_checked_on_the_host():
     from tests.shapes import MINI_TILE
     # batch 1 never reads tiled weights; MINI's ffn (264) is not a multiple of 32
@@ -67,11 +79,9 @@ def test_tiled_weights_flag_is_checked_on_the_host():
         with pytest.raises(abi.MkError) as e:
             abi.mk_graph_inspect(c, 8)
         assert e.value.status == abi.MK_ERR_INVALID_ARG, (shape.name, B)
-    # a valid batched tiled config passes the checks (the task graph itself is batch-1 only)
+    # a valid batched tiled config passes the checks and its batched graph validates
     c = cfg_for(MINI_TILE, max_batch=4, flags=abi.MK_FLAG_TILED_WEIGHTS)
-    with pytest.raises(abi.MkError) as e:
-        abi.mk_graph_inspect(c, 8)
-    assert e.value.status == abi.MK_ERR_UNSUPPORTED
+    assert abi.mk_graph_inspect(c, 8).n_stages > 0
 
 
 def test_tile_weights_rejects_bad_shapes_before_any_launch():
@@ -129,13 +139,52 @@ def test_megakernel_split_keeps_one_attention_unit_per_workgroup():
         assert shape.n_kv_heads * info.nsplit <= 256
 
 
-def test_task_graph_is_single_sequence():
-    """The tGraph builder covers batch 1; batched steps run as per-operator
-    launches with no task table, so asking for a batched graph is refused."""
-    c = cfg_for(presets.LLAMA8B, max_seq=4224, max_batch=8)
-    with pytest.raises(abi.MkError) as e:
-        abi.mk_graph_inspect(c, 256)
-    assert e.value.status == abi.MK_ERR_UNSUPPORTED
+def _projection_bytes(s):
+    """bf16 bytes of every projection of every layer plus the LM head."""
+    mats = s.hidden * (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim + s.hidden * s.n_q_heads * s.head_dim \
+        + 3 * s.hidden * s.ffn
+    return 2 * (s.n_layers * mats + s.vocab * s.hidden)
+
+
+BATCHED_CASES = [("llama8b_b8_kv4096", presets.LLAMA8B, 8, 4224), ("llama70b_b64", presets.LLAMA70B, 64, 576),
+                 ("mini_b2", MINI, 2, 40), ("mini_b17", MINI, 17, 40), ("mini_g8_b33", MINI_G8, 33, 24),
+                 ("tiny_b64", presets.TINY, 64, 2000)]
+
+
+@pytest.mark.parametrize("name,shape,B,max_seq", BATCHED_CASES, ids=[c[0] for c in BATCHED_CASES])
+@pytest.mark.parametrize("fused", [False, True], ids=["merge_launch", "fused_merge"])
+def test_batched_graph_validates_and_reads_every_weight_once(name, shape, B, max_seq, fused):
+    """The batched launch plan as a task graph (one stage per launch): it
+    validates, its projection tasks stream every weight exactly once, and it
+    has one stage per launch of the step: per layer two norms, four
+    projections each with a finishing stage when K is split, and attention
+    with a merge stage unless one split covers the context."""
+    flags = abi.MK_FLAG_FUSED_MERGE if fused else 0
+    c = cfg_for(shape, max_seq=max_seq, max_batch=B, flags=flags)
+    info = abi.mk_graph_inspect(c, 256)
+    assert info.weight_bytes == _projection_bytes(shape)
+    per_layer_min = 2 + 4 + 1 + (0 if info.nsplit == 1 else 1)
+    assert shape.n_layers * per_layer_min + 3 <= info.n_stages <= shape.n_layers * (per_layer_min + 4) + 3
+    assert info.min_queue >= 1 and info.max_queue >= B
+
+
+@pytest.mark.parametrize("fault", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("name,shape,B,max_seq", BATCHED_CASES[:2], ids=[c[0] for c in BATCHED_CASES[:2]])
+def test_batched_graph_validator_catches_planted_mistakes(name, shape, B, max_seq, fault):
+    """A workgroup on its neighbour's row block, a finishing task on its
+    neighbour's row group, the O projection moved before the merge, a
+    finishing launch that expects one K split more than ran, and an attention
+    split that repeats another: each must fail validation."""
+    c = cfg_for(shape, max_seq=max_seq, max_batch=B)
+    try:
+        abi.mk_batched_graph_fault(c, 256, fault)
+    except abi.MkError as e:
+        if e.status == abi.MK_ERR_UNSUPPORTED:
+            pytest.skip(str(e))
+        assert e.status == abi.MK_ERR_INVALID_ARG, str(e)
+        assert "validation" in str(e)
+    else:
+        pytest.fail(f"fault {fault} passed validation")
 
 
 @pytest.mark.parametrize("wl", ["tiny", "llama1b", "llama8b"])

@@ -1,5 +1,6 @@
 """Full-size parity: the Llama-3.2-1B and Llama-3-8B shapes in the launch
-configuration the benchmark times (kernel-per-operator mode, every CU).
+configurations the benchmark times (the persistent megakernel, one launch per
+step, and the kernel-per-operator build; every CU).
 
 The oracle cannot afford hundreds of fp64 decode steps at these sizes, so the
 GPU decodes seeded random tokens after the seeded 39-token prompt (teacher
@@ -20,8 +21,10 @@ from tests.gpu_util import rel_err
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("wl_name,kv_fp32", [("llama1b", True), ("llama1b", False), ("llama8b", True)])
-def test_full_size_logits_and_tokens(wl_name, kv_fp32):
+@pytest.mark.parametrize("wl_name,kv_fp32,mode", [("llama1b", True, "per_op"), ("llama1b", False, "per_op"),
+                                                   ("llama8b", True, "per_op"), ("llama1b", True, "megakernel"),
+                                                   ("llama8b", True, "megakernel")])
+def test_full_size_logits_and_tokens(wl_name, kv_fp32, mode):
     """fp32 KV cache: compared with the fp64 oracle.  bf16 KV cache: compared
     with the oracle that rounds its cached K/V to bf16 (the storage format)."""
     if not torch.cuda.is_available():
@@ -36,7 +39,8 @@ def test_full_size_logits_and_tokens(wl_name, kv_fp32):
     print(f"[{wl_name}] generating weights", flush=True)
     w = gen.gen_weights(shape, wl.weight_seed)
     dw = runtime.upload_weights(w)
-    h = runtime.create(shape, dw, wl.max_seq, mode=abi.MK_MODE_PER_OP, kv_fp32=kv_fp32)
+    m = abi.MK_MODE_MEGAKERNEL if mode == "megakernel" else abi.MK_MODE_PER_OP
+    h = runtime.create(shape, dw, wl.max_seq, mode=m, kv_fp32=kv_fp32)
     out = torch.zeros(1, dtype=torch.int32, device="cuda")
     lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
     got_logits, got_tok = [], []
@@ -60,7 +64,7 @@ def test_full_size_logits_and_tokens(wl_name, kv_fp32):
     errs = rel_err(np.stack(got_logits), ref)
     errs_kv = rel_err(np.stack(got_logits), ref_kv)
     kv_only = rel_err(ref_kv, ref)
-    print(f"[{wl_name} kv_fp32={kv_fp32}] max rel err vs fp64 oracle {errs.max():.3e}; vs bf16-KV oracle "
+    print(f"[{wl_name} kv_fp32={kv_fp32} {mode}] max rel err vs fp64 oracle {errs.max():.3e}; vs bf16-KV oracle "
           f"{errs_kv.max():.3e}; bf16-KV oracle vs fp64 oracle {kv_only.max():.3e}", flush=True)
     mine = errs if kv_fp32 else errs_kv
     assert np.all(mine <= 2e-2)   # the contract

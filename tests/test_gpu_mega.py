@@ -93,6 +93,40 @@ def test_megakernel_agrees_with_per_op(abi, shape):
     assert err <= 1e-5, err
 
 
+@pytest.mark.parametrize("shape,kv_bf16", [(MINI, False), (MINI_G8, True), (MINI_HD128_G2, False)],
+                         ids=["mini", "g8_bf16kv", "hd128_g2"])
+def test_shuffled_task_dealing_changes_nothing(abi, shape, kv_bf16):
+    """MK_FLAG_SHUFFLE rotates every GEMV operator's task list by a seeded
+    amount per operator and step, so other workgroups run the tasks in
+    another order.  Every task's result depends only on its rows and the
+    staged input, so the logits and ids must be bit-identical to the unshuffled
+    handle's, over a one-launch prefill, single steps and a multi-step launch,
+    for two seeds."""
+    from decode_persistent_megakernel_02_amd import runtime
+    w = gen.gen_weights(shape, 6, True)
+    prompt = gen.tokens(21, 3, 0, 11, shape.vocab)
+    p_t = torch.from_numpy(prompt.reshape(1, -1)).cuda()
+    dw = runtime.upload_weights(w)
+    runs = []
+    for flags, seed in ((0, 0), (abi.MK_FLAG_SHUFFLE, 1), (abi.MK_FLAG_SHUFFLE, 0xC0FFEE)):
+        h = runtime.create(shape, dw, 40, mode=MEGA, flags=flags, watchdog_ms=WATCHDOG_MS, attn_split=8,
+                           kv_fp32=not kv_bf16, debug_seed=seed)
+        toks = torch.zeros(12, dtype=torch.int32, device="cuda")
+        lg = torch.zeros(5, shape.vocab, dtype=torch.float32, device="cuda")
+        abi.mk_prefill(h, p_t, toks[0:1], lg[0:1])
+        for s in range(3):
+            abi.mk_decode_step(h, toks[s:s + 1], toks[s + 1:s + 2], lg[s + 1:s + 2])
+        abi.mk_generate(h, toks[3:4], 8, toks[4:12], lg[4:5])
+        abi.mk_synchronize(h)
+        runs.append((toks.cpu().numpy(), lg.cpu().numpy()))
+        abi.mk_destroy(h)
+    for r in runs[1:]:
+        assert np.array_equal(r[0], runs[0][0])
+        assert np.array_equal(r[1].view(np.uint32), runs[0][1].view(np.uint32))
+    ref = D.Decoder(shape, w, 1, 40, kv_bf16=kv_bf16).prefill(prompt.reshape(1, -1))[0]
+    assert rel_err(runs[0][1][0], ref) <= TIGHT
+
+
 def test_free_running_matches_until_low_margin(abi):
     from decode_persistent_megakernel_02_amd import runtime
     wl = presets.WORKLOADS["tiny"]
