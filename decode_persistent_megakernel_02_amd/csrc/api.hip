@@ -375,9 +375,16 @@ int bgemm_splits(const Params& P, int type, int ncu) {
   // Two per CU is also as many of those workgroups as the CUs hold at once
   // (LDS), so there the count rounds down: a few more would run in a second
   // round (70B shape, 64 sequences: QKV in 7 splits was 560 workgroups).
+  // With one batch tile (up to 16 sequences) it rounds down too: at the 8B
+  // shape with 8 sequences gate/up then runs unsplit (224 workgroups, no
+  // finishing launch) and QKV in 5 splits instead of 6 (240 workgroups, not
+  // 288): 4.710 -> 4.581 ms/step.  Rounding down at four batch tiles with two
+  // row groups per wave (the 70B shape's gate/up, 64 sequences: one split
+  // instead of two) was slower: 33.07 -> 33.85 ms/step.
   const bool two = bt == 4 && bgemm_gpw(P, type) == 1;
   const int target = (two ? 2 : 1) * ncu;
-  int ks = std::max(1, std::min(nch, two ? target / ngx : (target + ngx - 1) / ngx));
+  const bool round_down = two || bt == 1;
+  int ks = std::max(1, std::min(nch, round_down ? target / ngx : (target + ngx - 1) / ngx));
   const int per = (nch + ks - 1) / ks;
   return (nch + per - 1) / per;
 }
@@ -726,6 +733,7 @@ mk_status mk_create(const mk_config* cfg, const mk_weights* w, void* hip_stream,
   P.spin_limit = (uint32_t)std::min(4.0e9, wd_ms * 1000.0 * 50.0);
   if (cfg->flags & MK_FLAG_SPIN_LIMIT_1) P.spin_limit = 1;
   P.shuffle_seed = 0;
+  P.o_delay_ticks = (uint32_t)(kMegaOPrefetchDelayUs * tpu);
   if (cfg->flags & MK_FLAG_SHUFFLE) {  // splitmix64 of the caller's seed, made nonzero
     uint64_t z = (uint64_t)cfg->debug_seed + 0x9E3779B97F4A7C15ull;
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;

@@ -420,7 +420,24 @@ __device__ __forceinline__ void compute_wave(const Params& P, const MegaBufs& M,
     }
     // the next operator's first tasks go in flight before this one is
     // reported done: the stagers then poll the next input behind the burst
-    // of weight loads rather than competing with it
+    // of weight loads rather than competing with it.  After QKV the attention
+    // path (unit inputs, split records, merged outputs: three hand-overs
+    // between workgroups) is the critical path and the O projection's weights
+    // are not: their prefetch waits o_delay_ticks after QKV is reported done,
+    // so that it does not queue ahead of those hand-overs' reads (it still
+    // arrives before the O input does).
+    const bool hold = (k & 3) == 0 && k + 1 < nops && P.o_delay_ticks;
+    if (hold) {
+      if (M.trace && lane == 0) {
+        const uint64_t t1 = clock_now();
+        M.trace[((size_t)k * gridDim.x + blockIdx.x) * kTraceSlots + c] = ((t1 - t0) << 32) | (uint32_t)t1;
+      }
+      if (lane == 0) lds_rel_add(&L->done[k & 1], 1u);
+      const uint64_t d0 = clock_now();
+      while (clock_now() - d0 < P.o_delay_ticks) __builtin_amdgcn_s_sleep(8);
+      fetch_first<EXACT, SHUF>(P, k + 1, S.epoch, c, B, t, lane);
+      continue;
+    }
     if (k + 1 < nops) fetch_first<EXACT, SHUF>(P, k + 1, S.epoch, c, B, t, lane);
     else if (more) fetch_first<EXACT, SHUF>(P, 0, S.epoch + 1, c, B, t, lane);
     if (M.trace && lane == 0) {

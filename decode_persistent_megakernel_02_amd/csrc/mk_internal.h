@@ -204,6 +204,7 @@ struct Params {
   uint32_t timeout_ticks;   // wall-clock limit of any single wait
   uint32_t spin_limit;      // iteration limit of any single wait (backstop if the clock stalls)
   uint32_t shuffle_seed;    // nonzero: the megakernel rotates each operator's task dealing (MK_FLAG_SHUFFLE)
+  uint32_t o_delay_ticks;   // megakernel: clock ticks the O projection's prefetch waits after the local QKV tasks
   // weights (bf16)
   const uint16_t* embed;
   const uint16_t* lm_head;
@@ -284,6 +285,10 @@ constexpr int kMegaStagers = 4;   // waves that stage operator inputs and run at
 constexpr int kMegaCompute = 4;   // waves that stream weights (the GEMV tasks), four tasks in flight each
 constexpr int kMegaWaves = kMegaStagers + kMegaCompute;
 constexpr int kMegaTraceSlots = kMegaCompute + 10;  // timestamps per (operator, workgroup) when tracing
+// Microseconds the compute waves hold back the O projection's weight prefetch
+// after their QKV tasks (8B shape, 256 steps: 0 us 3.154, 3 us 3.127, 6 us
+// 3.133, 8 us 3.175 ms/token).
+constexpr double kMegaOPrefetchDelayUs = 3.0;
 
 // Buffers through which workgroups hand values to each other.  Each element
 // is a 64-bit word: fp32 value bits in the low half, the epoch of the step
