@@ -139,41 +139,51 @@ class Decoder:
         ("xmid", l) residual after attention, ("h", l) SwiGLU output, ("x", l+1)
         residual after layer l.
         """
-        sh = self.shape
         tokens = np.asarray(tokens, dtype=np.int64).reshape(self.B)
         p = self.length
         if p >= self.max_seq:
             raise IndexError("KV cache full")
-        nq, nkv, hd = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
-        emb = self.w["embed"]
-        x = widen_bf16(emb[tokens])                                  # [B, H]
-        for l in range(sh.n_layers):
-            pre = f"layers.{l}."
-            r = rmsnorm(x, self.W(pre + "attn_norm")[0], sh.rms_eps)
-            q = (r @ self.W(pre + "wq").T).reshape(self.B, nq, hd)
-            k = (r @ self.W(pre + "wk").T).reshape(self.B, nkv, hd)
-            v = (r @ self.W(pre + "wv").T).reshape(self.B, nkv, hd)
-            q = rope(q, p, sh.rope_theta)
-            k = rope(k, p, sh.rope_theta)
-            self.K[l, :, :, p] = self._store_kv(k)
-            self.V[l, :, :, p] = self._store_kv(v)
-            o = np.stack([gqa_attention(q[b], self.K[l, b, :, :p + 1], self.V[l, b, :, :p + 1])
-                          for b in range(self.B)])
-            x = x + o.reshape(self.B, nq * hd) @ self.W(pre + "wo").T
-            r = rmsnorm(x, self.W(pre + "ffn_norm")[0], sh.rms_eps)
-            hh = swiglu(r, self.W(pre + "w_gate"), self.W(pre + "w_up"))
-            if trace is not None:
-                trace[("q", l)] = q.reshape(self.B, nq * hd)
-                trace[("attn", l)] = o.reshape(self.B, nq * hd)
-                trace[("xmid", l)] = x
-                trace[("h", l)] = hh
-            x = x + hh @ self.W(pre + "w_down").T
-            if trace is not None:
-                trace[("x", l + 1)] = x
-        r = rmsnorm(x, self.W("final_norm")[0], sh.rms_eps)
-        logits = r @ self.W(self._lm_head()).T
+        x = widen_bf16(self.w["embed"][tokens])                      # [B, H]
+        for l in range(self.shape.n_layers):
+            x = self.layer(l, x, p, trace)
+        logits = self.head(x)
         self.length = p + 1
         return logits
+
+    def layer(self, l: int, x: np.ndarray, p: int, trace: dict = None) -> np.ndarray:
+        """Decoder layer l on the residual stream x [B, H] of the token at
+        position p: appends its K/V at p to the cache and returns the residual
+        stream after the layer (the body of `step`; see there for `trace`)."""
+        sh = self.shape
+        nq, nkv, hd = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
+        pre = f"layers.{l}."
+        r = rmsnorm(x, self.W(pre + "attn_norm")[0], sh.rms_eps)
+        q = (r @ self.W(pre + "wq").T).reshape(self.B, nq, hd)
+        k = (r @ self.W(pre + "wk").T).reshape(self.B, nkv, hd)
+        v = (r @ self.W(pre + "wv").T).reshape(self.B, nkv, hd)
+        q = rope(q, p, sh.rope_theta)
+        k = rope(k, p, sh.rope_theta)
+        self.K[l, :, :, p] = self._store_kv(k)
+        self.V[l, :, :, p] = self._store_kv(v)
+        o = np.stack([gqa_attention(q[b], self.K[l, b, :, :p + 1], self.V[l, b, :, :p + 1])
+                      for b in range(self.B)])
+        x = x + o.reshape(self.B, nq * hd) @ self.W(pre + "wo").T
+        r = rmsnorm(x, self.W(pre + "ffn_norm")[0], sh.rms_eps)
+        hh = swiglu(r, self.W(pre + "w_gate"), self.W(pre + "w_up"))
+        if trace is not None:
+            trace[("q", l)] = q.reshape(self.B, nq * hd)
+            trace[("attn", l)] = o.reshape(self.B, nq * hd)
+            trace[("xmid", l)] = x
+            trace[("h", l)] = hh
+        x = x + hh @ self.W(pre + "w_down").T
+        if trace is not None:
+            trace[("x", l + 1)] = x
+        return x
+
+    def head(self, x: np.ndarray) -> np.ndarray:
+        """Final RMSNorm and LM head on the last residual stream x [B, H]: logits [B, V]."""
+        r = rmsnorm(x, self.W("final_norm")[0], self.shape.rms_eps)
+        return r @ self.W(self._lm_head()).T
 
     def prefill(self, tokens) -> np.ndarray:
         """Token-by-token decode chain over a prompt [B, P]; returns the last logits [B, V]."""
