@@ -16,7 +16,7 @@ import torch
 
 from oracle import decoder as D
 from synth import gen, presets
-from tests.gpu_util import rel_err
+from tests.gpu_util import d2h, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -125,6 +125,140 @@ def test_batched_workload_long_cache_full_depth():
     for b in range(B):
         if D.top2_margin(ref[b]) > 5e-2:
             assert got_tok[b] == int(D.greedy(ref[b]))
+
+
+def test_megakernel_8b_bench_workload_layers_at_longest_context_against_oracle():
+    """The benchmark's own run, checked where its context is longest: the 8B
+    shape in megakernel mode (fp32 cache, the library's attention split: 18
+    live splits at 551 positions), the seeded 39-token prompt, 511 greedy steps
+    in one launch, then one step more at position 550.  The oracle takes the
+    GPU's residual stream entering layers 0 (the embedding row), 1, 16, 30 and
+    31 (the hand-over words of that step, every one carrying its epoch) and
+    those layers' GPU cache (mk_kv_read), runs each layer in fp64, and
+    compares the residual stream leaving it with the GPU's; then the final
+    norm and LM head on the GPU's last residual stream against the GPU's
+    logits.  fp32 arithmetic and cache against fp64: 1e-4."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_persistent_megakernel_02_amd import abi, runtime
+    wl = presets.WORKLOADS["llama8b"]
+    shape, P, S = wl.shape, wl.prompt_len, wl.decode_steps
+    max_seq, layers, tag = P + S, (0, 1, 16, 30, 31), "8b mega longest context"
+    L, nkv, hd, H = shape.n_layers, shape.n_kv_heads, shape.head_dim, shape.hidden
+    print(f"[{tag}] generating weights", flush=True)
+    w = gen.gen_weights(shape, wl.weight_seed)
+    dw = runtime.upload_weights(w)
+    h = runtime.create(shape, dw, max_seq, mode=abi.MK_MODE_MEGAKERNEL)
+    toks = torch.zeros(S + 1, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(1, shape.vocab, dtype=torch.float32, device="cuda")
+    print(f"[{tag}] prefill {P}, {S - 1} steps in one launch, one step more", flush=True)
+    abi.mk_prefill(h, torch.from_numpy(gen.gen_prompt(wl)).cuda(), toks[0:1])
+    abi.mk_generate(h, toks[0:1], S - 1, toks[1:S])
+    abi.mk_decode_step(h, toks[S - 1:S], toks[S:S + 1], lg)
+    abi.mk_synchronize(h)
+    last_tok = int(toks[S - 1].item())
+    kf = np.empty((L, 1, nkv, max_seq, hd), dtype=np.float32)
+    vf = np.empty_like(kf)
+    abi.mk_kv_read(h, kf, vf)
+    v = abi.mk_get_mega_view(h)
+    xw = np.empty((L + 1) * H, dtype=np.uint64)
+    d2h(xw.ctypes.data, v.x, xw.nbytes)
+    assert np.all((xw[H:] >> np.uint64(32)) == v.epoch), "a word without the last step's epoch"
+    xs = (xw & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32).astype(np.float64).reshape(L + 1, 1, H)
+    got = lg.cpu().numpy()
+    abi.mk_destroy(h)
+    del dw
+    p = max_seq - 1
+    ora = D.Decoder(shape, w, 1, max_seq, cache_weights=False)
+    for l in layers:
+        ora.K[l, :, :, :p] = kf[l, :, :, :p]
+        ora.V[l, :, :, :p] = vf[l, :, :, :p]
+    for l in layers:
+        x_in = D.widen_bf16(w["embed"][[last_tok]]) if l == 0 else xs[l]
+        err = rel_err(xs[l + 1], ora.layer(l, x_in, p))
+        print(f"[{tag}] layer {l}: residual stream after it, max rel err {err.max():.3e}", flush=True)
+        assert np.all(err <= 1e-4), (l, err)
+    errs = rel_err(got, ora.head(xs[L]))
+    print(f"[{tag}] LM head on the last residual stream: max rel logit err {errs.max():.3e}", flush=True)
+    assert np.all(errs <= 1e-4)
+
+
+class _RegeneratedWeights:
+    """The oracle's weight table for a shape too large to hold: every access
+    regenerates the tensor from the seeded generator (the bits the GPU was
+    given); the oracle widens it, uses it and drops it."""
+
+    def __init__(self, shape, seed, tag):
+        self.shape, self.seed, self.tag = shape, seed, tag
+
+    def __getitem__(self, name):
+        print(f"[{self.tag}] oracle: {name}", flush=True)
+        return gen.gen_weight(self.shape, name, self.seed)
+
+
+def test_batched_70b_workload_layers_at_full_depth_against_oracle():
+    """The 70B-shape batched workload at full depth and context: 64 sequences
+    prefilled with their 512-token seeded prompts (batched prefill, bf16
+    cache), then one seeded decode step for all of them.  A full fp64 oracle
+    step at this shape widens 141 GB of weights on the host (most of an hour),
+    so the oracle checks the step layer by layer instead: for two sequences it
+    takes the GPU's residual stream entering layers 0 (the embedding row), 1,
+    39, 78 and 79 and the GPU's cache of those layers (mk_kv_read), runs each layer
+    in fp64 with its weights regenerated from the seeded generator, and
+    compares the residual stream the layer leaves with the GPU's; then the
+    final norm and LM head on the GPU's last residual stream against the
+    GPU's logits.  Every compared layer sees the 513-position context
+    (measured: 1.1e-5 at layer 0, below 1e-6 at layers 39 and 79, 2.6e-6 on
+    the logits; about 40 s on the GPU machine)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from decode_persistent_megakernel_02_amd import abi, runtime
+    wl = presets.WORKLOADS["llama70b_b64"]
+    shape, B, P = wl.shape, wl.batch, wl.prompt_len
+    max_seq, rows, layers = P + 1, 2, (0, 1, 39, 78, 79)
+    tag = "c5 layers"
+    step_tok = gen.tokens(79, presets.TID_PROMPT, 0, B, shape.vocab).astype(np.int32)
+    print(f"[{tag}] generating weights on the device", flush=True)
+    dw = runtime.generate_device_weights(shape, wl.weight_seed)
+    h = runtime.create(shape, dw, max_seq, B, abi.MK_MODE_PER_OP, abi.MK_FLAG_BATCHED_PREFILL, kv_fp32=False)
+    out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(B, shape.vocab, dtype=torch.float32, device="cuda")
+    print(f"[{tag}] prefill {B} x {P}, then one decode step", flush=True)
+    abi.mk_prefill(h, torch.from_numpy(gen.gen_prompt(wl)).cuda(), out, lg)
+    abi.mk_synchronize(h)
+    L, nkv, hd, H = shape.n_layers, shape.n_kv_heads, shape.head_dim, shape.hidden
+    kb = np.empty((L, B, nkv, max_seq, hd), dtype=np.uint16)
+    vb = np.empty_like(kb)
+    abi.mk_kv_read(h, kb, vb)
+    abi.mk_decode_step(h, torch.from_numpy(step_tok).cuda(), out, lg)
+    abi.mk_synchronize(h)
+    xs = np.empty((L + 1) * B * H, dtype=np.float32)
+    d2h(xs.ctypes.data, abi.mk_get_debug_view(h).xs, xs.nbytes)
+    xs = xs.reshape(L + 1, B, H)[:, :rows].astype(np.float64)
+    got = lg.cpu().numpy()[:rows]
+    abi.mk_destroy(h)
+    del dw
+    torch.cuda.empty_cache()
+    ora = D.Decoder(shape, _RegeneratedWeights(shape, wl.weight_seed, tag), rows, max_seq, cache_weights=False,
+                    kv_bf16=True)
+    tid = presets.tensor_id("embed")
+    for l in layers:
+        ora.K[l, :, :, :P] = D.widen_bf16(kb[l, :rows, :, :P])
+        ora.V[l, :, :, :P] = D.widen_bf16(vb[l, :rows, :, :P])
+    del kb, vb
+    for l in layers:
+        if l == 0:  # the embedding rows of the step's tokens
+            x_in = np.stack([D.widen_bf16(gen.bf16_normal(wl.weight_seed, tid, int(t) * H, H)) for t in step_tok[:rows]])
+        else:
+            x_in = xs[l]
+        x_out = ora.layer(l, x_in, P)
+        err = rel_err(xs[l + 1], x_out)
+        print(f"[{tag}] layer {l}: residual stream after it, max rel err {err.max():.3e}", flush=True)
+        assert np.all(err <= 1e-3), (l, err)
+    ref = ora.head(xs[L])
+    errs = rel_err(got, ref)
+    print(f"[{tag}] LM head on the last residual stream: max rel logit err {errs.max():.3e}", flush=True)
+    assert np.all(errs <= 1e-3)
 
 
 _W8X2 = {}
