@@ -86,6 +86,26 @@ def test_counter_scaling_needs_a_copy_kernel(tmp_path):
         counters.copy_scale(cf, "FETCH_SIZE", 1 << 20)
 
 
+def test_matrix_core_summary_averages_each_kernel(tmp_path):
+    """mfma.py: one row per kernel, mean MfmaUtil and mean bf16 work per
+    dispatch, heaviest first; kernels outside --match are left out."""
+    d = tmp_path / "m"
+    d.mkdir()
+    rows = [("mk_b_gu_b4_t_g2", "MfmaUtil", 30.0), ("mk_b_gu_b4_t_g2", "MfmaFlopsBF16", 120e9),
+            ("mk_b_gu_b4_t_g2", "MfmaUtil", 28.0), ("mk_b_gu_b4_t_g2", "MfmaFlopsBF16", 120e9),
+            ("mk_b_o_b4_t", "MfmaUtil", 19.0), ("mk_b_o_b4_t", "MfmaFlopsBF16", 17e9),
+            ("other_kernel", "MfmaUtil", 1.0), ("other_kernel", "MfmaFlopsBF16", 1e9)]
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i // 2 + 1, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+    r = subprocess.run([sys.executable, "-m", "decode_persistent_megakernel_02_amd.mfma", str(d), "--match", "mk_b_"],
+                       check=True, cwd=ROOT, capture_output=True, text=True)
+    lines = [l for l in r.stdout.splitlines() if l.startswith("| mk_")]
+    assert lines == ["| mk_b_gu_b4_t_g2 | 2 | 29.0 | 120.00 |", "| mk_b_o_b4_t | 1 | 19.0 | 17.00 |"]
+
+
 def test_counter_last_dispatches_skip_the_prefill_launch(tmp_path):
     """A megakernel counter run: one launch of the whole prefill (40 steps'
     bytes), then one launch per decode step; --last 3 keeps the decode steps."""
